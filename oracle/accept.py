@@ -1,0 +1,231 @@
+"""Multi-round speculative sampling over a draft tree — oracle side
+(test infrastructure only).
+
+Notation: q = target distribution, p = draft distribution (the lesson page's
+Leviathan section uses this pair; the EAGLE notes page writes p and p-hat).
+
+What the walk does (EAGLE notes page, core mechanism §5 and the "multi-round
+speculative sampling" term; lesson page, "Concept" and build steps 1-3):
+
+  start at the root; at the current node n with children c_1 < c_2 < ... :
+    q_res = softmax(target[n] / tau),  p_n = softmax(draft[n] / tau)
+    for each child c_i in ascending node index:
+        draw r; accept c_i if r < q_res(t) / p_n(t), t = tokens[c_i]
+          -> emit t, move to c_i, start over there
+        otherwise q_res <- norm(max(0, q_res - p_n)) and try the next child
+    all children rejected: emit a sample of q_res and stop
+  a node without children: emit a sample of q_n (the bonus token) and stop
+
+Greedy mode (tau == 0, EAGLE's lossless greedy verification): a_n = argmax of
+target[n] (lowest id on ties); accept the first child whose token is a_n,
+otherwise emit a_n and stop; at a leaf emit a_n.
+
+Readings where the pages are silent or disagree (each listed in the design
+notes):
+  * every sibling is tested against the same parent draft row p_n;
+  * the residual update is cumulative over the rejected siblings;
+  * p_n(t) == 0: accept iff q_res(t) > 0 (the lesson's accept() returns True
+    for p <= 0; the two differ only when q_res(t) == 0 too) — flagged;
+  * residual mass 0: fall back to q_n (the lesson's residual() returns q) —
+    flagged;
+  * comparison is strict, r on the 24-bit grid of the Philox uniform;
+  * temperature divides both target and draft logits;
+  * samples are drawn by inverse CDF over ascending token ids: the smallest v
+    whose running sum exceeds u * (total sum).
+
+Outputs per sequence: accept_len, accepted_nodes (root path, -1 padded),
+out_tokens (tokens of the accepted nodes followed by the final token, -1
+padded), flags, near_ties (decisions on the walk whose margin is below 1e-6:
+|r - q_res(t)/p_n(t)| for a test, |running sum - u * total| / total for a
+sample).  A sequence with an invalid tree, an out-of-range token or an
+unusable logits row (NaN, +inf, or all -inf) is flagged and its integer
+outputs are all -1.
+"""
+import numpy as np
+
+from . import philox
+
+FLAG_BAD_TREE = 1
+FLAG_BAD_TOKEN = 2
+FLAG_NONFINITE = 4
+FLAG_P_ZERO = 8
+FLAG_DEGENERATE_RESIDUAL = 16
+NEAR_TIE = 1e-6
+
+
+def _is_number(x) -> bool:
+    return isinstance(x, (float, int, np.floating))
+
+
+def tree_children(parents):
+    T = len(parents)
+    kids = [[] for _ in range(T)]
+    for c in range(1, T):
+        kids[int(parents[c])].append(c)
+    return kids
+
+
+def softmax_t(row, tau: float):
+    z = np.asarray(row, dtype=np.float64) / tau
+    z = z - z.max()
+    w = np.exp(z)
+    return w / w.sum()
+
+
+def row_is_usable(row) -> bool:
+    r = np.asarray(row, dtype=np.float64)
+    if np.isnan(r).any() or np.isposinf(r).any():
+        return False
+    return bool(np.isfinite(r).any())
+
+
+def inv_cdf(w, u):
+    """Smallest id v with sum_{v' <= v} w[v'] > u * sum(w), ids ascending.
+
+    Returns (v, near_tie).  If rounding leaves no such v, the last id with
+    positive weight is returned.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    cum = np.cumsum(w)
+    total = cum[-1]
+    thr = u * total
+    if _is_number(thr):
+        v = int(np.searchsorted(cum, thr, side="right"))
+    else:                               # symbolic uniform (exact enumeration tests)
+        v = len(cum)
+        for j in range(len(cum)):
+            if thr < cum[j]:
+                v = j
+                break
+    if v >= len(cum):
+        return int(np.nonzero(w > 0)[0][-1]), False
+    near = False
+    if _is_number(thr):
+        lower = cum[v - 1] if v > 0 else 0.0
+        near = (cum[v] - thr) < NEAR_TIE * total or (thr - lower) < NEAR_TIE * total
+    return v, near
+
+
+def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw):
+    """Sequential multi-round walk of one tree.
+
+    target_rows(n) / draft_rows(n) return node n's logits rows (float64);
+    draw(node, slot) returns the uniform for that decision.
+    Returns (path, final_token, flags, near_ties).
+    """
+    kids = tree_children(parents)
+    flags = 0
+    near = 0
+    path = []
+    cur = 0
+    while True:
+        q = softmax_t(target_rows(cur), tau)
+        if not kids[cur]:
+            final, nt = inv_cdf(q, draw(cur, philox.SAMPLE_SLOT))
+            near += int(nt)
+            return path, final, flags, near
+        p = softmax_t(draft_rows(cur), tau)
+        q_res = q
+        accepted = None
+        for i, c in enumerate(kids[cur]):
+            r = draw(cur, i)
+            t = int(tokens[c])
+            if p[t] == 0.0:
+                flags |= FLAG_P_ZERO
+                ok = q_res[t] > 0.0
+            else:
+                ratio = q_res[t] / p[t]
+                ok = r < ratio
+                if _is_number(r) and abs(r - ratio) < NEAR_TIE:
+                    near += 1
+            if ok:
+                accepted = c
+                break
+            q_res = np.maximum(0.0, q_res - p)
+            z = q_res.sum()
+            if z == 0.0:
+                flags |= FLAG_DEGENERATE_RESIDUAL
+                q_res = q
+            else:
+                q_res = q_res / z
+        if accepted is None:
+            final, nt = inv_cdf(q_res, draw(cur, philox.SAMPLE_SLOT))
+            near += int(nt)
+            return path, final, flags, near
+        path.append(accepted)
+        cur = accepted
+
+
+def walk_greedy(target_rows, parents, tokens):
+    kids = tree_children(parents)
+    path = []
+    cur = 0
+    while True:
+        a = int(np.argmax(np.asarray(target_rows(cur))))  # first maximum = lowest id
+        nxt = next((c for c in kids[cur] if int(tokens[c]) == a), None)
+        if nxt is None:
+            return path, a, 0, 0
+        path.append(nxt)
+        cur = nxt
+
+
+def validate_sequence(target, draft, parents, tokens, tau) -> int:
+    """Flags that make a sequence unusable (outputs poisoned)."""
+    T, V = target.shape
+    if not (len(parents) == T and int(parents[0]) == -1
+            and all(0 <= int(parents[i]) < i for i in range(1, T))):
+        return FLAG_BAD_TREE
+    flags = 0
+    if any(not (0 <= int(tokens[c]) < V) for c in range(1, T)):
+        flags |= FLAG_BAD_TOKEN
+    kids = tree_children(parents)
+    for n in range(T):
+        if not row_is_usable(target[n]):
+            flags |= FLAG_NONFINITE
+        if tau > 0 and kids[n] and not row_is_usable(draft[n]):
+            flags |= FLAG_NONFINITE
+    return flags
+
+
+def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=None):
+    """Oracle for one verification step over a batch of trees.
+
+    target, draft: [B,T,V] float64 logits (draft may be None when
+    temperature == 0).  draw(b, node, slot) overrides the Philox uniforms.
+    Returns a dict of numpy arrays: accept_len [B], accepted_nodes [B,T],
+    out_tokens [B,T], flags [B], near_ties [B].
+    """
+    target = np.asarray(target, dtype=np.float64)
+    B, T, V = target.shape
+    tau = float(temperature)
+    res = {
+        "accept_len": np.full(B, -1, dtype=np.int32),
+        "accepted_nodes": np.full((B, T), -1, dtype=np.int32),
+        "out_tokens": np.full((B, T), -1, dtype=np.int32),
+        "flags": np.zeros(B, dtype=np.uint32),
+        "near_ties": np.zeros(B, dtype=np.int32),
+    }
+    for b in range(B):
+        drf = None if draft is None else np.asarray(draft[b], dtype=np.float64)
+        bad = validate_sequence(target[b], drf, parents[b], tokens[b], tau)
+        if bad:
+            res["flags"][b] = bad
+            continue
+        if tau == 0.0:
+            path, final, fl, near = walk_greedy(lambda n: target[b, n], parents[b], tokens[b])
+        else:
+            if draw is None:
+                def u(n, s, _b=b):
+                    return philox.uniform(seed, offset, _b, n, s)
+            else:
+                def u(n, s, _b=b):
+                    return draw(_b, n, s)
+            path, final, fl, near = walk_sampled(lambda n: target[b, n], lambda n: drf[n],
+                                                 parents[b], tokens[b], tau, u)
+        res["accept_len"][b] = len(path)
+        res["accepted_nodes"][b, :len(path)] = path
+        res["out_tokens"][b, :len(path)] = [int(tokens[b][c]) for c in path]
+        res["out_tokens"][b, len(path)] = final
+        res["flags"][b] = fl
+        res["near_ties"][b] = near
+    return res

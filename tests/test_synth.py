@@ -1,0 +1,69 @@
+"""The seeded input generator: determinism, shapes, tree recipes, rounding."""
+import numpy as np
+
+import synth
+from synth import inputs as si
+
+
+def test_bf16_rounding_is_round_to_nearest_even():
+    # bf16 keeps 7 explicit mantissa bits: the spacing at 1.0 is 2**-7
+    x = np.array([1.0, 1 + 2 ** -8, 1 + 2 ** -9, 1 + 3 * 2 ** -8, 1 + 2 ** -7 + 2 ** -9, -2.5])
+    want = np.array([1.0, 1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7, -2.5])
+    assert np.array_equal(si.bf16_bits_to_f64(si.to_bf16_bits(x)), want)
+    rng = np.random.default_rng(0)
+    y = rng.standard_normal(10000)
+    yb = si.bf16_bits_to_f64(si.to_bf16_bits(y))
+    assert np.all(np.abs(yb - y) <= np.abs(y) * 2 ** -8)
+
+
+def test_configs_shapes():
+    for i, spec in synth.CONFIGS.items():
+        if i == 3:
+            continue                         # the 128K prefix case is exercised on the GPU machine
+        inp = synth.make_inputs(spec, with_kv=(i in (0, 1)), with_logits=(i in (0, 1)))
+        T = inp.T
+        assert inp.parents.shape == (spec.batch, T)
+        assert inp.parents[0, 0] == -1
+        assert all(0 <= inp.parents[b, j] < j for b in range(spec.batch) for j in range(1, T))
+        assert inp.q.shape == (spec.batch, T, spec.q_heads, spec.head_dim)
+        assert inp.kv_indptr[-1] == sum(spec.prefix_lens) + spec.batch * T
+        if i in (1, 2, 4):
+            assert T == 61
+        if i == 0:
+            assert T == 11 and list(inp.parents[0, :5]) == [-1, 0, 0, 0, 0]
+
+
+def test_c3_tree():
+    p = si.make_tree(("c3",), np.random.default_rng(0))
+    assert list(p) == [-1, 0, 0, 1, 3, 4, 5, 6, 7]
+
+
+def test_deterministic():
+    spec = synth.CONFIGS[0]
+    a = synth.make_inputs(spec)
+    b = synth.make_inputs(spec)
+    for f in ("q", "k", "v", "parents", "tokens", "target", "draft"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+
+
+def test_kv_head_block_matches_full_layout():
+    spec = synth.CONFIGS[0].with_(batch=2, prefix_lens=(33, 70), kv_heads=2, q_heads=4)
+    inp = synth.make_inputs(spec)
+    for b in range(2):
+        for h in range(2):
+            kb, vb = si.kv_head_block(spec, inp.T, b, h)
+            lo, hi = inp.kv_indptr[b], inp.kv_indptr[b + 1]
+            assert np.array_equal(inp.k[lo:hi, h], kb) and np.array_equal(inp.v[lo:hi, h], vb)
+
+
+def test_greedy_tree_tokens_are_topk():
+    spec = synth.CONFIGS[1].with_(temperature=0.0, prefix_lens=(16,), q_heads=2, kv_heads=2,
+                                  vocab=500)
+    inp = synth.make_inputs(spec, with_kv=False)
+    d = inp.draft64()[0]
+    kids = {}
+    for c in range(1, inp.T):
+        kids.setdefault(int(inp.parents[0, c]), []).append(c)
+    for n, cs in kids.items():
+        top = list(np.argsort(-d[n], kind="stable")[:len(cs)])
+        assert [int(inp.tokens[0, c]) for c in cs] == top
