@@ -1,0 +1,265 @@
+"""Benchmark of the EAGLE verification hot path on one MI355X.
+
+One step = one verification of one draft tree for one target layer at the
+LLaMA-3.1-8B / 8K-prefix shape: tree attention (B=1, 32 q heads / 8 KV heads,
+D=128, prefix 8192, 61 tree rows) followed by multi-round speculative
+sampling over a 128256-token vocabulary.  Inputs are seeded synthetic data
+of that shape, resident in HBM before timing starts; eight independent input
+sets (over 256 MiB together) are rotated so that the 256 MiB Infinity Cache
+cannot serve a step from the previous one.
+
+Prints ONE JSON line on stdout; details go to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "verified tree nodes/s per layer (attn+accept) at 8B/8K shape; % of HBM peak"
+CONFIG_INDEX = 2
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--sets", type=int, default=8, help="rotated input sets (Infinity Cache defeat)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def workload_bytes(spec, T, parents):
+    """Algorithmic bytes of one step (see the design notes for the formulas)."""
+    B, Hq, Hkv, D, V = spec.batch, spec.q_heads, spec.kv_heads, spec.head_dim, spec.vocab
+    esz = 2 if spec.dtype == "bf16" else 4
+    lsz = 2 if spec.ldtype == "bf16" else 4
+    L = sum(spec.prefix_lens)
+    prefix_kv = 2 * L * Hkv * D * esz
+    tree_kv = 2 * B * T * Hkv * D * esz
+    q = B * T * Hq * D * esz
+    out = B * T * Hq * D * 4
+    logits = 2 * B * T * V * lsz
+    internal = sum(1 for b in range(B) for n in range(T) if (parents[b] == n).any())
+    logits_read = B * T * V * lsz + internal * V * lsz      # target rows + draft rows with children
+    return {
+        "metric_bytes": prefix_kv + logits,                 # prefix KV + logits read once
+        "attention_bytes": prefix_kv + tree_kv + q + out,   # one tree-attention launch
+        "accept_bytes": logits_read,                        # one acceptance call, leaf draft rows skipped
+        "compulsory_bytes": prefix_kv + tree_kv + q + out + logits_read,
+    }
+
+
+def cpu_baseline(inp, spec, budget_s):
+    """The oracle, untuned, on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import accept as oacc
+    from oracle import attention as oatt
+    from synth import inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    T, Hq, Hkv = inp.T, spec.q_heads, spec.kv_heads
+    g = Hq // Hkv
+    scale = 1.0 / np.sqrt(spec.head_dim)
+    q64 = inp.q64()
+    t0 = time.perf_counter()
+    nodes_done = 0
+    kv = [si.kv_head_block(spec, T, 0, h) for h in range(Hkv)]
+    kv = [(si.as_f64(k, spec.dtype), si.as_f64(v, spec.dtype)) for k, v in kv]
+    setup = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(T):                      # whole nodes: every query head of the node
+        for h in range(Hq):
+            k64, v64 = kv[h // g]
+            oatt.node_head_output(q64[0, i, h], k64, v64, spec.prefix_lens[0], inp.parents[0], i, scale)
+        nodes_done += 1
+        if time.perf_counter() - t0 > budget_s * 0.8:
+            break
+    t_attn_node = (time.perf_counter() - t0) / nodes_done
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oacc.spec_accept(inp.target64(), inp.draft64(), inp.parents, inp.tokens, spec.temperature,
+                         0x5EED0002, reps)
+        reps += 1
+        if time.perf_counter() - t0 > budget_s * 0.2 or reps >= 5:
+            break
+    t_accept = (time.perf_counter() - t0) / reps
+    t_step = t_attn_node * T + t_accept
+    return {
+        "value": (spec.batch * (T - 1)) / t_step,
+        "unit": "nodes/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 oracle on the host: tree attention for {nodes_done} of {T} nodes x {Hq} heads "
+                   f"(extrapolated to all {T}), acceptance walk x{reps}; per-step estimate "
+                   f"{t_step:.3f} s (KV setup {setup:.1f} s excluded)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import eagle_draft_tree_attention_amd as ev
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    spec = synth.config_spec(CONFIG_INDEX)
+    eprint(f"[bench] generating {spec.name} inputs")
+    inp = synth.make_inputs(spec)
+    T = inp.T
+    B, Hq, Hkv, D, V = spec.batch, spec.q_heads, spec.kv_heads, spec.head_dim, spec.vocab
+
+    def to_dev(a, dt=None):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    base = {
+        "q": to_dev(inp.q, spec.dtype), "k": to_dev(inp.k, spec.dtype), "v": to_dev(inp.v, spec.dtype),
+        "tgt": to_dev(inp.target, spec.ldtype), "drf": to_dev(inp.draft, spec.ldtype),
+    }
+    sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(args.sets - 1)]
+    indptr = to_dev(inp.kv_indptr)
+    parents = to_dev(inp.parents)
+    tokens = to_dev(inp.tokens)
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values())
+    eprint(f"[bench] {args.sets} input sets x {set_bytes / 2**20:.1f} MiB resident")
+
+    ver = ev.Verifier(B, Hq, Hkv, D, T, V, kv_dtype=spec.dtype, logits_dtype=spec.ldtype)
+    scale = 1.0 / np.sqrt(D)
+    out = torch.empty((B, T, Hq, D), dtype=torch.float32, device="cuda")
+    aflags = torch.empty((B,), dtype=torch.int32, device="cuda")
+    outs = {k: torch.empty(s, dtype=torch.int32, device="cuda") for k, s in
+            (("accept_len", (B,)), ("accepted_nodes", (B, T)), ("out_tokens", (B, T)), ("flags", (B,)),
+             ("near_ties", (B,)))}
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev_pairs=None):
+        s = sets[i % len(sets)]
+        if ev_pairs is not None:
+            ev_pairs[0][0].record(stream)
+        ver.tree_attention(s["q"], s["k"], s["v"], indptr, inp.prefix_lens, parents, scale, out=out,
+                           flags=aflags, stream=stream)
+        if ev_pairs is not None:
+            ev_pairs[0][1].record(stream)
+            ev_pairs[1][0].record(stream)
+        ver.spec_accept(s["tgt"], s["drf"], parents, tokens, spec.temperature, 0x5EED0002, i, outputs=outs,
+                        stream=stream)
+        if ev_pairs is not None:
+            ev_pairs[1][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: whole steps, back to back
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # timed region 2: same steps with events around each call (per-kernel durations)
+    pairs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2)]
+             for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(args.warmup + i, pairs[i])
+    torch.cuda.synchronize()
+    attn_ms = np.array([p[0][0].elapsed_time(p[0][1]) for p in pairs])
+    acc_ms = np.array([p[1][0].elapsed_time(p[1][1]) for p in pairs])
+
+    if args.copy_probe:
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint("[bench] copy probe: 5 x 256 MiB device-to-device copies")
+
+    nb = workload_bytes(spec, T, inp.parents)
+    nodes = B * (T - 1)
+    step_s = ms_per_step * 1e-3
+    attn_us = float(np.median(attn_ms) * 1e3)
+    acc_us = float(np.median(acc_ms) * 1e3)
+    attn_gbs = nb["attention_bytes"] / (float(attn_ms.mean()) * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": nodes / step_s,
+        "unit": "nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{spec.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} prefix={spec.prefix_lens[0]} "
+                        f"tree_rows={T} (60 draft nodes, depth 6) vocab={V} temperature={spec.temperature}",
+            "global_batch": B,
+            "seq_len": spec.prefix_lens[0],
+            "parallelism": "single GPU",
+            "input_sets_rotated": args.sets,
+        },
+        "hbm_frac_metric_bytes": nb["metric_bytes"] / step_s / (HBM_PEAK_GBS * 1e9),
+        "hbm_frac_compulsory_bytes": nb["compulsory_bytes"] / step_s / (HBM_PEAK_GBS * 1e9),
+        "attention_us_median": attn_us,
+        "attention_us_p10_p90": [float(np.percentile(attn_ms, 10) * 1e3), float(np.percentile(attn_ms, 90) * 1e3)],
+        "accept_us_median": acc_us,
+        "accept_us_p10_p90": [float(np.percentile(acc_ms, 10) * 1e3), float(np.percentile(acc_ms, 90) * 1e3)],
+        "roofline": {
+            "kernel": "tree_attention call (split kernel + LSE merge)",
+            "bound": "hbm",
+            "achieved": attn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": nb["attention_bytes"],
+        },
+    }
+    eprint(f"[bench] step {ms_per_step * 1e3:.1f} us  attention {attn_us:.1f} us  accept {acc_us:.1f} us")
+    if not args.no_cpu_baseline:
+        eprint("[bench] timing the oracle on the host (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(inp, spec, args.cpu_budget)
+    ver.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,76 @@
+"""ctypes mirror of include/eagle_verify.h (structs, constants, prototypes)."""
+import ctypes as C
+
+EAGLE_OK, EAGLE_ERR_ARG, EAGLE_ERR_UNSUPPORTED, EAGLE_ERR_CAPACITY, EAGLE_ERR_HIP, EAGLE_ERR_OOM = range(6)
+EAGLE_F32, EAGLE_BF16 = 0, 1
+
+FLAG_BAD_TREE = 1
+FLAG_BAD_TOKEN = 2
+FLAG_NONFINITE = 4
+FLAG_P_ZERO = 8
+FLAG_DEGENERATE_RESIDUAL = 16
+FLAG_BAD_KV_RANGE = 32
+MAX_TREE_ROWS = 64
+
+STATUS_NAMES = {0: "EAGLE_OK", 1: "EAGLE_ERR_ARG", 2: "EAGLE_ERR_UNSUPPORTED", 3: "EAGLE_ERR_CAPACITY",
+                4: "EAGLE_ERR_HIP", 5: "EAGLE_ERR_OOM"}
+
+EXPORTED_SYMBOLS = (
+    "eagle_verify_create", "eagle_verify_tree_attention", "eagle_verify_spec_accept",
+    "eagle_verify_destroy", "eagle_verify_last_error", "eagle_verify_check_tree_attention",
+    "eagle_verify_check_spec_accept",
+)
+
+
+class VerifyDesc(C.Structure):
+    _fields_ = [("max_batch", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("max_tree_rows", C.c_int32), ("vocab_size", C.c_int32),
+                ("kv_dtype", C.c_int), ("logits_dtype", C.c_int)]
+
+
+class TreeAttentionArgs(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("tree_rows", C.c_int32), ("num_kv_rows", C.c_int64),
+                ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+                ("kv_indptr", C.c_void_p), ("prefix_lens_host", C.POINTER(C.c_int32)),
+                ("parents", C.c_void_p), ("sm_scale", C.c_float), ("out", C.c_void_p),
+                ("flags", C.c_void_p)]
+
+
+class SpecAcceptArgs(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("tree_rows", C.c_int32),
+                ("target_logits", C.c_void_p), ("draft_logits", C.c_void_p),
+                ("parents", C.c_void_p), ("tokens", C.c_void_p), ("temperature", C.c_float),
+                ("seed", C.c_uint64), ("offset", C.c_uint64),
+                ("accept_len", C.c_void_p), ("accepted_nodes", C.c_void_p), ("out_tokens", C.c_void_p),
+                ("flags", C.c_void_p), ("near_ties", C.c_void_p)]
+
+
+class AttentionPlan(C.Structure):
+    _fields_ = [("path", C.c_int32), ("rows_per_kv_head", C.c_int32), ("row_tiles", C.c_int32),
+                ("rows_per_tile", C.c_int32), ("chunk_keys", C.c_int32), ("total_splits", C.c_int32),
+                ("workgroups", C.c_int32), ("merge_workgroups", C.c_int32)]
+
+
+class EagleVerifyError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def bind(lib):
+    H = C.c_void_p
+    lib.eagle_verify_create.argtypes = [C.POINTER(VerifyDesc), C.POINTER(H)]
+    lib.eagle_verify_create.restype = C.c_int
+    lib.eagle_verify_tree_attention.argtypes = [H, C.POINTER(TreeAttentionArgs), C.c_void_p]
+    lib.eagle_verify_tree_attention.restype = C.c_int
+    lib.eagle_verify_spec_accept.argtypes = [H, C.POINTER(SpecAcceptArgs), C.c_void_p]
+    lib.eagle_verify_spec_accept.restype = C.c_int
+    lib.eagle_verify_destroy.argtypes = [H]
+    lib.eagle_verify_destroy.restype = C.c_int
+    lib.eagle_verify_last_error.argtypes = [H]
+    lib.eagle_verify_last_error.restype = C.c_char_p
+    lib.eagle_verify_check_tree_attention.argtypes = [C.POINTER(VerifyDesc), C.POINTER(TreeAttentionArgs),
+                                                      C.POINTER(AttentionPlan)]
+    lib.eagle_verify_check_tree_attention.restype = C.c_int
+    lib.eagle_verify_check_spec_accept.argtypes = [C.POINTER(VerifyDesc), C.POINTER(SpecAcceptArgs)]
+    lib.eagle_verify_check_spec_accept.restype = C.c_int

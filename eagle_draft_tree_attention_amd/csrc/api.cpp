@@ -1,0 +1,262 @@
+// libeagle_verify: the exported C ABI (see include/eagle_verify.h).
+// Handle lifetime, workspace, argument marshalling into kernel argument
+// blocks, and launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "ev_internal.h"
+
+struct eagle_verify {
+  eagle_verify_desc desc;
+  int device = 0;
+  int num_cus = ev::kDefaultCUs;
+  ev::Workspace ws;
+  void* base = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool used = false;
+  char err[512] = {0};
+};
+
+namespace {
+
+thread_local char g_err[512];
+
+void set_err(eagle_verify* h, const char* msg) {
+  char* dst = h ? h->err : g_err;
+  std::snprintf(dst, 512, "%s", msg);
+}
+
+eagle_status hip_fail(eagle_verify* h, const char* what, int code) {
+  char buf[512];
+  std::snprintf(buf, sizeof(buf), "%s failed: %s (%d)", what, hipGetErrorString(static_cast<hipError_t>(code)), code);
+  set_err(h, buf);
+  return EAGLE_ERR_HIP;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** out) {
+  if (!out) {
+    set_err(nullptr, "out is NULL");
+    return EAGLE_ERR_ARG;
+  }
+  *out = nullptr;
+  char msg[512] = {0};
+  eagle_status st = ev::check_desc(desc, msg, sizeof(msg));
+  if (st != EAGLE_OK) {
+    set_err(nullptr, msg);
+    return st;
+  }
+  eagle_verify* h = new (std::nothrow) eagle_verify();
+  if (!h) {
+    set_err(nullptr, "host allocation failed");
+    return EAGLE_ERR_OOM;
+  }
+  h->desc = *desc;
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    hip_fail(nullptr, "hipGetDevice", e);
+    delete h;
+    return EAGLE_ERR_HIP;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess && cus > 0)
+    h->num_cus = cus;
+
+  const int64_t B = desc->max_batch, T = desc->max_tree_rows, NC = ev::vocab_chunks(desc->vocab_size);
+  size_t off = 0;
+  const size_t o_part = off;
+  off = align_up(off + sizeof(float) * static_cast<size_t>(ev::kAttnPartFloats), 256);
+  const size_t o_stats = off;
+  off = align_up(off + sizeof(ev::ChunkStat) * B * T * 2 * NC, 256);
+  const size_t o_nodes = off;
+  off = align_up(off + sizeof(ev::NodeState) * B * T, 256);
+  const size_t o_fpart = off;
+  off = align_up(off + sizeof(double) * B * T * NC, 256);
+  const size_t o_spart = off;
+  off = align_up(off + sizeof(double) * B * NC, 256);
+  const size_t o_cnt = off;
+  const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
+  off = align_up(off + cnt_bytes, 256);
+
+  e = hipMalloc(&h->base, off);
+  if (e != hipSuccess) {
+    hip_fail(nullptr, "hipMalloc(workspace)", e);
+    delete h;
+    return EAGLE_ERR_OOM;
+  }
+  char* p = static_cast<char*>(h->base);
+  h->ws.attn_part = reinterpret_cast<float*>(p + o_part);
+  h->ws.stats = reinterpret_cast<ev::ChunkStat*>(p + o_stats);
+  h->ws.nodes = reinterpret_cast<ev::NodeState*>(p + o_nodes);
+  h->ws.fpart = reinterpret_cast<double*>(p + o_fpart);
+  h->ws.spart = reinterpret_cast<double*>(p + o_spart);
+  h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
+  h->ws.bytes = off;
+  // counters start at zero; every call leaves them at zero again
+  e = hipMemset(h->ws.counters, 0, cnt_bytes);
+  if (e == hipSuccess) e = hipMemset(h->ws.nodes, 0, sizeof(ev::NodeState) * B * T);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    hip_fail(nullptr, "workspace initialisation", e);
+    hipFree(h->base);
+    delete h;
+    return EAGLE_ERR_HIP;
+  }
+  *out = h;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_attention_args* a, void* hip_stream) {
+  if (!h) {
+    set_err(nullptr, "handle is NULL");
+    return EAGLE_ERR_ARG;
+  }
+  ev::AttnPlan plan;
+  eagle_status st = ev::plan_tree_attention(&h->desc, a, h->num_cus, &plan, h->err, sizeof(h->err));
+  if (st != EAGLE_OK) return st;
+  ev::AttnKernelArgs k;
+  std::memset(&k, 0, sizeof(k));
+  k.q = a->q;
+  k.k = a->k;
+  k.v = a->v;
+  k.kv_indptr = a->kv_indptr;
+  k.parents = a->parents;
+  k.out = a->out;
+  k.flags = a->flags;
+  k.opart = h->ws.attn_part;
+  k.mlpart = h->ws.attn_part + plan.workgroups * static_cast<int64_t>(plan.rows_per_tile) * h->desc.head_dim;
+  k.num_kv_rows = a->num_kv_rows;
+  k.B = a->batch;
+  k.T = a->tree_rows;
+  k.Hq = h->desc.num_q_heads;
+  k.Hkv = h->desc.num_kv_heads;
+  k.g = k.Hq / k.Hkv;
+  k.D = h->desc.head_dim;
+  k.R = plan.R;
+  k.row_tiles = plan.row_tiles;
+  k.rows_per_tile = plan.rows_per_tile;
+  k.chunk = plan.chunk;
+  k.total_splits = plan.total_splits;
+  k.nwg = static_cast<int>(plan.workgroups);
+  k.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  for (int b = 0; b < a->batch; ++b) {
+    k.L[b] = a->prefix_lens_host[b];
+    k.split_base[b] = plan.split_base[b];
+  }
+  k.split_base[a->batch] = plan.split_base[a->batch];
+  // the partials of one launch must fit: (O + m,l) per partial row
+  const int64_t need = plan.workgroups * static_cast<int64_t>(plan.rows_per_tile) * (k.D + 2);
+  if (plan.merge_workgroups > 0 && need > ev::kAttnPartFloats) {
+    set_err(h, "split partials exceed the workspace");
+    return EAGLE_ERR_CAPACITY;
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int e = ev::launch_tree_attention(plan, k, h->desc.kv_dtype == EAGLE_BF16, stream);
+  h->last_stream = stream;
+  h->used = true;
+  if (e != 0) return hip_fail(h, "tree attention launch", e);
+  h->err[0] = 0;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_args* a, void* hip_stream) {
+  if (!h) {
+    set_err(nullptr, "handle is NULL");
+    return EAGLE_ERR_ARG;
+  }
+  eagle_status st = ev::check_spec_accept(&h->desc, a, h->err, sizeof(h->err));
+  if (st != EAGLE_OK) return st;
+  ev::AcceptKernelArgs k;
+  std::memset(&k, 0, sizeof(k));
+  const int V = h->desc.vocab_size;
+  const int esize = h->desc.logits_dtype == EAGLE_BF16 ? 2 : 4;
+  k.target = a->target_logits;
+  k.draft = a->draft_logits ? a->draft_logits : a->target_logits;
+  k.parents = a->parents;
+  k.tokens = a->tokens;
+  k.accept_len = a->accept_len;
+  k.accepted_nodes = a->accepted_nodes;
+  k.out_tokens = a->out_tokens;
+  k.flags = a->flags;
+  k.near_ties = a->near_ties;
+  k.stats = h->ws.stats;
+  k.nodes = h->ws.nodes;
+  k.fpart = h->ws.fpart;
+  k.spart = h->ws.spart;
+  const int64_t Bm = h->desc.max_batch, Tm = h->desc.max_tree_rows;
+  k.cnt_stats = h->ws.counters;
+  k.cnt_pass = h->ws.counters + Bm * Tm;
+  k.cnt_final = h->ws.counters + 2 * Bm * Tm;
+  k.B = a->batch;
+  k.T = a->tree_rows;
+  k.V = V;
+  k.NC = ev::vocab_chunks(V);
+  k.vec_ok = ((static_cast<int64_t>(V) * esize) % 16) == 0 ? 1 : 0;
+  k.tau = a->temperature;
+  k.c2 = a->temperature > 0.f ? static_cast<float>(1.4426950408889634 / a->temperature) : 0.f;
+  k.inv_tau = a->temperature > 0.f ? 1.0 / static_cast<double>(a->temperature) : 0.0;
+  k.seed_lo = static_cast<uint32_t>(a->seed);
+  k.seed_hi = static_cast<uint32_t>(a->seed >> 32);
+  k.off_lo = static_cast<uint32_t>(a->offset);
+  k.off_hi = static_cast<uint32_t>(a->offset >> 32);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
+  h->last_stream = stream;
+  h->used = true;
+  if (e != 0) return hip_fail(h, "spec accept launch", e);
+  h->err[0] = 0;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify_destroy(eagle_verify* h) {
+  if (!h) return EAGLE_OK;
+  eagle_status st = EAGLE_OK;
+  if (h->used) {
+    hipError_t e = hipStreamSynchronize(h->last_stream);
+    if (e != hipSuccess) st = hip_fail(nullptr, "hipStreamSynchronize", e);
+  }
+  if (h->base) {
+    hipError_t e = hipFree(h->base);
+    if (e != hipSuccess && st == EAGLE_OK) st = hip_fail(nullptr, "hipFree", e);
+  }
+  delete h;
+  return st;
+}
+
+const char* eagle_verify_last_error(const eagle_verify* h) { return h ? h->err : g_err; }
+
+eagle_status eagle_verify_check_tree_attention(const eagle_verify_desc* desc, const eagle_tree_attention_args* a,
+                                               eagle_attention_plan* plan) {
+  ev::AttnPlan p;
+  eagle_status st = ev::plan_tree_attention(desc, a, ev::kDefaultCUs, &p, g_err, sizeof(g_err));
+  if (st != EAGLE_OK) return st;
+  if (plan) {
+    plan->path = p.path;
+    plan->rows_per_kv_head = p.R;
+    plan->row_tiles = p.row_tiles;
+    plan->rows_per_tile = p.rows_per_tile;
+    plan->chunk_keys = p.chunk;
+    plan->total_splits = p.total_splits;
+    plan->workgroups = static_cast<int32_t>(p.workgroups);
+    plan->merge_workgroups = static_cast<int32_t>(p.merge_workgroups);
+  }
+  g_err[0] = 0;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* desc, const eagle_spec_accept_args* a) {
+  eagle_status st = ev::check_spec_accept(desc, a, g_err, sizeof(g_err));
+  if (st == EAGLE_OK) g_err[0] = 0;
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,522 @@
+// Tree-masked attention for EAGLE verification, gfx950 (MI355X).
+//
+// Every draft-tree node i of sequence b attends to the whole prefix KV cache
+// of b plus the tree rows of the nodes on its root path, itself included
+// (EAGLE notes page: core mechanism §3/§5 and the "tree attention" term;
+// lesson page: the glossary entry for tree attention, a standard flash
+// attention call whose mask follows the tree topology).  Query head h reads
+// KV head h / g (GQA, g = Hq / Hkv).
+//
+// Work decomposition (split-KV, flash-decoding style):
+//   * the R = T * g query rows that share one KV head are processed together,
+//     so each K/V tile is read from HBM once and shared by every tree node
+//     and every query head of the group;
+//   * the prefix of each sequence is cut into splits of `chunk` keys; the last
+//     split of a sequence also takes the T tree keys, masked with a per-node
+//     64-bit ancestor bitmask built in LDS from the parent array;
+//   * each split produces (O, m, l) per row; splits of one sequence are merged
+//     by log-sum-exp (the streaming-softmax fusion the Didi page uses to merge
+//     ring-attention partials), or written directly when a sequence has one.
+//
+// Two kernels do the split work:
+//   tree_attn_mfma  bf16, R >= 16: 256 threads = 4 waves, each wave owns
+//       16*MB rows; 64-key K and V tiles are staged in LDS (V transposed) and
+//       shared by the four waves.  S^T = K Q^T and O^T = V^T P^T run on
+//       v_mfma_f32_16x16x32_bf16, laid out so that lane (l % 16) owns one query
+//       row in both products: softmax statistics and the O rescale stay
+//       lane-local and P goes from the S accumulators straight into the B
+//       operand of the PV product, with no LDS round trip.
+//   tree_attn_fma   fp32 inputs (or bf16 with R < 16): one wave per query row,
+//       scalar FMA dot products.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ev_internal.h"
+
+namespace ev {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kNegInf = -__builtin_inff();
+
+// Workgroups are handed to the 8 XCDs round-robin; renumber them so that
+// consecutive logical ids (the row tiles of one KV chunk) share an XCD and
+// therefore its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+  const int q = nwg >> 3, r = nwg & 7;
+  const int xcd = bid & 7, idx = bid >> 3;
+  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+__device__ __forceinline__ int find_seq(const AttnKernelArgs& a, int split) {
+  int b = 0;
+  while (b + 1 < a.B && a.split_base[b + 1] <= split) ++b;
+  return b;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Validate sequence b (parent array + KV range) using one wave's lanes; all
+// lanes return the same flag word.
+__device__ __forceinline__ uint32_t validate_seq(const AttnKernelArgs& a, int b, int lane, int32_t* par_out) {
+  const int T = a.T;
+  int p = 0;
+  bool ok = true;
+  if (lane < T) {
+    p = a.parents[b * T + lane];
+    ok = (lane == 0) ? (p == -1) : (p >= 0 && p < lane);
+  }
+  if (par_out && lane < 64) par_out[lane] = p;
+  uint32_t bad = __any(!ok) ? EAGLE_FLAG_BAD_TREE : 0u;
+  const int64_t kv0 = a.kv_indptr[b], kv1 = a.kv_indptr[b + 1];
+  if (!(kv0 >= 0 && kv1 <= a.num_kv_rows && kv1 - kv0 >= (int64_t)a.L[b] + T)) bad |= EAGLE_FLAG_BAD_KV_RANGE;
+  return bad;
+}
+
+__device__ __forceinline__ uint64_t ancestors_of(const int32_t* par, int node) {
+  uint64_t m = 0;
+  for (int n = node; n >= 0; n = par[n]) m |= 1ull << n;
+  return m;
+}
+
+// ------------------------------------------------------------- MFMA kernel
+// key (within a 64-key tile) that MFMA row m of 16-key block kb stands for;
+// chosen so that the S^T accumulator lane group lg holds 8 consecutive keys
+// 32*(kb/2) + 8*lg + 0..7 across the two blocks of one 32-key PV step.
+__device__ __forceinline__ int tile_key(int kb, int m) {
+  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
+}
+
+template <int D, int MB>
+__global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
+  constexpr int KSTEPS = D / 32;          // QK^T contraction steps
+  constexpr int DBLK = D / 16;            // output column blocks
+  constexpr int KSTRIDE = D + 8;          // bf16 per K row in LDS (16 B pad)
+  constexpr int VSTRIDE = kTileKeys + 8;  // bf16 per V^T row in LDS
+  constexpr int DCH = D / 8;              // 16-byte chunks per K/V row
+  constexpr int KLOADS = kTileKeys * DCH / 256;
+  constexpr int VUNITS = (kTileKeys / 4) * DCH;   // 4-key x 8-d transpose units
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kTileKeys * KSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VSTRIDE];
+  __shared__ uint64_t anc_lds[kMaxTree];
+  __shared__ int32_t par_lds[kMaxTree];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, ln = lane & 15;
+  const int logical = xcd_remap(blockIdx.x, a.nwg);
+  const int rt = logical % a.row_tiles;
+  const int hk = (logical / a.row_tiles) % a.Hkv;
+  const int split = logical / (a.row_tiles * a.Hkv);
+  const int b = find_seq(a, split);
+  const int s_local = split - a.split_base[b];
+  const int S = a.split_base[b + 1] - a.split_base[b];
+  const int L = a.L[b];
+  const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
+
+  // per-lane rows: row_base + 16*rb + ln
+  const int row_base = rt * a.rows_per_tile + wave * 16 * MB;
+
+  uint32_t bad = validate_seq(a, b, lane, wave == 0 ? par_lds : nullptr);
+  if (s_local == 0 && hk == 0 && rt == 0 && tid == 0) a.flags[b] = bad;
+  if (bad) {
+    if (S == 1) {
+      for (int rb = 0; rb < MB; ++rb) {
+        const int r = row_base + 16 * rb + ln;
+        if (r >= R) continue;
+        float* o = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D;
+        for (int db = 0; db < DBLK; ++db)
+          *reinterpret_cast<f32x4_t*>(o + 16 * db + 4 * lg) = f32x4_t{__builtin_nanf(""), __builtin_nanf(""),
+                                                                       __builtin_nanf(""), __builtin_nanf("")};
+      }
+    }
+    return;
+  }
+  __syncthreads();
+  if (tid < T) anc_lds[tid] = ancestors_of(par_lds, tid);
+  __syncthreads();
+
+  const int64_t kv0 = a.kv_indptr[b];
+  const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a.v);
+  const int Hkv = a.Hkv;
+
+  // query rows -> B operands (Q^T), zero for padding rows
+  bool row_ok[MB];
+  int node[MB], head[MB];
+  uint64_t anc_row[MB];
+  bf16x8_t qf[MB][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const int r = row_base + 16 * rb + ln;
+    row_ok[rb] = r < R;
+    node[rb] = row_ok[rb] ? r / g : 0;
+    head[rb] = hk * g + (row_ok[rb] ? r % g : 0);
+    anc_row[rb] = anc_lds[node[rb]];
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(b * T + node[rb]) * Hq + head[rb]) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      u32x4_t w = row_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * s) : u32x4_t{0, 0, 0, 0};
+      qf[rb][s] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+
+  f32x4_t o[MB][DBLK];
+  float m_run[MB], l_run[MB];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) o[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int k_begin = s_local * a.chunk;
+  const int k_end = min(k_begin + a.chunk, L);
+  const int n_prefix_tiles = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
+  const bool last = (s_local == S - 1);
+  const int n_tiles = n_prefix_tiles + (last ? 1 : 0);
+  const float c = a.scale_log2;
+
+  u32x4_t kreg[KLOADS], vreg[4];
+  auto tile_start = [&](int t) { return t < n_prefix_tiles ? k_begin + t * kTileKeys : L; };
+  auto tile_count = [&](int t) { return t < n_prefix_tiles ? min(kTileKeys, k_end - (k_begin + t * kTileKeys)) : T; };
+
+  auto load_tile = [&](int t) {
+    const int64_t row0 = kv0 + tile_start(t);
+    const int cnt = tile_count(t);
+#pragma unroll
+    for (int e = 0; e < KLOADS; ++e) {
+      const int cidx = tid + 256 * e;
+      const int key = cidx / DCH, dc = cidx % DCH;
+      kreg[e] = (key < cnt) ? *reinterpret_cast<const u32x4_t*>(kbase + ((row0 + key) * Hkv + hk) * D + dc * 8)
+                            : u32x4_t{0, 0, 0, 0};
+    }
+    if (tid < VUNITS) {
+      const int kg = tid / DCH, dc = tid % DCH;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 4 * kg + e;
+        vreg[e] = (key < cnt) ? *reinterpret_cast<const u32x4_t*>(vbase + ((row0 + key) * Hkv + hk) * D + dc * 8)
+                              : u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int e = 0; e < KLOADS; ++e) {
+      const int cidx = tid + 256 * e;
+      const int key = cidx / DCH, dc = cidx % DCH;
+      *reinterpret_cast<u32x4_t*>(k_lds + key * KSTRIDE + dc * 8) = kreg[e];
+    }
+    if (tid < VUNITS) {
+      const int kg = tid / DCH, dc = tid % DCH;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const int sh = 16 * (dd & 1);
+        const uint32_t x0 = (vreg[0][dd >> 1] >> sh) & 0xFFFFu, x1 = (vreg[1][dd >> 1] >> sh) & 0xFFFFu;
+        const uint32_t x2 = (vreg[2][dd >> 1] >> sh) & 0xFFFFu, x3 = (vreg[3][dd >> 1] >> sh) & 0xFFFFu;
+        *reinterpret_cast<u32x2_t*>(vt_lds + (dc * 8 + dd) * VSTRIDE + 4 * kg) = u32x2_t{x0 | (x1 << 16), x2 | (x3 << 16)};
+      }
+    }
+  };
+
+  if (n_tiles > 0) load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    const bool is_tree = (t >= n_prefix_tiles);
+    const int cnt = tile_count(t);
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    // S^T[key][row] = K Q^T for four 16-key blocks
+    f32x4_t sacc[4][MB];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) sacc[kb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kp = k_lds + tile_key(kb, ln) * KSTRIDE + 8 * lg;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + 32 * s);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rb][s], sacc[kb][rb], 0, 0, 0);
+      }
+    }
+
+    // online softmax per row (lane-local, rows shared across the 4 lane groups)
+    bf16x8_t pb[MB][2];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      float x[4][4];
+      float tmax = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = tile_key(kb, 4 * lg + i);
+          const bool valid = is_tree ? (key < T && ((anc_row[rb] >> key) & 1ull)) : (key < cnt);
+          x[kb][i] = valid ? sacc[kb][rb][i] : kNegInf;
+          tmax = fmaxf(tmax, x[kb][i]);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run[rb], tmax * c);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2f(m_run[rb] - m_use);
+      float psum = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[kb][i] = exp2f(__builtin_fmaf(x[kb][i], c, -m_use));
+          psum += p[kb][i];
+        }
+      }
+      l_run[rb] = l_run[rb] * alpha + psum;
+      m_run[rb] = m_new;
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pb[rb][ks] = bf16x8_t{(__bf16)p[2 * ks][0], (__bf16)p[2 * ks][1], (__bf16)p[2 * ks][2], (__bf16)p[2 * ks][3],
+                              (__bf16)p[2 * ks + 1][0], (__bf16)p[2 * ks + 1][1], (__bf16)p[2 * ks + 1][2],
+                              (__bf16)p[2 * ks + 1][3]};
+      }
+    }
+
+    // O^T[d][row] += V^T P^T
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+      const uint16_t* vp = vt_lds + (16 * db + ln) * VSTRIDE + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vp + 32 * ks);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb][ks], o[rb][db], 0, 0, 0);
+      }
+    }
+  }
+
+  // epilogue
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    float l_tot = l_run[rb];
+    l_tot += __shfl_xor(l_tot, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const int r = row_base + 16 * rb + ln;
+    if (!row_ok[rb]) continue;
+    if (S == 1) {
+      const float inv = 1.f / l_tot;
+      float* op = a.out + ((int64_t)(b * T + node[rb]) * Hq + head[rb]) * D + 4 * lg;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) *reinterpret_cast<f32x4_t*>(op + 16 * db) = o[rb][db] * inv;
+    } else {
+      const int64_t prow = (int64_t)logical * a.rows_per_tile + (r - rt * a.rows_per_tile);
+      float* op = a.opart + prow * D + 4 * lg;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) *reinterpret_cast<f32x4_t*>(op + 16 * db) = o[rb][db];
+      if (lg == 0) {
+        a.mlpart[2 * prow] = m_run[rb];
+        a.mlpart[2 * prow + 1] = l_tot;
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------- FMA kernel
+template <typename TIn>
+__device__ __forceinline__ float load_elem(const TIn* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+
+template <typename TIn, int D>
+__global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
+  constexpr int DPL = D / 64;   // output columns per lane
+  __shared__ float q_lds[D];
+  __shared__ float p_lds[kTileKeys];
+  __shared__ int32_t par_lds[kMaxTree];
+
+  const int lane = threadIdx.x;
+  const int logical = blockIdx.x;
+  const int R = a.R;
+  const int r = logical % R;
+  const int hk = (logical / R) % a.Hkv;
+  const int split = logical / (R * a.Hkv);
+  const int b = find_seq(a, split);
+  const int s_local = split - a.split_base[b];
+  const int S = a.split_base[b + 1] - a.split_base[b];
+  const int L = a.L[b];
+  const int T = a.T, g = a.g, Hq = a.Hq, Hkv = a.Hkv;
+  const int nodei = r / g, head = hk * g + r % g;
+
+  const uint32_t bad = validate_seq(a, b, lane, par_lds);
+  if (s_local == 0 && hk == 0 && r == 0 && lane == 0) a.flags[b] = bad;
+  if (bad) {
+    if (S == 1) {
+      float* o = a.out + ((int64_t)(b * T + nodei) * Hq + head) * D;
+      for (int e = 0; e < DPL; ++e) o[lane + 64 * e] = __builtin_nanf("");
+    }
+    return;
+  }
+  __syncthreads();
+  const uint64_t anc = ancestors_of(par_lds, nodei);
+  const TIn* qp = reinterpret_cast<const TIn*>(a.q) + ((int64_t)(b * T + nodei) * Hq + head) * D;
+  for (int e = 0; e < DPL; ++e) q_lds[lane + 64 * e] = load_elem<TIn>(qp, lane + 64 * e);
+  __syncthreads();
+
+  const TIn* kb = reinterpret_cast<const TIn*>(a.k);
+  const TIn* vb = reinterpret_cast<const TIn*>(a.v);
+  const int64_t kv0 = a.kv_indptr[b];
+  const int k_begin = s_local * a.chunk;
+  const int k_end = min(k_begin + a.chunk, L);
+  const int n_prefix_tiles = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
+  const int n_tiles = n_prefix_tiles + ((s_local == S - 1) ? 1 : 0);
+  const float c = a.scale_log2;
+
+  float acc[DPL];
+  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+  for (int t = 0; t < n_tiles; ++t) {
+    const bool is_tree = t >= n_prefix_tiles;
+    const int start = is_tree ? L : k_begin + t * kTileKeys;
+    const int cnt = is_tree ? T : min(kTileKeys, k_end - start);
+    const int64_t row0 = kv0 + start;
+    float s = kNegInf;
+    const bool valid = lane < cnt && (!is_tree || ((anc >> lane) & 1ull));
+    if (valid) {
+      const TIn* kr = kb + ((row0 + lane) * Hkv + hk) * D;
+      float dot = 0.f;
+      for (int d = 0; d < D; ++d) dot = __builtin_fmaf(q_lds[d], load_elem<TIn>(kr, d), dot);
+      s = dot;
+    }
+    float tmax = s;
+    for (int o = 32; o > 0; o >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, o));
+    const float m_new = fmaxf(m_run, tmax * c);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    const float p = exp2f(__builtin_fmaf(s, c, -m_use));
+    float psum = p;
+    for (int o = 32; o > 0; o >>= 1) psum += __shfl_xor(psum, o);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    __syncthreads();
+    p_lds[lane] = p;
+    __syncthreads();
+    for (int e = 0; e < DPL; ++e) {
+      float sum = 0.f;
+      for (int k = 0; k < cnt; ++k) sum = __builtin_fmaf(p_lds[k], load_elem<TIn>(vb, ((row0 + k) * Hkv + hk) * D + lane + 64 * e), sum);
+      acc[e] = acc[e] * alpha + sum;
+    }
+  }
+  if (S == 1) {
+    float* o = a.out + ((int64_t)(b * T + nodei) * Hq + head) * D;
+    const float inv = 1.f / l_run;
+    for (int e = 0; e < DPL; ++e) o[lane + 64 * e] = acc[e] * inv;
+  } else {
+    const int64_t prow = (int64_t)logical;   // one row per slot
+    for (int e = 0; e < DPL; ++e) a.opart[prow * D + lane + 64 * e] = acc[e];
+    if (lane == 0) {
+      a.mlpart[2 * prow] = m_run;
+      a.mlpart[2 * prow + 1] = l_run;
+    }
+  }
+}
+
+// ------------------------------------------------------------ LSE merge
+template <int D>
+__global__ __launch_bounds__(256) void tree_attn_merge(const AttnKernelArgs a) {
+  const int logical = blockIdx.x;   // (b, hk, rt)
+  const int rt = logical % a.row_tiles;
+  const int hk = (logical / a.row_tiles) % a.Hkv;
+  const int b = logical / (a.row_tiles * a.Hkv);
+  const int base = a.split_base[b];
+  const int S = a.split_base[b + 1] - base;
+  if (S <= 1) return;
+  const int tid = threadIdx.x;
+  const int T = a.T, g = a.g, R = a.R, Hq = a.Hq, rpt = a.rows_per_tile;
+  __shared__ uint32_t bad_lds;
+  if (tid < 64) {
+    const uint32_t bad = validate_seq(a, b, tid, nullptr);
+    if (tid == 0) bad_lds = bad;
+  }
+  __syncthreads();
+  const uint32_t bad = bad_lds;
+  const int r0 = rt * rpt;
+  const int nrows = min(rpt, R - r0);
+  for (int idx = tid; idx < nrows * (D / 4); idx += 256) {
+    const int rl = idx / (D / 4), d4 = idx % (D / 4);
+    const int r = r0 + rl;
+    float* op = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * d4;
+    if (bad) {
+      *reinterpret_cast<f32x4_t*>(op) = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                __builtin_nanf("")};
+      continue;
+    }
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s) {
+      const int64_t prow = ((int64_t)((base + s) * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
+      M = fmaxf(M, a.mlpart[2 * prow]);
+    }
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const int64_t prow = ((int64_t)((base + s) * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
+      const float w = exp2f(a.mlpart[2 * prow] - Mu);
+      num += w * *reinterpret_cast<const f32x4_t*>(a.opart + prow * D + 4 * d4);
+      den += w * a.mlpart[2 * prow + 1];
+    }
+    *reinterpret_cast<f32x4_t*>(op) = num * (1.f / den);
+  }
+}
+
+template <int D>
+hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hipStream_t st) {
+  if (p.path == 1) {
+    const dim3 grid((unsigned)p.workgroups), block(256);
+    switch (p.mb) {
+      case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 1>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 2>), grid, block, 0, st, a); break;
+      case 3: hipLaunchKernelGGL((tree_attn_mfma<D, 3>), grid, block, 0, st, a); break;
+      case 4: hipLaunchKernelGGL((tree_attn_mfma<D, 4>), grid, block, 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    const dim3 grid((unsigned)p.workgroups), block(64);
+    if (kv_bf16)
+      hipLaunchKernelGGL((tree_attn_fma<uint16_t, D>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((tree_attn_fma<float, D>), grid, block, 0, st, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.merge_workgroups > 0) {
+    hipLaunchKernelGGL((tree_attn_merge<D>), dim3((unsigned)p.merge_workgroups), dim3(256), 0, st, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int kv_bf16, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (args.D == 128) ? launch_d<128>(plan, args, kv_bf16, st) : launch_d<64>(plan, args, kv_bf16, st);
+  return static_cast<int>(e);
+}
+
+}  // namespace ev

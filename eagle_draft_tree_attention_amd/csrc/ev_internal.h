@@ -1,0 +1,127 @@
+// Internal definitions shared by the host library and the HIP kernels of
+// libeagle_verify: launch plans, kernel argument blocks and the workspace
+// layout.  Nothing here is part of the public C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/eagle_verify.h"
+
+namespace ev {
+
+constexpr int kMaxBatch = 256;       // per-sequence plan travels in the kernel arguments
+constexpr int kMaxTree = EAGLE_MAX_TREE_ROWS;
+constexpr int kTileKeys = 64;        // keys per attention tile (one LDS stage)
+constexpr int kVocabChunk = 8192;    // vocabulary elements per acceptance workgroup
+constexpr int kDefaultCUs = 256;     // MI355X compute units (planning without a device)
+constexpr int64_t kAttnPartFloats = 32ll << 20;   // 128 MiB of split partials
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+  int path;            // 0 = FMA kernel (fp32, or bf16 with R < 16), 1 = MFMA kernel
+  int R;               // rows per KV head = T * g
+  int mb;              // MFMA: 16-row blocks per wave (rows per workgroup = 64 * mb)
+  int row_tiles;       // workgroups along R (FMA path: one row each)
+  int rows_per_tile;
+  int chunk;           // prefix keys per split (multiple of kTileKeys)
+  int total_splits;
+  int64_t workgroups;
+  int64_t merge_workgroups;
+  int64_t part_floats; // workspace floats used by split partials
+  int32_t splits[kMaxBatch];
+  int32_t split_base[kMaxBatch + 1];
+};
+
+struct AttnKernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int64_t* kv_indptr;
+  const int32_t* parents;
+  float* out;
+  uint32_t* flags;
+  float* opart;        // [slot][rows_per_tile][D]
+  float* mlpart;       // [slot][rows_per_tile][2]  (m in log2 units, l)
+  int64_t num_kv_rows;
+  int B, T, Hq, Hkv, g, D, R;
+  int row_tiles, rows_per_tile, chunk, total_splits;
+  int nwg;
+  float scale_log2;    // sm_scale * log2(e)
+  int32_t L[kMaxBatch];
+  int32_t split_base[kMaxBatch + 1];
+};
+
+// ---------------------------------------------------------------- acceptance
+struct ChunkStat {     // one (sequence, node, row, vocab chunk)
+  float m;             // chunk max of the raw logits (-inf if all -inf)
+  uint32_t bad;        // 1 = NaN or +inf seen
+  int32_t argmax;      // lowest id holding the chunk max (greedy mode)
+  int32_t pad;
+  double z;            // sum exp((x - m) / tau) over the chunk
+};
+
+enum NodeKind : int32_t { kNodeLeaf = 0, kNodeAccepted = 1, kNodeRejected = 2, kNodeNeedsPass = 3 };
+
+struct NodeState {     // one (sequence, node)
+  double zq, zp;       // softmax normalisers of target / draft rows
+  double C, s;         // residual = max(0, q - C p) / s after the tested children
+  float mq, mp;        // row maxima of target / draft logits
+  int32_t kind;        // NodeKind
+  int32_t outcome;     // accepted child (kNodeAccepted), else -1
+  int32_t next_child;  // kNodeNeedsPass: ordinal of the next child to test
+  int32_t argmax;      // greedy mode: target argmax
+  uint32_t flags;      // NONFINITE for unusable rows, P_ZERO / DEGENERATE events
+  int32_t near;        // near-threshold decisions taken at this node
+};
+
+struct AcceptKernelArgs {
+  const void* target;
+  const void* draft;
+  const int32_t* parents;
+  const int32_t* tokens;
+  int32_t* accept_len;
+  int32_t* accepted_nodes;
+  int32_t* out_tokens;
+  uint32_t* flags;
+  int32_t* near_ties;
+  ChunkStat* stats;    // [B][T][2][NC]
+  NodeState* nodes;    // [B][T]
+  double* fpart;       // [B][T][NC]
+  double* spart;       // [B][NC]
+  uint32_t* cnt_stats; // [B][T]
+  uint32_t* cnt_pass;  // [B][T]
+  uint32_t* cnt_final; // [B]
+  int B, T, V, NC;
+  int vec_ok;          // rows start 16-byte aligned
+  float tau;           // > 0 sampled, == 0 greedy
+  float c2;            // log2(e) / tau
+  double inv_tau;
+  uint32_t seed_lo, seed_hi, off_lo, off_hi;
+};
+
+// ---------------------------------------------------------------- host side
+struct Workspace {
+  float* attn_part = nullptr;   // kAttnPartFloats
+  ChunkStat* stats = nullptr;
+  NodeState* nodes = nullptr;
+  double* fpart = nullptr;
+  double* spart = nullptr;
+  uint32_t* counters = nullptr; // cnt_stats | cnt_pass | cnt_final
+  size_t bytes = 0;
+};
+
+// plan.cpp (pure C++, no HIP)
+eagle_status check_desc(const eagle_verify_desc* d, char* err, size_t errlen);
+eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_attention_args* a,
+                                 int num_cus, AttnPlan* plan, char* err, size_t errlen);
+eagle_status check_spec_accept(const eagle_verify_desc* d, const eagle_spec_accept_args* a,
+                               char* err, size_t errlen);
+int vocab_chunks(int V);
+
+// attention.hip / accept.hip
+int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int kv_bf16,
+                          void* stream);
+int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stream);
+
+}  // namespace ev

@@ -1,0 +1,181 @@
+// Host-side argument validation and launch planning for libeagle_verify.
+// Pure C++: no HIP call is made here, so everything in this file runs (and is
+// tested) without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "ev_internal.h"
+
+namespace ev {
+namespace {
+
+eagle_status fail(eagle_status st, char* err, size_t errlen, const char* fmt, ...) {
+  if (err && errlen) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(err, errlen, fmt, ap);
+    va_end(ap);
+  }
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  int v = std::atoi(s);
+  return v > 0 ? v : dflt;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int vocab_chunks(int V) { return static_cast<int>(ceil_div(V, kVocabChunk)); }
+
+eagle_status check_desc(const eagle_verify_desc* d, char* err, size_t errlen) {
+  if (!d) return fail(EAGLE_ERR_ARG, err, errlen, "descriptor is NULL");
+  if (d->max_batch < 1 || d->max_batch > kMaxBatch)
+    return fail(EAGLE_ERR_ARG, err, errlen, "max_batch=%d outside [1, %d]", d->max_batch, kMaxBatch);
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads != 0)
+    return fail(EAGLE_ERR_ARG, err, errlen, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d",
+                d->num_q_heads, d->num_kv_heads);
+  if (d->num_q_heads > 4096)
+    return fail(EAGLE_ERR_ARG, err, errlen, "num_q_heads=%d above 4096", d->num_q_heads);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(EAGLE_ERR_UNSUPPORTED, err, errlen, "head_dim=%d (supported: 64, 128)", d->head_dim);
+  if (d->max_tree_rows < 1 || d->max_tree_rows > kMaxTree)
+    return fail(EAGLE_ERR_ARG, err, errlen, "max_tree_rows=%d outside [1, %d]", d->max_tree_rows, kMaxTree);
+  if (d->vocab_size < 2 || d->vocab_size > (1 << 30))
+    return fail(EAGLE_ERR_ARG, err, errlen, "vocab_size=%d outside [2, 2^30]", d->vocab_size);
+  if ((d->kv_dtype != EAGLE_F32 && d->kv_dtype != EAGLE_BF16) ||
+      (d->logits_dtype != EAGLE_F32 && d->logits_dtype != EAGLE_BF16))
+    return fail(EAGLE_ERR_ARG, err, errlen, "unknown dtype");
+  return EAGLE_OK;
+}
+
+eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_attention_args* a,
+                                 int num_cus, AttnPlan* plan, char* err, size_t errlen) {
+  eagle_status st = check_desc(d, err, errlen);
+  if (st != EAGLE_OK) return st;
+  if (!a) return fail(EAGLE_ERR_ARG, err, errlen, "args is NULL");
+  if (!plan) return fail(EAGLE_ERR_ARG, err, errlen, "plan is NULL");
+  if (a->batch < 1) return fail(EAGLE_ERR_ARG, err, errlen, "batch=%d < 1", a->batch);
+  if (a->batch > d->max_batch)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "batch=%d above max_batch=%d", a->batch, d->max_batch);
+  if (a->tree_rows < 1) return fail(EAGLE_ERR_ARG, err, errlen, "tree_rows=%d < 1", a->tree_rows);
+  if (a->tree_rows > d->max_tree_rows)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "tree_rows=%d above max_tree_rows=%d", a->tree_rows,
+                d->max_tree_rows);
+  if (a->num_kv_rows < 0) return fail(EAGLE_ERR_ARG, err, errlen, "num_kv_rows < 0");
+  if (!a->q || !a->k || !a->v || !a->kv_indptr || !a->prefix_lens_host || !a->parents || !a->out ||
+      !a->flags)
+    return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->out, 16))
+    return fail(EAGLE_ERR_ARG, err, errlen, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(a->kv_indptr, 8) || !aligned(a->parents, 4) || !aligned(a->flags, 4))
+    return fail(EAGLE_ERR_ARG, err, errlen, "kv_indptr/parents/flags misaligned");
+  if (!std::isfinite(a->sm_scale) || a->sm_scale <= 0.f)
+    return fail(EAGLE_ERR_ARG, err, errlen, "sm_scale must be finite and > 0");
+
+  const int B = a->batch, T = a->tree_rows;
+  const int Hkv = d->num_kv_heads, g = d->num_q_heads / d->num_kv_heads, D = d->head_dim;
+  int64_t total_keys = 0;
+  for (int b = 0; b < B; ++b) {
+    const int32_t L = a->prefix_lens_host[b];
+    if (L < 0) return fail(EAGLE_ERR_ARG, err, errlen, "prefix_lens_host[%d]=%d < 0", b, L);
+    if (static_cast<int64_t>(L) + T > a->num_kv_rows)
+      return fail(EAGLE_ERR_CAPACITY, err, errlen, "sequence %d needs %lld KV rows, only %lld allocated",
+                  b, static_cast<long long>(L) + T, static_cast<long long>(a->num_kv_rows));
+    total_keys += L;
+  }
+
+  std::memset(plan, 0, sizeof(*plan));
+  const int R = T * g;
+  plan->R = R;
+  plan->path = (d->kv_dtype == EAGLE_BF16 && R >= 16) ? 1 : 0;
+  int target_wgs;
+  int min_chunk;
+  if (plan->path == 1) {
+    int rt = static_cast<int>(ceil_div(R, 256));
+    int rows = static_cast<int>(ceil_div(ceil_div(R, rt), 64) * 64);
+    plan->row_tiles = rt;
+    plan->rows_per_tile = rows;
+    plan->mb = rows / 64;
+    target_wgs = num_cus * env_int("EAGLE_VERIFY_ATTN_WG_PER_CU", 2);
+    min_chunk = 2 * kTileKeys;
+  } else {
+    plan->row_tiles = R;
+    plan->rows_per_tile = 1;
+    plan->mb = 0;
+    target_wgs = num_cus * env_int("EAGLE_VERIFY_FMA_WG_PER_CU", 8);
+    min_chunk = kTileKeys;
+  }
+  const int64_t units = static_cast<int64_t>(Hkv) * plan->row_tiles;
+  int64_t chunk = ceil_div(total_keys * units, target_wgs);
+  chunk = ceil_div(chunk, kTileKeys) * kTileKeys;
+  if (chunk < min_chunk) chunk = min_chunk;
+  if (const char* f = std::getenv("EAGLE_VERIFY_ATTN_CHUNK")) {   // tuning override
+    int v = std::atoi(f);
+    if (v >= kTileKeys) chunk = ceil_div(v, kTileKeys) * kTileKeys;
+  }
+  for (;;) {
+    int64_t splits = 0, part = 0;
+    bool any_multi = false;
+    for (int b = 0; b < B; ++b) {
+      const int64_t L = a->prefix_lens_host[b];
+      const int64_t S = L > 0 ? ceil_div(L, chunk) : 1;
+      plan->splits[b] = static_cast<int32_t>(S);
+      plan->split_base[b] = static_cast<int32_t>(splits);
+      splits += S;
+      if (S > 1) any_multi = true;
+    }
+    plan->split_base[B] = static_cast<int32_t>(splits);
+    // partial slots are indexed by workgroup, so all of them are reserved
+    if (any_multi) part = splits * units * plan->rows_per_tile * (D + 2);
+    if (part <= kAttnPartFloats && splits < (1ll << 30)) {
+      plan->total_splits = static_cast<int>(splits);
+      plan->part_floats = part;
+      plan->chunk = static_cast<int>(chunk);
+      plan->workgroups = splits * units;
+      plan->merge_workgroups = any_multi ? static_cast<int64_t>(B) * units : 0;
+      break;
+    }
+    chunk *= 2;
+  }
+  return EAGLE_OK;
+}
+
+eagle_status check_spec_accept(const eagle_verify_desc* d, const eagle_spec_accept_args* a,
+                               char* err, size_t errlen) {
+  eagle_status st = check_desc(d, err, errlen);
+  if (st != EAGLE_OK) return st;
+  if (!a) return fail(EAGLE_ERR_ARG, err, errlen, "args is NULL");
+  if (a->batch < 1) return fail(EAGLE_ERR_ARG, err, errlen, "batch=%d < 1", a->batch);
+  if (a->batch > d->max_batch)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "batch=%d above max_batch=%d", a->batch, d->max_batch);
+  if (a->tree_rows < 1) return fail(EAGLE_ERR_ARG, err, errlen, "tree_rows=%d < 1", a->tree_rows);
+  if (a->tree_rows > d->max_tree_rows)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "tree_rows=%d above max_tree_rows=%d", a->tree_rows,
+                d->max_tree_rows);
+  if (!std::isfinite(a->temperature) || a->temperature < 0.f)
+    return fail(EAGLE_ERR_ARG, err, errlen, "temperature must be finite and >= 0");
+  if (!a->target_logits || !a->parents || !a->tokens || !a->accept_len || !a->accepted_nodes ||
+      !a->out_tokens || !a->flags || !a->near_ties)
+    return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");
+  if (a->temperature > 0.f && !a->draft_logits)
+    return fail(EAGLE_ERR_ARG, err, errlen, "draft_logits is NULL with temperature > 0");
+  if (!aligned(a->target_logits, 16) || (a->draft_logits && !aligned(a->draft_logits, 16)))
+    return fail(EAGLE_ERR_ARG, err, errlen, "logits must be 16-byte aligned");
+  if (!aligned(a->parents, 4) || !aligned(a->tokens, 4) || !aligned(a->accept_len, 4) ||
+      !aligned(a->accepted_nodes, 4) || !aligned(a->out_tokens, 4) || !aligned(a->flags, 4) ||
+      !aligned(a->near_ties, 4))
+    return fail(EAGLE_ERR_ARG, err, errlen, "integer buffers must be 4-byte aligned");
+  return EAGLE_OK;
+}
+
+}  // namespace ev

@@ -1,0 +1,156 @@
+"""Argument marshalling for the libeagle_verify entry points.
+
+The functions named like the C entry points take plain integers (device
+addresses, host arrays, a stream handle) and return the C status, raising
+EagleVerifyError on failure.  `Verifier` wraps a handle and accepts torch
+tensors that already live on the GPU; it allocates the output tensors when
+none are given.  No computation happens here.
+"""
+import ctypes as C
+
+import numpy as np
+
+from . import _abi
+from ._abi import (EAGLE_BF16, EAGLE_F32, EagleVerifyError, SpecAcceptArgs, TreeAttentionArgs,
+                   VerifyDesc, AttentionPlan)
+
+
+def _lib():
+    from . import _lib as lib
+    return lib
+
+
+def _check(status, handle=None):
+    if status != _abi.EAGLE_OK:
+        msg = _lib().eagle_verify_last_error(handle)
+        raise EagleVerifyError(status, (msg or b"").decode(errors="replace"))
+    return status
+
+
+def make_desc(max_batch, num_q_heads, num_kv_heads, head_dim, max_tree_rows, vocab_size,
+              kv_dtype="bf16", logits_dtype="bf16") -> VerifyDesc:
+    dt = {"bf16": EAGLE_BF16, "f32": EAGLE_F32}
+    return VerifyDesc(int(max_batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                      int(max_tree_rows), int(vocab_size), dt[kv_dtype], dt[logits_dtype])
+
+
+# ---------------------------------------------------------------- C names
+def eagle_verify_create(desc: VerifyDesc) -> int:
+    h = C.c_void_p()
+    _check(_lib().eagle_verify_create(C.byref(desc), C.byref(h)))
+    return h.value
+
+
+def eagle_verify_destroy(handle: int) -> None:
+    _check(_lib().eagle_verify_destroy(handle))
+
+
+def eagle_verify_last_error(handle=None) -> str:
+    return (_lib().eagle_verify_last_error(handle) or b"").decode(errors="replace")
+
+
+def eagle_verify_tree_attention(handle: int, args: TreeAttentionArgs, stream: int) -> int:
+    return _check(_lib().eagle_verify_tree_attention(handle, C.byref(args), C.c_void_p(stream)), handle)
+
+
+def eagle_verify_spec_accept(handle: int, args: SpecAcceptArgs, stream: int) -> int:
+    return _check(_lib().eagle_verify_spec_accept(handle, C.byref(args), C.c_void_p(stream)), handle)
+
+
+def eagle_verify_check_tree_attention(desc: VerifyDesc, args: TreeAttentionArgs):
+    """(status, AttentionPlan) without touching the device."""
+    plan = AttentionPlan()
+    st = _lib().eagle_verify_check_tree_attention(C.byref(desc), C.byref(args), C.byref(plan))
+    return st, plan
+
+
+def eagle_verify_check_spec_accept(desc: VerifyDesc, args: SpecAcceptArgs) -> int:
+    return _lib().eagle_verify_check_spec_accept(C.byref(desc), C.byref(args))
+
+
+# ---------------------------------------------------------------- torch layer
+def _ptr(t):
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out, flags):
+    lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32))
+    a = TreeAttentionArgs()
+    a.batch, a.tree_rows = int(q.shape[0]), int(q.shape[1])
+    a.num_kv_rows = int(k.shape[0])
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.kv_indptr = _ptr(kv_indptr)
+    a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))
+    a.parents = _ptr(parents)
+    a.sm_scale = float(sm_scale)
+    a.out, a.flags = _ptr(out), _ptr(flags)
+    return a, lens          # keep lens alive while the call runs
+
+
+class Verifier:
+    """One handle (one stream at a time).  Tensors must be CUDA/HIP tensors."""
+
+    def __init__(self, max_batch, num_q_heads, num_kv_heads, head_dim, max_tree_rows, vocab_size,
+                 kv_dtype="bf16", logits_dtype="bf16"):
+        self.desc = make_desc(max_batch, num_q_heads, num_kv_heads, head_dim, max_tree_rows, vocab_size,
+                              kv_dtype, logits_dtype)
+        self.handle = eagle_verify_create(self.desc)
+
+    def close(self):
+        if self.handle:
+            eagle_verify_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def tree_attention(self, q, k, v, kv_indptr, prefix_lens, parents, sm_scale=None, out=None,
+                       flags=None, stream=None):
+        import torch
+        B, T, Hq, D = q.shape
+        if sm_scale is None:
+            sm_scale = 1.0 / float(D) ** 0.5
+        if out is None:
+            out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+        if flags is None:
+            flags = torch.empty((B,), dtype=torch.int32, device=q.device)
+        a, _keep = tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out, flags)
+        eagle_verify_tree_attention(self.handle, a, _stream(stream))
+        return out, flags
+
+    def spec_accept(self, target, draft, parents, tokens, temperature, seed, offset, outputs=None,
+                    stream=None):
+        import torch
+        B, T, V = target.shape
+        dev = target.device
+        if outputs is None:
+            outputs = {
+                "accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+                "accepted_nodes": torch.empty((B, T), dtype=torch.int32, device=dev),
+                "out_tokens": torch.empty((B, T), dtype=torch.int32, device=dev),
+                "flags": torch.empty((B,), dtype=torch.int32, device=dev),
+                "near_ties": torch.empty((B,), dtype=torch.int32, device=dev),
+            }
+        a = SpecAcceptArgs()
+        a.batch, a.tree_rows = int(B), int(T)
+        a.target_logits, a.draft_logits = _ptr(target), _ptr(draft)
+        a.parents, a.tokens = _ptr(parents), _ptr(tokens)
+        a.temperature = float(temperature)
+        a.seed, a.offset = int(seed), int(offset)
+        a.accept_len = _ptr(outputs["accept_len"])
+        a.accepted_nodes = _ptr(outputs["accepted_nodes"])
+        a.out_tokens = _ptr(outputs["out_tokens"])
+        a.flags = _ptr(outputs["flags"])
+        a.near_ties = _ptr(outputs["near_ties"])
+        eagle_verify_spec_accept(self.handle, a, _stream(stream))
+        return outputs

@@ -1,0 +1,213 @@
+/*
+ * eagle_verify.h — C ABI of the EAGLE draft-tree verification step, one
+ * target layer at a time, for AMD Instinct MI355X (gfx950).
+ *
+ * The verification step of EAGLE speculative decoding (EAGLE notes page,
+ * core mechanism §5 and the GPU data-path steps ⑥–⑦; speculative-decoding
+ * lesson page, "Concept" and build steps 1–3) has two parts, each one call:
+ *
+ *   eagle_verify_tree_attention  every draft-tree node attends to the whole
+ *       prefix KV cache plus only its own ancestors and itself (the "tree
+ *       attention" term on the EAGLE notes page; the lesson page's glossary
+ *       calls it attention under a non-causal mask that follows the tree).
+ *   eagle_verify_spec_accept     multi-round speculative sampling over the
+ *       vocabulary: softmax of target (q) and draft (p) logits, a walk of the
+ *       tree from the root in which the children of a node are tried in
+ *       ascending index, a child with token t is accepted if r < q(t)/p(t),
+ *       otherwise q <- norm(max(0, q - p)) and the next child is tried; if
+ *       every child is rejected the token is sampled from that residual, and
+ *       at a node without children a bonus token is sampled from q.
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor pointer is DEVICE memory owned by the caller, 16-byte
+ *    aligned, row-major with the innermost dimension last, and must stay
+ *    alive until the work enqueued on `hip_stream` has completed.  Pointers
+ *    named *_host are host memory read synchronously during the call.
+ *  - Calls enqueue asynchronously on `hip_stream` (a hipStream_t, NULL = the
+ *    null stream) and return; nothing is allocated per call and there is no
+ *    device-wide synchronisation.  The library owns only its workspace,
+ *    allocated by eagle_verify_create and freed by eagle_verify_destroy.
+ *  - Argument errors are detected before any launch and returned as an
+ *    eagle_status; eagle_verify_last_error() then describes the problem.
+ *    Problems in device-resident contents (a parent array that is not a tree
+ *    in topological order, a token outside the vocabulary, a logits row that
+ *    holds NaN or +inf or is entirely -inf, a KV range that does not fit)
+ *    set bits in the per-sequence `flags` output; that sequence's outputs
+ *    are poisoned (NaN floats, -1 integers).  Kernels never trap.
+ *  - A handle is not thread-safe and keeps per-call scratch state: use one
+ *    handle per stream and do not run two calls of one handle concurrently.
+ *  - Same inputs and the same (seed, offset) give bit-identical outputs.
+ *  - No exception crosses this ABI.
+ */
+#ifndef EAGLE_VERIFY_H_
+#define EAGLE_VERIFY_H_
+
+#include <stdint.h>
+
+#ifndef EAGLE_API
+#define EAGLE_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct eagle_verify eagle_verify; /* opaque handle */
+
+typedef enum {
+  EAGLE_OK = 0,
+  EAGLE_ERR_ARG = 1,         /* null/misaligned pointer, value out of range       */
+  EAGLE_ERR_UNSUPPORTED = 2, /* shape/dtype combination this build does not run    */
+  EAGLE_ERR_CAPACITY = 3,    /* above the maxima given to eagle_verify_create      */
+  EAGLE_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed         */
+  EAGLE_ERR_OOM = 5          /* workspace allocation failed                        */
+} eagle_status;
+
+typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
+
+/* Per-sequence `flags` bits.  Bits 0-2 and 5 poison the sequence's outputs;
+ * bits 3-4 report events on the accepted walk (outputs stay valid). */
+#define EAGLE_FLAG_BAD_TREE 1u          /* parents[b,0] != -1 or !(0 <= parents[b,i] < i) */
+#define EAGLE_FLAG_BAD_TOKEN 2u         /* tokens[b,i] outside [0, V) for some i >= 1     */
+#define EAGLE_FLAG_NONFINITE 4u         /* a target row, or a draft row of a node with
+                                           children, holds NaN/+inf or is all -inf      */
+#define EAGLE_FLAG_P_ZERO 8u            /* a tested child had draft probability 0: it was
+                                           accepted iff its residual target mass > 0     */
+#define EAGLE_FLAG_DEGENERATE_RESIDUAL 16u /* residual mass was 0: fell back to q        */
+#define EAGLE_FLAG_BAD_KV_RANGE 32u     /* kv_indptr[b..b+1] does not hold L_b + T rows
+                                           inside [0, num_kv_rows)                       */
+
+#define EAGLE_MAX_TREE_ROWS 64 /* T = root + up to 63 draft nodes */
+
+/* Create-time maxima; the workspace is sized from them. */
+typedef struct {
+  int32_t max_batch;      /* B <= max_batch, 1..256                                */
+  int32_t num_q_heads;    /* Hq                                                    */
+  int32_t num_kv_heads;   /* Hkv, Hq % Hkv == 0                                    */
+  int32_t head_dim;       /* D in {64, 128}                                        */
+  int32_t max_tree_rows;  /* T = N + 1 <= 64                                       */
+  int32_t vocab_size;     /* V >= 2                                                */
+  eagle_dtype kv_dtype;     /* dtype of q, k and v                                 */
+  eagle_dtype logits_dtype; /* dtype of target and draft logits                    */
+} eagle_verify_desc;
+
+/* Tree attention (one layer).
+ *   q         [B, T, Hq, D]             queries of the tree nodes (kv_dtype)
+ *   k, v      [num_kv_rows, Hkv, D]     keys/values (kv_dtype); sequence b uses
+ *             rows kv_indptr[b] .. kv_indptr[b] + L_b + T - 1: its L_b prefix
+ *             rows followed by the T tree-node rows in node order (the tree's
+ *             own K/V, appended by the verification forward before the cache
+ *             is truncated to the accepted path)
+ *   kv_indptr [B+1] int64 (device)      first KV row of each sequence
+ *   prefix_lens_host [B] int32 (host)   L_b >= 0, used to plan the launch
+ *   parents   [B, T] int32 (device)     parents[b,0] = -1, 0 <= parents[b,i] < i
+ *   sm_scale  softmax scale (1/sqrt(D) by convention)
+ *   out       [B, T, Hq, D] float32     O[b,i,h] = sum_j softmax_j(scale q.k_j) v_j over
+ *             prefix rows and the tree rows of the nodes on the root path of i
+ *             (i included); query head h reads KV head h / (Hq/Hkv)
+ *   flags     [B] uint32 (device)       EAGLE_FLAG_BAD_TREE | EAGLE_FLAG_BAD_KV_RANGE
+ * Inputs are not modified.  Keys/values are read once from HBM per launch. */
+typedef struct {
+  int32_t batch;           /* B <= max_batch            */
+  int32_t tree_rows;       /* T <= max_tree_rows, >= 1  */
+  int64_t num_kv_rows;     /* rows allocated in k and v */
+  const void* q;
+  const void* k;
+  const void* v;
+  const int64_t* kv_indptr;
+  const int32_t* prefix_lens_host;
+  const int32_t* parents;
+  float sm_scale;
+  float* out;
+  uint32_t* flags;
+} eagle_tree_attention_args;
+
+/* Multi-round speculative sampling over the vocabulary.
+ *   target_logits [B, T, V]  row n: the target's next-token logits after node n
+ *   draft_logits  [B, T, V]  row n: the draft logits that proposed n's children
+ *                            (rows of nodes without children are never read;
+ *                            not read at all when temperature == 0)
+ *   parents [B, T] int32, tokens [B, T] int32 (tokens[b,0] = the already
+ *            committed root token, unused)
+ *   temperature  > 0: q = softmax(target/t), p = softmax(draft/t);
+ *                == 0: greedy — accept the first child whose token is the
+ *                target argmax (lowest id on ties), else emit that argmax.
+ *   seed, offset Philox4x32-10 key / per-step counter word: the uniform for the
+ *                test of the i-th child (0-based) of node n in sequence b uses
+ *                counter (i, n | b << 8, offset_lo, offset_hi), key (seed_lo,
+ *                seed_hi), and u = (x0 >> 8) * 2^-24; the terminal sample of
+ *                node n uses slot i = 0xffffffff.  Samples are inverse-CDF over
+ *                ascending token ids.
+ * Outputs (device):
+ *   accept_len [B]        number of accepted draft nodes (-1 if poisoned)
+ *   accepted_nodes [B, T] accepted node indices along the root path, -1 padded
+ *   out_tokens [B, T]     tokens of the accepted nodes, then one final token
+ *                         (residual sample or bonus), -1 padded
+ *   flags [B]             EAGLE_FLAG_* bits
+ *   near_ties [B]         decisions on the walk within 1e-6 of their threshold
+ *                         (|r - q_res(t)/p(t)| or |running sum - u*total|/total) */
+typedef struct {
+  int32_t batch;
+  int32_t tree_rows;
+  const void* target_logits;
+  const void* draft_logits;
+  const int32_t* parents;
+  const int32_t* tokens;
+  float temperature;
+  uint64_t seed;
+  uint64_t offset;
+  int32_t* accept_len;
+  int32_t* accepted_nodes;
+  int32_t* out_tokens;
+  uint32_t* flags;
+  int32_t* near_ties;
+} eagle_spec_accept_args;
+
+/* Launch plan of one tree-attention call (what eagle_verify_tree_attention
+ * will launch for these arguments). */
+typedef struct {
+  int32_t path;            /* 0 = fp32/FMA kernel, 1 = bf16 MFMA kernel          */
+  int32_t rows_per_kv_head;/* R = T * Hq / Hkv                                   */
+  int32_t row_tiles;       /* workgroups along R per (sequence, split, KV head)  */
+  int32_t rows_per_tile;   /* rows one workgroup covers                          */
+  int32_t chunk_keys;      /* prefix keys per split                              */
+  int32_t total_splits;    /* sum over sequences of the split counts             */
+  int32_t workgroups;      /* attention workgroups launched                      */
+  int32_t merge_workgroups;/* LSE-merge workgroups launched (0 = none)           */
+} eagle_attention_plan;
+
+/* Allocate a handle and its workspace on the current HIP device.
+ * Errors: EAGLE_ERR_ARG (bad descriptor), EAGLE_ERR_HIP, EAGLE_ERR_OOM.
+ * On error *out is set to NULL. */
+EAGLE_API eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** out);
+
+/* Tree-masked attention, see eagle_tree_attention_args. */
+EAGLE_API eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_attention_args* a,
+                                         void* hip_stream);
+
+/* Multi-round speculative sampling, see eagle_spec_accept_args. */
+EAGLE_API eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_args* a,
+                                      void* hip_stream);
+
+/* Synchronise the last stream the handle used, free the workspace and the
+ * handle.  NULL is accepted. */
+EAGLE_API eagle_status eagle_verify_destroy(eagle_verify* h);
+
+/* Text of the last error on this handle ("" if none); a thread-local
+ * message is returned for h == NULL (e.g. after a failed create). */
+EAGLE_API const char* eagle_verify_last_error(const eagle_verify* h);
+
+/* Validate arguments exactly as the calls above do and report the launch
+ * plan, without touching the device (no HIP call is made).  `desc` is the
+ * descriptor the handle was (or would be) created with. */
+EAGLE_API eagle_status eagle_verify_check_tree_attention(const eagle_verify_desc* desc,
+                                               const eagle_tree_attention_args* a,
+                                               eagle_attention_plan* plan);
+EAGLE_API eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* desc,
+                                            const eagle_spec_accept_args* a);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EAGLE_VERIFY_H_ */

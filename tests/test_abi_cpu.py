@@ -1,0 +1,126 @@
+"""The C-ABI library on the CPU: it loads, exports what include/eagle_verify.h
+declares, and validates/plans without touching the device."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ev = pytest.importorskip("eagle_draft_tree_attention_amd")
+
+
+def test_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "eagle_verify.h")).read()
+    declared = set(re.findall(r"EAGLE_API\s+[\w\s\*]+?\b(eagle_verify_\w+)\s*\(", header))
+    assert declared == set(ev.EXPORTED_SYMBOLS)
+    lib = ev.library()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _desc(**kw):
+    d = dict(max_batch=4, num_q_heads=32, num_kv_heads=8, head_dim=128, max_tree_rows=61, vocab_size=128256,
+             kv_dtype="bf16", logits_dtype="bf16")
+    d.update(kw)
+    return ev.make_desc(**d)
+
+
+def _attn_args(B=1, T=61, lens=(8192,), rows=None, **over):
+    a = ev.TreeAttentionArgs()
+    a.batch, a.tree_rows = B, T
+    lens = np.asarray(lens, dtype=np.int32)
+    a.num_kv_rows = int(rows if rows is not None else lens.sum() + B * T)
+    fake = 1 << 20   # aligned non-null addresses: never dereferenced by the check
+    a.q = a.k = a.v = a.out = fake
+    a.kv_indptr = fake
+    a.parents = a.flags = fake
+    a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))
+    a.sm_scale = 1.0 / np.sqrt(128.0)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a, lens
+
+
+def test_plan_for_the_workload_shapes():
+    # 8B/8K: R = 61*4 = 244 rows per KV head -> one 256-row MFMA tile
+    a, keep = _attn_args()
+    st, plan = ev.eagle_verify_check_tree_attention(_desc(), a)
+    assert st == ev.EAGLE_OK
+    assert plan.path == 1 and plan.rows_per_kv_head == 244
+    assert plan.row_tiles == 1 and plan.rows_per_tile == 256
+    assert plan.chunk_keys % 64 == 0 and plan.total_splits == -(-8192 // plan.chunk_keys)
+    assert plan.workgroups == plan.total_splits * 8
+    assert plan.merge_workgroups == (8 if plan.total_splits > 1 else 0)
+    # 70B batch of four: R = 488 -> two 256-row tiles per KV head
+    a, keep = _attn_args(B=4, lens=(1024, 2048, 3072, 4096))
+    st, plan = ev.eagle_verify_check_tree_attention(_desc(num_q_heads=64), a)
+    assert st == ev.EAGLE_OK and plan.row_tiles == 2 and plan.rows_per_tile == 256
+    # tiny fp32 goes to the FMA path, one row per workgroup
+    a, keep = _attn_args(T=11, lens=(128,))
+    st, plan = ev.eagle_verify_check_tree_attention(
+        _desc(num_q_heads=4, num_kv_heads=4, head_dim=64, kv_dtype="f32", logits_dtype="f32"), a)
+    assert st == ev.EAGLE_OK and plan.path == 0 and plan.row_tiles == 11
+    # bf16 with fewer than 16 rows per KV head also takes the FMA path
+    a, keep = _attn_args(T=3, lens=(300,))
+    st, plan = ev.eagle_verify_check_tree_attention(_desc(num_q_heads=8, num_kv_heads=8), a)
+    assert st == ev.EAGLE_OK and plan.path == 0
+
+
+def test_attention_argument_errors():
+    d = _desc()
+    a, keep = _attn_args(T=65)
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_CAPACITY
+    a, keep = _attn_args(B=5, lens=(1,) * 5)
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_CAPACITY
+    a, keep = _attn_args(B=0, lens=())
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_ARG
+    a, keep = _attn_args(q=None)
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_ARG
+    a, keep = _attn_args(k=(1 << 20) + 8)
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_ARG
+    a, keep = _attn_args(sm_scale=float("nan"))
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_ARG
+    a, keep = _attn_args(lens=(-1,))
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_ARG
+    a, keep = _attn_args(rows=100)
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_CAPACITY
+    assert "KV rows" in ev.eagle_verify_last_error()
+    assert ev.eagle_verify_check_tree_attention(_desc(head_dim=96), _attn_args()[0])[0] == \
+        ev.EAGLE_ERR_UNSUPPORTED
+    assert ev.eagle_verify_check_tree_attention(_desc(num_kv_heads=7), _attn_args()[0])[0] == ev.EAGLE_ERR_ARG
+
+
+def _sa_args(**over):
+    a = ev.SpecAcceptArgs()
+    a.batch, a.tree_rows = 1, 61
+    fake = 1 << 20
+    a.target_logits = a.draft_logits = fake
+    a.parents = a.tokens = a.accept_len = a.accepted_nodes = a.out_tokens = a.flags = a.near_ties = fake
+    a.temperature, a.seed, a.offset = 1.0, 1, 0
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_spec_accept_argument_errors():
+    d = _desc()
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args()) == ev.EAGLE_OK
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(temperature=-1.0)) == ev.EAGLE_ERR_ARG
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(temperature=float("nan"))) == ev.EAGLE_ERR_ARG
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(draft_logits=None)) == ev.EAGLE_ERR_ARG
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(draft_logits=None, temperature=0.0)) == ev.EAGLE_OK
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(tree_rows=62)) == ev.EAGLE_ERR_CAPACITY
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(batch=9)) == ev.EAGLE_ERR_CAPACITY
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(target_logits=(1 << 20) + 4)) == ev.EAGLE_ERR_ARG
+    assert ev.eagle_verify_check_spec_accept(d, _sa_args(near_ties=None)) == ev.EAGLE_ERR_ARG
+
+
+def test_descriptor_errors():
+    for kw in (dict(max_batch=0), dict(max_batch=257), dict(max_tree_rows=65), dict(vocab_size=1),
+               dict(num_q_heads=0)):
+        assert ev.eagle_verify_check_spec_accept(_desc(**kw), _sa_args()) == ev.EAGLE_ERR_ARG, kw
+    with pytest.raises(ev.EagleVerifyError) as e:
+        ev.eagle_verify_create(_desc(max_batch=0))
+    assert e.value.status == ev.EAGLE_ERR_ARG

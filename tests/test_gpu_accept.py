@@ -1,0 +1,199 @@
+"""GPU parity of multi-round speculative sampling (through the C ABI) against
+the scalar fp64 oracle on the same Philox stream.
+
+Integers (accept_len, accepted_nodes, out_tokens) must match bit for bit; a
+sequence may only differ if a decision on its walk came within 1e-6 of its
+threshold (counted as a near tie by one side).  Flags must match.  Besides
+parity: losslessness statistics over Philox offsets (chi-square vs the target
+distribution; chain closed form), determinism, and the edge cases.
+"""
+import numpy as np
+import pytest
+from scipy.special import softmax as sp_softmax
+from scipy.stats import chi2 as chi2_dist
+
+import synth
+from gpu_util import compare_accept, log, make_verifier, run_accept, small_spec
+from oracle import accept as oacc
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x5EED0000
+
+CASES = [
+    small_spec("bf16_t1", B=8, V=1000, levels=(4, 6, 10)),
+    small_spec("bf16_t07_unaligned_rows", B=4, V=5003, levels=(10, 10, 10), temperature=0.7),
+    small_spec("f32_multi_chunk", dtype="f32", B=3, V=20000, levels=(4, 4, 4, 4)),
+    small_spec("bf16_low_alpha_many_rounds", B=8, V=20000, sigma_d=2.5, levels=(10, 10)),
+    small_spec("bf16_greedy", B=8, V=3000, temperature=0.0, levels=(4, 6, 10)),
+    small_spec("bf16_chain", B=6, V=4096, tree=("chain", 9)),
+    small_spec("bf16_star", B=6, V=2000, tree=("star", 12), sigma_d=1.5),
+]
+
+
+def _oracle(inp, temperature, offset, **over):
+    tgt = over.get("target")
+    drf = over.get("draft")
+    from synth.inputs import as_f64
+    t64 = inp.target64() if tgt is None else as_f64(tgt, inp.spec.ldtype)
+    d64 = inp.draft64() if drf is None else as_f64(drf, inp.spec.ldtype)
+    par = over.get("parents", inp.parents)
+    tok = over.get("tokens", inp.tokens)
+    return oacc.spec_accept(t64, None if temperature == 0 else d64, par, tok, temperature, SEED, offset)
+
+
+@pytest.mark.parametrize("spec", CASES, ids=lambda s: s.name)
+def test_accept_matches_oracle(spec):
+    log(f"[accept] {spec.name}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    ver = make_verifier(spec, inp.T)
+    diverged = 0
+    for off in range(12):
+        got = run_accept(ver, inp, spec.temperature, SEED, off)
+        ref = _oracle(inp, spec.temperature, off)
+        diverged += compare_accept(got, ref, f"{spec.name} offset {off}")
+    log(f"    near-tie divergences: {diverged}")
+    again = run_accept(ver, inp, spec.temperature, SEED, 11)
+    for key in again:
+        assert np.array_equal(again[key], got[key]), "not bitwise deterministic"
+    ver.close()
+
+
+@pytest.mark.parametrize("cfg,temp", [(0, 1.0), (1, 1.0), (1, 0.0), (2, 1.0), (3, 1.0), (4, 1.0)])
+def test_accept_full_configs(cfg, temp):
+    spec = synth.config_spec(cfg, temperature=temp)
+    log(f"[accept] full size {spec.name} temperature {temp}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    ver = make_verifier(spec, inp.T)
+    for off in range(3):
+        got = run_accept(ver, inp, temp, SEED + cfg, off)
+        ref = oacc.spec_accept(inp.target64(), None if temp == 0 else inp.draft64(), inp.parents, inp.tokens,
+                               temp, SEED + cfg, off)
+        compare_accept(got, ref, f"{spec.name} offset {off}")
+        log(f"    offset {off}: accept_len {got['accept_len'].tolist()} near ties {got['near_ties'].tolist()}")
+    ver.close()
+
+
+def _custom(B, T, V, dtype="f32"):
+    return small_spec("custom", dtype=dtype, B=B, V=V, tree=("chain", T - 1))
+
+
+def test_edge_cases_flags_and_poison():
+    import eagle_draft_tree_attention_amd as ev
+    log("[accept] edge cases")
+    B, T, V = 6, 4, 64
+    rng = np.random.default_rng(0)
+    spec = _custom(B, T, V)
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
+    tgt = (rng.standard_normal((B, T, V)) * 2).astype(np.float32)
+    drf = (tgt + rng.standard_normal((B, T, V)) * 0.5).astype(np.float32)
+    par = np.tile(np.array([-1, 0, 0, 1], dtype=np.int32), (B, 1))
+    tok = np.tile(np.array([0, 5, 9, 3], dtype=np.int32), (B, 1))
+    par[1, 3] = 3                                   # bad tree
+    tok[2, 2] = V                                   # bad token
+    tgt[3, 1, 7] = np.nan                           # unusable target row
+    tgt[4, 2, :] = -np.inf                          # all -inf target row
+    drf[5, 3, :] = np.nan                           # draft row of a leaf: never read
+    ver = make_verifier(spec.with_(batch=B), T)
+    got = run_accept(ver, inp, 1.0, SEED, 0, target=tgt, draft=drf, parents=par, tokens=tok)
+    ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
+    assert got["flags"].tolist() == ref["flags"].tolist() == [0, ev.FLAG_BAD_TREE, ev.FLAG_BAD_TOKEN,
+                                                             ev.FLAG_NONFINITE, ev.FLAG_NONFINITE, 0]
+    compare_accept(got, ref, "edge")
+    for b in (1, 2, 3, 4):
+        assert got["accept_len"][b] == -1 and (got["out_tokens"][b] == -1).all()
+    ver.close()
+
+
+def test_p_zero_and_degenerate_residual():
+    import eagle_draft_tree_attention_amd as ev
+    log("[accept] p = 0 and zero residual")
+    spec = _custom(2, 3, 3)
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1, 1)), with_kv=False)
+    row = np.log(np.array([0.5, 0.5, 1.0])).astype(np.float32)
+    row[2] = -np.inf
+    tgt = np.stack([np.stack([row] * 3)] * 2)
+    drf = tgt.copy()
+    par = np.array([[-1, 0, 0], [-1, 0, 0]], dtype=np.int32)
+    tok = np.array([[0, 2, 1], [0, 2, 2]], dtype=np.int32)
+    ver = make_verifier(spec.with_(batch=2), 3)
+    got = run_accept(ver, inp, 1.0, SEED, 0, target=tgt, draft=drf, parents=par, tokens=tok)
+    ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
+    compare_accept(got, ref, "p0")
+    assert got["flags"][0] & ev.FLAG_P_ZERO and got["flags"][0] & ev.FLAG_DEGENERATE_RESIDUAL
+    assert got["accept_len"][0] == 1 and got["accepted_nodes"][0, 0] == 2
+    # sequence 1: both children rejected (q = 0 at their token), residual 0 -> sample from q
+    assert got["accept_len"][1] == 0 and got["out_tokens"][1, 0] in (0, 1)
+    assert got["flags"][1] & ev.FLAG_DEGENERATE_RESIDUAL
+    ver.close()
+
+
+def test_root_only_tree_draws_bonus_from_target():
+    log("[accept] T = 1")
+    V, B = 7, 64
+    spec = small_spec("root_only", dtype="f32", B=B, V=V, tree=("chain", 0))
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
+    ver = make_verifier(spec, 1)
+    counts = np.zeros(V)
+    for off in range(40):
+        got = run_accept(ver, inp, 1.0, SEED, off)
+        ref = _oracle(inp, 1.0, off)
+        compare_accept(got, ref, f"root-only {off}")
+        assert (got["accept_len"] == 0).all()
+        for b in range(B):
+            counts[got["out_tokens"][b, 0]] += 1
+    ver.close()
+
+
+def test_lossless_statistics_over_offsets():
+    """Root with three i.i.d. draft children: the first emitted token follows
+    the target distribution (chi-square), and every run equals the oracle."""
+    log("[accept] chi-square over Philox offsets")
+    V, B, K = 6, 256, 40
+    rng = np.random.default_rng(3)
+    t_row = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    d_row = (t_row + rng.standard_normal(V) * 0.9).astype(np.float32)
+    q = sp_softmax(t_row.astype(np.float64))
+    p = sp_softmax(d_row.astype(np.float64))
+    spec = small_spec("stats", dtype="f32", B=B, V=V, tree=("star", 3))
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
+    par = np.tile(np.array([-1, 0, 0, 0], dtype=np.int32), (B, 1))
+    tgt = np.tile(t_row, (B, 4, 1))
+    drf = np.tile(d_row, (B, 4, 1))
+    ver = make_verifier(spec, 4)
+    counts = np.zeros(V)
+    for off in range(K):
+        tok = np.zeros((B, 4), dtype=np.int32)
+        tok[:, 1:] = rng.choice(V, size=(B, 3), p=p)
+        got = run_accept(ver, inp, 1.0, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok)
+        ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, off)
+        compare_accept(got, ref, f"stats offset {off}")
+        counts += np.bincount(got["out_tokens"][:, 0], minlength=V)
+    n = B * K
+    stat = ((counts - n * q) ** 2 / (n * q)).sum()
+    log(f"    chi2 {stat:.2f} (99.9% critical {chi2_dist.ppf(0.999, V - 1):.2f})")
+    assert stat < chi2_dist.ppf(0.999, V - 1)
+    ver.close()
+
+
+def test_chain_closed_form_on_gpu():
+    """E[emitted] = (1 - a^(N+1)) / (1 - a) for a chain with acceptance rate a."""
+    log("[accept] chain closed form")
+    N, B, K, alpha = 5, 256, 16, 0.8
+    spec = small_spec("chain_cf", dtype="f32", B=B, V=2, tree=("chain", N))
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
+    tgt = np.tile(np.log(np.array([0.3, 0.7], dtype=np.float32)), (B, N + 1, 1))
+    drf = np.tile(np.log(np.array([0.5, 0.5], dtype=np.float32)), (B, N + 1, 1))
+    par = np.tile(np.arange(-1, N, dtype=np.int32), (B, 1))
+    rng = np.random.default_rng(9)
+    ver = make_verifier(spec, N + 1)
+    emitted = []
+    for off in range(K):
+        tok = rng.integers(0, 2, size=(B, N + 1)).astype(np.int32)
+        got = run_accept(ver, inp, 1.0, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok)
+        emitted.append(got["accept_len"] + 1)
+    e = np.concatenate(emitted)
+    mean = (1 - alpha ** (N + 1)) / (1 - alpha)
+    log(f"    mean emitted {e.mean():.4f} vs {mean:.4f}")
+    assert abs(e.mean() - mean) < 4.5 * e.std(ddof=1) / np.sqrt(len(e))
+    ver.close()
