@@ -25,6 +25,11 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build the HIP library first "
         "(python eagle_draft_tree_attention_amd/build.py); there is no fallback path")
 
+# torch ships its own HIP runtime (same SONAME as the system one).  Load it
+# first so the library binds to the runtime torch's tensors and streams live
+# in: one process must not carry two HIP runtimes.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 from . import _abi  # noqa: E402

@@ -21,7 +21,8 @@ SOURCES = ["plan.cpp", "api.cpp", "attention.hip", "accept.hip"]
 
 # Packed FP32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function", f"--offload-arch={ARCH}"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wno-unused-function", f"--offload-arch={ARCH}",
+          "-mcode-object-version=5"]
 
 
 def hipcc() -> str:

@@ -25,7 +25,9 @@
 //       v_mfma_f32_16x16x32_bf16, laid out so that lane (l % 16) owns one query
 //       row in both products: softmax statistics and the O rescale stay
 //       lane-local and P goes from the S accumulators straight into the B
-//       operand of the PV product, with no LDS round trip.
+//       operand of the PV product, with no LDS round trip.  P enters the PV
+//       product as a bf16 hi/lo pair (two MFMAs), keeping the output within
+//       a few 1e-6 of fp32 arithmetic.
 //   tree_attn_fma   fp32 inputs (or bf16 with R < 16): one wave per query row,
 //       scalar FMA dot products.
 #include <hip/hip_runtime.h>
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
     }
 
     // online softmax per row (lane-local, rows shared across the 4 lane groups)
-    bf16x8_t pb[MB][2];
+    bf16x8_t pb[MB][2], pl[MB][2];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
       float x[4][4];
@@ -287,11 +289,18 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
       }
+      // P = hi + lo, both bf16: the PV product then carries ~16 significant
+      // bits of each weight instead of 8 (bf16 rounding of P alone leaves
+      // errors of a few 1e-3 relative to the output row).
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        pb[rb][ks] = bf16x8_t{(__bf16)p[2 * ks][0], (__bf16)p[2 * ks][1], (__bf16)p[2 * ks][2], (__bf16)p[2 * ks][3],
-                              (__bf16)p[2 * ks + 1][0], (__bf16)p[2 * ks + 1][1], (__bf16)p[2 * ks + 1][2],
-                              (__bf16)p[2 * ks + 1][3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = p[2 * ks + (e >> 2)][e & 3];
+          const __bf16 hi = (__bf16)pv;
+          pb[rb][ks][e] = hi;
+          pl[rb][ks][e] = (__bf16)(pv - (float)hi);
+        }
       }
     }
 
@@ -303,8 +312,10 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vp + 32 * ks);
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
+        for (int rb = 0; rb < MB; ++rb) {
           o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb][ks], o[rb][db], 0, 0, 0);
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb][ks], o[rb][db], 0, 0, 0);
+        }
       }
     }
   }
@@ -437,9 +448,17 @@ __global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
 }
 
 // ------------------------------------------------------------ LSE merge
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// One workgroup per (sequence, KV head, row tile, 16-row slice): 16 threads
+// per row, each owning D/16 output columns, so the S split partials of a row
+// are read in parallel across the chip.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge(const AttnKernelArgs a) {
-  const int logical = blockIdx.x;   // (b, hk, rt)
+  constexpr int CPT = D / 16;       // columns per thread
+  const int slices = (a.rows_per_tile + 15) / 16;
+  int logical = blockIdx.x;
+  const int slice = logical % slices;
+  logical /= slices;
   const int rt = logical % a.row_tiles;
   const int hk = (logical / a.row_tiles) % a.Hkv;
   const int b = logical / (a.row_tiles * a.Hkv);
@@ -448,40 +467,44 @@ __global__ __launch_bounds__(256) void tree_attn_merge(const AttnKernelArgs a) {
   if (S <= 1) return;
   const int tid = threadIdx.x;
   const int T = a.T, g = a.g, R = a.R, Hq = a.Hq, rpt = a.rows_per_tile;
+  const int rl = slice * 16 + (tid >> 4);           // row within the tile
+  const int r = rt * rpt + rl;
   __shared__ uint32_t bad_lds;
   if (tid < 64) {
     const uint32_t bad = validate_seq(a, b, tid, nullptr);
     if (tid == 0) bad_lds = bad;
   }
   __syncthreads();
-  const uint32_t bad = bad_lds;
-  const int r0 = rt * rpt;
-  const int nrows = min(rpt, R - r0);
-  for (int idx = tid; idx < nrows * (D / 4); idx += 256) {
-    const int rl = idx / (D / 4), d4 = idx % (D / 4);
-    const int r = r0 + rl;
-    float* op = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * d4;
-    if (bad) {
-      *reinterpret_cast<f32x4_t*>(op) = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                                                __builtin_nanf("")};
-      continue;
-    }
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) {
-      const int64_t prow = ((int64_t)((base + s) * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
-      M = fmaxf(M, a.mlpart[2 * prow]);
-    }
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    f32x4_t num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const int64_t prow = ((int64_t)((base + s) * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
-      const float w = exp2f(a.mlpart[2 * prow] - Mu);
-      num += w * *reinterpret_cast<const f32x4_t*>(a.opart + prow * D + 4 * d4);
-      den += w * a.mlpart[2 * prow + 1];
-    }
-    *reinterpret_cast<f32x4_t*>(op) = num * (1.f / den);
+  if (rl >= rpt || r >= R) return;
+  float* op = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + (tid & 15) * CPT;
+  if (bad_lds) {
+#pragma unroll
+    for (int c = 0; c < CPT; c += 4)
+      *reinterpret_cast<f32x4_t*>(op + c) = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                    __builtin_nanf("")};
+    return;
   }
+  const int64_t stride = (int64_t)a.Hkv * a.row_tiles * rpt;    // partial rows between splits
+  const int64_t prow0 = ((int64_t)(base * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
+  float M = kNegInf;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, a.mlpart[2 * (prow0 + s * stride)]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  f32x4_t num[CPT / 4];
+#pragma unroll
+  for (int c = 0; c < CPT / 4; ++c) num[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < S; ++s) {
+    const int64_t prow = prow0 + s * stride;
+    const float w = exp2f(a.mlpart[2 * prow] - Mu);
+    den += w * a.mlpart[2 * prow + 1];
+    const float* src = a.opart + prow * D + (tid & 15) * CPT;
+#pragma unroll
+    for (int c = 0; c < CPT / 4; ++c) num[c] += w * *reinterpret_cast<const f32x4_t*>(src + 4 * c);
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int c = 0; c < CPT / 4; ++c) *reinterpret_cast<f32x4_t*>(op + 4 * c) = num[c] * inv;
 }
 
 template <int D>
@@ -505,7 +528,8 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.merge_workgroups > 0) {
-    hipLaunchKernelGGL((tree_attn_merge<D>), dim3((unsigned)p.merge_workgroups), dim3(256), 0, st, a);
+    const unsigned slices = (unsigned)((p.rows_per_tile + 15) / 16);
+    hipLaunchKernelGGL((tree_attn_merge<D>), dim3((unsigned)p.merge_workgroups * slices), dim3(256), 0, st, a);
     e = hipGetLastError();
   }
   return e;

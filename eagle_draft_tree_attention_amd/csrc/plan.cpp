@@ -101,7 +101,9 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
   int target_wgs;
   int min_chunk;
   if (plan->path == 1) {
-    int rt = static_cast<int>(ceil_div(R, 256));
+    // rows per workgroup: 64 * mb, mb <= 4 (tuning override EAGLE_VERIFY_ATTN_MB)
+    const int max_mb = env_int("EAGLE_VERIFY_ATTN_MB", 4) > 4 ? 4 : env_int("EAGLE_VERIFY_ATTN_MB", 4);
+    int rt = static_cast<int>(ceil_div(R, 64 * max_mb));
     int rows = static_cast<int>(ceil_div(ceil_div(R, rt), 64) * 64);
     plan->row_tiles = rt;
     plan->rows_per_tile = rows;

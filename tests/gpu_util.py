@@ -87,6 +87,8 @@ def compare_accept(got, ref, context=""):
 def small_spec(name, dtype="bf16", B=1, Hq=8, Hkv=8, D=128, lens=(1000,), levels=(4, 6, 10), rule="rank",
                V=1000, sigma_t=3.0, sigma_d=0.7, temperature=1.0, seed=7, zipf=0.0, tree=None):
     recipe = tree if tree is not None else ("levels", tuple(levels), rule)
+    if len(lens) == 1 and B > 1:
+        lens = tuple(lens) * B
     return si.WorkloadSpec(name, dtype, B, Hq, Hkv, D, tuple(lens), recipe, V,
                            sigma_t, sigma_d, zipf=zipf, temperature=temperature, seed=seed)
 
