@@ -88,10 +88,20 @@ struct AcceptKernelArgs {
   ChunkStat* stats;    // [B][T][2][NC]
   NodeState* nodes;    // [B][T]
   double* fpart;       // [B][T][NC]
-  double* spart;       // [B][NC]
+  double* spart;       // [B][NC][2]
   uint32_t* cnt_stats; // [B][T]
   uint32_t* cnt_pass;  // [B][T]
   uint32_t* cnt_final; // [B]
+  // fused path: per-node / per-sequence arrival words and publication words,
+  // tagged with the call epoch so they never need resetting
+  uint64_t* node_arrive;  // [B][T]
+  uint64_t* node_pub;     // [B][T]
+  uint64_t* seq_arrive;   // [B]
+  uint64_t* seq_pub;      // [B]
+  double* seq_sample;     // [B][4]: run, S, thr, (cstar | degenerate << 32) bits
+  uint64_t epoch;         // strictly increasing per call on a handle
+  uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
+  int fused;              // 1: one co-resident kernel; 0: three-kernel path
   int B, T, V, NC;
   int vec_ok;          // rows start 16-byte aligned
   float tau;           // > 0 sampled, == 0 greedy
@@ -102,6 +112,8 @@ struct AcceptKernelArgs {
 
 // ---------------------------------------------------------------- host side
 struct Workspace {
+  uint64_t* sync = nullptr;     // node_arrive | node_pub | seq_arrive | seq_pub
+  double* seq_sample = nullptr;
   float* attn_part = nullptr;   // kAttnPartFloats
   ChunkStat* stats = nullptr;
   NodeState* nodes = nullptr;
@@ -123,5 +135,8 @@ int vocab_chunks(int V);
 int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int kv_bf16,
                           void* stream);
 int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stream);
+// workgroups of the fused acceptance kernel that can be co-resident on the
+// device (0 if the query fails); the fused path is used when B*T*NC fits
+int fused_accept_capacity(int logits_bf16, int num_cus);
 
 }  // namespace ev

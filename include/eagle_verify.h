@@ -76,6 +76,8 @@ typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
 #define EAGLE_FLAG_DEGENERATE_RESIDUAL 16u /* residual mass was 0: fell back to q        */
 #define EAGLE_FLAG_BAD_KV_RANGE 32u     /* kv_indptr[b..b+1] does not hold L_b + T rows
                                            inside [0, num_kv_rows)                       */
+#define EAGLE_FLAG_INTERNAL 64u         /* a bounded device-side wait expired (workgroups
+                                           not co-resident); outputs are not valid       */
 
 #define EAGLE_MAX_TREE_ROWS 64 /* T = root + up to 63 draft nodes */
 

@@ -197,3 +197,38 @@ def test_chain_closed_form_on_gpu():
     log(f"    mean emitted {e.mean():.4f} vs {mean:.4f}")
     assert abs(e.mean() - mean) < 4.5 * e.std(ddof=1) / np.sqrt(len(e))
     ver.close()
+
+
+def test_large_batch_takes_the_general_path():
+    """B*T*chunks beyond what the fused kernel can keep co-resident: the
+    three-kernel path must give the same answers."""
+    spec = small_spec("large_batch", B=40, V=32000, levels=(10,) * 6, sigma_d=1.2)
+    log(f"[accept] {spec.name}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    ver = make_verifier(spec, inp.T)
+    for off in range(2):
+        got = run_accept(ver, inp, 1.0, SEED, off)
+        ref = _oracle(inp, 1.0, off)
+        compare_accept(got, ref, f"large batch offset {off}")
+    ver.close()
+
+
+def test_mixed_invalid_inputs_report_every_flag():
+    import eagle_draft_tree_attention_amd as ev
+    log("[accept] bad token together with an unusable row")
+    B, T, V = 2, 4, 64
+    rng = np.random.default_rng(5)
+    spec = _custom(B, T, V)
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
+    tgt = rng.standard_normal((B, T, V)).astype(np.float32)
+    drf = rng.standard_normal((B, T, V)).astype(np.float32)
+    par = np.tile(np.array([-1, 0, 0, 1], dtype=np.int32), (B, 1))
+    tok = np.tile(np.array([0, 5, 9, 3], dtype=np.int32), (B, 1))
+    tok[1, 3] = -2
+    tgt[1, 2, 0] = np.inf
+    ver = make_verifier(spec.with_(batch=B), T)
+    got = run_accept(ver, inp, 1.0, SEED, 0, target=tgt, draft=drf, parents=par, tokens=tok)
+    ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
+    assert got["flags"].tolist() == ref["flags"].tolist() == [0, ev.FLAG_BAD_TOKEN | ev.FLAG_NONFINITE]
+    compare_accept(got, ref, "mixed")
+    ver.close()
