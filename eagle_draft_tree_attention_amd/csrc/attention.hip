@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ev_internal.h"
 
 namespace ev {
@@ -86,25 +88,38 @@ __device__ __forceinline__ uint64_t ancestors_of(const int32_t* par, int node) {
 }
 
 // ------------------------------------------------------------- MFMA kernel
-// key (within a 64-key tile) that MFMA row m of 16-key block kb stands for;
-// chosen so that the S^T accumulator lane group lg holds 8 consecutive keys
-// 32*(kb/2) + 8*lg + 0..7 across the two blocks of one 32-key PV step.
-__device__ __forceinline__ int tile_key(int kb, int m) {
-  return 32 * (kb >> 1) + 8 * (m >> 2) + 4 * (kb & 1) + (m & 3);
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// gfx950 transposing LDS read: in each 16-lane group, lane j supplies the
+// address of 4 consecutive 16-bit values (row j of a 16x4 block) and lane i
+// receives rows 4e + i/4, column i%4 (e = 0..3).  Pointing lane j at
+// V[key0 + j/4][d0 + 4*(j%4)] of a key-major V tile therefore hands lane i
+// the four values V[key0 + e][d0 + i]: a column of V, i.e. a row of V^T.
+__device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4_t*)((__attribute__((address_space(3))) char*)(const_cast<uint16_t*>(p))));
 }
 
+// One (sequence, KV head, key split, row tile) per workgroup of 4 waves;
+// each wave owns MB blocks of 16 query rows.  Per 64-key tile:
+//   S^T[key][row] = K Q^T       16 (MB x 4 x D/32) v_mfma_f32_16x16x32_bf16
+//   online softmax per row      lane-local (lane % 16 = row), 2 cross-lane steps
+//   O^T[d][row] += V^T P^T      with P split into bf16 hi + lo
+// Key k of block kb sits in S^T row 16*kb + (k%16); lane group lg = lane/16
+// holds keys 16*kb + 4*lg + i, which is exactly the k-slot order the PV
+// operands need (slots 0..3 from block 2*ks, 4..7 from block 2*ks+1).
 template <int D, int MB>
 __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
   constexpr int KSTEPS = D / 32;          // QK^T contraction steps
   constexpr int DBLK = D / 16;            // output column blocks
-  constexpr int KSTRIDE = D + 8;          // bf16 per K row in LDS (16 B pad)
-  constexpr int VSTRIDE = kTileKeys + 8;  // bf16 per V^T row in LDS
-  constexpr int DCH = D / 8;              // 16-byte chunks per K/V row
-  constexpr int KLOADS = kTileKeys * DCH / 256;
-  constexpr int VUNITS = (kTileKeys / 4) * DCH;   // 4-key x 8-d transpose units
+  constexpr int KSTRIDE = D + 8;          // K row in LDS: +16 B, 8-row reads hit distinct banks
+  constexpr int VSTRIDE = D + 16;         // V row in LDS: +32 B, 4-row transposed reads hit distinct banks
+  constexpr int DCH = D / 8;              // 16-byte chunks per row
+  constexpr int LOADS = kTileKeys * DCH / 256;   // per thread per tile, for K and for V
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kTileKeys * KSTRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VSTRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kTileKeys * VSTRIDE];
   __shared__ uint64_t anc_lds[kMaxTree];
   __shared__ int32_t par_lds[kMaxTree];
 
@@ -118,11 +133,9 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
   const int S = a.split_base[b + 1] - a.split_base[b];
   const int L = a.L[b];
   const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
+  const int row_base = rt * a.rows_per_tile + wave * 16 * MB;   // lane rows: row_base + 16*rb + ln
 
-  // per-lane rows: row_base + 16*rb + ln
-  const int row_base = rt * a.rows_per_tile + wave * 16 * MB;
-
-  uint32_t bad = validate_seq(a, b, lane, wave == 0 ? par_lds : nullptr);
+  const uint32_t bad = validate_seq(a, b, lane, wave == 0 ? par_lds : nullptr);
   if (s_local == 0 && hk == 0 && rt == 0 && tid == 0) a.flags[b] = bad;
   if (bad) {
     if (S == 1) {
@@ -142,11 +155,12 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
   __syncthreads();
 
   const int64_t kv0 = a.kv_indptr[b];
-  const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a.k);
-  const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a.v);
   const int Hkv = a.Hkv;
+  const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)hk * D;
+  const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)hk * D;
+  const int64_t row_stride = (int64_t)Hkv * D;   // elements between consecutive KV rows
 
-  // query rows -> B operands (Q^T), zero for padding rows
+  // query rows -> B operands of S^T = K Q^T (zero for padding rows)
   bool row_ok[MB];
   int node[MB], head[MB];
   uint64_t anc_row[MB];
@@ -158,11 +172,10 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
     node[rb] = row_ok[rb] ? r / g : 0;
     head[rb] = hk * g + (row_ok[rb] ? r % g : 0);
     anc_row[rb] = anc_lds[node[rb]];
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(b * T + node[rb]) * Hq + head[rb]) * D + 8 * lg;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(b * T + node[rb]) * Hq + head[rb]) * D + 8 * lg;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
-      u32x4_t w = row_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * s) : u32x4_t{0, 0, 0, 0};
+      const u32x4_t w = row_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * s) : u32x4_t{0, 0, 0, 0};
       qf[rb][s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
@@ -179,50 +192,113 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
 
   const int k_begin = s_local * a.chunk;
   const int k_end = min(k_begin + a.chunk, L);
-  const int n_prefix_tiles = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
-  const bool last = (s_local == S - 1);
-  const int n_tiles = n_prefix_tiles + (last ? 1 : 0);
+  const int n_prefix = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
+  const int n_full = (k_end - k_begin) / kTileKeys > 0 ? (k_end - k_begin) / kTileKeys : 0;   // unmasked tiles
+  const int n_tiles = n_prefix + (s_local == S - 1 ? 1 : 0);
   const float c = a.scale_log2;
 
-  u32x4_t kreg[KLOADS], vreg[4];
-  auto tile_start = [&](int t) { return t < n_prefix_tiles ? k_begin + t * kTileKeys : L; };
-  auto tile_count = [&](int t) { return t < n_prefix_tiles ? min(kTileKeys, k_end - (k_begin + t * kTileKeys)) : T; };
-
+  // thread -> (row, 16-byte chunk) of the K and V tiles
+  int ld_row[LOADS], ld_chk[LOADS];
+#pragma unroll
+  for (int e = 0; e < LOADS; ++e) {
+    const int cidx = tid + 256 * e;
+    ld_row[e] = cidx / DCH;
+    ld_chk[e] = cidx % DCH;
+  }
+  u32x4_t kreg[LOADS], vreg[LOADS];
   auto load_tile = [&](int t) {
-    const int64_t row0 = kv0 + tile_start(t);
-    const int cnt = tile_count(t);
+    const bool tree = t >= n_prefix;
+    const int start = tree ? L : k_begin + t * kTileKeys;
+    const int cnt = tree ? T : min(kTileKeys, k_end - start);
+    const int64_t row0 = kv0 + start;
 #pragma unroll
-    for (int e = 0; e < KLOADS; ++e) {
-      const int cidx = tid + 256 * e;
-      const int key = cidx / DCH, dc = cidx % DCH;
-      kreg[e] = (key < cnt) ? *reinterpret_cast<const u32x4_t*>(kbase + ((row0 + key) * Hkv + hk) * D + dc * 8)
-                            : u32x4_t{0, 0, 0, 0};
-    }
-    if (tid < VUNITS) {
-      const int kg = tid / DCH, dc = tid % DCH;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = 4 * kg + e;
-        vreg[e] = (key < cnt) ? *reinterpret_cast<const u32x4_t*>(vbase + ((row0 + key) * Hkv + hk) * D + dc * 8)
-                              : u32x4_t{0, 0, 0, 0};
-      }
+    for (int e = 0; e < LOADS; ++e) {
+      const int64_t row = row0 + min(ld_row[e], cnt - 1);   // rows past the tile repeat a valid row; masked later
+      kreg[e] = *reinterpret_cast<const u32x4_t*>(kbase + row * row_stride + ld_chk[e] * 8);
+      vreg[e] = *reinterpret_cast<const u32x4_t*>(vbase + row * row_stride + ld_chk[e] * 8);
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int e = 0; e < KLOADS; ++e) {
-      const int cidx = tid + 256 * e;
-      const int key = cidx / DCH, dc = cidx % DCH;
-      *reinterpret_cast<u32x4_t*>(k_lds + key * KSTRIDE + dc * 8) = kreg[e];
+    for (int e = 0; e < LOADS; ++e) {
+      *reinterpret_cast<u32x4_t*>(k_lds + ld_row[e] * KSTRIDE + ld_chk[e] * 8) = kreg[e];
+      *reinterpret_cast<u32x4_t*>(v_lds + ld_row[e] * VSTRIDE + ld_chk[e] * 8) = vreg[e];
     }
-    if (tid < VUNITS) {
-      const int kg = tid / DCH, dc = tid % DCH;
+  };
+
+  // one 64-key tile; MASK: partial prefix tile (key < cnt) or tree tile
+  // (key < T and key is an ancestor of the row's node)
+  auto tile = [&](auto mask_tag, bool is_tree, int cnt) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x4_t sacc[4][MB];
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int sh = 16 * (dd & 1);
-        const uint32_t x0 = (vreg[0][dd >> 1] >> sh) & 0xFFFFu, x1 = (vreg[1][dd >> 1] >> sh) & 0xFFFFu;
-        const uint32_t x2 = (vreg[2][dd >> 1] >> sh) & 0xFFFFu, x3 = (vreg[3][dd >> 1] >> sh) & 0xFFFFu;
-        *reinterpret_cast<u32x2_t*>(vt_lds + (dc * 8 + dd) * VSTRIDE + 4 * kg) = u32x2_t{x0 | (x1 << 16), x2 | (x3 << 16)};
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) sacc[kb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kp = k_lds + (16 * kb + ln) * KSTRIDE + 8 * lg;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + 32 * s);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rb][s], sacc[kb][rb], 0, 0, 0);
+      }
+    }
+    bf16x8_t pb[MB][2], pl[MB][2];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = 16 * kb + 4 * lg + i;
+            const bool valid = is_tree ? (key < T && ((anc_row[rb] >> key) & 1ull)) : (key < cnt);
+            sacc[kb][rb][i] = valid ? sacc[kb][rb][i] : kNegInf;
+          }
+        }
+      }
+      float tmax = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(sacc[kb][rb][0], sacc[kb][rb][1]), fmaxf(sacc[kb][rb][2], sacc[kb][rb][3])));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m_run[rb], tmax * c);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = exp2f(m_run[rb] - m_use);
+      float psum = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = exp2f(__builtin_fmaf(sacc[2 * ks + (e >> 2)][rb][e & 3], c, -m_use));
+          psum += pv;
+          const __bf16 hi = (__bf16)pv;
+          pb[rb][ks][e] = hi;
+          pl[rb][ks][e] = (__bf16)(pv - (float)hi);
+        }
+      }
+      l_run[rb] = l_run[rb] * alpha + psum;
+      m_run[rb] = m_new;
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* vp = v_lds + (32 * ks + 4 * lg + (ln >> 2)) * VSTRIDE + 16 * db + 4 * (ln & 3);
+        const i16x4_t lo4 = lds_read_tr16(vp);
+        const i16x4_t hi4 = lds_read_tr16(vp + 16 * VSTRIDE);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb][ks], o[rb][db], 0, 0, 0);
+          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb][ks], o[rb][db], 0, 0, 0);
+        }
       }
     }
   };
@@ -232,91 +308,13 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
     __syncthreads();
     store_tile();
     __syncthreads();
-    const bool is_tree = (t >= n_prefix_tiles);
-    const int cnt = tile_count(t);
     if (t + 1 < n_tiles) load_tile(t + 1);
-
-    // S^T[key][row] = K Q^T for four 16-key blocks
-    f32x4_t sacc[4][MB];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int rb = 0; rb < MB; ++rb) sacc[kb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kp = k_lds + tile_key(kb, ln) * KSTRIDE + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + 32 * s);
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
-          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rb][s], sacc[kb][rb], 0, 0, 0);
-      }
-    }
-
-    // online softmax per row (lane-local, rows shared across the 4 lane groups)
-    bf16x8_t pb[MB][2], pl[MB][2];
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-      float x[4][4];
-      float tmax = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = tile_key(kb, 4 * lg + i);
-          const bool valid = is_tree ? (key < T && ((anc_row[rb] >> key) & 1ull)) : (key < cnt);
-          x[kb][i] = valid ? sacc[kb][rb][i] : kNegInf;
-          tmax = fmaxf(tmax, x[kb][i]);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run[rb], tmax * c);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[rb] - m_use);
-      float psum = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = exp2f(__builtin_fmaf(x[kb][i], c, -m_use));
-          psum += p[kb][i];
-        }
-      }
-      l_run[rb] = l_run[rb] * alpha + psum;
-      m_run[rb] = m_new;
-      if (alpha != 1.f) {
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
-      }
-      // P = hi + lo, both bf16: the PV product then carries ~16 significant
-      // bits of each weight instead of 8 (bf16 rounding of P alone leaves
-      // errors of a few 1e-3 relative to the output row).
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = p[2 * ks + (e >> 2)][e & 3];
-          const __bf16 hi = (__bf16)pv;
-          pb[rb][ks][e] = hi;
-          pl[rb][ks][e] = (__bf16)(pv - (float)hi);
-        }
-      }
-    }
-
-    // O^T[d][row] += V^T P^T
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const uint16_t* vp = vt_lds + (16 * db + ln) * VSTRIDE + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vp + 32 * ks);
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb][ks], o[rb][db], 0, 0, 0);
-          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb][ks], o[rb][db], 0, 0, 0);
-        }
-      }
+    if (t < n_full) {
+      tile(std::integral_constant<bool, false>{}, false, kTileKeys);
+    } else {
+      const bool is_tree = t >= n_prefix;
+      const int cnt = is_tree ? T : min(kTileKeys, k_end - (k_begin + t * kTileKeys));
+      tile(std::integral_constant<bool, true>{}, is_tree, cnt);
     }
   }
 

@@ -101,8 +101,11 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
   int target_wgs;
   int min_chunk;
   if (plan->path == 1) {
-    // rows per workgroup: 64 * mb, mb <= 4 (tuning override EAGLE_VERIFY_ATTN_MB)
-    const int max_mb = env_int("EAGLE_VERIFY_ATTN_MB", 4) > 4 ? 4 : env_int("EAGLE_VERIFY_ATTN_MB", 4);
+    // rows per workgroup: 64 * mb, mb <= 4 (tuning override EAGLE_VERIFY_ATTN_MB).
+    // One 16-row block per wave keeps the kernel at two waves per SIMD; the
+    // row tiles of one KV chunk then share its K/V tiles through L2.
+    const int mb_env = env_int("EAGLE_VERIFY_ATTN_MB", 1);
+    const int max_mb = mb_env > 4 ? 4 : (mb_env < 1 ? 1 : mb_env);
     int rt = static_cast<int>(ceil_div(R, 64 * max_mb));
     int rows = static_cast<int>(ceil_div(ceil_div(R, rt), 64) * 64);
     plan->row_tiles = rt;

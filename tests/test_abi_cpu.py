@@ -44,19 +44,19 @@ def _attn_args(B=1, T=61, lens=(8192,), rows=None, **over):
 
 
 def test_plan_for_the_workload_shapes():
-    # 8B/8K: R = 61*4 = 244 rows per KV head -> one 256-row MFMA tile
+    # 8B/8K: R = 61*4 = 244 rows per KV head -> four 64-row MFMA tiles
     a, keep = _attn_args()
     st, plan = ev.eagle_verify_check_tree_attention(_desc(), a)
     assert st == ev.EAGLE_OK
     assert plan.path == 1 and plan.rows_per_kv_head == 244
-    assert plan.row_tiles == 1 and plan.rows_per_tile == 256
+    assert plan.row_tiles == 4 and plan.rows_per_tile == 64
     assert plan.chunk_keys % 64 == 0 and plan.total_splits == -(-8192 // plan.chunk_keys)
-    assert plan.workgroups == plan.total_splits * 8
-    assert plan.merge_workgroups == (8 if plan.total_splits > 1 else 0)
-    # 70B batch of four: R = 488 -> two 256-row tiles per KV head
+    assert plan.workgroups == plan.total_splits * 8 * 4
+    assert plan.merge_workgroups == (8 * 4 if plan.total_splits > 1 else 0)
+    # 70B batch of four: R = 488 -> eight 64-row tiles per KV head
     a, keep = _attn_args(B=4, lens=(1024, 2048, 3072, 4096))
     st, plan = ev.eagle_verify_check_tree_attention(_desc(num_q_heads=64), a)
-    assert st == ev.EAGLE_OK and plan.row_tiles == 2 and plan.rows_per_tile == 256
+    assert st == ev.EAGLE_OK and plan.row_tiles == 8 and plan.rows_per_tile == 64
     # tiny fp32 goes to the FMA path, one row per workgroup
     a, keep = _attn_args(T=11, lens=(128,))
     st, plan = ev.eagle_verify_check_tree_attention(
