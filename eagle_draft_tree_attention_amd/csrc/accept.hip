@@ -219,8 +219,32 @@ __device__ bool arrive_last(uint32_t* counter, uint32_t expected, int32_t* lds_f
   return *lds_flag != 0;
 }
 
-// Test child ordinal i of node n under residual (C, s).  Returns +1 accepted,
-// 0 rejected, -1 token out of range (sequence is poisoned later).
+// Accept test of one child under residual (C, s): q(t), p(t) at its token
+// and the test's uniform r.  Returns +1 accepted, 0 rejected, -1 token out of
+// range (the sequence is poisoned later).
+__device__ int decide_pre(double qt, double pt, double r, int tok, int V, double C, double s, uint32_t& flags,
+                          int32_t& near) {
+  if (tok < 0 || tok >= V) return -1;
+  if (pt == 0.0) {
+    flags |= EAGLE_FLAG_P_ZERO;
+    return (qt - C * pt) > 0.0 ? 1 : 0;
+  }
+  const double num = fmax(0.0, qt - C * pt);
+  if (fabs(r - num / (s * pt)) < kNearTie) ++near;
+  return (r * s * pt < num) ? 1 : 0;
+}
+
+// The same test from the raw logits xt / yt of the node's target / draft rows
+// at the child's token (child ordinal i draws slot i).
+__device__ int decide_values(const AcceptKernelArgs& a, int b, int n, int ordinal, int tok, double xt, double yt,
+                             double C, double s, const NodeState& st, uint32_t& flags, int32_t& near) {
+  if (tok < 0 || tok >= a.V) return -1;
+  const double qt = exp((xt - static_cast<double>(st.mq)) * a.inv_tau) / st.zq;
+  const double pt = exp((yt - static_cast<double>(st.mp)) * a.inv_tau) / st.zp;
+  const double r = decision_uniform(a, b, n, static_cast<uint32_t>(ordinal));
+  return decide_pre(qt, pt, r, tok, a.V, C, s, flags, near);
+}
+
 template <typename TL>
 __device__ int decide_child(const AcceptKernelArgs& a, int b, int n, int child, int ordinal, double C, double s,
                             const NodeState& st, uint32_t& flags, int32_t& near) {
@@ -229,16 +253,7 @@ __device__ int decide_child(const AcceptKernelArgs& a, int b, int n, int child, 
   const int64_t row = static_cast<int64_t>(b * a.T + n) * a.V;
   const double xt = logit<TL>(reinterpret_cast<const TL*>(a.target) + row, tok);
   const double yt = logit<TL>(reinterpret_cast<const TL*>(a.draft) + row, tok);
-  const double qt = exp((xt - static_cast<double>(st.mq)) * a.inv_tau) / st.zq;
-  const double pt = exp((yt - static_cast<double>(st.mp)) * a.inv_tau) / st.zp;
-  const double r = decision_uniform(a, b, n, static_cast<uint32_t>(ordinal));
-  if (pt == 0.0) {
-    flags |= EAGLE_FLAG_P_ZERO;
-    return (qt - C * pt) > 0.0 ? 1 : 0;
-  }
-  const double num = fmax(0.0, qt - C * pt);
-  if (fabs(r - num / (s * pt)) < kNearTie) ++near;
-  return (r * s * pt < num) ? 1 : 0;
+  return decide_values(a, b, n, ordinal, tok, xt, yt, C, s, st, flags, near);
 }
 
 // Residual mass sum_v max(0, q_v - C p_v) of node n over [v0, v1), fp64,
@@ -675,30 +690,42 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
 // ============================================================ fused path
 // One launch, B*T*NC workgroups, all co-resident (the host only takes this
 // path when the occupancy query says the grid fits).  The NC workgroups of a
-// node keep their slice of the node's target and draft exponentials in
-// registers from the statistics pass to the end, and coordinate through
-// device-scope arrival words (tagged with the call epoch and phase, so they
-// never need resetting) and publication words:
-//   stats  -> last arrival combines, decides the first child, publishes
-//   rounds -> while the node needs another residual mass: partial sums from
-//             registers, last arrival takes the next decision, publishes
+// node stage their slice of the node's target and draft rows in LDS once and
+// work from there to the end:
+//   stats  -> chunk statistics and one barrier per node; every workgroup of
+//             the node then combines them (same arithmetic in the same order,
+//             so all of them hold the same node state) and takes the first
+//             decision itself
+//   rounds -> while the node needs another residual mass, each workgroup adds
+//             (1 << 57) + its partial mass in 2^-49 fixed point to the round's
+//             word with one atomic: the word carries the arrival count and an
+//             exact, order-independent sum, so one poll ends the round with
+//             the same s in every workgroup
 //   walk   -> a node that ends without an accepted child checks, once its
 //             ancestors are decided, whether the walk reaches it
-//   sample -> the terminal node's workgroups add up their chunk masses, the
-//             last arrival finds the chunk holding u*S, and that workgroup
-//             scans its registers in token order and writes the outputs.
+//   sample -> the terminal node's workgroups publish their chunk masses, each
+//             finds the chunk holding u*S, and that workgroup scans its LDS
+//             slice in token order and writes the outputs.
 // Every wait is bounded by spin_limit; a wait that expires flags the
 // sequence EAGLE_FLAG_INTERNAL instead of hanging.
 
 constexpr uint64_t kPubDone = 255;
 constexpr int kFusedMaxChunks = 64;   // V <= 64 * 8192 on the fused path
+// Round words: bits 57..63 count arrivals (<= 64 chunks), bits 0..56 hold the
+// sum of the chunks' partial masses in units of 2^-49.  A partial is a mass
+// of a probability distribution (at most 1 up to rounding; clamped to 2), so
+// 64 of them stay below 2^56.
+constexpr int kCountShift = 57;
+constexpr uint64_t kSumMask = (1ull << kCountShift) - 1;
+constexpr double kFixScale = 0x1p49;
+constexpr double kFixUnit = 0x1p-49;
 
 // Cross-workgroup traffic of the fused path.  The L2 caches of the XCDs are
 // not coherent with each other, and agent-scope release/acquire would write
 // back / invalidate a whole L2 per operation.  Instead every word that one
 // workgroup writes for another goes through system-scope relaxed atomics,
 // which bypass the non-coherent caches, and ordering comes from waiting for
-// the stores to complete (a workgroup-scope release) before signalling.
+// the stores to complete before signalling.
 __device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
@@ -723,12 +750,6 @@ __device__ __forceinline__ void loads_after() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-__device__ void load_state(const NodeState* src, NodeState* dst) {
-  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
-  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
-#pragma unroll
-  for (int i = 0; i < static_cast<int>(sizeof(NodeState) / 8); ++i) d[i] = ld_u64(s + i);
-}
 __device__ void store_state(NodeState* dst, const NodeState& src) {
   const uint64_t* s = reinterpret_cast<const uint64_t*>(&src);
   uint64_t* d = reinterpret_cast<uint64_t*>(dst);
@@ -745,19 +766,19 @@ __device__ __forceinline__ uint64_t poll(const uint64_t* w) {
   return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Every thread t < count waits until w[t] >= target (relaxed polls, one
-// acquire when done); block-wide verdict in *ok (all threads call).
-__device__ bool wait_all(const uint64_t* w, int count, uint64_t target, uint32_t limit, int32_t* ok) {
+// Every thread t < count waits until w[t * stride] >= target; block-wide
+// verdict in *ok (all threads call).
+__device__ bool wait_all(const uint64_t* w, int stride, int count, uint64_t target, uint32_t limit, int32_t* ok) {
   if (threadIdx.x == 0) *ok = 1;
   __syncthreads();
   if (static_cast<int>(threadIdx.x) < count) {
     uint32_t it = 0;
-    while (poll(w + threadIdx.x) < target) {
+    while (poll(w + static_cast<int64_t>(threadIdx.x) * stride) < target) {
       if (++it > limit) {
         *ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(4);
     }
     loads_after();
   }
@@ -765,14 +786,22 @@ __device__ bool wait_all(const uint64_t* w, int count, uint64_t target, uint32_t
   return *ok != 0;
 }
 
+// A child of the node: its token, the node's two logits at that token and,
+// once the node's normalisers are known, q(t), p(t) and the test's uniform.
+struct Cand {
+  double qt, pt, r;
+  float xq, yp;
+  int32_t tok, child;
+};
+
 struct FusedShared {
   TreeInfo ti;
   NodeState st;
-  double dscr[4];
-  float fscr[4];
-  uint32_t uscr[4];
+  Cand cand[kMaxTree];   // by child ordinal
+  int32_t nkids;
+  double dscr[8];
+  float fscr[8];
   int32_t iscr[4];
-  int32_t flag;
   int32_t ok;
   int32_t onpath;
   uint32_t seqflags;
@@ -780,88 +809,159 @@ struct FusedShared {
   int32_t found;
   double scan[kThreads / 64];
   double sample[4];
-  double mass[2 * kFusedMaxChunks];
 };
 
-
-// One row chunk staged in LDS in token order (index = token - v0); tokens
-// past the chunk hold -inf.  Thread t owns the slots j = 0..31 at index
-// ((j / G) * 256 + t) * G + j % G, G = 16 / sizeof(TL), so a thread reads
-// 16-byte groups and consecutive lanes read consecutive groups.
-template <typename TL>
-struct ChunkView {
-  const TL* lds;
-  static constexpr int G = 16 / static_cast<int>(sizeof(TL));
-  __device__ __forceinline__ static int index(int j) { return ((j / G) * kThreads + static_cast<int>(threadIdx.x)) * G + (j % G); }
-  __device__ __forceinline__ float get(int j) const {
-    if constexpr (sizeof(TL) == 2)
-      return __uint_as_float(static_cast<uint32_t>(lds[index(j)]) << 16);
-    else
-      return lds[index(j)];
+// Two reductions over the block sharing one pair of barriers (all threads call).
+template <typename T, typename Op>
+__device__ void block_reduce2(T& x, T& y, Op op, T* scratch /* >= 8 */) {
+  x = wave_reduce(x, op);
+  y = wave_reduce(y, op);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    scratch[w] = x;
+    scratch[4 + w] = y;
   }
+  __syncthreads();
+  x = op(op(scratch[0], scratch[1]), op(scratch[2], scratch[3]));
+  y = op(op(scratch[4], scratch[5]), op(scratch[6], scratch[7]));
+}
+
+// 16 bytes of logits <-> G values in token order.
+template <typename TL>
+struct Pack;
+template <>
+struct Pack<uint16_t> {
+  static constexpr int G = 8;
+  __device__ __forceinline__ static void unpack(const u32x4_t w, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+  __device__ __forceinline__ static uint32_t neg_inf_word() { return 0xFF80FF80u; }
+  __device__ __forceinline__ static uint32_t bits(uint16_t x) { return x; }
+};
+template <>
+struct Pack<float> {
+  static constexpr int G = 4;
+  __device__ __forceinline__ static void unpack(const u32x4_t w, float (&f)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+  __device__ __forceinline__ static uint32_t neg_inf_word() { return 0xFF800000u; }
+  __device__ __forceinline__ static uint32_t bits(float x) { return __float_as_uint(x); }
 };
 
+// One logit of a chunk staged in LDS, as fp32.
 template <typename TL>
-__device__ void stage_chunk(const TL* row, int v0, int v1, bool vecpath, TL* lds) {
-  const int tid = threadIdx.x;
-  constexpr int G = 16 / sizeof(TL);
-  if (vecpath) {
+__device__ __forceinline__ float lds_logit(const TL* l, int i) {
+  if constexpr (sizeof(TL) == 2)
+    return __uint_as_float(static_cast<uint32_t>(l[i]) << 16);
+  else
+    return l[i];
+}
+
+// A row chunk lives in LDS in token order (index = token - v0; tokens past
+// the vocabulary hold -inf).  In the "strided" view thread t owns the
+// 16-byte groups jj * 256 + t (jj < NV), so a warp reads consecutive groups.
+template <typename TL>
+__device__ __forceinline__ int group_index(int jj) {
+  return (jj * kThreads + static_cast<int>(threadIdx.x)) * Pack<TL>::G;
+}
+
+// Load this thread's strided groups of [v0, v1) from a row.
+template <typename TL, int NV>
+__device__ __forceinline__ void load_groups(const TL* row, int v0, int v1, bool vecpath, u32x4_t (&w)[NV]) {
+  constexpr int G = Pack<TL>::G;
 #pragma unroll
-    for (int jj = 0; jj < kPerThread / G; ++jj) {
-      const int i0 = (jj * kThreads + tid) * G;
-      u32x4_t w;
-      if (v0 + i0 < v1) {
-        w = *reinterpret_cast<const u32x4_t*>(row + v0 + i0);
-      } else {
-        const uint32_t ni = sizeof(TL) == 2 ? 0xFF80FF80u : 0xFF800000u;
-        w = u32x4_t{ni, ni, ni, ni};
+  for (int jj = 0; jj < NV; ++jj) {
+    const int i0 = group_index<TL>(jj);
+    const uint32_t ni = Pack<TL>::neg_inf_word();
+    if (vecpath) {
+      w[jj] = (v0 + i0 < v1) ? *reinterpret_cast<const u32x4_t*>(row + v0 + i0) : u32x4_t{ni, ni, ni, ni};
+    } else {
+      uint32_t e32[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        const uint32_t x = (v0 + i0 + e < v1) ? Pack<TL>::bits(row[v0 + i0 + e]) : (ni & (sizeof(TL) == 2 ? 0xFFFFu : ~0u));
+        if constexpr (sizeof(TL) == 2)
+          e32[e >> 1] |= x << (16 * (e & 1));
+        else
+          e32[e] = x;
       }
-      *reinterpret_cast<u32x4_t*>(lds + i0) = w;
-    }
-  } else {
-    for (int i = tid; i < kVocabChunk; i += kThreads) {
-      const float x = (v0 + i < v1) ? logit<TL>(row, v0 + i) : kNegInf;
-      if constexpr (sizeof(TL) == 2)
-        lds[i] = static_cast<TL>(__float_as_uint(x) >> 16);
-      else
-        lds[i] = x;
+      w[jj] = u32x4_t{e32[0], e32[1], e32[2], e32[3]};
     }
   }
 }
 
-// Chunk statistics of one row: block max m, NaN/+inf flag, chunk argmax
-// (greedy mode) or sum of exp((x - m)/tau) (fp64).
-template <typename TL>
-__device__ void chunk_stats(const ChunkView<TL>& r, int v0, int v1, const AcceptKernelArgs& a, bool greedy,
-                            float& m, uint32_t& bad, int& am, double& z, FusedShared& sh) {
-  float lm = kNegInf;
-  uint32_t lb = 0;
-#pragma unroll 4
-  for (int j = 0; j < kPerThread; ++j) {
-    const float v = r.get(j);
-    if (v != v || v == __builtin_inff()) lb = 1;
-    lm = fmaxf(lm, v);
+// Row statistics of this thread's values: the maximum, or +inf when a NaN or
+// +inf is present (the row is then unusable).
+template <typename TL, int NV>
+__device__ __forceinline__ float local_max(const u32x4_t (&w)[NV]) {
+  float m = kNegInf;
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) {
+    float f[Pack<TL>::G];
+    Pack<TL>::unpack(w[jj], f);
+#pragma unroll
+    for (int e = 0; e < Pack<TL>::G; ++e) m = (f[e] != f[e] || f[e] == __builtin_inff()) ? __builtin_inff() : fmaxf(m, f[e]);
   }
-  m = block_reduce(lm, MaxOp{}, sh.fscr);
-  bad = block_reduce(lb, OrU{}, sh.uscr);
-  am = -1;
-  z = 0.0;
-  if (greedy) {
-    int la = 0x7FFFFFFF;
-#pragma unroll 4
-    for (int j = 0; j < kPerThread; ++j) {
-      const int t = v0 + ChunkView<TL>::index(j);
-      if (r.get(j) == m && t < v1 && t < la) la = t;
+  return m;
+}
+
+// exp((x - m) / tau) = 2^(x c2 - m c2) on the hardware exp2 (results below
+// 2^-126 of the row maximum, irrelevant to any sum here, may flush to 0)
+__device__ __forceinline__ float ex2(float x, float c2, float mc2) { return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2, mc2)); }
+
+// sum of exp((x - m) / tau) over this thread's values, fp64
+template <typename TL, int NV>
+__device__ __forceinline__ double local_expsum(const u32x4_t (&w)[NV], float m, float c2) {
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  const float mc2 = -m * c2;
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) {
+    float f[Pack<TL>::G];
+    Pack<TL>::unpack(w[jj], f);
+#pragma unroll
+    for (int e = 0; e < Pack<TL>::G; ++e) acc[e & 3] += static_cast<double>(ex2(f[e], c2, mc2));
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Residual mass sum max(0, q - C p) and plain mass sum q of this thread's
+// strided slots, from LDS.  With q = fq e_q and p = fp e_p (e = exp2 of the
+// scaled logit minus the chunk maximum; mqs / mps are 0 for an all -inf
+// chunk, whose exponentials are then 0), max(0, q - C p) = fq max(0, e_q -
+// K e_p) with K = C fp / fq: per token two exp2, one fma and one max in
+// fp32, accumulated in fp64.
+template <typename TL, int NV>
+__device__ __forceinline__ void local_masses(const TL* lq, const TL* lp, bool use_p, float mqs, float mps, float c2,
+                                             double fq, double fp, double C, double& res, double& qsum) {
+  double ra[4] = {0.0, 0.0, 0.0, 0.0}, qa[4] = {0.0, 0.0, 0.0, 0.0};
+  const float qc = -mqs * c2, pc = -mps * c2;
+  const float K = (use_p && fq > 0.0) ? static_cast<float>(C * fp / fq) : 0.f;
+  u32x4_t wq[NV], wp[NV];
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) {
+    wq[jj] = *reinterpret_cast<const u32x4_t*>(lq + group_index<TL>(jj));
+    if (use_p) wp[jj] = *reinterpret_cast<const u32x4_t*>(lp + group_index<TL>(jj));
+  }
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) {
+    float fa[Pack<TL>::G], fb[Pack<TL>::G];
+    Pack<TL>::unpack(wq[jj], fa);
+    if (use_p) Pack<TL>::unpack(wp[jj], fb);
+#pragma unroll
+    for (int e = 0; e < Pack<TL>::G; ++e) {
+      const float eq = ex2(fa[e], c2, qc);
+      qa[e & 3] += static_cast<double>(eq);
+      if (use_p) ra[e & 3] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ex2(fb[e], c2, pc), eq)));
     }
-    am = block_reduce(la, MinI{}, sh.iscr);
-    return;
   }
-  double lz = 0.0;
-  if (m != kNegInf && !bad) {
-#pragma unroll 4
-    for (int j = 0; j < kPerThread; ++j) lz += static_cast<double>(exp2f((r.get(j) - m) * a.c2));
-  }
-  z = block_reduce(lz, AddD{}, sh.dscr);
+  qsum = ((qa[0] + qa[1]) + (qa[2] + qa[3])) * fq;
+  res = use_p ? ((ra[0] + ra[1]) + (ra[2] + ra[3])) * fq : qsum;
 }
 
 __device__ void write_poison(const AcceptKernelArgs& a, int b, uint32_t flags) {
@@ -896,7 +996,7 @@ __device__ bool phase_barrier(uint64_t* w, uint32_t group, uint32_t limit) {
   uint32_t it = 0;
   while (poll(w) < target) {
     if (++it > limit) return false;
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(2);
   }
   loads_after();
   return true;
@@ -904,6 +1004,8 @@ __device__ bool phase_barrier(uint64_t* w, uint32_t group, uint32_t limit) {
 
 template <typename TL>
 __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a) {
+  constexpr int G = Pack<TL>::G;
+  constexpr int NV = kPerThread / G;   // 16-byte groups per thread and row
   __shared__ FusedShared sh;
   __shared__ int32_t path_lds[kMaxTree];
   __shared__ __attribute__((aligned(16))) TL lq[kVocabChunk];
@@ -914,108 +1016,187 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   const int b = blockIdx.x / (NC * T);
   const bool greedy = a.tau == 0.f;
   const uint64_t base = a.epoch << 8;
-  uint64_t* npub = a.node_pub + static_cast<int64_t>(b) * T;
-  uint64_t* narr = a.node_arrive + static_cast<int64_t>(b) * T;
   const uint32_t limit = a.spin_limit;
   const bool lead = (c == 0);   // publishes the node's state for the other nodes' groups
+
+  // the round words of the previous fused call start this call's successor at zero
+  {
+    const int64_t total = static_cast<int64_t>(a.zero_b) * a.Tm * kRoundWords;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + tid; i < total;
+         i += static_cast<int64_t>(gridDim.x) * kThreads)
+      st_u64(a.round_clear + i, 0ull);
+  }
+
+  // node j of this sequence: arrivals at nsync[j * kSyncWords], publication
+  // at nsync[j * kSyncWords + 1]
+  uint64_t* nsync = a.node_sync + static_cast<int64_t>(b) * a.Tm * kSyncWords;
+  uint64_t* const narr = nsync + n * kSyncWords;
+  uint64_t* const npub = nsync + n * kSyncWords + 1;
 
   auto fail_internal = [&]() {
     if (tid == 0) atomicOr(&a.flags[b], EAGLE_FLAG_INTERNAL);
   };
 
-  // ---- sequence validity, the same verdict in every workgroup of b
+  // ---- sequence validity (the same verdict in every workgroup of b) and
+  // this node's children, in ascending index = child ordinal
   load_tree(a, b, sh.ti);
-  if (tid < 64) {
-    bool tb = false;
-    if (tid >= 1 && tid < T) {
-      const int tok = a.tokens[b * T + tid];
-      tb = tok < 0 || tok >= V;
-    }
-    const bool any_tb = __any(tb);
-    if (tid == 0) sh.uscr[0] = any_tb ? EAGLE_FLAG_BAD_TOKEN : 0u;
-  }
-  __syncthreads();
   if (!sh.ti.ok) {
     if (n == 0 && c == 0) write_poison(a, b, EAGLE_FLAG_BAD_TREE);
     return;
   }
-  // a token outside the vocabulary poisons the sequence too, but the row
-  // checks still run so that every unusable input is reported
-  const uint32_t tokbad = sh.uscr[0];
+  const int64_t rowoff = static_cast<int64_t>(b * T + n) * V;
+  const TL* trow = reinterpret_cast<const TL*>(a.target) + rowoff;
+  const TL* drow = reinterpret_cast<const TL*>(a.draft) + rowoff;
+  if (tid < 64) {
+    int tok = 0;
+    bool tb = false;
+    if (tid >= 1 && tid < T) {
+      tok = a.tokens[b * T + tid];
+      tb = tok < 0 || tok >= V;
+    }
+    const bool is_child = tid >= 1 && tid < T && sh.ti.par[tid] == n;
+    const uint64_t kids_mask = __ballot(is_child);
+    const bool any_tb = __any(tb);
+    if (is_child) {
+      const int ord = __popcll(kids_mask & ((1ull << tid) - 1ull));
+      Cand cd;
+      cd.qt = cd.pt = cd.r = 0.0;
+      cd.xq = cd.yp = 0.f;
+      cd.tok = tok;
+      cd.child = tid;
+      if (!greedy && !tb) {
+        cd.xq = logit<TL>(trow, tok);
+        cd.yp = logit<TL>(drow, tok);
+      }
+      sh.cand[ord] = cd;
+    }
+    if (tid == 0) {
+      sh.nkids = __popcll(kids_mask);
+      // a token outside the vocabulary poisons the sequence too, but the row
+      // checks still run so that every unusable input is reported
+      sh.seqflags = any_tb ? EAGLE_FLAG_BAD_TOKEN : 0u;
+    }
+  }
   __syncthreads();
-  const bool kids = has_children(sh.ti, T, n);
-  const bool two = kids && !greedy;
+  const uint32_t tokbad = sh.seqflags;
+  const int nkids = sh.nkids;
+  const bool two = nkids > 0 && !greedy;
   const int v0 = c * kVocabChunk, v1 = min(V, v0 + kVocabChunk);
-  constexpr int G = 16 / sizeof(TL);
   const bool vecpath = a.vec_ok != 0 && ((v1 - v0) % G) == 0;
 
-  // ---- statistics pass: the chunk goes to LDS once and stays there
-  const int64_t rowoff = static_cast<int64_t>(b * T + n) * V;
-  stage_chunk<TL>(reinterpret_cast<const TL*>(a.target) + rowoff, v0, v1, vecpath, lq);
-  if (two) stage_chunk<TL>(reinterpret_cast<const TL*>(a.draft) + rowoff, v0, v1, vecpath, lp);
-  __syncthreads();
-  const ChunkView<TL> rq{lq}, rp{lp};
+  // ---- statistics pass: the chunk is loaded once, kept in LDS, and its
+  // statistics come straight from the loaded registers
   float mq_c, mp_c = kNegInf;
-  uint32_t badq, badp = 0;
-  int amq, amp;
-  double zq_c, zp_c = 0.0;
-  chunk_stats<TL>(rq, v0, v1, a, greedy, mq_c, badq, amq, zq_c, sh);
-  if (two) chunk_stats<TL>(rp, v0, v1, a, false, mp_c, badp, amp, zp_c, sh);
+  int amq = -1;
+  double zq_c = 0.0, zp_c = 0.0;
+  {
+    u32x4_t wq[NV], wd[NV];
+    load_groups<TL, NV>(trow, v0, v1, vecpath, wq);
+    if (two) load_groups<TL, NV>(drow, v0, v1, vecpath, wd);
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      *reinterpret_cast<u32x4_t*>(lq + group_index<TL>(jj)) = wq[jj];
+      if (two) *reinterpret_cast<u32x4_t*>(lp + group_index<TL>(jj)) = wd[jj];
+    }
+    mq_c = local_max<TL, NV>(wq);
+    if (two) mp_c = local_max<TL, NV>(wd);
+    block_reduce2(mq_c, mp_c, MaxOp{}, sh.fscr);
+    if (greedy) {
+      int la = 0x7FFFFFFF;
+#pragma unroll
+      for (int jj = 0; jj < NV; ++jj) {
+        float f[G];
+        Pack<TL>::unpack(wq[jj], f);
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          const int t = v0 + group_index<TL>(jj) + e;
+          if (f[e] == mq_c && t < v1 && t < la) la = t;
+        }
+      }
+      amq = block_reduce(la, MinI{}, sh.iscr);
+    } else {
+      double lzq = 0.0, lzp = 0.0;
+      if (mq_c != kNegInf && mq_c != __builtin_inff()) lzq = local_expsum<TL, NV>(wq, mq_c, a.c2);
+      if (two && mp_c != kNegInf && mp_c != __builtin_inff()) lzp = local_expsum<TL, NV>(wd, mp_c, a.c2);
+      block_reduce2(lzq, lzp, AddD{}, sh.dscr);
+      zq_c = lzq;
+      zp_c = lzp;
+    }
+  }
   ChunkStat* cs = a.stats + (static_cast<int64_t>(b * T + n) * 2) * NC;
   if (tid == 0) {
-    auto put = [](ChunkStat* d, float m, uint32_t bad, int am, double z) {
+    auto put = [](ChunkStat* d, float m, int am, double z) {
       uint64_t* w = reinterpret_cast<uint64_t*>(d);
+      const uint32_t bad = (m == __builtin_inff()) ? 1u : 0u;
       st_u64(w, static_cast<uint64_t>(__float_as_uint(m)) | (static_cast<uint64_t>(bad) << 32));
       st_u64(w + 1, static_cast<uint64_t>(static_cast<uint32_t>(am)));
       st_f64(&d->z, z);
     };
-    put(cs + c, mq_c, badq, amq, zq_c);
-    if (two) put(cs + NC + c, mp_c, badp, -1, zp_c);
-    sh.ok = phase_barrier(narr + n, static_cast<uint32_t>(NC), limit) ? 1 : 0;
+    put(cs + c, mq_c, amq, zq_c);
+    if (two) put(cs + NC + c, mp_c, -1, zp_c);
+    sh.ok = phase_barrier(narr, static_cast<uint32_t>(NC), limit) ? 1 : 0;
   }
   __syncthreads();
   if (!sh.ok) return fail_internal();
 
   // ---- every workgroup of the node combines the chunks (same arithmetic in
-  // the same order everywhere, so all of them hold the same node state)
-  if (tid < 64) {
-    for (int r = 0; r < (two ? 2 : 1); ++r) {
+  // the same order everywhere, so all of them hold the same node state):
+  // wave 0 the target row, wave 1 the draft row, one chunk per lane
+  if (tid < 128) {
+    const int r = tid >> 6, q = tid & 63;
+    if (r == 0 || two) {
       const ChunkStat* rs = cs + r * NC;
-      float M = kNegInf;
-      uint32_t rb = 0;
-      for (int q = tid; q < NC; q += 64) {
-        const uint64_t w0 = ld_u64(reinterpret_cast<const uint64_t*>(rs + q));
-        M = fmaxf(M, __builtin_bit_cast(float, static_cast<uint32_t>(w0)));
-        rb |= static_cast<uint32_t>(w0 >> 32);
+      float mc = kNegInf;
+      uint32_t bc = 0;
+      int ac = 0x7FFFFFFF;
+      double zc = 0.0;
+      if (q < NC) {
+        const uint64_t* w = reinterpret_cast<const uint64_t*>(rs + q);
+        const uint64_t w0 = ld_u64(w), w1 = ld_u64(w + 1), w2 = ld_u64(w + 2);
+        mc = __builtin_bit_cast(float, static_cast<uint32_t>(w0));
+        bc = static_cast<uint32_t>(w0 >> 32);
+        ac = static_cast<int>(static_cast<uint32_t>(w1));
+        zc = __builtin_bit_cast(double, w2);
       }
-      M = wave_reduce(M, MaxOp{});
-      rb = wave_reduce(rb, OrU{});
-      double Z = 0.0;
-      int arg = 0x7FFFFFFF;
-      for (int q = tid; q < NC; q += 64) {
-        const uint64_t w0 = ld_u64(reinterpret_cast<const uint64_t*>(rs + q));
-        const float mq = __builtin_bit_cast(float, static_cast<uint32_t>(w0));
-        if (greedy) {
-          const int aq = static_cast<int>(static_cast<uint32_t>(ld_u64(reinterpret_cast<const uint64_t*>(rs + q) + 1)));
-          if (mq == M && aq < arg) arg = aq;
-        } else if (mq != kNegInf) {
-          Z += ld_f64(&rs[q].z) * exp2((static_cast<double>(mq) - M) * static_cast<double>(a.c2));
-        }
-      }
-      Z = wave_reduce(Z, AddD{});
-      arg = wave_reduce(arg, MinI{});
-      if (tid == 0) {
+      const float M = wave_reduce(mc, MaxOp{});
+      const uint32_t rb = wave_reduce(bc, OrU{});
+      const double Z = wave_reduce(
+          (!greedy && q < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - M) * static_cast<double>(a.c2)) : 0.0,
+          AddD{});
+      const int arg = wave_reduce((greedy && q < NC && mc == M) ? ac : 0x7FFFFFFF, MinI{});
+      if (q == 0) {
+        const uint32_t fl = (rb || M == kNegInf) ? EAGLE_FLAG_NONFINITE : 0u;
         if (r == 0) {
           sh.st.mq = M;
           sh.st.zq = Z;
           sh.st.argmax = arg;
-          sh.st.flags = (rb || M == kNegInf) ? EAGLE_FLAG_NONFINITE : 0u;
+          sh.st.flags = fl;
         } else {
           sh.st.mp = M;
           sh.st.zp = Z;
-          if (rb || M == kNegInf) sh.st.flags |= EAGLE_FLAG_NONFINITE;
+          sh.iscr[1] = static_cast<int32_t>(fl);
         }
       }
+    }
+  }
+  __syncthreads();
+  if (tid == 0 && two) sh.st.flags |= static_cast<uint32_t>(sh.iscr[1]);
+  __syncthreads();
+  if (tid < 64) {
+    // q(t), p(t) and the uniform of every child test, in parallel
+    if (two && tid < nkids && !(sh.st.flags & EAGLE_FLAG_NONFINITE)) {
+      Cand& cd = sh.cand[tid];
+      if (cd.tok >= 0 && cd.tok < V) {
+        cd.qt = exp((static_cast<double>(cd.xq) - static_cast<double>(sh.st.mq)) * a.inv_tau) / sh.st.zq;
+        cd.pt = exp((static_cast<double>(cd.yp) - static_cast<double>(sh.st.mp)) * a.inv_tau) / sh.st.zp;
+      }
+      cd.r = decision_uniform(a, b, n, static_cast<uint32_t>(tid));
+    }
+    // greedy: the first child carrying the target argmax
+    if (greedy) {
+      const bool match = tid < nkids && sh.cand[tid].tok == sh.st.argmax;
+      const uint64_t mm = __ballot(match);
+      if (tid == 0) sh.iscr[0] = mm ? sh.cand[__ffsll(static_cast<long long>(mm)) - 1].child : -1;
     }
   }
   __syncthreads();
@@ -1031,161 +1212,367 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     st.outcome = -1;
     st.next_child = 0;
     st.near = 0;
-    if (!kids) {
+    if (nkids == 0) {
       st.kind = kNodeLeaf;
     } else if (st.flags & EAGLE_FLAG_NONFINITE) {
       st.kind = kNodeRejected;
     } else if (greedy) {
-      st.kind = kNodeRejected;
-      for (int ch = n + 1; ch < T; ++ch)
-        if (sh.ti.par[ch] == n && a.tokens[b * T + ch] == st.argmax) {
-          st.kind = kNodeAccepted;
-          st.outcome = ch;
-          break;
-        }
+      st.outcome = sh.iscr[0];
+      st.kind = st.outcome >= 0 ? kNodeAccepted : kNodeRejected;
     } else {
-      const int child = kth_child(sh.ti, T, n, 0);
+      const Cand& cd = sh.cand[0];
       uint32_t fl = st.flags;
       int32_t nr = 0;
-      const int res = decide_child<TL>(a, b, n, child, 0, 0.0, 1.0, st, fl, nr);
+      const int res = decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, 0.0, 1.0, fl, nr);
       st.flags = fl;
       st.near = nr;
       if (res > 0) {
         st.kind = kNodeAccepted;
-        st.outcome = child;
+        st.outcome = cd.child;
       } else {
         st.C = 1.0;
         st.next_child = 1;
-        st.kind = (res == 0 && num_children(sh.ti, T, n) > 1) ? kNodeNeedsPass : kNodeRejected;
+        st.kind = (res == 0 && nkids > 1) ? kNodeNeedsPass : kNodeRejected;
       }
     }
     sh.st = st;
     if (lead) {
       store_state(&a.nodes[b * T + n], st);
-      publish(npub + n, base + (st.kind == kNodeNeedsPass ? 1u : kPubDone));
+      publish(npub, base + (st.kind == kNodeNeedsPass ? 1u : kPubDone));
     }
   }
   __syncthreads();
 
-  // ---- residual-mass rounds from LDS; partials double-buffered by round
+  // ---- residual-mass rounds from LDS
   const bool q_live = mq_c != kNegInf, p_live = two && mp_c != kNegInf;
+  const float mqs = q_live ? mq_c : 0.f, mps = p_live ? mp_c : 0.f;
   const double fq = q_live ? exp2((static_cast<double>(mq_c) - sh.st.mq) * static_cast<double>(a.c2)) / sh.st.zq : 0.0;
   const double fp = p_live ? exp2((static_cast<double>(mp_c) - sh.st.mp) * static_cast<double>(a.c2)) / sh.st.zp : 0.0;
-  // normalised probabilities of slot j (fp64)
-  auto qv = [&](int j) -> double {
-    return q_live ? static_cast<double>(exp2f((rq.get(j) - mq_c) * a.c2)) * fq : 0.0;
-  };
-  auto pv = [&](int j) -> double {
-    return p_live ? static_cast<double>(exp2f((rp.get(j) - mp_c) * a.c2)) * fp : 0.0;
-  };
+  uint64_t* const rwords = a.round_sum + (static_cast<int64_t>(b) * a.Tm + n) * kRoundWords;
   int round = 0;
   while (sh.st.kind == kNodeNeedsPass) {
-    const double C = sh.st.C;
-    double part = 0.0;
-#pragma unroll 4
-    for (int j = 0; j < kPerThread; ++j) part += fmax(0.0, qv(j) - C * pv(j));
+    double part, unused;
+    local_masses<TL, NV>(lq, lp, true, mqs, mps, a.c2, fq, fp, sh.st.C, part, unused);
     part = block_reduce(part, AddD{}, sh.dscr);
-    double* fbuf = a.fpart + (static_cast<int64_t>(round & 1) * a.B * T + b * T + n) * NC;
     if (tid == 0) {
-      st_f64(fbuf + c, part);
-      sh.ok = phase_barrier(narr + n, static_cast<uint32_t>(NC), limit) ? 1 : 0;
-    }
-    __syncthreads();
-    if (!sh.ok) return fail_internal();
-    double s = 0.0;
-    if (tid < 64) {
-      for (int q = tid; q < NC; q += 64) s += ld_f64(fbuf + q);
-      s = wave_reduce(s, AddD{});
-    }
-    if (tid == 0) {
+      const double pc = fmin(fmax(part, 0.0), 2.0);
+      const uint64_t add = (1ull << kCountShift) + static_cast<uint64_t>(__double2ull_rn(pc * kFixScale));
+      __hip_atomic_fetch_add(rwords + round, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      uint64_t w = poll(rwords + round);
+      uint32_t it = 0;
+      bool fine = true;
+      while ((w >> kCountShift) < static_cast<uint64_t>(NC)) {
+        if (++it > limit) {
+          fine = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w = poll(rwords + round);
+      }
+      sh.ok = fine ? 1 : 0;
       NodeState st = sh.st;
-      const int k = num_children(sh.ti, T, n);
       int i = st.next_child;
       double Cn = st.C;
+      double s = static_cast<double>(w & kSumMask) * kFixUnit;
       if (!(s > 0.0)) {
         st.flags |= EAGLE_FLAG_DEGENERATE_RESIDUAL;
         Cn = 0.0;
         s = 1.0;
       }
-      const int child = kth_child(sh.ti, T, n, i);
+      const Cand& cd = sh.cand[i];
       uint32_t fl = st.flags;
       int32_t nr = st.near;
-      const int res = decide_child<TL>(a, b, n, child, i, Cn, s, st, fl, nr);
+      const int res = decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, Cn, s, fl, nr);
       st.flags = fl;
       st.near = nr;
       if (res > 0) {
         st.kind = kNodeAccepted;
-        st.outcome = child;
+        st.outcome = cd.child;
       } else {
         Cn += s;
         ++i;
-        st.kind = (res == 0 && i < k) ? kNodeNeedsPass : kNodeRejected;
+        st.kind = (res == 0 && i < nkids) ? kNodeNeedsPass : kNodeRejected;
       }
       st.C = Cn;
       st.s = s;
       st.next_child = i;
       sh.st = st;
-      if (lead && st.kind != kNodeNeedsPass) {
+      if (fine && lead && st.kind != kNodeNeedsPass) {
         store_state(&a.nodes[b * T + n], st);
-        publish(npub + n, base + kPubDone);
+        publish(npub, base + kPubDone);
       }
     }
     __syncthreads();
+    if (!sh.ok) return fail_internal();
     ++round;
   }
 
-  // ---- is this node where the walk ends?
-  const bool poison_writer = (n == 0 && c == 0);
-  if (sh.st.kind == kNodeAccepted && !poison_writer) return;
-  // every node's statistics must be known (an unusable row poisons the sequence)
-  if (tid == 0) sh.seqflags = tokbad;
-  wait_all(npub, T, base + 1, limit, &sh.ok);
-  if (sh.ok && tid < T) {
-    const uint32_t f = static_cast<uint32_t>(ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + tid].flags)));
-    if (f & EAGLE_FLAG_NONFINITE) atomicOr(&sh.seqflags, EAGLE_FLAG_NONFINITE);
-  }
-  __syncthreads();
-  if (!sh.ok) return fail_internal();
-  if (sh.seqflags) {
-    if (poison_writer) write_poison(a, b, sh.seqflags);
-    return;
+  // ---- sequence verdict: workgroup 0 of the root waits for every node's
+  // first publication and publishes whether any row was unusable (then it
+  // also writes the poisoned outputs)
+  uint64_t* const verdict = a.seq_sync + static_cast<int64_t>(b) * kSyncWords + 1;
+  const bool master = (n == 0 && c == 0);
+  if (master) {
+    if (tid == 0) sh.seqflags = tokbad;
+    wait_all(nsync + 1, kSyncWords, T, base + 1, limit, &sh.ok);
+    if (sh.ok && tid < T) {
+      const uint32_t f = static_cast<uint32_t>(ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + tid].flags)));
+      if (f & EAGLE_FLAG_NONFINITE) atomicOr(&sh.seqflags, EAGLE_FLAG_NONFINITE);
+    }
+    __syncthreads();
+    if (!sh.ok) return fail_internal();
+    const uint32_t sf = sh.seqflags;
+    if (sf) write_poison(a, b, sf);
+    if (tid == 0) publish(verdict, base + (sf ? 2u : 1u));
+    if (sf) return;
   }
   if (sh.st.kind == kNodeAccepted) return;
-  // on the walk iff every ancestor accepted the next node of this root path
+  // an unusable row poisons the whole sequence: nothing to sample here
+  if (sh.st.flags & EAGLE_FLAG_NONFINITE) return;
+
+  // ---- is this node where the walk ends?  Yes iff every ancestor accepted
+  // the next node of this root path.  One thread polls the ancestors and
+  // gives up as soon as one of them decided otherwise.
   if (tid == 0) {
-    sh.iscr[0] = root_path(sh.ti, n, path_lds);
-    sh.onpath = 1;
-    sh.ok = 1;
-  }
-  __syncthreads();
-  const int plen = sh.iscr[0];
-  if (tid < plen - 1) {
-    const int anc = path_lds[tid];
+    const int pl = root_path(sh.ti, n, path_lds);
+    int on = 1, fine = 1;
+    uint64_t confirmed = 0;
     uint32_t it = 0;
-    while (poll(npub + anc) < base + kPubDone) {
+    for (;;) {
+      bool all = true;
+      for (int i = 0; i + 1 < pl && on; ++i) {
+        if ((confirmed >> i) & 1ull) continue;
+        const int anc = path_lds[i];
+        if (poll(nsync + anc * kSyncWords + 1) < base + kPubDone) {
+          all = false;
+          continue;
+        }
+        loads_after();
+        const uint64_t w = ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + anc].kind));
+        const int kind = static_cast<int>(static_cast<uint32_t>(w));
+        const int outc = static_cast<int>(static_cast<uint32_t>(w >> 32));
+        if (kind != kNodeAccepted || outc != path_lds[i + 1])
+          on = 0;
+        else
+          confirmed |= 1ull << i;
+      }
+      if (!on || all) break;
       if (++it > limit) {
-        sh.ok = 0;
+        fine = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(1);
+      __builtin_amdgcn_s_sleep(8);
     }
-    loads_after();
-    if (sh.ok) {
-      const uint64_t w = ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + anc].kind));
-      const int kind = static_cast<int>(static_cast<uint32_t>(w));
-      const int outc = static_cast<int>(static_cast<uint32_t>(w >> 32));
-      if (kind != kNodeAccepted || outc != path_lds[tid + 1]) sh.onpath = 0;
+    // the terminal node also needs the verdict on the whole sequence
+    if (on && fine) {
+      uint64_t v;
+      it = 0;
+      while ((v = poll(verdict)) < base + 1) {
+        if (++it > limit) {
+          fine = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (fine && v != base + 1) on = 0;   // poisoned: the root's workgroup wrote the outputs
     }
+    sh.iscr[0] = pl;
+    sh.onpath = on;
+    sh.ok = fine;
   }
   __syncthreads();
   if (!sh.ok) return fail_internal();
   if (!sh.onpath) return;
+  const int plen = sh.iscr[0];
   const int len = plen - 1;   // accepted draft nodes
+  if (greedy && c != 0) return;
+
+  // ---- terminal sample: inverse CDF of the residual max(0, q - C p) (of q
+  // at a leaf; of q again if the residual mass is zero).  Thread t owns the
+  // LDS slots [32t, 32t + 32), i.e. consecutive tokens.
+  int final_tok = sh.st.argmax;
+  uint32_t extra_flags = 0;
+  int extra_near = 0;
+  if (!greedy) {
+    const bool leaf = (sh.st.kind == kNodeLeaf);
+    const double Ct = leaf ? 0.0 : sh.st.C;
+    const int i0 = tid * kPerThread;
+    // weight of the token at LDS slot i0 + jj * G + e, from its two logits
+    const float qc = -mqs * a.c2, pc = -mps * a.c2;
+    const float Kt = fq > 0.0 ? static_cast<float>(Ct * fp / fq) : 0.f;
+    auto weight = [&](bool q_only, float xq, float xp) -> double {
+      const float eq = ex2(xq, a.c2, qc);
+      return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(xp, a.c2, pc), eq)));
+    };
+    // this thread's sums of the weights and of q
+    auto sums = [&](bool q_only, double& ts, double& tq) {
+      double wa[4] = {0.0, 0.0, 0.0, 0.0}, qa[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+      for (int jj = 0; jj < NV; ++jj) {
+        const u32x4_t gq = *reinterpret_cast<const u32x4_t*>(lq + i0 + jj * G);
+        const u32x4_t gp = q_only ? gq : *reinterpret_cast<const u32x4_t*>(lp + i0 + jj * G);
+        float fa[G], fb[G];
+        Pack<TL>::unpack(gq, fa);
+        Pack<TL>::unpack(gp, fb);
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          const float eq = ex2(fa[e], a.c2, qc);
+          qa[e & 3] += static_cast<double>(eq);
+          wa[e & 3] += static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(fb[e], a.c2, pc), eq)));
+        }
+      }
+      ts = ((wa[0] + wa[1]) + (wa[2] + wa[3])) * fq;
+      tq = ((qa[0] + qa[1]) + (qa[2] + qa[3])) * fq;
+    };
+    // block exclusive scan of the per-thread sums: this thread's starting
+    // offset inside the chunk and the chunk total
+    double chunk_total = 0.0;
+    auto scan_offsets = [&](double ts) -> double {
+      double incl = ts;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        if ((tid & 63) >= o) incl += y;
+      }
+      double excl = __shfl_up(incl, 1);
+      if ((tid & 63) == 0) excl = 0.0;
+      __syncthreads();
+      if ((tid & 63) == 63) sh.scan[tid >> 6] = incl;
+      __syncthreads();
+      double off = 0.0, tot = 0.0;
+#pragma unroll
+      for (int wv = 0; wv < kThreads / 64; ++wv) {
+        if (wv < (tid >> 6)) off += sh.scan[wv];
+        tot += sh.scan[wv];
+      }
+      chunk_total = tot;
+      return off + excl;
+    };
+    double ts, tq;
+    sums(leaf, ts, tq);
+    double offset = scan_offsets(ts);
+    double mqsum = block_reduce(tq, AddD{}, sh.dscr);
+    double* const sp = a.spart + (static_cast<int64_t>(b * T + n) * NC) * 2;
+    if (tid == 0) {
+      st_f64(&sp[2 * c], chunk_total);
+      st_f64(&sp[2 * c + 1], mqsum);
+      sh.ok = phase_barrier(narr, static_cast<uint32_t>(NC), limit) ? 1 : 0;
+    }
+    __syncthreads();
+    if (!sh.ok) return fail_internal();
+    // the chunk holding u * S (wave 0, one chunk per lane; same arithmetic
+    // in every workgroup of the node)
+    if (tid < 64) {
+      const double mr = (tid < NC) ? ld_f64(&sp[2 * tid]) : 0.0;
+      const double mq = (tid < NC) ? ld_f64(&sp[2 * tid + 1]) : 0.0;
+      const double sr = wave_reduce(mr, AddD{});
+      const bool degen = !(sr > 0.0);
+      const double m = degen ? mq : mr;
+      const double S = degen ? wave_reduce(mq, AddD{}) : sr;
+      const double thr = decision_uniform(a, b, n, kSampleSlot) * S;
+      double incl = m;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(incl, o);
+        if (tid >= o) incl += y;
+      }
+      const double excl = incl - m;
+      const uint64_t cross = __ballot(tid < NC && incl > thr);
+      // rounding: no crossing -> the last chunk with positive mass
+      const uint64_t pos = __ballot(tid < NC && m > 0.0);
+      const int cs_ = cross ? (__ffsll(static_cast<long long>(cross)) - 1) : (pos ? 63 - __clzll(static_cast<long long>(pos)) : 0);
+      const double run = __shfl(excl, cs_);
+      if (tid == 0) {
+        sh.sample[0] = run;
+        sh.sample[1] = S;
+        sh.sample[2] = thr;
+        sh.iscr[3] = cs_ | (degen ? 0x40000000 : 0);
+      }
+    }
+    __syncthreads();
+    const int cstar = sh.iscr[3] & 0x3FFFFFFF;
+    const bool degen = (sh.iscr[3] & 0x40000000) != 0;
+    if (c != cstar) return;
+    const double S = sh.sample[1], thr = sh.sample[2];
+    const bool q_only = leaf || degen;
+    if (degen && !leaf) {   // the residual vanished: sample q instead
+      sums(true, ts, tq);
+      offset = scan_offsets(ts);
+    }
+    // the smallest token whose running sum exceeds u*S.  The first thread
+    // whose range reaches u*S is found by a block minimum; wave 0 then
+    // scans that thread's 32 tokens one per lane.  A thread starting past
+    // u*S offers its first token (rounding hid the crossing just before it,
+    // which the near-tie test reports).
+    const double start = sh.sample[0] + offset;
+    if (tid == 0) sh.found = 0x7FFFFFFF;
+    __syncthreads();
+    if (start > thr || thr - start < ts * (1.0 + 1e-9)) atomicMin(&sh.found, tid);
+    __syncthreads();
+    const int tstar = sh.found;
+    if (tid == tstar) sh.sample[3] = start;
+    __syncthreads();
+    if (tid < 64) {
+      int hit = -1;
+      double lo = 0.0, hi = 0.0;
+      if (tstar != 0x7FFFFFFF) {
+        const double s0 = sh.sample[3];
+        const int t0 = tstar * kPerThread;
+        const int l = tid & 31;
+        const float xq = lds_logit<TL>(lq, t0 + l);
+        const float xp = q_only ? xq : lds_logit<TL>(lp, t0 + l);
+        const double w = (tid < 32) ? weight(q_only, xq, xp) : 0.0;
+        double incl = w;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) {
+          const double y = __shfl_up(incl, o);
+          if (l >= o) incl += y;
+        }
+        const double cum = s0 + incl;
+        const uint64_t over = __ballot(tid < 32 && (s0 > thr || cum > thr));
+        if (over) {
+          const int f = __ffsll(static_cast<long long>(over)) - 1;
+          hit = t0 + f;
+          hi = __shfl(cum, f);
+          lo = hi - __shfl(w, f);
+          if (s0 > thr) lo = hi = s0;
+        } else if (tstar + 1 < kThreads) {   // the crossing fell just past this thread
+          hit = t0 + kPerThread;
+          lo = hi = __shfl(cum, 31);
+        }
+      }
+      if (tid == 0) {
+        const bool ok = hit >= 0 && v0 + hit < v1;
+        sh.iscr[1] = ok ? hit : -1;
+        sh.iscr[2] = ok ? (((hi - thr) < kNearTie * S || (thr - lo) < kNearTie * S) ? 1 : 0) : 0;
+      }
+    }
+    __syncthreads();
+    if (sh.iscr[1] >= 0) {
+      extra_near = sh.iscr[2];
+      final_tok = v0 + sh.iscr[1];
+    } else {
+      // rounding left no crossing: the last token of the chunk with positive weight
+      int last = -1;
+#pragma unroll 1
+      for (int e = 0; e < kPerThread; ++e) {
+        const float xq = lds_logit<TL>(lq, i0 + e);
+        const float xp = q_only ? xq : lds_logit<TL>(lp, i0 + e);
+        if (v0 + i0 + e < v1 && weight(q_only, xq, xp) > 0.0) last = v0 + i0 + e;
+      }
+      if (tid == 0) sh.iscr[2] = -1;
+      __syncthreads();
+      atomicMax(&sh.iscr[2], last);
+      __syncthreads();
+      final_tok = sh.iscr[2];
+    }
+    extra_flags = degen ? EAGLE_FLAG_DEGENERATE_RESIDUAL : 0u;
+  }
 
   // flags and near ties along the path (ancestors from memory, this node from LDS)
   if (tid == 0) {
-    sh.seqflags = sh.st.flags;
-    sh.seqnear = sh.st.near;
+    sh.seqflags = sh.st.flags | extra_flags;
+    sh.seqnear = sh.st.near + extra_near;
   }
   __syncthreads();
   if (tid < plen - 1) {
@@ -1194,154 +1581,15 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     atomicAdd(&sh.seqnear, static_cast<int32_t>(static_cast<uint32_t>(w >> 32)));
   }
   __syncthreads();
-
-  auto write_outputs = [&](int final_tok, uint32_t extra_flags, int extra_near) {
-    if (tid == 0) {
-      a.accept_len[b] = len;
-      a.flags[b] = sh.seqflags | extra_flags;
-      a.near_ties[b] = sh.seqnear + extra_near;
-    }
-    for (int j = tid; j < T; j += kThreads) {
-      a.accepted_nodes[b * T + j] = (j < len) ? path_lds[j + 1] : -1;
-      a.out_tokens[b * T + j] = (j < len) ? a.tokens[b * T + path_lds[j + 1]] : (j == len ? final_tok : -1);
-    }
-  };
-
-  if (greedy) {
-    if (c == 0) write_outputs(sh.st.argmax, 0u, 0);
-    return;
-  }
-
-  // ---- terminal sample: chunk masses of the residual (and of q, used if the
-  // residual mass turns out to be zero)
-  const bool leaf = (sh.st.kind == kNodeLeaf);
-  const double Ct = leaf ? 0.0 : sh.st.C;
-  double mres = 0.0, mqs = 0.0;
-#pragma unroll 4
-  for (int j = 0; j < kPerThread; ++j) {
-    const double q = qv(j);
-    mqs += q;
-    mres += leaf ? q : fmax(0.0, q - Ct * pv(j));
-  }
-  mres = block_reduce(mres, AddD{}, sh.dscr);
-  mqs = block_reduce(mqs, AddD{}, sh.dscr);
   if (tid == 0) {
-    st_f64(&a.spart[(static_cast<int64_t>(b) * NC + c) * 2], mres);
-    st_f64(&a.spart[(static_cast<int64_t>(b) * NC + c) * 2 + 1], mqs);
-    sh.ok = phase_barrier(a.seq_arrive + b, static_cast<uint32_t>(NC), limit) ? 1 : 0;
+    a.accept_len[b] = len;
+    a.flags[b] = sh.seqflags;
+    a.near_ties[b] = sh.seqnear;
   }
-  __syncthreads();
-  if (!sh.ok) return fail_internal();
-  // every terminal workgroup: the chunk holding u * S (chunk order, same
-  // arithmetic everywhere)
-  for (int q = tid; q < NC; q += kThreads) {
-    sh.mass[2 * q] = ld_f64(&a.spart[(static_cast<int64_t>(b) * NC + q) * 2]);
-    sh.mass[2 * q + 1] = ld_f64(&a.spart[(static_cast<int64_t>(b) * NC + q) * 2 + 1]);
+  for (int j = tid; j < T; j += kThreads) {
+    a.accepted_nodes[b * T + j] = (j < len) ? path_lds[j + 1] : -1;
+    a.out_tokens[b * T + j] = (j < len) ? a.tokens[b * T + path_lds[j + 1]] : (j == len ? final_tok : -1);
   }
-  __syncthreads();
-  if (tid == 0) {
-    double sr = 0.0;
-    for (int q = 0; q < NC; ++q) sr += sh.mass[2 * q];
-    const bool degen = !(sr > 0.0);
-    const int col = degen ? 1 : 0;
-    double S = 0.0;
-    for (int q = 0; q < NC; ++q) S += sh.mass[2 * q + col];
-    const double u = decision_uniform(a, b, n, kSampleSlot);
-    const double thr = u * S;
-    int cstar = -1;
-    double run = 0.0;
-    for (int q = 0; q < NC; ++q) {
-      if (run + sh.mass[2 * q + col] > thr) {
-        cstar = q;
-        break;
-      }
-      run += sh.mass[2 * q + col];
-    }
-    if (cstar < 0) {     // rounding: the last chunk with positive mass
-      run = 0.0;
-      for (int q = 0; q < NC; ++q)
-        if (sh.mass[2 * q + col] > 0.0) cstar = q;
-      for (int q = 0; q < cstar; ++q) run += sh.mass[2 * q + col];
-    }
-    sh.sample[0] = run;
-    sh.sample[1] = S;
-    sh.sample[2] = thr;
-    sh.iscr[3] = cstar | (degen ? 0x40000000 : 0);
-  }
-  __syncthreads();
-  const int cstar = sh.iscr[3] & 0x3FFFFFFF;
-  const bool degen = (sh.iscr[3] & 0x40000000) != 0;
-  if (c != cstar) return;
-  const double S = sh.sample[1], thr = sh.sample[2];
-  double run = sh.sample[0];
-
-  // ---- scan this chunk's weights in token order, from registers
-  auto weight = [&](int j) -> double {
-    const double q = qv(j);
-    return (leaf || degen) ? q : fmax(0.0, q - Ct * pv(j));
-  };
-  if (tid == 0) sh.found = 0x7FFFFFFF;
-  int hit = 0x7FFFFFFF;
-  double hit_hi = 0.0, hit_lo = 0.0;
-  // token order = (group jj, thread, element e), G tokens per group
-  {
-    constexpr int GG = ChunkView<TL>::G;
-    for (int jj = 0; jj < kPerThread / GG; ++jj) {
-      double gs = 0.0;
-#pragma unroll
-      for (int e = 0; e < GG; ++e) gs += weight(jj * GG + e);
-      double incl = gs;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o);
-        if ((tid & 63) >= o) incl += y;
-      }
-      __syncthreads();
-      if ((tid & 63) == 63) sh.scan[tid >> 6] = incl;
-      __syncthreads();
-      double wave_off = 0.0, total = 0.0;
-#pragma unroll
-      for (int wv = 0; wv < kThreads / 64; ++wv) {
-        if (wv < (tid >> 6)) wave_off += sh.scan[wv];
-        total += sh.scan[wv];
-      }
-      double cum = run + wave_off + incl - gs;
-#pragma unroll
-      for (int e = 0; e < GG; ++e) {
-        const double before = cum;
-        cum += weight(jj * GG + e);
-        if (hit == 0x7FFFFFFF && cum > thr) {
-          hit = v0 + ChunkView<TL>::index(jj * GG + e);
-          hit_hi = cum;
-          hit_lo = before;
-        }
-      }
-      run += total;
-    }
-  }
-  atomicMin(&sh.found, hit);
-  __syncthreads();
-  int tok = sh.found;
-  int near = 0;
-  if (tok != 0x7FFFFFFF) {
-    if (hit == tok) sh.iscr[1] = ((hit_hi - thr) < kNearTie * S || (thr - hit_lo) < kNearTie * S) ? 1 : 0;
-    __syncthreads();
-    near = sh.iscr[1];
-  } else {
-    // rounding left no crossing: the last token of the chunk with positive weight
-    int lastpos = -1;
-#pragma unroll 4
-    for (int j = 0; j < kPerThread; ++j) {
-      const int t = v0 + ChunkView<TL>::index(j);
-      if (t < v1 && weight(j) > 0.0 && t > lastpos) lastpos = t;
-    }
-    if (tid == 0) sh.iscr[2] = -1;
-    __syncthreads();
-    atomicMax(&sh.iscr[2], lastpos);
-    __syncthreads();
-    tok = sh.iscr[2];
-  }
-  write_outputs(tok, degen ? EAGLE_FLAG_DEGENERATE_RESIDUAL : 0u, near);
 }
 
 template <typename TL>

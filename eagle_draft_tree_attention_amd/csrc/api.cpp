@@ -19,6 +19,8 @@ struct eagle_verify {
   hipStream_t last_stream = nullptr;
   bool used = false;
   uint64_t epoch = 0;          // acceptance calls issued on this handle
+  uint64_t fused_calls = 0;    // of which took the fused path
+  int last_fused_b = 0;        // batch of the last fused call (its round words need clearing)
   int fused_cap[2] = {0, 0};   // co-resident fused-acceptance workgroups (f32, bf16)
   char err[512] = {0};
 };
@@ -84,15 +86,16 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t o_fpart = off;
   off = align_up(off + sizeof(double) * 2 * B * T * NC, 256);   // two round buffers
   const size_t o_spart = off;
-  off = align_up(off + sizeof(double) * B * NC * 2, 256);
+  off = align_up(off + sizeof(double) * B * T * NC * 2, 256);
   const size_t o_cnt = off;
   const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
   off = align_up(off + cnt_bytes, 256);
   const size_t o_sync = off;
-  const size_t sync_bytes = sizeof(uint64_t) * (2 * B * T + 2 * B);
+  const size_t sync_bytes = sizeof(uint64_t) * ev::kSyncWords * (B * T + B);
   off = align_up(off + sync_bytes, 256);
-  const size_t o_sample = off;
-  off = align_up(off + sizeof(double) * 4 * B, 256);
+  const size_t o_round = off;
+  const size_t round_bytes = sizeof(uint64_t) * 2 * B * T * ev::kRoundWords;
+  off = align_up(off + round_bytes, 256);
 
   e = hipMalloc(&h->base, off);
   if (e != hipSuccess) {
@@ -107,15 +110,18 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.fpart = reinterpret_cast<double*>(p + o_fpart);
   h->ws.spart = reinterpret_cast<double*>(p + o_spart);
   h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
-  h->ws.sync = reinterpret_cast<uint64_t*>(p + o_sync);
-  h->ws.seq_sample = reinterpret_cast<double*>(p + o_sample);
+  h->ws.node_sync = reinterpret_cast<uint64_t*>(p + o_sync);
+  h->ws.seq_sync = h->ws.node_sync + ev::kSyncWords * B * T;
+  h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
   h->ws.bytes = off;
   h->fused_cap[0] = ev::fused_accept_capacity(0, h->num_cus);
   h->fused_cap[1] = ev::fused_accept_capacity(1, h->num_cus);
-  // counters start at zero; every call leaves them at zero again (the fused
-  // path's words are tagged with the call epoch instead)
+  // counters start at zero; every call leaves them at zero again.  On the
+  // fused path, arrival words only grow, publication words carry the call
+  // epoch, and each fused call clears the round words the previous one used.
   e = hipMemset(h->ws.counters, 0, cnt_bytes);
-  if (e == hipSuccess) e = hipMemset(h->ws.sync, 0, sync_bytes);
+  if (e == hipSuccess) e = hipMemset(h->ws.node_sync, 0, sync_bytes);
+  if (e == hipSuccess) e = hipMemset(h->ws.round_sum, 0, round_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.nodes, 0, sizeof(ev::NodeState) * B * T);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -221,20 +227,30 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   k.seed_hi = static_cast<uint32_t>(a->seed >> 32);
   k.off_lo = static_cast<uint32_t>(a->offset);
   k.off_hi = static_cast<uint32_t>(a->offset >> 32);
-  k.node_arrive = h->ws.sync;
-  k.node_pub = h->ws.sync + Bm * Tm;
-  k.seq_arrive = h->ws.sync + 2 * Bm * Tm;
-  k.seq_pub = h->ws.sync + 2 * Bm * Tm + Bm;
-  k.seq_sample = h->ws.seq_sample;
+  k.node_sync = h->ws.node_sync;
+  k.seq_sync = h->ws.seq_sync;
+  k.Tm = static_cast<int>(Tm);
   k.epoch = ++h->epoch;
   k.spin_limit = 1u << 20;
   const int64_t fused_wgs = static_cast<int64_t>(k.B) * k.T * k.NC;
   k.fused = (fused_wgs <= h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0] && k.NC <= 64) ? 1 : 0;
+  if (k.fused) {
+    // the two halves of the round words alternate between fused calls
+    const int64_t half = Bm * Tm * ev::kRoundWords;
+    const int parity = static_cast<int>(h->fused_calls & 1);
+    k.round_sum = h->ws.round_sum + parity * half;
+    k.round_clear = h->ws.round_sum + (1 - parity) * half;
+    k.zero_b = h->last_fused_b;
+  }
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
   h->last_stream = stream;
   h->used = true;
   if (e != 0) return hip_fail(h, "spec accept launch", e);
+  if (k.fused) {
+    ++h->fused_calls;
+    h->last_fused_b = k.B;
+  }
   h->err[0] = 0;
   return EAGLE_OK;
 }

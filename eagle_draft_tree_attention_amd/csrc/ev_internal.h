@@ -16,6 +16,8 @@ constexpr int kTileKeys = 64;        // keys per attention tile (one LDS stage)
 constexpr int kVocabChunk = 8192;    // vocabulary elements per acceptance workgroup
 constexpr int kDefaultCUs = 256;     // MI355X compute units (planning without a device)
 constexpr int64_t kAttnPartFloats = 32ll << 20;   // 128 MiB of split partials
+constexpr int kSyncWords = 32;       // 64-bit words per synchronisation line (256 bytes)
+constexpr int kRoundWords = kMaxTree;   // residual-mass rounds a node can need (< its children)
 
 // ---------------------------------------------------------------- attention
 struct AttnPlan {
@@ -88,17 +90,18 @@ struct AcceptKernelArgs {
   ChunkStat* stats;    // [B][T][2][NC]
   NodeState* nodes;    // [B][T]
   double* fpart;       // [B][T][NC]
-  double* spart;       // [B][NC][2]
+  double* spart;       // fused: [B][T][NC][2] chunk masses; three-kernel path: [B][NC]
   uint32_t* cnt_stats; // [B][T]
   uint32_t* cnt_pass;  // [B][T]
   uint32_t* cnt_final; // [B]
-  // fused path: per-node / per-sequence arrival words and publication words,
-  // tagged with the call epoch so they never need resetting
-  uint64_t* node_arrive;  // [B][T]
-  uint64_t* node_pub;     // [B][T]
-  uint64_t* seq_arrive;   // [B]
-  uint64_t* seq_pub;      // [B]
-  double* seq_sample;     // [B][4]: run, S, thr, (cstar | degenerate << 32) bits
+  // fused path.  Synchronisation words sit one per 256-byte line so that the
+  // memory-side atomics of different nodes never share a line.
+  uint64_t* node_sync;    // [Bm][Tm] lines: [0] arrivals (cumulative), [1] publication
+  uint64_t* seq_sync;     // [Bm] lines: [0] arrivals (cumulative)
+  uint64_t* round_sum;    // [Bm][Tm][kRoundWords]: (count << 57) | fixed-point residual mass
+  uint64_t* round_clear;  // the other half, used by the previous fused call; cleared here
+  int Tm;                 // node stride of node_sync and round_sum (max_tree_rows)
+  int zero_b;             // batch of the previous fused call (extent of round_clear to clear)
   uint64_t epoch;         // strictly increasing per call on a handle
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
   int fused;              // 1: one co-resident kernel; 0: three-kernel path
@@ -112,8 +115,9 @@ struct AcceptKernelArgs {
 
 // ---------------------------------------------------------------- host side
 struct Workspace {
-  uint64_t* sync = nullptr;     // node_arrive | node_pub | seq_arrive | seq_pub
-  double* seq_sample = nullptr;
+  uint64_t* node_sync = nullptr;
+  uint64_t* seq_sync = nullptr;
+  uint64_t* round_sum = nullptr;
   float* attn_part = nullptr;   // kAttnPartFloats
   ChunkStat* stats = nullptr;
   NodeState* nodes = nullptr;
