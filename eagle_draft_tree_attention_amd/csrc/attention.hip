@@ -46,6 +46,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleLog2 = 8.f;   // lazy softmax rescale threshold (log2 units)
 
 // Workgroups are handed to the 8 XCDs round-robin; renumber them so that
 // consecutive logical ids (the row tiles of one KV chunk) share an XCD and
@@ -262,29 +263,34 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
         tmax = fmaxf(tmax, fmaxf(fmaxf(sacc[kb][rb][0], sacc[kb][rb][1]), fmaxf(sacc[kb][rb][2], sacc[kb][rb][3])));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run[rb], tmax * c);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[rb] - m_use);
+      // The reference maximum of a row moves only when a score exceeds it by
+      // more than 2^kRescaleLog2 (P then stays below that, harmless in fp32
+      // and in the bf16 hi/lo pair), so most tiles skip the cross-lane
+      // maximum and the rescale of O.  The test is wave-uniform.
+      if (__any(tmax * c > m_run[rb] + kRescaleLog2)) {
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run[rb], tmax * c);
+        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
+        m_run[rb] = m_new;
+      }
+      const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
       float psum = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = exp2f(__builtin_fmaf(sacc[2 * ks + (e >> 2)][rb][e & 3], c, -m_use));
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * ks + (e >> 2)][rb][e & 3], c, -m_use));
           psum += pv;
           const __bf16 hi = (__bf16)pv;
           pb[rb][ks][e] = hi;
           pl[rb][ks][e] = (__bf16)(pv - (float)hi);
         }
       }
-      l_run[rb] = l_run[rb] * alpha + psum;
-      m_run[rb] = m_new;
-      if (alpha != 1.f) {
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
-      }
+      l_run[rb] += psum;
     }
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
