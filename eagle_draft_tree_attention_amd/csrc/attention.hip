@@ -104,23 +104,62 @@ __device__ __forceinline__ i16x4_t lds_read_tr16(const uint16_t* p) {
 
 // One (sequence, KV head, key split, row tile) per workgroup of 4 waves;
 // each wave owns MB blocks of 16 query rows.  Per 64-key tile:
-//   S^T[key][row] = K Q^T       16 (MB x 4 x D/32) v_mfma_f32_16x16x32_bf16
-//   online softmax per row      lane-local (lane % 16 = row), 2 cross-lane steps
+//   S^T[key][row] = K Q^T       MB x 4 x D/32 v_mfma_f32_16x16x32_bf16
+//   online softmax per row      lane-local (lane % 16 = row)
 //   O^T[d][row] += V^T P^T      with P split into bf16 hi + lo
 // Key k of block kb sits in S^T row 16*kb + (k%16); lane group lg = lane/16
 // holds keys 16*kb + 4*lg + i, which is exactly the k-slot order the PV
 // operands need (slots 0..3 from block 2*ks, 4..7 from block 2*ks+1).
-template <int D, int MB>
-__global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
+//
+// K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (lane l of an
+// instruction lands at LDS base + 16 l, so no registers are spent on
+// staging), through a ring of NST stages: the loads of tile t + NST - 1 are
+// issued while tile t is computed, and one barrier per tile both publishes
+// tile t and frees the stage tile t - 1 used.  Tiles are stored unpadded
+// with 16-byte chunks XOR-swizzled per row, so the K reads (16 rows, one
+// chunk column) and the transposing V reads (4 rows x 32 bytes per lane
+// group) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return 2 * (r & (D / 16 - 1)); }
+
+// wait until at most N of this wave's vector-memory operations are pending
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char*)(p)));
+}
+
+// 16 bytes per lane, global -> LDS at lds_base + 16 * lane (lds_base is
+// wave-uniform).  Written as inline assembly so that the compiler, which
+// cannot see which LDS bytes the transfer writes, does not make every later
+// LDS read wait for it: completion is awaited explicitly (wait_vmcnt) before
+// the barrier that publishes a tile.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int D, int MB, int NST>
+__global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a) {
   constexpr int KSTEPS = D / 32;          // QK^T contraction steps
   constexpr int DBLK = D / 16;            // output column blocks
-  constexpr int KSTRIDE = D + 8;          // K row in LDS: +16 B, 8-row reads hit distinct banks
-  constexpr int VSTRIDE = D + 16;         // V row in LDS: +32 B, 4-row transposed reads hit distinct banks
-  constexpr int DCH = D / 8;              // 16-byte chunks per row
-  constexpr int LOADS = kTileKeys * DCH / 256;   // per thread per tile, for K and for V
+  constexpr int CH = D / 8;               // 16-byte chunks per row
+  constexpr int TILE = kTileKeys * D;     // elements of one K or V tile
+  constexpr int RPI = 64 / CH;            // rows per 1 KB load instruction
+  constexpr int IPW = kTileKeys / RPI / 4;   // K (and V) load instructions per wave and tile
+  static_assert(IPW >= 1 && 2 * IPW * (NST - 1) < 64, "load geometry");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kTileKeys * KSTRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kTileKeys * VSTRIDE];
+  __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NST * 2 * TILE];
   __shared__ uint64_t anc_lds[kMaxTree];
   __shared__ int32_t par_lds[kMaxTree];
 
@@ -136,9 +175,94 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
   const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
   const int row_base = rt * a.rows_per_tile + wave * 16 * MB;   // lane rows: row_base + 16*rb + ln
 
+  const int64_t kv0 = a.kv_indptr[b];
+  const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)hk * D;
+  const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)hk * D;
+  const int64_t row_stride = (int64_t)a.Hkv * D;   // elements between consecutive KV rows
+  const int64_t last_row = a.num_kv_rows - 1;
+
+  const int k_begin = s_local * a.chunk;
+  const int k_end = min(k_begin + a.chunk, L);
+  const int n_prefix = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
+  const int n_full = (k_end - k_begin) / kTileKeys > 0 ? (k_end - k_begin) / kTileKeys : 0;   // unmasked tiles
+  const int n_tiles = n_prefix + (s_local == S - 1 ? 1 : 0);
+
+  // K/V tile t -> ring stage t % NST.  Full tiles of a split whose prefix
+  // rows all lie inside the KV array use precomputed per-lane offsets; any
+  // other tile repeats its last valid row past the key count (masked in the
+  // softmax) and clamps every row index into the array, so the loads stay in
+  // bounds even for a sequence that the validation below rejects.
+  const int l_row = lane / CH, l_pos = lane % CH;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds_kv = lds_offset(kv_lds);
+  // per-lane element offsets of this wave's transfer lanes inside a tile
+  // whose rows are all valid (row r of the tile = row0 + r)
+  uint32_t koff[IPW], voff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    const int r = (wave_u * IPW + j) * RPI + l_row;
+    koff[j] = static_cast<uint32_t>(r * row_stride + (l_pos ^ swz_k<D>(r)) * 8);
+    voff[j] = static_cast<uint32_t>(r * row_stride + (l_pos ^ swz_v<D>(r)) * 8);
+  }
+  // every prefix row of this split lies inside the KV array (checked once, so
+  // full tiles need no per-row clamping)
+  const bool split_in_bounds = kv0 >= 0 && kv0 + k_end <= a.num_kv_rows;
+  auto issue = [&](int t) {
+    const uint32_t kdst = lds_kv + static_cast<uint32_t>((t % NST) * 2 * TILE * 2);
+    const uint32_t vdst = kdst + TILE * 2;
+    if (t < n_full && split_in_bounds) {
+      const int64_t row0 = kv0 + k_begin + (int64_t)t * kTileKeys;
+      const uint16_t* kt = kbase + row0 * row_stride;
+      const uint16_t* vt = vbase + row0 * row_stride;
+#pragma unroll
+      for (int j = 0; j < IPW; ++j) {
+        const uint32_t ldsoff = static_cast<uint32_t>((wave_u * IPW + j) * RPI * D * 2);
+        lds_dma16(kt + koff[j], kdst + ldsoff);
+        lds_dma16(vt + voff[j], vdst + ldsoff);
+      }
+      return;
+    }
+    const bool tree = t >= n_prefix;
+    const int start = tree ? L : k_begin + t * kTileKeys;
+    const int cnt = tree ? T : min(kTileKeys, k_end - start);
+    const int64_t row0 = kv0 + start;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int r0 = (wave_u * IPW + j) * RPI;
+      const int r = r0 + l_row;
+      const int64_t gr = min(max(row0 + min(r, cnt - 1), (int64_t)0), last_row);
+      lds_dma16(kbase + gr * row_stride + (l_pos ^ swz_k<D>(r)) * 8, kdst + static_cast<uint32_t>(r0 * D * 2));
+      lds_dma16(vbase + gr * row_stride + (l_pos ^ swz_v<D>(r)) * 8, vdst + static_cast<uint32_t>(r0 * D * 2));
+    }
+  };
+  // the first tiles and the query rows are requested before the sequence is
+  // validated, so their latency overlaps the validation
+#pragma unroll
+  for (int j = 0; j < NST - 1; ++j)
+    if (j < n_tiles) issue(j);
+
+  // query rows -> B operands of S^T = K Q^T (zero for padding rows)
+  bool row_ok[MB];
+  int node[MB], head[MB];
+  bf16x8_t qf[MB][KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const int r = row_base + 16 * rb + ln;
+    row_ok[rb] = r < R;
+    node[rb] = row_ok[rb] ? r / g : 0;
+    head[rb] = hk * g + (row_ok[rb] ? r % g : 0);
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(b * T + node[rb]) * Hq + head[rb]) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const u32x4_t w = row_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * s) : u32x4_t{0, 0, 0, 0};
+      qf[rb][s] = __builtin_bit_cast(bf16x8_t, w);
+    }
+  }
+
   const uint32_t bad = validate_seq(a, b, lane, wave == 0 ? par_lds : nullptr);
   if (s_local == 0 && hk == 0 && rt == 0 && tid == 0) a.flags[b] = bad;
   if (bad) {
+    wait_vmcnt<0>();   // no transfer into LDS may outlive the workgroup
     if (S == 1) {
       for (int rb = 0; rb < MB; ++rb) {
         const int r = row_base + 16 * rb + ln;
@@ -153,33 +277,10 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
   }
   __syncthreads();
   if (tid < T) anc_lds[tid] = ancestors_of(par_lds, tid);
-  __syncthreads();
-
-  const int64_t kv0 = a.kv_indptr[b];
-  const int Hkv = a.Hkv;
-  const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)hk * D;
-  const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)hk * D;
-  const int64_t row_stride = (int64_t)Hkv * D;   // elements between consecutive KV rows
-
-  // query rows -> B operands of S^T = K Q^T (zero for padding rows)
-  bool row_ok[MB];
-  int node[MB], head[MB];
+  __syncthreads();   // ancestor words
   uint64_t anc_row[MB];
-  bf16x8_t qf[MB][KSTEPS];
 #pragma unroll
-  for (int rb = 0; rb < MB; ++rb) {
-    const int r = row_base + 16 * rb + ln;
-    row_ok[rb] = r < R;
-    node[rb] = row_ok[rb] ? r / g : 0;
-    head[rb] = hk * g + (row_ok[rb] ? r % g : 0);
-    anc_row[rb] = anc_lds[node[rb]];
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)(b * T + node[rb]) * Hq + head[rb]) * D + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const u32x4_t w = row_ok[rb] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * s) : u32x4_t{0, 0, 0, 0};
-      qf[rb][s] = __builtin_bit_cast(bf16x8_t, w);
-    }
-  }
+  for (int rb = 0; rb < MB; ++rb) anc_row[rb] = anc_lds[node[rb]];
 
   f32x4_t o[MB][DBLK];
   float m_run[MB], l_run[MB];
@@ -190,138 +291,156 @@ __global__ __launch_bounds__(256) void tree_attn_mfma(const AttnKernelArgs a) {
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-
-  const int k_begin = s_local * a.chunk;
-  const int k_end = min(k_begin + a.chunk, L);
-  const int n_prefix = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
-  const int n_full = (k_end - k_begin) / kTileKeys > 0 ? (k_end - k_begin) / kTileKeys : 0;   // unmasked tiles
-  const int n_tiles = n_prefix + (s_local == S - 1 ? 1 : 0);
   const float c = a.scale_log2;
 
-  // thread -> (row, 16-byte chunk) of the K and V tiles
-  int ld_row[LOADS], ld_chk[LOADS];
-#pragma unroll
-  for (int e = 0; e < LOADS; ++e) {
-    const int cidx = tid + 256 * e;
-    ld_row[e] = cidx / DCH;
-    ld_chk[e] = cidx % DCH;
-  }
-  u32x4_t kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int t) {
-    const bool tree = t >= n_prefix;
-    const int start = tree ? L : k_begin + t * kTileKeys;
-    const int cnt = tree ? T : min(kTileKeys, k_end - start);
-    const int64_t row0 = kv0 + start;
-#pragma unroll
-    for (int e = 0; e < LOADS; ++e) {
-      const int64_t row = row0 + min(ld_row[e], cnt - 1);   // rows past the tile repeat a valid row; masked later
-      kreg[e] = *reinterpret_cast<const u32x4_t*>(kbase + row * row_stride + ld_chk[e] * 8);
-      vreg[e] = *reinterpret_cast<const u32x4_t*>(vbase + row * row_stride + ld_chk[e] * 8);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int e = 0; e < LOADS; ++e) {
-      *reinterpret_cast<u32x4_t*>(k_lds + ld_row[e] * KSTRIDE + ld_chk[e] * 8) = kreg[e];
-      *reinterpret_cast<u32x4_t*>(v_lds + ld_row[e] * VSTRIDE + ld_chk[e] * 8) = vreg[e];
-    }
-  };
-
-  // one 64-key tile; MASK: partial prefix tile (key < cnt) or tree tile
-  // (key < T and key is an ancestor of the row's node)
-  auto tile = [&](auto mask_tag, bool is_tree, int cnt) {
+  // One 64-key tile from ring stage ST (a compile-time constant, so every LDS
+  // address below is a per-lane register plus an immediate).  MASK: partial
+  // prefix tile (key < cnt) or tree tile (key < T and key an ancestor of the
+  // row's node).  The tile is processed as two 32-key halves so that each
+  // wave always has independent matrix and vector work in flight:
+  //   QK(0) QK(1) | softmax(0) under QK(1) | PV(0) | softmax(1) under PV(0) | PV(1)
+  auto tile = [&](auto mask_tag, auto stage_tag, bool is_tree, int cnt) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int ST = decltype(stage_tag)::value;
+    const uint16_t* kst = kv_lds + ST * 2 * TILE;
+    const uint16_t* vst = kst + TILE;
     f32x4_t sacc[4][MB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) sacc[kb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* kp = k_lds + (16 * kb + ln) * KSTRIDE + 8 * lg;
+    // S^T for keys 32 h .. 32 h + 31 (key blocks 2h, 2h+1).  All K fragments
+    // of the half are read before the first product, and the contraction is
+    // split over two accumulators per block, so four independent MFMA chains
+    // are in flight.
+    auto qk = [&](auto h_tag) {
+      constexpr int H = decltype(h_tag)::value;
+      bf16x8_t kf[KSTEPS][2];
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kp + 32 * s);
+      for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
-          sacc[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[rb][s], sacc[kb][rb], 0, 0, 0);
-      }
-    }
-    bf16x8_t pb[MB][2], pl[MB][2];
+        for (int kk = 0; kk < 2; ++kk) {
+          const int r = 16 * (2 * H + kk) + ln;
+          kf[s][kk] = *reinterpret_cast<const bf16x8_t*>(kst + r * D + (((lg + 4 * s) ^ swz_k<D>(r)) * 8));
+        }
+      f32x4_t part[2][2][MB];
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-      if constexpr (MASK) {
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = 16 * kb + 4 * lg + i;
-            const bool valid = is_tree ? (key < T && ((anc_row[rb] >> key) & 1ull)) : (key < cnt);
-            sacc[kb][rb][i] = valid ? sacc[kb][rb][i] : kNegInf;
+          for (int rb = 0; rb < MB; ++rb) part[kk][pp][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb)
+            part[kk][s & 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s][kk], qf[rb][s], part[kk][s & 1][rb], 0, 0, 0);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) sacc[2 * H + kk][rb] = part[kk][0][rb] + part[kk][1][rb];
+    };
+    // P for the half: masks, lazy reference maximum, exp2, bf16 hi/lo pair
+    auto softmax = [&](auto h_tag, bf16x8_t (&pb)[MB], bf16x8_t (&pl)[MB]) {
+      constexpr int H = decltype(h_tag)::value;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) {
+        if constexpr (MASK) {
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = 16 * (2 * H + kk) + 4 * lg + i;
+              const bool valid = is_tree ? (key < T && ((anc_row[rb] >> key) & 1ull)) : (key < cnt);
+              sacc[2 * H + kk][rb][i] = valid ? sacc[2 * H + kk][rb][i] : kNegInf;
+            }
           }
         }
-      }
-      float tmax = kNegInf;
+        const f32x4_t s0 = sacc[2 * H][rb], s1 = sacc[2 * H + 1][rb];
+        float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        // The reference maximum of a row moves only when a score exceeds it
+        // by more than 2^kRescaleLog2 (P then stays below that, harmless in
+        // fp32 and in the bf16 hi/lo pair), so most halves skip the
+        // cross-lane maximum and the rescale of O.  The test is wave-uniform.
+        if (__any(tmax * c > m_run[rb] + kRescaleLog2)) {
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+          const float m_new = fmaxf(m_run[rb], tmax * c);
+          const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+          l_run[rb] *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        tmax = fmaxf(tmax, fmaxf(fmaxf(sacc[kb][rb][0], sacc[kb][rb][1]), fmaxf(sacc[kb][rb][2], sacc[kb][rb][3])));
-      // The reference maximum of a row moves only when a score exceeds it by
-      // more than 2^kRescaleLog2 (P then stays below that, harmless in fp32
-      // and in the bf16 hi/lo pair), so most tiles skip the cross-lane
-      // maximum and the rescale of O.  The test is wave-uniform.
-      if (__any(tmax * c > m_run[rb] + kRescaleLog2)) {
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run[rb], tmax * c);
-        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
-        m_run[rb] = m_new;
-      }
-      const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
-      float psum = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+          for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
+          m_run[rb] = m_new;
+        }
+        const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
+        float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * ks + (e >> 2)][rb][e & 3], c, -m_use));
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * H + (e >> 2)][rb][e & 3], c, -m_use));
           psum += pv;
           const __bf16 hi = (__bf16)pv;
-          pb[rb][ks][e] = hi;
-          pl[rb][ks][e] = (__bf16)(pv - (float)hi);
+          pb[rb][e] = hi;
+          pl[rb][e] = (__bf16)(pv - (float)hi);
         }
+        l_run[rb] += psum;
       }
-      l_run[rb] += psum;
-    }
+    };
+    // O^T += V^T P^T for keys 32 h .. 32 h + 31.  Lane (lg, ln) points the
+    // transposing read at key 32 h + 4 lg + ln/4 (and + 16), dims
+    // 16 db + 4 (ln % 4) .. + 3.
+    auto pv = [&](auto h_tag, const bf16x8_t (&pb)[MB], const bf16x8_t (&pl)[MB]) {
+      constexpr int H = decltype(h_tag)::value;
+      bf16x8_t va[DBLK];
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint16_t* vp = v_lds + (32 * ks + 4 * lg + (ln >> 2)) * VSTRIDE + 16 * db + 4 * (ln & 3);
+      for (int db = 0; db < DBLK; ++db) {
+        const int r = 32 * H + 4 * lg + (ln >> 2);
+        const int chunk = 2 * db + ((ln & 3) >> 1);
+        const uint16_t* vp = vst + r * D + ((chunk ^ swz_v<D>(r)) * 8) + 4 * (ln & 1);
         const i16x4_t lo4 = lds_read_tr16(vp);
-        const i16x4_t hi4 = lds_read_tr16(vp + 16 * VSTRIDE);
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb][ks], o[rb][db], 0, 0, 0);
-          o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl[rb][ks], o[rb][db], 0, 0, 0);
-        }
+        const i16x4_t hi4 = lds_read_tr16(vp + 16 * D);   // key + 16: same swizzle (r & 7 unchanged)
+        va[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    }
+      // hi products of every column block, then the lo products: the two
+      // MFMAs into one accumulator are DBLK instructions apart
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[rb], o[rb][db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[rb], o[rb][db], 0, 0, 0);
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    bf16x8_t pb0[MB], pl0[MB], pb1[MB], pl1[MB];
+    qk(H0{});
+    qk(H1{});
+    softmax(H0{}, pb0, pl0);
+    pv(H0{}, pb0, pl0);
+    softmax(H1{}, pb1, pl1);
+    pv(H1{}, pb1, pl1);
   };
 
-  if (n_tiles > 0) load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(t + 1);
+  auto step = [&](int t, auto stage_tag) {
+    // this wave's loads of tile t have landed
+    wait_vmcnt<0>();
+    __syncthreads();   // every wave's part of tile t is in LDS; the other stage is free
+    if (t + 1 < n_tiles) issue(t + 1);
     if (t < n_full) {
-      tile(std::integral_constant<bool, false>{}, false, kTileKeys);
+      tile(std::integral_constant<bool, false>{}, stage_tag, false, kTileKeys);
     } else {
       const bool is_tree = t >= n_prefix;
       const int cnt = is_tree ? T : min(kTileKeys, k_end - (k_begin + t * kTileKeys));
-      tile(std::integral_constant<bool, true>{}, is_tree, cnt);
+      tile(std::integral_constant<bool, true>{}, stage_tag, is_tree, cnt);
     }
+  };
+  static_assert(NST == 2, "the tile loop alternates two ring stages");
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue
@@ -453,62 +572,62 @@ __global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
 
 // ------------------------------------------------------------ LSE merge
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// One workgroup per (sequence, KV head, row tile, 16-row slice): 16 threads
-// per row, each owning D/16 output columns, so the S split partials of a row
-// are read in parallel across the chip.
+// One thread per (query row, 4 output columns); a block covers 256 / (D/4)
+// consecutive rows of one (sequence, KV head).  The splits are folded in
+// groups of 8 whose loads are all issued before any is used, with a running
+// maximum (one pass over the partials).  A sequence the split kernel found
+// invalid (its flags word, written by that kernel) gets NaN rows.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge(const AttnKernelArgs a) {
-  constexpr int CPT = D / 16;       // columns per thread
-  const int slices = (a.rows_per_tile + 15) / 16;
-  int logical = blockIdx.x;
-  const int slice = logical % slices;
-  logical /= slices;
-  const int rt = logical % a.row_tiles;
-  const int hk = (logical / a.row_tiles) % a.Hkv;
-  const int b = logical / (a.row_tiles * a.Hkv);
+  constexpr int CG = D / 4;          // column groups per row
+  constexpr int RPB = 256 / CG;      // rows per block
+  constexpr int GRP = 8;             // splits folded per group
+  const int R = a.R;
+  const int nrb = (R + RPB - 1) / RPB;
+  const int hk = (blockIdx.x / nrb) % a.Hkv;
+  const int b = blockIdx.x / (nrb * a.Hkv);
   const int base = a.split_base[b];
   const int S = a.split_base[b + 1] - base;
   if (S <= 1) return;
   const int tid = threadIdx.x;
-  const int T = a.T, g = a.g, R = a.R, Hq = a.Hq, rpt = a.rows_per_tile;
-  const int rl = slice * 16 + (tid >> 4);           // row within the tile
-  const int r = rt * rpt + rl;
-  __shared__ uint32_t bad_lds;
-  if (tid < 64) {
-    const uint32_t bad = validate_seq(a, b, tid, nullptr);
-    if (tid == 0) bad_lds = bad;
-  }
-  __syncthreads();
-  if (rl >= rpt || r >= R) return;
-  float* op = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + (tid & 15) * CPT;
-  if (bad_lds) {
-#pragma unroll
-    for (int c = 0; c < CPT; c += 4)
-      *reinterpret_cast<f32x4_t*>(op + c) = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
-                                                    __builtin_nanf("")};
-    return;
-  }
+  const int r = (blockIdx.x % nrb) * RPB + tid / CG;
+  const int cg = tid % CG;
+  if (r >= R) return;
+  const int T = a.T, g = a.g, Hq = a.Hq, rpt = a.rows_per_tile;
+  const uint32_t bad = a.flags[b];
+  float* op = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * cg;
+  const int rt = r / rpt, rl = r % rpt;
   const int64_t stride = (int64_t)a.Hkv * a.row_tiles * rpt;    // partial rows between splits
   const int64_t prow0 = ((int64_t)(base * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.mlpart[2 * (prow0 + s * stride)]);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  f32x4_t num[CPT / 4];
+  float M = kNegInf, den = 0.f;
+  f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += GRP) {
+    float m[GRP], l[GRP];
+    f32x4_t o[GRP];
 #pragma unroll
-  for (int c = 0; c < CPT / 4; ++c) num[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < S; ++s) {
-    const int64_t prow = prow0 + s * stride;
-    const float w = exp2f(a.mlpart[2 * prow] - Mu);
-    den += w * a.mlpart[2 * prow + 1];
-    const float* src = a.opart + prow * D + (tid & 15) * CPT;
+    for (int j = 0; j < GRP; ++j) {
+      const int64_t prow = prow0 + (int64_t)min(s0 + j, S - 1) * stride;
+      m[j] = (s0 + j < S) ? a.mlpart[2 * prow] : kNegInf;
+      l[j] = a.mlpart[2 * prow + 1];
+      o[j] = *reinterpret_cast<const f32x4_t*>(a.opart + prow * D + 4 * cg);
+    }
+    float Mn = M;
 #pragma unroll
-    for (int c = 0; c < CPT / 4; ++c) num[c] += w * *reinterpret_cast<const f32x4_t*>(src + 4 * c);
+    for (int j = 0; j < GRP; ++j) Mn = fmaxf(Mn, m[j]);
+    const float Mu = (Mn == kNegInf) ? 0.f : Mn;
+    const float sc = __builtin_amdgcn_exp2f(M - Mu);
+    den *= sc;
+    num *= sc;
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const float w = __builtin_amdgcn_exp2f(m[j] - Mu);
+      den += w * l[j];
+      num += w * o[j];
+    }
+    M = Mn;
   }
-  const float inv = 1.f / den;
-#pragma unroll
-  for (int c = 0; c < CPT / 4; ++c) *reinterpret_cast<f32x4_t*>(op + 4 * c) = num[c] * inv;
+  const float nan = __builtin_nanf("");
+  *reinterpret_cast<f32x4_t*>(op) = bad ? f32x4_t{nan, nan, nan, nan} : num * (1.f / den);
 }
 
 template <int D>
@@ -516,10 +635,8 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
   if (p.path == 1) {
     const dim3 grid((unsigned)p.workgroups), block(256);
     switch (p.mb) {
-      case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 1>), grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 2>), grid, block, 0, st, a); break;
-      case 3: hipLaunchKernelGGL((tree_attn_mfma<D, 3>), grid, block, 0, st, a); break;
-      case 4: hipLaunchKernelGGL((tree_attn_mfma<D, 4>), grid, block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2>), grid, block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -532,8 +649,9 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.merge_workgroups > 0) {
-    const unsigned slices = (unsigned)((p.rows_per_tile + 15) / 16);
-    hipLaunchKernelGGL((tree_attn_merge<D>), dim3((unsigned)p.merge_workgroups * slices), dim3(256), 0, st, a);
+    const unsigned rpb = 256 / (D / 4);
+    const unsigned nrb = (unsigned)((a.R + rpb - 1) / rpb);
+    hipLaunchKernelGGL((tree_attn_merge<D>), dim3((unsigned)(a.B * a.Hkv) * nrb), dim3(256), 0, st, a);
     e = hipGetLastError();
   }
   return e;

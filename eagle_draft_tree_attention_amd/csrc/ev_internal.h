@@ -23,7 +23,8 @@ constexpr int kRoundWords = kMaxTree;   // residual-mass rounds a node can need 
 struct AttnPlan {
   int path;            // 0 = FMA kernel (fp32, or bf16 with R < 16), 1 = MFMA kernel
   int R;               // rows per KV head = T * g
-  int mb;              // MFMA: 16-row blocks per wave (rows per workgroup = 64 * mb)
+  int mb;              // MFMA: 16-row blocks per wave (rows per workgroup = 64 * mb), 1 or 2
+  int stages;          // MFMA: K/V tiles in the LDS ring (2 or 3)
   int row_tiles;       // workgroups along R (FMA path: one row each)
   int rows_per_tile;
   int chunk;           // prefix keys per split (multiple of kTileKeys)

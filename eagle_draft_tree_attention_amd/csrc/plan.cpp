@@ -105,7 +105,8 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
     // One 16-row block per wave keeps the kernel at two waves per SIMD; the
     // row tiles of one KV chunk then share its K/V tiles through L2.
     const int mb_env = env_int("EAGLE_VERIFY_ATTN_MB", 1);
-    const int max_mb = mb_env > 4 ? 4 : (mb_env < 1 ? 1 : mb_env);
+    const int max_mb = mb_env > 2 ? 2 : (mb_env < 1 ? 1 : mb_env);
+    plan->stages = 2;
     int rt = static_cast<int>(ceil_div(R, 64 * max_mb));
     int rows = static_cast<int>(ceil_div(ceil_div(R, rt), 64) * 64);
     plan->row_tiles = rt;
