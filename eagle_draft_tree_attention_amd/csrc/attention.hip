@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ev_internal.h"
@@ -572,16 +573,20 @@ __global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
 
 // ------------------------------------------------------------ LSE merge
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// One thread per (query row, 4 output columns); a block covers 256 / (D/4)
-// consecutive rows of one (sequence, KV head).  The splits are folded in
-// groups of 8 whose loads are all issued before any is used, with a running
-// maximum (one pass over the partials).  A sequence the split kernel found
-// invalid (its flags word, written by that kernel) gets NaN rows.
-template <int D>
+// SPL adjacent lanes share one (query row, 4 output columns): lane sl folds
+// the splits sl, sl + SPL, ... in rounds of up to 8 whose loads are all
+// issued before any is used, then the SPL partial states are combined by
+// log-sum-exp over lane shuffles.  SPL is chosen from the largest split
+// count so that a lane needs at most two rounds.  A block covers
+// 256 / (SPL * D/4) query rows of one (sequence, KV head).  A sequence the
+// split kernel found invalid (its flags word, written by that kernel) gets
+// NaN rows.
+constexpr int kMergeRound = 8;   // splits folded per lane per load round
+
+template <int D, int SPL>
 __global__ __launch_bounds__(256) void tree_attn_merge(const AttnKernelArgs a) {
-  constexpr int CG = D / 4;          // column groups per row
-  constexpr int RPB = 256 / CG;      // rows per block
-  constexpr int GRP = 8;             // splits folded per group
+  constexpr int CG = D / 4;                  // column groups per row
+  constexpr int RPB = 256 / (CG * SPL);      // rows per block
   const int R = a.R;
   const int nrb = (R + RPB - 1) / RPB;
   const int hk = (blockIdx.x / nrb) % a.Hkv;
@@ -590,44 +595,76 @@ __global__ __launch_bounds__(256) void tree_attn_merge(const AttnKernelArgs a) {
   const int S = a.split_base[b + 1] - base;
   if (S <= 1) return;
   const int tid = threadIdx.x;
-  const int r = (blockIdx.x % nrb) * RPB + tid / CG;
-  const int cg = tid % CG;
-  if (r >= R) return;
+  const int sl = tid % SPL;
+  const int cg = (tid / SPL) % CG;
+  const int r = (blockIdx.x % nrb) * RPB + tid / (SPL * CG);
+  const bool live = r < R;                   // whole groups of SPL lanes agree
+  const int rr = live ? r : R - 1;
   const int T = a.T, g = a.g, Hq = a.Hq, rpt = a.rows_per_tile;
-  const uint32_t bad = a.flags[b];
-  float* op = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * cg;
-  const int rt = r / rpt, rl = r % rpt;
+  const int rt = rr / rpt, rl = rr % rpt;
   const int64_t stride = (int64_t)a.Hkv * a.row_tiles * rpt;    // partial rows between splits
   const int64_t prow0 = ((int64_t)(base * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
   float M = kNegInf, den = 0.f;
   f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += GRP) {
-    float m[GRP], l[GRP];
-    f32x4_t o[GRP];
+  for (int s0 = sl; s0 < S; s0 += SPL * kMergeRound) {
+    float m[kMergeRound], l[kMergeRound];
+    f32x4_t o[kMergeRound];
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const int64_t prow = prow0 + (int64_t)min(s0 + j, S - 1) * stride;
-      m[j] = (s0 + j < S) ? a.mlpart[2 * prow] : kNegInf;
-      l[j] = a.mlpart[2 * prow + 1];
-      o[j] = *reinterpret_cast<const f32x4_t*>(a.opart + prow * D + 4 * cg);
+    for (int j = 0; j < kMergeRound; ++j) {
+      const int sj = s0 + j * SPL;
+      m[j] = kNegInf;
+      l[j] = 0.f;
+      o[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (sj < S) {
+        const int64_t prow = prow0 + (int64_t)sj * stride;
+        m[j] = a.mlpart[2 * prow];
+        l[j] = a.mlpart[2 * prow + 1];
+        o[j] = *reinterpret_cast<const f32x4_t*>(a.opart + prow * D + 4 * cg);
+      }
     }
     float Mn = M;
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) Mn = fmaxf(Mn, m[j]);
+    for (int j = 0; j < kMergeRound; ++j) Mn = fmaxf(Mn, m[j]);
     const float Mu = (Mn == kNegInf) ? 0.f : Mn;
     const float sc = __builtin_amdgcn_exp2f(M - Mu);
     den *= sc;
     num *= sc;
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
+    for (int j = 0; j < kMergeRound; ++j) {
       const float w = __builtin_amdgcn_exp2f(m[j] - Mu);
       den += w * l[j];
       num += w * o[j];
     }
     M = Mn;
   }
+  // combine the SPL lanes' states
+#pragma unroll
+  for (int x = 1; x < SPL; x <<= 1) {
+    const float Mo = __shfl_xor(M, x);
+    const float Do = __shfl_xor(den, x);
+    f32x4_t No;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) No[i] = __shfl_xor(num[i], x);
+    const float Mn = fmaxf(M, Mo);
+    const float Mu = (Mn == kNegInf) ? 0.f : Mn;
+    const float ws = __builtin_amdgcn_exp2f(M - Mu), wo = __builtin_amdgcn_exp2f(Mo - Mu);
+    den = den * ws + Do * wo;
+    num = num * ws + No * wo;
+    M = Mn;
+  }
+  if (!live || sl != 0) return;
+  const uint32_t bad = a.flags[b];
   const float nan = __builtin_nanf("");
+  float* op = a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * cg;
   *reinterpret_cast<f32x4_t*>(op) = bad ? f32x4_t{nan, nan, nan, nan} : num * (1.f / den);
+}
+
+template <int D, int SPL>
+hipError_t launch_merge(const AttnKernelArgs& a, hipStream_t st) {
+  const unsigned rpb = 256 / ((D / 4) * SPL);
+  const unsigned nrb = (unsigned)((a.R + rpb - 1) / rpb);
+  hipLaunchKernelGGL((tree_attn_merge<D, SPL>), dim3((unsigned)(a.B * a.Hkv) * nrb), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -649,10 +686,17 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.merge_workgroups > 0) {
-    const unsigned rpb = 256 / (D / 4);
-    const unsigned nrb = (unsigned)((a.R + rpb - 1) / rpb);
-    hipLaunchKernelGGL((tree_attn_merge<D>), dim3((unsigned)(a.B * a.Hkv) * nrb), dim3(256), 0, st, a);
-    e = hipGetLastError();
+    int smax = 1;
+    for (int b = 0; b < a.B; ++b) smax = std::max(smax, a.split_base[b + 1] - a.split_base[b]);
+    // up to two load rounds per lane before lanes are added (measured best)
+    if (smax <= 2 * kMergeRound)
+      e = launch_merge<D, 1>(a, st);
+    else if (smax <= 4 * kMergeRound)
+      e = launch_merge<D, 2>(a, st);
+    else if (smax <= 8 * kMergeRound)
+      e = launch_merge<D, 4>(a, st);
+    else
+      e = launch_merge<D, 8>(a, st);
   }
   return e;
 }
