@@ -166,9 +166,12 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, ln = lane & 15;
   const int logical = xcd_remap(blockIdx.x, a.nwg);
+  // logical order: row tile fastest, then key split, then KV head, so the
+  // row tiles of one K/V chunk share an XCD's L2 and every XCD receives its
+  // share of the splits that carry the tree tile
   const int rt = logical % a.row_tiles;
-  const int hk = (logical / a.row_tiles) % a.Hkv;
-  const int split = logical / (a.row_tiles * a.Hkv);
+  const int split = (logical / a.row_tiles) % a.total_splits;
+  const int hk = logical / (a.row_tiles * a.total_splits);
   const int b = find_seq(a, split);
   const int s_local = split - a.split_base[b];
   const int S = a.split_base[b + 1] - a.split_base[b];
@@ -349,14 +352,15 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) {
         if constexpr (MASK) {
+          // visible keys of this row as a 64-bit word: the ancestor bits on
+          // the tree tile, the first cnt keys on a partial prefix tile
+          const uint64_t vis = is_tree ? anc_row[rb] : (cnt >= 64 ? ~0ull : ((1ull << cnt) - 1ull));
 #pragma unroll
           for (int kk = 0; kk < 2; ++kk) {
+            const uint32_t nib = static_cast<uint32_t>(vis >> (16 * (2 * H + kk) + 4 * lg)) & 0xFu;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = 16 * (2 * H + kk) + 4 * lg + i;
-              const bool valid = is_tree ? (key < T && ((anc_row[rb] >> key) & 1ull)) : (key < cnt);
-              sacc[2 * H + kk][rb][i] = valid ? sacc[2 * H + kk][rb][i] : kNegInf;
-            }
+            for (int i = 0; i < 4; ++i)
+              sacc[2 * H + kk][rb][i] = ((nib >> i) & 1u) ? sacc[2 * H + kk][rb][i] : kNegInf;
           }
         }
         const f32x4_t s0 = sacc[2 * H][rb], s1 = sacc[2 * H + 1][rb];
@@ -489,8 +493,8 @@ __global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
   const int logical = blockIdx.x;
   const int R = a.R;
   const int r = logical % R;
-  const int hk = (logical / R) % a.Hkv;
-  const int split = logical / (R * a.Hkv);
+  const int split = (logical / R) % a.total_splits;
+  const int hk = logical / (R * a.total_splits);
   const int b = find_seq(a, split);
   const int s_local = split - a.split_base[b];
   const int S = a.split_base[b + 1] - a.split_base[b];
@@ -602,8 +606,8 @@ __global__ __launch_bounds__(256) void tree_attn_merge(const AttnKernelArgs a) {
   const int rr = live ? r : R - 1;
   const int T = a.T, g = a.g, Hq = a.Hq, rpt = a.rows_per_tile;
   const int rt = rr / rpt, rl = rr % rpt;
-  const int64_t stride = (int64_t)a.Hkv * a.row_tiles * rpt;    // partial rows between splits
-  const int64_t prow0 = ((int64_t)(base * a.Hkv + hk) * a.row_tiles + rt) * rpt + rl;
+  const int64_t stride = (int64_t)a.row_tiles * rpt;    // partial rows between splits
+  const int64_t prow0 = ((int64_t)hk * a.total_splits + base) * stride + (int64_t)rt * rpt + rl;
   float M = kNegInf, den = 0.f;
   f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int s0 = sl; s0 < S; s0 += SPL * kMergeRound) {
