@@ -272,8 +272,14 @@ def main():
     step_s = ms_per_step * 1e-3
     attn_us = float(np.median(attn_ms) * 1e3)
     acc_us = float(np.median(acc_ms) * 1e3)
+    aplan = ver.last_attention_plan()
+    attn_kernels = "tree_attn_mfma" if aplan.path == 1 else "tree_attn_fma"
+    if aplan.merge_in_kernel:
+        attn_kernels += " with its split merge inside"
+    elif aplan.merge_workgroups > 0:
+        attn_kernels += " + tree_attn_merge"
     rooflines = {
-        "tree_attention": roofline("tree_attn_mfma + tree_attn_merge (one tree_attention call)",
+        "tree_attention": roofline(f"{attn_kernels} (one tree_attention call)",
                                    nb["attention_bytes"], float(attn_ms.mean()) * 1e-3),
         "spec_accept": roofline("sa_fused (one spec_accept call)", nb["accept_bytes"], float(acc_ms.mean()) * 1e-3),
     }

@@ -39,7 +39,7 @@ _abi.bind(_lib)
 from .verify import (  # noqa: E402,F401
     eagle_verify_create, eagle_verify_destroy, eagle_verify_tree_attention, eagle_verify_spec_accept,
     eagle_verify_last_error, eagle_verify_check_tree_attention, eagle_verify_check_spec_accept,
-    Verifier, make_desc,
+    eagle_verify_last_attention_plan, Verifier, make_desc,
 )
 
 

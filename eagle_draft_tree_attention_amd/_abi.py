@@ -18,7 +18,7 @@ STATUS_NAMES = {0: "EAGLE_OK", 1: "EAGLE_ERR_ARG", 2: "EAGLE_ERR_UNSUPPORTED", 3
 EXPORTED_SYMBOLS = (
     "eagle_verify_create", "eagle_verify_tree_attention", "eagle_verify_spec_accept",
     "eagle_verify_destroy", "eagle_verify_last_error", "eagle_verify_check_tree_attention",
-    "eagle_verify_check_spec_accept",
+    "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan",
 )
 
 
@@ -48,7 +48,7 @@ class SpecAcceptArgs(C.Structure):
 class AttentionPlan(C.Structure):
     _fields_ = [("path", C.c_int32), ("rows_per_kv_head", C.c_int32), ("row_tiles", C.c_int32),
                 ("rows_per_tile", C.c_int32), ("chunk_keys", C.c_int32), ("total_splits", C.c_int32),
-                ("workgroups", C.c_int32), ("merge_workgroups", C.c_int32)]
+                ("workgroups", C.c_int32), ("merge_workgroups", C.c_int32), ("merge_in_kernel", C.c_int32)]
 
 
 class EagleVerifyError(RuntimeError):
@@ -74,3 +74,5 @@ def bind(lib):
     lib.eagle_verify_check_tree_attention.restype = C.c_int
     lib.eagle_verify_check_spec_accept.argtypes = [C.POINTER(VerifyDesc), C.POINTER(SpecAcceptArgs)]
     lib.eagle_verify_check_spec_accept.restype = C.c_int
+    lib.eagle_verify_last_attention_plan.argtypes = [H, C.POINTER(AttentionPlan)]
+    lib.eagle_verify_last_attention_plan.restype = C.c_int

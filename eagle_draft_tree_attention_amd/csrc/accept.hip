@@ -40,6 +40,7 @@
 
 #include <type_traits>
 
+#include "ev_device.h"
 #include "ev_internal.h"
 
 namespace ev {
@@ -720,50 +721,13 @@ constexpr uint64_t kSumMask = (1ull << kCountShift) - 1;
 constexpr double kFixScale = 0x1p49;
 constexpr double kFixUnit = 0x1p-49;
 
-// Cross-workgroup traffic of the fused path.  The L2 caches of the XCDs are
-// not coherent with each other, and agent-scope release/acquire would write
-// back / invalidate a whole L2 per operation.  Instead every word that one
-// workgroup writes for another goes through system-scope relaxed atomics,
-// which bypass the non-coherent caches, and ordering comes from waiting for
-// the stores to complete before signalling.
-__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ double ld_f64(const double* p) {
-  return __builtin_bit_cast(double, ld_u64(reinterpret_cast<const uint64_t*>(p)));
-}
-__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ void st_f64(double* p, double v) { st_u64(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v)); }
-// this thread's earlier stores have completed (been acknowledged by the
-// coherent memory side) before anything that follows is issued
-__device__ __forceinline__ void stores_done() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-// later loads are not moved above the poll that allowed them
-__device__ __forceinline__ void loads_after() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
+// Cross-workgroup words of the fused path use the system-scope helpers of
+// ev_device.h (ld_u64, st_u64, stores_done, loads_after, poll, publish).
 __device__ void store_state(NodeState* dst, const NodeState& src) {
   const uint64_t* s = reinterpret_cast<const uint64_t*>(&src);
   uint64_t* d = reinterpret_cast<uint64_t*>(dst);
 #pragma unroll
   for (int i = 0; i < static_cast<int>(sizeof(NodeState) / 8); ++i) st_u64(d + i, s[i]);
-}
-
-__device__ __forceinline__ void publish(uint64_t* w, uint64_t v) {
-  stores_done();
-  __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-__device__ __forceinline__ uint64_t poll(const uint64_t* w) {
-  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Every thread t < count waits until w[t * stride] >= target; block-wide

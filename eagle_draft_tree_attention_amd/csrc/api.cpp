@@ -3,8 +3,10 @@
 // blocks, and launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -19,6 +21,10 @@ struct eagle_verify {
   hipStream_t last_stream = nullptr;
   bool used = false;
   uint64_t epoch = 0;          // acceptance calls issued on this handle
+  uint64_t attn_epoch = 0;     // attention calls issued on this handle
+  eagle_attention_plan last_plan{};         // of the last successful tree_attention call
+  bool have_plan = false;
+  int attn_cap[2][2] = {{0, 0}, {0, 0}};   // co-resident MFMA attention workgroups [D == 128][mb - 1]
   uint64_t fused_calls = 0;    // of which took the fused path
   int last_fused_b = 0;        // batch of the last fused call (its round words need clearing)
   int fused_cap[2] = {0, 0};   // co-resident fused-acceptance workgroups (f32, bf16)
@@ -42,6 +48,18 @@ eagle_status hip_fail(eagle_verify* h, const char* what, int code) {
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+void public_plan(const ev::AttnPlan& p, eagle_attention_plan* plan) {
+  plan->path = p.path;
+  plan->rows_per_kv_head = p.R;
+  plan->row_tiles = p.row_tiles;
+  plan->rows_per_tile = p.rows_per_tile;
+  plan->chunk_keys = p.chunk;
+  plan->total_splits = p.total_splits;
+  plan->workgroups = static_cast<int32_t>(p.workgroups);
+  plan->merge_workgroups = static_cast<int32_t>(p.merge_workgroups);
+  plan->merge_in_kernel = 0;
+}
 
 }  // namespace
 
@@ -93,6 +111,13 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t o_sync = off;
   const size_t sync_bytes = sizeof(uint64_t) * ev::kSyncWords * (B * T + B);
   off = align_up(off + sync_bytes, 256);
+  // attention split barriers: one line per (sequence, KV head, row tile)
+  const int64_t g_max = desc->num_q_heads / desc->num_kv_heads;
+  const int64_t rt_max = (T * g_max + 63) / 64;
+  const size_t unit_lines = static_cast<size_t>(B * desc->num_kv_heads * rt_max);
+  const size_t o_units = off;
+  const size_t unit_bytes = sizeof(uint64_t) * ev::kSyncWords * unit_lines;
+  off = align_up(off + unit_bytes, 256);
   const size_t o_round = off;
   const size_t round_bytes = sizeof(uint64_t) * 2 * B * T * ev::kRoundWords;
   off = align_up(off + round_bytes, 256);
@@ -113,15 +138,23 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.node_sync = reinterpret_cast<uint64_t*>(p + o_sync);
   h->ws.seq_sync = h->ws.node_sync + ev::kSyncWords * B * T;
   h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
+  h->ws.unit_sync = reinterpret_cast<uint64_t*>(p + o_units);
+  h->ws.unit_lines = unit_lines;
   h->ws.bytes = off;
   h->fused_cap[0] = ev::fused_accept_capacity(0, h->num_cus);
   h->fused_cap[1] = ev::fused_accept_capacity(1, h->num_cus);
+  // the in-kernel split merge can be switched off for comparison (EAGLE_VERIFY_ATTN_FUSED_MERGE=0)
+  const char* fm = std::getenv("EAGLE_VERIFY_ATTN_FUSED_MERGE");
+  if (desc->kv_dtype == EAGLE_BF16 && !(fm && fm[0] == '0'))
+    for (int mb = 1; mb <= 2; ++mb)
+      h->attn_cap[desc->head_dim == 128 ? 1 : 0][mb - 1] = ev::attention_capacity(desc->head_dim, mb, h->num_cus);
   // counters start at zero; every call leaves them at zero again.  On the
   // fused path, arrival words only grow, publication words carry the call
   // epoch, and each fused call clears the round words the previous one used.
   e = hipMemset(h->ws.counters, 0, cnt_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.node_sync, 0, sync_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.round_sum, 0, round_bytes);
+  if (e == hipSuccess) e = hipMemset(h->ws.unit_sync, 0, unit_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.nodes, 0, sizeof(ev::NodeState) * B * T);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -172,6 +205,21 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
     k.split_base[b] = plan.split_base[b];
   }
   k.split_base[a->batch] = plan.split_base[a->batch];
+  k.epoch = ++h->attn_epoch;
+  k.spin_limit = 1u << 20;
+  k.unit_sync = h->ws.unit_sync;
+  // the splits merge inside the kernel when every workgroup is resident at
+  // once (they wait for each other); otherwise a separate merge kernel runs
+  // once every workgroup has arrived, the weights of the rows a split merges
+  // (at most rows_per_tile + S - 1 (row, split) pairs) are staged in its K/V ring
+  int max_splits = 1;
+  for (int b = 0; b < a->batch; ++b) max_splits = std::max(max_splits, plan.split_base[b + 1] - plan.split_base[b]);
+  k.fused_merge = (plan.path == 1 && plan.merge_workgroups > 0 &&
+                   plan.workgroups <= h->attn_cap[k.D == 128 ? 1 : 0][plan.mb - 1] &&
+                   static_cast<size_t>(k.B) * k.Hkv * plan.row_tiles <= h->ws.unit_lines &&
+                   plan.rows_per_tile + max_splits <= ev::kFusedMergePairs)
+                      ? 1
+                      : 0;
   // the partials of one launch must fit: (O + m,l) per partial row
   const int64_t need = plan.workgroups * static_cast<int64_t>(plan.rows_per_tile) * (k.D + 2);
   if (plan.merge_workgroups > 0 && need > ev::kAttnPartFloats) {
@@ -183,6 +231,9 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
   h->last_stream = stream;
   h->used = true;
   if (e != 0) return hip_fail(h, "tree attention launch", e);
+  public_plan(plan, &h->last_plan);
+  h->last_plan.merge_in_kernel = k.fused_merge;
+  h->have_plan = true;
   h->err[0] = 0;
   return EAGLE_OK;
 }
@@ -277,17 +328,14 @@ eagle_status eagle_verify_check_tree_attention(const eagle_verify_desc* desc, co
   ev::AttnPlan p;
   eagle_status st = ev::plan_tree_attention(desc, a, ev::kDefaultCUs, &p, g_err, sizeof(g_err));
   if (st != EAGLE_OK) return st;
-  if (plan) {
-    plan->path = p.path;
-    plan->rows_per_kv_head = p.R;
-    plan->row_tiles = p.row_tiles;
-    plan->rows_per_tile = p.rows_per_tile;
-    plan->chunk_keys = p.chunk;
-    plan->total_splits = p.total_splits;
-    plan->workgroups = static_cast<int32_t>(p.workgroups);
-    plan->merge_workgroups = static_cast<int32_t>(p.merge_workgroups);
-  }
+  if (plan) public_plan(p, plan);
   g_err[0] = 0;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify_last_attention_plan(const eagle_verify* h, eagle_attention_plan* plan) {
+  if (!h || !plan || !h->have_plan) return EAGLE_ERR_ARG;
+  *plan = h->last_plan;
   return EAGLE_OK;
 }
 

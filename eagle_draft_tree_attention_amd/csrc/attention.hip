@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "ev_device.h"
 #include "ev_internal.h"
 
 namespace ev {
@@ -148,6 +149,13 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
                :
                : "v"(gptr), "s"(lds_base)
                : "memory", "m0");
+}
+
+// cache policy of partial results that workgroups on other XCDs read inside
+// the same launch: system-coherent (sc0 sc1), i.e. past the XCD's own L2
+constexpr int kSysCoherent = 1 | 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
 }
 
 template <int D, int MB, int NST>
@@ -267,7 +275,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   if (s_local == 0 && hk == 0 && rt == 0 && tid == 0) a.flags[b] = bad;
   if (bad) {
     wait_vmcnt<0>();   // no transfer into LDS may outlive the workgroup
-    if (S == 1) {
+    // NaN rows: written here when no separate merge follows (one split, or
+    // the merge is done inside this kernel: then split 0 writes its tile)
+    if (S == 1 || (a.fused_merge && s_local == 0)) {
       for (int rb = 0; rb < MB; ++rb) {
         const int r = row_base + 16 * rb + ln;
         if (r >= R) continue;
@@ -449,6 +459,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   }
 
   // epilogue
+  const bool fused = S > 1 && a.fused_merge;
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) {
     float l_tot = l_run[rb];
@@ -464,13 +475,132 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     } else {
       const int64_t prow = (int64_t)logical * a.rows_per_tile + (r - rt * a.rows_per_tile);
       float* op = a.opart + prow * D + 4 * lg;
+      const uint64_t ml = static_cast<uint64_t>(__float_as_uint(m_run[rb])) |
+                          (static_cast<uint64_t>(__float_as_uint(l_tot)) << 32);
+      if (fused) {   // read by workgroups on other XCDs: written through to memory
+        const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.opart);
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) *reinterpret_cast<f32x4_t*>(op + 16 * db) = o[rb][db];
-      if (lg == 0) {
-        a.mlpart[2 * prow] = m_run[rb];
-        a.mlpart[2 * prow + 1] = l_tot;
+        for (int db = 0; db < DBLK; ++db)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[rb][db]), prs,
+                                                 static_cast<int>((prow * D + 16 * db + 4 * lg) * 4), 0, kSysCoherent);
+        if (lg == 0) st_u64(reinterpret_cast<uint64_t*>(a.mlpart + 2 * prow), ml);
+      } else {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) *reinterpret_cast<f32x4_t*>(op + 16 * db) = o[rb][db];
+        if (lg == 0) *reinterpret_cast<uint64_t*>(a.mlpart + 2 * prow) = ml;
       }
     }
+  }
+  if (!fused) return;
+
+  // ---- the S splits of this (sequence, KV head, row tile) meet; then each
+  // merges its own slice of the tile's rows:
+  //   out = sum_s w_s O_s,  w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'
+  __shared__ int32_t sync_ok;
+  stores_done();
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t* line = a.unit_sync + ((int64_t)(b * a.Hkv + hk) * a.row_tiles + rt) * kSyncWords;
+    const uint64_t old = __hip_atomic_fetch_add(line, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    int fine = 1;
+    if (old == static_cast<uint64_t>(S - 1)) {   // last to arrive: reset for the next call, release
+      st_u64(line, 0ull);
+      publish(line + 1, a.epoch);
+    } else {
+      uint32_t it = 0;
+      while (poll(line + 1) < a.epoch) {
+        if (++it > a.spin_limit) {
+          fine = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    sync_ok = fine;
+  }
+  __syncthreads();
+  if (!sync_ok) {
+    if (tid == 0) atomicOr(&a.flags[b], EAGLE_FLAG_INTERNAL);
+    return;
+  }
+  loads_after();
+
+  constexpr int CG = D / 4;   // 4-column groups per row
+  const int rpt = a.rows_per_tile;
+  const int rps = (rpt + S - 1) / S;
+  const int r_lo = s_local * rps;
+  const int nr = min(min(r_lo + rps, rpt), R - rt * rpt) - r_lo;   // rows this split merges
+  if (nr <= 0) return;
+  const int64_t stride = (int64_t)a.row_tiles * rpt;   // partial rows between splits
+  const int64_t prow_lo = ((int64_t)hk * a.total_splits + a.split_base[b]) * stride + (int64_t)rt * rpt + r_lo;
+  const int np = nr * S;
+  // the K/V ring is free now: [0, 4 KB) lane partials, then m / weights
+  // [np] and l [np] (the host keeps 2 np floats within the ring)
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(kv_lds);
+  float* wsm = reinterpret_cast<float*>(kv_lds) + 1024;
+  for (int p = tid; p < np; p += 256) {
+    const int i = p / S, sj = p - i * S;
+    const uint64_t ml = ld_u64(reinterpret_cast<const uint64_t*>(a.mlpart + 2 * (prow_lo + i + sj * stride)));
+    wsm[p] = __uint_as_float(static_cast<uint32_t>(ml));
+    wsm[np + p] = __uint_as_float(static_cast<uint32_t>(ml >> 32));
+  }
+  __syncthreads();
+  for (int i = wave; i < nr; i += 4) {   // one wave per row
+    float* mw = wsm + i * S;
+    const float* lw = wsm + np + i * S;
+    float mx = kNegInf;
+    for (int sj = lane; sj < S; sj += 64) mx = fmaxf(mx, mw[sj]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
+    const float Mu = (mx == kNegInf) ? 0.f : mx;
+    float den = 0.f;
+    for (int sj = lane; sj < S; sj += 64) den += __builtin_amdgcn_exp2f(mw[sj] - Mu) * lw[sj];
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) den += __shfl_xor(den, x);
+    const float inv = 1.f / den;
+    for (int sj = lane; sj < S; sj += 64) mw[sj] = __builtin_amdgcn_exp2f(mw[sj] - Mu) * inv;
+  }
+  __syncthreads();
+  // weighted sum: item = (row, column group); spl lanes share an item and
+  // take the splits sl, sl + spl, ... in rounds of 8 loads issued together
+  const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.opart);
+  const int items = nr * CG;
+  const int spl = items >= 256 ? 1 : min(256 / items, S);
+  for (int t0 = 0; t0 < items * spl; t0 += 256) {
+    const int t = t0 + tid;
+    if (t >= items * spl) break;
+    const int item = t % items, sl = t / items;
+    const int i = item / CG, cg = item % CG;
+    const int boff = static_cast<int>(((prow_lo + i) * D + 4 * cg) * 4);
+    const int bstride = static_cast<int>(stride * D * 4);
+    f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = sl; s0 < S; s0 += 8 * spl) {
+      u32x4_t ov[8];
+      float wv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int sj = min(s0 + j * spl, S - 1);
+        ov[j] = __builtin_amdgcn_raw_buffer_load_b128(prs, boff + sj * bstride, 0, kSysCoherent);
+        wv[j] = (s0 + j * spl < S) ? wsm[i * S + sj] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += wv[j] * __builtin_bit_cast(f32x4_t, ov[j]);
+    }
+    if (spl == 1) {
+      const int r = rt * rpt + r_lo + i;
+      *reinterpret_cast<f32x4_t*>(a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * cg) = acc;
+    } else {
+      red[sl * items + item] = acc;
+    }
+  }
+  if (spl == 1) return;
+  __syncthreads();
+  if (tid < items) {
+    f32x4_t acc = red[tid];
+    for (int sl = 1; sl < spl; ++sl) acc += red[sl * items + tid];
+    const int i = tid / CG, cg = tid % CG;
+    const int r = rt * rpt + r_lo + i;
+    *reinterpret_cast<f32x4_t*>(a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * cg) = acc;
   }
 }
 
@@ -689,7 +819,7 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.merge_workgroups > 0) {
+  if (p.merge_workgroups > 0 && !a.fused_merge) {
     int smax = 1;
     for (int b = 0; b < a.B; ++b) smax = std::max(smax, a.split_base[b + 1] - a.split_base[b]);
     // up to two load rounds per lane before lanes are added (measured best)
@@ -706,6 +836,17 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
 }
 
 }  // namespace
+
+int attention_capacity(int D, int mb, int num_cus) {
+  int per_cu = 0;
+  const void* fn = nullptr;
+  if (D == 128)
+    fn = (mb == 2) ? reinterpret_cast<const void*>(&tree_attn_mfma<128, 2, 2>) : reinterpret_cast<const void*>(&tree_attn_mfma<128, 1, 2>);
+  else
+    fn = (mb == 2) ? reinterpret_cast<const void*>(&tree_attn_mfma<64, 2, 2>) : reinterpret_cast<const void*>(&tree_attn_mfma<64, 1, 2>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu <= 0) return 0;
+  return per_cu * num_cus;
+}
 
 int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int kv_bf16, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

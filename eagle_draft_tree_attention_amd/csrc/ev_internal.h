@@ -16,6 +16,9 @@ constexpr int kTileKeys = 64;        // keys per attention tile (one LDS stage)
 constexpr int kVocabChunk = 8192;    // vocabulary elements per acceptance workgroup
 constexpr int kDefaultCUs = 256;     // MI355X compute units (planning without a device)
 constexpr int64_t kAttnPartFloats = 32ll << 20;   // 128 MiB of split partials
+// (row, split) pairs whose merge weights fit in the smallest (D = 64) MFMA
+// K/V ring next to the 4 KB of lane partials: 2 floats per pair
+constexpr int kFusedMergePairs = (2 * 2 * 64 * 64 * 2 - 4096) / 8;
 constexpr int kSyncWords = 32;       // 64-bit words per synchronisation line (256 bytes)
 constexpr int kRoundWords = kMaxTree;   // residual-mass rounds a node can need (< its children)
 
@@ -51,6 +54,12 @@ struct AttnKernelArgs {
   int row_tiles, rows_per_tile, chunk, total_splits;
   int nwg;
   float scale_log2;    // sm_scale * log2(e)
+  // in-kernel merge (MFMA path, every workgroup co-resident): the splits of a
+  // (sequence, KV head, row tile) meet at a barrier and each merges a slice
+  int fused_merge;
+  uint32_t spin_limit; // bounded wait; an expired wait flags EAGLE_FLAG_INTERNAL
+  uint64_t epoch;      // strictly increasing per attention call on a handle
+  uint64_t* unit_sync; // [B][Hkv][row_tiles] lines of kSyncWords: [0] arrivals, [1] release
   int32_t L[kMaxBatch];
   int32_t split_base[kMaxBatch + 1];
 };
@@ -118,6 +127,8 @@ struct AcceptKernelArgs {
 struct Workspace {
   uint64_t* node_sync = nullptr;
   uint64_t* seq_sync = nullptr;
+  uint64_t* unit_sync = nullptr;   // attention split barriers
+  size_t unit_lines = 0;
   uint64_t* round_sum = nullptr;
   float* attn_part = nullptr;   // kAttnPartFloats
   ChunkStat* stats = nullptr;
@@ -143,5 +154,8 @@ int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stre
 // workgroups of the fused acceptance kernel that can be co-resident on the
 // device (0 if the query fails); the fused path is used when B*T*NC fits
 int fused_accept_capacity(int logits_bf16, int num_cus);
+// co-resident workgroups of the MFMA attention kernel for head_dim D and mb
+// 16-row blocks per wave (0 if the query fails)
+int attention_capacity(int D, int mb, int num_cus);
 
 }  // namespace ev

@@ -68,6 +68,13 @@ def eagle_verify_check_spec_accept(desc: VerifyDesc, args: SpecAcceptArgs) -> in
     return _lib().eagle_verify_check_spec_accept(C.byref(desc), C.byref(args))
 
 
+def eagle_verify_last_attention_plan(handle: int) -> AttentionPlan:
+    """Plan of the handle's last successful tree-attention call."""
+    plan = AttentionPlan()
+    _check(_lib().eagle_verify_last_attention_plan(handle, C.byref(plan)), handle)
+    return plan
+
+
 # ---------------------------------------------------------------- torch layer
 def _ptr(t):
     return None if t is None else int(t.data_ptr())
@@ -127,6 +134,9 @@ class Verifier:
         a, _keep = tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out, flags)
         eagle_verify_tree_attention(self.handle, a, _stream(stream))
         return out, flags
+
+    def last_attention_plan(self) -> AttentionPlan:
+        return eagle_verify_last_attention_plan(self.handle)
 
     def spec_accept(self, target, draft, parents, tokens, temperature, seed, offset, outputs=None,
                     stream=None):

@@ -108,7 +108,12 @@ typedef struct {
  *             prefix rows and the tree rows of the nodes on the root path of i
  *             (i included); query head h reads KV head h / (Hq/Hkv)
  *   flags     [B] uint32 (device)       EAGLE_FLAG_BAD_TREE | EAGLE_FLAG_BAD_KV_RANGE
- * Inputs are not modified.  Keys/values are read once from HBM per launch. */
+ * Inputs are not modified.  Keys/values are read once from HBM per launch.
+ * Long prefixes are split into key chunks whose partial results are merged by
+ * log-sum-exp; on the bf16 path the merge runs inside the attention kernel
+ * when all of its workgroups fit on the device at once (they then wait for
+ * each other), otherwise as a second kernel.  Calls on one handle must not
+ * overlap: they share the workspace. */
 typedef struct {
   int32_t batch;           /* B <= max_batch            */
   int32_t tree_rows;       /* T <= max_tree_rows, >= 1  */
@@ -175,7 +180,13 @@ typedef struct {
   int32_t chunk_keys;      /* prefix keys per split                              */
   int32_t total_splits;    /* sum over sequences of the split counts             */
   int32_t workgroups;      /* attention workgroups launched                      */
-  int32_t merge_workgroups;/* LSE-merge workgroups launched (0 = none)           */
+  int32_t merge_workgroups;/* workgroups of a separate LSE merge (0 = one split  *
+                            * per sequence); not launched when the merge runs   *
+                            * inside the attention kernel                       */
+  int32_t merge_in_kernel; /* 1: the splits merge inside the attention kernel.  *
+                            * Decided per call from the device's capacity, so   *
+                            * it is only known for a handle's last call; the    *
+                            * descriptor-only check reports 0                   */
 } eagle_attention_plan;
 
 /* Allocate a handle and its workspace on the current HIP device.
@@ -207,6 +218,11 @@ EAGLE_API eagle_status eagle_verify_check_tree_attention(const eagle_verify_desc
                                                eagle_attention_plan* plan);
 EAGLE_API eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* desc,
                                             const eagle_spec_accept_args* a);
+
+/* Launch plan of the last successful eagle_verify_tree_attention call on h
+ * (merge_in_kernel included).  No HIP call is made.
+ * Errors: EAGLE_ERR_ARG when h or plan is NULL or h has made no such call. */
+EAGLE_API eagle_status eagle_verify_last_attention_plan(const eagle_verify* h, eagle_attention_plan* plan);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,7 @@ def test_plan_for_the_workload_shapes():
     assert plan.chunk_keys % 64 == 0 and plan.total_splits == -(-8192 // plan.chunk_keys)
     assert plan.workgroups == plan.total_splits * 8 * 4
     assert plan.merge_workgroups == (8 * 4 if plan.total_splits > 1 else 0)
+    assert plan.merge_in_kernel == 0      # only a handle's call knows the device
     # 70B batch of four: R = 488 -> eight 64-row tiles per KV head
     a, keep = _attn_args(B=4, lens=(1024, 2048, 3072, 4096))
     st, plan = ev.eagle_verify_check_tree_attention(_desc(num_q_heads=64), a)
@@ -102,6 +103,14 @@ def _sa_args(**over):
     for k, v in over.items():
         setattr(a, k, v)
     return a
+
+
+def test_last_attention_plan_needs_a_call():
+    import ctypes as C
+    lib = ev.library()
+    plan = ev.verify.AttentionPlan()
+    assert lib.eagle_verify_last_attention_plan(None, C.byref(plan)) == ev.EAGLE_ERR_ARG
+    assert lib.eagle_verify_last_attention_plan(None, None) == ev.EAGLE_ERR_ARG
 
 
 def test_spec_accept_argument_errors():

@@ -55,6 +55,31 @@ def test_attention_matches_oracle(spec):
     ver.close()
 
 
+MERGE_CASES = [c for c in CASES if c.name in ("bf16_mb1_two_seqs", "bf16_two_row_tiles", "bf16_d64", "bf16_chain")]
+
+
+@pytest.mark.parametrize("spec", MERGE_CASES, ids=lambda s: s.name)
+def test_attention_separate_merge_kernel(spec, monkeypatch):
+    """The split merge as its own kernel (the path taken when the attention
+    workgroups cannot all be resident at once) against the oracle and
+    against the merge done inside the attention kernel."""
+    log(f"[attention] separate merge kernel: {spec.name}")
+    inp = synth.make_inputs(spec, with_logits=False)
+    ver = make_verifier(spec, inp.T)
+    fused, _ = run_attention(ver, inp)
+    plan = ver.last_attention_plan()
+    assert plan.total_splits > spec.batch and plan.merge_in_kernel == 1
+    ver.close()
+    monkeypatch.setenv("EAGLE_VERIFY_ATTN_FUSED_MERGE", "0")
+    ver = make_verifier(spec, inp.T)
+    got, flags = run_attention(ver, inp)
+    plan = ver.last_attention_plan()
+    assert plan.merge_in_kernel == 0 and plan.merge_workgroups > 0
+    ver.close()
+    _check(spec, inp, got, flags)
+    assert row_error(got, fused).max() <= ATTN_TOL[spec.dtype]
+
+
 def test_attention_tiny_config_exact():
     spec = synth.config_spec(0)
     log("[attention] tiny fp32 workload")
