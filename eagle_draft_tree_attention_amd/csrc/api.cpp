@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -111,13 +112,6 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t o_sync = off;
   const size_t sync_bytes = sizeof(uint64_t) * ev::kSyncWords * (B * T + B);
   off = align_up(off + sync_bytes, 256);
-  // attention split barriers: one line per (sequence, KV head, row tile)
-  const int64_t g_max = desc->num_q_heads / desc->num_kv_heads;
-  const int64_t rt_max = (T * g_max + 63) / 64;
-  const size_t unit_lines = static_cast<size_t>(B * desc->num_kv_heads * rt_max);
-  const size_t o_units = off;
-  const size_t unit_bytes = sizeof(uint64_t) * ev::kSyncWords * unit_lines;
-  off = align_up(off + unit_bytes, 256);
   const size_t o_round = off;
   const size_t round_bytes = sizeof(uint64_t) * 2 * B * T * ev::kRoundWords;
   off = align_up(off + round_bytes, 256);
@@ -138,8 +132,6 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.node_sync = reinterpret_cast<uint64_t*>(p + o_sync);
   h->ws.seq_sync = h->ws.node_sync + ev::kSyncWords * B * T;
   h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
-  h->ws.unit_sync = reinterpret_cast<uint64_t*>(p + o_units);
-  h->ws.unit_lines = unit_lines;
   h->ws.bytes = off;
   h->fused_cap[0] = ev::fused_accept_capacity(0, h->num_cus);
   h->fused_cap[1] = ev::fused_accept_capacity(1, h->num_cus);
@@ -151,10 +143,12 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   // counters start at zero; every call leaves them at zero again.  On the
   // fused path, arrival words only grow, publication words carry the call
   // epoch, and each fused call clears the round words the previous one used.
+  // The attention partials start at zero so that no tagged m/l word holds a
+  // call's epoch before that call writes it.
   e = hipMemset(h->ws.counters, 0, cnt_bytes);
+  if (e == hipSuccess) e = hipMemset(h->ws.attn_part, 0, sizeof(float) * static_cast<size_t>(ev::kAttnPartFloats));
   if (e == hipSuccess) e = hipMemset(h->ws.node_sync, 0, sync_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.round_sum, 0, round_bytes);
-  if (e == hipSuccess) e = hipMemset(h->ws.unit_sync, 0, unit_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.nodes, 0, sizeof(ev::NodeState) * B * T);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
@@ -205,9 +199,15 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
     k.split_base[b] = plan.split_base[b];
   }
   k.split_base[a->batch] = plan.split_base[a->batch];
+  int64_t packed = 0;
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t need = static_cast<int64_t>(a->prefix_lens_host[b]) + a->tree_rows;
+    k.kv0_guess[b] = (packed + need <= a->num_kv_rows && packed <= INT32_MAX) ? static_cast<int32_t>(packed) : -1;
+    packed += need;
+  }
   k.epoch = ++h->attn_epoch;
-  k.spin_limit = 1u << 20;
-  k.unit_sync = h->ws.unit_sync;
+  k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)
+  k.mlrec = reinterpret_cast<uint64_t*>(k.mlpart + 2 * plan.workgroups * static_cast<int64_t>(plan.rows_per_tile));
   // the splits merge inside the kernel when every workgroup is resident at
   // once (they wait for each other); otherwise a separate merge kernel runs
   // once every workgroup has arrived, the weights of the rows a split merges
@@ -216,12 +216,12 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
   for (int b = 0; b < a->batch; ++b) max_splits = std::max(max_splits, plan.split_base[b + 1] - plan.split_base[b]);
   k.fused_merge = (plan.path == 1 && plan.merge_workgroups > 0 &&
                    plan.workgroups <= h->attn_cap[k.D == 128 ? 1 : 0][plan.mb - 1] &&
-                   static_cast<size_t>(k.B) * k.Hkv * plan.row_tiles <= h->ws.unit_lines &&
                    plan.rows_per_tile + max_splits <= ev::kFusedMergePairs)
                       ? 1
                       : 0;
-  // the partials of one launch must fit: (O + m,l) per partial row
-  const int64_t need = plan.workgroups * static_cast<int64_t>(plan.rows_per_tile) * (k.D + 2);
+  // the partials of one launch must fit: O, (m, l) and the two tagged m/l
+  // words per partial row
+  const int64_t need = plan.workgroups * static_cast<int64_t>(plan.rows_per_tile) * (k.D + 6);
   if (plan.merge_workgroups > 0 && need > ev::kAttnPartFloats) {
     set_err(h, "split partials exceed the workspace");
     return EAGLE_ERR_CAPACITY;
@@ -282,7 +282,7 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   k.seq_sync = h->ws.seq_sync;
   k.Tm = static_cast<int>(Tm);
   k.epoch = ++h->epoch;
-  k.spin_limit = 1u << 20;
+  k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)
   const int64_t fused_wgs = static_cast<int64_t>(k.B) * k.T * k.NC;
   k.fused = (fused_wgs <= h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0] && k.NC <= 64) ? 1 : 0;
   if (k.fused) {

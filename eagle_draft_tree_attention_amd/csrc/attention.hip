@@ -67,6 +67,16 @@ __device__ __forceinline__ int find_seq(const AttnKernelArgs& a, int split) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// Flags of sequence b from values already loaded: p = parents[b][lane] (lane
+// < T), kv0/kv1 = kv_indptr[b], kv_indptr[b + 1].  All lanes of the wave
+// return the same word.
+__device__ __forceinline__ uint32_t seq_flags(const AttnKernelArgs& a, int b, int lane, int p, int64_t kv0, int64_t kv1) {
+  const bool ok = lane >= a.T || ((lane == 0) ? (p == -1) : (p >= 0 && p < lane));
+  uint32_t bad = __any(!ok) ? EAGLE_FLAG_BAD_TREE : 0u;
+  if (!(kv0 >= 0 && kv1 <= a.num_kv_rows && kv1 - kv0 >= (int64_t)a.L[b] + a.T)) bad |= EAGLE_FLAG_BAD_KV_RANGE;
+  return bad;
+}
+
 // Validate sequence b (parent array + KV range) using one wave's lanes; all
 // lanes return the same flag word.
 __device__ __forceinline__ uint32_t validate_seq(const AttnKernelArgs& a, int b, int lane, int32_t* par_out) {
@@ -187,7 +197,11 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
   const int row_base = rt * a.rows_per_tile + wave * 16 * MB;   // lane rows: row_base + 16*rb + ln
 
-  const int64_t kv0 = a.kv_indptr[b];
+  // The first tile is requested from the expected row offset of the
+  // sequence, without waiting for kv_indptr[b]; the parent array is requested
+  // before it, and nothing waits on either until the tile has landed.
+  const int par_lane = lane < T ? a.parents[b * T + lane] : 0;
+  int64_t kv0 = a.kv0_guess[b] >= 0 ? (int64_t)a.kv0_guess[b] : a.kv_indptr[b];
   const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)hk * D;
   const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)hk * D;
   const int64_t row_stride = (int64_t)a.Hkv * D;   // elements between consecutive KV rows
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   }
   // every prefix row of this split lies inside the KV array (checked once, so
   // full tiles need no per-row clamping)
-  const bool split_in_bounds = kv0 >= 0 && kv0 + k_end <= a.num_kv_rows;
+  bool split_in_bounds = kv0 >= 0 && kv0 + k_end <= a.num_kv_rows;
   auto issue = [&](int t) {
     const uint32_t kdst = lds_kv + static_cast<uint32_t>((t % NST) * 2 * TILE * 2);
     const uint32_t vdst = kdst + TILE * 2;
@@ -247,8 +261,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
       lds_dma16(vbase + gr * row_stride + (l_pos ^ swz_v<D>(r)) * 8, vdst + static_cast<uint32_t>(r0 * D * 2));
     }
   };
-  // the first tiles and the query rows are requested before the sequence is
-  // validated, so their latency overlaps the validation
+  // the first tile and the query rows are in flight together; the sequence
+  // is validated once they have landed
 #pragma unroll
   for (int j = 0; j < NST - 1; ++j)
     if (j < n_tiles) issue(j);
@@ -271,7 +285,18 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     }
   }
 
-  const uint32_t bad = validate_seq(a, b, lane, wave == 0 ? par_lds : nullptr);
+  const int64_t kv0_true = a.kv_indptr[b];
+  const int64_t kv1_true = a.kv_indptr[b + 1];
+  wait_vmcnt<0>();   // the first tile, the parents and the query rows have landed
+  if (kv0 != kv0_true) {   // the expected offset was wrong: request the first tile again
+    kv0 = kv0_true;
+    split_in_bounds = kv0 >= 0 && kv0 + k_end <= a.num_kv_rows;
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+      if (j < n_tiles) issue(j);
+  }
+  if (wave == 0 && lane < 64) par_lds[lane] = par_lane;
+  const uint32_t bad = seq_flags(a, b, lane, par_lane, kv0_true, kv1_true);
   if (s_local == 0 && hk == 0 && rt == 0 && tid == 0) a.flags[b] = bad;
   if (bad) {
     wait_vmcnt<0>();   // no transfer into LDS may outlive the workgroup
@@ -460,11 +485,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
 
   // epilogue
   const bool fused = S > 1 && a.fused_merge;
+  float l_fin[MB];
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) {
     float l_tot = l_run[rb];
     l_tot += __shfl_xor(l_tot, 16);
     l_tot += __shfl_xor(l_tot, 32);
+    l_fin[rb] = l_tot;
     const int r = row_base + 16 * rb + ln;
     if (!row_ok[rb]) continue;
     if (S == 1) {
@@ -475,55 +502,39 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     } else {
       const int64_t prow = (int64_t)logical * a.rows_per_tile + (r - rt * a.rows_per_tile);
       float* op = a.opart + prow * D + 4 * lg;
-      const uint64_t ml = static_cast<uint64_t>(__float_as_uint(m_run[rb])) |
-                          (static_cast<uint64_t>(__float_as_uint(l_tot)) << 32);
       if (fused) {   // read by workgroups on other XCDs: written through to memory
         const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.opart);
 #pragma unroll
         for (int db = 0; db < DBLK; ++db)
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o[rb][db]), prs,
                                                  static_cast<int>((prow * D + 16 * db + 4 * lg) * 4), 0, kSysCoherent);
-        if (lg == 0) st_u64(reinterpret_cast<uint64_t*>(a.mlpart + 2 * prow), ml);
       } else {
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) *reinterpret_cast<f32x4_t*>(op + 16 * db) = o[rb][db];
-        if (lg == 0) *reinterpret_cast<uint64_t*>(a.mlpart + 2 * prow) = ml;
+        if (lg == 0)
+          *reinterpret_cast<uint64_t*>(a.mlpart + 2 * prow) = static_cast<uint64_t>(__float_as_uint(m_run[rb])) |
+                                                              (static_cast<uint64_t>(__float_as_uint(l_tot)) << 32);
       }
     }
   }
   if (!fused) return;
 
-  // ---- the S splits of this (sequence, KV head, row tile) meet; then each
-  // merges its own slice of the tile's rows:
+  // ---- in-kernel merge.  Each partial row's m and l are published as two
+  // words tagged with the call's epoch, once the workgroup's partial O rows
+  // have reached memory.  Each split then merges its own slice of the tile's
+  // rows as soon as the words of all S splits for those rows carry the tag:
   //   out = sum_s w_s O_s,  w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'
-  __shared__ int32_t sync_ok;
+  const uint64_t tag = static_cast<uint64_t>(static_cast<uint32_t>(a.epoch)) << 32;
   stores_done();
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t* line = a.unit_sync + ((int64_t)(b * a.Hkv + hk) * a.row_tiles + rt) * kSyncWords;
-    const uint64_t old = __hip_atomic_fetch_add(line, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    int fine = 1;
-    if (old == static_cast<uint64_t>(S - 1)) {   // last to arrive: reset for the next call, release
-      st_u64(line, 0ull);
-      publish(line + 1, a.epoch);
-    } else {
-      uint32_t it = 0;
-      while (poll(line + 1) < a.epoch) {
-        if (++it > a.spin_limit) {
-          fine = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
-    sync_ok = fine;
+  __syncthreads();   // every wave's partial O rows are in memory
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) {
+    const int r = row_base + 16 * rb + ln;
+    if (!row_ok[rb] || lg != 0) continue;
+    uint64_t* rec = a.mlrec + 2 * ((int64_t)logical * a.rows_per_tile + (r - rt * a.rows_per_tile));
+    st_u64(rec, tag | __float_as_uint(m_run[rb]));
+    st_u64(rec + 1, tag | __float_as_uint(l_fin[rb]));
   }
-  __syncthreads();
-  if (!sync_ok) {
-    if (tid == 0) atomicOr(&a.flags[b], EAGLE_FLAG_INTERNAL);
-    return;
-  }
-  loads_after();
 
   constexpr int CG = D / 4;   // 4-column groups per row
   const int rpt = a.rows_per_tile;
@@ -538,11 +549,43 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   // [np] and l [np] (the host keeps 2 np floats within the ring)
   f32x4_t* red = reinterpret_cast<f32x4_t*>(kv_lds);
   float* wsm = reinterpret_cast<float*>(kv_lds) + 1024;
-  for (int p = tid; p < np; p += 256) {
-    const int i = p / S, sj = p - i * S;
-    const uint64_t ml = ld_u64(reinterpret_cast<const uint64_t*>(a.mlpart + 2 * (prow_lo + i + sj * stride)));
-    wsm[p] = __uint_as_float(static_cast<uint32_t>(ml));
-    wsm[np + p] = __uint_as_float(static_cast<uint32_t>(ml >> 32));
+  for (uint32_t it = 0;; ++it) {
+    int ready = 1;
+    for (int p = tid; p < np; p += 256) {
+      const int i = p / S, sj = p - i * S;
+      const uint64_t* rec = a.mlrec + 2 * (prow_lo + i + (int64_t)sj * stride);
+      const uint64_t wm = ld_u64(rec), wl = ld_u64(rec + 1);
+      if ((wm & ~0xffffffffull) != tag || (wl & ~0xffffffffull) != tag) ready = 0;
+      wsm[p] = __uint_as_float(static_cast<uint32_t>(wm));
+      wsm[np + p] = __uint_as_float(static_cast<uint32_t>(wl));
+    }
+    if (__syncthreads_and(ready)) break;
+    if (it >= a.spin_limit) {
+      if (tid == 0) atomicOr(&a.flags[b], EAGLE_FLAG_INTERNAL);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  loads_after();
+  // weighted sum: slot = (row, column group, split lane); spl lanes share a
+  // (row, column group) and take the splits sl, sl + spl, ... in rounds of
+  // 8 loads issued together.  A thread's first round is requested before
+  // the weights are formed.
+  const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.opart);
+  const int items = nr * CG;
+  const int spl = items >= 256 ? 1 : min(256 / items, S);
+  const int slots = items * spl;
+  const int bstride = static_cast<int>(stride * D * 4);
+  u32x4_t ov[8];
+  auto load_round = [&](int i, int cg, int s0) {
+    const int boff = static_cast<int>(((prow_lo + i) * D + 4 * cg) * 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ov[j] = __builtin_amdgcn_raw_buffer_load_b128(prs, boff + min(s0 + j * spl, S - 1) * bstride, 0, kSysCoherent);
+  };
+  if (tid < slots) {
+    const int item = tid % items;
+    load_round(item / CG, item % CG, tid / items);
   }
   __syncthreads();
   for (int i = wave; i < nr; i += 4) {   // one wave per row
@@ -561,30 +604,17 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     for (int sj = lane; sj < S; sj += 64) mw[sj] = __builtin_amdgcn_exp2f(mw[sj] - Mu) * inv;
   }
   __syncthreads();
-  // weighted sum: item = (row, column group); spl lanes share an item and
-  // take the splits sl, sl + spl, ... in rounds of 8 loads issued together
-  const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.opart);
-  const int items = nr * CG;
-  const int spl = items >= 256 ? 1 : min(256 / items, S);
-  for (int t0 = 0; t0 < items * spl; t0 += 256) {
-    const int t = t0 + tid;
-    if (t >= items * spl) break;
+  for (int t = tid; t < slots; t += 256) {
     const int item = t % items, sl = t / items;
     const int i = item / CG, cg = item % CG;
-    const int boff = static_cast<int>(((prow_lo + i) * D + 4 * cg) * 4);
-    const int bstride = static_cast<int>(stride * D * 4);
     f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int s0 = sl; s0 < S; s0 += 8 * spl) {
-      u32x4_t ov[8];
-      float wv[8];
+      if (t != tid || s0 != sl) load_round(i, cg, s0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int sj = min(s0 + j * spl, S - 1);
-        ov[j] = __builtin_amdgcn_raw_buffer_load_b128(prs, boff + sj * bstride, 0, kSysCoherent);
-        wv[j] = (s0 + j * spl < S) ? wsm[i * S + sj] : 0.f;
+        const float w = (s0 + j * spl < S) ? wsm[i * S + s0 + j * spl] : 0.f;
+        acc += w * __builtin_bit_cast(f32x4_t, ov[j]);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc += wv[j] * __builtin_bit_cast(f32x4_t, ov[j]);
     }
     if (spl == 1) {
       const int r = rt * rpt + r_lo + i;

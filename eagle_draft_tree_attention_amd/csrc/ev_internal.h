@@ -54,14 +54,20 @@ struct AttnKernelArgs {
   int row_tiles, rows_per_tile, chunk, total_splits;
   int nwg;
   float scale_log2;    // sm_scale * log2(e)
-  // in-kernel merge (MFMA path, every workgroup co-resident): the splits of a
-  // (sequence, KV head, row tile) meet at a barrier and each merges a slice
+  // in-kernel merge (MFMA path, every workgroup co-resident): each split of a
+  // (sequence, KV head, row tile) merges a slice of its rows once every
+  // split has published the tagged m/l words of those rows
   int fused_merge;
-  uint32_t spin_limit; // bounded wait; an expired wait flags EAGLE_FLAG_INTERNAL
-  uint64_t epoch;      // strictly increasing per attention call on a handle
-  uint64_t* unit_sync; // [B][Hkv][row_tiles] lines of kSyncWords: [0] arrivals, [1] release
+  uint32_t spin_limit; // polls of the bounded wait; an expired wait flags EAGLE_FLAG_INTERNAL
+  uint64_t epoch;      // strictly increasing per attention call on a handle (tags use its low 32 bits)
+  uint64_t* mlrec;      // [slot][rows_per_tile][2]: m and l (low 32 bits), epoch tag (high 32 bits)
   int32_t L[kMaxBatch];
   int32_t split_base[kMaxBatch + 1];
+  // expected kv_indptr[b] (rows packed back to back, L_b + T per sequence),
+  // -1 when it does not fit 31 bits or the array: the MFMA kernel requests
+  // its first tile from there before kv_indptr[b] arrives, and fetches the
+  // tile again if the guess was wrong
+  int32_t kv0_guess[kMaxBatch];
 };
 
 // ---------------------------------------------------------------- acceptance
@@ -127,8 +133,6 @@ struct AcceptKernelArgs {
 struct Workspace {
   uint64_t* node_sync = nullptr;
   uint64_t* seq_sync = nullptr;
-  uint64_t* unit_sync = nullptr;   // attention split barriers
-  size_t unit_lines = 0;
   uint64_t* round_sum = nullptr;
   float* attn_part = nullptr;   // kAttnPartFloats
   ChunkStat* stats = nullptr;

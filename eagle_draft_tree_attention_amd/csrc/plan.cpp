@@ -142,7 +142,7 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
     }
     plan->split_base[B] = static_cast<int32_t>(splits);
     // partial slots are indexed by workgroup, so all of them are reserved
-    if (any_multi) part = splits * units * plan->rows_per_tile * (D + 2);
+    if (any_multi) part = splits * units * plan->rows_per_tile * (D + 6);
     if (part <= kAttnPartFloats && splits < (1ll << 30)) {
       plan->total_splits = static_cast<int>(splits);
       plan->part_floats = part;

@@ -80,6 +80,40 @@ def test_attention_separate_merge_kernel(spec, monkeypatch):
     assert row_error(got, fused).max() <= ATTN_TOL[spec.dtype]
 
 
+def _with_gaps(inp, gap):
+    """The same sequences with `gap` unused rows before each KV block (filled
+    with large values that a wrong row offset would pick up)."""
+    import dataclasses
+    B = inp.spec.batch
+    sizes = np.diff(inp.kv_indptr)
+    k = np.empty((int(sizes.sum()) + gap * B,) + inp.k.shape[1:], dtype=inp.k.dtype)
+    v = np.empty_like(k)
+    k[:] = synth.to_bf16_bits(np.float64(300.0)) if inp.k.dtype == np.uint16 else np.float32(300.0)
+    v[:] = k
+    ind = np.zeros(B + 1, dtype=np.int64)
+    for b in range(B):
+        start = int(ind[b]) + gap
+        k[start:start + sizes[b]] = inp.k[inp.kv_indptr[b]:inp.kv_indptr[b + 1]]
+        v[start:start + sizes[b]] = inp.v[inp.kv_indptr[b]:inp.kv_indptr[b + 1]]
+        ind[b] = start
+        ind[b + 1] = start + sizes[b]
+    return dataclasses.replace(inp, k=k, v=v, kv_indptr=ind)
+
+
+def test_attention_unpacked_kv_layout():
+    """KV blocks that are not packed back to back: the first tile, requested
+    early from the packed offset, is requested again from kv_indptr."""
+    spec = small_spec("unpacked", B=3, Hq=8, Hkv=2, lens=(700, 64, 300), levels=(4, 6, 10))
+    log("[attention] unpacked KV layout")
+    inp = synth.make_inputs(spec, with_logits=False)
+    moved = _with_gaps(inp, gap=37)
+    ver = make_verifier(spec, inp.T)
+    got, flags = run_attention(ver, moved)
+    ver.close()
+    _check(spec, moved, got, flags)
+    assert np.array_equal(flags, np.zeros(3, dtype=np.uint32))
+
+
 def test_attention_tiny_config_exact():
     spec = synth.config_spec(0)
     log("[attention] tiny fp32 workload")
