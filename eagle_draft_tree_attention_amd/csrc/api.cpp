@@ -25,7 +25,7 @@ struct eagle_verify {
   uint64_t attn_epoch = 0;     // attention calls issued on this handle
   eagle_attention_plan last_plan{};         // of the last successful tree_attention call
   bool have_plan = false;
-  int attn_cap[2][2] = {{0, 0}, {0, 0}};   // co-resident MFMA attention workgroups [D == 128][mb - 1]
+  int attn_cap[2][ev::kMfmaVariants] = {};   // co-resident MFMA attention workgroups [D == 128][kernel variant]
   uint64_t fused_calls = 0;    // of which took the fused path
   int last_fused_b = 0;        // batch of the last fused call (its round words need clearing)
   int fused_cap[2] = {0, 0};   // co-resident fused-acceptance workgroups (f32, bf16)
@@ -138,8 +138,8 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   // the in-kernel split merge can be switched off for comparison (EAGLE_VERIFY_ATTN_FUSED_MERGE=0)
   const char* fm = std::getenv("EAGLE_VERIFY_ATTN_FUSED_MERGE");
   if (desc->kv_dtype == EAGLE_BF16 && !(fm && fm[0] == '0'))
-    for (int mb = 1; mb <= 2; ++mb)
-      h->attn_cap[desc->head_dim == 128 ? 1 : 0][mb - 1] = ev::attention_capacity(desc->head_dim, mb, h->num_cus);
+    for (int v = 0; v < ev::kMfmaVariants; ++v)
+      h->attn_cap[desc->head_dim == 128 ? 1 : 0][v] = ev::attention_capacity(desc->head_dim, v, h->num_cus);
   // counters start at zero; every call leaves them at zero again.  On the
   // fused path, arrival words only grow, publication words carry the call
   // epoch, and each fused call clears the round words the previous one used.
@@ -215,7 +215,7 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
   int max_splits = 1;
   for (int b = 0; b < a->batch; ++b) max_splits = std::max(max_splits, plan.split_base[b + 1] - plan.split_base[b]);
   k.fused_merge = (plan.path == 1 && plan.merge_workgroups > 0 &&
-                   plan.workgroups <= h->attn_cap[k.D == 128 ? 1 : 0][plan.mb - 1] &&
+                   plan.workgroups <= h->attn_cap[k.D == 128 ? 1 : 0][ev::mfma_variant(plan)] &&
                    plan.rows_per_tile + max_splits <= ev::kFusedMergePairs)
                       ? 1
                       : 0;

@@ -168,8 +168,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
 }
 
-template <int D, int MB, int NST>
+template <int D, int MB, int NST, int KG>
 __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a) {
+  static_assert(KG == 1 || (KG == 2 && MB == 1), "key halves are split only between single row blocks");
   constexpr int KSTEPS = D / 32;          // QK^T contraction steps
   constexpr int DBLK = D / 16;            // output column blocks
   constexpr int CH = D / 8;               // 16-byte chunks per row
@@ -183,6 +184,10 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   __shared__ int32_t par_lds[kMaxTree];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, ln = lane & 15;
+  // KG = 2: waves w and w + 2 own the same row block and take the first and
+  // the second 32 keys of every tile; their states are combined at the end
+  const int rw = wave % (4 / KG);
+  const int kh = __builtin_amdgcn_readfirstlane(wave / (4 / KG));
   const int logical = xcd_remap(blockIdx.x, a.nwg);
   // logical order: row tile fastest, then key split, then KV head, so the
   // row tiles of one K/V chunk share an XCD's L2 and every XCD receives its
@@ -190,12 +195,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   const int rt = logical % a.row_tiles;
   const int split = (logical / a.row_tiles) % a.total_splits;
   const int hk = logical / (a.row_tiles * a.total_splits);
+  const int64_t slot = logical;   // partial-row slot of this workgroup
   const int b = find_seq(a, split);
   const int s_local = split - a.split_base[b];
   const int S = a.split_base[b + 1] - a.split_base[b];
   const int L = a.L[b];
   const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
-  const int row_base = rt * a.rows_per_tile + wave * 16 * MB;   // lane rows: row_base + 16*rb + ln
+  const int row_base = rt * a.rows_per_tile + rw * 16 * MB;   // lane rows: row_base + 16*rb + ln
 
   // The first tile is requested from the expected row offset of the
   // sequence, without waiting for kv_indptr[b]; the parent array is requested
@@ -302,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     wait_vmcnt<0>();   // no transfer into LDS may outlive the workgroup
     // NaN rows: written here when no separate merge follows (one split, or
     // the merge is done inside this kernel: then split 0 writes its tile)
-    if (S == 1 || (a.fused_merge && s_local == 0)) {
+    if ((S == 1 || (a.fused_merge && s_local == 0)) && kh == 0) {
       for (int rb = 0; rb < MB; ++rb) {
         const int r = row_base + 16 * rb + ln;
         if (r >= R) continue;
@@ -338,10 +344,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   // row's node).  The tile is processed as two 32-key halves so that each
   // wave always has independent matrix and vector work in flight:
   //   QK(0) QK(1) | softmax(0) under QK(1) | PV(0) | softmax(1) under PV(0) | PV(1)
-  auto tile = [&](auto mask_tag, auto stage_tag, bool is_tree, int cnt) {
+  auto tile = [&](auto mask_tag, const uint16_t* kst, bool is_tree, int cnt) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int ST = decltype(stage_tag)::value;
-    const uint16_t* kst = kv_lds + ST * 2 * TILE;
     const uint16_t* vst = kst + TILE;
     f32x4_t sacc[4][MB];
 #pragma unroll
@@ -349,10 +353,9 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) sacc[kb][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // S^T for keys 32 h .. 32 h + 31 (key blocks 2h, 2h+1).  All K fragments
-    // of the half are read before the first product, and the contraction is
-    // split over two accumulators per block, so four independent MFMA chains
-    // are in flight.
-    auto qk = [&](auto h_tag) {
+    // of the half are read before the first product; the products of one
+    // block accumulate back to back (same shape, same accumulator).
+    auto qk = [&](auto h_tag) __attribute__((always_inline)) {
       constexpr int H = decltype(h_tag)::value;
       bf16x8_t kf[KSTEPS][2];
 #pragma unroll
@@ -362,27 +365,16 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
           const int r = 16 * (2 * H + kk) + ln;
           kf[s][kk] = *reinterpret_cast<const bf16x8_t*>(kst + r * D + (((lg + 4 * s) ^ swz_k<D>(r)) * 8));
         }
-      f32x4_t part[2][2][MB];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-          for (int rb = 0; rb < MB; ++rb) part[kk][pp][rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
           for (int rb = 0; rb < MB; ++rb)
-            part[kk][s & 1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s][kk], qf[rb][s], part[kk][s & 1][rb], 0, 0, 0);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) sacc[2 * H + kk][rb] = part[kk][0][rb] + part[kk][1][rb];
+            sacc[2 * H + kk][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s][kk], qf[rb][s], sacc[2 * H + kk][rb], 0, 0, 0);
     };
     // P for the half: masks, lazy reference maximum, exp2, bf16 hi/lo pair
-    auto softmax = [&](auto h_tag, bf16x8_t (&pb)[MB], bf16x8_t (&pl)[MB]) {
+    auto softmax = [&](auto h_tag, bf16x8_t (&pb)[MB], bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
       constexpr int H = decltype(h_tag)::value;
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb) {
@@ -430,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     // O^T += V^T P^T for keys 32 h .. 32 h + 31.  Lane (lg, ln) points the
     // transposing read at key 32 h + 4 lg + ln/4 (and + 16), dims
     // 16 db + 4 (ln % 4) .. + 3.
-    auto pv = [&](auto h_tag, const bf16x8_t (&pb)[MB], const bf16x8_t (&pl)[MB]) {
+    auto pv = [&](auto h_tag, const bf16x8_t (&pb)[MB], const bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
       constexpr int H = decltype(h_tag)::value;
       bf16x8_t va[DBLK];
 #pragma unroll
@@ -456,34 +448,73 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
     bf16x8_t pb0[MB], pl0[MB], pb1[MB], pl1[MB];
-    qk(H0{});
-    qk(H1{});
-    softmax(H0{}, pb0, pl0);
-    pv(H0{}, pb0, pl0);
-    softmax(H1{}, pb1, pl1);
-    pv(H1{}, pb1, pl1);
+    if constexpr (KG == 1) {
+      qk(H0{});
+      qk(H1{});
+      softmax(H0{}, pb0, pl0);
+      pv(H0{}, pb0, pl0);
+      softmax(H1{}, pb1, pl1);
+      pv(H1{}, pb1, pl1);
+    } else if (kh == 0) {
+      qk(H0{});
+      softmax(H0{}, pb0, pl0);
+      pv(H0{}, pb0, pl0);
+    } else {
+      qk(H1{});
+      softmax(H1{}, pb1, pl1);
+      pv(H1{}, pb1, pl1);
+    }
   };
 
-  auto step = [&](int t, auto stage_tag) {
-    // this wave's loads of tile t have landed
-    wait_vmcnt<0>();
-    __syncthreads();   // every wave's part of tile t is in LDS; the other stage is free
-    if (t + 1 < n_tiles) issue(t + 1);
+  auto run_tile = [&](int t, const uint16_t* kst) __attribute__((always_inline)) {
     if (t < n_full) {
-      tile(std::integral_constant<bool, false>{}, stage_tag, false, kTileKeys);
+      tile(std::integral_constant<bool, false>{}, kst, false, kTileKeys);
     } else {
       const bool is_tree = t >= n_prefix;
       const int cnt = is_tree ? T : min(kTileKeys, k_end - (k_begin + t * kTileKeys));
-      tile(std::integral_constant<bool, true>{}, stage_tag, is_tree, cnt);
+      tile(std::integral_constant<bool, true>{}, kst, is_tree, cnt);
     }
   };
+  // two stages: the stage of every LDS address is a compile-time constant
   static_assert(NST == 2, "the tile loop alternates two ring stages");
+  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    wait_vmcnt<0>();   // this wave's loads of tile t have landed
+    __syncthreads();   // every wave's part of tile t is in LDS; the other stage is free
+    if (t + 1 < n_tiles) issue(t + 1);
+    run_tile(t, kv_lds + ST * 2 * TILE);
+  };
   for (int t = 0; t < n_tiles; t += 2) {
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // epilogue
+  if constexpr (KG == 2) {
+    // the key-half states of each row meet in the (now free) K/V ring:
+    // M = max(m0, m1), O = 2^(m0-M) O0 + 2^(m1-M) O1, l likewise
+    __syncthreads();   // every wave has finished its last tile
+    f32x4_t* xo = reinterpret_cast<f32x4_t*>(kv_lds);   // [row block][db][lane]
+    float* xm = reinterpret_cast<float*>(xo + 2 * DBLK * 64);   // [row block][lane][m, l]
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) xo[(rw * DBLK + db) * 64 + lane] = o[0][db];
+      xm[(rw * 64 + lane) * 2] = m_run[0];
+      xm[(rw * 64 + lane) * 2 + 1] = l_run[0];
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float m1 = xm[(rw * 64 + lane) * 2], l1 = xm[(rw * 64 + lane) * 2 + 1];
+      const float M = fmaxf(m_run[0], m1);
+      const float Mu = (M == kNegInf) ? 0.f : M;
+      const float a0 = __builtin_amdgcn_exp2f(m_run[0] - Mu), a1 = __builtin_amdgcn_exp2f(m1 - Mu);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) o[0][db] = o[0][db] * a0 + xo[(rw * DBLK + db) * 64 + lane] * a1;
+      l_run[0] = l_run[0] * a0 + l1 * a1;
+      m_run[0] = M;
+    }
+  }
+
+  // epilogue (KG = 2: the waves of the first key half hold the rows)
   const bool fused = S > 1 && a.fused_merge;
   float l_fin[MB];
 #pragma unroll
@@ -493,14 +524,14 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     l_tot += __shfl_xor(l_tot, 32);
     l_fin[rb] = l_tot;
     const int r = row_base + 16 * rb + ln;
-    if (!row_ok[rb]) continue;
+    if (!row_ok[rb] || kh != 0) continue;
     if (S == 1) {
       const float inv = 1.f / l_tot;
       float* op = a.out + ((int64_t)(b * T + node[rb]) * Hq + head[rb]) * D + 4 * lg;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) *reinterpret_cast<f32x4_t*>(op + 16 * db) = o[rb][db] * inv;
     } else {
-      const int64_t prow = (int64_t)logical * a.rows_per_tile + (r - rt * a.rows_per_tile);
+      const int64_t prow = slot * a.rows_per_tile + (r - rt * a.rows_per_tile);
       float* op = a.opart + prow * D + 4 * lg;
       if (fused) {   // read by workgroups on other XCDs: written through to memory
         const __amdgpu_buffer_rsrc_t prs = part_rsrc(a.opart);
@@ -530,8 +561,8 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) {
     const int r = row_base + 16 * rb + ln;
-    if (!row_ok[rb] || lg != 0) continue;
-    uint64_t* rec = a.mlrec + 2 * ((int64_t)logical * a.rows_per_tile + (r - rt * a.rows_per_tile));
+    if (!row_ok[rb] || lg != 0 || kh != 0) continue;
+    uint64_t* rec = a.mlrec + 2 * (slot * a.rows_per_tile + (r - rt * a.rows_per_tile));
     st_u64(rec, tag | __float_as_uint(m_run[rb]));
     st_u64(rec + 1, tag | __float_as_uint(l_fin[rb]));
   }
@@ -835,9 +866,10 @@ template <int D>
 hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hipStream_t st) {
   if (p.path == 1) {
     const dim3 grid((unsigned)p.workgroups), block(256);
-    switch (p.mb) {
-      case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2>), grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2>), grid, block, 0, st, a); break;
+    switch (mfma_variant(p)) {
+      case 0: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 1>), grid, block, 0, st, a); break;
+      case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2, 1>), grid, block, 0, st, a); break;
+      case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 2>), grid, block, 0, st, a); break;
       default: return hipErrorInvalidValue;
     }
   } else {
@@ -867,13 +899,16 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
 
 }  // namespace
 
-int attention_capacity(int D, int mb, int num_cus) {
+int attention_capacity(int D, int variant, int num_cus) {
   int per_cu = 0;
-  const void* fn = nullptr;
-  if (D == 128)
-    fn = (mb == 2) ? reinterpret_cast<const void*>(&tree_attn_mfma<128, 2, 2>) : reinterpret_cast<const void*>(&tree_attn_mfma<128, 1, 2>);
-  else
-    fn = (mb == 2) ? reinterpret_cast<const void*>(&tree_attn_mfma<64, 2, 2>) : reinterpret_cast<const void*>(&tree_attn_mfma<64, 1, 2>);
+  const void* fns128[kMfmaVariants] = {reinterpret_cast<const void*>(&tree_attn_mfma<128, 1, 2, 1>),
+                                       reinterpret_cast<const void*>(&tree_attn_mfma<128, 2, 2, 1>),
+                                       reinterpret_cast<const void*>(&tree_attn_mfma<128, 1, 2, 2>)};
+  const void* fns64[kMfmaVariants] = {reinterpret_cast<const void*>(&tree_attn_mfma<64, 1, 2, 1>),
+                                      reinterpret_cast<const void*>(&tree_attn_mfma<64, 2, 2, 1>),
+                                      reinterpret_cast<const void*>(&tree_attn_mfma<64, 1, 2, 2>)};
+  if (variant < 0 || variant >= kMfmaVariants) return 0;
+  const void* fn = (D == 128) ? fns128[variant] : fns64[variant];
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu <= 0) return 0;
   return per_cu * num_cus;
 }

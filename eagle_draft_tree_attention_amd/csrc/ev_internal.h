@@ -27,7 +27,8 @@ struct AttnPlan {
   int path;            // 0 = FMA kernel (fp32, or bf16 with R < 16), 1 = MFMA kernel
   int R;               // rows per KV head = T * g
   int mb;              // MFMA: 16-row blocks per wave (rows per workgroup = 64 * mb), 1 or 2
-  int stages;          // MFMA: K/V tiles in the LDS ring (2 or 3)
+  int stages;          // MFMA: K/V tiles in the LDS ring
+  int kg;              // MFMA: key groups per tile (2: wave pairs take the two 32-key halves)
   int row_tiles;       // workgroups along R (FMA path: one row each)
   int rows_per_tile;
   int chunk;           // prefix keys per split (multiple of kTileKeys)
@@ -160,6 +161,10 @@ int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stre
 int fused_accept_capacity(int logits_bf16, int num_cus);
 // co-resident workgroups of the MFMA attention kernel for head_dim D and mb
 // 16-row blocks per wave (0 if the query fails)
-int attention_capacity(int D, int mb, int num_cus);
+// MFMA kernel variants: 0 = one 16-row block per wave, 1 = two, 2 = key halves
+// split between wave pairs (32 rows per workgroup)
+constexpr int kMfmaVariants = 3;
+inline int mfma_variant(const AttnPlan& p) { return p.kg == 2 ? 2 : p.mb - 1; }
+int attention_capacity(int D, int variant, int num_cus);
 
 }  // namespace ev

@@ -107,11 +107,21 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
     const int mb_env = env_int("EAGLE_VERIFY_ATTN_MB", 1);
     const int max_mb = mb_env > 2 ? 2 : (mb_env < 1 ? 1 : mb_env);
     plan->stages = 2;
-    int rt = static_cast<int>(ceil_div(R, 64 * max_mb));
-    int rows = static_cast<int>(ceil_div(ceil_div(R, rt), 64) * 64);
-    plan->row_tiles = rt;
-    plan->rows_per_tile = rows;
-    plan->mb = rows / 64;
+    if (R <= 32) {
+      // at most two 16-row blocks per KV head: wave pairs split the keys of
+      // each tile instead of padding the workgroup to 64 rows
+      plan->row_tiles = 1;
+      plan->rows_per_tile = 32;
+      plan->mb = 1;
+      plan->kg = 2;
+    } else {
+      int rt = static_cast<int>(ceil_div(R, 64 * max_mb));
+      int rows = static_cast<int>(ceil_div(ceil_div(R, rt), 64) * 64);
+      plan->row_tiles = rt;
+      plan->rows_per_tile = rows;
+      plan->mb = rows / 64;
+      plan->kg = 1;
+    }
     target_wgs = num_cus * env_int("EAGLE_VERIFY_ATTN_WG_PER_CU", 2);
     min_chunk = 2 * kTileKeys;
   } else {

@@ -30,6 +30,10 @@ CASES = [
     small_spec("bf16_chain", B=1, Hq=8, Hkv=2, lens=(900,), tree=("chain", 12)),
     small_spec("bf16_root_only", B=2, Hq=16, Hkv=1, lens=(129, 5), tree=("chain", 0)),
     small_spec("bf16_full_tree_64", B=1, Hq=4, Hkv=4, lens=(333,), levels=(8, 15, 20, 20)),
+    # at most 32 rows per KV head: wave pairs split the keys of each tile
+    small_spec("bf16_key_halves_chain8", B=2, Hq=8, Hkv=2, lens=(1500, 130), tree=("chain", 7)),
+    small_spec("bf16_key_halves_d64_r20", B=1, Hq=12, Hkv=3, D=64, lens=(700,), levels=(2, 2)),
+    small_spec("bf16_key_halves_r16_short", B=2, Hq=16, Hkv=1, lens=(20, 0), tree=("chain", 0)),
 ]
 
 
@@ -55,7 +59,8 @@ def test_attention_matches_oracle(spec):
     ver.close()
 
 
-MERGE_CASES = [c for c in CASES if c.name in ("bf16_mb1_two_seqs", "bf16_two_row_tiles", "bf16_d64", "bf16_chain")]
+MERGE_CASES = [c for c in CASES if c.name in ("bf16_mb1_two_seqs", "bf16_two_row_tiles", "bf16_d64", "bf16_chain",
+                                               "bf16_key_halves_chain8")]
 
 
 @pytest.mark.parametrize("spec", MERGE_CASES, ids=lambda s: s.name)
