@@ -710,7 +710,19 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
 // Every wait is bounded by spin_limit; a wait that expires flags the
 // sequence EAGLE_FLAG_INTERNAL instead of hanging.
 
-constexpr uint64_t kPubDone = 255;
+// Publication word of a node, relative to the call's base (epoch << 10):
+//   2 + u                       first decision taken, another residual round follows
+//   512 + 256 u + 64 kind + o   final state: kind, accepted child o (0 otherwise)
+// with u = 1 when one of the node's rows is unusable (non-finite), so a poll
+// of the word alone tells the walk everything it needs.
+constexpr uint64_t kPubFirst = 2;
+constexpr uint64_t kPubDone = 512;
+__device__ __forceinline__ uint64_t pub_word(const NodeState& st) {
+  const uint64_t u = (st.flags & EAGLE_FLAG_NONFINITE) ? 1u : 0u;
+  if (st.kind == kNodeNeedsPass) return kPubFirst + u;
+  const uint64_t o = st.kind == kNodeAccepted ? static_cast<uint64_t>(st.outcome & 63) : 0u;
+  return kPubDone + (u << 8) + (static_cast<uint64_t>(st.kind & 3) << 6) + o;
+}
 constexpr int kFusedMaxChunks = 64;   // V <= 64 * 8192 on the fused path
 // Round words: bits 57..63 count arrivals (<= 64 chunks), bits 0..56 hold the
 // sum of the chunks' partial masses in units of 2^-49.  A partial is a mass
@@ -770,8 +782,9 @@ struct FusedShared {
   int32_t onpath;
   uint32_t seqflags;
   int32_t seqnear;
-  int32_t found;
   double scan[kThreads / 64];
+  int32_t wfirst[kThreads / 64];
+  double cmass[kFusedMaxChunks];   // q mass of each chunk (from the chunk statistics)
   double sample[4];
 };
 
@@ -979,7 +992,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   const int n = (blockIdx.x / NC) % T;
   const int b = blockIdx.x / (NC * T);
   const bool greedy = a.tau == 0.f;
-  const uint64_t base = a.epoch << 8;
+  const uint64_t base = a.epoch << 10;
   const uint32_t limit = a.spin_limit;
   const bool lead = (c == 0);   // publishes the node's state for the other nodes' groups
 
@@ -1128,6 +1141,10 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
           (!greedy && q < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - M) * static_cast<double>(a.c2)) : 0.0,
           AddD{});
       const int arg = wave_reduce((greedy && q < NC && mc == M) ? ac : 0x7FFFFFFF, MinI{});
+      if (r == 0)   // q mass of chunk q: the terminal distribution of a leaf, per chunk
+        sh.cmass[q] = (!greedy && q < NC && mc != kNegInf && Z > 0.0)
+                          ? zc * exp2((static_cast<double>(mc) - M) * static_cast<double>(a.c2)) / Z
+                          : 0.0;
       if (q == 0) {
         const uint32_t fl = (rb || M == kNegInf) ? EAGLE_FLAG_NONFINITE : 0u;
         if (r == 0) {
@@ -1202,7 +1219,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     sh.st = st;
     if (lead) {
       store_state(&a.nodes[b * T + n], st);
-      publish(npub, base + (st.kind == kNodeNeedsPass ? 1u : kPubDone));
+      publish(npub, base + pub_word(st));
     }
   }
   __syncthreads();
@@ -1263,7 +1280,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       sh.st = st;
       if (fine && lead && st.kind != kNodeNeedsPass) {
         store_state(&a.nodes[b * T + n], st);
-        publish(npub, base + kPubDone);
+        publish(npub, base + pub_word(st));
       }
     }
     __syncthreads();
@@ -1272,13 +1289,12 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
 
   // ---- sequence verdict: workgroup 0 of the root waits for every node's
-  // first publication and publishes whether any row was unusable (then it
-  // also writes the poisoned outputs)
-  uint64_t* const verdict = a.seq_sync + static_cast<int64_t>(b) * kSyncWords + 1;
+  // first publication and writes the poisoned outputs if any row was
+  // unusable (the terminal node reaches the same verdict from the words)
   const bool master = (n == 0 && c == 0);
   if (master) {
     if (tid == 0) sh.seqflags = tokbad;
-    wait_all(nsync + 1, kSyncWords, T, base + 1, limit, &sh.ok);
+    wait_all(nsync + 1, kSyncWords, T, base + kPubFirst, limit, &sh.ok);
     if (sh.ok && tid < T) {
       const uint32_t f = static_cast<uint32_t>(ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + tid].flags)));
       if (f & EAGLE_FLAG_NONFINITE) atomicOr(&sh.seqflags, EAGLE_FLAG_NONFINITE);
@@ -1286,149 +1302,99 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     __syncthreads();
     if (!sh.ok) return fail_internal();
     const uint32_t sf = sh.seqflags;
-    if (sf) write_poison(a, b, sf);
-    if (tid == 0) publish(verdict, base + (sf ? 2u : 1u));
-    if (sf) return;
+    if (sf) {
+      write_poison(a, b, sf);
+      return;
+    }
   }
   if (sh.st.kind == kNodeAccepted) return;
   // an unusable row poisons the whole sequence: nothing to sample here
   if (sh.st.flags & EAGLE_FLAG_NONFINITE) return;
 
-  // ---- is this node where the walk ends?  Yes iff every ancestor accepted
-  // the next node of this root path.  One thread polls the ancestors and
-  // gives up as soon as one of them decided otherwise.
-  if (tid == 0) {
-    const int pl = root_path(sh.ti, n, path_lds);
-    int on = 1, fine = 1;
-    uint64_t confirmed = 0;
-    uint32_t it = 0;
-    for (;;) {
-      bool all = true;
-      for (int i = 0; i + 1 < pl && on; ++i) {
-        if ((confirmed >> i) & 1ull) continue;
-        const int anc = path_lds[i];
-        if (poll(nsync + anc * kSyncWords + 1) < base + kPubDone) {
-          all = false;
-          continue;
-        }
-        loads_after();
-        const uint64_t w = ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + anc].kind));
-        const int kind = static_cast<int>(static_cast<uint32_t>(w));
-        const int outc = static_cast<int>(static_cast<uint32_t>(w >> 32));
-        if (kind != kNodeAccepted || outc != path_lds[i + 1])
-          on = 0;
-        else
-          confirmed |= 1ull << i;
-      }
-      if (!on || all) break;
-      if (++it > limit) {
-        fine = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(8);
-    }
-    // the terminal node also needs the verdict on the whole sequence
-    if (on && fine) {
-      uint64_t v;
-      it = 0;
-      while ((v = poll(verdict)) < base + 1) {
-        if (++it > limit) {
-          fine = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
-      }
-      if (fine && v != base + 1) on = 0;   // poisoned: the root's workgroup wrote the outputs
-    }
-    sh.iscr[0] = pl;
-    sh.onpath = on;
-    sh.ok = fine;
-  }
-  __syncthreads();
-  if (!sh.ok) return fail_internal();
-  if (!sh.onpath) return;
-  const int plen = sh.iscr[0];
-  const int len = plen - 1;   // accepted draft nodes
-  if (greedy && c != 0) return;
-
-  // ---- terminal sample: inverse CDF of the residual max(0, q - C p) (of q
-  // at a leaf; of q again if the residual mass is zero).  Thread t owns the
-  // LDS slots [32t, 32t + 32), i.e. consecutive tokens.
-  int final_tok = sh.st.argmax;
-  uint32_t extra_flags = 0;
-  int extra_near = 0;
-  if (!greedy) {
-    const bool leaf = (sh.st.kind == kNodeLeaf);
-    const double Ct = leaf ? 0.0 : sh.st.C;
-    const int i0 = tid * kPerThread;
-    // weight of the token at LDS slot i0 + jj * G + e, from its two logits
-    const float qc = -mqs * a.c2, pc = -mps * a.c2;
-    const float Kt = fq > 0.0 ? static_cast<float>(Ct * fp / fq) : 0.f;
-    auto weight = [&](bool q_only, float xq, float xp) -> double {
-      const float eq = ex2(xq, a.c2, qc);
-      return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(xp, a.c2, pc), eq)));
-    };
-    // this thread's sums of the weights and of q
-    auto sums = [&](bool q_only, double& ts, double& tq) {
-      double wa[4] = {0.0, 0.0, 0.0, 0.0}, qa[4] = {0.0, 0.0, 0.0, 0.0};
+  // ---- terminal distribution of this node, prepared before the walk is
+  // known to end here (it overlaps the walk): inverse CDF of the residual
+  // max(0, q - C p) (of q at a leaf; of q again if the residual mass is
+  // zero).  Thread t owns the LDS slots [32t, 32t + 32), i.e. consecutive
+  // tokens.  Every workgroup of the node publishes its chunk mass and
+  // finds the chunk holding u*S; only that workgroup continues once the
+  // walk is known to end here.
+  const bool leaf = (sh.st.kind == kNodeLeaf);
+  const double Ct = leaf ? 0.0 : sh.st.C;
+  const int i0 = tid * kPerThread;
+  // weight of the token at LDS slot i0 + jj * G + e, from its two logits
+  const float qc = -mqs * a.c2, pc = -mps * a.c2;
+  const float Kt = fq > 0.0 ? static_cast<float>(Ct * fp / fq) : 0.f;
+  auto weight = [&](bool q_only, float xq, float xp) __attribute__((always_inline)) -> double {
+    const float eq = ex2(xq, a.c2, qc);
+    return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(xp, a.c2, pc), eq)));
+  };
+  // this thread's sums of the weights and of q
+  auto sums = [&](bool q_only, double& ts, double& tq) __attribute__((always_inline)) {
+    double wa[4] = {0.0, 0.0, 0.0, 0.0}, qa[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 1
-      for (int jj = 0; jj < NV; ++jj) {
-        const u32x4_t gq = *reinterpret_cast<const u32x4_t*>(lq + i0 + jj * G);
-        const u32x4_t gp = q_only ? gq : *reinterpret_cast<const u32x4_t*>(lp + i0 + jj * G);
-        float fa[G], fb[G];
-        Pack<TL>::unpack(gq, fa);
-        Pack<TL>::unpack(gp, fb);
+    for (int jj = 0; jj < NV; ++jj) {
+      const u32x4_t gq = *reinterpret_cast<const u32x4_t*>(lq + i0 + jj * G);
+      const u32x4_t gp = q_only ? gq : *reinterpret_cast<const u32x4_t*>(lp + i0 + jj * G);
+      float fa[G], fb[G];
+      Pack<TL>::unpack(gq, fa);
+      Pack<TL>::unpack(gp, fb);
 #pragma unroll
-        for (int e = 0; e < G; ++e) {
-          const float eq = ex2(fa[e], a.c2, qc);
-          qa[e & 3] += static_cast<double>(eq);
-          wa[e & 3] += static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(fb[e], a.c2, pc), eq)));
-        }
+      for (int e = 0; e < G; ++e) {
+        const float eq = ex2(fa[e], a.c2, qc);
+        qa[e & 3] += static_cast<double>(eq);
+        wa[e & 3] += static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(fb[e], a.c2, pc), eq)));
       }
-      ts = ((wa[0] + wa[1]) + (wa[2] + wa[3])) * fq;
-      tq = ((qa[0] + qa[1]) + (qa[2] + qa[3])) * fq;
-    };
-    // block exclusive scan of the per-thread sums: this thread's starting
-    // offset inside the chunk and the chunk total
-    double chunk_total = 0.0;
-    auto scan_offsets = [&](double ts) -> double {
-      double incl = ts;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o);
-        if ((tid & 63) >= o) incl += y;
-      }
-      double excl = __shfl_up(incl, 1);
-      if ((tid & 63) == 0) excl = 0.0;
-      __syncthreads();
-      if ((tid & 63) == 63) sh.scan[tid >> 6] = incl;
-      __syncthreads();
-      double off = 0.0, tot = 0.0;
-#pragma unroll
-      for (int wv = 0; wv < kThreads / 64; ++wv) {
-        if (wv < (tid >> 6)) off += sh.scan[wv];
-        tot += sh.scan[wv];
-      }
-      chunk_total = tot;
-      return off + excl;
-    };
-    double ts, tq;
-    sums(leaf, ts, tq);
-    double offset = scan_offsets(ts);
-    double mqsum = block_reduce(tq, AddD{}, sh.dscr);
-    double* const sp = a.spart + (static_cast<int64_t>(b * T + n) * NC) * 2;
-    if (tid == 0) {
-      st_f64(&sp[2 * c], chunk_total);
-      st_f64(&sp[2 * c + 1], mqsum);
-      sh.ok = phase_barrier(narr, static_cast<uint32_t>(NC), limit) ? 1 : 0;
     }
+    ts = ((wa[0] + wa[1]) + (wa[2] + wa[3])) * fq;
+    tq = ((qa[0] + qa[1]) + (qa[2] + qa[3])) * fq;
+  };
+  // block exclusive scan of the per-thread sums: this thread's starting
+  // offset inside the chunk and the chunk total
+  double chunk_total = 0.0;
+  auto scan_offsets = [&](double ts) __attribute__((always_inline)) -> double {
+    double incl = ts;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(incl, o);
+      if ((tid & 63) >= o) incl += y;
+    }
+    double excl = __shfl_up(incl, 1);
+    if ((tid & 63) == 0) excl = 0.0;
     __syncthreads();
-    if (!sh.ok) return fail_internal();
+    if ((tid & 63) == 63) sh.scan[tid >> 6] = incl;
+    __syncthreads();
+    double off = 0.0, tot = 0.0;
+#pragma unroll
+    for (int wv = 0; wv < kThreads / 64; ++wv) {
+      if (wv < (tid >> 6)) off += sh.scan[wv];
+      tot += sh.scan[wv];
+    }
+    chunk_total = tot;
+    return off + excl;
+  };
+  double ts = 0.0, tq = 0.0, offset = 0.0;
+  int cstar = 0;
+  bool degen = false;
+  if (!greedy) {
+    sums(leaf, ts, tq);
+    offset = scan_offsets(ts);
+    double* const sp = a.spart + (static_cast<int64_t>(b * T + n) * NC) * 2;
+    if (!leaf) {   // residual masses of every chunk: published, then read back
+      const double mqsum = block_reduce(tq, AddD{}, sh.dscr);
+      if (tid == 0) {
+        st_f64(&sp[2 * c], chunk_total);
+        st_f64(&sp[2 * c + 1], mqsum);
+        sh.ok = phase_barrier(narr, static_cast<uint32_t>(NC), limit) ? 1 : 0;
+      }
+      __syncthreads();
+      if (!sh.ok) return fail_internal();
+    }
     // the chunk holding u * S (wave 0, one chunk per lane; same arithmetic
     // in every workgroup of the node)
     if (tid < 64) {
-      const double mr = (tid < NC) ? ld_f64(&sp[2 * tid]) : 0.0;
-      const double mq = (tid < NC) ? ld_f64(&sp[2 * tid + 1]) : 0.0;
+      // leaf: the chunk statistics already hold every chunk's q mass
+      const double mr = (tid >= NC) ? 0.0 : (leaf ? sh.cmass[tid] : ld_f64(&sp[2 * tid]));
+      const double mq = (tid >= NC) ? 0.0 : (leaf ? mr : ld_f64(&sp[2 * tid + 1]));
       const double sr = wave_reduce(mr, AddD{});
       const bool degen = !(sr > 0.0);
       const double m = degen ? mq : mr;
@@ -1454,8 +1420,67 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       }
     }
     __syncthreads();
-    const int cstar = sh.iscr[3] & 0x3FFFFFFF;
-    const bool degen = (sh.iscr[3] & 0x40000000) != 0;
+    cstar = sh.iscr[3] & 0x3FFFFFFF;
+    degen = (sh.iscr[3] & 0x40000000) != 0;
+  }
+
+  // ---- is this node where the walk ends?  Yes iff every ancestor accepted
+  // the next node of this root path and no node of the sequence has an
+  // unusable row.  Lane j of wave 0 polls node j's publication word; the
+  // wave gives up as soon as one word rules this node out.
+  if (tid == 0) sh.iscr[0] = root_path(sh.ti, n, path_lds);
+  __syncthreads();
+  if (tid < 64) {
+    const int pl = sh.iscr[0];
+    int pos = -1;   // position of node tid on the root path, if an ancestor
+    for (int i = 0; i + 1 < pl; ++i)
+      if (path_lds[i] == tid) pos = i;
+    const int nxt = pos >= 0 ? path_lds[pos + 1] : -1;
+    int state = tid < T ? 0 : 1;   // 0 undecided, 1 consistent with the walk ending here, 2 not
+    bool on = false, fine = true;
+    for (uint32_t it = 0;; ++it) {
+      if (state == 0) {
+        const uint64_t w = poll(nsync + static_cast<int64_t>(tid) * kSyncWords + 1);
+        if (w >= base + kPubFirst) {
+          const uint64_t code = w - base;
+          const bool done = code >= kPubDone;
+          const bool unusable = done ? ((code >> 8) & 1u) : ((code - kPubFirst) & 1u);
+          if (unusable)
+            state = 2;
+          else if (pos < 0)
+            state = 1;
+          else if (done)
+            state = (static_cast<int>((code >> 6) & 3u) == kNodeAccepted && static_cast<int>(code & 63u) == nxt) ? 1 : 2;
+        }
+      }
+      if (__any(state == 2)) break;
+      if (__all(state == 1)) {
+        on = true;
+        break;
+      }
+      if (it >= limit) {
+        fine = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (tid == 0) {
+      sh.onpath = (on && !tokbad) ? 1 : 0;   // a bad token: the root's workgroup wrote the outputs
+      sh.ok = fine ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (!sh.ok) return fail_internal();
+  if (!sh.onpath) return;
+  const int plen = sh.iscr[0];
+  const int len = plen - 1;   // accepted draft nodes
+  if (greedy && c != 0) return;
+
+  // ---- terminal sample (the workgroup of the chunk holding u*S)
+  int final_tok = sh.st.argmax;
+  uint32_t extra_flags = 0;
+  int extra_near = 0;
+  if (!greedy) {
     if (c != cstar) return;
     const double S = sh.sample[1], thr = sh.sample[2];
     const bool q_only = leaf || degen;
@@ -1464,16 +1489,19 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       offset = scan_offsets(ts);
     }
     // the smallest token whose running sum exceeds u*S.  The first thread
-    // whose range reaches u*S is found by a block minimum; wave 0 then
+    // whose range reaches u*S is found from per-wave ballots; wave 0 then
     // scans that thread's 32 tokens one per lane.  A thread starting past
     // u*S offers its first token (rounding hid the crossing just before it,
     // which the near-tie test reports).
     const double start = sh.sample[0] + offset;
-    if (tid == 0) sh.found = 0x7FFFFFFF;
+    {
+      const uint64_t reach = __ballot(start > thr || thr - start < ts * (1.0 + 1e-9));
+      if ((tid & 63) == 0) sh.wfirst[tid >> 6] = reach ? (tid + __ffsll(static_cast<long long>(reach)) - 1) : 0x7FFFFFFF;
+    }
     __syncthreads();
-    if (start > thr || thr - start < ts * (1.0 + 1e-9)) atomicMin(&sh.found, tid);
-    __syncthreads();
-    const int tstar = sh.found;
+    int tstar = 0x7FFFFFFF;
+#pragma unroll
+    for (int wv = 0; wv < kThreads / 64; ++wv) tstar = min(tstar, sh.wfirst[wv]);
     if (tid == tstar) sh.sample[3] = start;
     __syncthreads();
     if (tid < 64) {
