@@ -125,11 +125,67 @@ __device__ __forceinline__ void load_chunk(const TL* row, int v0, int v1, bool v
 }
 
 // ------------------------------------------------------ block reductions
+// Lane-to-lane moves for reductions: DPP row rotations (16-lane rows) move
+// a 32- or 64-bit value between the lanes of a row without going through
+// LDS, and readlane takes a row's value into a scalar register.
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_move(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(T, static_cast<uint64_t>(static_cast<uint32_t>(lo)) | (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32));
+  }
+}
+template <typename T>
+__device__ __forceinline__ T read_lane(T v, int l) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  } else {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), l));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), l));
+    return __builtin_bit_cast(T, static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
+  }
+}
+
+// Moves whose source may lie outside the row (or the enabled rows): such
+// lanes receive 0, the identity of the sums below.
+template <int CTRL, int ROWS, typename T>
+__device__ __forceinline__ T dpp_shift(T v) {
+  static_assert(sizeof(T) == 8, "64-bit values");
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, ROWS, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, ROWS, 0xF, false);
+  return __builtin_bit_cast(T, static_cast<uint64_t>(static_cast<uint32_t>(lo)) | (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32));
+}
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active):
+// log-step sums inside each 16-lane row, then the row totals are carried
+// forward by row broadcasts.
+__device__ __forceinline__ double wave_scan_add(double v) {
+  v += dpp_shift<0x111, 0xF>(v);   // row_shr:1
+  v += dpp_shift<0x112, 0xF>(v);   // row_shr:2
+  v += dpp_shift<0x114, 0xF>(v);   // row_shr:4
+  v += dpp_shift<0x118, 0xF>(v);   // row_shr:8
+  v += dpp_shift<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_shift<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+// the value of the previous lane (0 in lane 0)
+__device__ __forceinline__ double wave_prev(double v) { return dpp_shift<0x138, 0xF>(v); }   // wave_shr:1
+
+// Reduction over the 64 lanes of a wave (every lane active); the result is
+// the same in every lane and is combined in one fixed order.
 template <typename T, typename Op>
 __device__ __forceinline__ T wave_reduce(T v, Op op) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
-  return v;
+  v = op(v, dpp_move<0x128>(v));   // row_ror:8
+  v = op(v, dpp_move<0x124>(v));   // row_ror:4
+  v = op(v, dpp_move<0x122>(v));   // row_ror:2
+  v = op(v, dpp_move<0x121>(v));   // row_ror:1 -> every lane holds its row's result
+  return op(op(read_lane(v, 0), read_lane(v, 16)), op(read_lane(v, 32), read_lane(v, 48)));
 }
 
 template <typename T, typename Op>
@@ -1352,14 +1408,8 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // offset inside the chunk and the chunk total
   double chunk_total = 0.0;
   auto scan_offsets = [&](double ts) __attribute__((always_inline)) -> double {
-    double incl = ts;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double y = __shfl_up(incl, o);
-      if ((tid & 63) >= o) incl += y;
-    }
-    double excl = __shfl_up(incl, 1);
-    if ((tid & 63) == 0) excl = 0.0;
+    const double incl = wave_scan_add(ts);
+    const double excl = wave_prev(incl);
     __syncthreads();
     if ((tid & 63) == 63) sh.scan[tid >> 6] = incl;
     __syncthreads();
@@ -1400,12 +1450,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       const double m = degen ? mq : mr;
       const double S = degen ? wave_reduce(mq, AddD{}) : sr;
       const double thr = decision_uniform(a, b, n, kSampleSlot) * S;
-      double incl = m;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(incl, o);
-        if (tid >= o) incl += y;
-      }
+      const double incl = wave_scan_add(m);
       const double excl = incl - m;
       const uint64_t cross = __ballot(tid < NC && incl > thr);
       // rounding: no crossing -> the last chunk with positive mass
@@ -1514,12 +1559,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         const float xq = lds_logit<TL>(lq, t0 + l);
         const float xp = q_only ? xq : lds_logit<TL>(lp, t0 + l);
         const double w = (tid < 32) ? weight(q_only, xq, xp) : 0.0;
-        double incl = w;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-          const double y = __shfl_up(incl, o);
-          if (l >= o) incl += y;
-        }
+        const double incl = wave_scan_add(w);   // lanes 32..63 carry 0
         const double cum = s0 + incl;
         const uint64_t over = __ballot(tid < 32 && (s0 > thr || cum > thr));
         if (over) {
