@@ -749,35 +749,50 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
 // path when the occupancy query says the grid fits).  The NC workgroups of a
 // node stage their slice of the node's target and draft rows in LDS once and
 // work from there to the end:
-//   stats  -> chunk statistics and one barrier per node; every workgroup of
-//             the node then combines them (same arithmetic in the same order,
-//             so all of them hold the same node state) and takes the first
-//             decision itself
+//   stats  -> chunk statistics published as self-tagged words; every
+//             workgroup of the node polls them, combines them (same arithmetic
+//             in the same order, so all of them hold the same node state) and
+//             takes the first decision itself
 //   rounds -> while the node needs another residual mass, each workgroup adds
 //             (1 << 57) + its partial mass in 2^-49 fixed point to the round's
 //             word with one atomic: the word carries the arrival count and an
 //             exact, order-independent sum, so one poll ends the round with
 //             the same s in every workgroup
-//   walk   -> a node that ends without an accepted child checks, once its
-//             ancestors are decided, whether the walk reaches it
-//   sample -> the terminal node's workgroups publish their chunk masses, each
-//             finds the chunk holding u*S, and that workgroup scans its LDS
-//             slice in token order and writes the outputs.
+//   walk   -> a node that ends without an accepted child prepares its
+//             terminal chunk masses, then checks from the nodes' publication
+//             words whether the walk reaches it
+//   sample -> the workgroup of the chunk holding u*S scans its LDS slice in
+//             token order and writes the outputs.
 // Every wait is bounded by spin_limit; a wait that expires flags the
 // sequence EAGLE_FLAG_INTERNAL instead of hanging.
 
-// Publication word of a node, relative to the call's base (epoch << 10):
-//   2 + u                       first decision taken, another residual round follows
-//   512 + 256 u + 64 kind + o   final state: kind, accepted child o (0 otherwise)
-// with u = 1 when one of the node's rows is unusable (non-finite), so a poll
-// of the word alone tells the walk everything it needs.
+// Publication word of a node, relative to the call's base (epoch << 20):
+//   2 + u          first decision taken, another residual round follows
+//                  (u = 1: one of the node's rows is unusable, non-finite)
+//   2^19 + 2^12 near + 2^9 f + 2^6 kind + o
+//                  final state: near-tie count, flags f (bit 0 non-finite,
+//                  bit 1 P_ZERO, bit 2 degenerate residual), kind and the
+//                  accepted child o (0 otherwise)
+// A poll of the word alone tells the walk and the outputs everything they
+// need from another node, so no node state goes through memory.
 constexpr uint64_t kPubFirst = 2;
-constexpr uint64_t kPubDone = 512;
+constexpr uint64_t kPubDone = 1ull << 19;
 __device__ __forceinline__ uint64_t pub_word(const NodeState& st) {
   const uint64_t u = (st.flags & EAGLE_FLAG_NONFINITE) ? 1u : 0u;
   if (st.kind == kNodeNeedsPass) return kPubFirst + u;
+  const uint64_t f = u | ((st.flags & EAGLE_FLAG_P_ZERO) ? 2u : 0u) | ((st.flags & EAGLE_FLAG_DEGENERATE_RESIDUAL) ? 4u : 0u);
+  const uint64_t nr = static_cast<uint64_t>(min(max(st.near, 0), 127));
   const uint64_t o = st.kind == kNodeAccepted ? static_cast<uint64_t>(st.outcome & 63) : 0u;
-  return kPubDone + (u << 8) + (static_cast<uint64_t>(st.kind & 3) << 6) + o;
+  return kPubDone + (nr << 12) + (f << 9) + (static_cast<uint64_t>(st.kind & 3) << 6) + o;
+}
+__device__ __forceinline__ uint32_t pub_flags(uint64_t code) {
+  const uint32_t f = static_cast<uint32_t>(code >> 9) & 7u;
+  return ((f & 1u) ? EAGLE_FLAG_NONFINITE : 0u) | ((f & 2u) ? EAGLE_FLAG_P_ZERO : 0u) |
+         ((f & 4u) ? EAGLE_FLAG_DEGENERATE_RESIDUAL : 0u);
+}
+// unusable-row bit of a published word (first or final)
+__device__ __forceinline__ bool pub_unusable(uint64_t code) {
+  return code >= kPubDone ? ((code >> 9) & 1u) : ((code - kPubFirst) & 1u);
 }
 constexpr int kFusedMaxChunks = 64;   // V <= 64 * 8192 on the fused path
 // Round words: bits 57..63 count arrivals (<= 64 chunks), bits 0..56 hold the
@@ -791,32 +806,7 @@ constexpr double kFixUnit = 0x1p-49;
 
 // Cross-workgroup words of the fused path use the system-scope helpers of
 // ev_device.h (ld_u64, st_u64, stores_done, loads_after, poll, publish).
-__device__ void store_state(NodeState* dst, const NodeState& src) {
-  const uint64_t* s = reinterpret_cast<const uint64_t*>(&src);
-  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
-#pragma unroll
-  for (int i = 0; i < static_cast<int>(sizeof(NodeState) / 8); ++i) st_u64(d + i, s[i]);
-}
 
-// Every thread t < count waits until w[t * stride] >= target; block-wide
-// verdict in *ok (all threads call).
-__device__ bool wait_all(const uint64_t* w, int stride, int count, uint64_t target, uint32_t limit, int32_t* ok) {
-  if (threadIdx.x == 0) *ok = 1;
-  __syncthreads();
-  if (static_cast<int>(threadIdx.x) < count) {
-    uint32_t it = 0;
-    while (poll(w + static_cast<int64_t>(threadIdx.x) * stride) < target) {
-      if (++it > limit) {
-        *ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(4);
-    }
-    loads_after();
-  }
-  __syncthreads();
-  return *ok != 0;
-}
 
 // A child of the node: its token, the node's two logits at that token and,
 // once the node's normalisers are known, q(t), p(t) and the test's uniform.
@@ -840,6 +830,8 @@ struct FusedShared {
   int32_t seqnear;
   double scan[kThreads / 64];
   int32_t wfirst[kThreads / 64];
+  uint32_t pflags[kMaxTree];   // flags and near-tie counts of the root path's nodes,
+  int32_t pnear[kMaxTree];     // decoded from their publication words
   double cmass[kFusedMaxChunks];   // q mass of each chunk (from the chunk statistics)
   double sample[4];
 };
@@ -1048,7 +1040,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   const int n = (blockIdx.x / NC) % T;
   const int b = blockIdx.x / (NC * T);
   const bool greedy = a.tau == 0.f;
-  const uint64_t base = a.epoch << 10;
+  const uint64_t base = a.epoch << 20;
   const uint32_t limit = a.spin_limit;
   const bool lead = (c == 0);   // publishes the node's state for the other nodes' groups
 
@@ -1156,40 +1148,58 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       zp_c = lzp;
     }
   }
-  ChunkStat* cs = a.stats + (static_cast<int64_t>(b * T + n) * 2) * NC;
-  if (tid == 0) {
-    auto put = [](ChunkStat* d, float m, int am, double z) {
-      uint64_t* w = reinterpret_cast<uint64_t*>(d);
+  // Chunk statistics go out as four 64-bit words per row, each carrying the
+  // call's tag in its high half (m, z low, z high, argmax | bad << 31), and
+  // are read back by polling the words themselves: no arrival counter.
+  const uint64_t stag = static_cast<uint64_t>(static_cast<uint32_t>(a.epoch)) << 32;
+  uint64_t* const cw = reinterpret_cast<uint64_t*>(a.stats) + (static_cast<int64_t>(b * T + n) * 2) * NC * 4;
+  if (tid < 8) {   // lanes 0..3 the target row, 4..7 the draft row
+    const int r = tid >> 2, k = tid & 3;
+    if (r == 0 || two) {
+      const float m = r == 0 ? mq_c : mp_c;
+      const double z = r == 0 ? zq_c : zp_c;
+      const uint64_t zb = __builtin_bit_cast(uint64_t, z);
       const uint32_t bad = (m == __builtin_inff()) ? 1u : 0u;
-      st_u64(w, static_cast<uint64_t>(__float_as_uint(m)) | (static_cast<uint64_t>(bad) << 32));
-      st_u64(w + 1, static_cast<uint64_t>(static_cast<uint32_t>(am)));
-      st_f64(&d->z, z);
-    };
-    put(cs + c, mq_c, amq, zq_c);
-    if (two) put(cs + NC + c, mp_c, -1, zp_c);
-    sh.ok = phase_barrier(narr, static_cast<uint32_t>(NC), limit) ? 1 : 0;
+      const uint32_t lo = k == 0 ? __float_as_uint(m)
+                        : k == 1 ? static_cast<uint32_t>(zb)
+                        : k == 2 ? static_cast<uint32_t>(zb >> 32)
+                                 : ((static_cast<uint32_t>(r == 0 ? amq : 0) & 0x7FFFFFFFu) | (bad << 31));
+      st_u64(cw + (r * NC + c) * 4 + k, stag | lo);
+    }
   }
-  __syncthreads();
-  if (!sh.ok) return fail_internal();
 
   // ---- every workgroup of the node combines the chunks (same arithmetic in
   // the same order everywhere, so all of them hold the same node state):
   // wave 0 the target row, wave 1 the draft row, one chunk per lane
+  if (tid == 0) sh.ok = 1;
+  __syncthreads();
   if (tid < 128) {
     const int r = tid >> 6, q = tid & 63;
     if (r == 0 || two) {
-      const ChunkStat* rs = cs + r * NC;
       float mc = kNegInf;
       uint32_t bc = 0;
       int ac = 0x7FFFFFFF;
       double zc = 0.0;
+      uint64_t w[4] = {0, 0, 0, 0};
+      bool have = q >= NC;
+      for (uint32_t it = 0;; ++it) {
+        if (!have) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = ld_u64(cw + (r * NC + q) * 4 + k);
+          have = ((w[0] & w[1] & w[2] & w[3]) >> 32) == (stag >> 32) && ((w[0] | w[1] | w[2] | w[3]) >> 32) == (stag >> 32);
+        }
+        if (__all(have)) break;
+        if (it >= limit) {
+          sh.ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
       if (q < NC) {
-        const uint64_t* w = reinterpret_cast<const uint64_t*>(rs + q);
-        const uint64_t w0 = ld_u64(w), w1 = ld_u64(w + 1), w2 = ld_u64(w + 2);
-        mc = __builtin_bit_cast(float, static_cast<uint32_t>(w0));
-        bc = static_cast<uint32_t>(w0 >> 32);
-        ac = static_cast<int>(static_cast<uint32_t>(w1));
-        zc = __builtin_bit_cast(double, w2);
+        mc = __uint_as_float(static_cast<uint32_t>(w[0]));
+        zc = __builtin_bit_cast(double, (w[1] & 0xFFFFFFFFull) | (w[2] << 32));
+        bc = static_cast<uint32_t>(w[3]) >> 31;
+        ac = static_cast<int>(static_cast<uint32_t>(w[3]) & 0x7FFFFFFFu);
       }
       const float M = wave_reduce(mc, MaxOp{});
       const uint32_t rb = wave_reduce(bc, OrU{});
@@ -1217,6 +1227,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     }
   }
   __syncthreads();
+  if (!sh.ok) return fail_internal();
   if (tid == 0 && two) sh.st.flags |= static_cast<uint32_t>(sh.iscr[1]);
   __syncthreads();
   if (tid < 64) {
@@ -1273,10 +1284,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       }
     }
     sh.st = st;
-    if (lead) {
-      store_state(&a.nodes[b * T + n], st);
-      publish(npub, base + pub_word(st));
-    }
+    if (lead) publish(npub, base + pub_word(st));
   }
   __syncthreads();
 
@@ -1334,10 +1342,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       st.s = s;
       st.next_child = i;
       sh.st = st;
-      if (fine && lead && st.kind != kNodeNeedsPass) {
-        store_state(&a.nodes[b * T + n], st);
-        publish(npub, base + pub_word(st));
-      }
+      if (fine && lead && st.kind != kNodeNeedsPass) publish(npub, base + pub_word(st));
     }
     __syncthreads();
     if (!sh.ok) return fail_internal();
@@ -1349,11 +1354,28 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // unusable (the terminal node reaches the same verdict from the words)
   const bool master = (n == 0 && c == 0);
   if (master) {
-    if (tid == 0) sh.seqflags = tokbad;
-    wait_all(nsync + 1, kSyncWords, T, base + kPubFirst, limit, &sh.ok);
-    if (sh.ok && tid < T) {
-      const uint32_t f = static_cast<uint32_t>(ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + tid].flags)));
-      if (f & EAGLE_FLAG_NONFINITE) atomicOr(&sh.seqflags, EAGLE_FLAG_NONFINITE);
+    if (tid == 0) {
+      sh.seqflags = tokbad;
+      sh.ok = 1;
+    }
+    __syncthreads();
+    if (tid < 64) {   // lane j waits for node j's first publication
+      bool seen = tid >= T;
+      for (uint32_t it = 0;; ++it) {
+        if (!seen) {
+          const uint64_t w = poll(nsync + static_cast<int64_t>(tid) * kSyncWords + 1);
+          if (w >= base + kPubFirst) {
+            seen = true;
+            if (pub_unusable(w - base)) atomicOr(&sh.seqflags, EAGLE_FLAG_NONFINITE);
+          }
+        }
+        if (__all(seen)) break;
+        if (it >= limit) {
+          sh.ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
     }
     __syncthreads();
     if (!sh.ok) return fail_internal();
@@ -1489,13 +1511,15 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         if (w >= base + kPubFirst) {
           const uint64_t code = w - base;
           const bool done = code >= kPubDone;
-          const bool unusable = done ? ((code >> 8) & 1u) : ((code - kPubFirst) & 1u);
-          if (unusable)
+          if (pub_unusable(code)) {
             state = 2;
-          else if (pos < 0)
+          } else if (pos < 0) {
             state = 1;
-          else if (done)
+          } else if (done) {
             state = (static_cast<int>((code >> 6) & 3u) == kNodeAccepted && static_cast<int>(code & 63u) == nxt) ? 1 : 2;
+            sh.pflags[tid] = pub_flags(code);   // this ancestor's flags and near ties, for the outputs
+            sh.pnear[tid] = static_cast<int32_t>((code >> 12) & 127u);
+          }
         }
       }
       if (__any(state == 2)) break;
@@ -1608,9 +1632,8 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
   __syncthreads();
   if (tid < plen - 1) {
-    const uint64_t w = ld_u64(reinterpret_cast<const uint64_t*>(&a.nodes[b * T + path_lds[tid]].flags));
-    atomicOr(&sh.seqflags, static_cast<uint32_t>(w));
-    atomicAdd(&sh.seqnear, static_cast<int32_t>(static_cast<uint32_t>(w >> 32)));
+    atomicOr(&sh.seqflags, sh.pflags[path_lds[tid]]);
+    atomicAdd(&sh.seqnear, sh.pnear[path_lds[tid]]);
   }
   __syncthreads();
   if (tid == 0) {

@@ -99,7 +99,10 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t o_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(ev::kAttnPartFloats), 256);
   const size_t o_stats = off;
-  off = align_up(off + sizeof(ev::ChunkStat) * B * T * 2 * NC, 256);
+  // per (sequence, node, row, chunk): a ChunkStat (three-kernel path) or four
+  // tagged 64-bit words (fused path)
+  const size_t stats_bytes = std::max(sizeof(ev::ChunkStat), 4 * sizeof(uint64_t)) * B * T * 2 * NC;
+  off = align_up(off + stats_bytes, 256);
   const size_t o_nodes = off;
   off = align_up(off + sizeof(ev::NodeState) * B * T, 256);
   const size_t o_fpart = off;
@@ -149,6 +152,7 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   if (e == hipSuccess) e = hipMemset(h->ws.node_sync, 0, sync_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.round_sum, 0, round_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.nodes, 0, sizeof(ev::NodeState) * B * T);
+  if (e == hipSuccess) e = hipMemset(h->ws.stats, 0, stats_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     hip_fail(nullptr, "workspace initialisation", e);
