@@ -188,28 +188,40 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   // the second 32 keys of every tile; their states are combined at the end
   const int rw = wave % (4 / KG);
   const int kh = __builtin_amdgcn_readfirstlane(wave / (4 / KG));
-  const int logical = xcd_remap(blockIdx.x, a.nwg);
+  // The launch scalars (and the first sequence's split range, prefix length
+  // and expected row offset) are requested together and waited for once,
+  // instead of one dependent round trip per use.
+  const int a_nwg = a.nwg, a_rt = a.row_tiles, a_ts = a.total_splits, a_B = a.B;
+  const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
+  const int b0_base = 0, b0_next = a.split_base[1], b0_L = a.L[0], b0_guess = a.kv0_guess[0];
+  const void* const a_k = a.k;
+  const void* const a_v = a.v;
+  const int32_t* const a_par = a.parents;
+  asm volatile("" ::"s"(a_nwg), "s"(a_rt), "s"(a_ts), "s"(a_B), "s"(T), "s"(g), "s"(R), "s"(Hq), "s"(b0_next), "s"(b0_L),
+               "s"(b0_guess), "s"(a_k), "s"(a_v), "s"(a_par));
+  const int logical = xcd_remap(blockIdx.x, a_nwg);
   // logical order: row tile fastest, then key split, then KV head, so the
   // row tiles of one K/V chunk share an XCD's L2 and every XCD receives its
   // share of the splits that carry the tree tile
-  const int rt = logical % a.row_tiles;
-  const int split = (logical / a.row_tiles) % a.total_splits;
-  const int hk = logical / (a.row_tiles * a.total_splits);
+  const int rt = logical % a_rt;
+  const int split = (logical / a_rt) % a_ts;
+  const int hk = logical / (a_rt * a_ts);
   const int64_t slot = logical;   // partial-row slot of this workgroup
-  const int b = find_seq(a, split);
-  const int s_local = split - a.split_base[b];
-  const int S = a.split_base[b + 1] - a.split_base[b];
-  const int L = a.L[b];
-  const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
+  const int b = a_B == 1 ? 0 : find_seq(a, split);
+  const int sb0 = b == 0 ? b0_base : a.split_base[b];
+  const int s_local = split - sb0;
+  const int S = (b == 0 ? b0_next : a.split_base[b + 1]) - sb0;
+  const int L = b == 0 ? b0_L : a.L[b];
   const int row_base = rt * a.rows_per_tile + rw * 16 * MB;   // lane rows: row_base + 16*rb + ln
 
   // The first tile is requested from the expected row offset of the
   // sequence, without waiting for kv_indptr[b]; the parent array is requested
   // before it, and nothing waits on either until the tile has landed.
-  const int par_lane = lane < T ? a.parents[b * T + lane] : 0;
-  int64_t kv0 = a.kv0_guess[b] >= 0 ? (int64_t)a.kv0_guess[b] : a.kv_indptr[b];
-  const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a.k) + (int64_t)hk * D;
-  const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a.v) + (int64_t)hk * D;
+  const int par_lane = lane < T ? a_par[b * T + lane] : 0;
+  const int guess = b == 0 ? b0_guess : a.kv0_guess[b];
+  int64_t kv0 = guess >= 0 ? (int64_t)guess : a.kv_indptr[b];
+  const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a_k) + (int64_t)hk * D;
+  const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a_v) + (int64_t)hk * D;
   const int64_t row_stride = (int64_t)a.Hkv * D;   // elements between consecutive KV rows
   const int64_t last_row = a.num_kv_rows - 1;
 
