@@ -196,6 +196,7 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
   k.chunk = plan.chunk;
   k.total_splits = plan.total_splits;
   k.nwg = static_cast<int>(plan.workgroups);
+  k.late_priority = plan.late_priority;
   k.scale_log2 = a->sm_scale * 1.4426950408889634f;
   for (int b = 0; b < a->batch; ++b) {
     k.L[b] = a->prefix_lens_host[b];

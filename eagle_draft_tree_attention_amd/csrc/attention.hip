@@ -161,6 +161,21 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same transfer from a wave-uniform base address held in scalar
+// registers plus a 32-bit per-lane byte offset (no 64-bit address per lane).
+__device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff_bytes, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff_bytes), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // cache policy of partial results that workgroups on other XCDs read inside
 // the same launch: system-coherent (sc0 sc1), i.e. past the XCD's own L2
 constexpr int kSysCoherent = 1 | 16;
@@ -239,14 +254,14 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
   const int l_row = lane / CH, l_pos = lane % CH;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_kv = lds_offset(kv_lds);
-  // per-lane element offsets of this wave's transfer lanes inside a tile
-  // whose rows are all valid (row r of the tile = row0 + r)
+  // per-lane byte offsets of this wave's transfer lanes inside a tile whose
+  // rows are all valid (row r of the tile = row0 + r)
   uint32_t koff[IPW], voff[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int r = (wave_u * IPW + j) * RPI + l_row;
-    koff[j] = static_cast<uint32_t>(r * row_stride + (l_pos ^ swz_k<D>(r)) * 8);
-    voff[j] = static_cast<uint32_t>(r * row_stride + (l_pos ^ swz_v<D>(r)) * 8);
+    koff[j] = static_cast<uint32_t>(r * row_stride + (l_pos ^ swz_k<D>(r)) * 8) * 2;
+    voff[j] = static_cast<uint32_t>(r * row_stride + (l_pos ^ swz_v<D>(r)) * 8) * 2;
   }
   // every prefix row of this split lies inside the KV array (checked once, so
   // full tiles need no per-row clamping)
@@ -256,13 +271,13 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     const uint32_t vdst = kdst + TILE * 2;
     if (t < n_full && split_in_bounds) {
       const int64_t row0 = kv0 + k_begin + (int64_t)t * kTileKeys;
-      const uint16_t* kt = kbase + row0 * row_stride;
-      const uint16_t* vt = vbase + row0 * row_stride;
+      const void* kt = uniform_ptr(kbase + row0 * row_stride);
+      const void* vt = uniform_ptr(vbase + row0 * row_stride);
 #pragma unroll
       for (int j = 0; j < IPW; ++j) {
         const uint32_t ldsoff = static_cast<uint32_t>((wave_u * IPW + j) * RPI * D * 2);
-        lds_dma16(kt + koff[j], kdst + ldsoff);
-        lds_dma16(vt + voff[j], vdst + ldsoff);
+        lds_dma16_sbase(kt, koff[j], kdst + ldsoff);
+        lds_dma16_sbase(vt, voff[j], vdst + ldsoff);
       }
       return;
     }
@@ -369,6 +384,19 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     // block accumulate back to back (same shape, same accumulator).
     auto qk = [&](auto h_tag) __attribute__((always_inline)) {
       constexpr int H = decltype(h_tag)::value;
+      if constexpr (MB > 1) {   // each fragment feeds MB products: read it just before them
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int r = 16 * (2 * H + kk) + ln;
+            const bf16x8_t f = *reinterpret_cast<const bf16x8_t*>(kst + r * D + (((lg + 4 * s) ^ swz_k<D>(r)) * 8));
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+              sacc[2 * H + kk][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, qf[rb][s], sacc[2 * H + kk][rb], 0, 0, 0);
+          }
+        return;
+      }
       bf16x8_t kf[KSTEPS][2];
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s)
@@ -436,6 +464,21 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     // 16 db + 4 (ln % 4) .. + 3.
     auto pv = [&](auto h_tag, const bf16x8_t (&pb)[MB], const bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
       constexpr int H = decltype(h_tag)::value;
+      if constexpr (MB > 1) {   // each fragment feeds 2 MB products: read it just before them
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          const int r = 32 * H + 4 * lg + (ln >> 2);
+          const int chunk = 2 * db + ((ln & 3) >> 1);
+          const uint16_t* vp = vst + r * D + ((chunk ^ swz_v<D>(r)) * 8) + 4 * (ln & 1);
+          const bf16x8_t f = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lds_read_tr16(vp), lds_read_tr16(vp + 16 * D),
+                                                                                   0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, pb[rb], o[rb][db], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, pl[rb], o[rb][db], 0, 0, 0);
+        }
+        return;
+      }
       bf16x8_t va[DBLK];
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
@@ -460,7 +503,14 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
     bf16x8_t pb0[MB], pl0[MB], pb1[MB], pl1[MB];
-    if constexpr (KG == 1) {
+    if constexpr (KG == 1 && MB > 1) {   // one half at a time keeps the registers in bounds
+      qk(H0{});
+      softmax(H0{}, pb0, pl0);
+      pv(H0{}, pb0, pl0);
+      qk(H1{});
+      softmax(H1{}, pb1, pl1);
+      pv(H1{}, pb1, pl1);
+    } else if constexpr (KG == 1) {
       qk(H0{});
       qk(H1{});
       softmax(H0{}, pb0, pl0);
@@ -487,6 +537,11 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
       tile(std::integral_constant<bool, true>{}, kst, is_tree, cnt);
     }
   };
+  // Older waves win issue arbitration, so a workgroup dispatched onto a CU
+  // after another one (or in a later dispatch round) falls behind and ends
+  // last.  With several tiles per workgroup, the later half of the grid
+  // runs at a raised priority, which evens out the finish times.
+  if (a.late_priority && blockIdx.x >= gridDim.x / 2) __builtin_amdgcn_s_setprio(1);
   // two stages: the stage of every LDS address is a compile-time constant
   static_assert(NST == 2, "the tile loop alternates two ring stages");
   auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {

@@ -29,6 +29,7 @@ struct AttnPlan {
   int mb;              // MFMA: 16-row blocks per wave (rows per workgroup = 64 * mb), 1 or 2
   int stages;          // MFMA: K/V tiles in the LDS ring
   int kg;              // MFMA: key groups per tile (2: wave pairs take the two 32-key halves)
+  int late_priority;   // MFMA: the later half of the grid runs at a raised wave priority
   int row_tiles;       // workgroups along R (FMA path: one row each)
   int rows_per_tile;
   int chunk;           // prefix keys per split (multiple of kTileKeys)
@@ -59,6 +60,7 @@ struct AttnKernelArgs {
   // (sequence, KV head, row tile) merges a slice of its rows once every
   // split has published the tagged m/l words of those rows
   int fused_merge;
+  int late_priority;   // raise the wave priority of the later half of the grid
   uint32_t spin_limit; // polls of the bounded wait; an expired wait flags EAGLE_FLAG_INTERNAL
   uint64_t epoch;      // strictly increasing per attention call on a handle (tags use its low 32 bits)
   uint64_t* mlrec;      // [slot][rows_per_tile][2]: m and l (low 32 bits), epoch tag (high 32 bits)

@@ -158,6 +158,10 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
       plan->part_floats = part;
       plan->chunk = static_cast<int>(chunk);
       plan->workgroups = splits * units;
+      // measured: pays from 4 prefix tiles per workgroup (tuning override
+      // EAGLE_VERIFY_ATTN_LATE_PRIORITY = 1 on, 2 off)
+      const int lp = env_int("EAGLE_VERIFY_ATTN_LATE_PRIORITY", 0);
+      plan->late_priority = (plan->path == 1 && (lp == 1 || (lp != 2 && chunk >= 4 * kTileKeys))) ? 1 : 0;
       plan->merge_workgroups = any_multi ? static_cast<int64_t>(B) * units : 0;
       break;
     }
