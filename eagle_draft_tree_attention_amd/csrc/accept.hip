@@ -1052,11 +1052,12 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       st_u64(a.round_clear + i, 0ull);
   }
 
-  // node j of this sequence: arrivals at nsync[j * kSyncWords], publication
-  // at nsync[j * kSyncWords + 1]
+  // node j of this sequence: arrival counter at nsync[j * kSyncWords] (a line
+  // of its own), publication word at pubs[j]
   uint64_t* nsync = a.node_sync + static_cast<int64_t>(b) * a.Tm * kSyncWords;
   uint64_t* const narr = nsync + n * kSyncWords;
-  uint64_t* const npub = nsync + n * kSyncWords + 1;
+  uint64_t* const pubs = a.node_pub + static_cast<int64_t>(b) * a.Tm;   // publication words of the sequence
+  uint64_t* const npub = pubs + n;
 
   auto fail_internal = [&]() {
     if (tid == 0) atomicOr(&a.flags[b], EAGLE_FLAG_INTERNAL);
@@ -1363,7 +1364,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       bool seen = tid >= T;
       for (uint32_t it = 0;; ++it) {
         if (!seen) {
-          const uint64_t w = poll(nsync + static_cast<int64_t>(tid) * kSyncWords + 1);
+          const uint64_t w = poll(pubs + tid);
           if (w >= base + kPubFirst) {
             seen = true;
             if (pub_unusable(w - base)) atomicOr(&sh.seqflags, EAGLE_FLAG_NONFINITE);
@@ -1507,7 +1508,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     bool on = false, fine = true;
     for (uint32_t it = 0;; ++it) {
       if (state == 0) {
-        const uint64_t w = poll(nsync + static_cast<int64_t>(tid) * kSyncWords + 1);
+        const uint64_t w = poll(pubs + tid);
         if (w >= base + kPubFirst) {
           const uint64_t code = w - base;
           const bool done = code >= kPubDone;

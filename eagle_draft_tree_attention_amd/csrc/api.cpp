@@ -113,7 +113,9 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
   off = align_up(off + cnt_bytes, 256);
   const size_t o_sync = off;
-  const size_t sync_bytes = sizeof(uint64_t) * ev::kSyncWords * B * T;
+  // per node: a line of kSyncWords (arrival counter), then one contiguous
+  // publication word per node
+  const size_t sync_bytes = sizeof(uint64_t) * (ev::kSyncWords + 1) * B * T;
   off = align_up(off + sync_bytes, 256);
   const size_t o_round = off;
   const size_t round_bytes = sizeof(uint64_t) * 2 * B * T * ev::kRoundWords;
@@ -133,6 +135,7 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.spart = reinterpret_cast<double*>(p + o_spart);
   h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
   h->ws.node_sync = reinterpret_cast<uint64_t*>(p + o_sync);
+  h->ws.node_pub = h->ws.node_sync + static_cast<size_t>(ev::kSyncWords) * B * T;
   h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
   h->ws.bytes = off;
   h->fused_cap[0] = ev::fused_accept_capacity(0, h->num_cus);
@@ -283,6 +286,7 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   k.off_lo = static_cast<uint32_t>(a->offset);
   k.off_hi = static_cast<uint32_t>(a->offset >> 32);
   k.node_sync = h->ws.node_sync;
+  k.node_pub = h->ws.node_pub;
   k.Tm = static_cast<int>(Tm);
   k.epoch = ++h->epoch;
   k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)

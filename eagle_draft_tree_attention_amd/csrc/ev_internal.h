@@ -115,7 +115,8 @@ struct AcceptKernelArgs {
   uint32_t* cnt_final; // [B]
   // fused path.  Synchronisation words sit one per 256-byte line so that the
   // memory-side atomics of different nodes never share a line.
-  uint64_t* node_sync;    // [Bm][Tm] lines: [0] arrivals (cumulative), [1] publication
+  uint64_t* node_sync;    // [Bm][Tm] lines: [0] arrivals (cumulative)
+  uint64_t* node_pub;     // [Bm][Tm] publication words, contiguous (one poll covers a sequence)
   uint64_t* round_sum;    // [Bm][Tm][kRoundWords]: (count << 57) | fixed-point residual mass
   uint64_t* round_clear;  // the other half, used by the previous fused call; cleared here
   int Tm;                 // node stride of node_sync and round_sum (max_tree_rows)
@@ -134,6 +135,7 @@ struct AcceptKernelArgs {
 // ---------------------------------------------------------------- host side
 struct Workspace {
   uint64_t* node_sync = nullptr;
+  uint64_t* node_pub = nullptr;
   uint64_t* round_sum = nullptr;
   float* attn_part = nullptr;   // kAttnPartFloats
   ChunkStat* stats = nullptr;
