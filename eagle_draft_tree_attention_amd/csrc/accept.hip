@@ -921,6 +921,26 @@ __device__ __forceinline__ void load_groups(const TL* row, int v0, int v1, bool 
   }
 }
 
+// The chunk [v0, v1) as 16-byte groups when every row and chunk boundary is
+// a whole group: each request is made unconditionally (a group past v1
+// re-reads the chunk's last group), so the loads of a wave form one
+// straight run and a later wait can name how many of them may still be in
+// flight.  mask_groups then replaces the groups past v1 by -inf.
+template <typename TL, int NV>
+__device__ __forceinline__ void request_groups(const TL* row, int v0, int v1, u32x4_t (&w)[NV]) {
+  constexpr int G = Pack<TL>::G;
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj)
+    w[jj] = *reinterpret_cast<const u32x4_t*>(row + min(v0 + group_index<TL>(jj), v1 - G));
+}
+template <typename TL, int NV>
+__device__ __forceinline__ void mask_groups(int v0, int v1, u32x4_t (&w)[NV]) {
+  const uint32_t ni = Pack<TL>::neg_inf_word();
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj)
+    if (v0 + group_index<TL>(jj) >= v1) w[jj] = u32x4_t{ni, ni, ni, ni};
+}
+
 // Row statistics of this thread's values: the maximum, or +inf when a NaN or
 // +inf is present (the row is then unusable).
 template <typename TL, int NV>
@@ -1027,7 +1047,9 @@ __device__ bool phase_barrier(uint64_t* w, uint32_t group, uint32_t limit) {
   return true;
 }
 
-template <typename TL>
+// VEC: rows and chunks are whole 16-byte groups (then every chunk is read
+// with straight-line vector requests)
+template <typename TL, bool VEC>
 __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a) {
   constexpr int G = Pack<TL>::G;
   constexpr int NV = kPerThread / G;   // 16-byte groups per thread and row
@@ -1064,51 +1086,58 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   };
 
   // ---- sequence validity (the same verdict in every workgroup of b) and
-  // this node's children, in ascending index = child ordinal
-  load_tree(a, b, sh.ti);
-  if (!sh.ti.ok) {
-    if (n == 0 && c == 0) write_poison(a, b, EAGLE_FLAG_BAD_TREE);
-    return;
-  }
+  // this node's children, in ascending index = child ordinal.  Every wave
+  // reads the sequence's parents and tokens one per lane and requests its
+  // share of the target chunk right behind them, so the row transfer is
+  // under way while the tree is checked; the draft chunk follows once the
+  // node is known to have children.  (Loads of one wave complete in order:
+  // waiting for the parents leaves the chunk requests outstanding.)
+  const int lane = tid & 63;
+  const int v0 = c * kVocabChunk, v1 = min(V, v0 + kVocabChunk);
   const int64_t rowoff = static_cast<int64_t>(b * T + n) * V;
   const TL* trow = reinterpret_cast<const TL*>(a.target) + rowoff;
   const TL* drow = reinterpret_cast<const TL*>(a.draft) + rowoff;
+  const int li = b * T + min(lane, T - 1);   // lanes past the tree re-read its last row
+  int par = a.parents[li];
+  int tok = a.tokens[li];
+  u32x4_t wq[NV], wd[NV];
+  if constexpr (VEC) request_groups<TL, NV>(trow, v0, v1, wq);
+  else load_groups<TL, NV>(trow, v0, v1, false, wq);
+  if (lane >= T) par = 0;
+  if (lane < 1 || lane >= T) tok = 0;
+  const bool good = lane >= T || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
+  if (__any(!good)) {
+    if (n == 0 && c == 0) write_poison(a, b, EAGLE_FLAG_BAD_TREE);
+    return;
+  }
+  const bool tb = lane >= 1 && lane < T && (tok < 0 || tok >= V);
+  const bool is_child = lane >= 1 && lane < T && par == n;
+  const uint64_t kids_mask = __ballot(is_child);
+  const int nkids = __popcll(kids_mask);
+  // a token outside the vocabulary poisons the sequence too, but the row
+  // checks still run so that every unusable input is reported
+  const uint32_t tokbad = __any(tb) ? EAGLE_FLAG_BAD_TOKEN : 0u;
+  const bool two = nkids > 0 && !greedy;
+  if (two) {
+    if constexpr (VEC) request_groups<TL, NV>(drow, v0, v1, wd);
+    else load_groups<TL, NV>(drow, v0, v1, false, wd);
+  }
   if (tid < 64) {
-    int tok = 0;
-    bool tb = false;
-    if (tid >= 1 && tid < T) {
-      tok = a.tokens[b * T + tid];
-      tb = tok < 0 || tok >= V;
-    }
-    const bool is_child = tid >= 1 && tid < T && sh.ti.par[tid] == n;
-    const uint64_t kids_mask = __ballot(is_child);
-    const bool any_tb = __any(tb);
+    sh.ti.par[lane] = par;
     if (is_child) {
-      const int ord = __popcll(kids_mask & ((1ull << tid) - 1ull));
+      const int ord = __popcll(kids_mask & ((1ull << lane) - 1ull));
       Cand cd;
       cd.qt = cd.pt = cd.r = 0.0;
       cd.xq = cd.yp = 0.f;
       cd.tok = tok;
-      cd.child = tid;
+      cd.child = lane;
       if (!greedy && !tb) {
         cd.xq = logit<TL>(trow, tok);
         cd.yp = logit<TL>(drow, tok);
       }
       sh.cand[ord] = cd;
     }
-    if (tid == 0) {
-      sh.nkids = __popcll(kids_mask);
-      // a token outside the vocabulary poisons the sequence too, but the row
-      // checks still run so that every unusable input is reported
-      sh.seqflags = any_tb ? EAGLE_FLAG_BAD_TOKEN : 0u;
-    }
   }
-  __syncthreads();
-  const uint32_t tokbad = sh.seqflags;
-  const int nkids = sh.nkids;
-  const bool two = nkids > 0 && !greedy;
-  const int v0 = c * kVocabChunk, v1 = min(V, v0 + kVocabChunk);
-  const bool vecpath = a.vec_ok != 0 && ((v1 - v0) % G) == 0;
 
   // ---- statistics pass: the chunk is loaded once, kept in LDS, and its
   // statistics come straight from the loaded registers
@@ -1116,9 +1145,10 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   int amq = -1;
   double zq_c = 0.0, zp_c = 0.0;
   {
-    u32x4_t wq[NV], wd[NV];
-    load_groups<TL, NV>(trow, v0, v1, vecpath, wq);
-    if (two) load_groups<TL, NV>(drow, v0, v1, vecpath, wd);
+    if constexpr (VEC) {
+      mask_groups<TL, NV>(v0, v1, wq);
+      if (two) mask_groups<TL, NV>(v0, v1, wd);
+    }
 #pragma unroll
     for (int jj = 0; jj < NV; ++jj) {
       *reinterpret_cast<u32x4_t*>(lq + group_index<TL>(jj)) = wq[jj];
@@ -1652,7 +1682,8 @@ template <typename TL>
 hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
   const dim3 block(kThreads);
   if (a.fused) {
-    hipLaunchKernelGGL((sa_fused<TL>), dim3(static_cast<unsigned>(a.B * a.T * a.NC)), block, 0, st, a);
+    if (a.vec_ok) hipLaunchKernelGGL((sa_fused<TL, true>), dim3(static_cast<unsigned>(a.B * a.T * a.NC)), block, 0, st, a);
+    else hipLaunchKernelGGL((sa_fused<TL, false>), dim3(static_cast<unsigned>(a.B * a.T * a.NC)), block, 0, st, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((sa_stats<TL>), dim3(static_cast<unsigned>(a.B * a.T * 2 * a.NC)), block, 0, st, a);
@@ -1672,12 +1703,16 @@ hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
 }  // namespace
 
 int fused_accept_capacity(int logits_bf16, int num_cus) {
-  int per_cu = 0;
-  (void)kFusedMaxChunks;
-  const hipError_t e = logits_bf16
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&sa_fused<uint16_t>), kThreads, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&sa_fused<float>), kThreads, 0);
-  if (e != hipSuccess || per_cu <= 0) return 0;
+  // the two loader variants must both fit: the smaller occupancy decides
+  int per_cu = 1 << 30;
+  const void* kernels[2] = {
+      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, true>) : reinterpret_cast<const void*>(&sa_fused<float, true>),
+      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, false>) : reinterpret_cast<const void*>(&sa_fused<float, false>)};
+  for (const void* k : kernels) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess || n <= 0) return 0;
+    per_cu = n < per_cu ? n : per_cu;
+  }
   return per_cu * num_cus;
 }
 
