@@ -1419,6 +1419,51 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   if (sh.st.kind == kNodeAccepted) return;
   // an unusable row poisons the whole sequence: nothing to sample here
   if (sh.st.flags & EAGLE_FLAG_NONFINITE) return;
+  const bool leaf = (sh.st.kind == kNodeLeaf);
+
+  // ---- the walk ends at this node iff every ancestor accepted the next node
+  // of this root path and no node of the sequence has an unusable row.
+  // Lane j of wave 0 follows node j's publication word: wpos is node j's
+  // position on the root path if it is an ancestor (else -1), wnxt the
+  // node after it there.
+  if (tid == 0) sh.iscr[0] = root_path(sh.ti, n, path_lds);
+  __syncthreads();
+  const int plen = sh.iscr[0];
+  int wpos = -1, wnxt = -1;
+  if (tid < 64) {
+    for (int i = 0; i + 1 < plen; ++i)
+      if (path_lds[i] == tid) wpos = i;
+    wnxt = wpos >= 0 ? path_lds[wpos + 1] : -1;
+  }
+  // 0: undecided, 1: consistent with the walk ending here, 2: rules it out.
+  // A final word of an ancestor also gives its flags and near ties (record).
+  auto walk_state = [&](uint64_t w, bool record) __attribute__((always_inline)) -> int {
+    if (w < base + kPubFirst) return 0;
+    const uint64_t code = w - base;
+    if (pub_unusable(code)) return 2;
+    if (wpos < 0) return 1;
+    if (code < kPubDone) return 0;
+    if (record) {
+      sh.pflags[tid] = pub_flags(code);
+      sh.pnear[tid] = static_cast<int32_t>((code >> 12) & 127u);
+    }
+    return (static_cast<int>((code >> 6) & 3u) == kNodeAccepted && static_cast<int>(code & 63u) == wnxt) ? 1 : 2;
+  };
+  // Decisions published by now may already rule this node out: then it
+  // skips the terminal preparation.  Its workgroups still arrive at the
+  // node's phase counter, where other workgroups of the node (which read
+  // the words earlier) may be waiting.
+  if (tid < 64) {
+    const int st0 = tid < T ? walk_state(poll(pubs + tid), false) : 1;
+    const bool out = __any(st0 == 2);
+    if (tid == 0) sh.iscr[1] = out ? 1 : 0;
+  }
+  __syncthreads();
+  if (sh.iscr[1]) {
+    if (!leaf && !greedy && tid == 0)
+      __hip_atomic_fetch_add(narr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    return;
+  }
 
   // ---- terminal distribution of this node, prepared before the walk is
   // known to end here (it overlaps the walk): inverse CDF of the residual
@@ -1427,7 +1472,6 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // tokens.  Every workgroup of the node publishes its chunk mass and
   // finds the chunk holding u*S; only that workgroup continues once the
   // walk is known to end here.
-  const bool leaf = (sh.st.kind == kNodeLeaf);
   const double Ct = leaf ? 0.0 : sh.st.C;
   const int i0 = tid * kPerThread;
   // weight of the token at LDS slot i0 + jj * G + e, from its two logits
@@ -1522,37 +1566,13 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     degen = (sh.iscr[3] & 0x40000000) != 0;
   }
 
-  // ---- is this node where the walk ends?  Yes iff every ancestor accepted
-  // the next node of this root path and no node of the sequence has an
-  // unusable row.  Lane j of wave 0 polls node j's publication word; the
-  // wave gives up as soon as one word rules this node out.
-  if (tid == 0) sh.iscr[0] = root_path(sh.ti, n, path_lds);
-  __syncthreads();
+  // ---- is this node where the walk ends?  The wave gives up as soon as one
+  // word rules this node out.
   if (tid < 64) {
-    const int pl = sh.iscr[0];
-    int pos = -1;   // position of node tid on the root path, if an ancestor
-    for (int i = 0; i + 1 < pl; ++i)
-      if (path_lds[i] == tid) pos = i;
-    const int nxt = pos >= 0 ? path_lds[pos + 1] : -1;
-    int state = tid < T ? 0 : 1;   // 0 undecided, 1 consistent with the walk ending here, 2 not
+    int state = tid < T ? 0 : 1;
     bool on = false, fine = true;
     for (uint32_t it = 0;; ++it) {
-      if (state == 0) {
-        const uint64_t w = poll(pubs + tid);
-        if (w >= base + kPubFirst) {
-          const uint64_t code = w - base;
-          const bool done = code >= kPubDone;
-          if (pub_unusable(code)) {
-            state = 2;
-          } else if (pos < 0) {
-            state = 1;
-          } else if (done) {
-            state = (static_cast<int>((code >> 6) & 3u) == kNodeAccepted && static_cast<int>(code & 63u) == nxt) ? 1 : 2;
-            sh.pflags[tid] = pub_flags(code);   // this ancestor's flags and near ties, for the outputs
-            sh.pnear[tid] = static_cast<int32_t>((code >> 12) & 127u);
-          }
-        }
-      }
+      if (state == 0) state = walk_state(poll(pubs + tid), true);
       if (__any(state == 2)) break;
       if (__all(state == 1)) {
         on = true;
@@ -1572,7 +1592,6 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   __syncthreads();
   if (!sh.ok) return fail_internal();
   if (!sh.onpath) return;
-  const int plen = sh.iscr[0];
   const int len = plen - 1;   // accepted draft nodes
   if (greedy && c != 0) return;
 
