@@ -1565,6 +1565,9 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     cstar = sh.iscr[3] & 0x3FFFFFFF;
     degen = (sh.iscr[3] & 0x40000000) != 0;
   }
+  // only the workgroup that samples (the chunk holding u*S; chunk 0 in
+  // greedy mode) needs to know whether the walk ends here
+  if (c != (greedy ? 0 : cstar)) return;
 
   // ---- is this node where the walk ends?  The wave gives up as soon as one
   // word rules this node out.
@@ -1593,14 +1596,12 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   if (!sh.ok) return fail_internal();
   if (!sh.onpath) return;
   const int len = plen - 1;   // accepted draft nodes
-  if (greedy && c != 0) return;
 
   // ---- terminal sample (the workgroup of the chunk holding u*S)
   int final_tok = sh.st.argmax;
   uint32_t extra_flags = 0;
   int extra_near = 0;
   if (!greedy) {
-    if (c != cstar) return;
     const double S = sh.sample[1], thr = sh.sample[2];
     const bool q_only = leaf || degen;
     if (degen && !leaf) {   // the residual vanished: sample q instead
