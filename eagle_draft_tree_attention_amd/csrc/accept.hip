@@ -1031,22 +1031,6 @@ __device__ int root_path(const TreeInfo& ti, int n, int* path) {
   return len;
 }
 
-// Arrive at a phase counter shared by `group` workgroups and wait until all
-// of them have arrived (thread 0).  The counter only grows: each phase adds
-// `group`.  This workgroup's results were stored before the arrival.
-__device__ bool phase_barrier(uint64_t* w, uint32_t group, uint32_t limit) {
-  stores_done();
-  const uint64_t old = __hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  const uint64_t target = (old / group + 1) * group;
-  uint32_t it = 0;
-  while (poll(w) < target) {
-    if (++it > limit) return false;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  loads_after();
-  return true;
-}
-
 // VEC: rows and chunks are whole 16-byte groups (then every chunk is read
 // with straight-line vector requests)
 template <typename TL, bool VEC>
@@ -1074,10 +1058,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       st_u64(a.round_clear + i, 0ull);
   }
 
-  // node j of this sequence: arrival counter at nsync[j * kSyncWords] (a line
-  // of its own), publication word at pubs[j]
-  uint64_t* nsync = a.node_sync + static_cast<int64_t>(b) * a.Tm * kSyncWords;
-  uint64_t* const narr = nsync + n * kSyncWords;
+  // node j of this sequence publishes its decisions at pubs[j]
   uint64_t* const pubs = a.node_pub + static_cast<int64_t>(b) * a.Tm;   // publication words of the sequence
   uint64_t* const npub = pubs + n;
 
@@ -1450,9 +1431,11 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     return (static_cast<int>((code >> 6) & 3u) == kNodeAccepted && static_cast<int>(code & 63u) == wnxt) ? 1 : 2;
   };
   // Decisions published by now may already rule this node out: then it
-  // skips the terminal preparation.  Its workgroups still arrive at the
-  // node's phase counter, where other workgroups of the node (which read
-  // the words earlier) may be waiting.
+  // skips the terminal preparation.  Its workgroups still publish (empty)
+  // chunk masses, which other workgroups of the node (that read the words
+  // earlier) may be waiting for; the node cannot be sampled from, so their
+  // values do not matter.
+  uint64_t* const mw = reinterpret_cast<uint64_t*>(a.spart) + static_cast<int64_t>(b * T + n) * NC * 4;
   if (tid < 64) {
     const int st0 = tid < T ? walk_state(poll(pubs + tid), false) : 1;
     const bool out = __any(st0 == 2);
@@ -1460,8 +1443,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
   __syncthreads();
   if (sh.iscr[1]) {
-    if (!leaf && !greedy && tid == 0)
-      __hip_atomic_fetch_add(narr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (!leaf && !greedy && tid < 4) st_u64(mw + c * 4 + tid, stag);
     return;
   }
 
@@ -1525,23 +1507,45 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   if (!greedy) {
     sums(leaf, ts, tq);
     offset = scan_offsets(ts);
-    double* const sp = a.spart + (static_cast<int64_t>(b * T + n) * NC) * 2;
-    if (!leaf) {   // residual masses of every chunk: published, then read back
+    // residual and q masses of every chunk: four words per chunk (low and
+    // high halves of the two doubles) whose high halves carry the call's
+    // tag, read back by polling the words themselves (as the statistics)
+    if (!leaf) {
       const double mqsum = block_reduce(tq, AddD{}, sh.dscr);
-      if (tid == 0) {
-        st_f64(&sp[2 * c], chunk_total);
-        st_f64(&sp[2 * c + 1], mqsum);
-        sh.ok = phase_barrier(narr, static_cast<uint32_t>(NC), limit) ? 1 : 0;
+      if (tid < 4) {
+        const uint64_t bits = __builtin_bit_cast(uint64_t, tid < 2 ? chunk_total : mqsum);
+        st_u64(mw + c * 4 + tid, stag | ((tid & 1) ? (bits >> 32) : (bits & 0xFFFFFFFFull)));
       }
-      __syncthreads();
-      if (!sh.ok) return fail_internal();
     }
     // the chunk holding u * S (wave 0, one chunk per lane; same arithmetic
     // in every workgroup of the node)
     if (tid < 64) {
       // leaf: the chunk statistics already hold every chunk's q mass
-      const double mr = (tid >= NC) ? 0.0 : (leaf ? sh.cmass[tid] : ld_f64(&sp[2 * tid]));
-      const double mq = (tid >= NC) ? 0.0 : (leaf ? mr : ld_f64(&sp[2 * tid + 1]));
+      double mr = 0.0, mq = 0.0;
+      if (leaf) {
+        mr = mq = tid < NC ? sh.cmass[tid] : 0.0;
+      } else {
+        uint64_t w[4] = {0, 0, 0, 0};
+        bool have = tid >= NC, fine = true;
+        for (uint32_t it = 0;; ++it) {
+          if (!have) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = ld_u64(mw + tid * 4 + k);
+            have = ((w[0] & w[1] & w[2] & w[3]) >> 32) == (stag >> 32) && ((w[0] | w[1] | w[2] | w[3]) >> 32) == (stag >> 32);
+          }
+          if (__all(have)) break;
+          if (it >= limit) {
+            fine = false;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (tid == 0) sh.ok = fine ? 1 : 0;
+        if (tid < NC) {
+          mr = __builtin_bit_cast(double, (w[0] & 0xFFFFFFFFull) | (w[1] << 32));
+          mq = __builtin_bit_cast(double, (w[2] & 0xFFFFFFFFull) | (w[3] << 32));
+        }
+      }
       const double sr = wave_reduce(mr, AddD{});
       const bool degen = !(sr > 0.0);
       const double m = degen ? mq : mr;
@@ -1562,6 +1566,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       }
     }
     __syncthreads();
+    if (!leaf && !sh.ok) return fail_internal();
     cstar = sh.iscr[3] & 0x3FFFFFFF;
     degen = (sh.iscr[3] & 0x40000000) != 0;
   }

@@ -108,14 +108,14 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t o_fpart = off;
   off = align_up(off + sizeof(double) * 2 * B * T * NC, 256);   // two round buffers
   const size_t o_spart = off;
-  off = align_up(off + sizeof(double) * B * T * NC * 2, 256);
+  const size_t spart_bytes = sizeof(uint64_t) * 4 * B * T * NC;   // fused: four tagged words per chunk
+  off = align_up(off + spart_bytes, 256);
   const size_t o_cnt = off;
   const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
   off = align_up(off + cnt_bytes, 256);
   const size_t o_sync = off;
-  // per node: a line of kSyncWords (arrival counter), then one contiguous
-  // publication word per node
-  const size_t sync_bytes = sizeof(uint64_t) * (ev::kSyncWords + 1) * B * T;
+  // one publication word per node, contiguous per sequence
+  const size_t sync_bytes = sizeof(uint64_t) * B * T;
   off = align_up(off + sync_bytes, 256);
   const size_t o_round = off;
   const size_t round_bytes = sizeof(uint64_t) * 2 * B * T * ev::kRoundWords;
@@ -134,8 +134,7 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.fpart = reinterpret_cast<double*>(p + o_fpart);
   h->ws.spart = reinterpret_cast<double*>(p + o_spart);
   h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
-  h->ws.node_sync = reinterpret_cast<uint64_t*>(p + o_sync);
-  h->ws.node_pub = h->ws.node_sync + static_cast<size_t>(ev::kSyncWords) * B * T;
+  h->ws.node_pub = reinterpret_cast<uint64_t*>(p + o_sync);
   h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
   h->ws.bytes = off;
   h->fused_cap[0] = ev::fused_accept_capacity(0, h->num_cus);
@@ -146,13 +145,14 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
     for (int v = 0; v < ev::kMfmaVariants; ++v)
       h->attn_cap[desc->head_dim == 128 ? 1 : 0][v] = ev::attention_capacity(desc->head_dim, v, h->num_cus);
   // counters start at zero; every call leaves them at zero again.  On the
-  // fused path, arrival words only grow, publication words carry the call
+  // fused path, publication, statistics and chunk-mass words carry the call
   // epoch, and each fused call clears the round words the previous one used.
   // The attention partials start at zero so that no tagged m/l word holds a
   // call's epoch before that call writes it.
   e = hipMemset(h->ws.counters, 0, cnt_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.attn_part, 0, sizeof(float) * static_cast<size_t>(ev::kAttnPartFloats));
-  if (e == hipSuccess) e = hipMemset(h->ws.node_sync, 0, sync_bytes);
+  if (e == hipSuccess) e = hipMemset(h->ws.node_pub, 0, sync_bytes);
+  if (e == hipSuccess) e = hipMemset(h->ws.spart, 0, spart_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.round_sum, 0, round_bytes);
   if (e == hipSuccess) e = hipMemset(h->ws.nodes, 0, sizeof(ev::NodeState) * B * T);
   if (e == hipSuccess) e = hipMemset(h->ws.stats, 0, stats_bytes);
@@ -285,7 +285,6 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   k.seed_hi = static_cast<uint32_t>(a->seed >> 32);
   k.off_lo = static_cast<uint32_t>(a->offset);
   k.off_hi = static_cast<uint32_t>(a->offset >> 32);
-  k.node_sync = h->ws.node_sync;
   k.node_pub = h->ws.node_pub;
   k.Tm = static_cast<int>(Tm);
   k.epoch = ++h->epoch;

@@ -19,7 +19,6 @@ constexpr int64_t kAttnPartFloats = 32ll << 20;   // 128 MiB of split partials
 // (row, split) pairs whose merge weights fit in the smallest (D = 64) MFMA
 // K/V ring next to the 4 KB of lane partials: 2 floats per pair
 constexpr int kFusedMergePairs = (2 * 2 * 64 * 64 * 2 - 4096) / 8;
-constexpr int kSyncWords = 32;       // 64-bit words per synchronisation line (256 bytes)
 constexpr int kRoundWords = kMaxTree;   // residual-mass rounds a node can need (< its children)
 
 // ---------------------------------------------------------------- attention
@@ -109,17 +108,15 @@ struct AcceptKernelArgs {
   ChunkStat* stats;    // [B][T][2][NC]
   NodeState* nodes;    // [B][T]
   double* fpart;       // [B][T][NC]
-  double* spart;       // fused: [B][T][NC][2] chunk masses; three-kernel path: [B][NC]
+  double* spart;       // fused: [B][T][NC][4] tagged words (chunk masses); three-kernel path: [B][NC]
   uint32_t* cnt_stats; // [B][T]
   uint32_t* cnt_pass;  // [B][T]
   uint32_t* cnt_final; // [B]
-  // fused path.  Synchronisation words sit one per 256-byte line so that the
-  // memory-side atomics of different nodes never share a line.
-  uint64_t* node_sync;    // [Bm][Tm] lines: [0] arrivals (cumulative)
+  // fused path
   uint64_t* node_pub;     // [Bm][Tm] publication words, contiguous (one poll covers a sequence)
   uint64_t* round_sum;    // [Bm][Tm][kRoundWords]: (count << 57) | fixed-point residual mass
   uint64_t* round_clear;  // the other half, used by the previous fused call; cleared here
-  int Tm;                 // node stride of node_sync and round_sum (max_tree_rows)
+  int Tm;                 // node stride of node_pub and round_sum (max_tree_rows)
   int zero_b;             // batch of the previous fused call (extent of round_clear to clear)
   uint64_t epoch;         // strictly increasing per call on a handle
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
@@ -134,7 +131,6 @@ struct AcceptKernelArgs {
 
 // ---------------------------------------------------------------- host side
 struct Workspace {
-  uint64_t* node_sync = nullptr;
   uint64_t* node_pub = nullptr;
   uint64_t* round_sum = nullptr;
   float* attn_part = nullptr;   // kAttnPartFloats
