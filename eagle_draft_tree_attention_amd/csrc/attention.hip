@@ -43,6 +43,7 @@ namespace ev {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -354,23 +355,26 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) anc_row[rb] = anc_lds[node[rb]];
 
-  f32x4_t o[MB][DBLK];
+  // O^T accumulators, and the row sums of P: the matrix unit adds them as the
+  // product of an all-ones block with P^T (every lane of a row then holds the
+  // row's whole sum, of exactly the hi + lo values that enter O)
+  f32x4_t o[MB][DBLK], lacc[MB];
   float m_run[MB], l_run[MB];
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) {
     m_run[rb] = kNegInf;
-    l_run[rb] = 0.f;
+    lacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8_t ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                         (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   const float c = a.scale_log2;
 
   // One 64-key tile from ring stage ST (a compile-time constant, so every LDS
   // address below is a per-lane register plus an immediate).  MASK: partial
   // prefix tile (key < cnt) or tree tile (key < T and key an ancestor of the
-  // row's node).  The tile is processed as two 32-key halves so that each
-  // wave always has independent matrix and vector work in flight:
-  //   QK(0) QK(1) | softmax(0) under QK(1) | PV(0) | softmax(1) under PV(0) | PV(1)
+  // row's node).  The tile is processed as two 32-key halves.
   auto tile = [&](auto mask_tag, const uint16_t* kst, bool is_tree, int cnt) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* vst = kst + TILE;
@@ -413,12 +417,12 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
           for (int rb = 0; rb < MB; ++rb)
             sacc[2 * H + kk][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s][kk], qf[rb][s], sacc[2 * H + kk][rb], 0, 0, 0);
     };
-    // P for the half: masks, lazy reference maximum, exp2, bf16 hi/lo pair
-    auto softmax = [&](auto h_tag, bf16x8_t (&pb)[MB], bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
+    // Masks of the half (partial prefix tile: key < cnt; tree tile: ancestors).
+    auto mask_half = [&](auto h_tag) __attribute__((always_inline)) {
       constexpr int H = decltype(h_tag)::value;
+      if constexpr (MASK) {
 #pragma unroll
-      for (int rb = 0; rb < MB; ++rb) {
-        if constexpr (MASK) {
+        for (int rb = 0; rb < MB; ++rb) {
           // visible keys of this row as a 64-bit word: the ancestor bits on
           // the tree tile, the first cnt keys on a partial prefix tile
           const uint64_t vis = is_tree ? anc_row[rb] : (cnt >= 64 ? ~0ull : ((1ull << cnt) - 1ull));
@@ -430,38 +434,94 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
               sacc[2 * H + kk][rb][i] = ((nib >> i) & 1u) ? sacc[2 * H + kk][rb][i] : kNegInf;
           }
         }
-        const f32x4_t s0 = sacc[2 * H][rb], s1 = sacc[2 * H + 1][rb];
-        float tmax = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])), fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
-        // The reference maximum of a row moves only when a score exceeds it
-        // by more than 2^kRescaleLog2 (P then stays below that, harmless in
-        // fp32 and in the bf16 hi/lo pair), so most halves skip the
-        // cross-lane maximum and the rescale of O.  The test is wave-uniform.
-        if (__any(tmax * c > m_run[rb] + kRescaleLog2)) {
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-          const float m_new = fmaxf(m_run[rb], tmax * c);
-          const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-          l_run[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
-          m_run[rb] = m_new;
-        }
-        const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * H + (e >> 2)][rb][e & 3], c, -m_use));
-          psum += pv;
-          const __bf16 hi = (__bf16)pv;
-          pb[rb][e] = hi;
-          pl[rb][e] = (__bf16)(pv - (float)hi);
-        }
-        l_run[rb] += psum;
       }
     };
-    // O^T += V^T P^T for keys 32 h .. 32 h + 31.  Lane (lg, ln) points the
-    // transposing read at key 32 h + 4 lg + ln/4 (and + 16), dims
-    // 16 db + 4 (ln % 4) .. + 3.
+    // this lane's largest score of key blocks [kb0, kb1)
+    auto lane_max = [&](int rb, int kb0, int kb1) __attribute__((always_inline)) -> float {
+      float tmax = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        if (kb >= kb0 && kb < kb1)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(sacc[kb][rb][0], sacc[kb][rb][1]), fmaxf(sacc[kb][rb][2], sacc[kb][rb][3])));
+      return tmax;
+    };
+    // The reference maximum of a row moves only when a score exceeds it by
+    // more than 2^kRescaleLog2 (P then stays below that, harmless in fp32
+    // and in the bf16 hi/lo pair), so most tiles skip the cross-lane maximum
+    // and the rescale of O.  The test is wave-uniform.
+    auto rescale = [&](int rb, float tmax) __attribute__((always_inline)) {
+      if (__any(tmax * c > m_run[rb] + kRescaleLog2)) {
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run[rb], tmax * c);
+        const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        lacc[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
+        m_run[rb] = m_new;
+      }
+    };
+    // P of the half from the current reference maximum: exp2, then the bf16
+    // pair hi = bf16(p), lo = bf16(p - hi), two values at a time (the packed
+    // hi word gives both hi values back as fp32 by a shift and a mask)
+    auto p_half = [&](auto h_tag, bf16x8_t (&pb)[MB], bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
+      constexpr int H = decltype(h_tag)::value;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) {
+        const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * H + (e >> 2)][rb][e & 3], c, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * H + (e >> 2)][rb][(e & 3) + 1], c, -m_use));
+          const bf16x2_t h = {(__bf16)p0, (__bf16)p1};
+          const uint32_t hw = __builtin_bit_cast(uint32_t, h);
+          const bf16x2_t l = {(__bf16)(p0 - __uint_as_float(hw << 16)), (__bf16)(p1 - __uint_as_float(hw & 0xFFFF0000u))};
+          pb[rb][e] = h[0];
+          pb[rb][e + 1] = h[1];
+          pl[rb][e] = l[0];
+          pl[rb][e + 1] = l[1];
+        }
+      }
+    };
+    // P for the half: masks, lazy reference maximum, exp2, bf16 hi/lo pair
+    auto softmax = [&](auto h_tag, bf16x8_t (&pb)[MB], bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
+      constexpr int H = decltype(h_tag)::value;
+      mask_half(h_tag);
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) rescale(rb, lane_max(rb, 2 * H, 2 * H + 2));
+      p_half(h_tag, pb, pl);
+    };
+    // V^T fragments of the half: lane (lg, ln) points the transposing read
+    // at key 32 h + 4 lg + ln/4 (and + 16), dims 16 db + 4 (ln % 4) .. + 3
+    auto read_v = [&](auto h_tag, bf16x8_t (&va)[DBLK]) __attribute__((always_inline)) {
+      constexpr int H = decltype(h_tag)::value;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const int r = 32 * H + 4 * lg + (ln >> 2);
+        const int chunk = 2 * db + ((ln & 3) >> 1);
+        const uint16_t* vp = vst + r * D + ((chunk ^ swz_v<D>(r)) * 8) + 4 * (ln & 1);
+        const i16x4_t lo4 = lds_read_tr16(vp);
+        const i16x4_t hi4 = lds_read_tr16(vp + 16 * D);   // key + 16: same swizzle (r & 7 unchanged)
+        va[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    };
+    // hi products of every column block, then the lo products: the two
+    // MFMAs into one accumulator are DBLK instructions apart
+    auto pv_mfma = [&](const bf16x8_t (&va)[DBLK], const bf16x8_t (&pb)[MB], const bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[rb], o[rb][db], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[rb], lacc[rb], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[rb], o[rb][db], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[rb], lacc[rb], 0, 0, 0);
+    };
+    // O^T += V^T P^T for keys 32 h .. 32 h + 31
     auto pv = [&](auto h_tag, const bf16x8_t (&pb)[MB], const bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
       constexpr int H = decltype(h_tag)::value;
       if constexpr (MB > 1) {   // each fragment feeds 2 MB products: read it just before them
@@ -477,28 +537,16 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
 #pragma unroll
           for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, pl[rb], o[rb][db], 0, 0, 0);
         }
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[rb], lacc[rb], 0, 0, 0);
+          lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[rb], lacc[rb], 0, 0, 0);
+        }
         return;
       }
       bf16x8_t va[DBLK];
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int r = 32 * H + 4 * lg + (ln >> 2);
-        const int chunk = 2 * db + ((ln & 3) >> 1);
-        const uint16_t* vp = vst + r * D + ((chunk ^ swz_v<D>(r)) * 8) + 4 * (ln & 1);
-        const i16x4_t lo4 = lds_read_tr16(vp);
-        const i16x4_t hi4 = lds_read_tr16(vp + 16 * D);   // key + 16: same swizzle (r & 7 unchanged)
-        va[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-      // hi products of every column block, then the lo products: the two
-      // MFMAs into one accumulator are DBLK instructions apart
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pb[rb], o[rb][db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[db], pl[rb], o[rb][db], 0, 0, 0);
+      read_v(h_tag, va);
+      pv_mfma(va, pb, pl);
     };
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
@@ -511,12 +559,23 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
       softmax(H1{}, pb1, pl1);
       pv(H1{}, pb1, pl1);
     } else if constexpr (KG == 1) {
+      // one reference-maximum test for the whole tile, and every V fragment
+      // requested before the softmax: the exponentials of both halves and
+      // the PV products then form one straight run (no branch between them),
+      // so the matrix work of one half overlaps the vector work of the other
+      // and the LDS reads of V overlap the softmax
       qk(H0{});
       qk(H1{});
-      softmax(H0{}, pb0, pl0);
-      pv(H0{}, pb0, pl0);
-      softmax(H1{}, pb1, pl1);
-      pv(H1{}, pb1, pl1);
+      bf16x8_t va0[DBLK], va1[DBLK];
+      read_v(H0{}, va0);
+      read_v(H1{}, va1);
+      mask_half(H0{});
+      mask_half(H1{});
+      rescale(0, lane_max(0, 0, 4));
+      p_half(H0{}, pb0, pl0);
+      p_half(H1{}, pb1, pl1);
+      pv_mfma(va0, pb0, pl0);
+      pv_mfma(va1, pb1, pl1);
     } else if (kh == 0) {
       qk(H0{});
       softmax(H0{}, pb0, pl0);
@@ -555,6 +614,11 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
   }
+
+  // every lane of a row holds the row's whole sum: a quarter per lane keeps
+  // the sums over the row's four lanes below exact (powers of two)
+#pragma unroll
+  for (int rb = 0; rb < MB; ++rb) l_run[rb] = lacc[rb][0] * 0.25f;
 
   if constexpr (KG == 2) {
     // the key-half states of each row meet in the (now free) K/V ring:
