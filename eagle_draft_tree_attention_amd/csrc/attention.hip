@@ -184,8 +184,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, 0x7fffffff, 0x00020000);
 }
 
+// MB = 1: two workgroups per CU (two waves per SIMD, 256 registers each);
+// MB = 2: one workgroup per CU, whose waves may then hold 512 registers
 template <int D, int MB, int NST, int KG>
-__global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a) {
+__global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const AttnKernelArgs a) {
   static_assert(KG == 1 || (KG == 2 && MB == 1), "key halves are split only between single row blocks");
   constexpr int KSTEPS = D / 32;          // QK^T contraction steps
   constexpr int DBLK = D / 16;            // output column blocks
@@ -523,27 +525,6 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     };
     // O^T += V^T P^T for keys 32 h .. 32 h + 31
     auto pv = [&](auto h_tag, const bf16x8_t (&pb)[MB], const bf16x8_t (&pl)[MB]) __attribute__((always_inline)) {
-      constexpr int H = decltype(h_tag)::value;
-      if constexpr (MB > 1) {   // each fragment feeds 2 MB products: read it just before them
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int r = 32 * H + 4 * lg + (ln >> 2);
-          const int chunk = 2 * db + ((ln & 3) >> 1);
-          const uint16_t* vp = vst + r * D + ((chunk ^ swz_v<D>(r)) * 8) + 4 * (ln & 1);
-          const bf16x8_t f = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lds_read_tr16(vp), lds_read_tr16(vp + 16 * D),
-                                                                                   0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, pb[rb], o[rb][db], 0, 0, 0);
-#pragma unroll
-          for (int rb = 0; rb < MB; ++rb) o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f, pl[rb], o[rb][db], 0, 0, 0);
-        }
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-          lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[rb], lacc[rb], 0, 0, 0);
-          lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[rb], lacc[rb], 0, 0, 0);
-        }
-        return;
-      }
       bf16x8_t va[DBLK];
       read_v(h_tag, va);
       pv_mfma(va, pb, pl);
@@ -551,14 +532,7 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
     bf16x8_t pb0[MB], pl0[MB], pb1[MB], pl1[MB];
-    if constexpr (KG == 1 && MB > 1) {   // one half at a time keeps the registers in bounds
-      qk(H0{});
-      softmax(H0{}, pb0, pl0);
-      pv(H0{}, pb0, pl0);
-      qk(H1{});
-      softmax(H1{}, pb1, pl1);
-      pv(H1{}, pb1, pl1);
-    } else if constexpr (KG == 1) {
+    if constexpr (KG == 1) {
       // one reference-maximum test for the whole tile, and every V fragment
       // requested before the softmax: the exponentials of both halves and
       // the PV products then form one straight run (no branch between them),
@@ -571,9 +545,48 @@ __global__ __launch_bounds__(256, 2) void tree_attn_mfma(const AttnKernelArgs a)
       read_v(H1{}, va1);
       mask_half(H0{});
       mask_half(H1{});
-      rescale(0, lane_max(0, 0, 4));
-      p_half(H0{}, pb0, pl0);
-      p_half(H1{}, pb1, pl1);
+      // exponent arguments x = s c - m of the lane's 16 scores of each row
+      // block; the rescale test runs on them (results of an fma need no NaN
+      // quieting before a maximum, raw matrix results would)
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) {
+        const float m_use = (m_run[rb] == kNegInf) ? 0.f : m_run[rb];
+        float xs[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[i] = __builtin_fmaf(sacc[i >> 2][rb][i & 3], c, -m_use);
+        float tx = xs[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tx = fmaxf(tx, xs[i]);
+        // same test as rescale(): some score exceeds the reference maximum by
+        // more than 2^kRescaleLog2 (any finite score while there is none)
+        if (__any(tx > (m_run[rb] == kNegInf ? kNegInf : kRescaleLog2))) {
+          tx = fmaxf(tx, __shfl_xor(tx, 16));
+          tx = fmaxf(tx, __shfl_xor(tx, 32));
+          const float m_new = fmaxf(m_run[rb], tx + m_use);
+          const float alpha = (m_new == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+          lacc[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DBLK; ++db) o[rb][db] *= alpha;
+          m_run[rb] = m_new;
+          const float m_nu = (m_new == kNegInf) ? 0.f : m_new;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xs[i] = __builtin_fmaf(sacc[i >> 2][rb][i & 3], c, -m_nu);
+        }
+        // P = 2^x as the bf16 pair hi = bf16(p), lo = bf16(p - hi), two at a time
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(xs[e]), p1 = __builtin_amdgcn_exp2f(xs[e + 1]);
+          const bf16x2_t h = {(__bf16)p0, (__bf16)p1};
+          const uint32_t hw = __builtin_bit_cast(uint32_t, h);
+          const bf16x2_t l = {(__bf16)(p0 - __uint_as_float(hw << 16)), (__bf16)(p1 - __uint_as_float(hw & 0xFFFF0000u))};
+          bf16x8_t& hb = e < 8 ? pb0[rb] : pb1[rb];
+          bf16x8_t& lb = e < 8 ? pl0[rb] : pl1[rb];
+          hb[e & 7] = h[0];
+          hb[(e & 7) + 1] = h[1];
+          lb[e & 7] = l[0];
+          lb[(e & 7) + 1] = l[1];
+        }
+      }
       pv_mfma(va0, pb0, pl0);
       pv_mfma(va1, pb1, pl1);
     } else if (kh == 0) {

@@ -122,7 +122,8 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
       plan->mb = rows / 64;
       plan->kg = 1;
     }
-    target_wgs = num_cus * env_int("EAGLE_VERIFY_ATTN_WG_PER_CU", 2);
+    // two row blocks per wave run one workgroup per CU (512 registers a wave)
+    target_wgs = num_cus * env_int("EAGLE_VERIFY_ATTN_WG_PER_CU", plan->mb > 1 ? 1 : 2);
     min_chunk = 2 * kTileKeys;
   } else {
     plan->row_tiles = R;
