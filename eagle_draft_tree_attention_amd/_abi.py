@@ -18,7 +18,8 @@ STATUS_NAMES = {0: "EAGLE_OK", 1: "EAGLE_ERR_ARG", 2: "EAGLE_ERR_UNSUPPORTED", 3
 EXPORTED_SYMBOLS = (
     "eagle_verify_create", "eagle_verify_tree_attention", "eagle_verify_spec_accept",
     "eagle_verify_destroy", "eagle_verify_last_error", "eagle_verify_check_tree_attention",
-    "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan",
+    "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan", "eagle_verify_kv_commit",
+    "eagle_verify_check_kv_commit",
 )
 
 
@@ -43,6 +44,13 @@ class SpecAcceptArgs(C.Structure):
                 ("seed", C.c_uint64), ("offset", C.c_uint64),
                 ("accept_len", C.c_void_p), ("accepted_nodes", C.c_void_p), ("out_tokens", C.c_void_p),
                 ("flags", C.c_void_p), ("near_ties", C.c_void_p)]
+
+
+class KvCommitArgs(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("tree_rows", C.c_int32), ("num_kv_rows", C.c_int64),
+                ("k", C.c_void_p), ("v", C.c_void_p), ("kv_indptr", C.c_void_p),
+                ("prefix_lens_host", C.POINTER(C.c_int32)), ("accept_len", C.c_void_p),
+                ("accepted_nodes", C.c_void_p), ("new_lens", C.c_void_p), ("flags", C.c_void_p)]
 
 
 class AttentionPlan(C.Structure):
@@ -76,3 +84,7 @@ def bind(lib):
     lib.eagle_verify_check_spec_accept.restype = C.c_int
     lib.eagle_verify_last_attention_plan.argtypes = [H, C.POINTER(AttentionPlan)]
     lib.eagle_verify_last_attention_plan.restype = C.c_int
+    lib.eagle_verify_kv_commit.argtypes = [H, C.POINTER(KvCommitArgs), C.c_void_p]
+    lib.eagle_verify_kv_commit.restype = C.c_int
+    lib.eagle_verify_check_kv_commit.argtypes = [C.POINTER(VerifyDesc), C.POINTER(KvCommitArgs)]
+    lib.eagle_verify_check_kv_commit.restype = C.c_int

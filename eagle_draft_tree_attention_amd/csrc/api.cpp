@@ -312,6 +312,37 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   return EAGLE_OK;
 }
 
+eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args* a, void* hip_stream) {
+  if (!h) {
+    set_err(nullptr, "handle is NULL");
+    return EAGLE_ERR_ARG;
+  }
+  eagle_status st = ev::check_kv_commit(&h->desc, a, h->err, sizeof(h->err));
+  if (st != EAGLE_OK) return st;
+  ev::CommitKernelArgs k;
+  std::memset(&k, 0, sizeof(k));
+  k.k = a->k;
+  k.v = a->v;
+  k.kv_indptr = a->kv_indptr;
+  k.accept_len = a->accept_len;
+  k.accepted_nodes = a->accepted_nodes;
+  k.new_lens = a->new_lens;
+  k.flags = a->flags;
+  k.num_kv_rows = a->num_kv_rows;
+  k.B = a->batch;
+  k.T = a->tree_rows;
+  k.Hkv = h->desc.num_kv_heads;
+  k.D = h->desc.head_dim;
+  for (int b = 0; b < a->batch; ++b) k.L[b] = a->prefix_lens_host[b];
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int e = ev::launch_kv_commit(k, h->desc.kv_dtype == EAGLE_BF16, stream);
+  h->last_stream = stream;
+  h->used = true;
+  if (e != 0) return hip_fail(h, "kv commit launch", e);
+  h->err[0] = 0;
+  return EAGLE_OK;
+}
+
 eagle_status eagle_verify_destroy(eagle_verify* h) {
   if (!h) return EAGLE_OK;
   eagle_status st = EAGLE_OK;
@@ -347,6 +378,12 @@ eagle_status eagle_verify_last_attention_plan(const eagle_verify* h, eagle_atten
 
 eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* desc, const eagle_spec_accept_args* a) {
   eagle_status st = ev::check_spec_accept(desc, a, g_err, sizeof(g_err));
+  if (st == EAGLE_OK) g_err[0] = 0;
+  return st;
+}
+
+eagle_status eagle_verify_check_kv_commit(const eagle_verify_desc* desc, const eagle_kv_commit_args* a) {
+  eagle_status st = ev::check_kv_commit(desc, a, g_err, sizeof(g_err));
   if (st == EAGLE_OK) g_err[0] = 0;
   return st;
 }

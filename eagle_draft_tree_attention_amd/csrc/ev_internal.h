@@ -129,6 +129,20 @@ struct AcceptKernelArgs {
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
 };
 
+// ---------------------------------------------------------------- KV commit
+struct CommitKernelArgs {
+  void* k;
+  void* v;
+  const int64_t* kv_indptr;
+  const int32_t* accept_len;
+  const int32_t* accepted_nodes;
+  int32_t* new_lens;
+  uint32_t* flags;
+  int64_t num_kv_rows;
+  int B, T, Hkv, D;
+  int32_t L[kMaxBatch];
+};
+
 // ---------------------------------------------------------------- host side
 struct Workspace {
   uint64_t* node_pub = nullptr;
@@ -148,12 +162,14 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
                                  int num_cus, AttnPlan* plan, char* err, size_t errlen);
 eagle_status check_spec_accept(const eagle_verify_desc* d, const eagle_spec_accept_args* a,
                                char* err, size_t errlen);
+eagle_status check_kv_commit(const eagle_verify_desc* d, const eagle_kv_commit_args* a, char* err, size_t errlen);
 int vocab_chunks(int V);
 
 // attention.hip / accept.hip
 int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int kv_bf16,
                           void* stream);
 int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stream);
+int launch_kv_commit(const CommitKernelArgs& args, int kv_bf16, void* stream);   // commit.hip
 // workgroups of the fused acceptance kernel that can be co-resident on the
 // device (0 if the query fails); the fused path is used when B*T*NC fits
 int fused_accept_capacity(int logits_bf16, int num_cus);

@@ -199,4 +199,30 @@ eagle_status check_spec_accept(const eagle_verify_desc* d, const eagle_spec_acce
   return EAGLE_OK;
 }
 
+eagle_status check_kv_commit(const eagle_verify_desc* d, const eagle_kv_commit_args* a, char* err, size_t errlen) {
+  eagle_status st = check_desc(d, err, errlen);
+  if (st != EAGLE_OK) return st;
+  if (!a) return fail(EAGLE_ERR_ARG, err, errlen, "args is NULL");
+  if (a->batch < 1) return fail(EAGLE_ERR_ARG, err, errlen, "batch=%d < 1", a->batch);
+  if (a->batch > d->max_batch)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "batch=%d above max_batch=%d", a->batch, d->max_batch);
+  if (a->tree_rows < 1) return fail(EAGLE_ERR_ARG, err, errlen, "tree_rows=%d < 1", a->tree_rows);
+  if (a->tree_rows > d->max_tree_rows)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "tree_rows=%d above max_tree_rows=%d", a->tree_rows,
+                d->max_tree_rows);
+  if (a->num_kv_rows < 0) return fail(EAGLE_ERR_ARG, err, errlen, "num_kv_rows < 0");
+  if (!a->k || !a->v || !a->kv_indptr || !a->prefix_lens_host || !a->accept_len || !a->accepted_nodes ||
+      !a->new_lens || !a->flags)
+    return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");
+  if (!aligned(a->k, 16) || !aligned(a->v, 16))
+    return fail(EAGLE_ERR_ARG, err, errlen, "k and v must be 16-byte aligned");
+  if (!aligned(a->kv_indptr, 8) || !aligned(a->accept_len, 4) || !aligned(a->accepted_nodes, 4) ||
+      !aligned(a->new_lens, 4) || !aligned(a->flags, 4))
+    return fail(EAGLE_ERR_ARG, err, errlen, "integer buffers misaligned");
+  for (int b = 0; b < a->batch; ++b)
+    if (a->prefix_lens_host[b] < 0)
+      return fail(EAGLE_ERR_ARG, err, errlen, "prefix_lens_host[%d]=%d < 0", b, a->prefix_lens_host[b]);
+  return EAGLE_OK;
+}
+
 }  // namespace ev

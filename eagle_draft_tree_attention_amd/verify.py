@@ -11,7 +11,7 @@ import ctypes as C
 import numpy as np
 
 from . import _abi
-from ._abi import (EAGLE_BF16, EAGLE_F32, EagleVerifyError, SpecAcceptArgs, TreeAttentionArgs,
+from ._abi import (EAGLE_BF16, EAGLE_F32, EagleVerifyError, KvCommitArgs, SpecAcceptArgs, TreeAttentionArgs,
                    VerifyDesc, AttentionPlan)
 
 
@@ -57,6 +57,14 @@ def eagle_verify_spec_accept(handle: int, args: SpecAcceptArgs, stream: int) -> 
     return _check(_lib().eagle_verify_spec_accept(handle, C.byref(args), C.c_void_p(stream)), handle)
 
 
+def eagle_verify_kv_commit(handle: int, args: KvCommitArgs, stream: int) -> int:
+    return _check(_lib().eagle_verify_kv_commit(handle, C.byref(args), C.c_void_p(stream)), handle)
+
+
+def eagle_verify_check_kv_commit(desc: VerifyDesc, args: KvCommitArgs) -> int:
+    return _lib().eagle_verify_check_kv_commit(C.byref(desc), C.byref(args))
+
+
 def eagle_verify_check_tree_attention(desc: VerifyDesc, args: TreeAttentionArgs):
     """(status, AttentionPlan) without touching the device."""
     plan = AttentionPlan()
@@ -98,6 +106,19 @@ def tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out,
     a.parents = _ptr(parents)
     a.sm_scale = float(sm_scale)
     a.out, a.flags = _ptr(out), _ptr(flags)
+    return a, lens          # keep lens alive while the call runs
+
+
+def kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags):
+    lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32))
+    a = KvCommitArgs()
+    a.batch, a.tree_rows = int(accepted_nodes.shape[0]), int(accepted_nodes.shape[1])
+    a.num_kv_rows = int(k.shape[0])
+    a.k, a.v = _ptr(k), _ptr(v)
+    a.kv_indptr = _ptr(kv_indptr)
+    a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))
+    a.accept_len, a.accepted_nodes = _ptr(accept_len), _ptr(accepted_nodes)
+    a.new_lens, a.flags = _ptr(new_lens), _ptr(flags)
     return a, lens          # keep lens alive while the call runs
 
 
@@ -164,3 +185,16 @@ class Verifier:
         a.near_ties = _ptr(outputs["near_ties"])
         eagle_verify_spec_accept(self.handle, a, _stream(stream))
         return outputs
+
+    def kv_commit(self, k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens=None, flags=None,
+                  stream=None):
+        """Commit the accepted path into k and v in place; returns (new_lens, flags)."""
+        import torch
+        B = int(accepted_nodes.shape[0])
+        if new_lens is None:
+            new_lens = torch.empty((B,), dtype=torch.int32, device=k.device)
+        if flags is None:
+            flags = torch.empty((B,), dtype=torch.int32, device=k.device)
+        a, _keep = kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags)
+        eagle_verify_kv_commit(self.handle, a, _stream(stream))
+        return new_lens, flags

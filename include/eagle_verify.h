@@ -170,6 +170,45 @@ typedef struct {
   int32_t* near_ties;
 } eagle_spec_accept_args;
 
+/* Commit the accepted path into the KV cache, in place (lesson page, the
+ * "KV cache rollback" section and build step 4, KV accounting).  For
+ * sequence b with n = accept_len[b] (spec_accept's outputs):
+ *   row kv_indptr[b] + L_b + i receives what row kv_indptr[b] + L_b + path_i
+ *   held before the call, i = 0 .. n, with path_0 = 0 (the root: the token
+ *   the previous step emitted, whose K/V this step computed) and
+ *   path_i = accepted_nodes[b, i-1]; rows of rejected nodes are left as
+ *   they are (rolled back by the length alone)
+ *   new_lens[b] = L_b + n + 1, the rows that now hold committed tokens (the
+ *   step's final token gets its row from the next forward, as its root)
+ * accept_len < 0 (a poisoned sequence) commits the root only.  A path that is
+ * not strictly increasing inside [1, T) moves nothing: new_lens[b] = L_b + 1,
+ * flags[b] = EAGLE_FLAG_BAD_TREE.  kv_indptr[b..b+1] not holding L_b + T rows
+ * inside [0, num_kv_rows): nothing moves, new_lens[b] = -1, flags[b] =
+ * EAGLE_FLAG_BAD_KV_RANGE.  Otherwise flags[b] = 0.
+ *   k, v             [num_kv_rows, Hkv, D] (kv_dtype), device, modified
+ *   kv_indptr        [B+1] int64 (device)
+ *   prefix_lens_host [B] int32 (host), L_b >= 0
+ *   accept_len       [B] int32 (device)
+ *   accepted_nodes   [B, T] int32 (device)
+ *   new_lens         [B] int32 (device, written)
+ *   flags            [B] uint32 (device, written)
+ * Every moving row is read before any is written, so a path whose sources
+ * and destinations overlap is safe.  Nothing else may touch k or v while the
+ * call runs. */
+typedef struct {
+  int32_t batch;           /* B <= max_batch            */
+  int32_t tree_rows;       /* T <= max_tree_rows, >= 1  */
+  int64_t num_kv_rows;     /* rows allocated in k and v */
+  void* k;
+  void* v;
+  const int64_t* kv_indptr;
+  const int32_t* prefix_lens_host;
+  const int32_t* accept_len;
+  const int32_t* accepted_nodes;
+  int32_t* new_lens;
+  uint32_t* flags;
+} eagle_kv_commit_args;
+
 /* Launch plan of one tree-attention call (what eagle_verify_tree_attention
  * will launch for these arguments). */
 typedef struct {
@@ -202,6 +241,11 @@ EAGLE_API eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_
 EAGLE_API eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_args* a,
                                       void* hip_stream);
 
+/* Commit of the accepted path into the KV cache, see eagle_kv_commit_args.
+ * Errors: EAGLE_ERR_ARG / EAGLE_ERR_CAPACITY (bad arguments, nothing
+ * launched), EAGLE_ERR_HIP (launch failed). */
+EAGLE_API eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args* a, void* hip_stream);
+
 /* Synchronise the last stream the handle used, free the workspace and the
  * handle.  NULL is accepted. */
 EAGLE_API eagle_status eagle_verify_destroy(eagle_verify* h);
@@ -218,6 +262,7 @@ EAGLE_API eagle_status eagle_verify_check_tree_attention(const eagle_verify_desc
                                                eagle_attention_plan* plan);
 EAGLE_API eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* desc,
                                             const eagle_spec_accept_args* a);
+EAGLE_API eagle_status eagle_verify_check_kv_commit(const eagle_verify_desc* desc, const eagle_kv_commit_args* a);
 
 /* Launch plan of the last successful eagle_verify_tree_attention call on h
  * (merge_in_kernel included).  No HIP call is made.

@@ -126,6 +126,36 @@ def test_spec_accept_argument_errors():
     assert ev.eagle_verify_check_spec_accept(d, _sa_args(near_ties=None)) == ev.EAGLE_ERR_ARG
 
 
+def _kc_args(lens=(5, 9), T=61, **over):
+    a = ev.KvCommitArgs()
+    lens = np.asarray(lens, dtype=np.int32)
+    a.batch, a.tree_rows = len(lens), T
+    a.num_kv_rows = int(lens.sum() + len(lens) * T)
+    fake = 1 << 20
+    a.k = a.v = a.kv_indptr = a.accept_len = a.accepted_nodes = a.new_lens = a.flags = fake
+    a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a, lens
+
+
+def test_kv_commit_argument_errors():
+    d = _desc()
+    a, keep = _kc_args()
+    assert ev.eagle_verify_check_kv_commit(d, a) == ev.EAGLE_OK
+    for over, want in ((dict(batch=0), ev.EAGLE_ERR_ARG), (dict(batch=9), ev.EAGLE_ERR_CAPACITY),
+                       (dict(tree_rows=0), ev.EAGLE_ERR_ARG), (dict(tree_rows=62), ev.EAGLE_ERR_CAPACITY),
+                       (dict(num_kv_rows=-1), ev.EAGLE_ERR_ARG), (dict(k=None), ev.EAGLE_ERR_ARG),
+                       (dict(new_lens=None), ev.EAGLE_ERR_ARG), (dict(v=(1 << 20) + 8), ev.EAGLE_ERR_ARG),
+                       (dict(kv_indptr=(1 << 20) + 4), ev.EAGLE_ERR_ARG),
+                       (dict(accepted_nodes=(1 << 20) + 2), ev.EAGLE_ERR_ARG)):
+        a, keep = _kc_args(**over)
+        assert ev.eagle_verify_check_kv_commit(d, a) == want, over
+    a, keep = _kc_args(lens=(5, -1))
+    assert ev.eagle_verify_check_kv_commit(d, a) == ev.EAGLE_ERR_ARG
+    assert "prefix_lens_host[1]" in ev.eagle_verify_last_error()
+
+
 def test_descriptor_errors():
     for kw in (dict(max_batch=0), dict(max_batch=257), dict(max_tree_rows=65), dict(vocab_size=1),
                dict(num_q_heads=0)):
