@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MODEL_LAYERS = 32   # decoder layers of the 8B model whose caches one commit call covers
 METRIC = "verified tree nodes/s per layer (attn+accept) at 8B/8K shape; % of HBM peak"
 CONFIG_INDEX = 2
 
@@ -37,6 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=8, help="rotated input sets (Infinity Cache defeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-commit", action="store_true", help="skip timing the KV commit of the accepted path")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
@@ -257,6 +259,38 @@ def main():
     attn_ms = np.array([p[0][0].elapsed_time(p[0][1]) for p in pairs])
     acc_ms = np.array([p[1][0].elapsed_time(p[1][1]) for p in pairs])
 
+    # timed region 3 (reported beside the step, not part of it): committing the
+    # last step's accepted path into the K/V caches of every layer of the
+    # model (one call, in place; the caches' contents do not matter for the
+    # timing, so they are left uninitialised)
+    commit_ms = None
+    if not args.no_commit:
+        layers = MODEL_LAYERS
+        kv_shape = (layers,) + tuple(sets[0]["k"].shape)
+        kl = torch.empty(kv_shape, dtype=sets[0]["k"].dtype, device="cuda")
+        vl = torch.empty(kv_shape, dtype=sets[0]["v"].dtype, device="cuda")
+        new_lens = torch.empty((B,), dtype=torch.int32, device="cuda")
+        cflags = torch.empty((B,), dtype=torch.int32, device="cuda")
+        ca, ckeep = ev.verify.kv_commit_args(kl, vl, indptr, inp.prefix_lens,
+                                             outs["accept_len"], outs["accepted_nodes"], new_lens, cflags)
+        call_commit = ev.verify.eagle_verify_kv_commit
+        for _ in range(5):
+            call_commit(handle, ca, sptr)
+        torch.cuda.synchronize()
+        cpairs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            cpairs[i][0].record(stream)
+            call_commit(handle, ca, sptr)
+            cpairs[i][1].record(stream)
+        torch.cuda.synchronize()
+        commit_ms = np.array([p[0].elapsed_time(p[1]) for p in cpairs])
+        alen = int(outs["accept_len"].cpu()[0])
+        path = outs["accepted_nodes"].cpu().numpy()[0][:max(alen, 0)].tolist()
+        moved = sum(1 for i, node in enumerate(path, start=1) if node != i)
+        esz = 2 if spec.dtype == "bf16" else 4
+        commit_bytes = layers * 2 * moved * Hkv * D * esz * 2   # K and V slices, read once and written once
+        del kl, vl
+
     if args.copy_probe:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -283,6 +317,10 @@ def main():
                                    nb["attention_bytes"], float(attn_ms.mean()) * 1e-3),
         "spec_accept": roofline("sa_fused (one spec_accept call)", nb["accept_bytes"], float(acc_ms.mean()) * 1e-3),
     }
+    if commit_ms is not None:
+        rooflines["kv_commit"] = roofline(f"kv_commit_rows (one kv_commit call over {layers} layers, "
+                                          f"{moved} of {len(path)} accepted rows move)",
+                                          commit_bytes, float(commit_ms.mean()) * 1e-3)
     dominant = "spec_accept" if acc_ms.mean() > attn_ms.mean() else "tree_attention"
     main_roof = dict(rooflines[dominant])
     main_roof["traffic"] = recorded_traffic(dominant)
@@ -313,6 +351,7 @@ def main():
         "attention_us_p10_p90": [float(np.percentile(attn_ms, 10) * 1e3), float(np.percentile(attn_ms, 90) * 1e3)],
         "accept_us_median": acc_us,
         "accept_us_p10_p90": [float(np.percentile(acc_ms, 10) * 1e3), float(np.percentile(acc_ms, 90) * 1e3)],
+        "kv_commit_us_median": float(np.median(commit_ms) * 1e3) if commit_ms is not None else None,
         "roofline": main_roof,
         "roofline_per_call": rooflines,
     }

@@ -50,7 +50,8 @@ class KvCommitArgs(C.Structure):
     _fields_ = [("batch", C.c_int32), ("tree_rows", C.c_int32), ("num_kv_rows", C.c_int64),
                 ("k", C.c_void_p), ("v", C.c_void_p), ("kv_indptr", C.c_void_p),
                 ("prefix_lens_host", C.POINTER(C.c_int32)), ("accept_len", C.c_void_p),
-                ("accepted_nodes", C.c_void_p), ("new_lens", C.c_void_p), ("flags", C.c_void_p)]
+                ("accepted_nodes", C.c_void_p), ("new_lens", C.c_void_p), ("flags", C.c_void_p),
+                ("num_layers", C.c_int32), ("layer_stride", C.c_int64)]
 
 
 class AttentionPlan(C.Structure):

@@ -333,6 +333,8 @@ eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args*
   k.T = a->tree_rows;
   k.Hkv = h->desc.num_kv_heads;
   k.D = h->desc.head_dim;
+  k.layers = a->num_layers;
+  k.layer_stride = a->layer_stride;
   for (int b = 0; b < a->batch; ++b) k.L[b] = a->prefix_lens_host[b];
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int e = ev::launch_kv_commit(k, h->desc.kv_dtype == EAGLE_BF16, stream);

@@ -10,9 +10,10 @@
 // row L_b + i receives row L_b + path_i, path_0 = 0 (the root),
 // path_i = accepted_nodes[b, i - 1], i = 0 .. accept_len[b].
 //
-// GPU formulation.  One workgroup per (sequence, KV head) owns that head's
-// slice (D elements of K and of V) of every row of the sequence, so no two
-// workgroups touch the same bytes.  Wave 0 reads the path one lane per node
+// GPU formulation.  One workgroup per (layer, sequence, KV head) owns that
+// head's slice (D elements of K and of V) of every row of the sequence in
+// that layer's cache, so no two workgroups touch the same bytes; one launch
+// covers every layer.  Wave 0 reads the path one lane per node
 // and validates it (strictly increasing indices in [1, T): a root path of a
 // tree whose parents precede their children) together with the KV range.
 // Every source slice that moves is then read into LDS before any
@@ -40,7 +41,8 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
   __shared__ int32_t moved[kMaxTree];                          // path positions whose row moves
   __shared__ int32_t nmove_sh, ok_sh;
   const int tid = threadIdx.x;
-  const int b = blockIdx.x / a.Hkv, h = blockIdx.x % a.Hkv;
+  const int layer = blockIdx.x / (a.B * a.Hkv);
+  const int b = (blockIdx.x / a.Hkv) % a.B, h = blockIdx.x % a.Hkv;
   const int T = a.T, L = a.L[b];
 
   if (tid < 64) {
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
     if (tid == 0) {
       nmove_sh = __popcll(mv);
       ok_sh = range_ok && path_ok;
-      if (h == 0) {
+      if (h == 0 && layer == 0) {
         a.new_lens[b] = !range_ok ? -1 : (path_ok ? L + nn + 1 : L + 1);
         a.flags[b] = !range_ok ? EAGLE_FLAG_BAD_KV_RANGE : (path_ok ? 0u : EAGLE_FLAG_BAD_TREE);
       }
@@ -76,8 +78,9 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
   // slice of row r for this head, as 16-byte vectors
   const int64_t base = a.kv_indptr[b] + L;
   const int64_t rowstride = static_cast<int64_t>(a.Hkv) * VPR;
-  u32x4_t* const kp = reinterpret_cast<u32x4_t*>(a.k) + static_cast<int64_t>(h) * VPR;
-  u32x4_t* const vp = reinterpret_cast<u32x4_t*>(a.v) + static_cast<int64_t>(h) * VPR;
+  const int64_t loff = static_cast<int64_t>(layer) * (a.layer_stride * static_cast<int64_t>(sizeof(TK)) / 16);
+  u32x4_t* const kp = reinterpret_cast<u32x4_t*>(a.k) + loff + static_cast<int64_t>(h) * VPR;
+  u32x4_t* const vp = reinterpret_cast<u32x4_t*>(a.v) + loff + static_cast<int64_t>(h) * VPR;
   const int total = 2 * nmove * VPR;
   for (int idx = tid; idx < total; idx += kCommitThreads) {
     const int which = idx / (nmove * VPR);   // 0: K, 1: V
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
 
 template <typename TK>
 hipError_t launch_t(const CommitKernelArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B * a.Hkv)), block(kCommitThreads);
+  const dim3 grid(static_cast<unsigned>(a.layers * a.B * a.Hkv)), block(kCommitThreads);
   if (a.D == 128) hipLaunchKernelGGL((kv_commit_rows<TK, 128>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((kv_commit_rows<TK, 64>), grid, block, 0, st, a);
   return hipGetLastError();

@@ -139,7 +139,8 @@ struct CommitKernelArgs {
   int32_t* new_lens;
   uint32_t* flags;
   int64_t num_kv_rows;
-  int B, T, Hkv, D;
+  int64_t layer_stride;   // elements between consecutive layers' k (and v)
+  int B, T, Hkv, D, layers;
   int32_t L[kMaxBatch];
 };
 

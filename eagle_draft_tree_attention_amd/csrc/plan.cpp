@@ -1,6 +1,7 @@
 // Host-side argument validation and launch planning for libeagle_verify.
 // Pure C++: no HIP call is made here, so everything in this file runs (and is
 // tested) without a GPU.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -222,6 +223,17 @@ eagle_status check_kv_commit(const eagle_verify_desc* d, const eagle_kv_commit_a
   for (int b = 0; b < a->batch; ++b)
     if (a->prefix_lens_host[b] < 0)
       return fail(EAGLE_ERR_ARG, err, errlen, "prefix_lens_host[%d]=%d < 0", b, a->prefix_lens_host[b]);
+  if (a->num_layers < 1 || a->num_layers > 4096)
+    return fail(EAGLE_ERR_ARG, err, errlen, "num_layers=%d outside [1, 4096]", a->num_layers);
+  if (static_cast<int64_t>(a->num_layers) * a->batch * d->num_kv_heads > INT32_MAX)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "num_layers * batch * num_kv_heads above 2^31 - 1");
+  const int64_t layer_elems = a->num_kv_rows * d->num_kv_heads * d->head_dim;
+  if (a->num_layers > 1 && a->layer_stride < layer_elems)
+    return fail(EAGLE_ERR_ARG, err, errlen, "layer_stride=%lld below one layer's %lld elements",
+                static_cast<long long>(a->layer_stride), static_cast<long long>(layer_elems));
+  const int esize = d->kv_dtype == EAGLE_BF16 ? 2 : 4;
+  if ((a->layer_stride * esize) % 16 != 0)
+    return fail(EAGLE_ERR_ARG, err, errlen, "layer_stride must keep every layer 16-byte aligned");
   return EAGLE_OK;
 }
 

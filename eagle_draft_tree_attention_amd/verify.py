@@ -110,10 +110,16 @@ def tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out,
 
 
 def kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags):
+    """k, v: [rows, Hkv, D] (one layer) or [layers, rows, Hkv, D] (every layer, contiguous)."""
     lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32))
     a = KvCommitArgs()
     a.batch, a.tree_rows = int(accepted_nodes.shape[0]), int(accepted_nodes.shape[1])
-    a.num_kv_rows = int(k.shape[0])
+    if k.dim() == 4:
+        a.num_layers, a.layer_stride = int(k.shape[0]), int(k.stride(0))
+        a.num_kv_rows = int(k.shape[1])
+    else:
+        a.num_layers, a.layer_stride = 1, 0
+        a.num_kv_rows = int(k.shape[0])
     a.k, a.v = _ptr(k), _ptr(v)
     a.kv_indptr = _ptr(kv_indptr)
     a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))

@@ -192,9 +192,12 @@ typedef struct {
  *   accepted_nodes   [B, T] int32 (device)
  *   new_lens         [B] int32 (device, written)
  *   flags            [B] uint32 (device, written)
- * Every moving row is read before any is written, so a path whose sources
- * and destinations overlap is safe.  Nothing else may touch k or v while the
- * call runs. */
+ *   num_layers       >= 1: the same commit is applied to every layer's cache
+ *   layer_stride     elements from one layer's k (and v) to the next's;
+ *                    >= num_kv_rows * Hkv * D when num_layers > 1
+ * One launch covers every layer.  Every moving row is read before any is
+ * written, so a path whose sources and destinations overlap is safe.
+ * Nothing else may touch k or v while the call runs. */
 typedef struct {
   int32_t batch;           /* B <= max_batch            */
   int32_t tree_rows;       /* T <= max_tree_rows, >= 1  */
@@ -207,6 +210,8 @@ typedef struct {
   const int32_t* accepted_nodes;
   int32_t* new_lens;
   uint32_t* flags;
+  int32_t num_layers;
+  int64_t layer_stride;
 } eagle_kv_commit_args;
 
 /* Launch plan of one tree-attention call (what eagle_verify_tree_attention

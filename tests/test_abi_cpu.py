@@ -134,6 +134,7 @@ def _kc_args(lens=(5, 9), T=61, **over):
     fake = 1 << 20
     a.k = a.v = a.kv_indptr = a.accept_len = a.accepted_nodes = a.new_lens = a.flags = fake
     a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))
+    a.num_layers, a.layer_stride = 1, 0
     for k, v in over.items():
         setattr(a, k, v)
     return a, lens
@@ -148,7 +149,11 @@ def test_kv_commit_argument_errors():
                        (dict(num_kv_rows=-1), ev.EAGLE_ERR_ARG), (dict(k=None), ev.EAGLE_ERR_ARG),
                        (dict(new_lens=None), ev.EAGLE_ERR_ARG), (dict(v=(1 << 20) + 8), ev.EAGLE_ERR_ARG),
                        (dict(kv_indptr=(1 << 20) + 4), ev.EAGLE_ERR_ARG),
-                       (dict(accepted_nodes=(1 << 20) + 2), ev.EAGLE_ERR_ARG)):
+                       (dict(accepted_nodes=(1 << 20) + 2), ev.EAGLE_ERR_ARG),
+                       (dict(num_layers=0), ev.EAGLE_ERR_ARG),
+                       (dict(num_layers=32, layer_stride=1000), ev.EAGLE_ERR_ARG),
+                       (dict(num_layers=32, layer_stride=(5 + 9 + 122) * 8 * 128 + 4), ev.EAGLE_ERR_ARG),
+                       (dict(num_layers=32, layer_stride=(5 + 9 + 122) * 8 * 128), ev.EAGLE_OK)):
         a, keep = _kc_args(**over)
         assert ev.eagle_verify_check_kv_commit(d, a) == want, over
     a, keep = _kc_args(lens=(5, -1))

@@ -156,6 +156,28 @@ def test_two_calls_in_a_row_act_on_the_committed_cache():
     ver.close()
 
 
+def test_every_layer_in_one_launch():
+    rng = np.random.default_rng(10)
+    T, Hkv, D, layers = 9, 2, 64, 3
+    lens = [6, 14]
+    per = [_case(rng, lens, T, Hkv, D, "bf16") for _ in range(layers)]
+    indptr = per[0][2]
+    k = np.stack([p[0] for p in per])
+    v = np.stack([p[1] for p in per])
+    nodes = _nodes([[2, 5, 8], [3, 4]], T)
+    alen = [3, 2]
+    ver = _verifier(2, Hkv, D, T, "bf16")
+    got = _gpu_commit(ver, k, v, indptr, lens, alen, nodes, "bf16")
+    want_k, want_v = [], []
+    for layer in range(layers):
+        r = okc.kv_commit(k[layer], v[layer], indptr, lens, np.asarray(alen), nodes, T)
+        want_k.append(r[0])
+        want_v.append(r[1])
+        nl, fl = r[2], r[3]
+    _check("layers", got, (np.stack(want_k), np.stack(want_v), nl, fl))
+    ver.close()
+
+
 @pytest.mark.parametrize("cfg", [0, 2])
 def test_after_the_oracle_walk_at_workload_shape(cfg):
     """The path the oracle's acceptance walk takes on the workload's synthetic
