@@ -9,8 +9,9 @@ drafting takes each node's top-k children by probability):
   frontier node f of sequence b carries the log-probability s_f of the path
   that reaches it (the root: 0) and the draft model's next-token logits x_f;
   with p_f = softmax(x_f / tau):
-    candidates: for every active frontier node (s_f > -inf) its k most
-                probable tokens (largest logit first, ties to the lower id)
+    candidates: for every active frontier node (s_f > -inf; NaN counts as
+                inactive) its k most probable tokens (largest logit first,
+                ties to the lower id)
     value of a candidate (f, t): s_f + log p_f(t)
     kept: the M candidates of largest value, ranked by value, ties to the
           lower frontier index, then the lower token id
@@ -67,7 +68,7 @@ def expand(logits, scores, tau, k, M):
         cands = []
         for f in range(F):
             s = float(scores[b][f])
-            if s == -np.inf:
+            if not s > -np.inf:                     # -inf or NaN: an inactive node
                 continue
             lp = row_logprobs(logits[b, f], tau)
             if lp is None:
