@@ -19,7 +19,7 @@ EXPORTED_SYMBOLS = (
     "eagle_verify_create", "eagle_verify_tree_attention", "eagle_verify_spec_accept",
     "eagle_verify_destroy", "eagle_verify_last_error", "eagle_verify_check_tree_attention",
     "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan", "eagle_verify_kv_commit",
-    "eagle_verify_check_kv_commit",
+    "eagle_verify_check_kv_commit", "eagle_verify_tree_expand", "eagle_verify_check_tree_expand",
 )
 
 
@@ -52,6 +52,13 @@ class KvCommitArgs(C.Structure):
                 ("prefix_lens_host", C.POINTER(C.c_int32)), ("accept_len", C.c_void_p),
                 ("accepted_nodes", C.c_void_p), ("new_lens", C.c_void_p), ("flags", C.c_void_p),
                 ("num_layers", C.c_int32), ("layer_stride", C.c_int64)]
+
+
+class TreeExpandArgs(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("frontier", C.c_int32), ("draft_logits", C.c_void_p),
+                ("scores", C.c_void_p), ("temperature", C.c_float), ("top_k", C.c_int32), ("keep", C.c_int32),
+                ("parent", C.c_void_p), ("token", C.c_void_p), ("value", C.c_void_p), ("flags", C.c_void_p),
+                ("near_ties", C.c_void_p)]
 
 
 class AttentionPlan(C.Structure):
@@ -89,3 +96,7 @@ def bind(lib):
     lib.eagle_verify_kv_commit.restype = C.c_int
     lib.eagle_verify_check_kv_commit.argtypes = [C.POINTER(VerifyDesc), C.POINTER(KvCommitArgs)]
     lib.eagle_verify_check_kv_commit.restype = C.c_int
+    lib.eagle_verify_tree_expand.argtypes = [H, C.POINTER(TreeExpandArgs), C.c_void_p]
+    lib.eagle_verify_tree_expand.restype = C.c_int
+    lib.eagle_verify_check_tree_expand.argtypes = [C.POINTER(VerifyDesc), C.POINTER(TreeExpandArgs)]
+    lib.eagle_verify_check_tree_expand.restype = C.c_int

@@ -110,6 +110,9 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t o_spart = off;
   const size_t spart_bytes = sizeof(uint64_t) * 4 * B * T * NC;   // fused: four tagged words per chunk
   off = align_up(off + spart_bytes, 256);
+  const size_t o_expand = off;   // tree-expansion chunk records
+  const int64_t nce = std::min<int64_t>(NC, ev::kMaxChunksExpand);
+  off = align_up(off + sizeof(ev::ChunkRecord) * B * T * nce, 256);
   const size_t o_cnt = off;
   const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
   off = align_up(off + cnt_bytes, 256);
@@ -134,6 +137,7 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.fpart = reinterpret_cast<double*>(p + o_fpart);
   h->ws.spart = reinterpret_cast<double*>(p + o_spart);
   h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
+  h->ws.expand = reinterpret_cast<ev::ChunkRecord*>(p + o_expand);
   h->ws.node_pub = reinterpret_cast<uint64_t*>(p + o_sync);
   h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
   h->ws.bytes = off;
@@ -345,6 +349,40 @@ eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args*
   return EAGLE_OK;
 }
 
+eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_args* a, void* hip_stream) {
+  if (!h) {
+    set_err(nullptr, "handle is NULL");
+    return EAGLE_ERR_ARG;
+  }
+  eagle_status st = ev::check_tree_expand(&h->desc, a, h->err, sizeof(h->err));
+  if (st != EAGLE_OK) return st;
+  ev::ExpandKernelArgs k;
+  std::memset(&k, 0, sizeof(k));
+  k.logits = a->draft_logits;
+  k.scores = a->scores;
+  k.chunks = h->ws.expand;
+  k.parent = a->parent;
+  k.token = a->token;
+  k.value = a->value;
+  k.flags = a->flags;
+  k.near_ties = a->near_ties;
+  k.B = a->batch;
+  k.F = a->frontier;
+  k.V = h->desc.vocab_size;
+  k.NC = ev::vocab_chunks(k.V);
+  k.K = a->top_k;
+  k.M = a->keep;
+  k.c2 = static_cast<float>(1.4426950408889634 / a->temperature);
+  k.inv_tau = 1.0 / static_cast<double>(a->temperature);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int e = ev::launch_tree_expand(k, h->desc.logits_dtype == EAGLE_BF16, stream);
+  h->last_stream = stream;
+  h->used = true;
+  if (e != 0) return hip_fail(h, "tree expansion launch", e);
+  h->err[0] = 0;
+  return EAGLE_OK;
+}
+
 eagle_status eagle_verify_destroy(eagle_verify* h) {
   if (!h) return EAGLE_OK;
   eagle_status st = EAGLE_OK;
@@ -386,6 +424,12 @@ eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* desc, const
 
 eagle_status eagle_verify_check_kv_commit(const eagle_verify_desc* desc, const eagle_kv_commit_args* a) {
   eagle_status st = ev::check_kv_commit(desc, a, g_err, sizeof(g_err));
+  if (st == EAGLE_OK) g_err[0] = 0;
+  return st;
+}
+
+eagle_status eagle_verify_check_tree_expand(const eagle_verify_desc* desc, const eagle_tree_expand_args* a) {
+  eagle_status st = ev::check_tree_expand(desc, a, g_err, sizeof(g_err));
   if (st == EAGLE_OK) g_err[0] = 0;
   return st;
 }

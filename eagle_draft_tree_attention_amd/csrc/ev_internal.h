@@ -144,6 +144,33 @@ struct CommitKernelArgs {
   int32_t L[kMaxBatch];
 };
 
+// ---------------------------------------------------------------- tree expansion
+constexpr int kMaxTopK = 16;          // children per frontier node
+constexpr int kMaxKeep = 64;          // candidates kept per sequence
+constexpr int kMaxChunksExpand = 64;  // vocabulary chunks of one row (V <= 64 * 8192)
+
+struct ChunkRecord {   // one (sequence, frontier row, vocab chunk)
+  float m;             // chunk maximum (-inf if none finite)
+  uint32_t bad;        // NaN or +inf seen
+  double z;            // sum exp((x - m) / t)
+  float val[kMaxTopK]; // the chunk's largest logits, descending (ties: lower id first)
+  int32_t id[kMaxTopK];// their token ids, -1 past the last
+};
+
+struct ExpandKernelArgs {
+  const void* logits;  // [B][F][V]
+  const float* scores; // [B][F]
+  ChunkRecord* chunks; // [B][F][NC]
+  int32_t* parent;     // [B][M]
+  int32_t* token;      // [B][M]
+  float* value;        // [B][M]
+  uint32_t* flags;     // [B]
+  int32_t* near_ties;  // [B]
+  int B, F, V, NC, K, M;
+  float c2;            // log2(e) / t
+  double inv_tau;      // 1 / t
+};
+
 // ---------------------------------------------------------------- host side
 struct Workspace {
   uint64_t* node_pub = nullptr;
@@ -154,6 +181,7 @@ struct Workspace {
   double* fpart = nullptr;
   double* spart = nullptr;
   uint32_t* counters = nullptr; // cnt_stats | cnt_pass | cnt_final
+  ChunkRecord* expand = nullptr; // [max_batch][max_tree_rows][min(NC, kMaxChunksExpand)]
   size_t bytes = 0;
 };
 
@@ -164,6 +192,8 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
 eagle_status check_spec_accept(const eagle_verify_desc* d, const eagle_spec_accept_args* a,
                                char* err, size_t errlen);
 eagle_status check_kv_commit(const eagle_verify_desc* d, const eagle_kv_commit_args* a, char* err, size_t errlen);
+eagle_status check_tree_expand(const eagle_verify_desc* d, const eagle_tree_expand_args* a, char* err,
+                               size_t errlen);
 int vocab_chunks(int V);
 
 // attention.hip / accept.hip
@@ -171,6 +201,7 @@ int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int 
                           void* stream);
 int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stream);
 int launch_kv_commit(const CommitKernelArgs& args, int kv_bf16, void* stream);   // commit.hip
+int launch_tree_expand(const ExpandKernelArgs& args, int logits_bf16, void* stream);   // expand.hip
 // workgroups of the fused acceptance kernel that can be co-resident on the
 // device (0 if the query fails); the fused path is used when B*T*NC fits
 int fused_accept_capacity(int logits_bf16, int num_cus);

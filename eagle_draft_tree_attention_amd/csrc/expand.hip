@@ -1,0 +1,287 @@
+// One expansion step of a dynamic draft tree (EAGLE-2), gfx950 (MI355X).
+//
+// Rule (EAGLE notes page, the EAGLE-2 section: the draft model's confidence
+// tracks the acceptance rate, so the tree grows where the cumulative
+// confidence of a path is high; the tree-drafting section: greedy drafting
+// takes each node's top-k children by probability).  Frontier node f carries
+// the log-probability s_f of its path and the draft logits x_f; with
+// p_f = softmax(x_f / t) its candidates are its k most probable tokens
+// (largest logit first, ties to the lower id), valued s_f + log p_f(token);
+// the M candidates of largest value are kept, ties to the lower frontier
+// index, then the lower token id.
+//
+// GPU formulation, two launches:
+//   te_chunk   one workgroup per (sequence, frontier row, 8192-token chunk):
+//              the chunk's maximum, its sum of exp((x - max)/t) (fp32
+//              exponentials, fp64 sum), NaN/+inf detection and its k largest
+//              logits with their ids (k rounds of a block-wide argmax over
+//              each thread's own sorted short list); one record per chunk.
+//   te_select  one wave per sequence, lane f = frontier row f: the row's
+//              maximum and normaliser from its chunks, its top k from the
+//              chunks' sorted lists (a k-step merge), the candidates' values
+//              s_f + (x - max)/t - log Z in fp64, then the global ranking as a
+//              merge of the rows' sorted lists: each step the wave picks the
+//              largest head (ties: the lowest lane), M + 1 steps, the last one
+//              only to see whether the boundary is a near tie.
+// Within a row the value is a monotone function of the logit, so a row's
+// list sorted by logit is sorted by value too.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ev_internal.h"
+
+namespace ev {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = kVocabChunk / kThreads;   // 32 logits per thread
+constexpr float kNegInf = -__builtin_inff();
+constexpr double kNear = 1e-6;                      // near-tie margin of the ranking (log-probability units)
+
+template <typename TL>
+__device__ __forceinline__ float logit_at(const TL* row, int v) {
+  if constexpr (sizeof(TL) == 2) return __uint_as_float(static_cast<uint32_t>(row[v]) << 16);
+  else return row[v];
+}
+
+// (value, id) order of the chunk lists: larger value first, then lower id
+__device__ __forceinline__ bool before(float a, int ia, float b, int ib) {
+  return a > b || (a == b && ia < ib);
+}
+
+template <typename TL>
+__global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
+  __shared__ float rmax[kThreads / 64];
+  __shared__ uint32_t rbad[kThreads / 64];
+  __shared__ double rsum[kThreads / 64];
+  __shared__ float wv[kThreads / 64];
+  __shared__ int wi[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NC = a.NC, V = a.V, K = a.K;
+  const int c = blockIdx.x % NC;
+  const int row = blockIdx.x / NC;   // b * F + f
+  const TL* x = reinterpret_cast<const TL*>(a.logits) + static_cast<int64_t>(row) * V;
+  const int v0 = c * kVocabChunk, v1 = min(V, v0 + kVocabChunk);
+
+  // this thread's logits: tokens v0 + tid + 256 j
+  float xs[kPerThread];
+  float m = kNegInf;
+  uint32_t bad = 0;
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int v = v0 + tid + kThreads * j;
+    xs[j] = v < v1 ? logit_at<TL>(x, v) : kNegInf;
+    if (xs[j] != xs[j] || xs[j] == __builtin_inff()) bad = 1;
+    else m = fmaxf(m, xs[j]);
+  }
+  // block maximum and bad flag
+  for (int off = 32; off > 0; off >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, off));
+    bad |= __shfl_xor(bad, off);
+  }
+  if (lane == 0) {
+    rmax[wave] = m;
+    rbad[wave] = bad;
+  }
+  __syncthreads();
+  m = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
+  bad = rbad[0] | rbad[1] | rbad[2] | rbad[3];
+  // sum of exp((x - m) / t) over the chunk: fp32 exponentials, fp64 sum
+  double z = 0.0;
+  if (m != kNegInf) {
+    const float mc = -m * a.c2;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) z += static_cast<double>(__builtin_amdgcn_exp2f(__builtin_fmaf(xs[j], a.c2, mc)));
+  }
+  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+  if (lane == 0) rsum[wave] = z;
+
+  // this thread's sorted short list (K largest of its 32, -inf excluded)
+  float lv[kMaxTopK];
+  int li[kMaxTopK];
+#pragma unroll
+  for (int q = 0; q < kMaxTopK; ++q) {
+    lv[q] = kNegInf;
+    li[q] = 0x7FFFFFFF;
+  }
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    float v = xs[j];
+    int id = v0 + tid + kThreads * j;
+    if (!(v > kNegInf) || v == __builtin_inff()) continue;   // -inf, NaN and +inf are never candidates
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q) {
+      if (q < K && before(v, id, lv[q], li[q])) {
+        const float tv = lv[q];
+        const int ti = li[q];
+        lv[q] = v;
+        li[q] = id;
+        v = tv;
+        id = ti;
+      }
+    }
+  }
+  __syncthreads();
+  ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC + c;
+  if (tid == 0) {
+    rec->m = m;
+    rec->bad = bad;
+    rec->z = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
+  }
+  // K rounds of a block-wide argmax over the threads' list heads
+  int head = 0;
+  for (int q = 0; q < K; ++q) {
+    float hv = kNegInf;
+    int hi = 0x7FFFFFFF;
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r)
+      if (r == head) {
+        hv = lv[r];
+        hi = li[r];
+      }
+    float bv = hv;
+    int bi = hi;
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      wv[wave] = bv;
+      wi[wave] = bi;
+    }
+    __syncthreads();
+    float gv = wv[0];
+    int gi = wi[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+      if (before(wv[w], wi[w], gv, gi)) {
+        gv = wv[w];
+        gi = wi[w];
+      }
+    __syncthreads();   // wv / wi are rewritten by the next round
+    if (tid == 0) {
+      rec->val[q] = gv;
+      rec->id[q] = gv > kNegInf ? gi : -1;
+    }
+    if (gv > kNegInf && hi == gi && hv == gv) ++head;   // the winning thread moves to its next entry
+  }
+}
+
+__global__ __launch_bounds__(64) void te_select(const ExpandKernelArgs a) {
+  __shared__ double sv[64][kMaxTopK];   // lane f's candidates: value
+  __shared__ int st[64][kMaxTopK];      // and token, sorted
+  __shared__ float sx[64][kMaxTopK];    // and logit (equal logits of one row tie exactly)
+  __shared__ uint8_t hd[64][kMaxChunksExpand];   // lane f's position in each chunk list during the merge
+  const int lane = threadIdx.x, b = blockIdx.x;
+  const int F = a.F, NC = a.NC, K = a.K, M = a.M;
+  int cnt = 0;            // candidates of row `lane`
+  bool unusable = false;
+  if (lane < F) {
+    const float s = a.scores[b * F + lane];
+    if (s > kNegInf) {    // active (NaN and -inf are not)
+      const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(b * F + lane) * NC;
+      float mx = kNegInf;
+      uint32_t bad = 0;
+      for (int c = 0; c < NC; ++c) {
+        mx = fmaxf(mx, rec[c].m);
+        bad |= rec[c].bad;
+      }
+      unusable = bad != 0 || mx == kNegInf;
+      if (!unusable) {
+        double z = 0.0;
+        for (int c = 0; c < NC; ++c)
+          if (rec[c].m != kNegInf) z += rec[c].z * exp2((static_cast<double>(rec[c].m) - mx) * static_cast<double>(a.c2));
+        const double lz = log(z);
+        // merge the chunks' sorted lists: K steps, each taking the best head
+        for (int c = 0; c < NC; ++c) hd[lane][c] = 0;
+        for (int q = 0; q < K; ++q) {
+          int bc = -1;
+          float bv = kNegInf;
+          int bi = 0x7FFFFFFF;
+          for (int c = 0; c < NC; ++c) {
+            const int h = hd[lane][c];
+            if (h >= K) continue;
+            const int id = rec[c].id[h];
+            if (id < 0) continue;
+            const float v = rec[c].val[h];
+            if (before(v, id, bv, bi)) {
+              bv = v;
+              bi = id;
+              bc = c;
+            }
+          }
+          if (bc < 0) break;
+          ++hd[lane][bc];
+          sx[lane][cnt] = bv;
+          st[lane][cnt] = bi;
+          sv[lane][cnt] = static_cast<double>(s) + (static_cast<double>(bv) - mx) * a.inv_tau - lz;
+          ++cnt;
+        }
+      }
+    }
+  }
+  // global ranking: merge of the rows' lists, the largest head each step,
+  // ties to the lowest lane (frontier index)
+  int pos = 0;
+  double prev_v = 0.0;
+  int prev_f = -1;
+  float prev_x = 0.f;
+  int near = 0;
+  for (int step = 0; step <= M; ++step) {
+    const double hv = (lane < F && pos < cnt) ? sv[lane][pos] : -__builtin_inf();
+    double best = hv;
+    for (int off = 32; off > 0; off >>= 1) best = fmax(best, __shfl_xor(best, off));
+    if (!(best > -__builtin_inf())) {   // no candidate left: pad
+      if (lane == 0 && step < M) {
+        a.parent[b * M + step] = -1;
+        a.token[b * M + step] = -1;
+        a.value[b * M + step] = kNegInf;
+      }
+      continue;
+    }
+    const uint64_t hit = __ballot(hv == best && lane < F && pos < cnt);
+    const int w = __ffsll(static_cast<long long>(hit)) - 1;
+    const int wt = __shfl(lane < F && pos < cnt ? st[lane][pos] : 0, w);
+    const float wx = __shfl(lane < F && pos < cnt ? sx[lane][pos] : 0.f, w);
+    if (step > 0 && prev_v - best < kNear && !(prev_f == w && prev_x == wx)) ++near;
+    prev_v = best;
+    prev_f = w;
+    prev_x = wx;
+    if (lane == 0 && step < M) {
+      a.parent[b * M + step] = w;
+      a.token[b * M + step] = wt;
+      a.value[b * M + step] = static_cast<float>(best);
+    }
+    if (lane == w) ++pos;
+  }
+  const bool any_bad = __any(unusable);
+  if (lane == 0) {
+    a.flags[b] = any_bad ? EAGLE_FLAG_NONFINITE : 0u;
+    a.near_ties[b] = near;
+  }
+}
+
+template <typename TL>
+hipError_t launch_t(const ExpandKernelArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((te_chunk<TL>), dim3(static_cast<unsigned>(a.B * a.F * a.NC)), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(te_select, dim3(static_cast<unsigned>(a.B)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_tree_expand(const ExpandKernelArgs& args, int logits_bf16, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = logits_bf16 ? launch_t<uint16_t>(args, st) : launch_t<float>(args, st);
+  return static_cast<int>(e);
+}
+
+}  // namespace ev

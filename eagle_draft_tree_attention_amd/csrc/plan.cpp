@@ -237,4 +237,33 @@ eagle_status check_kv_commit(const eagle_verify_desc* d, const eagle_kv_commit_a
   return EAGLE_OK;
 }
 
+eagle_status check_tree_expand(const eagle_verify_desc* d, const eagle_tree_expand_args* a, char* err,
+                               size_t errlen) {
+  eagle_status st = check_desc(d, err, errlen);
+  if (st != EAGLE_OK) return st;
+  if (!a) return fail(EAGLE_ERR_ARG, err, errlen, "args is NULL");
+  if (a->batch < 1) return fail(EAGLE_ERR_ARG, err, errlen, "batch=%d < 1", a->batch);
+  if (a->batch > d->max_batch)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "batch=%d above max_batch=%d", a->batch, d->max_batch);
+  if (a->frontier < 1) return fail(EAGLE_ERR_ARG, err, errlen, "frontier=%d < 1", a->frontier);
+  if (a->frontier > d->max_tree_rows)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "frontier=%d above max_tree_rows=%d", a->frontier,
+                d->max_tree_rows);
+  if (a->top_k < 1 || a->top_k > kMaxTopK)
+    return fail(EAGLE_ERR_ARG, err, errlen, "top_k=%d outside [1, %d]", a->top_k, kMaxTopK);
+  if (a->keep < 1 || a->keep > kMaxKeep)
+    return fail(EAGLE_ERR_ARG, err, errlen, "keep=%d outside [1, %d]", a->keep, kMaxKeep);
+  if (vocab_chunks(d->vocab_size) > kMaxChunksExpand)
+    return fail(EAGLE_ERR_UNSUPPORTED, err, errlen, "vocab_size=%d above %d for tree expansion", d->vocab_size,
+                kMaxChunksExpand * kVocabChunk);
+  if (!(a->temperature > 0.f) || !std::isfinite(a->temperature))
+    return fail(EAGLE_ERR_ARG, err, errlen, "temperature must be finite and > 0");
+  if (!a->draft_logits || !a->scores || !a->parent || !a->token || !a->value || !a->flags || !a->near_ties)
+    return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");
+  if (!aligned(a->draft_logits, 4) || !aligned(a->scores, 4) || !aligned(a->parent, 4) || !aligned(a->token, 4) ||
+      !aligned(a->value, 4) || !aligned(a->flags, 4) || !aligned(a->near_ties, 4))
+    return fail(EAGLE_ERR_ARG, err, errlen, "buffers must be 4-byte aligned");
+  return EAGLE_OK;
+}
+
 }  // namespace ev

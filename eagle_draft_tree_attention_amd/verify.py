@@ -12,7 +12,7 @@ import numpy as np
 
 from . import _abi
 from ._abi import (EAGLE_BF16, EAGLE_F32, EagleVerifyError, KvCommitArgs, SpecAcceptArgs, TreeAttentionArgs,
-                   VerifyDesc, AttentionPlan)
+                   TreeExpandArgs, VerifyDesc, AttentionPlan)
 
 
 def _lib():
@@ -63,6 +63,14 @@ def eagle_verify_kv_commit(handle: int, args: KvCommitArgs, stream: int) -> int:
 
 def eagle_verify_check_kv_commit(desc: VerifyDesc, args: KvCommitArgs) -> int:
     return _lib().eagle_verify_check_kv_commit(C.byref(desc), C.byref(args))
+
+
+def eagle_verify_tree_expand(handle: int, args: TreeExpandArgs, stream: int) -> int:
+    return _check(_lib().eagle_verify_tree_expand(handle, C.byref(args), C.c_void_p(stream)), handle)
+
+
+def eagle_verify_check_tree_expand(desc: VerifyDesc, args: TreeExpandArgs) -> int:
+    return _lib().eagle_verify_check_tree_expand(C.byref(desc), C.byref(args))
 
 
 def eagle_verify_check_tree_attention(desc: VerifyDesc, args: TreeAttentionArgs):
@@ -204,3 +212,25 @@ class Verifier:
         a, _keep = kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags)
         eagle_verify_kv_commit(self.handle, a, _stream(stream))
         return new_lens, flags
+
+    def tree_expand(self, logits, scores, temperature, top_k, keep, outputs=None, stream=None):
+        """One dynamic draft-tree expansion step: logits [B, F, V], scores [B, F] float32."""
+        import torch
+        B, F = int(logits.shape[0]), int(logits.shape[1])
+        dev = logits.device
+        if outputs is None:
+            outputs = {
+                "parent": torch.empty((B, keep), dtype=torch.int32, device=dev),
+                "token": torch.empty((B, keep), dtype=torch.int32, device=dev),
+                "value": torch.empty((B, keep), dtype=torch.float32, device=dev),
+                "flags": torch.empty((B,), dtype=torch.int32, device=dev),
+                "near_ties": torch.empty((B,), dtype=torch.int32, device=dev),
+            }
+        a = TreeExpandArgs()
+        a.batch, a.frontier = B, F
+        a.draft_logits, a.scores = _ptr(logits), _ptr(scores)
+        a.temperature, a.top_k, a.keep = float(temperature), int(top_k), int(keep)
+        a.parent, a.token, a.value = _ptr(outputs["parent"]), _ptr(outputs["token"]), _ptr(outputs["value"])
+        a.flags, a.near_ties = _ptr(outputs["flags"]), _ptr(outputs["near_ties"])
+        eagle_verify_tree_expand(self.handle, a, _stream(stream))
+        return outputs

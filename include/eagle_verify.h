@@ -214,6 +214,41 @@ typedef struct {
   int64_t layer_stride;
 } eagle_kv_commit_args;
 
+/* One expansion step of a dynamic draft tree (EAGLE notes page, the EAGLE-2
+ * section: the draft's confidence tracks the acceptance rate, so the tree
+ * grows where a path's cumulative confidence is high; the tree-drafting
+ * section: greedy drafting takes each node's top-k children).  For sequence b:
+ *   frontier node f has value s_f = scores[b, f] (log-probability of its
+ *   path; not > -inf (including NaN): inactive) and draft logits
+ *   draft_logits[b, f, :]; p_f = softmax(logits / temperature)
+ *   candidates: each active node's top_k most probable tokens (largest logit
+ *   first, ties to the lower id), valued s_f + log p_f(token)
+ *   kept: the `keep` candidates of largest value, in that order, ties to the
+ *   lower frontier index, then the lower token id
+ * Outputs (device): parent/token/value [B, keep] (frontier index, token id,
+ * value as float32; -1, -1, -inf past the last candidate), flags [B]
+ * (EAGLE_FLAG_NONFINITE when an active row holds NaN/+inf or is all -inf:
+ * that node is skipped), near_ties [B] (ranking decisions, up to the boundary
+ * between kept and dropped, between values less than 1e-6 apart; equal
+ * logits of one row are exact ties and not counted).  Values are computed in
+ * fp64 from fp32 exponentials summed in fp64.
+ * Limits: frontier <= max_tree_rows, 1 <= top_k <= 16, 1 <= keep <= 64,
+ * vocab_size <= 64 * 8192. */
+typedef struct {
+  int32_t batch;           /* B <= max_batch                 */
+  int32_t frontier;        /* F rows per sequence            */
+  const void* draft_logits;/* [B, F, V] logits_dtype         */
+  const float* scores;     /* [B, F] float32                 */
+  float temperature;       /* > 0                            */
+  int32_t top_k;
+  int32_t keep;
+  int32_t* parent;
+  int32_t* token;
+  float* value;
+  uint32_t* flags;
+  int32_t* near_ties;
+} eagle_tree_expand_args;
+
 /* Launch plan of one tree-attention call (what eagle_verify_tree_attention
  * will launch for these arguments). */
 typedef struct {
@@ -251,6 +286,12 @@ EAGLE_API eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spe
  * launched), EAGLE_ERR_HIP (launch failed). */
 EAGLE_API eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args* a, void* hip_stream);
 
+/* One dynamic draft-tree expansion step, see eagle_tree_expand_args.
+ * Errors: EAGLE_ERR_ARG / EAGLE_ERR_CAPACITY / EAGLE_ERR_UNSUPPORTED (nothing
+ * launched), EAGLE_ERR_HIP (launch failed).  Shares the handle's workspace:
+ * calls on one handle must not overlap. */
+EAGLE_API eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_args* a, void* hip_stream);
+
 /* Synchronise the last stream the handle used, free the workspace and the
  * handle.  NULL is accepted. */
 EAGLE_API eagle_status eagle_verify_destroy(eagle_verify* h);
@@ -268,6 +309,7 @@ EAGLE_API eagle_status eagle_verify_check_tree_attention(const eagle_verify_desc
 EAGLE_API eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* desc,
                                             const eagle_spec_accept_args* a);
 EAGLE_API eagle_status eagle_verify_check_kv_commit(const eagle_verify_desc* desc, const eagle_kv_commit_args* a);
+EAGLE_API eagle_status eagle_verify_check_tree_expand(const eagle_verify_desc* desc, const eagle_tree_expand_args* a);
 
 /* Launch plan of the last successful eagle_verify_tree_attention call on h
  * (merge_in_kernel included).  No HIP call is made.

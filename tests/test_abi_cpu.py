@@ -161,6 +161,30 @@ def test_kv_commit_argument_errors():
     assert "prefix_lens_host[1]" in ev.eagle_verify_last_error()
 
 
+def _te_args(**over):
+    a = ev.TreeExpandArgs()
+    a.batch, a.frontier = 2, 8
+    fake = 1 << 20
+    a.draft_logits = a.scores = a.parent = a.token = a.value = a.flags = a.near_ties = fake
+    a.temperature, a.top_k, a.keep = 1.0, 8, 16
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_tree_expand_argument_errors():
+    d = _desc()
+    assert ev.eagle_verify_check_tree_expand(d, _te_args()) == ev.EAGLE_OK
+    for over, want in ((dict(batch=0), ev.EAGLE_ERR_ARG), (dict(batch=9), ev.EAGLE_ERR_CAPACITY),
+                       (dict(frontier=0), ev.EAGLE_ERR_ARG), (dict(frontier=62), ev.EAGLE_ERR_CAPACITY),
+                       (dict(top_k=0), ev.EAGLE_ERR_ARG), (dict(top_k=17), ev.EAGLE_ERR_ARG),
+                       (dict(keep=0), ev.EAGLE_ERR_ARG), (dict(keep=65), ev.EAGLE_ERR_ARG),
+                       (dict(temperature=0.0), ev.EAGLE_ERR_ARG), (dict(temperature=float("inf")), ev.EAGLE_ERR_ARG),
+                       (dict(scores=None), ev.EAGLE_ERR_ARG), (dict(value=(1 << 20) + 2), ev.EAGLE_ERR_ARG)):
+        assert ev.eagle_verify_check_tree_expand(d, _te_args(**over)) == want, over
+    assert ev.eagle_verify_check_tree_expand(_desc(vocab_size=64 * 8192 + 1), _te_args()) == ev.EAGLE_ERR_UNSUPPORTED
+
+
 def test_descriptor_errors():
     for kw in (dict(max_batch=0), dict(max_batch=257), dict(max_tree_rows=65), dict(vocab_size=1),
                dict(num_q_heads=0)):
