@@ -90,3 +90,36 @@ def expand(logits, scores, tau, k, M):
             if v0 - v1 < NEAR and not same:
                 near[b] += 1
     return dict(parent=parent, token=token, value=value, flags=flags, near_ties=near)
+
+
+def rerank(parent, token, value, root_tokens, N):
+    """Final draft tree from D expansion steps (EAGLE notes page, the EAGLE-2
+    section: nodes are kept by the cumulative confidence of their paths).
+
+    parent/token/value [D, B, M]: step d's kept candidates (step 0 expands the
+    root, so its parents are 0; step d > 0 indexes step d-1's kept list;
+    parent -1 = no candidate).  The N nodes of largest value are kept, ties to
+    the earlier step, then the better rank in the step; a node's value never
+    exceeds its parent's, so the kept set contains every kept node's parent.
+    Output rows: 0 = the root (parent -1, token root_tokens[b]), then the
+    kept nodes in (step, rank) order, so parents precede children.
+    Returns dict(parents [B, N+1], tokens [B, N+1], rows [B]); rows past
+    `rows` hold parent -1, token -1."""
+    parent = np.asarray(parent)
+    value = np.asarray(value, dtype=np.float64)
+    D, B, M = parent.shape
+    parents = np.full((B, N + 1), -1, dtype=np.int32)
+    tokens = np.full((B, N + 1), -1, dtype=np.int32)
+    rows = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        cands = [(value[d, b, r], d, r) for d in range(D) for r in range(M) if parent[d, b, r] >= 0]
+        cands.sort(key=lambda c: (-c[0], c[1], c[2]))
+        kept = sorted((d, r) for _, d, r in cands[:N])
+        index = {}
+        parents[b, 0], tokens[b, 0] = -1, int(root_tokens[b])
+        for i, (d, r) in enumerate(kept, start=1):
+            index[(d, r)] = i
+            parents[b, i] = 0 if d == 0 else index[(d - 1, int(parent[d, b, r]))]
+            tokens[b, i] = int(token[d, b, r])
+        rows[b] = 1 + len(kept)
+    return dict(parents=parents, tokens=tokens, rows=rows)

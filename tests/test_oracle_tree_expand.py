@@ -113,3 +113,57 @@ def test_near_ties_are_counted_across_rows_only():
     assert out["near_ties"][0] == 1          # the two rows' best tokens; row 0's equal tail is exact
     x1 = np.zeros((1, 1, 6), dtype=np.float32)   # one row, equal logits: exact ties, not counted
     assert ote.expand(x1, np.zeros((1, 1)), 1.0, 6, 5)["near_ties"][0] == 0
+
+
+def _chain_of_steps(seed, B=2, V=50, steps=((4, 4), (3, 6), (2, 6))):
+    rng = np.random.default_rng(seed)
+    fr = np.zeros((B, 1))
+    P, T, Vv = [], [], []
+    for k, M in steps:
+        F = fr.shape[1]
+        x = (rng.standard_normal((B, F, V)) * 2).astype(np.float32)
+        out = ote.expand(x, fr, 1.0, k, M)
+        P.append(out["parent"]); T.append(out["token"]); Vv.append(out["value"].astype(np.float32))
+        fr = out["value"]
+    Mx = max(p.shape[1] for p in P)
+    pad = lambda a, fill: np.stack([np.pad(x, ((0, 0), (0, Mx - x.shape[1])), constant_values=fill) for x in a])
+    return pad(P, -1), pad(T, -1), pad(Vv, -np.inf)
+
+
+def test_rerank_is_the_top_n_of_all_nodes_and_ancestor_closed():
+    P, T, V = _chain_of_steps(21)
+    D, B, M = P.shape
+    N = 9
+    out = ote.rerank(P, T, V, np.array([7, 8]), N)
+    for b in range(B):
+        # brute force: every node's value, the N largest (ties: earlier step, then rank)
+        allv = sorted(((V[d, b, r], d, r) for d in range(D) for r in range(M) if P[d, b, r] >= 0),
+                      key=lambda c: (-c[0], c[1], c[2]))[:N]
+        assert out["rows"][b] == N + 1
+        par, tok = out["parents"][b], out["tokens"][b]
+        assert par[0] == -1 and tok[0] == [7, 8][b]
+        assert all(0 <= par[i] < i for i in range(1, N + 1))          # a valid tree, parents first
+        # each output row's path of tokens, rebuilt from the steps' parent links
+        def path_tokens(d, r):
+            toks = []
+            while d >= 0:
+                toks.append(int(T[d, b, r]))
+                r = int(P[d, b, r])
+                d -= 1
+            return toks[::-1]
+        def out_path(i):
+            toks = []
+            while i > 0:
+                toks.append(int(tok[i]))
+                i = int(par[i])
+            return toks[::-1]
+        assert sorted(map(tuple, (path_tokens(d, r) for _, d, r in allv))) == \
+            sorted(map(tuple, (out_path(i) for i in range(1, N + 1))))
+
+
+def test_rerank_keeps_everything_when_n_is_large():
+    P, T, V = _chain_of_steps(22)
+    out = ote.rerank(P, T, V, np.zeros(2, dtype=np.int32), 40)
+    n = int((P >= 0).sum(axis=(0, 2))[0])
+    assert out["rows"][0] == n + 1
+    assert out["parents"][0][n + 1:].tolist() == [-1] * (40 - n)
