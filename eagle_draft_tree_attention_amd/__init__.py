@@ -15,8 +15,8 @@ from ._abi import (  # noqa: F401
     EAGLE_OK, EAGLE_ERR_ARG, EAGLE_ERR_UNSUPPORTED, EAGLE_ERR_CAPACITY, EAGLE_ERR_HIP, EAGLE_ERR_OOM,
     EAGLE_F32, EAGLE_BF16, FLAG_BAD_TREE, FLAG_BAD_TOKEN, FLAG_NONFINITE, FLAG_P_ZERO,
     FLAG_DEGENERATE_RESIDUAL, FLAG_BAD_KV_RANGE, MAX_TREE_ROWS, EXPORTED_SYMBOLS,
-    VerifyDesc, TreeAttentionArgs, SpecAcceptArgs, KvCommitArgs, TreeExpandArgs, AttentionPlan,
-    EagleVerifyError,
+    VerifyDesc, TreeAttentionArgs, SpecAcceptArgs, KvCommitArgs, TreeExpandArgs, TreeRerankArgs,
+    AttentionPlan, EagleVerifyError,
 )
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libeagle_verify.so")
@@ -41,7 +41,8 @@ from .verify import (  # noqa: E402,F401
     eagle_verify_create, eagle_verify_destroy, eagle_verify_tree_attention, eagle_verify_spec_accept,
     eagle_verify_last_error, eagle_verify_check_tree_attention, eagle_verify_check_spec_accept,
     eagle_verify_last_attention_plan, eagle_verify_kv_commit, eagle_verify_check_kv_commit,
-    eagle_verify_tree_expand, eagle_verify_check_tree_expand, Verifier, make_desc,
+    eagle_verify_tree_expand, eagle_verify_check_tree_expand, eagle_verify_tree_rerank,
+    eagle_verify_check_tree_rerank, Verifier, make_desc,
 )
 
 

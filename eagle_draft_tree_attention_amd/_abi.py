@@ -20,6 +20,7 @@ EXPORTED_SYMBOLS = (
     "eagle_verify_destroy", "eagle_verify_last_error", "eagle_verify_check_tree_attention",
     "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan", "eagle_verify_kv_commit",
     "eagle_verify_check_kv_commit", "eagle_verify_tree_expand", "eagle_verify_check_tree_expand",
+    "eagle_verify_tree_rerank", "eagle_verify_check_tree_rerank",
 )
 
 
@@ -61,6 +62,12 @@ class TreeExpandArgs(C.Structure):
                 ("near_ties", C.c_void_p)]
 
 
+class TreeRerankArgs(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("steps", C.c_int32), ("keep", C.c_int32), ("nodes", C.c_int32),
+                ("parent", C.c_void_p), ("token", C.c_void_p), ("value", C.c_void_p), ("root_tokens", C.c_void_p),
+                ("parents", C.c_void_p), ("tokens", C.c_void_p), ("rows", C.c_void_p)]
+
+
 class AttentionPlan(C.Structure):
     _fields_ = [("path", C.c_int32), ("rows_per_kv_head", C.c_int32), ("row_tiles", C.c_int32),
                 ("rows_per_tile", C.c_int32), ("chunk_keys", C.c_int32), ("total_splits", C.c_int32),
@@ -100,3 +107,7 @@ def bind(lib):
     lib.eagle_verify_tree_expand.restype = C.c_int
     lib.eagle_verify_check_tree_expand.argtypes = [C.POINTER(VerifyDesc), C.POINTER(TreeExpandArgs)]
     lib.eagle_verify_check_tree_expand.restype = C.c_int
+    lib.eagle_verify_tree_rerank.argtypes = [H, C.POINTER(TreeRerankArgs), C.c_void_p]
+    lib.eagle_verify_tree_rerank.restype = C.c_int
+    lib.eagle_verify_check_tree_rerank.argtypes = [C.POINTER(VerifyDesc), C.POINTER(TreeRerankArgs)]
+    lib.eagle_verify_check_tree_rerank.restype = C.c_int

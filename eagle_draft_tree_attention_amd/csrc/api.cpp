@@ -383,6 +383,35 @@ eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_a
   return EAGLE_OK;
 }
 
+eagle_status eagle_verify_tree_rerank(eagle_verify* h, const eagle_tree_rerank_args* a, void* hip_stream) {
+  if (!h) {
+    set_err(nullptr, "handle is NULL");
+    return EAGLE_ERR_ARG;
+  }
+  eagle_status st = ev::check_tree_rerank(&h->desc, a, h->err, sizeof(h->err));
+  if (st != EAGLE_OK) return st;
+  ev::RerankKernelArgs k;
+  std::memset(&k, 0, sizeof(k));
+  k.parent = a->parent;
+  k.token = a->token;
+  k.value = a->value;
+  k.root_tokens = a->root_tokens;
+  k.parents = a->parents;
+  k.tokens = a->tokens;
+  k.rows = a->rows;
+  k.B = a->batch;
+  k.D = a->steps;
+  k.M = a->keep;
+  k.N = a->nodes;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  const int e = ev::launch_tree_rerank(k, stream);
+  h->last_stream = stream;
+  h->used = true;
+  if (e != 0) return hip_fail(h, "tree rerank launch", e);
+  h->err[0] = 0;
+  return EAGLE_OK;
+}
+
 eagle_status eagle_verify_destroy(eagle_verify* h) {
   if (!h) return EAGLE_OK;
   eagle_status st = EAGLE_OK;
@@ -430,6 +459,12 @@ eagle_status eagle_verify_check_kv_commit(const eagle_verify_desc* desc, const e
 
 eagle_status eagle_verify_check_tree_expand(const eagle_verify_desc* desc, const eagle_tree_expand_args* a) {
   eagle_status st = ev::check_tree_expand(desc, a, g_err, sizeof(g_err));
+  if (st == EAGLE_OK) g_err[0] = 0;
+  return st;
+}
+
+eagle_status eagle_verify_check_tree_rerank(const eagle_verify_desc* desc, const eagle_tree_rerank_args* a) {
+  eagle_status st = ev::check_tree_rerank(desc, a, g_err, sizeof(g_err));
   if (st == EAGLE_OK) g_err[0] = 0;
   return st;
 }

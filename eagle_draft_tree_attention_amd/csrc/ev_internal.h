@@ -171,6 +171,19 @@ struct ExpandKernelArgs {
   double inv_tau;      // 1 / t
 };
 
+constexpr int kMaxSteps = 64;         // chained expansion steps one rerank reads
+
+struct RerankKernelArgs {
+  const int32_t* parent;     // [D][B][M]
+  const int32_t* token;      // [D][B][M]
+  const float* value;        // [D][B][M]
+  const int32_t* root_tokens;// [B]
+  int32_t* parents;          // [B][N + 1]
+  int32_t* tokens;           // [B][N + 1]
+  int32_t* rows;             // [B]
+  int B, D, M, N;
+};
+
 // ---------------------------------------------------------------- host side
 struct Workspace {
   uint64_t* node_pub = nullptr;
@@ -194,6 +207,8 @@ eagle_status check_spec_accept(const eagle_verify_desc* d, const eagle_spec_acce
 eagle_status check_kv_commit(const eagle_verify_desc* d, const eagle_kv_commit_args* a, char* err, size_t errlen);
 eagle_status check_tree_expand(const eagle_verify_desc* d, const eagle_tree_expand_args* a, char* err,
                                size_t errlen);
+eagle_status check_tree_rerank(const eagle_verify_desc* d, const eagle_tree_rerank_args* a, char* err,
+                               size_t errlen);
 int vocab_chunks(int V);
 
 // attention.hip / accept.hip
@@ -202,6 +217,7 @@ int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int 
 int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stream);
 int launch_kv_commit(const CommitKernelArgs& args, int kv_bf16, void* stream);   // commit.hip
 int launch_tree_expand(const ExpandKernelArgs& args, int logits_bf16, void* stream);   // expand.hip
+int launch_tree_rerank(const RerankKernelArgs& args, void* stream);                    // expand.hip
 // workgroups of the fused acceptance kernel that can be co-resident on the
 // device (0 if the query fails); the fused path is used when B*T*NC fits
 int fused_accept_capacity(int logits_bf16, int num_cus);

@@ -23,6 +23,7 @@
 //              merge of the rows' sorted lists: each step the wave picks the
 //              largest head (ties: the lowest lane), M + 1 steps, the last one
 //              only to see whether the boundary is a near tie.
+//   te_rerank  (separate call) the final tree from the chained steps.
 // Within a row the value is a monotone function of the logit, so a row's
 // list sorted by logit is sorted by value too.
 #include <hip/hip_runtime.h>
@@ -267,6 +268,73 @@ __global__ __launch_bounds__(64) void te_select(const ExpandKernelArgs a) {
   }
 }
 
+// Final draft tree from D chained expansion steps: the N nodes of largest
+// value (ties: earlier step, then better rank), written in (step, rank)
+// order after the root, so parents precede children.  One wave per
+// sequence: lane d walks step d's ranked list; each of the N selections takes
+// the largest head (ties: the lowest lane = earliest step), then the kept
+// nodes get their row numbers step by step with a ballot prefix count.
+__global__ __launch_bounds__(64) void te_rerank(const RerankKernelArgs a) {
+  __shared__ uint8_t kept[kMaxSteps][kMaxKeep];
+  __shared__ int16_t rowof[kMaxSteps][kMaxKeep];
+  const int lane = threadIdx.x, b = blockIdx.x;
+  const int D = a.D, M = a.M, N = a.N, B = a.B;
+  for (int i = lane; i < kMaxSteps * kMaxKeep; i += 64) {
+    kept[i / kMaxKeep][i % kMaxKeep] = 0;
+    rowof[i / kMaxKeep][i % kMaxKeep] = -1;
+  }
+  __syncthreads();
+  int pos = 0;
+  int taken = 0;
+  for (int step = 0; step < N; ++step) {
+    float hv = kNegInf;
+    bool has = false;
+    if (lane < D && pos < M) {
+      const int64_t at = (static_cast<int64_t>(lane) * B + b) * M + pos;
+      has = a.parent[at] >= 0;
+      if (has) hv = a.value[at];
+    }
+    float best = has ? hv : kNegInf;
+    for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+    const uint64_t hit = __ballot(has && hv == best);
+    if (!hit) break;   // no candidate left
+    const int w = __ffsll(static_cast<long long>(hit)) - 1;
+    if (lane == w) {
+      kept[lane][pos] = 1;
+      ++pos;
+    }
+    ++taken;
+  }
+  __syncthreads();
+  // row numbers in (step, rank) order, then parents and tokens
+  int base = 1;
+  for (int d = 0; d < D; ++d) {
+    const bool k = lane < M && kept[d][lane];
+    const uint64_t mask = __ballot(k);
+    if (k) rowof[d][lane] = static_cast<int16_t>(base + __popcll(mask & ((1ull << lane) - 1ull)));
+    base += __popcll(mask);
+    __syncthreads();
+  }
+  int32_t* const par = a.parents + static_cast<int64_t>(b) * (N + 1);
+  int32_t* const tok = a.tokens + static_cast<int64_t>(b) * (N + 1);
+  for (int i = lane; i <= N; i += 64) {
+    par[i] = -1;
+    tok[i] = -1;
+  }
+  __syncthreads();
+  if (lane == 0) tok[0] = a.root_tokens[b];
+  for (int d = 0; d < D; ++d) {
+    if (lane < M && kept[d][lane]) {
+      const int64_t at = (static_cast<int64_t>(d) * B + b) * M + lane;
+      const int row = rowof[d][lane];
+      const int pi = a.parent[at];   // an index outside the previous list leaves the row without a parent
+      par[row] = d == 0 ? 0 : ((pi >= 0 && pi < M) ? rowof[d - 1][pi] : -1);
+      tok[row] = a.token[at];
+    }
+  }
+  if (lane == 0) a.rows[b] = 1 + taken;
+}
+
 template <typename TL>
 hipError_t launch_t(const ExpandKernelArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((te_chunk<TL>), dim3(static_cast<unsigned>(a.B * a.F * a.NC)), dim3(kThreads), 0, st, a);
@@ -277,6 +345,12 @@ hipError_t launch_t(const ExpandKernelArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int launch_tree_rerank(const RerankKernelArgs& args, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(te_rerank, dim3(static_cast<unsigned>(args.B)), dim3(64), 0, st, args);
+  return static_cast<int>(hipGetLastError());
+}
 
 int launch_tree_expand(const ExpandKernelArgs& args, int logits_bf16, void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -266,4 +266,28 @@ eagle_status check_tree_expand(const eagle_verify_desc* d, const eagle_tree_expa
   return EAGLE_OK;
 }
 
+eagle_status check_tree_rerank(const eagle_verify_desc* d, const eagle_tree_rerank_args* a, char* err,
+                               size_t errlen) {
+  eagle_status st = check_desc(d, err, errlen);
+  if (st != EAGLE_OK) return st;
+  if (!a) return fail(EAGLE_ERR_ARG, err, errlen, "args is NULL");
+  if (a->batch < 1) return fail(EAGLE_ERR_ARG, err, errlen, "batch=%d < 1", a->batch);
+  if (a->batch > d->max_batch)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "batch=%d above max_batch=%d", a->batch, d->max_batch);
+  if (a->steps < 1 || a->steps > kMaxSteps)
+    return fail(EAGLE_ERR_ARG, err, errlen, "steps=%d outside [1, %d]", a->steps, kMaxSteps);
+  if (a->keep < 1 || a->keep > kMaxKeep)
+    return fail(EAGLE_ERR_ARG, err, errlen, "keep=%d outside [1, %d]", a->keep, kMaxKeep);
+  if (a->nodes < 0) return fail(EAGLE_ERR_ARG, err, errlen, "nodes=%d < 0", a->nodes);
+  if (a->nodes + 1 > d->max_tree_rows)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "nodes + 1 = %d above max_tree_rows=%d", a->nodes + 1,
+                d->max_tree_rows);
+  if (!a->parent || !a->token || !a->value || !a->root_tokens || !a->parents || !a->tokens || !a->rows)
+    return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");
+  if (!aligned(a->parent, 4) || !aligned(a->token, 4) || !aligned(a->value, 4) || !aligned(a->root_tokens, 4) ||
+      !aligned(a->parents, 4) || !aligned(a->tokens, 4) || !aligned(a->rows, 4))
+    return fail(EAGLE_ERR_ARG, err, errlen, "buffers must be 4-byte aligned");
+  return EAGLE_OK;
+}
+
 }  // namespace ev

@@ -12,7 +12,7 @@ import numpy as np
 
 from . import _abi
 from ._abi import (EAGLE_BF16, EAGLE_F32, EagleVerifyError, KvCommitArgs, SpecAcceptArgs, TreeAttentionArgs,
-                   TreeExpandArgs, VerifyDesc, AttentionPlan)
+                   TreeExpandArgs, TreeRerankArgs, VerifyDesc, AttentionPlan)
 
 
 def _lib():
@@ -71,6 +71,14 @@ def eagle_verify_tree_expand(handle: int, args: TreeExpandArgs, stream: int) -> 
 
 def eagle_verify_check_tree_expand(desc: VerifyDesc, args: TreeExpandArgs) -> int:
     return _lib().eagle_verify_check_tree_expand(C.byref(desc), C.byref(args))
+
+
+def eagle_verify_tree_rerank(handle: int, args: TreeRerankArgs, stream: int) -> int:
+    return _check(_lib().eagle_verify_tree_rerank(handle, C.byref(args), C.c_void_p(stream)), handle)
+
+
+def eagle_verify_check_tree_rerank(desc: VerifyDesc, args: TreeRerankArgs) -> int:
+    return _lib().eagle_verify_check_tree_rerank(C.byref(desc), C.byref(args))
 
 
 def eagle_verify_check_tree_attention(desc: VerifyDesc, args: TreeAttentionArgs):
@@ -234,3 +242,18 @@ class Verifier:
         a.flags, a.near_ties = _ptr(outputs["flags"]), _ptr(outputs["near_ties"])
         eagle_verify_tree_expand(self.handle, a, _stream(stream))
         return outputs
+
+    def tree_rerank(self, parent, token, value, root_tokens, nodes, stream=None):
+        """Final tree from chained expansion steps: parent/token/value [steps, B, keep]."""
+        import torch
+        D, B, M = (int(x) for x in parent.shape)
+        dev = parent.device
+        out = {"parents": torch.empty((B, nodes + 1), dtype=torch.int32, device=dev),
+               "tokens": torch.empty((B, nodes + 1), dtype=torch.int32, device=dev),
+               "rows": torch.empty((B,), dtype=torch.int32, device=dev)}
+        a = TreeRerankArgs()
+        a.batch, a.steps, a.keep, a.nodes = B, D, M, int(nodes)
+        a.parent, a.token, a.value, a.root_tokens = _ptr(parent), _ptr(token), _ptr(value), _ptr(root_tokens)
+        a.parents, a.tokens, a.rows = _ptr(out["parents"]), _ptr(out["tokens"]), _ptr(out["rows"])
+        eagle_verify_tree_rerank(self.handle, a, _stream(stream))
+        return out

@@ -249,6 +249,33 @@ typedef struct {
   int32_t* near_ties;
 } eagle_tree_expand_args;
 
+/* The final draft tree from chained expansion steps (EAGLE notes page, the
+ * EAGLE-2 section: nodes are kept by the cumulative confidence of their
+ * paths).  parent/token/value [steps, B, keep] hold the outputs of `steps`
+ * calls of eagle_verify_tree_expand: step 0 expanded the root (its parents
+ * are 0), step d > 0 expanded step d-1's kept list (its parents index that
+ * list); parent -1 = no candidate.  The `nodes` candidates of largest value
+ * are kept, ties to the earlier step, then the better rank; a node's value
+ * never exceeds its parent's, so every kept node's parent is kept.
+ * Outputs (device): parents/tokens [B, nodes + 1]: row 0 the root (parent -1,
+ * token root_tokens[b]), then the kept nodes in (step, rank) order, parents
+ * before children (the layout tree_attention and spec_accept read), rows
+ * past the last kept node -1; rows [B] = 1 + kept nodes.
+ * Limits: steps <= 64, keep <= 64, nodes + 1 <= max_tree_rows. */
+typedef struct {
+  int32_t batch;
+  int32_t steps;
+  int32_t keep;
+  int32_t nodes;
+  const int32_t* parent;
+  const int32_t* token;
+  const float* value;
+  const int32_t* root_tokens;
+  int32_t* parents;
+  int32_t* tokens;
+  int32_t* rows;
+} eagle_tree_rerank_args;
+
 /* Launch plan of one tree-attention call (what eagle_verify_tree_attention
  * will launch for these arguments). */
 typedef struct {
@@ -292,6 +319,9 @@ EAGLE_API eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_co
  * calls on one handle must not overlap. */
 EAGLE_API eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_args* a, void* hip_stream);
 
+/* Final draft tree from chained expansion steps, see eagle_tree_rerank_args. */
+EAGLE_API eagle_status eagle_verify_tree_rerank(eagle_verify* h, const eagle_tree_rerank_args* a, void* hip_stream);
+
 /* Synchronise the last stream the handle used, free the workspace and the
  * handle.  NULL is accepted. */
 EAGLE_API eagle_status eagle_verify_destroy(eagle_verify* h);
@@ -310,6 +340,7 @@ EAGLE_API eagle_status eagle_verify_check_spec_accept(const eagle_verify_desc* d
                                             const eagle_spec_accept_args* a);
 EAGLE_API eagle_status eagle_verify_check_kv_commit(const eagle_verify_desc* desc, const eagle_kv_commit_args* a);
 EAGLE_API eagle_status eagle_verify_check_tree_expand(const eagle_verify_desc* desc, const eagle_tree_expand_args* a);
+EAGLE_API eagle_status eagle_verify_check_tree_rerank(const eagle_verify_desc* desc, const eagle_tree_rerank_args* a);
 
 /* Launch plan of the last successful eagle_verify_tree_attention call on h
  * (merge_in_kernel included).  No HIP call is made.

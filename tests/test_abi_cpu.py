@@ -185,6 +185,26 @@ def test_tree_expand_argument_errors():
     assert ev.eagle_verify_check_tree_expand(_desc(vocab_size=64 * 8192 + 1), _te_args()) == ev.EAGLE_ERR_UNSUPPORTED
 
 
+def test_tree_rerank_argument_errors():
+    d = _desc()
+
+    def args(**over):
+        a = ev.TreeRerankArgs()
+        a.batch, a.steps, a.keep, a.nodes = 2, 6, 8, 60
+        fake = 1 << 20
+        a.parent = a.token = a.value = a.root_tokens = a.parents = a.tokens = a.rows = fake
+        for k, v in over.items():
+            setattr(a, k, v)
+        return a
+
+    assert ev.eagle_verify_check_tree_rerank(d, args()) == ev.EAGLE_OK
+    for over, want in ((dict(batch=0), ev.EAGLE_ERR_ARG), (dict(steps=0), ev.EAGLE_ERR_ARG),
+                       (dict(steps=65), ev.EAGLE_ERR_ARG), (dict(keep=65), ev.EAGLE_ERR_ARG),
+                       (dict(nodes=61), ev.EAGLE_ERR_CAPACITY), (dict(nodes=-1), ev.EAGLE_ERR_ARG),
+                       (dict(rows=None), ev.EAGLE_ERR_ARG), (dict(tokens=(1 << 20) + 2), ev.EAGLE_ERR_ARG)):
+        assert ev.eagle_verify_check_tree_rerank(d, args(**over)) == want, over
+
+
 def test_descriptor_errors():
     for kw in (dict(max_batch=0), dict(max_batch=257), dict(max_tree_rows=65), dict(vocab_size=1),
                dict(num_q_heads=0)):

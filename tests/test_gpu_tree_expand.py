@@ -131,3 +131,32 @@ def test_workload_shape_three_depths(dtype):
         frontier_gpu = got["value"].astype(np.float32)
         frontier_ora = want["value"]
     ver.close()
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_rerank_of_chained_oracle_steps(seed):
+    """Steps produced by the oracle (values as float32), reranked on both sides."""
+    import torch
+    rng = np.random.default_rng(seed)
+    B, V = 3, 700
+    steps = [(4, 6), (3, 8), (3, 8), (2, 8)]
+    Mx = 8
+    fr = np.zeros((B, 1))
+    P = np.full((len(steps), B, Mx), -1, dtype=np.int32)
+    T = np.full((len(steps), B, Mx), -1, dtype=np.int32)
+    Vv = np.full((len(steps), B, Mx), -np.inf, dtype=np.float32)
+    for d, (k, M) in enumerate(steps):
+        x = _logits(rng, B, fr.shape[1], V, scale=2.0)
+        out = ote.expand(x, fr, 1.0, k, M)
+        P[d, :, :M], T[d, :, :M], Vv[d, :, :M] = out["parent"], out["token"], out["value"].astype(np.float32)
+        fr = out["value"]
+    roots = np.array([5, 6, 7], dtype=np.int32)
+    ver = _verifier(B, 61, V, "f32")   # room for 60 nodes
+    for N in (5, 20, 60):
+        want = ote.rerank(P, T, Vv, roots, N)
+        got = ver.tree_rerank(dev(P), dev(T), dev(Vv), dev(roots), N)
+        torch.cuda.synchronize()
+        for key in ("parents", "tokens", "rows"):
+            assert np.array_equal(got[key].cpu().numpy(), want[key]), (N, key)
+    log(f"  rerank seed {seed}: rows {want['rows'].tolist()}")
+    ver.close()
