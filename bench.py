@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=8, help="rotated input sets (Infinity Cache defeat)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-commit", action="store_true", help="skip timing the KV commit of the accepted path")
+    ap.add_argument("--no-commit", action="store_true",
+                    help="skip timing the calls beside the step (KV commit, tree expansion)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (HBM counter calibration)")
@@ -291,6 +292,28 @@ def main():
         commit_bytes = layers * 2 * moved * Hkv * D * esz * 2   # K and V slices, read once and written once
         del kl, vl
 
+    # timed region 4 (beside the step): one draft-tree expansion step at the
+    # workload's vocabulary, an 8-node frontier with 4 children each, 8 kept
+    # (the draft's next-token rows are the synthetic draft logits of input
+    # set 0, whose first 8 rows stand in for the frontier)
+    expand_ms = None
+    if not args.no_commit:
+        F, K_EXP, M_EXP = 8, 4, 8
+        xl = sets[0]["drf"][:, :F].contiguous()
+        fr = torch.zeros((B, F), dtype=torch.float32, device="cuda")
+        eouts = None
+        for _ in range(5):
+            eouts = ver.tree_expand(xl, fr, 1.0, K_EXP, M_EXP, outputs=eouts)
+        torch.cuda.synchronize()
+        epairs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            epairs[i][0].record(stream)
+            ver.tree_expand(xl, fr, 1.0, K_EXP, M_EXP, outputs=eouts, stream=stream)
+            epairs[i][1].record(stream)
+        torch.cuda.synchronize()
+        expand_ms = np.array([p[0].elapsed_time(p[1]) for p in epairs])
+        expand_bytes = B * F * V * (2 if spec.ldtype == "bf16" else 4)   # the frontier's logit rows, read once
+
     if args.copy_probe:
         src = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -317,6 +340,10 @@ def main():
                                    nb["attention_bytes"], float(attn_ms.mean()) * 1e-3),
         "spec_accept": roofline("sa_fused (one spec_accept call)", nb["accept_bytes"], float(acc_ms.mean()) * 1e-3),
     }
+    if expand_ms is not None:
+        rooflines["tree_expand"] = roofline(f"te_chunk + te_row + te_select (one tree_expand call: {F}-node frontier, "
+                                            f"top-{K_EXP} each, {M_EXP} kept)", expand_bytes,
+                                            float(expand_ms.mean()) * 1e-3)
     if commit_ms is not None:
         rooflines["kv_commit"] = roofline(f"kv_commit_rows (one kv_commit call over {layers} layers, "
                                           f"{moved} of {len(path)} accepted rows move)",
@@ -352,6 +379,7 @@ def main():
         "accept_us_median": acc_us,
         "accept_us_p10_p90": [float(np.percentile(acc_ms, 10) * 1e3), float(np.percentile(acc_ms, 90) * 1e3)],
         "kv_commit_us_median": float(np.median(commit_ms) * 1e3) if commit_ms is not None else None,
+        "tree_expand_us_median": float(np.median(expand_ms) * 1e3) if expand_ms is not None else None,
         "roofline": main_roof,
         "roofline_per_call": rooflines,
     }

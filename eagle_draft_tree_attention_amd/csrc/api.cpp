@@ -111,8 +111,10 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t spart_bytes = sizeof(uint64_t) * 4 * B * T * NC;   // fused: four tagged words per chunk
   off = align_up(off + spart_bytes, 256);
   const size_t o_expand = off;   // tree-expansion chunk records
-  const int64_t nce = std::min<int64_t>(NC, ev::kMaxChunksExpand);
+  const int64_t nce = std::min<int64_t>(ev::expand_chunks(desc->vocab_size), ev::kMaxChunksExpand);
   off = align_up(off + sizeof(ev::ChunkRecord) * B * T * nce, 256);
+  const size_t o_expand_rows = off;
+  off = align_up(off + sizeof(ev::RowRecord) * B * T, 256);
   const size_t o_cnt = off;
   const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
   off = align_up(off + cnt_bytes, 256);
@@ -138,6 +140,7 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.spart = reinterpret_cast<double*>(p + o_spart);
   h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
   h->ws.expand = reinterpret_cast<ev::ChunkRecord*>(p + o_expand);
+  h->ws.expand_rows = reinterpret_cast<ev::RowRecord*>(p + o_expand_rows);
   h->ws.node_pub = reinterpret_cast<uint64_t*>(p + o_sync);
   h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
   h->ws.bytes = off;
@@ -361,6 +364,7 @@ eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_a
   k.logits = a->draft_logits;
   k.scores = a->scores;
   k.chunks = h->ws.expand;
+  k.rows = h->ws.expand_rows;
   k.parent = a->parent;
   k.token = a->token;
   k.value = a->value;
@@ -369,7 +373,8 @@ eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_a
   k.B = a->batch;
   k.F = a->frontier;
   k.V = h->desc.vocab_size;
-  k.NC = ev::vocab_chunks(k.V);
+  k.chunk = ev::expand_chunk(k.V);
+  k.NC = ev::expand_chunks(k.V);
   k.K = a->top_k;
   k.M = a->keep;
   k.c2 = static_cast<float>(1.4426950408889634 / a->temperature);

@@ -148,6 +148,10 @@ struct CommitKernelArgs {
 constexpr int kMaxTopK = 16;          // children per frontier node
 constexpr int kMaxKeep = 64;          // candidates kept per sequence
 constexpr int kMaxChunksExpand = 64;  // vocabulary chunks of one row (V <= 64 * 8192)
+// tokens per expansion chunk: the smallest of 2048, 4096, 8192 that keeps a
+// row within kMaxChunksExpand chunks
+inline int expand_chunk(int V) { return V <= 64 * 2048 ? 2048 : (V <= 64 * 4096 ? 4096 : 8192); }
+inline int expand_chunks(int V) { return (V + expand_chunk(V) - 1) / expand_chunk(V); }
 
 struct ChunkRecord {   // one (sequence, frontier row, vocab chunk)
   float m;             // chunk maximum (-inf if none finite)
@@ -157,16 +161,26 @@ struct ChunkRecord {   // one (sequence, frontier row, vocab chunk)
   int32_t id[kMaxTopK];// their token ids, -1 past the last
 };
 
+struct RowRecord {      // one (sequence, frontier row): its top-k candidates, best first
+  double value[kMaxTopK];
+  float logit[kMaxTopK];
+  int32_t token[kMaxTopK];
+  int32_t count;       // candidates (0 for an inactive or unusable row)
+  int32_t unusable;    // NaN/+inf or all -inf in an active row
+};
+
 struct ExpandKernelArgs {
   const void* logits;  // [B][F][V]
   const float* scores; // [B][F]
   ChunkRecord* chunks; // [B][F][NC]
+  RowRecord* rows;     // [B][F]
   int32_t* parent;     // [B][M]
   int32_t* token;      // [B][M]
   float* value;        // [B][M]
   uint32_t* flags;     // [B]
   int32_t* near_ties;  // [B]
   int B, F, V, NC, K, M;
+  int chunk;           // vocabulary tokens per chunk (2048, 4096 or 8192)
   float c2;            // log2(e) / t
   double inv_tau;      // 1 / t
 };
@@ -194,7 +208,8 @@ struct Workspace {
   double* fpart = nullptr;
   double* spart = nullptr;
   uint32_t* counters = nullptr; // cnt_stats | cnt_pass | cnt_final
-  ChunkRecord* expand = nullptr; // [max_batch][max_tree_rows][min(NC, kMaxChunksExpand)]
+  ChunkRecord* expand = nullptr; // [max_batch][max_tree_rows][expansion chunks of a row]
+  RowRecord* expand_rows = nullptr; // [max_batch][max_tree_rows]
   size_t bytes = 0;
 };
 

@@ -10,17 +10,19 @@
 // the M candidates of largest value are kept, ties to the lower frontier
 // index, then the lower token id.
 //
-// GPU formulation, two launches:
-//   te_chunk   one workgroup per (sequence, frontier row, 8192-token chunk):
+// GPU formulation, three launches:
+//   te_chunk   one workgroup per (sequence, frontier row, vocabulary chunk of
+//              2048, 4096 or 8192 tokens, at most 64 chunks a row):
 //              the chunk's maximum, its sum of exp((x - max)/t) (fp32
 //              exponentials, fp64 sum), NaN/+inf detection and its k largest
-//              logits with their ids (k rounds of a block-wide argmax over
-//              each thread's own sorted short list); one record per chunk.
-//   te_select  one wave per sequence, lane f = frontier row f: the row's
-//              maximum and normaliser from its chunks, its top k from the
-//              chunks' sorted lists (a k-step merge), the candidates' values
-//              s_f + (x - max)/t - log Z in fp64, then the global ranking as a
-//              merge of the rows' sorted lists: each step the wave picks the
+//              logits with their ids (k rounds of a wave argmax per wave, then
+//              a merge of the four waves' lists); one record per chunk.
+//   te_row     one wave per (sequence, frontier row), lane c = chunk c: the
+//              row's maximum and normaliser, its top k as a k-step merge of
+//              the chunks' sorted lists, the candidates' values
+//              s_f + (x - max)/t - log Z in fp64.
+//   te_select  one wave per sequence, lane f = frontier row f: the global
+//              ranking as a merge of the rows' sorted lists: each step the wave picks the
 //              largest head (ties: the lowest lane), M + 1 steps, the last one
 //              only to see whether the boundary is a near tie.
 //   te_rerank  (separate call) the final tree from the chained steps.
@@ -37,7 +39,6 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = kVocabChunk / kThreads;   // 32 logits per thread
 constexpr float kNegInf = -__builtin_inff();
 constexpr double kNear = 1e-6;                      // near-tie margin of the ranking (log-probability units)
 
@@ -52,19 +53,21 @@ __device__ __forceinline__ bool before(float a, int ia, float b, int ib) {
   return a > b || (a == b && ia < ib);
 }
 
-template <typename TL>
+// EPT logits per thread: chunks of 256 * EPT tokens (2048, 4096 or 8192,
+// the smallest that keeps a row within 64 chunks)
+template <typename TL, int EPT>
 __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
+  constexpr int kPerThread = EPT;
+  constexpr int kChunk = kThreads * EPT;
   __shared__ float rmax[kThreads / 64];
   __shared__ uint32_t rbad[kThreads / 64];
   __shared__ double rsum[kThreads / 64];
-  __shared__ float wv[kThreads / 64];
-  __shared__ int wi[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NC = a.NC, V = a.V, K = a.K;
   const int c = blockIdx.x % NC;
   const int row = blockIdx.x / NC;   // b * F + f
   const TL* x = reinterpret_cast<const TL*>(a.logits) + static_cast<int64_t>(row) * V;
-  const int v0 = c * kVocabChunk, v1 = min(V, v0 + kVocabChunk);
+  const int v0 = c * kChunk, v1 = min(V, v0 + kChunk);
 
   // this thread's logits: tokens v0 + tid + 256 j
   float xs[kPerThread];
@@ -99,29 +102,41 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
   for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
   if (lane == 0) rsum[wave] = z;
 
-  // this thread's sorted short list (K largest of its 32, -inf excluded)
-  float lv[kMaxTopK];
-  int li[kMaxTopK];
+  // top K of the chunk: each wave first takes the K largest of its 64 * EPT
+  // logits in K rounds (each lane offers its best not yet taken, the wave
+  // keeps the winner), then wave 0 merges the four waves' sorted lists.
+  // NaN and +inf are never candidates (the row is unusable anyway), -inf
+  // neither.  Within a lane, a lower j is a lower token id.
 #pragma unroll
-  for (int q = 0; q < kMaxTopK; ++q) {
-    lv[q] = kNegInf;
-    li[q] = 0x7FFFFFFF;
-  }
+  for (int j = 0; j < kPerThread; ++j)
+    if (!(xs[j] < __builtin_inff())) xs[j] = kNegInf;
+  __shared__ float wl_v[kThreads / 64][kMaxTopK];
+  __shared__ int wl_i[kThreads / 64][kMaxTopK];
+  uint32_t taken = 0;
+  for (int q = 0; q < K; ++q) {
+    float lb = kNegInf;
+    int lj = -1;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    float v = xs[j];
-    int id = v0 + tid + kThreads * j;
-    if (!(v > kNegInf) || v == __builtin_inff()) continue;   // -inf, NaN and +inf are never candidates
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q) {
-      if (q < K && before(v, id, lv[q], li[q])) {
-        const float tv = lv[q];
-        const int ti = li[q];
-        lv[q] = v;
-        li[q] = id;
-        v = tv;
-        id = ti;
+    for (int j = 0; j < kPerThread; ++j)
+      if (!((taken >> j) & 1u) && xs[j] > lb) {
+        lb = xs[j];
+        lj = j;
       }
+    const int lid = lj >= 0 ? v0 + tid + kThreads * lj : 0x7FFFFFFF;
+    float bv = lb;
+    int bi = lid;
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (before(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lj >= 0 && lid == bi) taken |= 1u << lj;
+    if (lane == 0) {
+      wl_v[wave][q] = bv;
+      wl_i[wave][q] = bv > kNegInf ? bi : -1;
     }
   }
   __syncthreads();
@@ -131,17 +146,90 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
     rec->bad = bad;
     rec->z = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
   }
-  // K rounds of a block-wide argmax over the threads' list heads
-  int head = 0;
+  if (wave == 0) {   // lanes 0..3 hold the heads of the four waves' lists
+    int hd = 0;
+    for (int q = 0; q < K; ++q) {
+      float hv = kNegInf;
+      int hi = 0x7FFFFFFF;
+      if (lane < kThreads / 64 && hd < K && wl_i[lane][hd] >= 0) {
+        hv = wl_v[lane][hd];
+        hi = wl_i[lane][hd];
+      }
+      float bv = hv;
+      int bi = hi;
+      for (int off = 2; off > 0; off >>= 1) {   // lanes 0..3
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (before(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (lane < kThreads / 64 && hv == bv && hi == bi && bv > kNegInf) ++hd;
+      if (lane == 0) {
+        rec->val[q] = bv;
+        rec->id[q] = bv > kNegInf ? bi : -1;
+      }
+    }
+  }
+}
+
+// One wave per (sequence, frontier row), lane c = chunk c: the row's maximum,
+// normaliser and unusable flag from its chunk records, then its top K as a
+// K-step merge of the chunks' sorted lists (each step the wave takes the best
+// head), valued s + (x - max)/t - log Z in fp64.
+__global__ __launch_bounds__(64) void te_row(const ExpandKernelArgs a) {
+  __shared__ float lv[kMaxChunksExpand][kMaxTopK];
+  __shared__ int li[kMaxChunksExpand][kMaxTopK];
+  const int lane = threadIdx.x, row = blockIdx.x;   // row = b * F + f
+  const int NC = a.NC, K = a.K;
+  RowRecord* const out = a.rows + row;
+  const float s = a.scores[row];
+  if (!(s > kNegInf)) {   // inactive (NaN and -inf): no candidates, not flagged
+    if (lane == 0) {
+      out->count = 0;
+      out->unusable = 0;
+    }
+    return;
+  }
+  const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC;
+  float mc = kNegInf;
+  uint32_t bad = 0;
+  double zc = 0.0;
+  if (lane < NC) {
+    mc = rec[lane].m;
+    bad = rec[lane].bad;
+    zc = rec[lane].z;
+    for (int q = 0; q < K; ++q) {
+      lv[lane][q] = rec[lane].val[q];
+      li[lane][q] = rec[lane].id[q];
+    }
+  }
+  float mx = mc;
+  for (int off = 32; off > 0; off >>= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+    bad |= __shfl_xor(bad, off);
+  }
+  const bool unusable = bad != 0 || mx == kNegInf;
+  if (unusable) {
+    if (lane == 0) {
+      out->count = 0;
+      out->unusable = 1;
+    }
+    return;
+  }
+  double z = (lane < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - mx) * static_cast<double>(a.c2)) : 0.0;
+  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+  const double lz = log(z);
+  __syncthreads();   // the lists are in LDS
+  int hd = 0, cnt = 0;
   for (int q = 0; q < K; ++q) {
     float hv = kNegInf;
     int hi = 0x7FFFFFFF;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r)
-      if (r == head) {
-        hv = lv[r];
-        hi = li[r];
-      }
+    if (lane < NC && hd < K && li[lane][hd] >= 0) {
+      hv = lv[lane][hd];
+      hi = li[lane][hd];
+    }
     float bv = hv;
     int bi = hi;
     for (int off = 32; off > 0; off >>= 1) {
@@ -152,25 +240,18 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
         bi = oi;
       }
     }
+    if (!(bv > kNegInf)) break;   // every list is exhausted
+    if (hi == bi && hv == bv) ++hd;   // token ids are unique: one lane wins
     if (lane == 0) {
-      wv[wave] = bv;
-      wi[wave] = bi;
+      out->logit[cnt] = bv;
+      out->token[cnt] = bi;
+      out->value[cnt] = static_cast<double>(s) + (static_cast<double>(bv) - mx) * a.inv_tau - lz;
     }
-    __syncthreads();
-    float gv = wv[0];
-    int gi = wi[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w)
-      if (before(wv[w], wi[w], gv, gi)) {
-        gv = wv[w];
-        gi = wi[w];
-      }
-    __syncthreads();   // wv / wi are rewritten by the next round
-    if (tid == 0) {
-      rec->val[q] = gv;
-      rec->id[q] = gv > kNegInf ? gi : -1;
-    }
-    if (gv > kNegInf && hi == gi && hv == gv) ++head;   // the winning thread moves to its next entry
+    ++cnt;
+  }
+  if (lane == 0) {
+    out->count = cnt;
+    out->unusable = 0;
   }
 }
 
@@ -178,54 +259,19 @@ __global__ __launch_bounds__(64) void te_select(const ExpandKernelArgs a) {
   __shared__ double sv[64][kMaxTopK];   // lane f's candidates: value
   __shared__ int st[64][kMaxTopK];      // and token, sorted
   __shared__ float sx[64][kMaxTopK];    // and logit (equal logits of one row tie exactly)
-  __shared__ uint8_t hd[64][kMaxChunksExpand];   // lane f's position in each chunk list during the merge
   const int lane = threadIdx.x, b = blockIdx.x;
-  const int F = a.F, NC = a.NC, K = a.K, M = a.M;
+  const int F = a.F, M = a.M;
   int cnt = 0;            // candidates of row `lane`
   bool unusable = false;
-  if (lane < F) {
-    const float s = a.scores[b * F + lane];
-    if (s > kNegInf) {    // active (NaN and -inf are not)
-      const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(b * F + lane) * NC;
-      float mx = kNegInf;
-      uint32_t bad = 0;
-      for (int c = 0; c < NC; ++c) {
-        mx = fmaxf(mx, rec[c].m);
-        bad |= rec[c].bad;
-      }
-      unusable = bad != 0 || mx == kNegInf;
-      if (!unusable) {
-        double z = 0.0;
-        for (int c = 0; c < NC; ++c)
-          if (rec[c].m != kNegInf) z += rec[c].z * exp2((static_cast<double>(rec[c].m) - mx) * static_cast<double>(a.c2));
-        const double lz = log(z);
-        // merge the chunks' sorted lists: K steps, each taking the best head
-        for (int c = 0; c < NC; ++c) hd[lane][c] = 0;
-        for (int q = 0; q < K; ++q) {
-          int bc = -1;
-          float bv = kNegInf;
-          int bi = 0x7FFFFFFF;
-          for (int c = 0; c < NC; ++c) {
-            const int h = hd[lane][c];
-            if (h >= K) continue;
-            const int id = rec[c].id[h];
-            if (id < 0) continue;
-            const float v = rec[c].val[h];
-            if (before(v, id, bv, bi)) {
-              bv = v;
-              bi = id;
-              bc = c;
-            }
-          }
-          if (bc < 0) break;
-          ++hd[lane][bc];
-          sx[lane][cnt] = bv;
-          st[lane][cnt] = bi;
-          sv[lane][cnt] = static_cast<double>(s) + (static_cast<double>(bv) - mx) * a.inv_tau - lz;
-          ++cnt;
-        }
-      }
+  if (lane < F) {   // every entry up to K is requested at once; the count says which are valid
+    const RowRecord* const r = a.rows + b * F + lane;
+    for (int q = 0; q < a.K; ++q) {
+      sv[lane][q] = r->value[q];
+      st[lane][q] = r->token[q];
+      sx[lane][q] = r->logit[q];
     }
+    cnt = r->count;
+    unusable = r->unusable != 0;
   }
   // global ranking: merge of the rows' lists, the largest head each step,
   // ties to the lowest lane (frontier index)
@@ -337,8 +383,14 @@ __global__ __launch_bounds__(64) void te_rerank(const RerankKernelArgs a) {
 
 template <typename TL>
 hipError_t launch_t(const ExpandKernelArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((te_chunk<TL>), dim3(static_cast<unsigned>(a.B * a.F * a.NC)), dim3(kThreads), 0, st, a);
+  const dim3 grid(static_cast<unsigned>(a.B * a.F * a.NC));
+  if (a.chunk == 2048) hipLaunchKernelGGL((te_chunk<TL, 8>), grid, dim3(kThreads), 0, st, a);
+  else if (a.chunk == 4096) hipLaunchKernelGGL((te_chunk<TL, 16>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((te_chunk<TL, 32>), grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(te_row, dim3(static_cast<unsigned>(a.B * a.F)), dim3(64), 0, st, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(te_select, dim3(static_cast<unsigned>(a.B)), dim3(64), 0, st, a);
   return hipGetLastError();

@@ -253,7 +253,7 @@ eagle_status check_tree_expand(const eagle_verify_desc* d, const eagle_tree_expa
     return fail(EAGLE_ERR_ARG, err, errlen, "top_k=%d outside [1, %d]", a->top_k, kMaxTopK);
   if (a->keep < 1 || a->keep > kMaxKeep)
     return fail(EAGLE_ERR_ARG, err, errlen, "keep=%d outside [1, %d]", a->keep, kMaxKeep);
-  if (vocab_chunks(d->vocab_size) > kMaxChunksExpand)
+  if (expand_chunks(d->vocab_size) > kMaxChunksExpand)
     return fail(EAGLE_ERR_UNSUPPORTED, err, errlen, "vocab_size=%d above %d for tree expansion", d->vocab_size,
                 kMaxChunksExpand * kVocabChunk);
   if (!(a->temperature > 0.f) || !std::isfinite(a->temperature))
