@@ -113,8 +113,6 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   const size_t o_expand = off;   // tree-expansion chunk records
   const int64_t nce = std::min<int64_t>(ev::expand_chunks(desc->vocab_size), ev::kMaxChunksExpand);
   off = align_up(off + sizeof(ev::ChunkRecord) * B * T * nce, 256);
-  const size_t o_expand_rows = off;
-  off = align_up(off + sizeof(ev::RowRecord) * B * T, 256);
   const size_t o_cnt = off;
   const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
   off = align_up(off + cnt_bytes, 256);
@@ -140,7 +138,6 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.spart = reinterpret_cast<double*>(p + o_spart);
   h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
   h->ws.expand = reinterpret_cast<ev::ChunkRecord*>(p + o_expand);
-  h->ws.expand_rows = reinterpret_cast<ev::RowRecord*>(p + o_expand_rows);
   h->ws.node_pub = reinterpret_cast<uint64_t*>(p + o_sync);
   h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
   h->ws.bytes = off;
@@ -364,7 +361,6 @@ eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_a
   k.logits = a->draft_logits;
   k.scores = a->scores;
   k.chunks = h->ws.expand;
-  k.rows = h->ws.expand_rows;
   k.parent = a->parent;
   k.token = a->token;
   k.value = a->value;

@@ -161,19 +161,11 @@ struct ChunkRecord {   // one (sequence, frontier row, vocab chunk)
   int32_t id[kMaxTopK];// their token ids, -1 past the last
 };
 
-struct RowRecord {      // one (sequence, frontier row): its top-k candidates, best first
-  double value[kMaxTopK];
-  float logit[kMaxTopK];
-  int32_t token[kMaxTopK];
-  int32_t count;       // candidates (0 for an inactive or unusable row)
-  int32_t unusable;    // NaN/+inf or all -inf in an active row
-};
 
 struct ExpandKernelArgs {
   const void* logits;  // [B][F][V]
   const float* scores; // [B][F]
   ChunkRecord* chunks; // [B][F][NC]
-  RowRecord* rows;     // [B][F]
   int32_t* parent;     // [B][M]
   int32_t* token;      // [B][M]
   float* value;        // [B][M]
@@ -209,7 +201,6 @@ struct Workspace {
   double* spart = nullptr;
   uint32_t* counters = nullptr; // cnt_stats | cnt_pass | cnt_final
   ChunkRecord* expand = nullptr; // [max_batch][max_tree_rows][expansion chunks of a row]
-  RowRecord* expand_rows = nullptr; // [max_batch][max_tree_rows]
   size_t bytes = 0;
 };
 

@@ -10,21 +10,22 @@
 // the M candidates of largest value are kept, ties to the lower frontier
 // index, then the lower token id.
 //
-// GPU formulation, three launches:
+// GPU formulation, two launches:
 //   te_chunk   one workgroup per (sequence, frontier row, vocabulary chunk of
 //              2048, 4096 or 8192 tokens, at most 64 chunks a row):
 //              the chunk's maximum, its sum of exp((x - max)/t) (fp32
 //              exponentials, fp64 sum), NaN/+inf detection and its k largest
 //              logits with their ids (k rounds of a wave argmax per wave, then
 //              a merge of the four waves' lists); one record per chunk.
-//   te_row     one wave per (sequence, frontier row), lane c = chunk c: the
-//              row's maximum and normaliser, its top k as a k-step merge of
-//              the chunks' sorted lists, the candidates' values
-//              s_f + (x - max)/t - log Z in fp64.
-//   te_select  one wave per sequence, lane f = frontier row f: the global
-//              ranking as a merge of the rows' sorted lists: each step the wave picks the
-//              largest head (ties: the lowest lane), M + 1 steps, the last one
-//              only to see whether the boundary is a near tie.
+//   te_select  one workgroup per sequence: one wave per frontier row reads
+//              the row's chunk records and reduces its maximum and
+//              normaliser, takes its top k as a k-step merge of the chunks'
+//              sorted lists and values them s_f + (x - max)/t - log Z in
+//              fp64 (lists handed over in LDS); then one wave, lane f =
+//              row f, ranks globally by merging the rows' lists: each step
+//              it takes the largest head (ties: the lowest lane), M + 1
+//              steps, the last one only to see whether the boundary is a
+//              near tie.
 //   te_rerank  (separate call) the final tree from the chained steps.
 // Within a row the value is a monotone function of the logit, so a row's
 // list sorted by logit is sorted by value too.
@@ -48,10 +49,88 @@ __device__ __forceinline__ float logit_at(const TL* row, int v) {
   else return row[v];
 }
 
-// (value, id) order of the chunk lists: larger value first, then lower id
-__device__ __forceinline__ bool before(float a, int ia, float b, int ib) {
-  return a > b || (a == b && ia < ib);
+// ---- wave reductions through DPP: row shifts 1, 2, 4, 8 (a scan within each
+// row of 16 lanes), then row broadcasts 15 and 31, so that lane 63 ends up
+// with the reduction of all 64 lanes; read out as a wave-uniform value.  Only
+// the ALU pipeline is used (no LDS round trips as with lane shuffles).  Every
+// lane of the wave must be active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v), CTRL, ROW_MASK, 0xf, false));
 }
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_mov64(uint64_t old, uint64_t v) {
+  const uint32_t lo = dpp_mov<CTRL, ROW_MASK>(static_cast<uint32_t>(old), static_cast<uint32_t>(v));
+  const uint32_t hi = dpp_mov<CTRL, ROW_MASK>(static_cast<uint32_t>(old >> 32), static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <typename Op>
+__device__ __forceinline__ uint64_t wave_reduce64(uint64_t x, const uint64_t ident, Op op) {
+  x = op(x, dpp_mov64<0x111, 0xf>(ident, x));   // row_shr:1
+  x = op(x, dpp_mov64<0x112, 0xf>(ident, x));   // row_shr:2
+  x = op(x, dpp_mov64<0x114, 0xf>(ident, x));   // row_shr:4
+  x = op(x, dpp_mov64<0x118, 0xf>(ident, x));   // row_shr:8 (lane 15 of a row: the row)
+  x = op(x, dpp_mov64<0x142, 0xa>(ident, x));   // row_bcast:15 into rows 1 and 3
+  x = op(x, dpp_mov64<0x143, 0xc>(ident, x));   // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x >> 32), 63));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce32(uint32_t x, const uint32_t ident, Op op) {
+  x = op(x, dpp_mov<0x111, 0xf>(ident, x));
+  x = op(x, dpp_mov<0x112, 0xf>(ident, x));
+  x = op(x, dpp_mov<0x114, 0xf>(ident, x));
+  x = op(x, dpp_mov<0x118, 0xf>(ident, x));
+  x = op(x, dpp_mov<0x142, 0xa>(ident, x));
+  x = op(x, dpp_mov<0x143, 0xc>(ident, x));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t p, uint64_t q) { return p > q ? p : q; }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) { return wave_reduce64(x, 0ull, max_u64); }
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+  return __uint_as_float(wave_reduce32(__float_as_uint(x), __float_as_uint(kNegInf),
+                                       [](uint32_t p, uint32_t q) { return __float_as_uint(fmaxf(__uint_as_float(p), __uint_as_float(q))); }));
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  return __longlong_as_double(static_cast<long long>(wave_reduce64(
+      static_cast<uint64_t>(__double_as_longlong(x)), 0ull, [](uint64_t p, uint64_t q) {
+        return static_cast<uint64_t>(__double_as_longlong(__longlong_as_double(static_cast<long long>(p)) +
+                                                          __longlong_as_double(static_cast<long long>(q))));
+      })));
+}
+
+// Order-preserving keys: a larger key is a larger number (-0 and +0 map to
+// one key, as they compare equal); key 0 lies below every number's key.
+__device__ __forceinline__ uint32_t ord32(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);   // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ uint64_t ord64(double d) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(d + 0.0));
+  return (u >> 63) ? ~u : (u | (1ull << 63));
+}
+__device__ __forceinline__ double unord64(uint64_t k) {
+  return __longlong_as_double(static_cast<long long>((k >> 63) ? (k & ~(1ull << 63)) : ~k));
+}
+
+// (logit, token) key of the top-k lists: larger logit first, then lower token
+// id; 0 = no entry
+__device__ __forceinline__ uint64_t cand_key(float x, int id) {
+  return (static_cast<uint64_t>(ord32(x)) << 32) | static_cast<uint32_t>(~id);
+}
+__device__ __forceinline__ float key_logit(uint64_t k) { return unord32(static_cast<uint32_t>(k >> 32)); }
+__device__ __forceinline__ int key_token(uint64_t k) { return static_cast<int>(~static_cast<uint32_t>(k)); }
 
 // EPT logits per thread: chunks of 256 * EPT tokens (2048, 4096 or 8192,
 // the smallest that keeps a row within 64 chunks)
@@ -81,10 +160,8 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
     else m = fmaxf(m, xs[j]);
   }
   // block maximum and bad flag
-  for (int off = 32; off > 0; off >>= 1) {
-    m = fmaxf(m, __shfl_xor(m, off));
-    bad |= __shfl_xor(bad, off);
-  }
+  m = wave_max_f32(m);
+  bad = __any(bad != 0) ? 1u : 0u;
   if (lane == 0) {
     rmax[wave] = m;
     rbad[wave] = bad;
@@ -99,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) z += static_cast<double>(__builtin_amdgcn_exp2f(__builtin_fmaf(xs[j], a.c2, mc)));
   }
-  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+  z = wave_sum_f64(z);
   if (lane == 0) rsum[wave] = z;
 
   // top K of the chunk: each wave first takes the K largest of its 64 * EPT
@@ -122,21 +199,12 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
         lb = xs[j];
         lj = j;
       }
-    const int lid = lj >= 0 ? v0 + tid + kThreads * lj : 0x7FFFFFFF;
-    float bv = lb;
-    int bi = lid;
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (lj >= 0 && lid == bi) taken |= 1u << lj;
+    const uint64_t key = lj >= 0 ? cand_key(lb, v0 + tid + kThreads * lj) : 0ull;
+    const uint64_t best = wave_max_u64(key);
+    if (lj >= 0 && key == best) taken |= 1u << lj;   // token ids are unique: one lane wins
     if (lane == 0) {
-      wl_v[wave][q] = bv;
-      wl_i[wave][q] = bv > kNegInf ? bi : -1;
+      wl_v[wave][q] = best ? key_logit(best) : kNegInf;
+      wl_i[wave][q] = best ? key_token(best) : -1;
     }
   }
   __syncthreads();
@@ -149,142 +217,120 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
   if (wave == 0) {   // lanes 0..3 hold the heads of the four waves' lists
     int hd = 0;
     for (int q = 0; q < K; ++q) {
-      float hv = kNegInf;
-      int hi = 0x7FFFFFFF;
-      if (lane < kThreads / 64 && hd < K && wl_i[lane][hd] >= 0) {
-        hv = wl_v[lane][hd];
-        hi = wl_i[lane][hd];
-      }
-      float bv = hv;
-      int bi = hi;
-      for (int off = 2; off > 0; off >>= 1) {   // lanes 0..3
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (before(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (lane < kThreads / 64 && hv == bv && hi == bi && bv > kNegInf) ++hd;
+      const uint64_t key = (lane < kThreads / 64 && hd < K && wl_i[lane][hd] >= 0)
+                               ? cand_key(wl_v[lane][hd], wl_i[lane][hd]) : 0ull;
+      uint64_t best = max_u64(key, dpp_mov64<0xB1, 0xf>(0ull, key));   // quad_perm 1,0,3,2
+      best = max_u64(best, dpp_mov64<0x4E, 0xf>(0ull, best));          // quad_perm 2,3,0,1
+      best = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(best >> 32), 0))) << 32) |
+             static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(best), 0));
+      if (key != 0ull && key == best) ++hd;
       if (lane == 0) {
-        rec->val[q] = bv;
-        rec->id[q] = bv > kNegInf ? bi : -1;
+        rec->val[q] = best ? key_logit(best) : kNegInf;
+        rec->id[q] = best ? key_token(best) : -1;
       }
     }
   }
 }
 
-// One wave per (sequence, frontier row), lane c = chunk c: the row's maximum,
-// normaliser and unusable flag from its chunk records, then its top K as a
-// K-step merge of the chunks' sorted lists (each step the wave takes the best
-// head), valued s + (x - max)/t - log Z in fp64.
-__global__ __launch_bounds__(64) void te_row(const ExpandKernelArgs a) {
-  __shared__ float lv[kMaxChunksExpand][kMaxTopK];
-  __shared__ int li[kMaxChunksExpand][kMaxTopK];
-  const int lane = threadIdx.x, row = blockIdx.x;   // row = b * F + f
-  const int NC = a.NC, K = a.K;
-  RowRecord* const out = a.rows + row;
-  const float s = a.scores[row];
-  if (!(s > kNegInf)) {   // inactive (NaN and -inf): no candidates, not flagged
-    if (lane == 0) {
-      out->count = 0;
-      out->unusable = 0;
+constexpr int kSelWaves = 8;   // frontier rows worked on at once by one workgroup
+
+// Wave-level hand-over through LDS: the wave's LDS writes are complete and
+// visible to its own lanes before any of them reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One workgroup per sequence.  Row phase: wave w takes frontier rows
+// w, w + 8, ...; for each, lane c reads chunk c's record, the wave reduces the
+// row's maximum, normaliser and unusable flag, and takes the row's top K as a
+// K-step merge of the chunks' sorted lists (each step the best head), valued
+// s + (x - max)/t - log Z in fp64, into LDS.  Selection phase (wave 0, lane
+// f = frontier row f): the global ranking as a merge of the rows' lists, the
+// largest head each step, ties to the lowest lane; M + 1 steps, the last one
+// only to see whether the boundary is a near tie.
+__global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelArgs a) {
+  __shared__ float lv[kSelWaves][kMaxChunksExpand][kMaxTopK];   // chunk lists of the wave's current row
+  __shared__ int li[kSelWaves][kMaxChunksExpand][kMaxTopK];
+  __shared__ double sv[kMaxTree][kMaxTopK];   // row f's candidates: value
+  __shared__ int st[kMaxTree][kMaxTopK];      // and token, sorted
+  __shared__ float sx[kMaxTree][kMaxTopK];    // and logit (equal logits of one row tie exactly)
+  __shared__ int scnt[kMaxTree], sbad[kMaxTree];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, b = blockIdx.x;
+  const int F = a.F, M = a.M, NC = a.NC, K = a.K;
+
+  for (int f = wave; f < F; f += kSelWaves) {
+    const int row = b * F + f;
+    const float s = a.scores[row];
+    if (!(s > kNegInf)) {   // inactive (NaN and -inf): no candidates, not flagged
+      if (lane == 0) {
+        scnt[f] = 0;
+        sbad[f] = 0;
+      }
+      continue;
     }
-    return;
-  }
-  const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC;
-  float mc = kNegInf;
-  uint32_t bad = 0;
-  double zc = 0.0;
-  if (lane < NC) {
-    mc = rec[lane].m;
-    bad = rec[lane].bad;
-    zc = rec[lane].z;
+    const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC;
+    float mc = kNegInf;
+    uint32_t bad = 0;
+    double zc = 0.0;
+    if (lane < NC) {
+      mc = rec[lane].m;
+      bad = rec[lane].bad;
+      zc = rec[lane].z;
+      for (int q = 0; q < K; ++q) {
+        lv[wave][lane][q] = rec[lane].val[q];
+        li[wave][lane][q] = rec[lane].id[q];
+      }
+    }
+    const float mx = wave_max_f32(mc);
+    if (__any(bad != 0) || mx == kNegInf) {   // unusable row: skipped, the sequence is flagged
+      if (lane == 0) {
+        scnt[f] = 0;
+        sbad[f] = 1;
+      }
+      continue;
+    }
+    const double z = wave_sum_f64(
+        (lane < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - mx) * static_cast<double>(a.c2)) : 0.0);
+    const double lz = log(z);
+    wave_lds_sync();   // the chunk lists are in LDS
+    int hd = 0, cnt = 0;
     for (int q = 0; q < K; ++q) {
-      lv[lane][q] = rec[lane].val[q];
-      li[lane][q] = rec[lane].id[q];
-    }
-  }
-  float mx = mc;
-  for (int off = 32; off > 0; off >>= 1) {
-    mx = fmaxf(mx, __shfl_xor(mx, off));
-    bad |= __shfl_xor(bad, off);
-  }
-  const bool unusable = bad != 0 || mx == kNegInf;
-  if (unusable) {
-    if (lane == 0) {
-      out->count = 0;
-      out->unusable = 1;
-    }
-    return;
-  }
-  double z = (lane < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - mx) * static_cast<double>(a.c2)) : 0.0;
-  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
-  const double lz = log(z);
-  __syncthreads();   // the lists are in LDS
-  int hd = 0, cnt = 0;
-  for (int q = 0; q < K; ++q) {
-    float hv = kNegInf;
-    int hi = 0x7FFFFFFF;
-    if (lane < NC && hd < K && li[lane][hd] >= 0) {
-      hv = lv[lane][hd];
-      hi = li[lane][hd];
-    }
-    float bv = hv;
-    int bi = hi;
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
+      const uint64_t key = (lane < NC && hd < K && li[wave][lane][hd] >= 0)
+                               ? cand_key(lv[wave][lane][hd], li[wave][lane][hd]) : 0ull;
+      const uint64_t best = wave_max_u64(key);
+      if (best == 0ull) break;   // every list is exhausted
+      if (key == best) ++hd;     // token ids are unique: one lane wins
+      const float bv = key_logit(best);
+      const int bi = key_token(best);
+      if (lane == 0) {
+        sx[f][cnt] = bv;
+        st[f][cnt] = bi;
+        sv[f][cnt] = static_cast<double>(s) + (static_cast<double>(bv) - mx) * a.inv_tau - lz;
       }
+      ++cnt;
     }
-    if (!(bv > kNegInf)) break;   // every list is exhausted
-    if (hi == bi && hv == bv) ++hd;   // token ids are unique: one lane wins
     if (lane == 0) {
-      out->logit[cnt] = bv;
-      out->token[cnt] = bi;
-      out->value[cnt] = static_cast<double>(s) + (static_cast<double>(bv) - mx) * a.inv_tau - lz;
+      scnt[f] = cnt;
+      sbad[f] = 0;
     }
-    ++cnt;
+    wave_lds_sync();   // the lists are read before the next row overwrites them
   }
-  if (lane == 0) {
-    out->count = cnt;
-    out->unusable = 0;
-  }
-}
+  __syncthreads();
+  if (wave != 0) return;
 
-__global__ __launch_bounds__(64) void te_select(const ExpandKernelArgs a) {
-  __shared__ double sv[64][kMaxTopK];   // lane f's candidates: value
-  __shared__ int st[64][kMaxTopK];      // and token, sorted
-  __shared__ float sx[64][kMaxTopK];    // and logit (equal logits of one row tie exactly)
-  const int lane = threadIdx.x, b = blockIdx.x;
-  const int F = a.F, M = a.M;
-  int cnt = 0;            // candidates of row `lane`
-  bool unusable = false;
-  if (lane < F) {   // every entry up to K is requested at once; the count says which are valid
-    const RowRecord* const r = a.rows + b * F + lane;
-    for (int q = 0; q < a.K; ++q) {
-      sv[lane][q] = r->value[q];
-      st[lane][q] = r->token[q];
-      sx[lane][q] = r->logit[q];
-    }
-    cnt = r->count;
-    unusable = r->unusable != 0;
-  }
-  // global ranking: merge of the rows' lists, the largest head each step,
-  // ties to the lowest lane (frontier index)
+  const int cnt = lane < F ? scnt[lane] : 0;   // candidates of row `lane`
+  const bool unusable = lane < F && sbad[lane] != 0;
   int pos = 0;
   double prev_v = 0.0;
   int prev_f = -1;
   float prev_x = 0.f;
   int near = 0;
   for (int step = 0; step <= M; ++step) {
-    const double hv = (lane < F && pos < cnt) ? sv[lane][pos] : -__builtin_inf();
-    double best = hv;
-    for (int off = 32; off > 0; off >>= 1) best = fmax(best, __shfl_xor(best, off));
-    if (!(best > -__builtin_inf())) {   // no candidate left: pad
+    const uint64_t key = pos < cnt ? ord64(sv[lane][pos]) : 0ull;
+    const uint64_t bkey = wave_max_u64(key);
+    if (bkey == 0ull) {   // no candidate left: pad
       if (lane == 0 && step < M) {
         a.parent[b * M + step] = -1;
         a.token[b * M + step] = -1;
@@ -292,10 +338,11 @@ __global__ __launch_bounds__(64) void te_select(const ExpandKernelArgs a) {
       }
       continue;
     }
-    const uint64_t hit = __ballot(hv == best && lane < F && pos < cnt);
+    const double best = unord64(bkey);
+    const uint64_t hit = __ballot(pos < cnt && key == bkey);
     const int w = __ffsll(static_cast<long long>(hit)) - 1;
-    const int wt = __shfl(lane < F && pos < cnt ? st[lane][pos] : 0, w);
-    const float wx = __shfl(lane < F && pos < cnt ? sx[lane][pos] : 0.f, w);
+    const int wt = __shfl(pos < cnt ? st[lane][pos] : 0, w);
+    const float wx = __shfl(pos < cnt ? sx[lane][pos] : 0.f, w);
     if (step > 0 && prev_v - best < kNear && !(prev_f == w && prev_x == wx)) ++near;
     prev_v = best;
     prev_f = w;
@@ -340,9 +387,9 @@ __global__ __launch_bounds__(64) void te_rerank(const RerankKernelArgs a) {
       has = a.parent[at] >= 0;
       if (has) hv = a.value[at];
     }
-    float best = has ? hv : kNegInf;
-    for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
-    const uint64_t hit = __ballot(has && hv == best);
+    const uint32_t key = has ? ord32(hv) : 0u;
+    const uint32_t bkey = static_cast<uint32_t>(wave_max_u64(key));
+    const uint64_t hit = __ballot(has && key == bkey);
     if (!hit) break;   // no candidate left
     const int w = __ffsll(static_cast<long long>(hit)) - 1;
     if (lane == w) {
@@ -389,10 +436,7 @@ hipError_t launch_t(const ExpandKernelArgs& a, hipStream_t st) {
   else hipLaunchKernelGGL((te_chunk<TL, 32>), grid, dim3(kThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(te_row, dim3(static_cast<unsigned>(a.B * a.F)), dim3(64), 0, st, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(te_select, dim3(static_cast<unsigned>(a.B)), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(te_select, dim3(static_cast<unsigned>(a.B)), dim3(64 * kSelWaves), 0, st, a);
   return hipGetLastError();
 }
 
