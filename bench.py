@@ -24,7 +24,6 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MODEL_LAYERS = 32   # decoder layers of the 8B model whose caches one commit call covers
 METRIC = "verified tree nodes/s per layer (attn+accept) at 8B/8K shape; % of HBM peak"
-CONFIG_INDEX = 2
 
 
 def eprint(*a):
@@ -37,6 +36,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--sets", type=int, default=8, help="rotated input sets (Infinity Cache defeat)")
+    ap.add_argument("--workload", default="llama31_8b_8k",
+                    help="synthetic workload by name (the headline is llama31_8b_8k; serving_b32 is the "
+                         "32-sequence serving batch)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true",
                     help="skip timing the calls beside the step (KV commit, tree expansion)")
@@ -75,12 +77,12 @@ def roofline(kernel, nbytes, seconds):
             "us_mean": seconds * 1e6}
 
 
-def recorded_traffic(call):
+def recorded_traffic(call, workload):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE + WRITE_SIZE,
     calibrated on a plain copy), as recorded in profiles/; None when no record exists
     or the kernel sources changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{call}_llama31_8b_8k.txt")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{call}_{workload}.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -165,7 +167,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    spec = synth.config_spec(CONFIG_INDEX)
+    by_name = {sp.name: i for i, sp in synth.CONFIGS.items()}
+    if args.workload not in by_name:
+        raise SystemExit(f"unknown workload {args.workload!r}; one of {sorted(by_name)}")
+    spec = synth.config_spec(by_name[args.workload])
     eprint(f"[bench] generating {spec.name} inputs")
     inp = synth.make_inputs(spec)
     T = inp.T
@@ -285,9 +290,10 @@ def main():
             cpairs[i][1].record(stream)
         torch.cuda.synchronize()
         commit_ms = np.array([p[0].elapsed_time(p[1]) for p in cpairs])
-        alen = int(outs["accept_len"].cpu()[0])
-        path = outs["accepted_nodes"].cpu().numpy()[0][:max(alen, 0)].tolist()
-        moved = sum(1 for i, node in enumerate(path, start=1) if node != i)
+        alens = outs["accept_len"].cpu().numpy()
+        nodes_acc = outs["accepted_nodes"].cpu().numpy()
+        moved = sum(1 for b in range(B) for i, node in enumerate(nodes_acc[b][:max(int(alens[b]), 0)], start=1)
+                    if node != i)
         esz = 2 if spec.dtype == "bf16" else 4
         commit_bytes = layers * 2 * moved * Hkv * D * esz * 2   # K and V slices, read once and written once
         del kl, vl
@@ -341,16 +347,16 @@ def main():
         "spec_accept": roofline("sa_fused (one spec_accept call)", nb["accept_bytes"], float(acc_ms.mean()) * 1e-3),
     }
     if expand_ms is not None:
-        rooflines["tree_expand"] = roofline(f"te_chunk + te_row + te_select (one tree_expand call: {F}-node frontier, "
+        rooflines["tree_expand"] = roofline(f"te_chunk + te_select (one tree_expand call: {F}-node frontier, "
                                             f"top-{K_EXP} each, {M_EXP} kept)", expand_bytes,
                                             float(expand_ms.mean()) * 1e-3)
     if commit_ms is not None:
         rooflines["kv_commit"] = roofline(f"kv_commit_rows (one kv_commit call over {layers} layers, "
-                                          f"{moved} of {len(path)} accepted rows move)",
+                                          f"{moved} of {int(np.maximum(alens, 0).sum())} accepted rows move over {B} sequences)",
                                           commit_bytes, float(commit_ms.mean()) * 1e-3)
     dominant = "spec_accept" if acc_ms.mean() > attn_ms.mean() else "tree_attention"
     main_roof = dict(rooflines[dominant])
-    main_roof["traffic"] = recorded_traffic(dominant)
+    main_roof["traffic"] = recorded_traffic(dominant, spec.name)
     result = {
         "metric": METRIC,
         "value": nodes / step_s,
@@ -365,10 +371,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{spec.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} prefix={spec.prefix_lens[0]} "
+            "workload": f"{spec.name}: B={B} Hq={Hq} Hkv={Hkv} D={D} "
+                        f"prefix={spec.prefix_lens[0] if B == 1 else f'{min(spec.prefix_lens)}..{max(spec.prefix_lens)}'} "
                         f"tree_rows={T} (60 draft nodes, depth 6) vocab={V} temperature={spec.temperature}",
             "global_batch": B,
-            "seq_len": spec.prefix_lens[0],
+            "seq_len": max(spec.prefix_lens),
             "parallelism": "single GPU",
             "input_sets_rotated": args.sets,
         },

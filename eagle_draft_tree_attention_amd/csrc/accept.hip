@@ -75,7 +75,7 @@ __device__ uint32_t philox4x32_10_x0(uint32_t c0, uint32_t c1, uint32_t c2, uint
 }
 
 __device__ double decision_uniform(const AcceptKernelArgs& a, int b, int node, uint32_t slot) {
-  const uint32_t x0 = philox4x32_10_x0(slot, static_cast<uint32_t>(node) | (static_cast<uint32_t>(b) << 8), a.off_lo,
+  const uint32_t x0 = philox4x32_10_x0(slot, static_cast<uint32_t>(node) | (static_cast<uint32_t>(a.b0 + b) << 8), a.off_lo,
                                        a.off_hi, a.seed_lo, a.seed_hi);
   return static_cast<double>(x0 >> 8) * (1.0 / 16777216.0);
 }

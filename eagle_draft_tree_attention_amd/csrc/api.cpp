@@ -293,22 +293,51 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   k.Tm = static_cast<int>(Tm);
   k.epoch = ++h->epoch;
   k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)
-  const int64_t fused_wgs = static_cast<int64_t>(k.B) * k.T * k.NC;
-  k.fused = (fused_wgs <= h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0] && k.NC <= 64) ? 1 : 0;
-  if (k.fused) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
+  h->last_stream = stream;
+  h->used = true;
+  // The fused kernel needs every workgroup of a launch resident at once.  A
+  // batch that does not fit is verified in slices of whole sequences, one
+  // fused launch each, back to back on the stream (each slice is a fused
+  // call of its own: its own epoch and round-word half); the uniforms keep
+  // the sequence's index in the whole batch.  Only a single sequence that
+  // does not fit takes the three-kernel path.
+  const int64_t per_seq = static_cast<int64_t>(k.T) * k.NC;
+  const int64_t cap = h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0];
+  if (per_seq > cap || k.NC > 64) {
+    k.fused = 0;
+    const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
+    if (e != 0) return hip_fail(h, "spec accept launch", e);
+    h->err[0] = 0;
+    return EAGLE_OK;
+  }
+  const int slice = static_cast<int>(std::min<int64_t>(k.B, cap / per_seq));
+  const int64_t row_bytes = static_cast<int64_t>(V) * esize;
+  const ev::AcceptKernelArgs whole = k;
+  for (int b0 = 0; b0 < whole.B; b0 += slice) {
+    k = whole;
+    k.fused = 1;
+    k.b0 = b0;
+    k.B = std::min(slice, whole.B - b0);
+    const int64_t rows0 = static_cast<int64_t>(b0) * whole.T;
+    k.target = static_cast<const char*>(whole.target) + rows0 * row_bytes;
+    if (whole.draft) k.draft = static_cast<const char*>(whole.draft) + rows0 * row_bytes;
+    k.parents = whole.parents + rows0;
+    k.tokens = whole.tokens + rows0;
+    k.accept_len = whole.accept_len + b0;
+    k.accepted_nodes = whole.accepted_nodes + rows0;
+    k.out_tokens = whole.out_tokens + rows0;
+    k.flags = whole.flags + b0;
+    k.near_ties = whole.near_ties + b0;
+    k.epoch = b0 == 0 ? whole.epoch : ++h->epoch;
     // the two halves of the round words alternate between fused calls
     const int64_t half = Bm * Tm * ev::kRoundWords;
     const int parity = static_cast<int>(h->fused_calls & 1);
     k.round_sum = h->ws.round_sum + parity * half;
     k.round_clear = h->ws.round_sum + (1 - parity) * half;
     k.zero_b = h->last_fused_b;
-  }
-  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
-  h->last_stream = stream;
-  h->used = true;
-  if (e != 0) return hip_fail(h, "spec accept launch", e);
-  if (k.fused) {
+    const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
+    if (e != 0) return hip_fail(h, "spec accept launch", e);
     ++h->fused_calls;
     h->last_fused_b = k.B;
   }

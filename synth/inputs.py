@@ -114,7 +114,8 @@ def _levels(sizes, rule):
 # The five workloads the method is characterised on (one layer each):
 #  0 tiny fp32 sanity case, 1 LLaMA-7B-shaped, 2 LLaMA-3.1-8B-shaped with GQA
 #  and an 8K prefix, 3 long-context agent shape (128K prefix, near-chain tree),
-#  4 70B-shaped batch of four ragged prefixes.
+#  4 70B-shaped batch of four ragged prefixes, 5 a serving batch of 32
+#  sequences with ragged prefixes.
 CONFIGS = {
     0: WorkloadSpec("tiny_fp32", "f32", 1, 4, 4, 64, (128,),
                     _levels((4, 4, 2), "uniform"), 1024, 3.0, 1.0, seed=1000),
@@ -127,6 +128,12 @@ CONFIGS = {
                     ("c3",), 128256, 4.0, 1.0, seed=1003),
     4: WorkloadSpec("llama70b_b4", "bf16", 4, 64, 8, 128, (1024, 2048, 3072, 4096),
                     _levels((10,) * 6, "rank"), 32000, 3.0, 0.7, seed=1004),
+    # serving batch: 32 sequences of an 8B-shaped model, prefixes log-uniform
+    # in [512, 4096] (drawn once from PCG64 seed 1005), 60-node trees
+    5: WorkloadSpec("serving_b32", "bf16", 32, 32, 8, 128,
+                    tuple(int(x) for x in np.rint(np.exp(np.random.default_rng(1005).uniform(
+                        np.log(512.0), np.log(4096.0), 32)))),
+                    _levels((10,) * 6, "rank"), 32000, 3.0, 0.7, seed=1005),
 }
 
 

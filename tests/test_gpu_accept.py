@@ -59,7 +59,8 @@ def test_accept_matches_oracle(spec):
     ver.close()
 
 
-@pytest.mark.parametrize("cfg,temp", [(0, 1.0), (1, 1.0), (1, 0.0), (2, 1.0), (3, 1.0), (4, 1.0)])
+@pytest.mark.parametrize("cfg,temp", [(0, 1.0), (1, 1.0), (1, 0.0), (2, 1.0), (3, 1.0), (4, 1.0), (5, 1.0),
+                                      (5, 0.0)])
 def test_accept_full_configs(cfg, temp):
     spec = synth.config_spec(cfg, temperature=temp)
     log(f"[accept] full size {spec.name} temperature {temp}")

@@ -168,7 +168,7 @@ def _samples(spec, inp, rng, n=10):
     return sorted(out, key=lambda s: (s[0], s[2] // g, s[1], s[2]))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 def test_attention_full_size_sampled(cfg):
     spec = synth.config_spec(cfg)
     log(f"[attention] full size {spec.name}: generating inputs")

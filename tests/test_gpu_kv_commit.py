@@ -178,7 +178,7 @@ def test_every_layer_in_one_launch():
     ver.close()
 
 
-@pytest.mark.parametrize("cfg", [0, 2])
+@pytest.mark.parametrize("cfg", [0, 2, 5])
 def test_after_the_oracle_walk_at_workload_shape(cfg):
     """The path the oracle's acceptance walk takes on the workload's synthetic
     logits, committed into a cache of the workload's shape (for the 8K

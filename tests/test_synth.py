@@ -27,8 +27,10 @@ def test_configs_shapes():
         assert all(0 <= inp.parents[b, j] < j for b in range(spec.batch) for j in range(1, T))
         assert inp.q.shape == (spec.batch, T, spec.q_heads, spec.head_dim)
         assert inp.kv_indptr[-1] == sum(spec.prefix_lens) + spec.batch * T
-        if i in (1, 2, 4):
+        if i in (1, 2, 4, 5):
             assert T == 61
+        if i == 5:
+            assert spec.batch == 32 and min(spec.prefix_lens) >= 512 and max(spec.prefix_lens) <= 4096
         if i == 0:
             assert T == 11 and list(inp.parents[0, :5]) == [-1, 0, 0, 0, 0]
 
