@@ -218,7 +218,20 @@ struct MinI {
 struct TreeInfo {
   int32_t par[kMaxTree];
   int32_t ok;
+  int32_t nreal;   // rows before the padding suffix (token -1): the tree proper
 };
+
+// Padding rows (token -1 at a row >= 1) let trees of different sizes share a
+// batch; they must form a suffix of the rows.  Returns the number of rows
+// before it, or -1 when the padding rows are not a suffix.  Called by a whole
+// wave with `pad` set for the padding rows among lanes 0 .. T-1.
+__device__ __forceinline__ int real_rows(bool pad, int T) {
+  const uint64_t pm = __ballot(pad);
+  if (pm == 0ull) return T;
+  const int nreal = __builtin_ctzll(pm);   // <= 63 here
+  const uint64_t rows = T >= 64 ? ~0ull : ((1ull << T) - 1ull);
+  return pm == (rows & ~((1ull << nreal) - 1ull)) ? nreal : -1;
+}
 
 // Load the parent array of sequence b into LDS and validate it (all threads).
 __device__ void load_tree(const AcceptKernelArgs& a, int b, TreeInfo& ti) {
@@ -226,34 +239,40 @@ __device__ void load_tree(const AcceptKernelArgs& a, int b, TreeInfo& ti) {
   const int T = a.T;
   if (tid < 64) {
     int p = 0;
-    bool good = true;
+    bool good = true, pad = false;
     if (tid < T) {
       p = a.parents[b * T + tid];
       good = (tid == 0) ? (p == -1) : (p >= 0 && p < tid);
+      pad = tid >= 1 && a.tokens[b * T + tid] == -1;
     }
     ti.par[tid] = p;
-    const bool all_good = !__any(!good);
-    if (tid == 0) ti.ok = all_good ? 1 : 0;
+    const int nreal = real_rows(pad, T);
+    const bool all_good = !__any(!good) && nreal >= 1;
+    if (tid == 0) {
+      ti.ok = all_good ? 1 : 0;
+      ti.nreal = nreal;
+    }
   }
   __syncthreads();
 }
 
+// children are rows of the tree proper (padding rows are never children)
 __device__ __forceinline__ bool has_children(const TreeInfo& ti, int T, int n) {
-  for (int c = n + 1; c < T; ++c)
+  for (int c = n + 1; c < min(T, ti.nreal); ++c)
     if (ti.par[c] == n) return true;
   return false;
 }
 
 // k-th child (ascending) of n, or -1
 __device__ __forceinline__ int kth_child(const TreeInfo& ti, int T, int n, int k) {
-  for (int c = n + 1; c < T; ++c)
+  for (int c = n + 1; c < min(T, ti.nreal); ++c)
     if (ti.par[c] == n && k-- == 0) return c;
   return -1;
 }
 
 __device__ __forceinline__ int num_children(const TreeInfo& ti, int T, int n) {
   int k = 0;
-  for (int c = n + 1; c < T; ++c) k += (ti.par[c] == n);
+  for (int c = n + 1; c < min(T, ti.nreal); ++c) k += (ti.par[c] == n);
   return k;
 }
 
@@ -397,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void sa_stats(const AcceptKernelArgs a) {
   if (greedy && row == 1) return;
 
   load_tree(a, b, ti);
-  if (!ti.ok) return;
+  if (!ti.ok || n >= ti.nreal) return;   // padding rows are not read
   const bool kids = has_children(ti, T, n);
   if (row == 1 && !kids) return;
   const uint32_t expected = static_cast<uint32_t>(NC) * ((!greedy && kids) ? 2u : 1u);
@@ -481,7 +500,7 @@ __global__ __launch_bounds__(kThreads) void sa_stats(const AcceptKernelArgs a) {
       st.kind = kNodeRejected;
     } else if (greedy) {
       st.kind = kNodeRejected;
-      for (int ch = n + 1; ch < T; ++ch) {
+      for (int ch = n + 1; ch < ti.nreal; ++ch) {
         if (ti.par[ch] == n && a.tokens[b * T + ch] == st.argmax) {
           st.kind = kNodeAccepted;
           st.outcome = ch;
@@ -528,11 +547,12 @@ __global__ __launch_bounds__(kThreads) void sa_pass(const AcceptKernelArgs a) {
   const int b = blockIdx.x / (NC * T);
   NodeState st = a.nodes[b * T + n];
   if (st.kind != kNodeNeedsPass) return;
+  load_tree(a, b, ti);
+  if (n >= ti.nreal) return;   // a padding row's state is left over from an earlier call
   const int v0 = c * kVocabChunk, v1 = min(a.V, v0 + kVocabChunk);
   const double part = residual_mass<TL>(a, b, n, st, st.C, v0, v1, dscr);
   if (threadIdx.x == 0) a.fpart[static_cast<int64_t>(b * T + n) * NC + c] = part;
   if (!arrive_last(&a.cnt_pass[b * T + n], static_cast<uint32_t>(NC), &last_flag)) return;
-  load_tree(a, b, ti);
   double s = 0.0;
   for (int q = 0; q < NC; ++q) s += a.fpart[static_cast<int64_t>(b * T + n) * NC + q];
   continue_siblings<TL>(a, b, n, ti, st, st.next_child, st.C, s, dscr, iscr);
@@ -575,7 +595,7 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
   uint32_t bad = ti.ok ? 0u : EAGLE_FLAG_BAD_TREE;
   if (!bad) {
     uint32_t tb = 0, nf = 0;
-    if (tid < T) {
+    if (tid < ti.nreal) {
       if (tid >= 1) {
         const int tok = a.tokens[b * T + tid];
         if (tok < 0 || tok >= a.V) tb = EAGLE_FLAG_BAD_TOKEN;
@@ -1087,12 +1107,14 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   if (lane >= T) par = 0;
   if (lane < 1 || lane >= T) tok = 0;
   const bool good = lane >= T || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
-  if (__any(!good)) {
+  const int Tr = real_rows(tok == -1, T);   // rows of the tree proper; -1: padding not a suffix
+  if (__any(!good) || Tr < 1) {
     if (n == 0 && c == 0) write_poison(a, b, EAGLE_FLAG_BAD_TREE);
     return;
   }
-  const bool tb = lane >= 1 && lane < T && (tok < 0 || tok >= V);
-  const bool is_child = lane >= 1 && lane < T && par == n;
+  if (n >= Tr) return;   // a padding row: nothing reads or waits for it
+  const bool tb = lane >= 1 && lane < Tr && (tok < 0 || tok >= V);
+  const bool is_child = lane >= 1 && lane < Tr && par == n;
   const uint64_t kids_mask = __ballot(is_child);
   const int nkids = __popcll(kids_mask);
   // a token outside the vocabulary poisons the sequence too, but the row
@@ -1372,7 +1394,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     }
     __syncthreads();
     if (tid < 64) {   // lane j waits for node j's first publication
-      bool seen = tid >= T;
+      bool seen = tid >= Tr;
       for (uint32_t it = 0;; ++it) {
         if (!seen) {
           const uint64_t w = poll(pubs + tid);
@@ -1437,7 +1459,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // values do not matter.
   uint64_t* const mw = reinterpret_cast<uint64_t*>(a.spart) + static_cast<int64_t>(b * T + n) * NC * 4;
   if (tid < 64) {
-    const int st0 = tid < T ? walk_state(poll(pubs + tid), false) : 1;
+    const int st0 = tid < Tr ? walk_state(poll(pubs + tid), false) : 1;
     const bool out = __any(st0 == 2);
     if (tid == 0) sh.iscr[1] = out ? 1 : 0;
   }
@@ -1577,7 +1599,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // ---- is this node where the walk ends?  The wave gives up as soon as one
   // word rules this node out.
   if (tid < 64) {
-    int state = tid < T ? 0 : 1;
+    int state = tid < Tr ? 0 : 1;
     bool on = false, fine = true;
     for (uint32_t it = 0;; ++it) {
       if (state == 0) state = walk_state(poll(pubs + tid), true);

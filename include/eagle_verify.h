@@ -68,7 +68,7 @@ typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
 /* Per-sequence `flags` bits.  Bits 0-2 and 5 poison the sequence's outputs;
  * bits 3-4 report events on the accepted walk (outputs stay valid). */
 #define EAGLE_FLAG_BAD_TREE 1u          /* parents[b,0] != -1 or !(0 <= parents[b,i] < i) */
-#define EAGLE_FLAG_BAD_TOKEN 2u         /* tokens[b,i] outside [0, V) for some i >= 1     */
+#define EAGLE_FLAG_BAD_TOKEN 2u         /* tokens[b,i] outside [0, V), i >= 1, not padding */
 #define EAGLE_FLAG_NONFINITE 4u         /* a target row, or a draft row of a node with
                                            children, holds NaN/+inf or is all -inf      */
 #define EAGLE_FLAG_P_ZERO 8u            /* a tested child had draft probability 0: it was
@@ -136,6 +136,10 @@ typedef struct {
  *                            not read at all when temperature == 0)
  *   parents [B, T] int32, tokens [B, T] int32 (tokens[b,0] = the already
  *            committed root token, unused)
+ *   Trees of different sizes share a batch by padding: rows i >= 1 whose
+ *   token is -1 are padding.  They must form a suffix of the T rows (else
+ *   EAGLE_FLAG_BAD_TREE), keep a valid parent, are never children and their
+ *   logits rows are never read; the result is that of the tree without them.
  *   temperature  > 0: q = softmax(target/t), p = softmax(draft/t);
  *                == 0: greedy — accept the first child whose token is the
  *                target argmax (lowest id on ties), else emit that argmax.

@@ -40,6 +40,12 @@ padded), flags, near_ties (decisions on the walk whose margin is below 1e-6:
 sample).  A sequence with an invalid tree, an out-of-range token or an
 unusable logits row (NaN, +inf, or all -inf) is flagged and its integer
 outputs are all -1.
+
+Trees of different sizes in one batch (a serving batch) are padded to the
+same row count: rows whose token is -1 are padding.  They must form a suffix
+of the rows (else the tree is invalid), still need a valid parent, are never
+children of anything and their logits rows are never read; the result is the
+one for the tree without them.
 """
 import numpy as np
 
@@ -57,10 +63,20 @@ def _is_number(x) -> bool:
     return isinstance(x, (float, int, np.floating))
 
 
-def tree_children(parents):
+def real_rows(tokens, T):
+    """Rows of the tree proper: those before the first padding row (token -1
+    at a row >= 1).  Padding lets trees of different sizes share a batch."""
+    for i in range(1, T):
+        if int(tokens[i]) == -1:
+            return i
+    return T
+
+
+def tree_children(parents, nreal=None):
     T = len(parents)
+    nreal = T if nreal is None else nreal
     kids = [[] for _ in range(T)]
-    for c in range(1, T):
+    for c in range(1, nreal):
         kids[int(parents[c])].append(c)
     return kids
 
@@ -113,7 +129,7 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw):
     draw(node, slot) returns the uniform for that decision.
     Returns (path, final_token, flags, near_ties).
     """
-    kids = tree_children(parents)
+    kids = tree_children(parents, real_rows(tokens, len(parents)))
     flags = 0
     near = 0
     path = []
@@ -157,7 +173,7 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw):
 
 
 def walk_greedy(target_rows, parents, tokens):
-    kids = tree_children(parents)
+    kids = tree_children(parents, real_rows(tokens, len(parents)))
     path = []
     cur = 0
     while True:
@@ -175,11 +191,14 @@ def validate_sequence(target, draft, parents, tokens, tau) -> int:
     if not (len(parents) == T and int(parents[0]) == -1
             and all(0 <= int(parents[i]) < i for i in range(1, T))):
         return FLAG_BAD_TREE
+    nreal = real_rows(tokens, T)
+    if any(int(tokens[c]) != -1 for c in range(nreal, T)):   # padding must be a suffix
+        return FLAG_BAD_TREE
     flags = 0
-    if any(not (0 <= int(tokens[c]) < V) for c in range(1, T)):
+    if any(not (0 <= int(tokens[c]) < V) for c in range(1, nreal)):
         flags |= FLAG_BAD_TOKEN
-    kids = tree_children(parents)
-    for n in range(T):
+    kids = tree_children(parents, nreal)
+    for n in range(nreal):                # padding rows are never read
         if not row_is_usable(target[n]):
             flags |= FLAG_NONFINITE
         if tau > 0 and kids[n] and not row_is_usable(draft[n]):

@@ -200,9 +200,10 @@ def test_chain_closed_form_on_gpu():
     ver.close()
 
 
-def test_large_batch_takes_the_general_path():
+def test_large_batch_in_fused_slices():
     """B*T*chunks beyond what the fused kernel can keep co-resident: the
-    three-kernel path must give the same answers."""
+    batch is verified in slices of whole sequences (the uniforms keep the
+    sequence's index in the whole batch)."""
     spec = small_spec("large_batch", B=40, V=32000, levels=(10,) * 6, sigma_d=1.2)
     log(f"[accept] {spec.name}")
     inp = synth.make_inputs(spec, with_kv=False)
@@ -232,4 +233,56 @@ def test_mixed_invalid_inputs_report_every_flag():
     ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
     assert got["flags"].tolist() == ref["flags"].tolist() == [0, ev.FLAG_BAD_TOKEN | ev.FLAG_NONFINITE]
     compare_accept(got, ref, "mixed")
+    ver.close()
+
+
+def _pad(spec, inp, sizes):
+    """Trees of different sizes in one batch: rows past sizes[b] become padding
+    (token -1, parent 0, NaN logits that must never be read)."""
+    par, tok = inp.parents.copy(), inp.tokens.copy()
+    tgt, drf = inp.target.copy(), inp.draft.copy()
+    nan = np.uint16(0x7FC0) if spec.ldtype == "bf16" else np.float32(np.nan)
+    for b, n in enumerate(sizes):
+        tok[b, n:] = -1
+        par[b, n:] = 0
+        tgt[b, n:] = nan
+        drf[b, n:] = nan
+    return par, tok, tgt, drf
+
+
+@pytest.mark.parametrize("temp", [1.0, 0.0])
+def test_trees_of_different_sizes_in_one_batch(temp):
+    spec = small_spec("padded", B=6, V=3000, levels=(10, 10, 10))
+    log(f"[accept] trees of different sizes, temperature {temp}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    sizes = [inp.T, 20, 9, 4, 2, 1]
+    par, tok, tgt, drf = _pad(spec, inp, sizes)
+    ver = make_verifier(spec, inp.T)
+    for off in range(4):
+        got = run_accept(ver, inp, temp, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok)
+        ref = oacc.spec_accept(synth.inputs.as_f64(tgt, spec.ldtype), None if temp == 0 else synth.inputs.as_f64(drf, spec.ldtype),
+                               par, tok, temp, SEED, off)
+        assert (ref["flags"] & 7).tolist() == [0] * spec.batch
+        compare_accept(got, ref, f"padded offset {off}")
+        for b, n in enumerate(sizes):
+            assert got["accept_len"][b] < n
+    ver.close()
+
+
+def test_general_path_with_padded_trees():
+    """One sequence needs more workgroups than the fused kernel can keep
+    resident (61 rows x 64 vocabulary chunks): the three-kernel path, with
+    trees of different sizes."""
+    spec = small_spec("general", B=2, V=520000, levels=(10,) * 6, sigma_d=1.2)
+    log(f"[accept] {spec.name}: three-kernel path, V {spec.vocab}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    sizes = [inp.T, 23]
+    par, tok, tgt, drf = _pad(spec, inp, sizes)
+    ver = make_verifier(spec, inp.T)
+    for temp in (1.0, 0.0):
+        for off in range(2):
+            got = run_accept(ver, inp, temp, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok)
+            ref = oacc.spec_accept(synth.inputs.as_f64(tgt, spec.ldtype),
+                                   None if temp == 0 else synth.inputs.as_f64(drf, spec.ldtype), par, tok, temp, SEED, off)
+            compare_accept(got, ref, f"general temperature {temp} offset {off}")
     ver.close()

@@ -420,3 +420,49 @@ def test_residual_closed_form_matches_iteration():
             q_res = nxt / z
             C = C + s
             s = np.maximum(0.0, q - C * p).sum()
+
+
+def _random_tree(rng, T):
+    return np.asarray([-1] + [int(rng.integers(0, i)) for i in range(1, T)], dtype=np.int32)
+
+
+@pytest.mark.parametrize("temperature", [1.0, 0.0])
+def test_padding_rows_give_the_truncated_trees_result(temperature):
+    """Trees of different sizes in one batch: padding a tree with rows of
+    token -1 (NaN logits, never read) gives, sequence by sequence, exactly
+    the result of the tree without them (run with no padding at all and the
+    same uniforms)."""
+    rng = np.random.default_rng(41 + int(temperature))
+    B, T, V = 6, 12, 40
+    sizes = [12, 7, 3, 1, 2, 11]
+    par = np.stack([_random_tree(rng, T) for _ in range(B)])
+    tok = rng.integers(0, V, size=(B, T)).astype(np.int32)
+    tgt = rng.standard_normal((B, T, V)) * 2
+    drf = tgt + rng.standard_normal((B, T, V)) * 0.8
+    par_p, tok_p, tgt_p, drf_p = par.copy(), tok.copy(), tgt.copy(), drf.copy()
+    for b, n in enumerate(sizes):
+        tok_p[b, n:] = -1
+        par_p[b, n:] = 0
+        tgt_p[b, n:] = np.nan
+        drf_p[b, n:] = np.nan
+    seed, off = 0x5EED0009, 3
+    padded = oacc.spec_accept(tgt_p, None if temperature == 0 else drf_p, par_p, tok_p, temperature, seed, off)
+    for b, n in enumerate(sizes):
+        alone = oacc.spec_accept(tgt[b:b + 1, :n], None if temperature == 0 else drf[b:b + 1, :n],
+                                 par[b:b + 1, :n], tok[b:b + 1, :n], temperature, seed, off,
+                                 draw=lambda _bb, node, slot, _b=b: philox.uniform(seed, off, _b, node, slot))
+        assert padded["accept_len"][b] == alone["accept_len"][0]
+        assert padded["flags"][b] == alone["flags"][0] and padded["near_ties"][b] == alone["near_ties"][0]
+        for key in ("accepted_nodes", "out_tokens"):
+            assert padded[key][b, :n].tolist() == alone[key][0].tolist()
+            assert (padded[key][b, n:] == -1).all()
+
+
+def test_padding_must_be_a_suffix():
+    rng = np.random.default_rng(43)
+    T, V = 6, 20
+    par = _random_tree(rng, T)[None]
+    tok = np.array([[0, 3, -1, 4, -1, -1]], dtype=np.int32)   # a real row after a padding row
+    tgt = rng.standard_normal((1, T, V))
+    out = oacc.spec_accept(tgt, tgt, par, tok, 1.0, 1, 0)
+    assert out["flags"].tolist() == [oacc.FLAG_BAD_TREE] and out["accept_len"].tolist() == [-1]
