@@ -35,7 +35,8 @@ class TreeAttentionArgs(C.Structure):
                 ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
                 ("kv_indptr", C.c_void_p), ("prefix_lens_host", C.POINTER(C.c_int32)),
                 ("parents", C.c_void_p), ("sm_scale", C.c_float), ("out", C.c_void_p),
-                ("flags", C.c_void_p)]
+                ("flags", C.c_void_p), ("page_table", C.c_void_p), ("page_size", C.c_int32),
+                ("pages_per_seq", C.c_int32)]
 
 
 class SpecAcceptArgs(C.Structure):
@@ -52,7 +53,8 @@ class KvCommitArgs(C.Structure):
                 ("k", C.c_void_p), ("v", C.c_void_p), ("kv_indptr", C.c_void_p),
                 ("prefix_lens_host", C.POINTER(C.c_int32)), ("accept_len", C.c_void_p),
                 ("accepted_nodes", C.c_void_p), ("new_lens", C.c_void_p), ("flags", C.c_void_p),
-                ("num_layers", C.c_int32), ("layer_stride", C.c_int64)]
+                ("num_layers", C.c_int32), ("layer_stride", C.c_int64),
+                ("page_table", C.c_void_p), ("page_size", C.c_int32), ("pages_per_seq", C.c_int32)]
 
 
 class TreeExpandArgs(C.Structure):

@@ -205,6 +205,10 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
   k.nwg = static_cast<int>(plan.workgroups);
   k.late_priority = plan.late_priority;
   k.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  k.page_table = a->page_size ? a->page_table : nullptr;
+  k.page_size = a->page_size;
+  k.pps = a->pages_per_seq;
+  k.num_pages = a->page_size ? a->num_kv_rows / a->page_size : 0;
   for (int b = 0; b < a->batch; ++b) {
     k.L[b] = a->prefix_lens_host[b];
     k.split_base[b] = plan.split_base[b];
@@ -368,6 +372,10 @@ eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args*
   k.D = h->desc.head_dim;
   k.layers = a->num_layers;
   k.layer_stride = a->layer_stride;
+  k.page_table = a->page_size ? a->page_table : nullptr;
+  k.page_size = a->page_size;
+  k.pps = a->pages_per_seq;
+  k.num_pages = a->page_size ? a->num_kv_rows / a->page_size : 0;
   for (int b = 0; b < a->batch; ++b) k.L[b] = a->prefix_lens_host[b];
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int e = ev::launch_kv_commit(k, h->desc.kv_dtype == EAGLE_BF16, stream);

@@ -68,13 +68,39 @@ __device__ __forceinline__ int find_seq(const AttnKernelArgs& a, int split) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// ---- paged K/V: sequence b's logical row x lives in page
+// page_table[b * pps + x / page_size]; an entry outside the array reads page
+// 0 instead (the sequence is flagged by paged_range_ok and poisoned)
+__device__ __forceinline__ int64_t page_of(const AttnKernelArgs& a, int b, int64_t x) {
+  const int64_t pg = a.page_table[static_cast<int64_t>(b) * a.pps + x / a.page_size];
+  return (pg >= 0 && pg < a.num_pages) ? pg : 0;
+}
+__device__ __forceinline__ int64_t paged_row(const AttnKernelArgs& a, int b, int64_t x) {
+  return page_of(a, b, x) * a.page_size + x % a.page_size;
+}
+// every page of sequence b (its L_b + T rows) lies inside the array (all
+// lanes of the wave return the same answer)
+__device__ __forceinline__ bool paged_range_ok(const AttnKernelArgs& a, int b, int lane) {
+  const int64_t np = (static_cast<int64_t>(a.L[b]) + a.T + a.page_size - 1) / a.page_size;
+  bool ok = true;
+  for (int64_t j = lane; j < np; j += 64) {
+    const int64_t pg = a.page_table[static_cast<int64_t>(b) * a.pps + j];
+    ok = ok && pg >= 0 && pg < a.num_pages;
+  }
+  return !__any(!ok);
+}
+
 // Flags of sequence b from values already loaded: p = parents[b][lane] (lane
-// < T), kv0/kv1 = kv_indptr[b], kv_indptr[b + 1].  All lanes of the wave
-// return the same word.
+// < T), kv0/kv1 = kv_indptr[b], kv_indptr[b + 1] (contiguous K/V).  All lanes
+// of the wave return the same word.
 __device__ __forceinline__ uint32_t seq_flags(const AttnKernelArgs& a, int b, int lane, int p, int64_t kv0, int64_t kv1) {
   const bool ok = lane >= a.T || ((lane == 0) ? (p == -1) : (p >= 0 && p < lane));
   uint32_t bad = __any(!ok) ? EAGLE_FLAG_BAD_TREE : 0u;
-  if (!(kv0 >= 0 && kv1 <= a.num_kv_rows && kv1 - kv0 >= (int64_t)a.L[b] + a.T)) bad |= EAGLE_FLAG_BAD_KV_RANGE;
+  if (a.page_size) {
+    if (!paged_range_ok(a, b, lane)) bad |= EAGLE_FLAG_BAD_KV_RANGE;
+  } else if (!(kv0 >= 0 && kv1 <= a.num_kv_rows && kv1 - kv0 >= (int64_t)a.L[b] + a.T)) {
+    bad |= EAGLE_FLAG_BAD_KV_RANGE;
+  }
   return bad;
 }
 
@@ -90,6 +116,10 @@ __device__ __forceinline__ uint32_t validate_seq(const AttnKernelArgs& a, int b,
   }
   if (par_out && lane < 64) par_out[lane] = p;
   uint32_t bad = __any(!ok) ? EAGLE_FLAG_BAD_TREE : 0u;
+  if (a.page_size) {
+    if (!paged_range_ok(a, b, lane)) bad |= EAGLE_FLAG_BAD_KV_RANGE;
+    return bad;
+  }
   const int64_t kv0 = a.kv_indptr[b], kv1 = a.kv_indptr[b + 1];
   if (!(kv0 >= 0 && kv1 <= a.num_kv_rows && kv1 - kv0 >= (int64_t)a.L[b] + T)) bad |= EAGLE_FLAG_BAD_KV_RANGE;
   return bad;
@@ -236,8 +266,9 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   // sequence, without waiting for kv_indptr[b]; the parent array is requested
   // before it, and nothing waits on either until the tile has landed.
   const int par_lane = lane < T ? a_par[b * T + lane] : 0;
+  const bool paged = a.page_size != 0;
   const int guess = b == 0 ? b0_guess : a.kv0_guess[b];
-  int64_t kv0 = guess >= 0 ? (int64_t)guess : a.kv_indptr[b];
+  int64_t kv0 = paged ? 0 : (guess >= 0 ? (int64_t)guess : a.kv_indptr[b]);
   const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a_k) + (int64_t)hk * D;
   const uint16_t* __restrict__ vbase = reinterpret_cast<const uint16_t*>(a_v) + (int64_t)hk * D;
   const int64_t row_stride = (int64_t)a.Hkv * D;   // elements between consecutive KV rows
@@ -268,12 +299,26 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   }
   // every prefix row of this split lies inside the KV array (checked once, so
   // full tiles need no per-row clamping)
-  bool split_in_bounds = kv0 >= 0 && kv0 + k_end <= a.num_kv_rows;
+  bool split_in_bounds = paged || (kv0 >= 0 && kv0 + k_end <= a.num_kv_rows);
+  // paged K/V: lane j holds the page of this split's j-th page (a full tile
+  // lies inside one page: tiles start at multiples of 64 and pages hold a
+  // multiple of 64 rows)
+  const int first_page = paged ? k_begin / a.page_size : 0;
+  const int64_t my_page = (paged && static_cast<int64_t>(first_page + lane) * a.page_size < (int64_t)L + T)
+                              ? page_of(a, b, static_cast<int64_t>(first_page + lane) * a.page_size)
+                              : 0;
   auto issue = [&](int t) {
     const uint32_t kdst = lds_kv + static_cast<uint32_t>((t % NST) * 2 * TILE * 2);
     const uint32_t vdst = kdst + TILE * 2;
     if (t < n_full && split_in_bounds) {
-      const int64_t row0 = kv0 + k_begin + (int64_t)t * kTileKeys;
+      int64_t row0 = kv0 + k_begin + (int64_t)t * kTileKeys;
+      if (paged) {
+        const int x = k_begin + t * kTileKeys;
+        const int pi = x / a.page_size - first_page;
+        const int64_t pg = pi < 64 ? (int64_t)__builtin_amdgcn_readlane(static_cast<int>(my_page), pi)
+                                   : page_of(a, b, x);
+        row0 = pg * a.page_size + x % a.page_size;
+      }
       const void* kt = uniform_ptr(kbase + row0 * row_stride);
       const void* vt = uniform_ptr(vbase + row0 * row_stride);
 #pragma unroll
@@ -292,7 +337,8 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
     for (int j = 0; j < IPW; ++j) {
       const int r0 = (wave_u * IPW + j) * RPI;
       const int r = r0 + l_row;
-      const int64_t gr = min(max(row0 + min(r, cnt - 1), (int64_t)0), last_row);
+      const int64_t gr = paged ? paged_row(a, b, start + min(r, cnt - 1))
+                               : min(max(row0 + min(r, cnt - 1), (int64_t)0), last_row);
       lds_dma16(kbase + gr * row_stride + (l_pos ^ swz_k<D>(r)) * 8, kdst + static_cast<uint32_t>(r0 * D * 2));
       lds_dma16(vbase + gr * row_stride + (l_pos ^ swz_v<D>(r)) * 8, vdst + static_cast<uint32_t>(r0 * D * 2));
     }
@@ -321,8 +367,8 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
     }
   }
 
-  const int64_t kv0_true = a.kv_indptr[b];
-  const int64_t kv1_true = a.kv_indptr[b + 1];
+  const int64_t kv0_true = paged ? 0 : a.kv_indptr[b];
+  const int64_t kv1_true = paged ? 0 : a.kv_indptr[b + 1];
   wait_vmcnt<0>();   // the first tile, the parents and the query rows have landed
   if (kv0 != kv0_true) {   // the expected offset was wrong: request the first tile again
     kv0 = kv0_true;
@@ -854,7 +900,9 @@ __global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
 
   const TIn* kb = reinterpret_cast<const TIn*>(a.k);
   const TIn* vb = reinterpret_cast<const TIn*>(a.v);
-  const int64_t kv0 = a.kv_indptr[b];
+  const bool paged = a.page_size != 0;
+  const int64_t kv0 = paged ? 0 : a.kv_indptr[b];
+  __shared__ int64_t prow[kTileKeys];   // physical rows of the tile's keys (paged K/V)
   const int k_begin = s_local * a.chunk;
   const int k_end = min(k_begin + a.chunk, L);
   const int n_prefix_tiles = k_end > k_begin ? (k_end - k_begin + kTileKeys - 1) / kTileKeys : 0;
@@ -869,10 +917,13 @@ __global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
     const int start = is_tree ? L : k_begin + t * kTileKeys;
     const int cnt = is_tree ? T : min(kTileKeys, k_end - start);
     const int64_t row0 = kv0 + start;
+    __syncthreads();   // the previous tile's rows are no longer read
+    if (lane < kTileKeys) prow[lane] = paged ? paged_row(a, b, start + min(lane, cnt - 1)) : row0 + lane;
+    __syncthreads();
     float s = kNegInf;
     const bool valid = lane < cnt && (!is_tree || ((anc >> lane) & 1ull));
     if (valid) {
-      const TIn* kr = kb + ((row0 + lane) * Hkv + hk) * D;
+      const TIn* kr = kb + (prow[lane] * Hkv + hk) * D;
       float dot = 0.f;
       for (int d = 0; d < D; ++d) dot = __builtin_fmaf(q_lds[d], load_elem<TIn>(kr, d), dot);
       s = dot;
@@ -892,7 +943,7 @@ __global__ __launch_bounds__(64) void tree_attn_fma(const AttnKernelArgs a) {
     __syncthreads();
     for (int e = 0; e < DPL; ++e) {
       float sum = 0.f;
-      for (int k = 0; k < cnt; ++k) sum = __builtin_fmaf(p_lds[k], load_elem<TIn>(vb, ((row0 + k) * Hkv + hk) * D + lane + 64 * e), sum);
+      for (int k = 0; k < cnt; ++k) sum = __builtin_fmaf(p_lds[k], load_elem<TIn>(vb, (prow[k] * Hkv + hk) * D + lane + 64 * e), sum);
       acc[e] = acc[e] * alpha + sum;
     }
   }

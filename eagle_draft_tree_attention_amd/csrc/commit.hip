@@ -8,7 +8,8 @@
 // are left where they are (rolled back by the length alone).  The accepted
 // nodes of a tree are not contiguous, so their rows are compacted in place:
 // row L_b + i receives row L_b + path_i, path_0 = 0 (the root),
-// path_i = accepted_nodes[b, i - 1], i = 0 .. accept_len[b].
+// path_i = accepted_nodes[b, i - 1], i = 0 .. accept_len[b].  With paged K/V
+// these are the sequence's logical rows, mapped through its page table.
 //
 // GPU formulation.  One workgroup per (layer, sequence, KV head) owns that
 // head's slice (D elements of K and of V) of every row of the sequence in
@@ -45,9 +46,21 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
   const int b = (blockIdx.x / a.Hkv) % a.B, h = blockIdx.x % a.Hkv;
   const int T = a.T, L = a.L[b];
 
+  const bool paged = a.page_size != 0;
   if (tid < 64) {
-    const int64_t lo = a.kv_indptr[b], hi = a.kv_indptr[b + 1];
-    const bool range_ok = lo >= 0 && lo + L + T <= hi && hi <= a.num_kv_rows;
+    bool range_ok;
+    if (paged) {   // every page of the sequence's L + T rows lies inside the array
+      const int64_t np = (static_cast<int64_t>(L) + T + a.page_size - 1) / a.page_size;
+      bool ok = true;
+      for (int64_t j = tid; j < np; j += 64) {
+        const int64_t pg = a.page_table[static_cast<int64_t>(b) * a.pps + j];
+        ok = ok && pg >= 0 && pg < a.num_pages;
+      }
+      range_ok = !__any(!ok);
+    } else {
+      const int64_t lo = a.kv_indptr[b], hi = a.kv_indptr[b + 1];
+      range_ok = lo >= 0 && lo + L + T <= hi && hi <= a.num_kv_rows;
+    }
     const int n = a.accept_len[b];
     const int nn = n < 0 ? 0 : n;
     // lane i holds path_i (i <= nn), -1 past the path
@@ -75,8 +88,14 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
   const int nmove = nmove_sh;
   if (nmove == 0) return;
 
+  // physical row of the sequence's logical row x (validated above)
+  const int64_t base = paged ? 0 : a.kv_indptr[b];
+  auto phys = [&](int64_t x) -> int64_t {
+    if (!paged) return base + x;
+    return static_cast<int64_t>(a.page_table[static_cast<int64_t>(b) * a.pps + x / a.page_size]) * a.page_size +
+           x % a.page_size;
+  };
   // slice of row r for this head, as 16-byte vectors
-  const int64_t base = a.kv_indptr[b] + L;
   const int64_t rowstride = static_cast<int64_t>(a.Hkv) * VPR;
   const int64_t loff = static_cast<int64_t>(layer) * (a.layer_stride * static_cast<int64_t>(sizeof(TK)) / 16);
   u32x4_t* const kp = reinterpret_cast<u32x4_t*>(a.k) + loff + static_cast<int64_t>(h) * VPR;
@@ -86,7 +105,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
     const int which = idx / (nmove * VPR);   // 0: K, 1: V
     const int rem = idx - which * nmove * VPR;
     const int j = rem / VPR, c = rem - j * VPR;
-    const int64_t src = (base + path[moved[j]]) * rowstride + c;
+    const int64_t src = phys(L + path[moved[j]]) * rowstride + c;
     stage[idx] = which ? vp[src] : kp[src];
   }
   __syncthreads();   // every source read before any destination is written
@@ -94,7 +113,7 @@ __global__ __launch_bounds__(kCommitThreads) void kv_commit_rows(const CommitKer
     const int which = idx / (nmove * VPR);
     const int rem = idx - which * nmove * VPR;
     const int j = rem / VPR, c = rem - j * VPR;
-    const int64_t dst = (base + moved[j]) * rowstride + c;
+    const int64_t dst = phys(L + moved[j]) * rowstride + c;
     if (which) vp[dst] = stage[idx];
     else kp[dst] = stage[idx];
   }

@@ -63,6 +63,11 @@ struct AttnKernelArgs {
   uint32_t spin_limit; // polls of the bounded wait; an expired wait flags EAGLE_FLAG_INTERNAL
   uint64_t epoch;      // strictly increasing per attention call on a handle (tags use its low 32 bits)
   uint64_t* mlrec;      // [slot][rows_per_tile][2]: m and l (low 32 bits), epoch tag (high 32 bits)
+  // paged K/V (page_size > 0): logical row x of sequence b is physical row
+  // page_table[b * pps + x / page_size] * page_size + x % page_size
+  const int32_t* page_table;
+  int page_size, pps;
+  int64_t num_pages;
   int32_t L[kMaxBatch];
   int32_t split_base[kMaxBatch + 1];
   // expected kv_indptr[b] (rows packed back to back, L_b + T per sequence),
@@ -141,6 +146,9 @@ struct CommitKernelArgs {
   uint32_t* flags;
   int64_t num_kv_rows;
   int64_t layer_stride;   // elements between consecutive layers' k (and v)
+  const int32_t* page_table;   // paged K/V (page_size > 0), as for attention
+  int page_size, pps;
+  int64_t num_pages;
   int B, T, Hkv, D, layers;
   int32_t L[kMaxBatch];
 };

@@ -59,6 +59,31 @@ eagle_status check_desc(const eagle_verify_desc* d, char* err, size_t errlen) {
   return EAGLE_OK;
 }
 
+// Paged K/V layout (page_size > 0): page size a multiple of 64 dividing the
+// row count, and a table row long enough for every sequence's L_b + T rows.
+static eagle_status check_paging(const int32_t* table, int32_t page_size, int32_t pages_per_seq,
+                                 int64_t num_kv_rows, const int32_t* lens, int B, int T, char* err,
+                                 size_t errlen) {
+  if (page_size == 0) return EAGLE_OK;
+  if (page_size < 0 || page_size % 64 != 0 || page_size > (1 << 20))
+    return fail(EAGLE_ERR_ARG, err, errlen, "page_size=%d: 0 or a multiple of 64 up to 2^20", page_size);
+  if (!table) return fail(EAGLE_ERR_ARG, err, errlen, "page_table is NULL with page_size > 0");
+  if (!aligned(table, 4)) return fail(EAGLE_ERR_ARG, err, errlen, "page_table misaligned");
+  if (num_kv_rows % page_size != 0)
+    return fail(EAGLE_ERR_ARG, err, errlen, "num_kv_rows=%lld not a multiple of page_size=%d",
+                static_cast<long long>(num_kv_rows), page_size);
+  if (pages_per_seq < 1) return fail(EAGLE_ERR_ARG, err, errlen, "pages_per_seq=%d < 1", pages_per_seq);
+  if (static_cast<int64_t>(B) * pages_per_seq > INT32_MAX)
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "batch * pages_per_seq above 2^31 - 1");
+  for (int b = 0; b < B; ++b) {
+    const int64_t need = (static_cast<int64_t>(lens[b]) + T + page_size - 1) / page_size;
+    if (need > pages_per_seq)
+      return fail(EAGLE_ERR_ARG, err, errlen, "sequence %d needs %lld pages, pages_per_seq=%d", b,
+                  static_cast<long long>(need), pages_per_seq);
+  }
+  return EAGLE_OK;
+}
+
 eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_attention_args* a,
                                  int num_cus, AttnPlan* plan, char* err, size_t errlen) {
   eagle_status st = check_desc(d, err, errlen);
@@ -73,12 +98,13 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
     return fail(EAGLE_ERR_CAPACITY, err, errlen, "tree_rows=%d above max_tree_rows=%d", a->tree_rows,
                 d->max_tree_rows);
   if (a->num_kv_rows < 0) return fail(EAGLE_ERR_ARG, err, errlen, "num_kv_rows < 0");
-  if (!a->q || !a->k || !a->v || !a->kv_indptr || !a->prefix_lens_host || !a->parents || !a->out ||
+  const bool paged = a->page_size != 0;
+  if (!a->q || !a->k || !a->v || (!paged && !a->kv_indptr) || !a->prefix_lens_host || !a->parents || !a->out ||
       !a->flags)
     return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");
   if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->out, 16))
     return fail(EAGLE_ERR_ARG, err, errlen, "q, k, v and out must be 16-byte aligned");
-  if (!aligned(a->kv_indptr, 8) || !aligned(a->parents, 4) || !aligned(a->flags, 4))
+  if ((!paged && !aligned(a->kv_indptr, 8)) || !aligned(a->parents, 4) || !aligned(a->flags, 4))
     return fail(EAGLE_ERR_ARG, err, errlen, "kv_indptr/parents/flags misaligned");
   if (!std::isfinite(a->sm_scale) || a->sm_scale <= 0.f)
     return fail(EAGLE_ERR_ARG, err, errlen, "sm_scale must be finite and > 0");
@@ -94,6 +120,9 @@ eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_at
                   b, static_cast<long long>(L) + T, static_cast<long long>(a->num_kv_rows));
     total_keys += L;
   }
+  st = check_paging(a->page_table, a->page_size, a->pages_per_seq, a->num_kv_rows, a->prefix_lens_host, B, T, err,
+                    errlen);
+  if (st != EAGLE_OK) return st;
 
   std::memset(plan, 0, sizeof(*plan));
   const int R = T * g;
@@ -212,17 +241,21 @@ eagle_status check_kv_commit(const eagle_verify_desc* d, const eagle_kv_commit_a
     return fail(EAGLE_ERR_CAPACITY, err, errlen, "tree_rows=%d above max_tree_rows=%d", a->tree_rows,
                 d->max_tree_rows);
   if (a->num_kv_rows < 0) return fail(EAGLE_ERR_ARG, err, errlen, "num_kv_rows < 0");
-  if (!a->k || !a->v || !a->kv_indptr || !a->prefix_lens_host || !a->accept_len || !a->accepted_nodes ||
+  const bool paged = a->page_size != 0;
+  if (!a->k || !a->v || (!paged && !a->kv_indptr) || !a->prefix_lens_host || !a->accept_len || !a->accepted_nodes ||
       !a->new_lens || !a->flags)
     return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");
   if (!aligned(a->k, 16) || !aligned(a->v, 16))
     return fail(EAGLE_ERR_ARG, err, errlen, "k and v must be 16-byte aligned");
-  if (!aligned(a->kv_indptr, 8) || !aligned(a->accept_len, 4) || !aligned(a->accepted_nodes, 4) ||
+  if ((!paged && !aligned(a->kv_indptr, 8)) || !aligned(a->accept_len, 4) || !aligned(a->accepted_nodes, 4) ||
       !aligned(a->new_lens, 4) || !aligned(a->flags, 4))
     return fail(EAGLE_ERR_ARG, err, errlen, "integer buffers misaligned");
   for (int b = 0; b < a->batch; ++b)
     if (a->prefix_lens_host[b] < 0)
       return fail(EAGLE_ERR_ARG, err, errlen, "prefix_lens_host[%d]=%d < 0", b, a->prefix_lens_host[b]);
+  st = check_paging(a->page_table, a->page_size, a->pages_per_seq, a->num_kv_rows, a->prefix_lens_host, a->batch,
+                    a->tree_rows, err, errlen);
+  if (st != EAGLE_OK) return st;
   if (a->num_layers < 1 || a->num_layers > 4096)
     return fail(EAGLE_ERR_ARG, err, errlen, "num_layers=%d outside [1, 4096]", a->num_layers);
   if (static_cast<int64_t>(a->num_layers) * a->batch * d->num_kv_heads > INT32_MAX)

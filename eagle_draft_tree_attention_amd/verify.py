@@ -111,21 +111,33 @@ def _stream(stream):
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out, flags):
+def _paging(a, page_table, page_size):
+    """page_table: [B, pages_per_seq] int32 device tensor (paged K/V), or None."""
+    if page_table is None:
+        a.page_table, a.page_size, a.pages_per_seq = None, 0, 0
+    else:
+        a.page_table = _ptr(page_table)
+        a.page_size, a.pages_per_seq = int(page_size), int(page_table.shape[1])
+
+
+def tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out, flags, page_table=None,
+                        page_size=0):
     lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32))
     a = TreeAttentionArgs()
     a.batch, a.tree_rows = int(q.shape[0]), int(q.shape[1])
     a.num_kv_rows = int(k.shape[0])
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
-    a.kv_indptr = _ptr(kv_indptr)
+    a.kv_indptr = None if kv_indptr is None else _ptr(kv_indptr)
     a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))
     a.parents = _ptr(parents)
     a.sm_scale = float(sm_scale)
     a.out, a.flags = _ptr(out), _ptr(flags)
+    _paging(a, page_table, page_size)
     return a, lens          # keep lens alive while the call runs
 
 
-def kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags):
+def kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags, page_table=None,
+                   page_size=0):
     """k, v: [rows, Hkv, D] (one layer) or [layers, rows, Hkv, D] (every layer, contiguous)."""
     lens = np.ascontiguousarray(np.asarray(prefix_lens, dtype=np.int32))
     a = KvCommitArgs()
@@ -137,10 +149,11 @@ def kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new
         a.num_layers, a.layer_stride = 1, 0
         a.num_kv_rows = int(k.shape[0])
     a.k, a.v = _ptr(k), _ptr(v)
-    a.kv_indptr = _ptr(kv_indptr)
+    a.kv_indptr = None if kv_indptr is None else _ptr(kv_indptr)
     a.prefix_lens_host = lens.ctypes.data_as(C.POINTER(C.c_int32))
     a.accept_len, a.accepted_nodes = _ptr(accept_len), _ptr(accepted_nodes)
     a.new_lens, a.flags = _ptr(new_lens), _ptr(flags)
+    _paging(a, page_table, page_size)
     return a, lens          # keep lens alive while the call runs
 
 
@@ -165,7 +178,9 @@ class Verifier:
             pass
 
     def tree_attention(self, q, k, v, kv_indptr, prefix_lens, parents, sm_scale=None, out=None,
-                       flags=None, stream=None):
+                       flags=None, stream=None, page_table=None, page_size=0):
+        """kv_indptr [B+1] int64 for contiguous K/V; or page_table [B, pages_per_seq]
+        int32 with page_size rows per page (kv_indptr may be None)."""
         import torch
         B, T, Hq, D = q.shape
         if sm_scale is None:
@@ -174,7 +189,8 @@ class Verifier:
             out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
         if flags is None:
             flags = torch.empty((B,), dtype=torch.int32, device=q.device)
-        a, _keep = tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out, flags)
+        a, _keep = tree_attention_args(q, k, v, kv_indptr, prefix_lens, parents, sm_scale, out, flags,
+                                       page_table, page_size)
         eagle_verify_tree_attention(self.handle, a, _stream(stream))
         return out, flags
 
@@ -209,7 +225,7 @@ class Verifier:
         return outputs
 
     def kv_commit(self, k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens=None, flags=None,
-                  stream=None):
+                  stream=None, page_table=None, page_size=0):
         """Commit the accepted path into k and v in place; returns (new_lens, flags)."""
         import torch
         B = int(accepted_nodes.shape[0])
@@ -217,7 +233,8 @@ class Verifier:
             new_lens = torch.empty((B,), dtype=torch.int32, device=k.device)
         if flags is None:
             flags = torch.empty((B,), dtype=torch.int32, device=k.device)
-        a, _keep = kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags)
+        a, _keep = kv_commit_args(k, v, kv_indptr, prefix_lens, accept_len, accepted_nodes, new_lens, flags,
+                                  page_table, page_size)
         eagle_verify_kv_commit(self.handle, a, _stream(stream))
         return new_lens, flags
 

@@ -108,6 +108,16 @@ typedef struct {
  *             prefix rows and the tree rows of the nodes on the root path of i
  *             (i included); query head h reads KV head h / (Hq/Hkv)
  *   flags     [B] uint32 (device)       EAGLE_FLAG_BAD_TREE | EAGLE_FLAG_BAD_KV_RANGE
+ * Paged K/V (page_size > 0; a serving engine's block tables): k and v hold
+ * num_kv_rows / page_size pages of page_size rows each, and sequence b's
+ * logical row x (its L_b prefix rows, then its T tree rows) is physical row
+ *   page_table[b * pages_per_seq + x / page_size] * page_size + x % page_size.
+ * kv_indptr is then not read (may be NULL).  page_size must be a multiple of
+ * 64 (one 64-key tile never spans two pages) dividing num_kv_rows, and
+ * pages_per_seq >= ceil((L_b + T) / page_size) for every b (EAGLE_ERR_ARG
+ * otherwise); a table entry outside [0, num_kv_rows / page_size) flags the
+ * sequence EAGLE_FLAG_BAD_KV_RANGE (poisoned, nothing read out of bounds).
+ * page_size == 0: the contiguous layout above.
  * Inputs are not modified.  Keys/values are read once from HBM per launch.
  * Long prefixes are split into key chunks whose partial results are merged by
  * log-sum-exp; on the bf16 path the merge runs inside the attention kernel
@@ -127,6 +137,9 @@ typedef struct {
   float sm_scale;
   float* out;
   uint32_t* flags;
+  const int32_t* page_table; /* [B, pages_per_seq] int32 (device), paged K/V only */
+  int32_t page_size;         /* 0: contiguous K/V; else rows per page, a multiple of 64 */
+  int32_t pages_per_seq;     /* row stride of page_table */
 } eagle_tree_attention_args;
 
 /* Multi-round speculative sampling over the vocabulary.
@@ -201,6 +214,9 @@ typedef struct {
  *                    >= num_kv_rows * Hkv * D when num_layers > 1
  * One launch covers every layer.  Every moving row is read before any is
  * written, so a path whose sources and destinations overlap is safe.
+ * Paged K/V (page_size > 0): rows are logical rows of the sequence, mapped
+ * through page_table exactly as for eagle_verify_tree_attention (kv_indptr
+ * not read); the moves happen between the physical rows.
  * Nothing else may touch k or v while the call runs. */
 typedef struct {
   int32_t batch;           /* B <= max_batch            */
@@ -216,6 +232,9 @@ typedef struct {
   uint32_t* flags;
   int32_t num_layers;
   int64_t layer_stride;
+  const int32_t* page_table; /* [B, pages_per_seq] int32 (device), paged K/V only */
+  int32_t page_size;         /* 0: contiguous K/V; else rows per page, a multiple of 64 */
+  int32_t pages_per_seq;
 } eagle_kv_commit_args;
 
 /* One expansion step of a dynamic draft tree (EAGLE notes page, the EAGLE-2

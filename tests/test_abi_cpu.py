@@ -212,3 +212,28 @@ def test_descriptor_errors():
     with pytest.raises(ev.EagleVerifyError) as e:
         ev.eagle_verify_create(_desc(max_batch=0))
     assert e.value.status == ev.EAGLE_ERR_ARG
+
+
+def test_paged_kv_argument_errors():
+    """Paged K/V (page_size > 0): a page size that is not a multiple of 64, a
+    row count it does not divide, a table row too short for a sequence's
+    L + T rows or a missing table are argument errors; kv_indptr may be NULL."""
+    d = _desc()
+    fake = 1 << 20
+    rows = 64 * 200                                      # 8192 + 61 rows need 129 pages of 64
+    ok = dict(page_table=fake, page_size=64, pages_per_seq=129, kv_indptr=None, rows=rows)
+    a, keep = _attn_args(**ok)
+    st, _ = ev.eagle_verify_check_tree_attention(d, a)
+    assert st == ev.EAGLE_OK, ev.eagle_verify_last_error()
+    for over in (dict(page_size=96), dict(page_size=-64), dict(pages_per_seq=128), dict(page_table=None),
+                 dict(rows=rows + 1), dict(page_table=fake + 2)):
+        a, keep = _attn_args(**{**ok, **over})
+        assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_ARG, over
+    a, keep = _attn_args(**{**ok, "page_size": 0})        # contiguous again: kv_indptr is required
+    assert ev.eagle_verify_check_tree_attention(d, a)[0] == ev.EAGLE_ERR_ARG
+    # the KV commit: T = 61 rows behind prefixes 5 and 9 need one page of 128 each
+    a, keep = _kc_args(page_table=fake, page_size=128, pages_per_seq=1, kv_indptr=None)
+    a.num_kv_rows = 128 * 4
+    assert ev.eagle_verify_check_kv_commit(d, a) == ev.EAGLE_OK, ev.eagle_verify_last_error()
+    a.page_size = 64
+    assert ev.eagle_verify_check_kv_commit(d, a) == ev.EAGLE_ERR_ARG
