@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="llama31_8b_8k",
                     help="synthetic workload by name (the headline is llama31_8b_8k; serving_b32 is the "
                          "32-sequence serving batch)")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged K/V: rows per page (a multiple of 64; pages at random slots of one pool); "
+                         "0 = contiguous")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-commit", action="store_true",
                     help="skip timing the calls beside the step (KV commit, tree expansion)")
@@ -182,8 +185,14 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
+    kv_k, kv_v, table = inp.k, inp.v, None
+    if args.page_size:
+        from synth.paging import to_paged
+        kv_k, kv_v, table = to_paged(inp.k, inp.v, inp.kv_indptr, inp.prefix_lens, T, args.page_size,
+                                     np.random.default_rng(spec.seed))
+        table = torch.from_numpy(table).cuda()
     base = {
-        "q": to_dev(inp.q, spec.dtype), "k": to_dev(inp.k, spec.dtype), "v": to_dev(inp.v, spec.dtype),
+        "q": to_dev(inp.q, spec.dtype), "k": to_dev(kv_k, spec.dtype), "v": to_dev(kv_v, spec.dtype),
         "tgt": to_dev(inp.target, spec.ldtype), "drf": to_dev(inp.draft, spec.ldtype),
     }
     sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(args.sets - 1)]
@@ -209,7 +218,7 @@ def main():
     attn_args, acc_args, keep = [], [], []
     for s in sets:
         a, lens = ev.verify.tree_attention_args(s["q"], s["k"], s["v"], indptr, inp.prefix_lens, parents, scale,
-                                                out, aflags)
+                                                out, aflags, table, args.page_size)
         attn_args.append(a)
         keep.append(lens)
         c = ev.SpecAcceptArgs()
@@ -278,7 +287,8 @@ def main():
         new_lens = torch.empty((B,), dtype=torch.int32, device="cuda")
         cflags = torch.empty((B,), dtype=torch.int32, device="cuda")
         ca, ckeep = ev.verify.kv_commit_args(kl, vl, indptr, inp.prefix_lens,
-                                             outs["accept_len"], outs["accepted_nodes"], new_lens, cflags)
+                                             outs["accept_len"], outs["accepted_nodes"], new_lens, cflags,
+                                             table, args.page_size)
         call_commit = ev.verify.eagle_verify_kv_commit
         for _ in range(5):
             call_commit(handle, ca, sptr)
@@ -378,6 +388,7 @@ def main():
             "seq_len": max(spec.prefix_lens),
             "parallelism": "single GPU",
             "input_sets_rotated": args.sets,
+            "kv_layout": f"paged, {args.page_size} rows per page" if args.page_size else "contiguous",
         },
         "hbm_frac_metric_bytes": nb["metric_bytes"] / step_s / (HBM_PEAK_GBS * 1e9),
         "hbm_frac_compulsory_bytes": nb["compulsory_bytes"] / step_s / (HBM_PEAK_GBS * 1e9),

@@ -69,6 +69,8 @@ static eagle_status check_paging(const int32_t* table, int32_t page_size, int32_
     return fail(EAGLE_ERR_ARG, err, errlen, "page_size=%d: 0 or a multiple of 64 up to 2^20", page_size);
   if (!table) return fail(EAGLE_ERR_ARG, err, errlen, "page_table is NULL with page_size > 0");
   if (!aligned(table, 4)) return fail(EAGLE_ERR_ARG, err, errlen, "page_table misaligned");
+  if (num_kv_rows > static_cast<int64_t>(UINT32_MAX))
+    return fail(EAGLE_ERR_CAPACITY, err, errlen, "paged K/V holds more than 2^32 - 1 rows");
   if (num_kv_rows % page_size != 0)
     return fail(EAGLE_ERR_ARG, err, errlen, "num_kv_rows=%lld not a multiple of page_size=%d",
                 static_cast<long long>(num_kv_rows), page_size);
