@@ -122,11 +122,15 @@ def inv_cdf(w, u):
     return v, near
 
 
-def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw):
+def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_replacement=False):
     """Sequential multi-round walk of one tree.
 
     target_rows(n) / draft_rows(n) return node n's logits rows (float64);
     draw(node, slot) returns the uniform for that decision.
+    without_replacement: the siblings were drawn from p_n without
+    replacement, so sibling i is tested against p_n with the tokens of the
+    siblings tried before it removed and the rest renormalised (all zero if
+    nothing is left); the residual update uses that same distribution.
     Returns (path, final_token, flags, near_ties).
     """
     kids = tree_children(parents, real_rows(tokens, len(parents)))
@@ -143,21 +147,29 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw):
         p = softmax_t(draft_rows(cur), tau)
         q_res = q
         accepted = None
+        tried = []
         for i, c in enumerate(kids[cur]):
             r = draw(cur, i)
             t = int(tokens[c])
-            if p[t] == 0.0:
+            p_i = p
+            if without_replacement and tried:
+                p_i = p.copy()
+                p_i[tried] = 0.0
+                left = p_i.sum()
+                p_i = p_i / left if left > 0.0 else np.zeros_like(p)
+            if p_i[t] == 0.0:
                 flags |= FLAG_P_ZERO
                 ok = q_res[t] > 0.0
             else:
-                ratio = q_res[t] / p[t]
+                ratio = q_res[t] / p_i[t]
                 ok = r < ratio
                 if _is_number(r) and abs(r - ratio) < NEAR_TIE:
                     near += 1
             if ok:
                 accepted = c
                 break
-            q_res = np.maximum(0.0, q_res - p)
+            tried.append(t)
+            q_res = np.maximum(0.0, q_res - p_i)
             z = q_res.sum()
             if z == 0.0:
                 flags |= FLAG_DEGENERATE_RESIDUAL
@@ -206,7 +218,7 @@ def validate_sequence(target, draft, parents, tokens, tau) -> int:
     return flags
 
 
-def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=None):
+def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=None, without_replacement=False):
     """Oracle for one verification step over a batch of trees.
 
     target, draft: [B,T,V] float64 logits (draft may be None when
@@ -240,7 +252,7 @@ def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=
                 def u(n, s, _b=b):
                     return draw(_b, n, s)
             path, final, fl, near = walk_sampled(lambda n: target[b, n], lambda n: drf[n],
-                                                 parents[b], tokens[b], tau, u)
+                                                 parents[b], tokens[b], tau, u, without_replacement)
         res["accept_len"][b] = len(path)
         res["accepted_nodes"][b, :len(path)] = path
         res["out_tokens"][b, :len(path)] = [int(tokens[b][c]) for c in path]

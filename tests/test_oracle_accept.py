@@ -120,8 +120,11 @@ def _tables(V, seed, spread=1.5, noise=0.8):
     return rows
 
 
-def _tree_outcomes(parents, V, rows, tau=1.0, want=2):
-    """Exact joint law of the first `want` emitted tokens (None = stopped)."""
+def _tree_outcomes(parents, V, rows, tau=1.0, want=2, without_replacement=False):
+    """Exact joint law of the first `want` emitted tokens (None = stopped).
+    Siblings are i.i.d. draws from the parent's draft distribution, or, with
+    without_replacement, drawn one after the other from it without
+    replacement (and verified by the walk's without-replacement rule)."""
     T = len(parents)
     kids = oacc.tree_children(parents)
     depth_path = {0: ()}
@@ -141,7 +144,7 @@ def _tree_outcomes(parents, V, rows, tau=1.0, want=2):
             def run(draw):
                 path, final, _, _ = oacc.walk_sampled(
                     lambda n: tgt[n], lambda n: drf[n], parents, tokens, tau,
-                    lambda n, s: draw(0, n, s))
+                    lambda n, s: draw(0, n, s), without_replacement)
                 emitted = [int(tokens[c]) for c in path] + [int(final)]
                 emitted += [None] * want
                 return tuple(emitted[:want])
@@ -157,6 +160,11 @@ def _tree_outcomes(parents, V, rows, tau=1.0, want=2):
             n = int(parents[n])
         ppath = tuple(reversed(toks))
         pd = sp_softmax(rows(ppath)[1] / tau)
+        if without_replacement:   # earlier siblings' tokens are gone, the rest renormalised
+            used = [int(tokens[o]) for o in range(1, c) if int(parents[o]) == par]
+            pd = pd.copy()
+            pd[used] = 0.0
+            pd = pd / pd.sum()
         for t in range(V):
             if pd[t] == 0:
                 continue
@@ -466,3 +474,58 @@ def test_padding_must_be_a_suffix():
     tgt = rng.standard_normal((1, T, V))
     out = oacc.spec_accept(tgt, tgt, par, tok, 1.0, 1, 0)
     assert out["flags"].tolist() == [oacc.FLAG_BAD_TREE] and out["accept_len"].tolist() == [-1]
+
+
+@pytest.mark.parametrize("parents,V,seed,tau", [
+    ([-1, 0, 0, 0], 4, 1, 1.0),         # three siblings drawn without replacement at the root
+    ([-1, 0, 0, 0, 0], 4, 4, 0.8),      # as many siblings as tokens: the last one is forced
+    ([-1, 0, 0, 1, 1], 3, 2, 1.0),      # depth 2, two siblings per level
+])
+def test_lossless_exact_without_replacement(parents, V, seed, tau):
+    """Siblings drawn without replacement and verified against the draft with
+    the tried tokens removed and renormalised: the emitted tokens follow the
+    target exactly (exact enumeration of tokens and uniforms)."""
+    rows = _tables(V, seed)
+    dist = _tree_outcomes(np.asarray(parents), V, rows, tau=tau, without_replacement=True)
+    assert abs(sum(dist.values()) - 1.0) < 1e-12
+    first = np.zeros(V)
+    for (a, _), pr in dist.items():
+        first[a] += pr
+    np.testing.assert_allclose(first, sp_softmax(rows(())[0] / tau), rtol=0, atol=1e-12)
+    for a in range(V):
+        cont = np.zeros(V)
+        for (x, y), pr in dist.items():
+            if x == a and y is not None:
+                cont[y] += pr
+        if cont.sum() > 1e-9:
+            np.testing.assert_allclose(cont / cont.sum(), sp_softmax(rows((a,))[0] / tau), rtol=0, atol=1e-10)
+
+
+def test_with_replacement_rule_is_not_lossless_for_distinct_siblings():
+    """The plain rule applied to siblings drawn without replacement is biased
+    (which is why the renormalised rule exists): the exact first-token law
+    then differs from the target."""
+    rows = _tables(3, 5)
+    par = np.asarray([-1, 0, 0])
+    T = 3
+    # distinct siblings drawn without replacement, verified with the i.i.d. rule
+    total = defaultdict(float)
+    t_root, d_root = rows(())
+    pd = sp_softmax(d_root)
+    for t1 in range(3):
+        for t2 in range(3):
+            if t2 == t1:
+                continue
+            w = pd[t1] * pd[t2] / (1.0 - pd[t1])
+            tokens = np.array([0, t1, t2])
+            tgt = np.stack([t_root, rows((t1,))[0], rows((t2,))[0]])
+            drf = np.stack([d_root, rows((t1,))[1], rows((t2,))[1]])
+
+            def run(draw, tokens=tokens, tgt=tgt, drf=drf):
+                path, final, _, _ = oacc.walk_sampled(lambda n: tgt[n], lambda n: drf[n], par, tokens, 1.0,
+                                                      lambda n, s: draw(0, n, s))
+                return int(tokens[path[0]]) if path else int(final)
+            for out, pr in enumerate_outcomes(run).items():
+                total[out] += w * pr
+    first = np.array([total[a] for a in range(3)])
+    assert np.abs(first - sp_softmax(t_root)).max() > 1e-3
