@@ -854,7 +854,56 @@ struct FusedShared {
   int32_t pnear[kMaxTree];     // decoded from their publication words
   double cmass[kFusedMaxChunks];   // q mass of each chunk (from the chunk statistics)
   double sample[4];
+  // siblings drawn without replacement: the residual weight each tried
+  // child's token keeps once later siblings no longer see it (-1: the token
+  // repeats an earlier sibling's), and the draft mass not yet tried
+  double wfz[kMaxTree];
+  double zrem;
 };
+
+// Siblings drawn without replacement (thread 0): sibling i is tested against
+// p_i = p without the earlier siblings' tokens, renormalised by the mass Z
+// left.  With the untried tokens' residual max(0, q - C p) / s as before,
+// rejecting sibling i gives C <- C + s / Z for the untried tokens, while a
+// tried token keeps the weight max(0, q(t) - C p(t)) it had just after its own
+// rejection (p_j no longer reaches it).  So the residual mass of round i is
+// the full-vocabulary sum at C minus the tried tokens' terms at C plus their
+// kept weights.
+__device__ __forceinline__ double wr_mass(const FusedShared& sh, int tried, double C, double full) {
+  double s = full;
+  for (int j = 0; j < tried; ++j) {
+    const double w = sh.wfz[j];
+    if (w < 0.0) continue;   // a repeated token: counted once
+    s += w - fmax(0.0, sh.cand[j].qt - C * sh.cand[j].pt);
+  }
+  return s;
+}
+// earlier sibling ordinal with the same token as sibling i, or -1
+__device__ __forceinline__ int wr_repeat(const FusedShared& sh, int i) {
+  for (int j = 0; j < i; ++j)
+    if (sh.cand[j].tok == sh.cand[i].tok) return j;
+  return -1;
+}
+// test of sibling i under (C, s) without replacement; returns 1 accept, 0 reject
+__device__ __forceinline__ int wr_decide(const FusedShared& sh, int i, int V, double C, double s, uint32_t& fl,
+                                         int32_t& nr) {
+  const Cand& cd = sh.cand[i];
+  const int rep = wr_repeat(sh, i);
+  if (rep >= 0 || !(sh.zrem > 0.0)) {   // p_i(t) = 0: accept iff the residual keeps mass there
+    fl |= EAGLE_FLAG_P_ZERO;
+    return (rep >= 0 ? sh.wfz[rep] : fmax(0.0, cd.qt - C * cd.pt)) > 0.0 ? 1 : 0;
+  }
+  return decide_pre(cd.qt, cd.pt / sh.zrem, cd.r, cd.tok, V, C * sh.zrem, s, fl, nr);
+}
+// after rejecting sibling i at (C, s): the next C, and the kept weight of its token
+__device__ __forceinline__ double wr_reject(FusedShared& sh, int i, double C, double s) {
+  const int rep = wr_repeat(sh, i);
+  const double Cn = sh.zrem > 0.0 ? C + s / sh.zrem : C;
+  const Cand& cd = sh.cand[i];
+  sh.wfz[i] = rep >= 0 ? -1.0 : fmax(0.0, cd.qt - Cn * cd.pt);
+  if (rep < 0) sh.zrem -= cd.pt;
+  return Cn;
+}
 
 // Two reductions over the block sharing one pair of barriers (all threads call).
 template <typename T, typename Op>
@@ -1305,6 +1354,8 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       const Cand& cd = sh.cand[0];
       uint32_t fl = st.flags;
       int32_t nr = 0;
+      sh.zrem = 1.0;
+      for (int j = 0; j < nkids; ++j) sh.wfz[j] = -1.0;   // no kept weight until the sibling is rejected
       const int res = decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, 0.0, 1.0, fl, nr);
       st.flags = fl;
       st.near = nr;
@@ -1312,7 +1363,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         st.kind = kNodeAccepted;
         st.outcome = cd.child;
       } else {
-        st.C = 1.0;
+        st.C = a.wr ? wr_reject(sh, 0, 0.0, 1.0) : 1.0;
         st.next_child = 1;
         st.kind = (res == 0 && nkids > 1) ? kNodeNeedsPass : kNodeRejected;
       }
@@ -1353,22 +1404,26 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       int i = st.next_child;
       double Cn = st.C;
       double s = static_cast<double>(w & kSumMask) * kFixUnit;
+      if (a.wr) s = wr_mass(sh, i, Cn, s);
       if (!(s > 0.0)) {
         st.flags |= EAGLE_FLAG_DEGENERATE_RESIDUAL;
         Cn = 0.0;
         s = 1.0;
+        if (a.wr)   // the residual starts over from q, tried tokens included
+          for (int j = 0; j < i; ++j)
+            if (sh.wfz[j] >= 0.0) sh.wfz[j] = sh.cand[j].qt;
       }
       const Cand& cd = sh.cand[i];
       uint32_t fl = st.flags;
       int32_t nr = st.near;
-      const int res = decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, Cn, s, fl, nr);
+      const int res = a.wr ? wr_decide(sh, i, V, Cn, s, fl, nr) : decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, Cn, s, fl, nr);
       st.flags = fl;
       st.near = nr;
       if (res > 0) {
         st.kind = kNodeAccepted;
         st.outcome = cd.child;
       } else {
-        Cn += s;
+        Cn = a.wr ? wr_reject(sh, i, Cn, s) : Cn + s;
         ++i;
         st.kind = (res == 0 && i < nkids) ? kNodeNeedsPass : kNodeRejected;
       }
@@ -1526,8 +1581,22 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   double ts = 0.0, tq = 0.0, offset = 0.0;
   int cstar = 0;
   bool degen = false;
+  // without replacement: a tried token's terminal weight is the one it kept
+  const bool wr_tail = a.wr && !leaf && !greedy;
+  auto kept_weight = [&](int token, double wdef) __attribute__((always_inline)) -> double {
+    for (int j = 0; j < nkids; ++j)
+      if (sh.wfz[j] >= 0.0 && sh.cand[j].tok == token) return sh.wfz[j];
+    return wdef;
+  };
   if (!greedy) {
     sums(leaf, ts, tq);
+    if (wr_tail) {   // replace the formula's weight of each tried token in this thread's range
+      for (int j = 0; j < nkids; ++j) {
+        const int slot = sh.cand[j].tok - v0;
+        if (sh.wfz[j] >= 0.0 && slot >= i0 && slot < i0 + kPerThread && sh.cand[j].tok < v1)
+          ts += sh.wfz[j] - weight(false, lds_logit<TL>(lq, slot), lds_logit<TL>(lp, slot));
+      }
+    }
     offset = scan_offsets(ts);
     // residual and q masses of every chunk: four words per chunk (low and
     // high halves of the two doubles) whose high halves carry the call's
@@ -1660,7 +1729,8 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         const int l = tid & 31;
         const float xq = lds_logit<TL>(lq, t0 + l);
         const float xp = q_only ? xq : lds_logit<TL>(lp, t0 + l);
-        const double w = (tid < 32) ? weight(q_only, xq, xp) : 0.0;
+        double w = (tid < 32) ? weight(q_only, xq, xp) : 0.0;
+        if (wr_tail && !q_only && tid < 32) w = kept_weight(v0 + t0 + l, w);
         const double incl = wave_scan_add(w);   // lanes 32..63 carry 0
         const double cum = s0 + incl;
         const uint64_t over = __ballot(tid < 32 && (s0 > thr || cum > thr));
@@ -1692,7 +1762,9 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       for (int e = 0; e < kPerThread; ++e) {
         const float xq = lds_logit<TL>(lq, i0 + e);
         const float xp = q_only ? xq : lds_logit<TL>(lp, i0 + e);
-        if (v0 + i0 + e < v1 && weight(q_only, xq, xp) > 0.0) last = v0 + i0 + e;
+        double we = weight(q_only, xq, xp);
+        if (wr_tail && !q_only) we = kept_weight(v0 + i0 + e, we);
+        if (v0 + i0 + e < v1 && we > 0.0) last = v0 + i0 + e;
       }
       if (tid == 0) sh.iscr[2] = -1;
       __syncthreads();

@@ -163,7 +163,7 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     hip_fail(nullptr, "workspace initialisation", e);
-    hipFree(h->base);
+    (void)hipFree(h->base);
     delete h;
     return EAGLE_ERR_HIP;
   }
@@ -308,7 +308,16 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   // does not fit takes the three-kernel path.
   const int64_t per_seq = static_cast<int64_t>(k.T) * k.NC;
   const int64_t cap = h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0];
+  k.wr = (a->without_replacement && a->temperature > 0.f) ? 1 : 0;
   if (per_seq > cap || k.NC > 64) {
+    if (k.wr) {
+      char msg[160];
+      std::snprintf(msg, sizeof(msg),
+                    "siblings without replacement need the fused path: %lld workgroups per sequence, %lld resident",
+                    static_cast<long long>(per_seq), static_cast<long long>(cap));
+      set_err(h, msg);
+      return EAGLE_ERR_UNSUPPORTED;
+    }
     k.fused = 0;
     const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
     if (e != 0) return hip_fail(h, "spec accept launch", e);

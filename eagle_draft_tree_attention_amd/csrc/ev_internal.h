@@ -127,6 +127,7 @@ struct AcceptKernelArgs {
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
   int fused;              // 1: one co-resident kernel; 0: three-kernel path
   int b0;                 // batch index of sequence 0 of this launch (a slice of the call's batch)
+  int wr;                 // 1: siblings were drawn without replacement (fused path only)
   int B, T, V, NC;
   int vec_ok;          // rows start 16-byte aligned
   float tau;           // > 0 sampled, == 0 greedy

@@ -198,7 +198,7 @@ class Verifier:
         return eagle_verify_last_attention_plan(self.handle)
 
     def spec_accept(self, target, draft, parents, tokens, temperature, seed, offset, outputs=None,
-                    stream=None):
+                    stream=None, without_replacement=False):
         import torch
         B, T, V = target.shape
         dev = target.device
@@ -221,6 +221,7 @@ class Verifier:
         a.out_tokens = _ptr(outputs["out_tokens"])
         a.flags = _ptr(outputs["flags"])
         a.near_ties = _ptr(outputs["near_ties"])
+        a.without_replacement = 1 if without_replacement else 0
         eagle_verify_spec_accept(self.handle, a, _stream(stream))
         return outputs
 

@@ -156,6 +156,16 @@ typedef struct {
  *   temperature  > 0: q = softmax(target/t), p = softmax(draft/t);
  *                == 0: greedy — accept the first child whose token is the
  *                target argmax (lowest id on ties), else emit that argmax.
+ *   without_replacement  1: the siblings of a node were drawn from its draft
+ *                distribution without replacement, so sibling i is tested
+ *                against that distribution with the earlier siblings' tokens
+ *                removed and renormalised, and the residual update uses the
+ *                same distribution (a repeated token has probability 0 there:
+ *                accepted iff the residual keeps mass on it); 0: i.i.d.
+ *                siblings, every sibling against the parent's draft row.
+ *                Ignored when temperature == 0.  Only for calls whose
+ *                sequences each fit the fused kernel (T x ceil(V / 8192)
+ *                workgroups resident at once), else EAGLE_ERR_UNSUPPORTED.
  *   seed, offset Philox4x32-10 key / per-step counter word: the uniform for the
  *                test of the i-th child (0-based) of node n in sequence b uses
  *                counter (i, n | b << 8, offset_lo, offset_hi), key (seed_lo,
@@ -185,6 +195,7 @@ typedef struct {
   int32_t* out_tokens;
   uint32_t* flags;
   int32_t* near_ties;
+  int32_t without_replacement; /* 0 or 1, see above */
 } eagle_spec_accept_args;
 
 /* Commit the accepted path into the KV cache, in place (lesson page, the

@@ -13,7 +13,7 @@ from scipy.special import softmax as sp_softmax
 from scipy.stats import chi2 as chi2_dist
 
 import synth
-from gpu_util import compare_accept, log, make_verifier, run_accept, small_spec
+from gpu_util import compare_accept, dev, log, make_verifier, run_accept, small_spec
 from oracle import accept as oacc
 
 pytestmark = pytest.mark.gpu
@@ -285,4 +285,79 @@ def test_general_path_with_padded_trees():
             ref = oacc.spec_accept(synth.inputs.as_f64(tgt, spec.ldtype),
                                    None if temp == 0 else synth.inputs.as_f64(drf, spec.ldtype), par, tok, temp, SEED, off)
             compare_accept(got, ref, f"general temperature {temp} offset {off}")
+    ver.close()
+
+
+def _tokens_without_replacement(spec, inp, rng, temp):
+    """Children's tokens drawn from their parent's draft row without
+    replacement (siblings distinct), in sibling order."""
+    d64 = synth.inputs.as_f64(inp.draft, spec.ldtype)
+    tok = inp.tokens.copy()
+    for b in range(spec.batch):
+        kids = oacc.tree_children(inp.parents[b])
+        for n, ch in enumerate(kids):
+            if not ch:
+                continue
+            p = sp_softmax(d64[b, n] / temp)
+            tok[b, ch] = rng.choice(spec.vocab, size=len(ch), replace=False, p=p)
+    return tok
+
+
+WR_CASES = [
+    small_spec("wr_bf16_t1", B=8, V=1000, levels=(4, 6, 10)),
+    small_spec("wr_bf16_t07_multi_chunk", B=3, V=20000, levels=(10, 10, 10), temperature=0.7),
+    small_spec("wr_bf16_low_alpha_many_rounds", B=6, V=3000, sigma_d=2.5, levels=(12, 12)),
+    small_spec("wr_f32_star", dtype="f32", B=4, V=64, tree=("star", 40), sigma_d=1.5),
+]
+
+
+@pytest.mark.parametrize("spec", WR_CASES, ids=lambda s: s.name)
+def test_siblings_without_replacement(spec):
+    log(f"[accept] without replacement: {spec.name}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    tok = _tokens_without_replacement(spec, inp, np.random.default_rng(3), spec.temperature)
+    ver = make_verifier(spec, inp.T)
+    diverged = 0
+    for off in range(6):
+        got = ver.spec_accept(*[dev(x, spec.ldtype) for x in (inp.target, inp.draft)], dev(inp.parents), dev(tok),
+                              spec.temperature, SEED, off, without_replacement=True)
+        import torch
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in got.items()}
+        got["flags"] = got["flags"].astype(np.uint32)
+        ref = oacc.spec_accept(inp.target64(), inp.draft64(), inp.parents, tok, spec.temperature, SEED, off,
+                               without_replacement=True)
+        diverged += compare_accept(got, ref, f"{spec.name} offset {off}")
+    log(f"    near-tie divergences: {diverged}")
+    ver.close()
+
+
+def test_without_replacement_with_repeated_tokens():
+    """i.i.d. siblings (tokens may repeat) under the without-replacement rule:
+    a repeated token has draft probability 0 there."""
+    spec = small_spec("wr_repeats", dtype="f32", B=6, V=6, tree=("star", 8), sigma_d=1.0)
+    inp = synth.make_inputs(spec, with_kv=False)
+    ver = make_verifier(spec, inp.T)
+    for off in range(4):
+        got = ver.spec_accept(dev(inp.target), dev(inp.draft), dev(inp.parents), dev(inp.tokens), 1.0, SEED, off,
+                              without_replacement=True)
+        import torch
+        torch.cuda.synchronize()
+        got = {k: v.cpu().numpy() for k, v in got.items()}
+        got["flags"] = got["flags"].astype(np.uint32)
+        ref = oacc.spec_accept(inp.target64(), inp.draft64(), inp.parents, inp.tokens, 1.0, SEED, off,
+                               without_replacement=True)
+        compare_accept(got, ref, f"repeats offset {off}")
+    ver.close()
+
+
+def test_without_replacement_needs_the_fused_path():
+    from eagle_draft_tree_attention_amd._abi import EagleVerifyError
+    spec = small_spec("wr_general", B=1, V=520000, levels=(10,) * 6)
+    inp = synth.make_inputs(spec, with_kv=False)
+    ver = make_verifier(spec, inp.T)
+    with pytest.raises(EagleVerifyError) as e:
+        ver.spec_accept(dev(inp.target, "bf16"), dev(inp.draft, "bf16"), dev(inp.parents), dev(inp.tokens), 1.0,
+                        SEED, 0, without_replacement=True)
+    assert "fused path" in str(e.value)
     ver.close()
