@@ -1102,7 +1102,9 @@ __device__ int root_path(const TreeInfo& ti, int n, int* path) {
 
 // VEC: rows and chunks are whole 16-byte groups (then every chunk is read
 // with straight-line vector requests)
-template <typename TL, bool VEC>
+// WR: siblings drawn without replacement (a separate instantiation, so that
+// the common kernel carries none of it)
+template <typename TL, bool VEC, bool WR>
 __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a) {
   constexpr int G = Pack<TL>::G;
   constexpr int NV = kPerThread / G;   // 16-byte groups per thread and row
@@ -1363,7 +1365,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         st.kind = kNodeAccepted;
         st.outcome = cd.child;
       } else {
-        st.C = a.wr ? wr_reject(sh, 0, 0.0, 1.0) : 1.0;
+        st.C = WR ? wr_reject(sh, 0, 0.0, 1.0) : 1.0;
         st.next_child = 1;
         st.kind = (res == 0 && nkids > 1) ? kNodeNeedsPass : kNodeRejected;
       }
@@ -1404,26 +1406,26 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       int i = st.next_child;
       double Cn = st.C;
       double s = static_cast<double>(w & kSumMask) * kFixUnit;
-      if (a.wr) s = wr_mass(sh, i, Cn, s);
+      if (WR) s = wr_mass(sh, i, Cn, s);
       if (!(s > 0.0)) {
         st.flags |= EAGLE_FLAG_DEGENERATE_RESIDUAL;
         Cn = 0.0;
         s = 1.0;
-        if (a.wr)   // the residual starts over from q, tried tokens included
+        if (WR)   // the residual starts over from q, tried tokens included
           for (int j = 0; j < i; ++j)
             if (sh.wfz[j] >= 0.0) sh.wfz[j] = sh.cand[j].qt;
       }
       const Cand& cd = sh.cand[i];
       uint32_t fl = st.flags;
       int32_t nr = st.near;
-      const int res = a.wr ? wr_decide(sh, i, V, Cn, s, fl, nr) : decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, Cn, s, fl, nr);
+      const int res = WR ? wr_decide(sh, i, V, Cn, s, fl, nr) : decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, Cn, s, fl, nr);
       st.flags = fl;
       st.near = nr;
       if (res > 0) {
         st.kind = kNodeAccepted;
         st.outcome = cd.child;
       } else {
-        Cn = a.wr ? wr_reject(sh, i, Cn, s) : Cn + s;
+        Cn = WR ? wr_reject(sh, i, Cn, s) : Cn + s;
         ++i;
         st.kind = (res == 0 && i < nkids) ? kNodeNeedsPass : kNodeRejected;
       }
@@ -1582,7 +1584,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   int cstar = 0;
   bool degen = false;
   // without replacement: a tried token's terminal weight is the one it kept
-  const bool wr_tail = a.wr && !leaf && !greedy;
+  const bool wr_tail = WR && !leaf && !greedy;
   auto kept_weight = [&](int token, double wdef) __attribute__((always_inline)) -> double {
     for (int j = 0; j < nkids; ++j)
       if (sh.wfz[j] >= 0.0 && sh.cand[j].tok == token) return sh.wfz[j];
@@ -1801,8 +1803,14 @@ template <typename TL>
 hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
   const dim3 block(kThreads);
   if (a.fused) {
-    if (a.vec_ok) hipLaunchKernelGGL((sa_fused<TL, true>), dim3(static_cast<unsigned>(a.B * a.T * a.NC)), block, 0, st, a);
-    else hipLaunchKernelGGL((sa_fused<TL, false>), dim3(static_cast<unsigned>(a.B * a.T * a.NC)), block, 0, st, a);
+    const dim3 grid(static_cast<unsigned>(a.B * a.T * a.NC));
+    if (a.wr) {
+      if (a.vec_ok) hipLaunchKernelGGL((sa_fused<TL, true, true>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((sa_fused<TL, false, true>), grid, block, 0, st, a);
+    } else {
+      if (a.vec_ok) hipLaunchKernelGGL((sa_fused<TL, true, false>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((sa_fused<TL, false, false>), grid, block, 0, st, a);
+    }
     return hipGetLastError();
   }
   hipLaunchKernelGGL((sa_stats<TL>), dim3(static_cast<unsigned>(a.B * a.T * 2 * a.NC)), block, 0, st, a);
@@ -1822,11 +1830,13 @@ hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
 }  // namespace
 
 int fused_accept_capacity(int logits_bf16, int num_cus) {
-  // the two loader variants must both fit: the smaller occupancy decides
+  // every loader and sibling-rule variant must fit: the smallest occupancy decides
   int per_cu = 1 << 30;
-  const void* kernels[2] = {
-      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, true>) : reinterpret_cast<const void*>(&sa_fused<float, true>),
-      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, false>) : reinterpret_cast<const void*>(&sa_fused<float, false>)};
+  const void* kernels[4] = {
+      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, true, false>) : reinterpret_cast<const void*>(&sa_fused<float, true, false>),
+      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, false, false>) : reinterpret_cast<const void*>(&sa_fused<float, false, false>),
+      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, true, true>) : reinterpret_cast<const void*>(&sa_fused<float, true, true>),
+      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, false, true>) : reinterpret_cast<const void*>(&sa_fused<float, false, true>)};
   for (const void* k : kernels) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, 0) != hipSuccess || n <= 0) return 0;

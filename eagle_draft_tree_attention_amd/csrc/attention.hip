@@ -216,7 +216,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* base) {
 
 // MB = 1: two workgroups per CU (two waves per SIMD, 256 registers each);
 // MB = 2: one workgroup per CU, whose waves may then hold 512 registers
-template <int D, int MB, int NST, int KG>
+// PAGED: K/V rows through per-sequence page tables (a separate instantiation,
+// so that the contiguous kernel carries none of it)
+template <int D, int MB, int NST, int KG, bool PAGED = false>
 __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const AttnKernelArgs a) {
   static_assert(KG == 1 || (KG == 2 && MB == 1), "key halves are split only between single row blocks");
   constexpr int KSTEPS = D / 32;          // QK^T contraction steps
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   // sequence, without waiting for kv_indptr[b]; the parent array is requested
   // before it, and nothing waits on either until the tile has landed.
   const int par_lane = lane < T ? a_par[b * T + lane] : 0;
-  const bool paged = a.page_size != 0;
+  constexpr bool paged = PAGED;
   const int guess = b == 0 ? b0_guess : a.kv0_guess[b];
   int64_t kv0 = paged ? 0 : (guess >= 0 ? (int64_t)guess : a.kv_indptr[b]);
   const uint16_t* __restrict__ kbase = reinterpret_cast<const uint16_t*>(a_k) + (int64_t)hk * D;
@@ -1061,11 +1063,21 @@ template <int D>
 hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hipStream_t st) {
   if (p.path == 1) {
     const dim3 grid((unsigned)p.workgroups), block(256);
-    switch (mfma_variant(p)) {
-      case 0: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 1>), grid, block, 0, st, a); break;
-      case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2, 1>), grid, block, 0, st, a); break;
-      case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 2>), grid, block, 0, st, a); break;
-      default: return hipErrorInvalidValue;
+    const int v = mfma_variant(p);
+    if (a.page_size) {
+      switch (v) {
+        case 0: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 1, true>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2, 1, true>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 2, true>), grid, block, 0, st, a); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (v) {
+        case 0: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 1>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2, 1>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 2>), grid, block, 0, st, a); break;
+        default: return hipErrorInvalidValue;
+      }
     }
   } else {
     const dim3 grid((unsigned)p.workgroups), block(64);
