@@ -21,11 +21,11 @@
 //              the row's chunk records and reduces its maximum and
 //              normaliser, takes its top k as a k-step merge of the chunks'
 //              sorted lists and values them s_f + (x - max)/t - log Z in
-//              fp64 (lists handed over in LDS); then one wave, lane f =
-//              row f, ranks globally by merging the rows' lists: each step
-//              it takes the largest head (ties: the lowest lane), M + 1
-//              steps, the last one only to see whether the boundary is a
-//              near tie.
+//              fp64 (lists handed over in LDS); then every candidate is
+//              ranked by counting the candidates before it (value, then
+//              frontier index, then position in its row) and written to its
+//              slot; adjacent ranks up to the kept/dropped boundary are
+//              tested for near ties.
 //   te_rerank  (separate call) the final tree from the chained steps.
 // Within a row the value is a monotone function of the logit, so a row's
 // list sorted by logit is sorted by value too.
@@ -246,10 +246,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // w, w + 8, ...; for each, lane c reads chunk c's record, the wave reduces the
 // row's maximum, normaliser and unusable flag, and takes the row's top K as a
 // K-step merge of the chunks' sorted lists (each step the best head), valued
-// s + (x - max)/t - log Z in fp64, into LDS.  Selection phase (wave 0, lane
-// f = frontier row f): the global ranking as a merge of the rows' lists, the
-// largest head each step, ties to the lowest lane; M + 1 steps, the last one
-// only to see whether the boundary is a near tie.
+// s + (x - max)/t - log Z in fp64, into LDS.  Selection phase (all threads):
+// each candidate's rank is the number of candidates before it, and it is
+// written straight to that output slot.
 __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelArgs a) {
   __shared__ float lv[kSelWaves][kMaxChunksExpand][kMaxTopK];   // chunk lists of the wave's current row
   __shared__ int li[kSelWaves][kMaxChunksExpand][kMaxTopK];
@@ -318,46 +317,65 @@ __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelAr
     wave_lds_sync();   // the lists are read before the next row overwrites them
   }
   __syncthreads();
-  if (wave != 0) return;
 
-  const int cnt = lane < F ? scnt[lane] : 0;   // candidates of row `lane`
-  const bool unusable = lane < F && sbad[lane] != 0;
-  int pos = 0;
-  double prev_v = 0.0;
-  int prev_f = -1;
-  float prev_x = 0.f;
-  int near = 0;
-  for (int step = 0; step <= M; ++step) {
-    const uint64_t key = pos < cnt ? ord64(sv[lane][pos]) : 0ull;
-    const uint64_t bkey = wave_max_u64(key);
-    if (bkey == 0ull) {   // no candidate left: pad
-      if (lane == 0 && step < M) {
-        a.parent[b * M + step] = -1;
-        a.token[b * M + step] = -1;
-        a.value[b * M + step] = kNegInf;
-      }
-      continue;
-    }
-    const double best = unord64(bkey);
-    const uint64_t hit = __ballot(pos < cnt && key == bkey);
-    const int w = __ffsll(static_cast<long long>(hit)) - 1;
-    const int wt = __shfl(pos < cnt ? st[lane][pos] : 0, w);
-    const float wx = __shfl(pos < cnt ? sx[lane][pos] : 0.f, w);
-    if (step > 0 && prev_v - best < kNear && !(prev_f == w && prev_x == wx)) ++near;
-    prev_v = best;
-    prev_f = w;
-    prev_x = wx;
-    if (lane == 0 && step < M) {
-      a.parent[b * M + step] = w;
-      a.token[b * M + step] = wt;
-      a.value[b * M + step] = static_cast<float>(best);
-    }
-    if (lane == w) ++pos;
+  // Selection by rank: candidate (f, q) of slot t = f * K + q ranks by the
+  // number of candidates before it (larger value, then lower frontier index,
+  // then earlier in its row: lower token id among equal values), so every
+  // thread writes its own output slot; the rows' lists are read from LDS as
+  // broadcasts.  Rank r and r + 1 (up to the kept/dropped boundary) form the
+  // decisions tested for near ties.
+  __shared__ int byrank[kMaxKeep + 1];
+  __shared__ double cv[kMaxTree * kMaxTopK];   // slot f * K + q: candidate value, -inf past a row's list
+  int n_valid = 0;
+  bool any_bad = false;
+  const int tot = F * K;
+  for (int t = threadIdx.x; t < tot; t += 64 * kSelWaves) {
+    const int f = t / K, q = t - f * K;
+    cv[t] = q < scnt[f] ? sv[f][q] : -__builtin_inf();
   }
-  const bool any_bad = __any(unusable);
-  if (lane == 0) {
+  for (int t = threadIdx.x; t < F; t += 64 * kSelWaves) any_bad = any_bad || sbad[t] != 0;
+  __syncthreads();
+  {
+    for (int t0 = 0; t0 < tot; t0 += 64 * kSelWaves) {
+      const int t = t0 + threadIdx.x;
+      const double v = t < tot ? cv[t] : -__builtin_inf();
+      const bool valid = v > -__builtin_inf();   // candidate values are finite
+      n_valid += __syncthreads_count(valid);
+      if (!valid) continue;
+      const int f = t / K, q = t - f * K;
+      // slots before t in (f, q) order are exactly the indices below t
+      int rank = 0;
+#pragma unroll 8
+      for (int j = 0; j < tot; ++j) {
+        const double w = cv[j];
+        rank += (w > v || (w == v && j < t)) ? 1 : 0;
+      }
+      if (rank <= M) byrank[rank] = (f << 8) | q;
+      if (rank < M) {
+        a.parent[b * M + rank] = f;
+        a.token[b * M + rank] = st[f][q];
+        a.value[b * M + rank] = static_cast<float>(v);
+      }
+    }
+  }
+  any_bad = __syncthreads_or(any_bad);
+  // padding past the candidates, and the near ties of adjacent ranks
+  const int t = threadIdx.x;
+  if (t >= n_valid && t < M) {
+    a.parent[b * M + t] = -1;
+    a.token[b * M + t] = -1;
+    a.value[b * M + t] = kNegInf;
+  }
+  bool near = false;
+  if (t + 1 < n_valid && t + 1 <= M) {
+    const int e0 = byrank[t], e1 = byrank[t + 1];
+    const int f0 = e0 >> 8, q0 = e0 & 255, f1 = e1 >> 8, q1 = e1 & 255;
+    near = sv[f0][q0] - sv[f1][q1] < kNear && !(f0 == f1 && sx[f0][q0] == sx[f1][q1]);
+  }
+  const int nnear = __syncthreads_count(near);
+  if (t == 0) {
     a.flags[b] = any_bad ? EAGLE_FLAG_NONFINITE : 0u;
-    a.near_ties[b] = near;
+    a.near_ties[b] = nnear;
   }
 }
 
