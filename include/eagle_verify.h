@@ -57,7 +57,7 @@ typedef struct eagle_verify eagle_verify; /* opaque handle */
 typedef enum {
   EAGLE_OK = 0,
   EAGLE_ERR_ARG = 1,         /* null/misaligned pointer, value out of range       */
-  EAGLE_ERR_UNSUPPORTED = 2, /* shape/dtype combination this build does not run    */
+  EAGLE_ERR_UNSUPPORTED = 2, /* shape/dtype combination the library does not run  */
   EAGLE_ERR_CAPACITY = 3,    /* above the maxima given to eagle_verify_create      */
   EAGLE_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed         */
   EAGLE_ERR_OOM = 5          /* workspace allocation failed                        */
