@@ -157,7 +157,8 @@ typedef struct {
  *                == 0: greedy — accept the first child whose token is the
  *                target argmax (lowest id on ties), else emit that argmax.
  *   without_replacement  1: the siblings of a node were drawn from its draft
- *                distribution without replacement, so sibling i is tested
+ *                distribution without replacement (the k sampled children of
+ *                the EAGLE notes page, core mechanism), so sibling i is tested
  *                against that distribution with the earlier siblings' tokens
  *                removed and renormalised, and the residual update uses the
  *                same distribution (a repeated token has probability 0 there:

@@ -128,7 +128,8 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_re
     target_rows(n) / draft_rows(n) return node n's logits rows (float64);
     draw(node, slot) returns the uniform for that decision.
     without_replacement: the siblings were drawn from p_n without
-    replacement, so sibling i is tested against p_n with the tokens of the
+    replacement (the k sampled children of the EAGLE notes page, core
+    mechanism), so sibling i is tested against p_n with the tokens of the
     siblings tried before it removed and the rest renormalised (all zero if
     nothing is left); the residual update uses that same distribution.
     Returns (path, final_token, flags, near_ties).
