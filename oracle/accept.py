@@ -122,7 +122,7 @@ def inv_cdf(w, u):
     return v, near
 
 
-def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_replacement=False):
+def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_replacement=False, where=None):
     """Sequential multi-round walk of one tree.
 
     target_rows(n) / draft_rows(n) return node n's logits rows (float64);
@@ -132,6 +132,10 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_re
     mechanism), so sibling i is tested against p_n with the tokens of the
     siblings tried before it removed and the rest renormalised (all zero if
     nothing is left); the residual update uses that same distribution.
+    where: if a list, every near-tie decision appends (depth, slot) to it:
+    depth = accepted nodes before the decision (the node deciding sits at
+    that depth of the path), slot = the sibling ordinal of a test, or -1 for
+    the terminal sample.
     Returns (path, final_token, flags, near_ties).
     """
     kids = tree_children(parents, real_rows(tokens, len(parents)))
@@ -144,6 +148,8 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_re
         if not kids[cur]:
             final, nt = inv_cdf(q, draw(cur, philox.SAMPLE_SLOT))
             near += int(nt)
+            if nt and where is not None:
+                where.append((len(path), -1))
             return path, final, flags, near
         p = softmax_t(draft_rows(cur), tau)
         q_res = q
@@ -166,6 +172,8 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_re
                 ok = r < ratio
                 if _is_number(r) and abs(r - ratio) < NEAR_TIE:
                     near += 1
+                    if where is not None:
+                        where.append((len(path), i))
             if ok:
                 accepted = c
                 break
@@ -180,6 +188,8 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_re
         if accepted is None:
             final, nt = inv_cdf(q_res, draw(cur, philox.SAMPLE_SLOT))
             near += int(nt)
+            if nt and where is not None:
+                where.append((len(path), -1))
             return path, final, flags, near
         path.append(accepted)
         cur = accepted
@@ -225,7 +235,11 @@ def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=
     target, draft: [B,T,V] float64 logits (draft may be None when
     temperature == 0).  draw(b, node, slot) overrides the Philox uniforms.
     Returns a dict of numpy arrays: accept_len [B], accepted_nodes [B,T],
-    out_tokens [B,T], flags [B], near_ties [B].
+    out_tokens [B,T], flags [B], near_ties [B], and where the walk's first
+    near-tie decision sits: first_near_depth [B] (accepted nodes before it,
+    -1 if none) and first_near_slot [B] (sibling ordinal of a test, -1 for
+    the terminal sample).  Up to that decision the result is fixed by the
+    arithmetic; past it another rounding could take the other branch.
     """
     target = np.asarray(target, dtype=np.float64)
     B, T, V = target.shape
@@ -236,6 +250,8 @@ def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=
         "out_tokens": np.full((B, T), -1, dtype=np.int32),
         "flags": np.zeros(B, dtype=np.uint32),
         "near_ties": np.zeros(B, dtype=np.int32),
+        "first_near_depth": np.full(B, -1, dtype=np.int32),
+        "first_near_slot": np.full(B, -1, dtype=np.int32),
     }
     for b in range(B):
         drf = None if draft is None else np.asarray(draft[b], dtype=np.float64)
@@ -252,8 +268,11 @@ def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=
             else:
                 def u(n, s, _b=b):
                     return draw(_b, n, s)
+            where = []
             path, final, fl, near = walk_sampled(lambda n: target[b, n], lambda n: drf[n],
-                                                 parents[b], tokens[b], tau, u, without_replacement)
+                                                 parents[b], tokens[b], tau, u, without_replacement, where)
+            if where:
+                res["first_near_depth"][b], res["first_near_slot"][b] = where[0]
         res["accept_len"][b] = len(path)
         res["accepted_nodes"][b, :len(path)] = path
         res["out_tokens"][b, :len(path)] = [int(tokens[b][c]) for c in path]

@@ -1,9 +1,11 @@
 """GPU parity of multi-round speculative sampling (through the C ABI) against
 the scalar fp64 oracle on the same Philox stream.
 
-Integers (accept_len, accepted_nodes, out_tokens) must match bit for bit; a
-sequence may only differ if a decision on its walk came within 1e-6 of its
-threshold (counted as a near tie by one side).  Flags must match.  Besides
+Integers (accept_len, accepted_nodes, out_tokens), flags and near-tie counts
+must match bit for bit; a sequence may only differ past the first decision on
+the oracle's walk that came within 1e-6 of its threshold (a near tie), and
+must agree on everything decided before it (tests/gpu_util.py,
+compare_accept).  Every test bounds how many sequences differ.  Besides
 parity: losslessness statistics over Philox offsets (chi-square vs the target
 distribution; chain closed form), determinism, and the edge cases.
 """
@@ -13,7 +15,7 @@ from scipy.special import softmax as sp_softmax
 from scipy.stats import chi2 as chi2_dist
 
 import synth
-from gpu_util import compare_accept, dev, log, make_verifier, run_accept, small_spec
+from gpu_util import compare_accept, dev, excused_bound, log, make_verifier, run_accept, small_spec
 from oracle import accept as oacc
 
 pytestmark = pytest.mark.gpu
@@ -51,8 +53,9 @@ def test_accept_matches_oracle(spec):
     for off in range(12):
         got = run_accept(ver, inp, spec.temperature, SEED, off)
         ref = _oracle(inp, spec.temperature, off)
-        diverged += compare_accept(got, ref, f"{spec.name} offset {off}")
+        diverged += compare_accept(got, ref, f"{spec.name} offset {off}", inp.parents, inp.tokens, spec.vocab)
     log(f"    near-tie divergences: {diverged}")
+    assert diverged <= excused_bound(12 * spec.batch)
     again = run_accept(ver, inp, spec.temperature, SEED, 11)
     for key in again:
         assert np.array_equal(again[key], got[key]), "not bitwise deterministic"
@@ -66,12 +69,15 @@ def test_accept_full_configs(cfg, temp):
     log(f"[accept] full size {spec.name} temperature {temp}")
     inp = synth.make_inputs(spec, with_kv=False)
     ver = make_verifier(spec, inp.T)
+    diverged = 0
     for off in range(3):
         got = run_accept(ver, inp, temp, SEED + cfg, off)
         ref = oacc.spec_accept(inp.target64(), None if temp == 0 else inp.draft64(), inp.parents, inp.tokens,
                                temp, SEED + cfg, off)
-        compare_accept(got, ref, f"{spec.name} offset {off}")
+        diverged += compare_accept(got, ref, f"{spec.name} offset {off}", inp.parents, inp.tokens, spec.vocab)
         log(f"    offset {off}: accept_len {got['accept_len'].tolist()} near ties {got['near_ties'].tolist()}")
+    log(f"    near-tie divergences: {diverged}")
+    assert diverged <= excused_bound(3 * spec.batch)
     ver.close()
 
 
@@ -100,7 +106,7 @@ def test_edge_cases_flags_and_poison():
     ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
     assert got["flags"].tolist() == ref["flags"].tolist() == [0, ev.FLAG_BAD_TREE, ev.FLAG_BAD_TOKEN,
                                                              ev.FLAG_NONFINITE, ev.FLAG_NONFINITE, 0]
-    compare_accept(got, ref, "edge")
+    assert compare_accept(got, ref, "edge", par, tok, V) == 0
     for b in (1, 2, 3, 4):
         assert got["accept_len"][b] == -1 and (got["out_tokens"][b] == -1).all()
     ver.close()
@@ -120,7 +126,7 @@ def test_p_zero_and_degenerate_residual():
     ver = make_verifier(spec.with_(batch=2), 3)
     got = run_accept(ver, inp, 1.0, SEED, 0, target=tgt, draft=drf, parents=par, tokens=tok)
     ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
-    compare_accept(got, ref, "p0")
+    assert compare_accept(got, ref, "p0", par, tok, 3) == 0
     assert got["flags"][0] & ev.FLAG_P_ZERO and got["flags"][0] & ev.FLAG_DEGENERATE_RESIDUAL
     assert got["accept_len"][0] == 1 and got["accepted_nodes"][0, 0] == 2
     # sequence 1: both children rejected (q = 0 at their token), residual 0 -> sample from q
@@ -136,13 +142,15 @@ def test_root_only_tree_draws_bonus_from_target():
     inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
     ver = make_verifier(spec, 1)
     counts = np.zeros(V)
+    diverged = 0
     for off in range(40):
         got = run_accept(ver, inp, 1.0, SEED, off)
         ref = _oracle(inp, 1.0, off)
-        compare_accept(got, ref, f"root-only {off}")
+        diverged += compare_accept(got, ref, f"root-only {off}", inp.parents, inp.tokens, V)
         assert (got["accept_len"] == 0).all()
         for b in range(B):
             counts[got["out_tokens"][b, 0]] += 1
+    assert diverged <= excused_bound(40 * B)
     ver.close()
 
 
@@ -163,16 +171,18 @@ def test_lossless_statistics_over_offsets():
     drf = np.tile(d_row, (B, 4, 1))
     ver = make_verifier(spec, 4)
     counts = np.zeros(V)
+    diverged = 0
     for off in range(K):
         tok = np.zeros((B, 4), dtype=np.int32)
         tok[:, 1:] = rng.choice(V, size=(B, 3), p=p)
         got = run_accept(ver, inp, 1.0, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok)
         ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, off)
-        compare_accept(got, ref, f"stats offset {off}")
+        diverged += compare_accept(got, ref, f"stats offset {off}", par, tok, V)
         counts += np.bincount(got["out_tokens"][:, 0], minlength=V)
     n = B * K
     stat = ((counts - n * q) ** 2 / (n * q)).sum()
-    log(f"    chi2 {stat:.2f} (99.9% critical {chi2_dist.ppf(0.999, V - 1):.2f})")
+    log(f"    chi2 {stat:.2f} (99.9% critical {chi2_dist.ppf(0.999, V - 1):.2f}), near-tie divergences {diverged}")
+    assert diverged <= excused_bound(n)
     assert stat < chi2_dist.ppf(0.999, V - 1)
     ver.close()
 
@@ -208,10 +218,12 @@ def test_large_batch_in_fused_slices():
     log(f"[accept] {spec.name}")
     inp = synth.make_inputs(spec, with_kv=False)
     ver = make_verifier(spec, inp.T)
+    diverged = 0
     for off in range(2):
         got = run_accept(ver, inp, 1.0, SEED, off)
         ref = _oracle(inp, 1.0, off)
-        compare_accept(got, ref, f"large batch offset {off}")
+        diverged += compare_accept(got, ref, f"large batch offset {off}", inp.parents, inp.tokens, spec.vocab)
+    assert diverged <= excused_bound(2 * spec.batch)
     ver.close()
 
 
@@ -232,7 +244,7 @@ def test_mixed_invalid_inputs_report_every_flag():
     got = run_accept(ver, inp, 1.0, SEED, 0, target=tgt, draft=drf, parents=par, tokens=tok)
     ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
     assert got["flags"].tolist() == ref["flags"].tolist() == [0, ev.FLAG_BAD_TOKEN | ev.FLAG_NONFINITE]
-    compare_accept(got, ref, "mixed")
+    assert compare_accept(got, ref, "mixed", par, tok, V) == 0
     ver.close()
 
 
@@ -258,14 +270,16 @@ def test_trees_of_different_sizes_in_one_batch(temp):
     sizes = [inp.T, 20, 9, 4, 2, 1]
     par, tok, tgt, drf = _pad(spec, inp, sizes)
     ver = make_verifier(spec, inp.T)
+    diverged = 0
     for off in range(4):
         got = run_accept(ver, inp, temp, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok)
         ref = oacc.spec_accept(synth.inputs.as_f64(tgt, spec.ldtype), None if temp == 0 else synth.inputs.as_f64(drf, spec.ldtype),
                                par, tok, temp, SEED, off)
         assert (ref["flags"] & 7).tolist() == [0] * spec.batch
-        compare_accept(got, ref, f"padded offset {off}")
+        diverged += compare_accept(got, ref, f"padded offset {off}", par, tok, spec.vocab)
         for b, n in enumerate(sizes):
             assert got["accept_len"][b] < n
+    assert diverged <= excused_bound(4 * spec.batch)
     ver.close()
 
 
@@ -279,12 +293,14 @@ def test_general_path_with_padded_trees():
     sizes = [inp.T, 23]
     par, tok, tgt, drf = _pad(spec, inp, sizes)
     ver = make_verifier(spec, inp.T)
+    diverged = 0
     for temp in (1.0, 0.0):
         for off in range(2):
             got = run_accept(ver, inp, temp, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok)
             ref = oacc.spec_accept(synth.inputs.as_f64(tgt, spec.ldtype),
                                    None if temp == 0 else synth.inputs.as_f64(drf, spec.ldtype), par, tok, temp, SEED, off)
-            compare_accept(got, ref, f"general temperature {temp} offset {off}")
+            diverged += compare_accept(got, ref, f"general temperature {temp} offset {off}", par, tok, spec.vocab)
+    assert diverged <= excused_bound(4 * spec.batch)
     ver.close()
 
 
@@ -319,16 +335,12 @@ def test_siblings_without_replacement(spec):
     ver = make_verifier(spec, inp.T)
     diverged = 0
     for off in range(6):
-        got = ver.spec_accept(*[dev(x, spec.ldtype) for x in (inp.target, inp.draft)], dev(inp.parents), dev(tok),
-                              spec.temperature, SEED, off, without_replacement=True)
-        import torch
-        torch.cuda.synchronize()
-        got = {k: v.cpu().numpy() for k, v in got.items()}
-        got["flags"] = got["flags"].astype(np.uint32)
+        got = run_accept(ver, inp, spec.temperature, SEED, off, tokens=tok, without_replacement=True)
         ref = oacc.spec_accept(inp.target64(), inp.draft64(), inp.parents, tok, spec.temperature, SEED, off,
                                without_replacement=True)
-        diverged += compare_accept(got, ref, f"{spec.name} offset {off}")
+        diverged += compare_accept(got, ref, f"{spec.name} offset {off}", inp.parents, tok, spec.vocab)
     log(f"    near-tie divergences: {diverged}")
+    assert diverged <= excused_bound(6 * spec.batch)
     ver.close()
 
 
@@ -338,16 +350,13 @@ def test_without_replacement_with_repeated_tokens():
     spec = small_spec("wr_repeats", dtype="f32", B=6, V=6, tree=("star", 8), sigma_d=1.0)
     inp = synth.make_inputs(spec, with_kv=False)
     ver = make_verifier(spec, inp.T)
+    diverged = 0
     for off in range(4):
-        got = ver.spec_accept(dev(inp.target), dev(inp.draft), dev(inp.parents), dev(inp.tokens), 1.0, SEED, off,
-                              without_replacement=True)
-        import torch
-        torch.cuda.synchronize()
-        got = {k: v.cpu().numpy() for k, v in got.items()}
-        got["flags"] = got["flags"].astype(np.uint32)
+        got = run_accept(ver, inp, 1.0, SEED, off, without_replacement=True)
         ref = oacc.spec_accept(inp.target64(), inp.draft64(), inp.parents, inp.tokens, 1.0, SEED, off,
                                without_replacement=True)
-        compare_accept(got, ref, f"repeats offset {off}")
+        diverged += compare_accept(got, ref, f"repeats offset {off}", inp.parents, inp.tokens, spec.vocab)
+    assert diverged <= excused_bound(4 * spec.batch)
     ver.close()
 
 
@@ -360,4 +369,41 @@ def test_without_replacement_needs_the_fused_path():
         ver.spec_accept(dev(inp.target, "bf16"), dev(inp.draft, "bf16"), dev(inp.parents), dev(inp.tokens), 1.0,
                         SEED, 0, without_replacement=True)
     assert "fused path" in str(e.value)
+    ver.close()
+
+
+def test_expected_accept_length_of_a_fixed_tree_on_gpu():
+    """The GPU's mean accepted length over Philox offsets equals the
+    probability flow of a fixed three-level tree (the same tree as the
+    oracle's pin), and every run equals the oracle."""
+    from test_oracle_accept import _expected_accept_len
+    log("[accept] probability flow of a fixed tree")
+    rng = np.random.default_rng(13)
+    V = 6
+    parents = np.array([-1, 0, 0, 0, 0, 1, 1, 5, 2], dtype=np.int32)
+    tokens = np.array([0, 1, 3, 2, 0, 2, 0, 5, 4], dtype=np.int32)
+    T = len(parents)
+    tgt = rng.standard_normal((T, V)) * 1.5
+    drf = tgt + rng.standard_normal((T, V)) * 1.5
+    tgt, drf = tgt.astype(np.float32), drf.astype(np.float32)
+    want = _expected_accept_len([sp_softmax(r) for r in tgt.astype(np.float64)],
+                                [sp_softmax(r) for r in drf.astype(np.float64)], parents, tokens)
+    B, K = 256, 16
+    spec = small_spec("flow", dtype="f32", B=B, V=V, tree=("chain", T - 1))
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
+    par, tok = np.tile(parents, (B, 1)), np.tile(tokens, (B, 1))
+    tg, dr = np.tile(tgt, (B, 1, 1)), np.tile(drf, (B, 1, 1))
+    ver = make_verifier(spec, T)
+    lens, diverged = [], 0
+    for off in range(K):
+        got = run_accept(ver, inp, 1.0, SEED, off, target=tg, draft=dr, parents=par, tokens=tok)
+        if off < 4:
+            ref = oacc.spec_accept(tg.astype(np.float64), dr.astype(np.float64), par, tok, 1.0, SEED, off)
+            diverged += compare_accept(got, ref, f"flow offset {off}", par, tok, V)
+        lens.append(got["accept_len"])
+    lens = np.concatenate(lens).astype(np.float64)
+    se = lens.std(ddof=1) / np.sqrt(len(lens))
+    log(f"    mean accepted {lens.mean():.4f} vs flow {want:.4f} (se {se:.4f})")
+    assert abs(lens.mean() - want) < 4.5 * se
+    assert diverged <= excused_bound(4 * B)
     ver.close()

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import ATTN_TOL, dev, log, make_verifier, oracle_rows_sampled, row_error, run_attention, small_spec
+from gpu_util import (ATTN_SENTINEL, ATTN_TOL, FLAGS_SENTINEL, dev, log, make_verifier, oracle_rows_sampled, row_error,
+                      run_attention, small_spec)
 from oracle import attention as oa
 from oracle import kv_commit as okc
 from oracle import paging as opg
@@ -31,11 +32,16 @@ CASES = [
 def _run_paged(ver, inp, kp, vp, table, P):
     import torch
     spec = inp.spec
+    B, T = inp.q.shape[:2]
+    out = torch.full((B, T, spec.q_heads, spec.head_dim), float(ATTN_SENTINEL), dtype=torch.float32, device="cuda")
+    flags = torch.full((B,), FLAGS_SENTINEL, dtype=torch.int32, device="cuda")
     out, flags = ver.tree_attention(dev(inp.q, spec.dtype), dev(kp, spec.dtype), dev(vp, spec.dtype), None,
                                     inp.prefix_lens, dev(inp.parents), 1.0 / np.sqrt(spec.head_dim),
-                                    page_table=dev(table), page_size=P)
+                                    out=out, flags=flags, page_table=dev(table), page_size=P)
     torch.cuda.synchronize()
-    return out.cpu().numpy().astype(np.float64), flags.cpu().numpy().astype(np.uint32)
+    got = out.cpu().numpy()
+    assert not (got == ATTN_SENTINEL).any(), "attention output rows left unwritten"
+    return got.astype(np.float64), flags.cpu().numpy().astype(np.uint32)
 
 
 @pytest.mark.parametrize("spec,P", CASES, ids=[c[0].name for c in CASES])

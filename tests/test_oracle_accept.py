@@ -408,6 +408,180 @@ def test_inv_cdf_definition():
     assert oacc.inv_cdf(w * 3.0, 0.5)[0] == 3     # unnormalised weights
 
 
+# ---------------------------------------------------------------------------
+# near-tie flags (several correct results: a decision within 1e-6 of its
+# threshold is flagged, lesson page build step 5 / EAGLE notes page core
+# mechanism §5 for the rule it guards).  The margins are relative to the
+# weights' total for an inverse-CDF sample and absolute for the ratio test
+# (r and the ratio are both on the [0, 1) scale there); both are strict.
+# ---------------------------------------------------------------------------
+def test_inv_cdf_near_tie_flags():
+    w = np.array([0.25, 0.25, 0.5])
+    cases = [                       # (u, token, near): boundary between tokens 0 and 1 at 0.25
+        (0.25 - 2e-6, 0, False),
+        (0.25 - 0.5e-6, 0, True),
+        (0.25, 1, True),            # exactly on it: strict > picks token 1, margin 0
+        (0.25 + 0.5e-6, 1, True),
+        (0.25 + 2e-6, 1, False),
+        (0.5 + 0.5e-6, 2, True),    # boundary between tokens 1 and 2: lower side of token 2
+        (0.5 - 0.5e-6, 1, True),    # ... upper side of token 1
+        (0.375, 1, False),          # the middle of token 1
+    ]
+    for scale in (1.0, 3.0, 1e3, 1e-3):     # relative to the total, not absolute
+        for u, tok, near in cases:
+            assert oacc.inv_cdf(w * scale, u) == (tok, near), (scale, u)
+    # strict: with a total of exactly 1 and the lower boundary 0, a margin of
+    # exactly 1e-6 is not a near tie, anything below it is
+    w2 = np.array([0.5, 0.5])
+    assert oacc.inv_cdf(w2, 1e-6) == (0, False)
+    assert oacc.inv_cdf(w2, np.nextafter(1e-6, 0.0)) == (0, True)
+    # a token whose weight is below 2e-6 of the total is always a near tie
+    # (both of its boundaries lie within 1e-6 of any draw that lands on it)
+    w3 = np.array([0.5, 1.5e-6, 0.5])
+    w3 = w3 / w3.sum()
+    for f in (0.1, 0.5, 0.9):
+        u = (w3[0] + f * w3[1])
+        assert oacc.inv_cdf(w3, u) == (1, True)
+    w4 = np.array([0.5, 3e-6, 0.5])
+    w4 = w4 / w4.sum()
+    assert oacc.inv_cdf(w4, w4[0] + 0.5 * w4[1]) == (1, False)
+
+
+def _scripted(draws):
+    def draw(node, slot):
+        return draws[(node, slot)]
+    return draw
+
+
+def test_ratio_test_near_tie_flags():
+    """Root with one child of token 0; q = (0.3, 0.7), p = (0.5, 0.5): the
+    ratio is 0.6; the child is a leaf, so its bonus sample follows."""
+    q = np.log([0.3, 0.7])
+    p = np.log([0.5, 0.5])
+    parents = np.array([-1, 0])
+    tokens = np.array([0, 0])
+    for r, acc, near in [(0.6 - 2e-6, True, 0), (0.6 - 0.5e-6, True, 1), (0.6 + 0.5e-6, False, 1),
+                         (0.6 + 2e-6, False, 0)]:
+        where = []
+        path, final, fl, nt = oacc.walk_sampled(lambda n: q, lambda n: p, parents, tokens, 1.0,
+                                                _scripted({(0, 0): r, (0, philox.SAMPLE_SLOT): 0.5,
+                                                           (1, philox.SAMPLE_SLOT): 0.5}), where=where)
+        assert (path == [1]) == acc and nt == near and fl == 0, r
+        assert where == ([(0, 0)] if near else [])
+        if not acc:
+            assert final == 1       # the residual max(0, q - p) = (0, 0.2) puts all its mass on token 1
+    # absolute margin: a ratio of 1e-3 is flagged for r within 1e-6 of it
+    q_small = np.log([1e-3 * 0.5, 1 - 1e-3 * 0.5])
+    for r, near in [(1e-3 + 0.5e-6, 1), (1e-3 - 0.5e-6, 1), (1e-3 + 2e-6, 0)]:
+        _, _, _, nt = oacc.walk_sampled(lambda n: q_small, lambda n: p, parents, tokens, 1.0,
+                                        _scripted({(0, 0): r, (0, philox.SAMPLE_SLOT): 0.7,
+                                                   (1, philox.SAMPLE_SLOT): 0.7}))
+        assert nt == near, r
+    # strict: q(t) = 0 makes the ratio 0; r = 1e-6 exactly is not a near tie
+    q_zero = np.array([-np.inf, 0.0])
+    for r, near in [(1e-6, 0), (np.nextafter(1e-6, 0.0), 1)]:
+        path, _, _, nt = oacc.walk_sampled(lambda n: q_zero, lambda n: p, parents, tokens, 1.0,
+                                           _scripted({(0, 0): r, (0, philox.SAMPLE_SLOT): 0.5}))
+        assert path == [] and nt == near, r
+
+
+def test_near_tie_is_measured_against_the_current_residual():
+    """Two siblings, tokens 2 then 1; q = (0.4, 0.35, 0.25), p = (0.2, 0.3, 0.5).
+    The first is rejected (ratio 0.5, r = 0.9); the residual is then
+    norm(max(0, q - p)) = (0.8, 0.2, 0), so the second sibling's ratio is
+    0.2 / 0.3 = 2/3, not q(1)/p(1) = 7/6."""
+    q = np.log([0.4, 0.35, 0.25])
+    p = np.log([0.2, 0.3, 0.5])
+    parents = np.array([-1, 0, 0])
+    tokens = np.array([0, 2, 1])
+    for r, acc, near in [(2 / 3 - 0.5e-6, True, 1), (2 / 3 + 0.5e-6, False, 1), (2 / 3 + 2e-6, False, 0),
+                         (7 / 6 - 1.0, True, 0)]:
+        where = []
+        path, _, _, nt = oacc.walk_sampled(lambda n: q, lambda n: p, parents, tokens, 1.0,
+                                           _scripted({(0, 0): 0.9, (0, 1): r, (0, philox.SAMPLE_SLOT): 0.31,
+                                                      (2, philox.SAMPLE_SLOT): 0.31}), where=where)
+        assert (path == [2]) == acc and nt == near, r
+        assert where == ([(0, 1)] if near else [])
+
+
+def test_first_near_tie_is_located_on_the_walk():
+    """Chain root -> 1 -> 2 (tokens 0, 0), q = (0.3, 0.7), p = (0.5, 0.5):
+    node 1 is accepted far from its threshold, node 2's test is a near tie
+    (rejected), then the residual sample; spec_accept reports depth 1, slot 0.
+    A near tie on a terminal sample reports slot -1."""
+    V = 2
+    tgt = np.tile(np.log([0.3, 0.7]), (1, 3, 1))
+    drf = np.tile(np.log([0.5, 0.5]), (1, 3, 1))
+    parents = np.array([[-1, 0, 1]])
+    tokens = np.array([[0, 0, 0]])
+    draws = {(0, 0, 0): 0.1, (0, 1, 0): 0.6 + 0.5e-6, (0, 1, philox.SAMPLE_SLOT): 0.5}
+    res = oacc.spec_accept(tgt, drf, parents, tokens, 1.0, 0, 0, draw=lambda b, n, s: draws[(b, n, s)])
+    assert res["accept_len"][0] == 1 and res["out_tokens"][0, :2].tolist() == [0, 1]
+    assert res["near_ties"][0] == 1
+    assert (res["first_near_depth"][0], res["first_near_slot"][0]) == (1, 0)
+    # both tests accepted far away; the bonus sample at leaf 2 lands 0.5e-6
+    # above the boundary at 0.3 between tokens 0 and 1
+    draws = {(0, 0, 0): 0.1, (0, 1, 0): 0.2, (0, 2, philox.SAMPLE_SLOT): 0.3 + 0.5e-6}
+    res = oacc.spec_accept(tgt, drf, parents, tokens, 1.0, 0, 0, draw=lambda b, n, s: draws[(b, n, s)])
+    assert res["accept_len"][0] == 2 and res["out_tokens"][0].tolist() == [0, 0, 1]
+    assert (res["first_near_depth"][0], res["first_near_slot"][0]) == (2, -1)
+    # no near tie anywhere
+    draws = {(0, 0, 0): 0.1, (0, 1, 0): 0.2, (0, 2, philox.SAMPLE_SLOT): 0.5}
+    res = oacc.spec_accept(tgt, drf, parents, tokens, 1.0, 0, 0, draw=lambda b, n, s: draws[(b, n, s)])
+    assert res["near_ties"][0] == 0 and (res["first_near_depth"][0], res["first_near_slot"][0]) == (-1, -1)
+    assert V == tgt.shape[-1]
+
+
+def _expected_accept_len(q_rows, p_rows, parents, tokens):
+    """Probability flow through a tree whose tokens are fixed: the i-th child
+    of n is accepted with probability a_i * prod_{j<i} (1 - a_j), where
+    a_i = min(1, q_i(t_i) / p(t_i)) and q_i is the residual left after the
+    i-1 rejections before it (the rule of the EAGLE notes page, core
+    mechanism §5).  Returns E[accepted nodes]."""
+    T = len(parents)
+    kids = [[c for c in range(1, T) if parents[c] == n] for n in range(T)]
+
+    def flow(n):
+        q, p = q_rows[n], p_rows[n]
+        res, reach, total = q.copy(), 1.0, 0.0
+        for c in kids[n]:
+            t = tokens[c]
+            a = min(1.0, res[t] / p[t])
+            total += reach * a * (1.0 + flow(c))
+            reach *= 1.0 - a
+            res = np.maximum(0.0, res - p)
+            res = res / res.sum()
+        return total
+    return flow(0)
+
+
+def test_expected_accept_length_of_a_fixed_tree():
+    """Pin P8: the walk's mean accepted length over Philox uniforms equals the
+    probability flow of a fixed three-level tree with distinct rows per node."""
+    # chosen so that a walk without the residual update (E = 2.29) or with a
+    # residual taken afresh from q at every rejection (E = 2.22) is far off
+    rng = np.random.default_rng(13)
+    V = 6
+    parents = np.array([-1, 0, 0, 0, 0, 1, 1, 5, 2])
+    tokens = np.array([0, 1, 3, 2, 0, 2, 0, 5, 4])
+    T = len(parents)
+    tgt = rng.standard_normal((T, V)) * 1.5
+    drf = tgt + rng.standard_normal((T, V)) * 1.5
+    q_rows = [sp_softmax(r) for r in tgt]
+    p_rows = [sp_softmax(r) for r in drf]
+    want = _expected_accept_len(q_rows, p_rows, parents, tokens)
+    B, K = 64, 60
+    lens = []
+    for off in range(K):
+        res = oacc.spec_accept(np.tile(tgt, (B, 1, 1)), np.tile(drf, (B, 1, 1)), np.tile(parents, (B, 1)),
+                               np.tile(tokens, (B, 1)), 1.0, 77, off)
+        lens.append(res["accept_len"])
+    lens = np.concatenate(lens).astype(np.float64)
+    se = lens.std(ddof=1) / np.sqrt(len(lens))
+    assert abs(want - 1.9778) < 1e-3
+    assert abs(lens.mean() - want) < 4.5 * se, (lens.mean(), want, se)
+
+
 def test_residual_closed_form_matches_iteration():
     """The GPU's division-free form of the cumulative residual:
     after i rejections q_res = max(0, q - C_i p) / s_i with C_1 = 0, s_1 = 1,
