@@ -428,8 +428,10 @@ __global__ __launch_bounds__(64) void te_rerank(const RerankKernelArgs a) {
   }
   int32_t* const par = a.parents + static_cast<int64_t>(b) * (N + 1);
   int32_t* const tok = a.tokens + static_cast<int64_t>(b) * (N + 1);
+  // rows past the last kept node are padding: token -1 under a valid parent
+  // (the root), which is how trees of different sizes share a batch
   for (int i = lane; i <= N; i += 64) {
-    par[i] = -1;
+    par[i] = i == 0 ? -1 : 0;
     tok[i] = -1;
   }
   __syncthreads();

@@ -294,8 +294,9 @@ typedef struct {
  * never exceeds its parent's, so every kept node's parent is kept.
  * Outputs (device): parents/tokens [B, nodes + 1]: row 0 the root (parent -1,
  * token root_tokens[b]), then the kept nodes in (step, rank) order, parents
- * before children (the layout tree_attention and spec_accept read), rows
- * past the last kept node -1; rows [B] = 1 + kept nodes.
+ * before children (the layout tree_attention and spec_accept read); rows
+ * past the last kept node are padding rows (parent 0, token -1), which both
+ * calls accept as a tree of rows[b] rows; rows [B] = 1 + kept nodes.
  * Limits: steps <= 64, keep <= 64, nodes + 1 <= max_tree_rows. */
 typedef struct {
   int32_t batch;

@@ -104,11 +104,13 @@ def rerank(parent, token, value, root_tokens, N):
     Output rows: 0 = the root (parent -1, token root_tokens[b]), then the
     kept nodes in (step, rank) order, so parents precede children.
     Returns dict(parents [B, N+1], tokens [B, N+1], rows [B]); rows past
-    `rows` hold parent -1, token -1."""
+    `rows` are padding rows, parent 0 and token -1 (the padding of a tree
+    that shares a batch with larger ones: a valid parent, token -1)."""
     parent = np.asarray(parent)
     value = np.asarray(value, dtype=np.float64)
     D, B, M = parent.shape
-    parents = np.full((B, N + 1), -1, dtype=np.int32)
+    parents = np.zeros((B, N + 1), dtype=np.int32)
+    parents[:, 0] = -1
     tokens = np.full((B, N + 1), -1, dtype=np.int32)
     rows = np.zeros(B, dtype=np.int32)
     for b in range(B):

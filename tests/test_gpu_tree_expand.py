@@ -160,3 +160,68 @@ def test_rerank_of_chained_oracle_steps(seed):
             assert np.array_equal(got[key].cpu().numpy(), want[key]), (N, key)
     log(f"  rerank seed {seed}: rows {want['rows'].tolist()}")
     ver.close()
+
+
+def test_short_rerank_output_feeds_verification():
+    """A rerank with fewer candidates than rows: its output goes straight into
+    spec_accept and tree_attention on the device; the padding rows (parent 0,
+    token -1) are accepted as padding and both calls match the oracle."""
+    import torch
+    from gpu_util import (ATTN_SENTINEL, ATTN_TOL, compare_accept, host_accept, row_error,
+                          sentinel_accept_outputs)
+    from oracle import accept as oacc
+    from oracle import attention as oatt
+    rng = np.random.default_rng(41)
+    B, V, N = 3, 700, 60
+    steps = [(4, 6), (3, 8), (3, 8), (2, 8)]
+    fr = np.zeros((B, 1))
+    P = np.full((len(steps), B, 8), -1, dtype=np.int32)
+    T = np.full((len(steps), B, 8), -1, dtype=np.int32)
+    Vv = np.full((len(steps), B, 8), -np.inf, dtype=np.float32)
+    for d, (k, M) in enumerate(steps):
+        out = ote.expand(_logits(rng, B, fr.shape[1], V, scale=2.0), fr, 1.0, k, M)
+        P[d, :, :M], T[d, :, :M], Vv[d, :, :M] = out["parent"], out["token"], out["value"].astype(np.float32)
+        fr = out["value"]
+    roots = np.array([5, 6, 7], dtype=np.int32)
+    ver = _verifier(B, N + 1, V, "f32")
+    tree = ver.tree_rerank(dev(P), dev(T), dev(Vv), dev(roots), N)
+    par_h, tok_h = tree["parents"].cpu().numpy(), tree["tokens"].cpu().numpy()
+    rows = tree["rows"].cpu().numpy()
+    assert (rows < N + 1).all() and (par_h[:, rows[0]:] == 0).all() and (tok_h[:, rows[0]:] == -1).all()
+    tgt = (rng.standard_normal((B, N + 1, V)) * 2).astype(np.float32)
+    drf = (tgt + rng.standard_normal((B, N + 1, V)) * 0.7).astype(np.float32)
+    for temp in (1.0, 0.0):
+        for off in range(3):
+            got = ver.spec_accept(dev(tgt), dev(drf), tree["parents"], tree["tokens"], temp, 0x5EED0000, off,
+                                  outputs=sentinel_accept_outputs(B, N + 1))
+            torch.cuda.synchronize()
+            got = host_accept(got)
+            ref = oacc.spec_accept(tgt.astype(np.float64), None if temp == 0 else drf.astype(np.float64),
+                                   par_h, tok_h, temp, 0x5EED0000, off)
+            assert (ref["flags"] & 7).tolist() == [0] * B and (got["flags"] & 7).tolist() == [0] * B
+            assert compare_accept(got, ref, f"rerank tree temperature {temp} offset {off}", par_h, tok_h, V) <= 1
+    # tree attention over the same padded trees (bf16, 8 heads, prefix 100)
+    Hq = Hkv = 8
+    D, L, Tr = 128, 100, N + 1
+    q_bits, q32 = _to_dtype(rng.standard_normal((B, Tr, Hq, D)).astype(np.float32), "bf16")
+    k_bits, k32 = _to_dtype(rng.standard_normal((B * (L + Tr), Hkv, D)).astype(np.float32), "bf16")
+    v_bits, v32 = _to_dtype(rng.standard_normal((B * (L + Tr), Hkv, D)).astype(np.float32), "bf16")
+    indptr = np.arange(B + 1, dtype=np.int64) * (L + Tr)
+    out = torch.full((B, Tr, Hq, D), float(ATTN_SENTINEL), dtype=torch.float32, device="cuda")
+    out, flags = ver.tree_attention(dev(q_bits, "bf16"), dev(k_bits, "bf16"), dev(v_bits, "bf16"), dev(indptr),
+                                    [L] * B, tree["parents"], out=out)
+    torch.cuda.synchronize()
+    assert flags.cpu().numpy().tolist() == [0] * B
+    got = out.cpu().numpy().astype(np.float64)
+    assert not (got == ATTN_SENTINEL).any()
+    scale = 1.0 / np.sqrt(D)
+    for b in range(B):
+        kb = k32[b * (L + Tr):(b + 1) * (L + Tr)].astype(np.float64)
+        vb = v32[b * (L + Tr):(b + 1) * (L + Tr)].astype(np.float64)
+        for i in range(int(rows[b])):
+            for h in range(Hq):
+                ref = oatt.node_head_output(q32[b, i, h].astype(np.float64), kb[:, h], vb[:, h], L, par_h[b], i,
+                                            scale)
+                assert row_error(got[b, i, h], ref) < ATTN_TOL["bf16"], (b, i, h)
+    log(f"  rerank tree rows {rows.tolist()} verified")
+    ver.close()

@@ -166,4 +166,46 @@ def test_rerank_keeps_everything_when_n_is_large():
     out = ote.rerank(P, T, V, np.zeros(2, dtype=np.int32), 40)
     n = int((P >= 0).sum(axis=(0, 2))[0])
     assert out["rows"][0] == n + 1
-    assert out["parents"][0][n + 1:].tolist() == [-1] * (40 - n)
+    assert out["parents"][0][n + 1:].tolist() == [0] * (40 - n)      # padding rows: parent 0, token -1
+    assert out["tokens"][0][n + 1:].tolist() == [-1] * (40 - n)
+
+
+def test_short_rerank_output_is_a_padded_tree_for_verification():
+    """Fewer candidates than rows: the rows past the kept nodes are padding
+    that the acceptance walk accepts (no flag) with the result of the tree
+    without them, and tree attention computes the real rows unchanged."""
+    from oracle import accept as oacc
+    from oracle import attention as oatt
+    from oracle import philox
+    P, T, V = _chain_of_steps(22)
+    N = 40
+    out = ote.rerank(P, T, V, np.array([3, 4], dtype=np.int32), N)
+    rows = out["rows"]
+    assert (rows < N + 1).all()
+    rng = np.random.default_rng(5)
+    B, Vv = 2, 50
+    tgt = rng.standard_normal((B, N + 1, Vv)) * 2
+    drf = tgt + rng.standard_normal((B, N + 1, Vv)) * 0.7
+    toks = np.where(out["tokens"] >= 0, out["tokens"] % Vv, -1).astype(np.int32)
+    toks[:, 0] = out["tokens"][:, 0]
+    for temp in (1.0, 0.0):
+        full = oacc.spec_accept(tgt, None if temp == 0 else drf, out["parents"], toks, temp, 11, 0)
+        assert (full["flags"] & 7).tolist() == [0, 0]
+        for b in range(B):
+            n = int(rows[b])
+            # the same uniforms: the sequence keeps its index in the batch
+            alone = oacc.spec_accept(tgt[b:b + 1, :n], None if temp == 0 else drf[b:b + 1, :n],
+                                     out["parents"][b:b + 1, :n], toks[b:b + 1, :n], temp, 11, 0,
+                                     draw=lambda _b, nd, sl, bb=b: philox.uniform(11, 0, bb, nd, sl))
+            assert full["accept_len"][b] == alone["accept_len"][0]
+            assert full["out_tokens"][b, :n].tolist() == alone["out_tokens"][0].tolist()
+    # attention: a padded row's parent is the root, a valid tree
+    L, D = 16, 8
+    k = rng.standard_normal((L + N + 1, D))
+    v = rng.standard_normal((L + N + 1, D))
+    q = rng.standard_normal(D)
+    n = int(rows[0])
+    for i in range(1, n):
+        full_o = oatt.node_head_output(q, k, v, L, out["parents"][0], i, 0.3)
+        part_o = oatt.node_head_output(q, k[:L + n], v[:L + n], L, out["parents"][0][:n], i, 0.3)
+        assert np.allclose(full_o, part_o, rtol=0, atol=1e-14)
