@@ -20,7 +20,7 @@ EXPORTED_SYMBOLS = (
     "eagle_verify_destroy", "eagle_verify_last_error", "eagle_verify_check_tree_attention",
     "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan", "eagle_verify_kv_commit",
     "eagle_verify_check_kv_commit", "eagle_verify_tree_expand", "eagle_verify_check_tree_expand",
-    "eagle_verify_tree_rerank", "eagle_verify_check_tree_rerank",
+    "eagle_verify_tree_rerank", "eagle_verify_check_tree_rerank", "eagle_verify_spec_accept_noalloc",
 )
 
 
@@ -90,6 +90,8 @@ def bind(lib):
     lib.eagle_verify_tree_attention.restype = C.c_int
     lib.eagle_verify_spec_accept.argtypes = [H, C.POINTER(SpecAcceptArgs), C.c_void_p]
     lib.eagle_verify_spec_accept.restype = C.c_int
+    lib.eagle_verify_spec_accept_noalloc.argtypes = [C.POINTER(VerifyDesc), C.POINTER(SpecAcceptArgs), C.c_void_p]
+    lib.eagle_verify_spec_accept_noalloc.restype = C.c_int
     lib.eagle_verify_destroy.argtypes = [H]
     lib.eagle_verify_destroy.restype = C.c_int
     lib.eagle_verify_last_error.argtypes = [H]

@@ -21,13 +21,11 @@ struct eagle_verify {
   void* base = nullptr;
   hipStream_t last_stream = nullptr;
   bool used = false;
-  uint64_t epoch = 0;          // acceptance calls issued on this handle
+  ev::AcceptCallState accept_state;   // acceptance epochs and round-word halves
   uint64_t attn_epoch = 0;     // attention calls issued on this handle
   eagle_attention_plan last_plan{};         // of the last successful tree_attention call
   bool have_plan = false;
   int attn_cap[2][ev::kMfmaVariants] = {};   // co-resident MFMA attention workgroups [D == 128][kernel variant]
-  uint64_t fused_calls = 0;    // of which took the fused path
-  int last_fused_b = 0;        // batch of the last fused call (its round words need clearing)
   int fused_cap[2] = {0, 0};   // co-resident fused-acceptance workgroups (f32, bf16)
   char err[512] = {0};
 };
@@ -41,11 +39,13 @@ void set_err(eagle_verify* h, const char* msg) {
   std::snprintf(dst, 512, "%s", msg);
 }
 
-eagle_status hip_fail(eagle_verify* h, const char* what, int code) {
-  char buf[512];
-  std::snprintf(buf, sizeof(buf), "%s failed: %s (%d)", what, hipGetErrorString(static_cast<hipError_t>(code)), code);
-  set_err(h, buf);
+eagle_status hip_fail_to(char* dst, size_t len, const char* what, int code) {
+  std::snprintf(dst, len, "%s failed: %s (%d)", what, hipGetErrorString(static_cast<hipError_t>(code)), code);
   return EAGLE_ERR_HIP;
+}
+
+eagle_status hip_fail(eagle_verify* h, const char* what, int code) {
+  return hip_fail_to(h ? h->err : g_err, 512, what, code);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -63,6 +63,134 @@ void public_plan(const ev::AttnPlan& p, eagle_attention_plan* plan) {
 }
 
 }  // namespace
+
+namespace ev {
+
+size_t accept_layout(int64_t Bm, int64_t Tm, int NC, size_t off, char* base, Workspace* ws) {
+  const size_t o_stats = off;
+  // per (sequence, node, row, chunk): a ChunkStat (three-kernel path) or four
+  // tagged 64-bit words (fused path)
+  off = align_up(off + std::max(sizeof(ChunkStat), 4 * sizeof(uint64_t)) * Bm * Tm * 2 * NC, 256);
+  const size_t o_nodes = off;
+  off = align_up(off + sizeof(NodeState) * Bm * Tm, 256);
+  const size_t o_fpart = off;
+  off = align_up(off + sizeof(double) * 2 * Bm * Tm * NC, 256);   // two round buffers
+  const size_t o_spart = off;
+  off = align_up(off + sizeof(uint64_t) * 4 * Bm * Tm * NC, 256);   // fused: four tagged words per chunk
+  const size_t o_cnt = off;
+  off = align_up(off + sizeof(uint32_t) * (2 * Bm * Tm + Bm), 256);
+  const size_t o_sync = off;   // one publication word per node, contiguous per sequence
+  off = align_up(off + sizeof(uint64_t) * Bm * Tm, 256);
+  const size_t o_round = off;
+  off = align_up(off + sizeof(uint64_t) * 2 * Bm * Tm * kRoundWords, 256);
+  if (base && ws) {
+    ws->stats = reinterpret_cast<ChunkStat*>(base + o_stats);
+    ws->nodes = reinterpret_cast<NodeState*>(base + o_nodes);
+    ws->fpart = reinterpret_cast<double*>(base + o_fpart);
+    ws->spart = reinterpret_cast<double*>(base + o_spart);
+    ws->counters = reinterpret_cast<uint32_t*>(base + o_cnt);
+    ws->node_pub = reinterpret_cast<uint64_t*>(base + o_sync);
+    ws->round_sum = reinterpret_cast<uint64_t*>(base + o_round);
+  }
+  return off;
+}
+
+void set_thread_error(const char* msg) { std::snprintf(g_err, sizeof(g_err), "%s", msg); }
+
+eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws, int64_t Bm, int64_t Tm,
+                             int64_t cap, AcceptCallState* cs, const eagle_spec_accept_args* a, void* hip_stream,
+                             char* err, size_t errlen) {
+  AcceptKernelArgs k;
+  std::memset(&k, 0, sizeof(k));
+  const int V = desc.vocab_size;
+  const int bf16 = desc.logits_dtype == EAGLE_BF16 ? 1 : 0;
+  const int esize = bf16 ? 2 : 4;
+  k.target = a->target_logits;
+  k.draft = a->draft_logits ? a->draft_logits : a->target_logits;
+  k.parents = a->parents;
+  k.tokens = a->tokens;
+  k.accept_len = a->accept_len;
+  k.accepted_nodes = a->accepted_nodes;
+  k.out_tokens = a->out_tokens;
+  k.flags = a->flags;
+  k.near_ties = a->near_ties;
+  k.stats = ws.stats;
+  k.nodes = ws.nodes;
+  k.fpart = ws.fpart;
+  k.spart = ws.spart;
+  k.cnt_stats = ws.counters;
+  k.cnt_pass = ws.counters + Bm * Tm;
+  k.cnt_final = ws.counters + 2 * Bm * Tm;
+  k.B = a->batch;
+  k.T = a->tree_rows;
+  k.V = V;
+  k.NC = vocab_chunks(V);
+  k.vec_ok = ((static_cast<int64_t>(V) * esize) % 16) == 0 ? 1 : 0;
+  k.tau = a->temperature;
+  k.c2 = a->temperature > 0.f ? static_cast<float>(1.4426950408889634 / a->temperature) : 0.f;
+  k.inv_tau = a->temperature > 0.f ? 1.0 / static_cast<double>(a->temperature) : 0.0;
+  k.seed_lo = static_cast<uint32_t>(a->seed);
+  k.seed_hi = static_cast<uint32_t>(a->seed >> 32);
+  k.off_lo = static_cast<uint32_t>(a->offset);
+  k.off_hi = static_cast<uint32_t>(a->offset >> 32);
+  k.node_pub = ws.node_pub;
+  k.Tm = static_cast<int>(Tm);
+  k.epoch = ++cs->epoch;
+  k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)
+  // The fused kernel needs every workgroup of a launch resident at once.  A
+  // batch that does not fit is verified in slices of whole sequences, one
+  // fused launch each, back to back on the stream (each slice is a fused
+  // call of its own: its own epoch and round-word half); the uniforms keep
+  // the sequence's index in the whole batch.  Only a single sequence that
+  // does not fit takes the three-kernel path.
+  const int64_t per_seq = static_cast<int64_t>(k.T) * k.NC;
+  k.wr = (a->without_replacement && a->temperature > 0.f) ? 1 : 0;
+  if (per_seq > cap || k.NC > 64) {
+    if (k.wr) {
+      std::snprintf(err, errlen,
+                    "siblings without replacement need the fused path: %lld workgroups per sequence, %lld resident",
+                    static_cast<long long>(per_seq), static_cast<long long>(cap));
+      return EAGLE_ERR_UNSUPPORTED;
+    }
+    k.fused = 0;
+    const int e = launch_spec_accept(k, bf16, hip_stream);
+    if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
+    return EAGLE_OK;
+  }
+  const int slice = static_cast<int>(std::min<int64_t>(k.B, cap / per_seq));
+  const int64_t row_bytes = static_cast<int64_t>(V) * esize;
+  const AcceptKernelArgs whole = k;
+  for (int b0 = 0; b0 < whole.B; b0 += slice) {
+    k = whole;
+    k.fused = 1;
+    k.b0 = b0;
+    k.B = std::min(slice, whole.B - b0);
+    const int64_t rows0 = static_cast<int64_t>(b0) * whole.T;
+    k.target = static_cast<const char*>(whole.target) + rows0 * row_bytes;
+    if (whole.draft) k.draft = static_cast<const char*>(whole.draft) + rows0 * row_bytes;
+    k.parents = whole.parents + rows0;
+    k.tokens = whole.tokens + rows0;
+    k.accept_len = whole.accept_len + b0;
+    k.accepted_nodes = whole.accepted_nodes + rows0;
+    k.out_tokens = whole.out_tokens + rows0;
+    k.flags = whole.flags + b0;
+    k.near_ties = whole.near_ties + b0;
+    k.epoch = b0 == 0 ? whole.epoch : ++cs->epoch;
+    // the two halves of the round words alternate between fused launches
+    const int64_t half = Bm * Tm * kRoundWords;
+    const int parity = static_cast<int>(cs->fused_calls & 1);
+    k.round_sum = ws.round_sum + parity * half;
+    k.round_clear = ws.round_sum + (1 - parity) * half;
+    k.zero_b = cs->last_fused_b;
+    const int e = launch_spec_accept(k, bf16, hip_stream);
+    if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
+    ++cs->fused_calls;
+    cs->last_fused_b = k.B;
+  }
+  return EAGLE_OK;
+}
+
+}  // namespace ev
 
 extern "C" {
 
@@ -98,31 +226,11 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   size_t off = 0;
   const size_t o_part = off;
   off = align_up(off + sizeof(float) * static_cast<size_t>(ev::kAttnPartFloats), 256);
-  const size_t o_stats = off;
-  // per (sequence, node, row, chunk): a ChunkStat (three-kernel path) or four
-  // tagged 64-bit words (fused path)
-  const size_t stats_bytes = std::max(sizeof(ev::ChunkStat), 4 * sizeof(uint64_t)) * B * T * 2 * NC;
-  off = align_up(off + stats_bytes, 256);
-  const size_t o_nodes = off;
-  off = align_up(off + sizeof(ev::NodeState) * B * T, 256);
-  const size_t o_fpart = off;
-  off = align_up(off + sizeof(double) * 2 * B * T * NC, 256);   // two round buffers
-  const size_t o_spart = off;
-  const size_t spart_bytes = sizeof(uint64_t) * 4 * B * T * NC;   // fused: four tagged words per chunk
-  off = align_up(off + spart_bytes, 256);
   const size_t o_expand = off;   // tree-expansion chunk records
   const int64_t nce = std::min<int64_t>(ev::expand_chunks(desc->vocab_size), ev::kMaxChunksExpand);
   off = align_up(off + sizeof(ev::ChunkRecord) * B * T * nce, 256);
-  const size_t o_cnt = off;
-  const size_t cnt_bytes = sizeof(uint32_t) * (2 * B * T + B);
-  off = align_up(off + cnt_bytes, 256);
-  const size_t o_sync = off;
-  // one publication word per node, contiguous per sequence
-  const size_t sync_bytes = sizeof(uint64_t) * B * T;
-  off = align_up(off + sync_bytes, 256);
-  const size_t o_round = off;
-  const size_t round_bytes = sizeof(uint64_t) * 2 * B * T * ev::kRoundWords;
-  off = align_up(off + round_bytes, 256);
+  const size_t o_accept = off;
+  off = ev::accept_layout(B, T, static_cast<int>(NC), o_accept, nullptr, nullptr);
 
   e = hipMalloc(&h->base, off);
   if (e != hipSuccess) {
@@ -132,14 +240,8 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   }
   char* p = static_cast<char*>(h->base);
   h->ws.attn_part = reinterpret_cast<float*>(p + o_part);
-  h->ws.stats = reinterpret_cast<ev::ChunkStat*>(p + o_stats);
-  h->ws.nodes = reinterpret_cast<ev::NodeState*>(p + o_nodes);
-  h->ws.fpart = reinterpret_cast<double*>(p + o_fpart);
-  h->ws.spart = reinterpret_cast<double*>(p + o_spart);
-  h->ws.counters = reinterpret_cast<uint32_t*>(p + o_cnt);
   h->ws.expand = reinterpret_cast<ev::ChunkRecord*>(p + o_expand);
-  h->ws.node_pub = reinterpret_cast<uint64_t*>(p + o_sync);
-  h->ws.round_sum = reinterpret_cast<uint64_t*>(p + o_round);
+  ev::accept_layout(B, T, static_cast<int>(NC), o_accept, p, &h->ws);
   h->ws.bytes = off;
   h->fused_cap[0] = ev::fused_accept_capacity(0, h->num_cus);
   h->fused_cap[1] = ev::fused_accept_capacity(1, h->num_cus);
@@ -148,19 +250,18 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   if (desc->kv_dtype == EAGLE_BF16 && !(fm && fm[0] == '0'))
     for (int v = 0; v < ev::kMfmaVariants; ++v)
       h->attn_cap[desc->head_dim == 128 ? 1 : 0][v] = ev::attention_capacity(desc->head_dim, v, h->num_cus);
-  // counters start at zero; every call leaves them at zero again.  On the
-  // fused path, publication, statistics and chunk-mass words carry the call
-  // epoch, and each fused call clears the round words the previous one used.
-  // The attention partials start at zero so that no tagged m/l word holds a
-  // call's epoch before that call writes it.
-  e = hipMemset(h->ws.counters, 0, cnt_bytes);
-  if (e == hipSuccess) e = hipMemset(h->ws.attn_part, 0, sizeof(float) * static_cast<size_t>(ev::kAttnPartFloats));
-  if (e == hipSuccess) e = hipMemset(h->ws.node_pub, 0, sync_bytes);
-  if (e == hipSuccess) e = hipMemset(h->ws.spart, 0, spart_bytes);
-  if (e == hipSuccess) e = hipMemset(h->ws.round_sum, 0, round_bytes);
-  if (e == hipSuccess) e = hipMemset(h->ws.nodes, 0, sizeof(ev::NodeState) * B * T);
-  if (e == hipSuccess) e = hipMemset(h->ws.stats, 0, stats_bytes);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
+  // The whole workspace starts at zero: counters (every call leaves them at
+  // zero again), the fused path's publication, statistics and chunk-mass
+  // words (tagged with the call epoch; each fused call clears the round words
+  // the previous one used), and the attention partials (no tagged m/l word
+  // holds a call's epoch before that call writes it).  The clear runs on a
+  // private stream that is waited for here, so no device-wide
+  // synchronisation is needed and the first call may use any stream.
+  hipStream_t init = nullptr;
+  e = hipStreamCreateWithFlags(&init, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipMemsetAsync(h->base, 0, off, init);
+  if (e == hipSuccess) e = hipStreamSynchronize(init);
+  if (init) (void)hipStreamDestroy(init);
   if (e != hipSuccess) {
     hip_fail(nullptr, "workspace initialisation", e);
     (void)hipFree(h->base);
@@ -260,102 +361,13 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   }
   eagle_status st = ev::check_spec_accept(&h->desc, a, h->err, sizeof(h->err));
   if (st != EAGLE_OK) return st;
-  ev::AcceptKernelArgs k;
-  std::memset(&k, 0, sizeof(k));
-  const int V = h->desc.vocab_size;
-  const int esize = h->desc.logits_dtype == EAGLE_BF16 ? 2 : 4;
-  k.target = a->target_logits;
-  k.draft = a->draft_logits ? a->draft_logits : a->target_logits;
-  k.parents = a->parents;
-  k.tokens = a->tokens;
-  k.accept_len = a->accept_len;
-  k.accepted_nodes = a->accepted_nodes;
-  k.out_tokens = a->out_tokens;
-  k.flags = a->flags;
-  k.near_ties = a->near_ties;
-  k.stats = h->ws.stats;
-  k.nodes = h->ws.nodes;
-  k.fpart = h->ws.fpart;
-  k.spart = h->ws.spart;
-  const int64_t Bm = h->desc.max_batch, Tm = h->desc.max_tree_rows;
-  k.cnt_stats = h->ws.counters;
-  k.cnt_pass = h->ws.counters + Bm * Tm;
-  k.cnt_final = h->ws.counters + 2 * Bm * Tm;
-  k.B = a->batch;
-  k.T = a->tree_rows;
-  k.V = V;
-  k.NC = ev::vocab_chunks(V);
-  k.vec_ok = ((static_cast<int64_t>(V) * esize) % 16) == 0 ? 1 : 0;
-  k.tau = a->temperature;
-  k.c2 = a->temperature > 0.f ? static_cast<float>(1.4426950408889634 / a->temperature) : 0.f;
-  k.inv_tau = a->temperature > 0.f ? 1.0 / static_cast<double>(a->temperature) : 0.0;
-  k.seed_lo = static_cast<uint32_t>(a->seed);
-  k.seed_hi = static_cast<uint32_t>(a->seed >> 32);
-  k.off_lo = static_cast<uint32_t>(a->offset);
-  k.off_hi = static_cast<uint32_t>(a->offset >> 32);
-  k.node_pub = h->ws.node_pub;
-  k.Tm = static_cast<int>(Tm);
-  k.epoch = ++h->epoch;
-  k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)
-  hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  h->last_stream = stream;
+  h->last_stream = reinterpret_cast<hipStream_t>(hip_stream);
   h->used = true;
-  // The fused kernel needs every workgroup of a launch resident at once.  A
-  // batch that does not fit is verified in slices of whole sequences, one
-  // fused launch each, back to back on the stream (each slice is a fused
-  // call of its own: its own epoch and round-word half); the uniforms keep
-  // the sequence's index in the whole batch.  Only a single sequence that
-  // does not fit takes the three-kernel path.
-  const int64_t per_seq = static_cast<int64_t>(k.T) * k.NC;
   const int64_t cap = h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0];
-  k.wr = (a->without_replacement && a->temperature > 0.f) ? 1 : 0;
-  if (per_seq > cap || k.NC > 64) {
-    if (k.wr) {
-      char msg[160];
-      std::snprintf(msg, sizeof(msg),
-                    "siblings without replacement need the fused path: %lld workgroups per sequence, %lld resident",
-                    static_cast<long long>(per_seq), static_cast<long long>(cap));
-      set_err(h, msg);
-      return EAGLE_ERR_UNSUPPORTED;
-    }
-    k.fused = 0;
-    const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
-    if (e != 0) return hip_fail(h, "spec accept launch", e);
-    h->err[0] = 0;
-    return EAGLE_OK;
-  }
-  const int slice = static_cast<int>(std::min<int64_t>(k.B, cap / per_seq));
-  const int64_t row_bytes = static_cast<int64_t>(V) * esize;
-  const ev::AcceptKernelArgs whole = k;
-  for (int b0 = 0; b0 < whole.B; b0 += slice) {
-    k = whole;
-    k.fused = 1;
-    k.b0 = b0;
-    k.B = std::min(slice, whole.B - b0);
-    const int64_t rows0 = static_cast<int64_t>(b0) * whole.T;
-    k.target = static_cast<const char*>(whole.target) + rows0 * row_bytes;
-    if (whole.draft) k.draft = static_cast<const char*>(whole.draft) + rows0 * row_bytes;
-    k.parents = whole.parents + rows0;
-    k.tokens = whole.tokens + rows0;
-    k.accept_len = whole.accept_len + b0;
-    k.accepted_nodes = whole.accepted_nodes + rows0;
-    k.out_tokens = whole.out_tokens + rows0;
-    k.flags = whole.flags + b0;
-    k.near_ties = whole.near_ties + b0;
-    k.epoch = b0 == 0 ? whole.epoch : ++h->epoch;
-    // the two halves of the round words alternate between fused calls
-    const int64_t half = Bm * Tm * ev::kRoundWords;
-    const int parity = static_cast<int>(h->fused_calls & 1);
-    k.round_sum = h->ws.round_sum + parity * half;
-    k.round_clear = h->ws.round_sum + (1 - parity) * half;
-    k.zero_b = h->last_fused_b;
-    const int e = ev::launch_spec_accept(k, h->desc.logits_dtype == EAGLE_BF16, stream);
-    if (e != 0) return hip_fail(h, "spec accept launch", e);
-    ++h->fused_calls;
-    h->last_fused_b = k.B;
-  }
-  h->err[0] = 0;
-  return EAGLE_OK;
+  st = ev::run_spec_accept(h->desc, h->ws, h->desc.max_batch, h->desc.max_tree_rows, cap, &h->accept_state, a,
+                           hip_stream, h->err, sizeof(h->err));
+  if (st == EAGLE_OK) h->err[0] = 0;
+  return st;
 }
 
 eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args* a, void* hip_stream) {

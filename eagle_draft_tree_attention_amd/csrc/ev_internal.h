@@ -214,6 +214,32 @@ struct Workspace {
   size_t bytes = 0;
 };
 
+// Acceptance scratch of one layout: statistics, node states, round
+// partials, chunk masses, counters, publication and round words for Bm
+// sequences of Tm rows and NC vocabulary chunks, placed from byte offset
+// `off` of a 256-byte-aligned base.  Fills the acceptance fields of *ws
+// (when base is not NULL) and returns the end offset.
+size_t accept_layout(int64_t Bm, int64_t Tm, int NC, size_t off, char* base, Workspace* ws);
+
+// Per-call state of the acceptance launches that outlives one launch: epochs
+// tag cross-workgroup words, and the two halves of the round words alternate
+// between fused launches (each clears the half the previous one used).
+struct AcceptCallState {
+  uint64_t epoch = 0;
+  uint64_t fused_calls = 0;
+  int last_fused_b = 0;
+};
+
+// One spec_accept call on workspace `ws` laid out for Bm x Tm (arguments
+// already checked against the descriptor); fused_cap = co-resident
+// fused-acceptance workgroups.  Messages go to err.
+eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws, int64_t Bm, int64_t Tm,
+                             int64_t fused_cap, AcceptCallState* cs, const eagle_spec_accept_args* a,
+                             void* stream, char* err, size_t errlen);
+
+// thread-local message returned by eagle_verify_last_error(NULL)
+void set_thread_error(const char* msg);
+
 // plan.cpp (pure C++, no HIP)
 eagle_status check_desc(const eagle_verify_desc* d, char* err, size_t errlen);
 eagle_status plan_tree_attention(const eagle_verify_desc* d, const eagle_tree_attention_args* a,

@@ -57,6 +57,10 @@ def eagle_verify_spec_accept(handle: int, args: SpecAcceptArgs, stream: int) -> 
     return _check(_lib().eagle_verify_spec_accept(handle, C.byref(args), C.c_void_p(stream)), handle)
 
 
+def eagle_verify_spec_accept_noalloc(desc: VerifyDesc, args: SpecAcceptArgs, stream: int) -> int:
+    return _check(_lib().eagle_verify_spec_accept_noalloc(C.byref(desc), C.byref(args), C.c_void_p(stream)))
+
+
 def eagle_verify_kv_commit(handle: int, args: KvCommitArgs, stream: int) -> int:
     return _check(_lib().eagle_verify_kv_commit(handle, C.byref(args), C.c_void_p(stream)), handle)
 

@@ -331,6 +331,24 @@ typedef struct {
                             * descriptor-only check reports 0                   */
 } eagle_attention_plan;
 
+/* Multi-round speculative sampling without a handle and without any device
+ * allocation, for callers that cannot allocate: code that is captured into a
+ * HIP graph, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results as eagle_verify_spec_accept (bit-identical
+ * outputs for the same inputs), with the create-time descriptor passed per
+ * call (`desc` maxima are checked, V and the logits dtype are read; the q/kv
+ * fields are validated but unused).  The kernels' scratch lives in a fixed
+ * 8 MiB array in device memory that the library holds on every GPU it runs
+ * on until the process ends; each call first clears the part it uses with a
+ * kernel on `hip_stream`.  A call whose scratch does not fit (it grows with
+ * batch x tree_rows x ceil(V / 8192): e.g. 64 sequences of 64 rows fit at
+ * V = 32000, 32 at V = 128256) returns EAGLE_ERR_CAPACITY before any launch.
+ * Calls that overlap on one GPU share that array and race: serialise them.
+ * Errors: as eagle_verify_spec_accept; the message is read with
+ * eagle_verify_last_error(NULL). */
+EAGLE_API eagle_status eagle_verify_spec_accept_noalloc(const eagle_verify_desc* desc,
+                                                        const eagle_spec_accept_args* a, void* hip_stream);
+
 /* Allocate a handle and its workspace on the current HIP device.
  * Errors: EAGLE_ERR_ARG (bad descriptor), EAGLE_ERR_HIP, EAGLE_ERR_OOM.
  * On error *out is set to NULL. */

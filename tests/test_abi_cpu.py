@@ -237,3 +237,18 @@ def test_paged_kv_argument_errors():
     assert ev.eagle_verify_check_kv_commit(d, a) == ev.EAGLE_OK, ev.eagle_verify_last_error()
     a.page_size = 64
     assert ev.eagle_verify_check_kv_commit(d, a) == ev.EAGLE_ERR_ARG
+
+
+def test_spec_accept_noalloc_rejects_before_any_launch():
+    """Argument and capacity errors come back without touching the device."""
+    from eagle_draft_tree_attention_amd import verify
+    d = _desc(max_batch=64, max_tree_rows=64, vocab_size=128256)
+    a = _sa_args(batch=64, tree_rows=64)
+    lib = ev.library()
+    st = lib.eagle_verify_spec_accept_noalloc(C.byref(d), C.byref(a), None)
+    assert st == ev.EAGLE_ERR_CAPACITY
+    assert "scratch" in verify.eagle_verify_last_error()
+    assert lib.eagle_verify_spec_accept_noalloc(C.byref(d), C.byref(_sa_args(near_ties=None)), None) == \
+        ev.EAGLE_ERR_ARG
+    bad = _desc(vocab_size=1)
+    assert lib.eagle_verify_spec_accept_noalloc(C.byref(bad), C.byref(_sa_args()), None) == ev.EAGLE_ERR_ARG
