@@ -45,7 +45,8 @@ class SpecAcceptArgs(C.Structure):
                 ("parents", C.c_void_p), ("tokens", C.c_void_p), ("temperature", C.c_float),
                 ("seed", C.c_uint64), ("offset", C.c_uint64),
                 ("accept_len", C.c_void_p), ("accepted_nodes", C.c_void_p), ("out_tokens", C.c_void_p),
-                ("flags", C.c_void_p), ("near_ties", C.c_void_p), ("without_replacement", C.c_int32)]
+                ("flags", C.c_void_p), ("near_ties", C.c_void_p), ("without_replacement", C.c_int32),
+                ("top_k", C.c_int32), ("top_p", C.c_float)]
 
 
 class KvCommitArgs(C.Structure):

@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libeagle_verify.so")
 ARCH = os.environ.get("EAGLE_VERIFY_ARCH", "gfx950")
 
-SOURCES = ["plan.cpp", "api.cpp", "attention.hip", "accept.hip", "commit.hip", "expand.hip", "noalloc.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "attention.hip", "accept.hip", "commit.hip", "expand.hip", "filter.hip", "noalloc.hip"]
 
 # Packed FP32 VALU forms are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -90,6 +90,21 @@ __device__ __forceinline__ float logit<uint16_t>(const uint16_t* row, int v) {
   return __uint_as_float(static_cast<uint32_t>(row[v]) << 16);
 }
 
+// Filtered distributions (top-k / top-p): logits below their row's
+// keep-threshold count as -inf.  NaN and +inf pass unchanged, so that an
+// unusable row is still reported.
+__device__ __forceinline__ float thr_of(const AcceptKernelArgs& a, int b, int n, int r) {
+  return a.thr ? a.thr[(static_cast<int64_t>(b) * a.T + n) * 2 + r] : kNegInf;
+}
+__device__ __forceinline__ float cut(float x, float th) { return x < th ? kNegInf : x; }
+// near ties of the filter boundaries of node n's rows (the draft row only
+// when the node tests children)
+__device__ __forceinline__ int32_t filter_near(const AcceptKernelArgs& a, int b, int n, bool draft_used) {
+  if (!a.thr) return 0;
+  const int64_t i = (static_cast<int64_t>(b) * a.T + n) * 2;
+  return a.thr_near[i] + (draft_used ? a.thr_near[i + 1] : 0);
+}
+
 // Load this thread's share of a chunk [v0, v1) into x[]; slots past v1 get -inf.
 // Element of slot j: vector path v0 + (tid + 256*(j/G))*G + j%G, scalar path v0 + tid + 256*j.
 template <typename TL>
@@ -327,8 +342,8 @@ __device__ int decide_child(const AcceptKernelArgs& a, int b, int n, int child, 
   const int tok = a.tokens[b * a.T + child];
   if (tok < 0 || tok >= a.V) return -1;
   const int64_t row = static_cast<int64_t>(b * a.T + n) * a.V;
-  const double xt = logit<TL>(reinterpret_cast<const TL*>(a.target) + row, tok);
-  const double yt = logit<TL>(reinterpret_cast<const TL*>(a.draft) + row, tok);
+  const double xt = cut(logit<TL>(reinterpret_cast<const TL*>(a.target) + row, tok), thr_of(a, b, n, 0));
+  const double yt = cut(logit<TL>(reinterpret_cast<const TL*>(a.draft) + row, tok), thr_of(a, b, n, 1));
   return decide_values(a, b, n, ordinal, tok, xt, yt, C, s, st, flags, near);
 }
 
@@ -341,10 +356,11 @@ __device__ double residual_mass(const AcceptKernelArgs& a, int b, int n, const N
   const TL* tr = reinterpret_cast<const TL*>(a.target) + row;
   const TL* dr = reinterpret_cast<const TL*>(a.draft) + row;
   const double izq = 1.0 / st.zq, izp = 1.0 / st.zp;
+  const float thq = thr_of(a, b, n, 0), thp = thr_of(a, b, n, 1);
   double acc = 0.0;
   for (int v = v0 + threadIdx.x; v < v1; v += kThreads) {
-    const double qv = static_cast<double>(exp2f((logit<TL>(tr, v) - st.mq) * a.c2)) * izq;
-    const double pv = static_cast<double>(exp2f((logit<TL>(dr, v) - st.mp) * a.c2)) * izp;
+    const double qv = static_cast<double>(exp2f((cut(logit<TL>(tr, v), thq) - st.mq) * a.c2)) * izq;
+    const double pv = static_cast<double>(exp2f((cut(logit<TL>(dr, v), thp) - st.mp) * a.c2)) * izp;
     acc += fmax(0.0, qv - C * pv);
   }
   return block_reduce(acc, AddD{}, dscratch);
@@ -426,6 +442,11 @@ __global__ __launch_bounds__(kThreads) void sa_stats(const AcceptKernelArgs a) {
   float x[kPerThread];
   int idx[kPerThread];
   load_chunk<TL>(rp, v0, v1, a.vec_ok != 0, x, idx);
+  if (a.thr) {
+    const float th = thr_of(a, b, n, row);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) x[j] = cut(x[j], th);
+  }
 
   float m = kNegInf;
   uint32_t bad = 0;
@@ -494,6 +515,7 @@ __global__ __launch_bounds__(kThreads) void sa_stats(const AcceptKernelArgs a) {
     st.flags = nonfinite ? EAGLE_FLAG_NONFINITE : 0u;
     st.C = 0.0;
     st.s = 1.0;
+    st.near = greedy ? 0 : filter_near(a, b, n, kids);
     if (!kids) {
       st.kind = kNodeLeaf;
     } else if (nonfinite) {
@@ -510,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void sa_stats(const AcceptKernelArgs a) {
     } else {
       const int child = kth_child(ti, T, n, 0);
       uint32_t fl = st.flags;
-      int32_t nr = 0;
+      int32_t nr = st.near;
       const int res = decide_child<TL>(a, b, n, child, 0, 0.0, 1.0, st, fl, nr);
       st.flags = fl;
       st.near = nr;
@@ -563,10 +585,10 @@ __global__ __launch_bounds__(kThreads) void sa_pass(const AcceptKernelArgs a) {
 // Terminal weight of token v: q_v (leaf) or max(0, q_v - C p_v).
 template <typename TL>
 __device__ __forceinline__ double terminal_weight(const TL* tr, const TL* dr, int v, const NodeState& st, double C,
-                                                  bool leaf, float c2, double izq, double izp) {
-  const double qv = static_cast<double>(exp2f((logit<TL>(tr, v) - st.mq) * c2)) * izq;
+                                                  bool leaf, float c2, double izq, double izp, float thq, float thp) {
+  const double qv = static_cast<double>(exp2f((cut(logit<TL>(tr, v), thq) - st.mq) * c2)) * izq;
   if (leaf || C == 0.0) return qv;
-  const double pv = static_cast<double>(exp2f((logit<TL>(dr, v) - st.mp) * c2)) * izp;
+  const double pv = static_cast<double>(exp2f((cut(logit<TL>(dr, v), thp) - st.mp) * c2)) * izp;
   return fmax(0.0, qv - C * pv);
 }
 
@@ -663,10 +685,11 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
   const TL* tr = reinterpret_cast<const TL*>(a.target) + rowoff;
   const TL* dr = reinterpret_cast<const TL*>(a.draft) + rowoff;
   const double izq = 1.0 / st.zq, izp = leaf ? 0.0 : 1.0 / st.zp;
+  const float thq = thr_of(a, b, term, 0), thp = thr_of(a, b, term, 1);
   {
     const int v0 = c * kVocabChunk, v1 = min(a.V, v0 + kVocabChunk);
     double acc = 0.0;
-    for (int v = v0 + tid; v < v1; v += kThreads) acc += terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp);
+    for (int v = v0 + tid; v < v1; v += kThreads) acc += terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp, thq, thp);
     acc = block_reduce(acc, AddD{}, dscr);
     if (tid == 0) a.spart[static_cast<int64_t>(b) * NC + c] = acc;
   }
@@ -682,7 +705,7 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
     for (int q = 0; q < NC; ++q) {
       const int v0 = q * kVocabChunk, v1 = min(a.V, v0 + kVocabChunk);
       double acc = 0.0;
-      for (int v = v0 + tid; v < v1; v += kThreads) acc += terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp);
+      for (int v = v0 + tid; v < v1; v += kThreads) acc += terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp, thq, thp);
       acc = block_reduce(acc, AddD{}, dscr);
       __syncthreads();
       if (tid == 0) sp[q] = acc;
@@ -709,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
 #pragma unroll
   for (int j = 0; j < kPerThread; ++j) {
     const int v = v0 + tid * kPerThread + j;
-    w[j] = (v < v1) ? terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp) : 0.0;
+    w[j] = (v < v1) ? terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp, thq, thp) : 0.0;
     tsum += w[j];
   }
   scan_lds[tid] = tsum;
@@ -1010,6 +1033,29 @@ __device__ __forceinline__ void mask_groups(int v0, int v1, u32x4_t (&w)[NV]) {
     if (v0 + group_index<TL>(jj) >= v1) w[jj] = u32x4_t{ni, ni, ni, ni};
 }
 
+// Logits below th become -inf (NaN and +inf pass unchanged).
+template <typename TL, int NV>
+__device__ __forceinline__ void cut_groups(u32x4_t (&w)[NV], float th) {
+  const uint32_t ni = Pack<TL>::neg_inf_word();
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) {
+    float f[Pack<TL>::G];
+    Pack<TL>::unpack(w[jj], f);
+    if constexpr (sizeof(TL) == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = f[2 * i] < th ? (ni & 0xFFFFu) : (w[jj][i] & 0xFFFFu);
+        const uint32_t hi = f[2 * i + 1] < th ? (ni & 0xFFFF0000u) : (w[jj][i] & 0xFFFF0000u);
+        w[jj][i] = lo | hi;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (f[i] < th) w[jj][i] = ni;
+    }
+  }
+}
+
 // Row statistics of this thread's values: the maximum, or +inf when a NaN or
 // +inf is present (the row is then unusable).
 template <typename TL, int NV>
@@ -1025,21 +1071,23 @@ __device__ __forceinline__ float local_max(const u32x4_t (&w)[NV]) {
   return m;
 }
 
-// exp((x - m) / tau) = 2^(x c2 - m c2) on the hardware exp2 (results below
-// 2^-126 of the row maximum, irrelevant to any sum here, may flush to 0)
-__device__ __forceinline__ float ex2(float x, float c2, float mc2) { return __builtin_amdgcn_exp2f(__builtin_fmaf(x, c2, mc2)); }
+// exp((x - m) / tau) = 2^((x - m) c2) on the hardware exp2 (results below
+// 2^-126 of the row maximum, irrelevant to any sum here, may flush to 0).
+// The difference is taken first: x c2 - m c2 as one fma would carry the
+// rounding error of m c2, a factor common to a chunk but not across chunks,
+// which grows with |m| (and overflows for |m| near the float range).
+__device__ __forceinline__ float ex2(float x, float c2, float m) { return __builtin_amdgcn_exp2f((x - m) * c2); }
 
 // sum of exp((x - m) / tau) over this thread's values, fp64
 template <typename TL, int NV>
 __device__ __forceinline__ double local_expsum(const u32x4_t (&w)[NV], float m, float c2) {
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  const float mc2 = -m * c2;
 #pragma unroll
   for (int jj = 0; jj < NV; ++jj) {
     float f[Pack<TL>::G];
     Pack<TL>::unpack(w[jj], f);
 #pragma unroll
-    for (int e = 0; e < Pack<TL>::G; ++e) acc[e & 3] += static_cast<double>(ex2(f[e], c2, mc2));
+    for (int e = 0; e < Pack<TL>::G; ++e) acc[e & 3] += static_cast<double>(ex2(f[e], c2, m));
   }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
@@ -1054,7 +1102,6 @@ template <typename TL, int NV>
 __device__ __forceinline__ void local_masses(const TL* lq, const TL* lp, bool use_p, float mqs, float mps, float c2,
                                              double fq, double fp, double C, double& res, double& qsum) {
   double ra[4] = {0.0, 0.0, 0.0, 0.0}, qa[4] = {0.0, 0.0, 0.0, 0.0};
-  const float qc = -mqs * c2, pc = -mps * c2;
   const float K = (use_p && fq > 0.0) ? static_cast<float>(C * fp / fq) : 0.f;
   u32x4_t wq[NV], wp[NV];
 #pragma unroll
@@ -1069,9 +1116,9 @@ __device__ __forceinline__ void local_masses(const TL* lq, const TL* lp, bool us
     if (use_p) Pack<TL>::unpack(wp[jj], fb);
 #pragma unroll
     for (int e = 0; e < Pack<TL>::G; ++e) {
-      const float eq = ex2(fa[e], c2, qc);
+      const float eq = ex2(fa[e], c2, mqs);
       qa[e & 3] += static_cast<double>(eq);
-      if (use_p) ra[e & 3] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ex2(fb[e], c2, pc), eq)));
+      if (use_p) ra[e & 3] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ex2(fb[e], c2, mps), eq)));
     }
   }
   qsum = ((qa[0] + qa[1]) + (qa[2] + qa[3])) * fq;
@@ -1186,8 +1233,8 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       cd.tok = tok;
       cd.child = lane;
       if (!greedy && !tb) {
-        cd.xq = logit<TL>(trow, tok);
-        cd.yp = logit<TL>(drow, tok);
+        cd.xq = cut(logit<TL>(trow, tok), thr_of(a, b, n, 0));
+        cd.yp = cut(logit<TL>(drow, tok), thr_of(a, b, n, 1));
       }
       sh.cand[ord] = cd;
     }
@@ -1202,6 +1249,10 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     if constexpr (VEC) {
       mask_groups<TL, NV>(v0, v1, wq);
       if (two) mask_groups<TL, NV>(v0, v1, wd);
+    }
+    if (a.thr) {   // filtered distributions: logits below the row's threshold become -inf
+      cut_groups<TL, NV>(wq, thr_of(a, b, n, 0));
+      if (two) cut_groups<TL, NV>(wd, thr_of(a, b, n, 1));
     }
 #pragma unroll
     for (int jj = 0; jj < NV; ++jj) {
@@ -1344,7 +1395,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     st.s = 1.0;
     st.outcome = -1;
     st.next_child = 0;
-    st.near = 0;
+    st.near = greedy ? 0 : filter_near(a, b, n, two);
     if (nkids == 0) {
       st.kind = kNodeLeaf;
     } else if (st.flags & EAGLE_FLAG_NONFINITE) {
@@ -1355,7 +1406,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     } else {
       const Cand& cd = sh.cand[0];
       uint32_t fl = st.flags;
-      int32_t nr = 0;
+      int32_t nr = st.near;
       sh.zrem = 1.0;
       for (int j = 0; j < nkids; ++j) sh.wfz[j] = -1.0;   // no kept weight until the sibling is rejected
       const int res = decide_pre(cd.qt, cd.pt, cd.r, cd.tok, V, 0.0, 1.0, fl, nr);
@@ -1536,11 +1587,10 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   const double Ct = leaf ? 0.0 : sh.st.C;
   const int i0 = tid * kPerThread;
   // weight of the token at LDS slot i0 + jj * G + e, from its two logits
-  const float qc = -mqs * a.c2, pc = -mps * a.c2;
   const float Kt = fq > 0.0 ? static_cast<float>(Ct * fp / fq) : 0.f;
   auto weight = [&](bool q_only, float xq, float xp) __attribute__((always_inline)) -> double {
-    const float eq = ex2(xq, a.c2, qc);
-    return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(xp, a.c2, pc), eq)));
+    const float eq = ex2(xq, a.c2, mqs);
+    return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(xp, a.c2, mps), eq)));
   };
   // this thread's sums of the weights and of q
   auto sums = [&](bool q_only, double& ts, double& tq) __attribute__((always_inline)) {
@@ -1554,9 +1604,9 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       Pack<TL>::unpack(gp, fb);
 #pragma unroll
       for (int e = 0; e < G; ++e) {
-        const float eq = ex2(fa[e], a.c2, qc);
+        const float eq = ex2(fa[e], a.c2, mqs);
         qa[e & 3] += static_cast<double>(eq);
-        wa[e & 3] += static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(fb[e], a.c2, pc), eq)));
+        wa[e & 3] += static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(fb[e], a.c2, mps), eq)));
       }
     }
     ts = ((wa[0] + wa[1]) + (wa[2] + wa[3])) * fq;

@@ -83,6 +83,10 @@ size_t accept_layout(int64_t Bm, int64_t Tm, int NC, size_t off, char* base, Wor
   off = align_up(off + sizeof(uint64_t) * Bm * Tm, 256);
   const size_t o_round = off;
   off = align_up(off + sizeof(uint64_t) * 2 * Bm * Tm * kRoundWords, 256);
+  const size_t o_thr = off;
+  off = align_up(off + sizeof(float) * 2 * Bm * Tm, 256);
+  const size_t o_thr_near = off;
+  off = align_up(off + sizeof(int32_t) * 2 * Bm * Tm, 256);
   if (base && ws) {
     ws->stats = reinterpret_cast<ChunkStat*>(base + o_stats);
     ws->nodes = reinterpret_cast<NodeState*>(base + o_nodes);
@@ -91,6 +95,8 @@ size_t accept_layout(int64_t Bm, int64_t Tm, int NC, size_t off, char* base, Wor
     ws->counters = reinterpret_cast<uint32_t*>(base + o_cnt);
     ws->node_pub = reinterpret_cast<uint64_t*>(base + o_sync);
     ws->round_sum = reinterpret_cast<uint64_t*>(base + o_round);
+    ws->thr = reinterpret_cast<float*>(base + o_thr);
+    ws->thr_near = reinterpret_cast<int32_t*>(base + o_thr_near);
   }
   return off;
 }
@@ -143,6 +149,27 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
   // call of its own: its own epoch and round-word half); the uniforms keep
   // the sequence's index in the whole batch.  Only a single sequence that
   // does not fit takes the three-kernel path.
+  // filtered distributions: one keep-threshold per row first (sampled mode only)
+  if (a->temperature > 0.f && (a->top_k > 0 || (a->top_p > 0.f && a->top_p < 1.f))) {
+    FilterKernelArgs f;
+    std::memset(&f, 0, sizeof(f));
+    f.target = k.target;
+    f.draft = k.draft;
+    f.parents = a->parents;
+    f.tokens = a->tokens;
+    f.thr = ws.thr;
+    f.near = ws.thr_near;
+    f.B = a->batch;
+    f.T = a->tree_rows;
+    f.V = V;
+    f.top_k = a->top_k;
+    f.top_p = a->top_p;
+    f.c2 = k.c2;
+    const int e = launch_filter(f, bf16, hip_stream);
+    if (e != 0) return hip_fail_to(err, errlen, "filter launch", e);
+    k.thr = ws.thr;
+    k.thr_near = ws.thr_near;
+  }
   const int64_t per_seq = static_cast<int64_t>(k.T) * k.NC;
   k.wr = (a->without_replacement && a->temperature > 0.f) ? 1 : 0;
   if (per_seq > cap || k.NC > 64) {
@@ -175,6 +202,10 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
     k.out_tokens = whole.out_tokens + rows0;
     k.flags = whole.flags + b0;
     k.near_ties = whole.near_ties + b0;
+    if (whole.thr) {
+      k.thr = whole.thr + rows0 * 2;
+      k.thr_near = whole.thr_near + rows0 * 2;
+    }
     k.epoch = b0 == 0 ? whole.epoch : ++cs->epoch;
     // the two halves of the round words alternate between fused launches
     const int64_t half = Bm * Tm * kRoundWords;

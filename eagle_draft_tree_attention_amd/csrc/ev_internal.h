@@ -130,10 +130,29 @@ struct AcceptKernelArgs {
   int wr;                 // 1: siblings were drawn without replacement (fused path only)
   int B, T, V, NC;
   int vec_ok;          // rows start 16-byte aligned
+  // filtered distributions: logits below thr[(b * T + n) * 2 + r] count as
+  // -inf (r = 0 target, 1 draft row of node n); NULL: no filter
+  const float* thr;
+  const int32_t* thr_near;   // per row: 1 adds a near tie to the node's decisions
   float tau;           // > 0 sampled, == 0 greedy
   float c2;            // log2(e) / tau
   double inv_tau;
   uint32_t seed_lo, seed_hi, off_lo, off_hi;
+};
+
+// Keep-thresholds of filtered (top-k / top-p) distributions, one per row:
+// thr[(b * T + n) * 2 + r] (r = 0 target, 1 draft); -inf keeps every token.
+struct FilterKernelArgs {
+  const void* target;
+  const void* draft;
+  const int32_t* parents;
+  const int32_t* tokens;
+  float* thr;
+  int32_t* near;       // 1: the row's top-p boundary lies within 1e-6 of its mass target
+  int B, T, V;
+  int top_k;           // 0: off
+  float top_p;         // 0 or 1: off
+  float c2;            // log2(e) / tau
 };
 
 // ---------------------------------------------------------------- KV commit
@@ -211,6 +230,8 @@ struct Workspace {
   double* spart = nullptr;
   uint32_t* counters = nullptr; // cnt_stats | cnt_pass | cnt_final
   ChunkRecord* expand = nullptr; // [max_batch][max_tree_rows][expansion chunks of a row]
+  float* thr = nullptr;          // [max_batch][max_tree_rows][2] keep-thresholds of filtered rows
+  int32_t* thr_near = nullptr;   // [max_batch][max_tree_rows][2]
   size_t bytes = 0;
 };
 
@@ -257,6 +278,7 @@ int vocab_chunks(int V);
 int launch_tree_attention(const AttnPlan& plan, const AttnKernelArgs& args, int kv_bf16,
                           void* stream);
 int launch_spec_accept(const AcceptKernelArgs& args, int logits_bf16, void* stream);
+int launch_filter(const FilterKernelArgs& args, int logits_bf16, void* stream);        // filter.hip
 int launch_kv_commit(const CommitKernelArgs& args, int kv_bf16, void* stream);   // commit.hip
 int launch_tree_expand(const ExpandKernelArgs& args, int logits_bf16, void* stream);   // expand.hip
 int launch_tree_rerank(const RerankKernelArgs& args, void* stream);                    // expand.hip

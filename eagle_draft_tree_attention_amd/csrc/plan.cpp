@@ -219,6 +219,9 @@ eagle_status check_spec_accept(const eagle_verify_desc* d, const eagle_spec_acce
     return fail(EAGLE_ERR_ARG, err, errlen, "temperature must be finite and >= 0");
   if (a->without_replacement != 0 && a->without_replacement != 1)
     return fail(EAGLE_ERR_ARG, err, errlen, "without_replacement=%d: 0 or 1", a->without_replacement);
+  if (a->top_k < 0) return fail(EAGLE_ERR_ARG, err, errlen, "top_k=%d < 0", a->top_k);
+  if (!(a->top_p >= 0.f && a->top_p <= 1.f))
+    return fail(EAGLE_ERR_ARG, err, errlen, "top_p must lie in [0, 1] (0 or 1: no nucleus filter)");
   if (!a->target_logits || !a->parents || !a->tokens || !a->accept_len || !a->accepted_nodes ||
       !a->out_tokens || !a->flags || !a->near_ties)
     return fail(EAGLE_ERR_ARG, err, errlen, "a required pointer is NULL");

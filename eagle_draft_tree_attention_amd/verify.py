@@ -202,7 +202,7 @@ class Verifier:
         return eagle_verify_last_attention_plan(self.handle)
 
     def spec_accept(self, target, draft, parents, tokens, temperature, seed, offset, outputs=None,
-                    stream=None, without_replacement=False):
+                    stream=None, without_replacement=False, top_k=0, top_p=0.0):
         import torch
         B, T, V = target.shape
         dev = target.device
@@ -226,6 +226,7 @@ class Verifier:
         a.flags = _ptr(outputs["flags"])
         a.near_ties = _ptr(outputs["near_ties"])
         a.without_replacement = 1 if without_replacement else 0
+        a.top_k, a.top_p = int(top_k), float(top_p)
         eagle_verify_spec_accept(self.handle, a, _stream(stream))
         return outputs
 

@@ -167,6 +167,20 @@ typedef struct {
  *                Ignored when temperature == 0.  Only for calls whose
  *                sequences each fit the fused kernel (T x ceil(V / 8192)
  *                workgroups resident at once), else EAGLE_ERR_UNSUPPORTED.
+ *   top_k, top_p filtered distributions (the request's sampling filters):
+ *                with temperature > 0, q and p are both replaced by their
+ *                filtered and renormalised versions before the walk, and the
+ *                children must have been drawn from the filtered draft.
+ *                top_k > 0 keeps the tokens whose logit is at least the
+ *                top_k-th largest of the row (ties at that value all kept;
+ *                top_k = 0 or >= V keeps everything).  top_p in (0, 1) then
+ *                keeps, among those, every token whose strictly larger
+ *                logits hold less than top_p of their mass (0 or 1: off).
+ *                A row whose nucleus boundary lies within 1e-6 of its mass
+ *                target adds a near tie to its node's decisions.  The
+ *                result is lossless for the filtered target (a rejection
+ *                never emits a filtered-out token).  Ignored when
+ *                temperature == 0 (the argmax is never filtered out).
  *   seed, offset Philox4x32-10 key / per-step counter word: the uniform for the
  *                test of the i-th child (0-based) of node n in sequence b uses
  *                counter (i, n | b << 8, offset_lo, offset_hi), key (seed_lo,
@@ -197,6 +211,8 @@ typedef struct {
   uint32_t* flags;
   int32_t* near_ties;
   int32_t without_replacement; /* 0 or 1, see above */
+  int32_t top_k;               /* >= 0, 0 = off, see above */
+  float top_p;                 /* [0, 1], 0 or 1 = off, see above */
 } eagle_spec_accept_args;
 
 /* Commit the accepted path into the KV cache, in place (lesson page, the

@@ -122,7 +122,42 @@ def inv_cdf(w, u):
     return v, near
 
 
-def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_replacement=False, where=None):
+def keep_threshold(row, tau, top_k=0, top_p=0.0):
+    """Keep-threshold of a filtered distribution (a request's top-k / top-p
+    sampling filters; the EAGLE notes page's tree drafting samples k children
+    per node).  Returns (theta, near): the filtered distribution keeps the
+    tokens whose logit is at least theta and renormalises softmax(row / tau)
+    over them.
+
+      top-k (0 < top_k < V): theta = the top_k-th largest logit, duplicates
+        counted, so every token tied with it is kept; otherwise no cut.
+      top-p (0 < top_p < 1), among the tokens top-k keeps: a token is kept
+        iff the mass of the tokens with a strictly larger logit is below
+        top_p times the kept mass; theta = the smallest kept logit.
+    near: the nucleus boundary is within 1e-6 of the mass target, i.e. the
+    kept mass minus top_p * Z, or top_p * Z minus the mass strictly above the
+    boundary value, is below 1e-6 * Z."""
+    x = np.asarray(row, dtype=np.float64)
+    V = len(x)
+    theta = -np.inf
+    if 0 < top_k < V:
+        theta = np.sort(x)[::-1][top_k - 1]
+    near = False
+    if 0.0 < top_p < 1.0:
+        w = np.where(x >= theta, np.exp((x - x.max()) / tau), 0.0)
+        order = np.argsort(-x, kind="stable")
+        run = np.cumsum(w[order])
+        z = run[-1]
+        i = min(int(np.searchsorted(run, top_p * z, side="left")), V - 1)
+        u = x[order][i]
+        above, upto = w[x > u].sum(), w[x >= u].sum()
+        near = bool((upto - top_p * z) < NEAR_TIE * z or (top_p * z - above) < NEAR_TIE * z)
+        theta = u
+    return theta, near
+
+
+def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_replacement=False, where=None,
+                 row_near=None):
     """Sequential multi-round walk of one tree.
 
     target_rows(n) / draft_rows(n) return node n's logits rows (float64);
@@ -136,6 +171,10 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_re
     depth = accepted nodes before the decision (the node deciding sits at
     that depth of the path), slot = the sibling ordinal of a test, or -1 for
     the terminal sample.
+    row_near(n) -> (target, draft): near ties of the filter boundaries of node
+    n's rows (filtered distributions), counted when the walk visits n (the
+    draft row's only when n has children), as slot 0 of that node: every
+    decision there depends on them.
     Returns (path, final_token, flags, near_ties).
     """
     kids = tree_children(parents, real_rows(tokens, len(parents)))
@@ -145,6 +184,13 @@ def walk_sampled(target_rows, draft_rows, parents, tokens, tau, draw, without_re
     cur = 0
     while True:
         q = softmax_t(target_rows(cur), tau)
+        if row_near is not None:
+            nq, nd = row_near(cur)
+            fnear = int(nq) + (int(nd) if kids[cur] else 0)
+            if fnear:
+                near += fnear
+                if where is not None:
+                    where.append((len(path), 0))
         if not kids[cur]:
             final, nt = inv_cdf(q, draw(cur, philox.SAMPLE_SLOT))
             near += int(nt)
@@ -229,11 +275,16 @@ def validate_sequence(target, draft, parents, tokens, tau) -> int:
     return flags
 
 
-def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=None, without_replacement=False):
+def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=None, without_replacement=False,
+                top_k=0, top_p=0.0):
     """Oracle for one verification step over a batch of trees.
 
     target, draft: [B,T,V] float64 logits (draft may be None when
     temperature == 0).  draw(b, node, slot) overrides the Philox uniforms.
+    top_k, top_p (temperature > 0): every target and draft row is replaced by
+    its filtered distribution (keep_threshold: logits below the threshold
+    become -inf) before the walk; the children must have been drawn from the
+    filtered draft rows.
     Returns a dict of numpy arrays: accept_len [B], accepted_nodes [B,T],
     out_tokens [B,T], flags [B], near_ties [B], and where the walk's first
     near-tie decision sits: first_near_depth [B] (accepted nodes before it,
@@ -269,8 +320,18 @@ def spec_accept(target, draft, parents, tokens, temperature, seed, offset, draw=
                 def u(n, s, _b=b):
                     return draw(_b, n, s)
             where = []
-            path, final, fl, near = walk_sampled(lambda n: target[b, n], lambda n: drf[n],
-                                                 parents[b], tokens[b], tau, u, without_replacement, where)
+            tgt_b, row_near = target[b], None
+            if top_k > 0 or 0.0 < top_p < 1.0:
+                tgt_b, drf, nears = tgt_b.copy(), drf.copy(), np.zeros((T, 2), dtype=bool)
+                for n in range(T):
+                    for r, rows in ((0, tgt_b), (1, drf)):
+                        if row_is_usable(rows[n]):   # rows never read may hold anything
+                            th, nears[n, r] = keep_threshold(rows[n], tau, top_k, top_p)
+                            rows[n] = np.where(rows[n] < th, -np.inf, rows[n])
+                row_near = lambda n, _nears=nears: (_nears[n, 0], _nears[n, 1])
+            path, final, fl, near = walk_sampled(lambda n, _t=tgt_b: _t[n], lambda n, _d=drf: _d[n],
+                                                 parents[b], tokens[b], tau, u, without_replacement, where,
+                                                 row_near)
             if where:
                 res["first_near_depth"][b], res["first_near_slot"][b] = where[0]
         res["accept_len"][b] = len(path)

@@ -407,3 +407,139 @@ def test_expected_accept_length_of_a_fixed_tree_on_gpu():
     assert abs(lens.mean() - want) < 4.5 * se
     assert diverged <= excused_bound(4 * B)
     ver.close()
+
+
+def _filtered_tokens(spec, inp, rng, k, p, temp):
+    """Children drawn from their parent's filtered draft distribution."""
+    d64 = synth.inputs.as_f64(inp.draft, spec.ldtype)
+    tok = inp.tokens.copy()
+    for b in range(spec.batch):
+        for n, ch in enumerate(oacc.tree_children(inp.parents[b])):
+            if not ch:
+                continue
+            th, _ = oacc.keep_threshold(d64[b, n], temp, k, p)
+            w = sp_softmax(np.where(d64[b, n] < th, -np.inf, d64[b, n]) / temp)
+            tok[b, ch] = rng.choice(spec.vocab, size=len(ch), p=w)
+    return tok
+
+
+FILTER_CASES = [
+    (small_spec("filt_topk_bf16", B=6, V=1000, levels=(4, 6, 10)), 20, 0.0),
+    (small_spec("filt_topp_bf16_multi_chunk", B=4, V=20000, levels=(10, 10, 10)), 0, 0.9),
+    (small_spec("filt_both_f32_t07", dtype="f32", B=4, V=5003, levels=(6, 6), temperature=0.7), 50, 0.8),
+    (small_spec("filt_topp_low_alpha", B=6, V=3000, sigma_d=2.5, levels=(10, 10)), 0, 0.5),
+    (small_spec("filt_topk_1_star", dtype="f32", B=4, V=64, tree=("star", 6)), 1, 0.0),
+]
+
+
+@pytest.mark.parametrize("spec,k,p", FILTER_CASES, ids=[c[0].name for c in FILTER_CASES])
+def test_filtered_distributions(spec, k, p):
+    """top-k / top-p filtered target and draft rows (thresholds found by the
+    filter kernel), children drawn from the filtered drafts."""
+    log(f"[accept] filtered: {spec.name} top_k {k} top_p {p}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    tok = _filtered_tokens(spec, inp, np.random.default_rng(5), k, p, spec.temperature)
+    ver = make_verifier(spec, inp.T)
+    diverged = 0
+    for off in range(6):
+        got = run_accept(ver, inp, spec.temperature, SEED, off, tokens=tok, top_k=k, top_p=p)
+        ref = oacc.spec_accept(inp.target64(), inp.draft64(), inp.parents, tok, spec.temperature, SEED, off,
+                               top_k=k, top_p=p)
+        assert (ref["flags"] & 7).tolist() == [0] * spec.batch
+        diverged += compare_accept(got, ref, f"{spec.name} offset {off}", inp.parents, tok, spec.vocab)
+    log(f"    near-tie divergences: {diverged}")
+    assert diverged <= excused_bound(6 * spec.batch)
+    ver.close()
+
+
+def test_filtered_distributions_at_the_8b_shape_and_three_kernel_path():
+    """The 8B workload (61 rows over 128256 bf16 logits, many tied values)
+    with nucleus and top-k filters, and one sequence too large for the fused
+    kernel (three-kernel path)."""
+    for spec, k, p, offs in ((synth.config_spec(2), 0, 0.95, 3), (synth.config_spec(2), 40, 0.0, 2),
+                             (small_spec("filt_general", B=1, V=520000, levels=(10,) * 6, sigma_d=1.2), 40, 0.9, 2)):
+        log(f"[accept] filtered: {spec.name} V {spec.vocab} top_k {k} top_p {p}")
+        inp = synth.make_inputs(spec, with_kv=False)
+        tok = _filtered_tokens(spec, inp, np.random.default_rng(6), k, p, spec.temperature)
+        ver = make_verifier(spec, inp.T)
+        t64, d64 = inp.target64(), inp.draft64()
+        diverged = 0
+        for off in range(offs):
+            got = run_accept(ver, inp, spec.temperature, SEED, off, tokens=tok, top_k=k, top_p=p)
+            ref = oacc.spec_accept(t64, d64, inp.parents, tok, spec.temperature, SEED, off, top_k=k, top_p=p)
+            diverged += compare_accept(got, ref, f"{spec.name} offset {off}", inp.parents, tok, spec.vocab)
+        assert diverged <= excused_bound(offs * spec.batch)
+        ver.close()
+
+
+def test_filter_edge_rows():
+    """Rows the threshold search must resolve by its special cases: all
+    logits equal (one value), two tied plateaus, a range of 2e37 (coarse first
+    bins), -inf entries beyond top-k, a bf16-like row of few distinct values,
+    and a cluster of 8190 distinct values 1e-7 wide in a row 1e30 wide (four
+    refinement levels do not separate them: exact bisection)."""
+    V, T = 8192, 5
+    rng = np.random.default_rng(12)
+    base = (rng.standard_normal((T, V)) * 2).astype(np.float32)
+    rows = [np.zeros((T, V), np.float32),
+            np.tile(np.where(np.arange(V) % 3 == 0, 1.0, 0.5).astype(np.float32), (T, 1))]
+    wide = base.copy()
+    wide[:, ::7] = -1.0e37
+    wide[:, 1] = 1.0e37
+    rows.append(wide)
+    minf = base.copy()
+    minf[:, V // 2:] = -np.inf
+    rows.append(minf)
+    rows.append((np.round(base * 2) / 2).astype(np.float32))
+    cluster = -rng.uniform(0.0, 1e-7, size=(T, V)).astype(np.float32)
+    cluster[:, 0] = 0.0
+    cluster[:, 1] = -1.0e30
+    rows.append(cluster)
+    tgt = np.stack(rows)
+    drf = tgt + np.float32(0.0)
+    B = tgt.shape[0]
+    spec = small_spec("filt_edges", dtype="f32", B=B, V=V, tree=("chain", T - 1))
+    inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
+    par = np.tile(np.arange(-1, T - 1, dtype=np.int32), (B, 1))
+    ver = make_verifier(spec, T)
+    for k, p in ((7, 0.0), (0, 0.6), (3000, 0.9), (1, 0.3)):
+        log(f"[accept] filter edge rows: top_k {k} top_p {p}")
+        tok = np.zeros((B, T), np.int32)
+        for b in range(B):
+            th, _ = oacc.keep_threshold(drf[b, 0].astype(np.float64), 1.0, k, p)
+            kept = np.nonzero(drf[b, 0] >= th)[0]
+            tok[b, 1:] = rng.choice(kept, size=T - 1)
+        diverged = 0
+        for off in range(3):
+            got = run_accept(ver, inp, 1.0, SEED, off, target=tgt, draft=drf, parents=par, tokens=tok, top_k=k, top_p=p)
+            ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, off,
+                                   top_k=k, top_p=p)
+            assert (ref["flags"] & 7).tolist() == [0] * B
+            diverged += compare_accept(got, ref, f"edges k {k} p {p} offset {off}", par, tok, V)
+        assert diverged <= 1
+    ver.close()
+
+
+def test_filters_with_siblings_without_replacement():
+    spec = small_spec("filt_wr", B=4, V=2000, levels=(8, 8), sigma_d=1.5)
+    log(f"[accept] filtered, without replacement: {spec.name}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    rng = np.random.default_rng(8)
+    d64 = inp.draft64()
+    tok = inp.tokens.copy()
+    k, p = 30, 0.9
+    for b in range(spec.batch):
+        for n, ch in enumerate(oacc.tree_children(inp.parents[b])):
+            if ch:
+                th, _ = oacc.keep_threshold(d64[b, n], 1.0, k, p)
+                w = sp_softmax(np.where(d64[b, n] < th, -np.inf, d64[b, n]))
+                tok[b, ch] = rng.choice(spec.vocab, size=len(ch), replace=len(ch) > int((w > 0).sum()), p=w)
+    ver = make_verifier(spec, inp.T)
+    diverged = 0
+    for off in range(4):
+        got = run_accept(ver, inp, 1.0, SEED, off, tokens=tok, top_k=k, top_p=p, without_replacement=True)
+        ref = oacc.spec_accept(inp.target64(), d64, inp.parents, tok, 1.0, SEED, off, without_replacement=True,
+                               top_k=k, top_p=p)
+        diverged += compare_accept(got, ref, f"filtered wr offset {off}", inp.parents, tok, spec.vocab)
+    assert diverged <= excused_bound(4 * spec.batch)
+    ver.close()
