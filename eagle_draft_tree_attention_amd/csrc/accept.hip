@@ -409,6 +409,123 @@ __device__ void continue_siblings(const AcceptKernelArgs& a, int b, int n, const
   st.next_child = i;
 }
 
+// q(t), p(t) of a child's token at node n, from the raw logits (the same
+// arithmetic as decide_values)
+template <typename TL>
+__device__ void child_qp(const AcceptKernelArgs& a, int b, int n, int tok, const NodeState& st, double& qt,
+                         double& pt) {
+  const int64_t row = static_cast<int64_t>(b * a.T + n) * a.V;
+  const double xt = cut(logit<TL>(reinterpret_cast<const TL*>(a.target) + row, tok), thr_of(a, b, n, 0));
+  const double yt = cut(logit<TL>(reinterpret_cast<const TL*>(a.draft) + row, tok), thr_of(a, b, n, 1));
+  qt = exp((xt - static_cast<double>(st.mq)) * a.inv_tau) / st.zq;
+  pt = exp((yt - static_cast<double>(st.mp)) * a.inv_tau) / st.zp;
+}
+
+// Siblings drawn without replacement, on the three-kernel path: sibling i is
+// tested against the draft without the earlier siblings' tokens,
+// renormalised by the mass Z left; rejecting it moves the untried tokens'
+// residual to C + s / Z, and its own token keeps the weight max(0, q(t) -
+// C p(t)) at that new C for good (the later siblings' draft puts no mass on
+// it).  A round's mass is the full-vocabulary sum at C with the tried
+// tokens' terms replaced by their kept weights.
+struct WrLds {
+  int32_t tok[kMaxTree];
+  double qt[kMaxTree], pt[kMaxTree], kept[kMaxTree];
+  double zrem, C;
+  int32_t i, stop;
+};
+
+template <typename TL>
+__device__ void continue_siblings_wr(const AcceptKernelArgs& a, int b, int n, const TreeInfo& ti, NodeState& st,
+                                     double s_full, double* dscratch, WrLds& w) {
+  const int tid = threadIdx.x;
+  const int k = num_children(ti, a.T, n);
+  double* const kw = a.wr_kept + static_cast<int64_t>(b * a.T + n) * kMaxTree;
+  if (tid < k) {
+    const int tok = a.tokens[b * a.T + kth_child(ti, a.T, n, tid)];
+    double qt = 0.0, pt = 0.0;
+    if (tok >= 0 && tok < a.V) child_qp<TL>(a, b, n, tok, st, qt, pt);
+    w.tok[tid] = tok;
+    w.qt[tid] = qt;
+    w.pt[tid] = pt;
+    w.kept[tid] = tid < st.next_child ? kw[tid] : -1.0;
+  }
+  if (tid == 0) {
+    w.zrem = kw[kMaxTree - 1];
+    w.C = st.C;
+    w.i = st.next_child;
+  }
+  __syncthreads();
+  for (;;) {
+    if (tid == 0) {
+      int i = w.i;
+      double C = w.C;
+      double s = s_full;
+      for (int j = 0; j < i; ++j)
+        if (w.kept[j] >= 0.0) s += w.kept[j] - fmax(0.0, w.qt[j] - C * w.pt[j]);
+      if (!(s > 0.0)) {   // residual mass vanished: start over from q, tried tokens included
+        st.flags |= EAGLE_FLAG_DEGENERATE_RESIDUAL;
+        C = 0.0;
+        s = 1.0;
+        for (int j = 0; j < i; ++j)
+          if (w.kept[j] >= 0.0) w.kept[j] = w.qt[j];
+      }
+      int rep = -1;
+      for (int j = 0; j < i && rep < 0; ++j)
+        if (w.tok[j] == w.tok[i]) rep = j;
+      uint32_t fl = st.flags;
+      int32_t nr = st.near;
+      int res;
+      if (w.tok[i] < 0 || w.tok[i] >= a.V) {
+        res = -1;
+      } else if (rep >= 0 || !(w.zrem > 0.0)) {   // p_i(t) = 0: accept iff the residual keeps mass there
+        fl |= EAGLE_FLAG_P_ZERO;
+        res = (rep >= 0 ? w.kept[rep] : fmax(0.0, w.qt[i] - C * w.pt[i])) > 0.0 ? 1 : 0;
+      } else {
+        const double r = decision_uniform(a, b, n, static_cast<uint32_t>(i));
+        res = decide_pre(w.qt[i], w.pt[i] / w.zrem, r, w.tok[i], a.V, C * w.zrem, s, fl, nr);
+      }
+      st.flags = fl;
+      st.near = nr;
+      int stop = 1;
+      if (res > 0) {
+        st.kind = kNodeAccepted;
+        st.outcome = kth_child(ti, a.T, n, i);
+      } else if (res < 0) {
+        st.kind = kNodeRejected;
+        st.outcome = -1;
+      } else {
+        const double Cn = w.zrem > 0.0 ? C + s / w.zrem : C;
+        w.kept[i] = rep >= 0 ? -1.0 : fmax(0.0, w.qt[i] - Cn * w.pt[i]);
+        if (rep < 0) w.zrem -= w.pt[i];
+        C = Cn;
+        ++i;
+        if (i >= k) {
+          st.kind = kNodeRejected;
+          st.outcome = -1;
+        } else {
+          stop = 0;
+        }
+      }
+      st.C = C;
+      st.s = s;
+      st.next_child = i;
+      w.C = C;
+      w.i = i;
+      w.stop = stop;
+    }
+    __syncthreads();
+    const int stop = w.stop;
+    const double C = w.C;
+    __syncthreads();
+    if (stop) break;
+    s_full = residual_mass<TL>(a, b, n, st, C, 0, a.V, dscratch);
+  }
+  // the kept weights and the draft mass left (the terminal sample reads them)
+  if (tid < k) kw[tid] = w.kept[tid];
+  if (tid == 0) kw[kMaxTree - 1] = w.zrem;
+}
+
 // -------------------------------------------------------------- sa_stats
 template <typename TL>
 __global__ __launch_bounds__(kThreads) void sa_stats(const AcceptKernelArgs a) {
@@ -542,6 +659,13 @@ __global__ __launch_bounds__(kThreads) void sa_stats(const AcceptKernelArgs a) {
       } else if (res < 0) {
         st.kind = kNodeRejected;
       } else {
+        if (a.wr) {   // without replacement: the first sibling's token keeps max(0, q - p); Z = 1 - p(t)
+          double qt, pt;
+          child_qp<TL>(a, b, n, a.tokens[b * T + child], st, qt, pt);
+          double* const kw = a.wr_kept + static_cast<int64_t>(b * T + n) * kMaxTree;
+          kw[0] = fmax(0.0, qt - pt);
+          kw[kMaxTree - 1] = 1.0 - pt;
+        }
         st.C = 1.0;   // C_2 = C_1 + s_1
         if (num_children(ti, T, n) > 1) {
           st.kind = kNodeNeedsPass;
@@ -563,6 +687,7 @@ __global__ __launch_bounds__(kThreads) void sa_pass(const AcceptKernelArgs a) {
   __shared__ double dscr[4];
   __shared__ int32_t iscr[4];
   __shared__ int32_t last_flag;
+  __shared__ WrLds wr_lds;
   const int NC = a.NC, T = a.T;
   const int c = blockIdx.x % NC;
   const int n = (blockIdx.x / NC) % T;
@@ -577,7 +702,8 @@ __global__ __launch_bounds__(kThreads) void sa_pass(const AcceptKernelArgs a) {
   if (!arrive_last(&a.cnt_pass[b * T + n], static_cast<uint32_t>(NC), &last_flag)) return;
   double s = 0.0;
   for (int q = 0; q < NC; ++q) s += a.fpart[static_cast<int64_t>(b * T + n) * NC + q];
-  continue_siblings<TL>(a, b, n, ti, st, st.next_child, st.C, s, dscr, iscr);
+  if (a.wr) continue_siblings_wr<TL>(a, b, n, ti, st, s, dscr, wr_lds);
+  else continue_siblings<TL>(a, b, n, ti, st, st.next_child, st.C, s, dscr, iscr);
   if (threadIdx.x == 0) a.nodes[b * T + n] = st;
 }
 
@@ -605,6 +731,8 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
   __shared__ int32_t near_lds;
   __shared__ int32_t found_lds;
   __shared__ double scan_lds[kThreads];
+  __shared__ int32_t wtok[kMaxTree];     // without replacement: the tried siblings' tokens
+  __shared__ double wkept[kMaxTree];     // ... and the weights they keep (-1: a repeated token)
 
   const bool greedy = a.tau == 0.f;
   const int NC = greedy ? 1 : a.NC, T = a.T;
@@ -686,12 +814,32 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
   const TL* dr = reinterpret_cast<const TL*>(a.draft) + rowoff;
   const double izq = 1.0 / st.zq, izp = leaf ? 0.0 : 1.0 / st.zp;
   const float thq = thr_of(a, b, term, 0), thp = thr_of(a, b, term, 1);
+  // siblings drawn without replacement: a tried token's weight is the one it
+  // kept after its rejection, not the closed form max(0, q - C p)
+  const bool wr_term = a.wr && !leaf;
+  const int ntried = wr_term ? min(st.next_child, num_children(ti, T, term)) : 0;
+  if (tid < ntried) {
+    wtok[tid] = a.tokens[b * T + kth_child(ti, T, term, tid)];
+    wkept[tid] = a.wr_kept[static_cast<int64_t>(b * T + term) * kMaxTree + tid];
+  }
+  __syncthreads();
+  auto kept_weight = [&](int v, double wv) {
+    for (int j = 0; j < ntried; ++j)
+      if (wkept[j] >= 0.0 && wtok[j] == v) return wkept[j];
+    return wv;
+  };
   {
     const int v0 = c * kVocabChunk, v1 = min(a.V, v0 + kVocabChunk);
     double acc = 0.0;
     for (int v = v0 + tid; v < v1; v += kThreads) acc += terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp, thq, thp);
     acc = block_reduce(acc, AddD{}, dscr);
-    if (tid == 0) a.spart[static_cast<int64_t>(b) * NC + c] = acc;
+    if (tid == 0) {
+      if (C != 0.0)
+        for (int j = 0; j < ntried; ++j)
+          if (wkept[j] >= 0.0 && wtok[j] >= v0 && wtok[j] < v1)
+            acc += wkept[j] - terminal_weight<TL>(tr, dr, wtok[j], st, C, leaf, a.c2, izq, izp, thq, thp);
+      a.spart[static_cast<int64_t>(b) * NC + c] = acc;
+    }
   }
   if (!arrive_last(&a.cnt_final[b], static_cast<uint32_t>(NC), &last_flag)) return;
 
@@ -733,6 +881,7 @@ __global__ __launch_bounds__(kThreads) void sa_final(const AcceptKernelArgs a) {
   for (int j = 0; j < kPerThread; ++j) {
     const int v = v0 + tid * kPerThread + j;
     w[j] = (v < v1) ? terminal_weight<TL>(tr, dr, v, st, C, leaf, a.c2, izq, izp, thq, thp) : 0.0;
+    if (ntried && C != 0.0 && v < v1) w[j] = kept_weight(v, w[j]);
     tsum += w[j];
   }
   scan_lds[tid] = tsum;

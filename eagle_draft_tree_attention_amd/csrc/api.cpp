@@ -83,6 +83,8 @@ size_t accept_layout(int64_t Bm, int64_t Tm, int NC, size_t off, char* base, Wor
   off = align_up(off + sizeof(uint64_t) * Bm * Tm, 256);
   const size_t o_round = off;
   off = align_up(off + sizeof(uint64_t) * 2 * Bm * Tm * kRoundWords, 256);
+  const size_t o_wr = off;
+  off = align_up(off + sizeof(double) * Bm * Tm * kMaxTree, 256);
   const size_t o_thr = off;
   off = align_up(off + sizeof(float) * 2 * Bm * Tm, 256);
   const size_t o_thr_near = off;
@@ -95,6 +97,7 @@ size_t accept_layout(int64_t Bm, int64_t Tm, int NC, size_t off, char* base, Wor
     ws->counters = reinterpret_cast<uint32_t*>(base + o_cnt);
     ws->node_pub = reinterpret_cast<uint64_t*>(base + o_sync);
     ws->round_sum = reinterpret_cast<uint64_t*>(base + o_round);
+    ws->wr_kept = reinterpret_cast<double*>(base + o_wr);
     ws->thr = reinterpret_cast<float*>(base + o_thr);
     ws->thr_near = reinterpret_cast<int32_t*>(base + o_thr_near);
   }
@@ -173,13 +176,8 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
   const int64_t per_seq = static_cast<int64_t>(k.T) * k.NC;
   k.wr = (a->without_replacement && a->temperature > 0.f) ? 1 : 0;
   if (per_seq > cap || k.NC > 64) {
-    if (k.wr) {
-      std::snprintf(err, errlen,
-                    "siblings without replacement need the fused path: %lld workgroups per sequence, %lld resident",
-                    static_cast<long long>(per_seq), static_cast<long long>(cap));
-      return EAGLE_ERR_UNSUPPORTED;
-    }
     k.fused = 0;
+    k.wr_kept = ws.wr_kept;
     const int e = launch_spec_accept(k, bf16, hip_stream);
     if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
     return EAGLE_OK;

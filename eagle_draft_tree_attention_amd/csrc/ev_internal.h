@@ -127,7 +127,11 @@ struct AcceptKernelArgs {
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
   int fused;              // 1: one co-resident kernel; 0: three-kernel path
   int b0;                 // batch index of sequence 0 of this launch (a slice of the call's batch)
-  int wr;                 // 1: siblings were drawn without replacement (fused path only)
+  int wr;                 // 1: siblings were drawn without replacement
+  // three-kernel path with wr: per node, the residual weight each tried
+  // sibling's token keeps ([B][T][kMaxTree], -1 for a repeated token) and, in
+  // the last slot, the draft mass not yet tried
+  double* wr_kept;
   int B, T, V, NC;
   int vec_ok;          // rows start 16-byte aligned
   // filtered distributions: logits below thr[(b * T + n) * 2 + r] count as
@@ -230,6 +234,7 @@ struct Workspace {
   double* spart = nullptr;
   uint32_t* counters = nullptr; // cnt_stats | cnt_pass | cnt_final
   ChunkRecord* expand = nullptr; // [max_batch][max_tree_rows][expansion chunks of a row]
+  double* wr_kept = nullptr;     // [max_batch][max_tree_rows][kMaxTree] (three-kernel path, without replacement)
   float* thr = nullptr;          // [max_batch][max_tree_rows][2] keep-thresholds of filtered rows
   int32_t* thr_near = nullptr;   // [max_batch][max_tree_rows][2]
   size_t bytes = 0;

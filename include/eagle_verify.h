@@ -164,9 +164,7 @@ typedef struct {
  *                same distribution (a repeated token has probability 0 there:
  *                accepted iff the residual keeps mass on it); 0: i.i.d.
  *                siblings, every sibling against the parent's draft row.
- *                Ignored when temperature == 0.  Only for calls whose
- *                sequences each fit the fused kernel (T x ceil(V / 8192)
- *                workgroups resident at once), else EAGLE_ERR_UNSUPPORTED.
+ *                Ignored when temperature == 0.
  *   top_k, top_p filtered distributions (the request's sampling filters):
  *                with temperature > 0, q and p are both replaced by their
  *                filtered and renormalised versions before the walk, and the

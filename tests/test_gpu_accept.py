@@ -360,15 +360,26 @@ def test_without_replacement_with_repeated_tokens():
     ver.close()
 
 
-def test_without_replacement_needs_the_fused_path():
-    from eagle_draft_tree_attention_amd._abi import EagleVerifyError
-    spec = small_spec("wr_general", B=1, V=520000, levels=(10,) * 6)
+def test_without_replacement_on_the_three_kernel_path():
+    """Sequences too large for the fused kernel (61 rows x 64 vocabulary
+    chunks): siblings drawn without replacement, many residual rounds, one
+    sequence with repeated tokens, and top-k / top-p filters on top."""
+    spec = small_spec("wr_general", B=2, V=520000, levels=(10,) * 6, sigma_d=2.0)
+    log(f"[accept] without replacement, three-kernel path: V {spec.vocab}")
     inp = synth.make_inputs(spec, with_kv=False)
+    tok = _tokens_without_replacement(spec, inp, np.random.default_rng(4), 1.0)
+    tok[1] = inp.tokens[1]                     # i.i.d. siblings: tokens may repeat
     ver = make_verifier(spec, inp.T)
-    with pytest.raises(EagleVerifyError) as e:
-        ver.spec_accept(dev(inp.target, "bf16"), dev(inp.draft, "bf16"), dev(inp.parents), dev(inp.tokens), 1.0,
-                        SEED, 0, without_replacement=True)
-    assert "fused path" in str(e.value)
+    t64, d64 = inp.target64(), inp.draft64()
+    diverged = 0
+    for k, p, offs in ((0, 0.0, 3), (50, 0.95, 1)):
+        for off in range(offs):
+            got = run_accept(ver, inp, 1.0, SEED, off, tokens=tok, without_replacement=True, top_k=k, top_p=p)
+            ref = oacc.spec_accept(t64, d64, inp.parents, tok, 1.0, SEED, off, without_replacement=True,
+                                   top_k=k, top_p=p)
+            diverged += compare_accept(got, ref, f"wr general k {k} p {p} offset {off}", inp.parents, tok,
+                                       spec.vocab)
+    assert diverged <= excused_bound(4 * spec.batch)
     ver.close()
 
 
