@@ -1330,7 +1330,8 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   uint64_t* const npub = pubs + n;
 
   auto fail_internal = [&]() {
-    if (tid == 0) atomicOr(&a.flags[b], EAGLE_FLAG_INTERNAL);
+    if (tid == 0) __hip_atomic_fetch_or(&a.flags[b], static_cast<uint32_t>(EAGLE_FLAG_INTERNAL), __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_SYSTEM);
   };
 
   // ---- sequence validity (the same verdict in every workgroup of b) and
@@ -1360,6 +1361,24 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     return;
   }
   if (n >= Tr) return;   // a padding row: nothing reads or waits for it
+  // The root's first workgroup poisons the sequence's outputs (flag
+  // INTERNAL) before its first publication, with stores that go through to
+  // memory.  The workgroup that writes the real outputs waits for that
+  // publication, so it overwrites them afterwards; if a bounded wait expires
+  // and nobody writes them, the caller finds them poisoned and flagged.
+  if (n == 0 && c == 0) {
+    if (tid == 0) {
+      __hip_atomic_store(&a.accept_len[b], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&a.flags[b], static_cast<uint32_t>(EAGLE_FLAG_INTERNAL), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&a.near_ties[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    for (int j = tid; j < T; j += kThreads) {
+      __hip_atomic_store(&a.accepted_nodes[b * T + j], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(&a.out_tokens[b * T + j], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    stores_done();   // complete before the barriers that precede the first publication
+  }
   const bool tb = lane >= 1 && lane < Tr && (tok < 0 || tok >= V);
   const bool is_child = lane >= 1 && lane < Tr && par == n;
   const uint64_t kids_mask = __ballot(is_child);
@@ -1998,19 +2017,26 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
 }
 
+// The fused kernel's workgroups wait for each other: launched cooperatively,
+// the runtime either makes all of them resident at once or refuses the
+// launch (hipErrorCooperativeLaunchTooLarge, nothing enqueued; the caller
+// then takes the three-kernel path).
+hipError_t launch_fused(const void* fn, dim3 grid, dim3 block, const AcceptKernelArgs& a, hipStream_t st) {
+  void* args[] = {const_cast<AcceptKernelArgs*>(&a)};
+  if (a.coop) return hipLaunchCooperativeKernel(fn, grid, block, args, 0, st);
+  return hipLaunchKernel(fn, grid, block, args, 0, st);
+}
+
 template <typename TL>
 hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
   const dim3 block(kThreads);
   if (a.fused) {
     const dim3 grid(static_cast<unsigned>(a.B * a.T * a.NC));
-    if (a.wr) {
-      if (a.vec_ok) hipLaunchKernelGGL((sa_fused<TL, true, true>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((sa_fused<TL, false, true>), grid, block, 0, st, a);
-    } else {
-      if (a.vec_ok) hipLaunchKernelGGL((sa_fused<TL, true, false>), grid, block, 0, st, a);
-      else hipLaunchKernelGGL((sa_fused<TL, false, false>), grid, block, 0, st, a);
-    }
-    return hipGetLastError();
+    const void* fn = a.wr ? (a.vec_ok ? reinterpret_cast<const void*>(&sa_fused<TL, true, true>)
+                                      : reinterpret_cast<const void*>(&sa_fused<TL, false, true>))
+                          : (a.vec_ok ? reinterpret_cast<const void*>(&sa_fused<TL, true, false>)
+                                      : reinterpret_cast<const void*>(&sa_fused<TL, false, false>));
+    return launch_fused(fn, grid, block, a, st);
   }
   hipLaunchKernelGGL((sa_stats<TL>), dim3(static_cast<unsigned>(a.B * a.T * 2 * a.NC)), block, 0, st, a);
   hipError_t e = hipGetLastError();

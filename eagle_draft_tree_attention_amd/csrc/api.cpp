@@ -27,6 +27,8 @@ struct eagle_verify {
   bool have_plan = false;
   int attn_cap[2][ev::kMfmaVariants] = {};   // co-resident MFMA attention workgroups [D == 128][kernel variant]
   int fused_cap[2] = {0, 0};   // co-resident fused-acceptance workgroups (f32, bf16)
+  uint32_t spin_limit = ev::kSpinLimit;   // polls of a bounded device-side wait
+  bool coop = false;           // cooperative launches of the self-synchronising kernels (opt-in)
   char err[512] = {0};
 };
 
@@ -106,9 +108,25 @@ size_t accept_layout(int64_t Bm, int64_t Tm, int NC, size_t off, char* base, Wor
 
 void set_thread_error(const char* msg) { std::snprintf(g_err, sizeof(g_err), "%s", msg); }
 
+bool cooperative_from_env() {
+  // opt-in: a cooperative launch costs about 16 us more per launch on this
+  // stack (measured: the 8B verification step 55.7 -> 91.5 us), so by default
+  // residency rests on the occupancy check and the bounded waits
+  const char* s = std::getenv("EAGLE_VERIFY_COOPERATIVE");
+  return s && s[0] == '1';
+}
+
+uint32_t spin_limit_from_env() {
+  // a test knob: the polls a bounded device-side wait makes before it gives up
+  const char* s = std::getenv("EAGLE_VERIFY_SPIN_LIMIT");
+  if (!s || !*s) return kSpinLimit;
+  const long v = std::strtol(s, nullptr, 10);
+  return v < 0 ? kSpinLimit : static_cast<uint32_t>(std::min<long>(v, kSpinLimit));
+}
+
 eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws, int64_t Bm, int64_t Tm,
                              int64_t cap, AcceptCallState* cs, const eagle_spec_accept_args* a, void* hip_stream,
-                             char* err, size_t errlen) {
+                             char* err, size_t errlen, uint32_t spin_limit, bool coop) {
   AcceptKernelArgs k;
   std::memset(&k, 0, sizeof(k));
   const int V = desc.vocab_size;
@@ -145,7 +163,7 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
   k.node_pub = ws.node_pub;
   k.Tm = static_cast<int>(Tm);
   k.epoch = ++cs->epoch;
-  k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)
+  k.spin_limit = spin_limit;
   // The fused kernel needs every workgroup of a launch resident at once.  A
   // batch that does not fit is verified in slices of whole sequences, one
   // fused launch each, back to back on the stream (each slice is a fused
@@ -211,7 +229,18 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
     k.round_sum = ws.round_sum + parity * half;
     k.round_clear = ws.round_sum + (1 - parity) * half;
     k.zero_b = cs->last_fused_b;
-    const int e = launch_spec_accept(k, bf16, hip_stream);
+    k.coop = coop ? 1 : 0;
+    int e = launch_spec_accept(k, bf16, hip_stream);
+    if (e == static_cast<int>(hipErrorCooperativeLaunchTooLarge)) {
+      // the slice's workgroups cannot all be resident now: the three-kernel
+      // path (no waiting between workgroups) verifies it instead
+      (void)hipGetLastError();
+      k.fused = 0;
+      k.wr_kept = ws.wr_kept;
+      e = launch_spec_accept(k, bf16, hip_stream);
+      if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
+      continue;
+    }
     if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
     ++cs->fused_calls;
     cs->last_fused_b = k.B;
@@ -272,6 +301,8 @@ eagle_status eagle_verify_create(const eagle_verify_desc* desc, eagle_verify** o
   h->ws.expand = reinterpret_cast<ev::ChunkRecord*>(p + o_expand);
   ev::accept_layout(B, T, static_cast<int>(NC), o_accept, p, &h->ws);
   h->ws.bytes = off;
+  h->spin_limit = ev::spin_limit_from_env();
+  h->coop = ev::cooperative_from_env();
   h->fused_cap[0] = ev::fused_accept_capacity(0, h->num_cus);
   h->fused_cap[1] = ev::fused_accept_capacity(1, h->num_cus);
   // the in-kernel split merge can be switched off for comparison (EAGLE_VERIFY_ATTN_FUSED_MERGE=0)
@@ -351,7 +382,7 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
     packed += need;
   }
   k.epoch = ++h->attn_epoch;
-  k.spin_limit = 1u << 16;   // each poll reloads the m/l words (about a microsecond)
+  k.spin_limit = h->spin_limit;
   k.mlrec = reinterpret_cast<uint64_t*>(k.mlpart + 2 * plan.workgroups * static_cast<int64_t>(plan.rows_per_tile));
   // the splits merge inside the kernel when every workgroup is resident at
   // once (they wait for each other); otherwise a separate merge kernel runs
@@ -372,7 +403,13 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
     return EAGLE_ERR_CAPACITY;
   }
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
-  const int e = ev::launch_tree_attention(plan, k, h->desc.kv_dtype == EAGLE_BF16, stream);
+  k.coop = h->coop ? 1 : 0;
+  int e = ev::launch_tree_attention(plan, k, h->desc.kv_dtype == EAGLE_BF16, stream);
+  if (e == static_cast<int>(hipErrorCooperativeLaunchTooLarge) && k.fused_merge) {
+    (void)hipGetLastError();
+    k.fused_merge = 0;   // not every workgroup fits at once: merge in a separate kernel
+    e = ev::launch_tree_attention(plan, k, h->desc.kv_dtype == EAGLE_BF16, stream);
+  }
   h->last_stream = stream;
   h->used = true;
   if (e != 0) return hip_fail(h, "tree attention launch", e);
@@ -394,7 +431,7 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   h->used = true;
   const int64_t cap = h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0];
   st = ev::run_spec_accept(h->desc, h->ws, h->desc.max_batch, h->desc.max_tree_rows, cap, &h->accept_state, a,
-                           hip_stream, h->err, sizeof(h->err));
+                           hip_stream, h->err, sizeof(h->err), h->spin_limit, h->coop);
   if (st == EAGLE_OK) h->err[0] = 0;
   return st;
 }

@@ -783,8 +783,14 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
       wsm[np + p] = __uint_as_float(static_cast<uint32_t>(wl));
     }
     if (__syncthreads_and(ready)) break;
-    if (it >= a.spin_limit) {
-      if (tid == 0) atomicOr(&a.flags[b], EAGLE_FLAG_INTERNAL);
+    if (it >= a.spin_limit) {   // gave up: this split's rows are poisoned and the sequence flagged
+      for (int e = tid; e < nr * D; e += 256) {
+        const int r = rt * rpt + r_lo + e / D;
+        a.out[((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + e % D] = __builtin_nanf("");
+      }
+      if (tid == 0)
+        __hip_atomic_fetch_or(&a.flags[b], static_cast<uint32_t>(EAGLE_FLAG_INTERNAL), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_SYSTEM);
       return;
     }
     __builtin_amdgcn_s_sleep(2);
@@ -1064,21 +1070,30 @@ hipError_t launch_d(const AttnPlan& p, const AttnKernelArgs& a, int kv_bf16, hip
   if (p.path == 1) {
     const dim3 grid((unsigned)p.workgroups), block(256);
     const int v = mfma_variant(p);
+    const void* fn = nullptr;
     if (a.page_size) {
       switch (v) {
-        case 0: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 1, true>), grid, block, 0, st, a); break;
-        case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2, 1, true>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 2, true>), grid, block, 0, st, a); break;
+        case 0: fn = reinterpret_cast<const void*>(&tree_attn_mfma<D, 1, 2, 1, true>); break;
+        case 1: fn = reinterpret_cast<const void*>(&tree_attn_mfma<D, 2, 2, 1, true>); break;
+        case 2: fn = reinterpret_cast<const void*>(&tree_attn_mfma<D, 1, 2, 2, true>); break;
         default: return hipErrorInvalidValue;
       }
     } else {
       switch (v) {
-        case 0: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 1>), grid, block, 0, st, a); break;
-        case 1: hipLaunchKernelGGL((tree_attn_mfma<D, 2, 2, 1>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((tree_attn_mfma<D, 1, 2, 2>), grid, block, 0, st, a); break;
+        case 0: fn = reinterpret_cast<const void*>(&tree_attn_mfma<D, 1, 2, 1>); break;
+        case 1: fn = reinterpret_cast<const void*>(&tree_attn_mfma<D, 2, 2, 1>); break;
+        case 2: fn = reinterpret_cast<const void*>(&tree_attn_mfma<D, 1, 2, 2>); break;
         default: return hipErrorInvalidValue;
       }
     }
+    // with the merge inside, the splits wait for each other: a cooperative
+    // launch makes every workgroup resident at once or is refused
+    // (hipErrorCooperativeLaunchTooLarge, nothing enqueued; the caller then
+    // runs the separate merge kernel)
+    void* args[] = {const_cast<AttnKernelArgs*>(&a)};
+    const hipError_t e = (a.fused_merge && a.coop) ? hipLaunchCooperativeKernel(fn, grid, block, args, 0, st)
+                                                   : hipLaunchKernel(fn, grid, block, args, 0, st);
+    if (e != hipSuccess) return e;
   } else {
     const dim3 grid((unsigned)p.workgroups), block(64);
     if (kv_bf16)

@@ -59,6 +59,7 @@ struct AttnKernelArgs {
   // (sequence, KV head, row tile) merges a slice of its rows once every
   // split has published the tagged m/l words of those rows
   int fused_merge;
+  int coop;            // host side: launch the merge-inside kernel cooperatively
   int late_priority;   // raise the wave priority of the later half of the grid
   uint32_t spin_limit; // polls of the bounded wait; an expired wait flags EAGLE_FLAG_INTERNAL
   uint64_t epoch;      // strictly increasing per attention call on a handle (tags use its low 32 bits)
@@ -126,6 +127,7 @@ struct AcceptKernelArgs {
   uint64_t epoch;         // strictly increasing per call on a handle
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
   int fused;              // 1: one co-resident kernel; 0: three-kernel path
+  int coop;               // host side: launch the fused kernel cooperatively
   int b0;                 // batch index of sequence 0 of this launch (a slice of the call's batch)
   int wr;                 // 1: siblings were drawn without replacement
   // three-kernel path with wr: per node, the residual weight each tried
@@ -261,7 +263,18 @@ struct AcceptCallState {
 // fused-acceptance workgroups.  Messages go to err.
 eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws, int64_t Bm, int64_t Tm,
                              int64_t fused_cap, AcceptCallState* cs, const eagle_spec_accept_args* a,
-                             void* stream, char* err, size_t errlen);
+                             void* stream, char* err, size_t errlen, uint32_t spin_limit, bool coop);
+
+// Polls of a bounded device-side wait (each about a microsecond): past it the
+// wait gives up and flags the sequence EAGLE_FLAG_INTERNAL.  The environment
+// variable EAGLE_VERIFY_SPIN_LIMIT lowers it (tests of the give-up path).
+constexpr uint32_t kSpinLimit = 1u << 16;
+uint32_t spin_limit_from_env();
+// cooperative launches of the kernels whose workgroups wait for each other:
+// EAGLE_VERIFY_COOPERATIVE=1 (read when a handle is created) guarantees that
+// every workgroup is resident (a refused launch falls back to the paths that
+// do not wait), at a cost of about 16 us per launch
+bool cooperative_from_env();
 
 // thread-local message returned by eagle_verify_last_error(NULL)
 void set_thread_error(const char* msg);

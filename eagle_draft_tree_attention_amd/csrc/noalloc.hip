@@ -122,7 +122,8 @@ extern "C" EAGLE_API eagle_status eagle_verify_spec_accept_noalloc(const eagle_v
   ev::accept_layout(a->batch, a->tree_rows, NC, 0, reinterpret_cast<char*>(ds.ptr), &ws);
   ev::AcceptCallState cs;   // fresh: the cleared scratch holds no earlier epoch
   const int64_t cap = ds.fused_cap[desc->logits_dtype == EAGLE_BF16 ? 1 : 0];
-  st = ev::run_spec_accept(*desc, ws, a->batch, a->tree_rows, cap, &cs, a, hip_stream, msg, sizeof(msg));
+  st = ev::run_spec_accept(*desc, ws, a->batch, a->tree_rows, cap, &cs, a, hip_stream, msg, sizeof(msg),
+                           ev::spin_limit_from_env(), ev::cooperative_from_env());
   ev::set_thread_error(st == EAGLE_OK ? "" : msg);
   return st;
 }

@@ -77,7 +77,9 @@ typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
 #define EAGLE_FLAG_BAD_KV_RANGE 32u     /* kv_indptr[b..b+1] does not hold L_b + T rows
                                            inside [0, num_kv_rows)                       */
 #define EAGLE_FLAG_INTERNAL 64u         /* a bounded device-side wait expired (workgroups
-                                           not co-resident); outputs are not valid       */
+                                           not co-resident, e.g. other kernels occupied
+                                           the device): the sequence's outputs are
+                                           poisoned (-1 / NaN rows); retry the call     */
 
 #define EAGLE_MAX_TREE_ROWS 64 /* T = root + up to 63 draft nodes */
 
