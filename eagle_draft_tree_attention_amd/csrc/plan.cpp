@@ -10,6 +10,8 @@
 
 #include "ev_internal.h"
 
+static_assert(sizeof(eagle_dtype) == sizeof(int32_t), "dtype fields are 32-bit in the C ABI");
+
 namespace ev {
 namespace {
 
@@ -53,8 +55,11 @@ eagle_status check_desc(const eagle_verify_desc* d, char* err, size_t errlen) {
     return fail(EAGLE_ERR_ARG, err, errlen, "max_tree_rows=%d outside [1, %d]", d->max_tree_rows, kMaxTree);
   if (d->vocab_size < 2 || d->vocab_size > (1 << 30))
     return fail(EAGLE_ERR_ARG, err, errlen, "vocab_size=%d outside [2, 2^30]", d->vocab_size);
-  if ((d->kv_dtype != EAGLE_F32 && d->kv_dtype != EAGLE_BF16) ||
-      (d->logits_dtype != EAGLE_F32 && d->logits_dtype != EAGLE_BF16))
+  // a C caller may store any integer in the enum fields: read their bits
+  int32_t kvd, lgd;
+  std::memcpy(&kvd, &d->kv_dtype, sizeof(kvd));
+  std::memcpy(&lgd, &d->logits_dtype, sizeof(lgd));
+  if ((kvd != EAGLE_F32 && kvd != EAGLE_BF16) || (lgd != EAGLE_F32 && lgd != EAGLE_BF16))
     return fail(EAGLE_ERR_ARG, err, errlen, "unknown dtype");
   return EAGLE_OK;
 }
