@@ -65,7 +65,8 @@ def workload_bytes(spec, T, parents):
     out = B * T * Hq * D * 4
     logits = 2 * B * T * V * lsz
     internal = sum(1 for b in range(B) for n in range(T) if (parents[b] == n).any())
-    logits_read = B * T * V * lsz + internal * V * lsz      # target rows + draft rows with children
+    # target rows + draft rows with children; greedy decoding reads no draft row
+    logits_read = B * T * V * lsz + (internal * V * lsz if spec.temperature > 0 else 0)
     return {
         "metric_bytes": prefix_kv + logits,                 # prefix KV + logits read once
         "attention_bytes": prefix_kv + tree_kv + q + out,   # one tree-attention launch
@@ -114,9 +115,10 @@ def cpu_baseline(inp, spec, budget_s):
     The sample: `n` whole nodes (every query head) of tree attention from
     each sequence of the batch, and one acceptance call over the whole batch
     at offset 0.  It is timed best of 3 with the BLAS pool limited to one
-    thread, then best of 3 with the BLAS pool's own thread count; the step
-    time is extrapolated to all T nodes of every sequence.  The acceptance
-    walk is scalar Python either way."""
+    thread, then best of 3 with the BLAS pool's own thread count; the faster
+    leg is the reported value and its thread count the reported cores.  The
+    step time is extrapolated to all T nodes of every sequence.  The
+    acceptance walk is scalar Python either way."""
     import numpy as np
     from oracle import accept as oacc
     from oracle import attention as oatt
@@ -175,18 +177,21 @@ def cpu_baseline(inp, spec, budget_s):
             used = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
             best = min(run_once() for _ in range(3))
         legs[label] = {"step_s": best, "value": (B * (T - 1)) / best, "blas_threads": used}
+    # the faster leg is the baseline (small per-head products can run slower
+    # on a multi-threaded BLAS pool than on one thread)
+    best_leg = max(legs, key=lambda k: legs[k]["value"])
     return {
-        "value": legs["all_cores"]["value"],
+        "value": legs[best_leg]["value"],
         "unit": "nodes/s",
-        "cores": legs["all_cores"]["blas_threads"],
+        "cores": legs[best_leg]["blas_threads"],
         "kind": "oracle",
         "affinity_cores": affinity,
-        "one_thread_value": legs["one_thread"]["value"],
-        "step_s": {k: v["step_s"] for k, v in legs.items()},
+        "legs": {k: {"value": v["value"], "blas_threads": v["blas_threads"], "step_s": v["step_s"]}
+                 for k, v in legs.items()},
         "sample": (f"fp64 oracle on the host: tree attention for {n} of {T} nodes x {Hq} heads of each of "
                    f"{B} sequence(s) (extrapolated to all {T} nodes) plus one acceptance call over the batch; "
                    f"best of 3 with 1 BLAS thread and with {legs['all_cores']['blas_threads']} "
-                   f"(affinity {affinity} cores); K/V setup {setup:.1f} s excluded"),
+                   f"(affinity {affinity} cores), the faster leg reported; K/V setup {setup:.1f} s excluded"),
     }
 
 
