@@ -42,7 +42,7 @@ from .verify import (  # noqa: E402,F401
     eagle_verify_last_error, eagle_verify_check_tree_attention, eagle_verify_check_spec_accept,
     eagle_verify_last_attention_plan, eagle_verify_kv_commit, eagle_verify_check_kv_commit,
     eagle_verify_tree_expand, eagle_verify_check_tree_expand, eagle_verify_tree_rerank,
-    eagle_verify_check_tree_rerank, Verifier, make_desc,
+    eagle_verify_check_tree_rerank, eagle_verify_set_timeline, Verifier, make_desc,
 )
 
 

@@ -21,6 +21,7 @@ EXPORTED_SYMBOLS = (
     "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan", "eagle_verify_kv_commit",
     "eagle_verify_check_kv_commit", "eagle_verify_tree_expand", "eagle_verify_check_tree_expand",
     "eagle_verify_tree_rerank", "eagle_verify_check_tree_rerank", "eagle_verify_spec_accept_noalloc",
+    "eagle_verify_set_timeline",
 )
 
 
@@ -104,6 +105,8 @@ def bind(lib):
     lib.eagle_verify_check_spec_accept.restype = C.c_int
     lib.eagle_verify_last_attention_plan.argtypes = [H, C.POINTER(AttentionPlan)]
     lib.eagle_verify_last_attention_plan.restype = C.c_int
+    lib.eagle_verify_set_timeline.argtypes = [H, C.c_void_p, C.c_int64]
+    lib.eagle_verify_set_timeline.restype = C.c_int
     lib.eagle_verify_kv_commit.argtypes = [H, C.POINTER(KvCommitArgs), C.c_void_p]
     lib.eagle_verify_kv_commit.restype = C.c_int
     lib.eagle_verify_check_kv_commit.argtypes = [C.POINTER(VerifyDesc), C.POINTER(KvCommitArgs)]

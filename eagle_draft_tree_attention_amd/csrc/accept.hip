@@ -1316,6 +1316,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   const uint64_t base = a.epoch << 20;
   const uint32_t limit = a.spin_limit;
   const bool lead = (c == 0);   // publishes the node's state for the other nodes' groups
+  stamp(a.stamps, 0);
 
   // the round words of the previous fused call start this call's successor at zero
   {
@@ -1427,6 +1428,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       *reinterpret_cast<u32x4_t*>(lq + group_index<TL>(jj)) = wq[jj];
       if (two) *reinterpret_cast<u32x4_t*>(lp + group_index<TL>(jj)) = wd[jj];
     }
+    stamp(a.stamps, 1);   // the chunk has arrived
     mq_c = local_max<TL, NV>(wq);
     if (two) mp_c = local_max<TL, NV>(wd);
     block_reduce2(mq_c, mp_c, MaxOp{}, sh.fscr);
@@ -1452,6 +1454,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       zp_c = lzp;
     }
   }
+  stamp(a.stamps, 2);   // chunk statistics
   // Chunk statistics go out as four 64-bit words per row, each carrying the
   // call's tag in its high half (m, z low, z high, argmax | bad << 31), and
   // are read back by polling the words themselves: no arrival counter.
@@ -1532,6 +1535,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
   __syncthreads();
   if (!sh.ok) return fail_internal();
+  stamp(a.stamps, 3);   // row statistics combined
   if (tid == 0 && two) sh.st.flags |= static_cast<uint32_t>(sh.iscr[1]);
   __syncthreads();
   if (tid < 64) {
@@ -1594,6 +1598,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
   __syncthreads();
 
+  stamp(a.stamps, 4);   // first decision
   // ---- residual-mass rounds from LDS
   const bool q_live = mq_c != kNegInf, p_live = two && mp_c != kNegInf;
   const float mqs = q_live ? mq_c : 0.f, mps = p_live ? mp_c : 0.f;
@@ -1656,8 +1661,13 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     }
     __syncthreads();
     if (!sh.ok) return fail_internal();
+    if (round < 12) stamp(a.stamps, 5 + round);   // end of residual round
     ++round;
   }
+  stamp_value(a.stamps, 30, static_cast<uint64_t>(round));
+  stamp_value(a.stamps, 31, static_cast<uint64_t>(n) | (static_cast<uint64_t>(c) << 8) |
+                                (static_cast<uint64_t>(sh.st.kind) << 16) | (static_cast<uint64_t>(b) << 24));
+  stamp(a.stamps, 17);   // node decided
 
   // ---- sequence verdict: workgroup 0 of the root waits for every node's
   // first publication and writes the poisoned outputs if any row was
@@ -1745,6 +1755,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     return;
   }
 
+  stamp(a.stamps, 18);   // terminal preparation starts
   // ---- terminal distribution of this node, prepared before the walk is
   // known to end here (it overlaps the walk): inverse CDF of the residual
   // max(0, q - C p) (of q at a leaf; of q again if the residual mass is
@@ -1881,6 +1892,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     cstar = sh.iscr[3] & 0x3FFFFFFF;
     degen = (sh.iscr[3] & 0x40000000) != 0;
   }
+  stamp(a.stamps, 19);   // the chunk holding u*S is known
   // only the workgroup that samples (the chunk holding u*S; chunk 0 in
   // greedy mode) needs to know whether the walk ends here
   if (c != (greedy ? 0 : cstar)) return;
@@ -1911,6 +1923,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   __syncthreads();
   if (!sh.ok) return fail_internal();
   if (!sh.onpath) return;
+  stamp(a.stamps, 20);   // the walk ends here
   const int len = plen - 1;   // accepted draft nodes
 
   // ---- terminal sample (the workgroup of the chunk holding u*S)
@@ -2015,6 +2028,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     a.accepted_nodes[b * T + j] = (j < len) ? path_lds[j + 1] : -1;
     a.out_tokens[b * T + j] = (j < len) ? a.tokens[b * T + path_lds[j + 1]] : (j == len ? final_tok : -1);
   }
+  stamp(a.stamps, 21);   // outputs written
 }
 
 // The fused kernel's workgroups wait for each other: launched cooperatively,

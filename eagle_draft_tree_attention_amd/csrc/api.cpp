@@ -29,6 +29,8 @@ struct eagle_verify {
   int fused_cap[2] = {0, 0};   // co-resident fused-acceptance workgroups (f32, bf16)
   uint32_t spin_limit = ev::kSpinLimit;   // polls of a bounded device-side wait
   bool coop = false;           // cooperative launches of the self-synchronising kernels (opt-in)
+  uint64_t* stamps = nullptr;  // diagnostic phase timeline (caller's device words), or NULL
+  int64_t stamp_words = 0;
   char err[512] = {0};
 };
 
@@ -126,7 +128,8 @@ uint32_t spin_limit_from_env() {
 
 eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws, int64_t Bm, int64_t Tm,
                              int64_t cap, AcceptCallState* cs, const eagle_spec_accept_args* a, void* hip_stream,
-                             char* err, size_t errlen, uint32_t spin_limit, bool coop) {
+                             char* err, size_t errlen, uint32_t spin_limit, bool coop, uint64_t* stamps,
+                             int64_t stamp_words) {
   AcceptKernelArgs k;
   std::memset(&k, 0, sizeof(k));
   const int V = desc.vocab_size;
@@ -230,6 +233,7 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
     k.round_clear = ws.round_sum + (1 - parity) * half;
     k.zero_b = cs->last_fused_b;
     k.coop = coop ? 1 : 0;
+    k.stamps = (stamps && static_cast<int64_t>(k.B) * per_seq * kStampSlots <= stamp_words) ? stamps : nullptr;
     int e = launch_spec_accept(k, bf16, hip_stream);
     if (e == static_cast<int>(hipErrorCooperativeLaunchTooLarge)) {
       // the slice's workgroups cannot all be resident now: the three-kernel
@@ -384,6 +388,7 @@ eagle_status eagle_verify_tree_attention(eagle_verify* h, const eagle_tree_atten
   k.epoch = ++h->attn_epoch;
   k.spin_limit = h->spin_limit;
   k.mlrec = reinterpret_cast<uint64_t*>(k.mlpart + 2 * plan.workgroups * static_cast<int64_t>(plan.rows_per_tile));
+  k.stamps = (h->stamps && plan.workgroups * ev::kStampSlots <= h->stamp_words) ? h->stamps : nullptr;
   // the splits merge inside the kernel when every workgroup is resident at
   // once (they wait for each other); otherwise a separate merge kernel runs
   // once every workgroup has arrived, the weights of the rows a split merges
@@ -431,7 +436,7 @@ eagle_status eagle_verify_spec_accept(eagle_verify* h, const eagle_spec_accept_a
   h->used = true;
   const int64_t cap = h->fused_cap[h->desc.logits_dtype == EAGLE_BF16 ? 1 : 0];
   st = ev::run_spec_accept(h->desc, h->ws, h->desc.max_batch, h->desc.max_tree_rows, cap, &h->accept_state, a,
-                           hip_stream, h->err, sizeof(h->err), h->spin_limit, h->coop);
+                           hip_stream, h->err, sizeof(h->err), h->spin_limit, h->coop, h->stamps, h->stamp_words);
   if (st == EAGLE_OK) h->err[0] = 0;
   return st;
 }
@@ -561,6 +566,21 @@ eagle_status eagle_verify_check_tree_attention(const eagle_verify_desc* desc, co
   if (st != EAGLE_OK) return st;
   if (plan) public_plan(p, plan);
   g_err[0] = 0;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify_set_timeline(eagle_verify* h, uint64_t* device_words, int64_t num_words) {
+  if (!h) {
+    set_err(nullptr, "handle is NULL");
+    return EAGLE_ERR_ARG;
+  }
+  if (num_words < 0 || (reinterpret_cast<uintptr_t>(device_words) & 7u) != 0) {
+    set_err(h, "timeline: num_words < 0 or device_words not 8-byte aligned");
+    return EAGLE_ERR_ARG;
+  }
+  h->stamps = (device_words && num_words > 0) ? device_words : nullptr;
+  h->stamp_words = h->stamps ? num_words : 0;
+  h->err[0] = 0;
   return EAGLE_OK;
 }
 

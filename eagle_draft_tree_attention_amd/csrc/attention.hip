@@ -234,6 +234,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   __shared__ int32_t par_lds[kMaxTree];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, ln = lane & 15;
+  stamp(a.stamps, 0);
   // KG = 2: waves w and w + 2 own the same row block and take the first and
   // the second 32 keys of every tile; their states are combined at the end
   const int rw = wave % (4 / KG);
@@ -372,6 +373,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   const int64_t kv0_true = paged ? 0 : a.kv_indptr[b];
   const int64_t kv1_true = paged ? 0 : a.kv_indptr[b + 1];
   wait_vmcnt<0>();   // the first tile, the parents and the query rows have landed
+  stamp(a.stamps, 1);
   if (kv0 != kv0_true) {   // the expected offset was wrong: request the first tile again
     kv0 = kv0_true;
     split_in_bounds = kv0 >= 0 && kv0 + k_end <= a.num_kv_rows;
@@ -404,6 +406,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   uint64_t anc_row[MB];
 #pragma unroll
   for (int rb = 0; rb < MB; ++rb) anc_row[rb] = anc_lds[node[rb]];
+  stamp(a.stamps, 2);   // ancestor words
 
   // O^T accumulators, and the row sums of P: the matrix unit adds them as the
   // product of an all-ones block with P^T (every lane of a row then holds the
@@ -675,6 +678,10 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
     step(t, std::integral_constant<int, 0>{});
     if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
   }
+  stamp(a.stamps, 3);   // tile loop done
+  stamp_value(a.stamps, 30, static_cast<uint64_t>(n_tiles));
+  stamp_value(a.stamps, 31, static_cast<uint64_t>(s_local) | (static_cast<uint64_t>(hk) << 16) |
+                                (static_cast<uint64_t>(rt) << 32) | (static_cast<uint64_t>(b) << 48));
 
   // every lane of a row holds the row's whole sum: a quarter per lane keeps
   // the sums over the row's four lanes below exact (powers of two)
@@ -740,6 +747,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
       }
     }
   }
+  stamp(a.stamps, 4);   // partial (or final) rows stored
   if (!fused) return;
 
   // ---- in-kernel merge.  Each partial row's m and l are published as two
@@ -758,6 +766,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
     st_u64(rec, tag | __float_as_uint(m_run[rb]));
     st_u64(rec + 1, tag | __float_as_uint(l_fin[rb]));
   }
+  stamp(a.stamps, 5);   // m and l published
 
   constexpr int CG = D / 4;   // 4-column groups per row
   const int rpt = a.rows_per_tile;
@@ -796,6 +805,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
     __builtin_amdgcn_s_sleep(2);
   }
   loads_after();
+  stamp(a.stamps, 6);   // every split of the rows has arrived
   // weighted sum: slot = (row, column group, split lane); spl lanes share a
   // (row, column group) and take the splits sl, sl + spl, ... in rounds of
   // 8 loads issued together.  A thread's first round is requested before
@@ -852,7 +862,10 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
       red[sl * items + item] = acc;
     }
   }
-  if (spl == 1) return;
+  if (spl == 1) {
+    stamp(a.stamps, 7);   // merged rows written
+    return;
+  }
   __syncthreads();
   if (tid < items) {
     f32x4_t acc = red[tid];
@@ -861,6 +874,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
     const int r = rt * rpt + r_lo + i;
     *reinterpret_cast<f32x4_t*>(a.out + ((int64_t)(b * T + r / g) * Hq + hk * g + r % g) * D + 4 * cg) = acc;
   }
+  stamp(a.stamps, 7);   // merged rows written
 }
 
 // -------------------------------------------------------------- FMA kernel

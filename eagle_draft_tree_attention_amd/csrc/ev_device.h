@@ -42,6 +42,16 @@ __device__ __forceinline__ uint64_t poll(const uint64_t* w) {
   return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Diagnostic timeline: thread 0 of the workgroup records the constant-rate
+// real-time counter (100 MHz) in word k of the workgroup's slots (32 words
+// per workgroup), or a value; nothing when no timeline buffer was given.
+__device__ __forceinline__ void stamp(uint64_t* stamps, int k) {
+  if (stamps && threadIdx.x == 0) stamps[static_cast<int64_t>(blockIdx.x) * 32 + k] = __builtin_amdgcn_s_memrealtime();
+}
+__device__ __forceinline__ void stamp_value(uint64_t* stamps, int k, uint64_t v) {
+  if (stamps && threadIdx.x == 0) stamps[static_cast<int64_t>(blockIdx.x) * 32 + k] = v;
+}
+
 __device__ __forceinline__ void publish(uint64_t* w, uint64_t v) {
   stores_done();
   __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

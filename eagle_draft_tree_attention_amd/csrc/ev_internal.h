@@ -13,6 +13,7 @@ namespace ev {
 constexpr int kMaxBatch = 256;       // per-sequence plan travels in the kernel arguments
 constexpr int kMaxTree = EAGLE_MAX_TREE_ROWS;
 constexpr int kTileKeys = 64;        // keys per attention tile (one LDS stage)
+constexpr int kStampSlots = 32;      // timeline words per workgroup (diagnostic)
 constexpr int kVocabChunk = 8192;    // vocabulary elements per acceptance workgroup
 constexpr int kDefaultCUs = 256;     // MI355X compute units (planning without a device)
 constexpr int64_t kAttnPartFloats = 32ll << 20;   // 128 MiB of split partials
@@ -64,6 +65,7 @@ struct AttnKernelArgs {
   uint32_t spin_limit; // polls of the bounded wait; an expired wait flags EAGLE_FLAG_INTERNAL
   uint64_t epoch;      // strictly increasing per attention call on a handle (tags use its low 32 bits)
   uint64_t* mlrec;      // [slot][rows_per_tile][2]: m and l (low 32 bits), epoch tag (high 32 bits)
+  uint64_t* stamps;     // phase timeline [workgroup][kStampSlots] (diagnostic), or NULL
   // paged K/V (page_size > 0): logical row x of sequence b is physical row
   // page_table[b * pps + x / page_size] * page_size + x % page_size
   const int32_t* page_table;
@@ -126,6 +128,7 @@ struct AcceptKernelArgs {
   int zero_b;             // batch of the previous fused call (extent of round_clear to clear)
   uint64_t epoch;         // strictly increasing per call on a handle
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
+  uint64_t* stamps;       // fused path: phase timeline [workgroup][kStampSlots] (diagnostic), or NULL
   int fused;              // 1: one co-resident kernel; 0: three-kernel path
   int coop;               // host side: launch the fused kernel cooperatively
   int b0;                 // batch index of sequence 0 of this launch (a slice of the call's batch)
@@ -263,7 +266,8 @@ struct AcceptCallState {
 // fused-acceptance workgroups.  Messages go to err.
 eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws, int64_t Bm, int64_t Tm,
                              int64_t fused_cap, AcceptCallState* cs, const eagle_spec_accept_args* a,
-                             void* stream, char* err, size_t errlen, uint32_t spin_limit, bool coop);
+                             void* stream, char* err, size_t errlen, uint32_t spin_limit, bool coop,
+                             uint64_t* stamps = nullptr, int64_t stamp_words = 0);
 
 // Polls of a bounded device-side wait (each about a microsecond): past it the
 // wait gives up and flags the sequence EAGLE_FLAG_INTERNAL.  The environment

@@ -104,6 +104,10 @@ def eagle_verify_last_attention_plan(handle: int) -> AttentionPlan:
 
 
 # ---------------------------------------------------------------- torch layer
+def eagle_verify_set_timeline(handle: int, device_words: int, num_words: int) -> int:
+    return _check(_lib().eagle_verify_set_timeline(handle, device_words, num_words), handle)
+
+
 def _ptr(t):
     return None if t is None else int(t.data_ptr())
 
@@ -200,6 +204,14 @@ class Verifier:
 
     def last_attention_plan(self) -> AttentionPlan:
         return eagle_verify_last_attention_plan(self.handle)
+
+    def set_timeline(self, words=None):
+        """Diagnostic phase timeline: a contiguous int64 device tensor (32
+        words per workgroup), or None to switch it off."""
+        if words is None:
+            return eagle_verify_set_timeline(self.handle, None, 0)
+        assert words.is_contiguous() and words.element_size() == 8
+        return eagle_verify_set_timeline(self.handle, words.data_ptr(), words.numel())
 
     def spec_accept(self, target, draft, parents, tokens, temperature, seed, offset, outputs=None,
                     stream=None, without_replacement=False, top_k=0, top_p=0.0):

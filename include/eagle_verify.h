@@ -417,6 +417,36 @@ EAGLE_API eagle_status eagle_verify_check_tree_rerank(const eagle_verify_desc* d
  * Errors: EAGLE_ERR_ARG when h or plan is NULL or h has made no such call. */
 EAGLE_API eagle_status eagle_verify_last_attention_plan(const eagle_verify* h, eagle_attention_plan* plan);
 
+/* Diagnostic phase timeline of the two step kernels (for profiling; the
+ * results of every call are the same with or without it).
+ *
+ * device_words: caller-owned device memory of num_words 64-bit words, kept
+ * alive while calls on h may use it; NULL (or num_words 0) switches the
+ * timeline off.  While it is set, every MFMA tree-attention launch and every
+ * fused acceptance launch on h whose workgroups need at most num_words words
+ * (32 per workgroup) records: thread 0 of workgroup w writes word w * 32 + k
+ * at phase k, as a reading of the device's constant-rate real-time counter
+ * (100 MHz on MI355X).  Nothing is cleared: a phase a workgroup does not
+ * reach keeps the word's old value, so the caller clears the buffer before a
+ * call.  A call of several fused launches (a batch cut into slices) leaves
+ * the last launch's words.  Other kernels record nothing.
+ *   tree attention (workgroup = (KV head, key split, row tile)):
+ *     0 start, 1 first K/V tile and query rows landed, 2 ancestor words
+ *     built, 3 tile loop done, 4 partial (or final) rows stored, 5 row
+ *     statistics published (in-kernel merge only), 6 every split of the rows
+ *     it merges has arrived, 7 merged rows written; word 30 = tiles of the
+ *     workgroup, 31 = split | KV head << 16 | row tile << 32 | sequence << 48
+ *   acceptance (workgroup = (sequence, node, vocabulary chunk)):
+ *     0 start, 1 chunk in LDS, 2 chunk statistics, 3 row statistics
+ *     combined, 4 first decision, 5 + i end of residual round i (i < 12),
+ *     17 node decided, 18 terminal preparation starts, 19 the chunk holding
+ *     the terminal sample is known, 20 the walk ends at this node, 21
+ *     outputs written; word 30 = residual rounds, 31 = node | chunk << 8 |
+ *     node state << 16 | sequence << 24
+ * Errors: EAGLE_ERR_ARG when h is NULL, num_words < 0, or device_words is
+ * not 8-byte aligned. */
+EAGLE_API eagle_status eagle_verify_set_timeline(eagle_verify* h, uint64_t* device_words, int64_t num_words);
+
 #ifdef __cplusplus
 }
 #endif

@@ -113,6 +113,12 @@ def test_last_attention_plan_needs_a_call():
     assert lib.eagle_verify_last_attention_plan(None, None) == ev.EAGLE_ERR_ARG
 
 
+def test_set_timeline_needs_a_handle():
+    lib = ev.library()
+    assert lib.eagle_verify_set_timeline(None, None, 0) == ev.EAGLE_ERR_ARG
+    assert lib.eagle_verify_set_timeline(None, 64, 32) == ev.EAGLE_ERR_ARG
+
+
 def test_spec_accept_argument_errors():
     d = _desc()
     assert ev.eagle_verify_check_spec_accept(d, _sa_args()) == ev.EAGLE_OK
