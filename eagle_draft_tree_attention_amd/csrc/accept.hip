@@ -1025,6 +1025,7 @@ struct FusedShared {
   uint32_t pflags[kMaxTree];   // flags and near-tie counts of the root path's nodes,
   int32_t pnear[kMaxTree];     // decoded from their publication words
   double cmass[kFusedMaxChunks];   // q mass of each chunk (from the chunk statistics)
+  double fscale[2];   // 2^((m_c - M) c2) / Z of this chunk's target (0) and draft (1) row
   double sample[4];
   // siblings drawn without replacement: the residual weight each tried
   // child's token keeps once later siblings no longer see it (-1: the token
@@ -1388,6 +1389,11 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // checks still run so that every unusable input is reported
   const uint32_t tokbad = __any(tb) ? EAGLE_FLAG_BAD_TOKEN : 0u;
   const bool two = nkids > 0 && !greedy;
+  // Internal nodes decide (statistics, first decision, residual rounds) on
+  // the way to every walk; a leaf's statistics matter only if the walk ends
+  // there.  Where the workgroups of a CU compete for the vector ALU, the
+  // internal nodes' waves are issued first.
+  if (nkids > 0 && a.node_priority) __builtin_amdgcn_s_setprio(2);
   if (two) {
     if constexpr (VEC) request_groups<TL, NV>(drow, v0, v1, wd);
     else load_groups<TL, NV>(drow, v0, v1, false, wd);
@@ -1405,6 +1411,9 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         cd.xq = cut(logit<TL>(trow, tok), thr_of(a, b, n, 0));
         cd.yp = cut(logit<TL>(drow, tok), thr_of(a, b, n, 1));
       }
+      // the test's uniform depends on nothing the statistics decide: drawn
+      // while the rows are still arriving
+      if (!greedy) cd.r = decision_uniform(a, b, n, static_cast<uint32_t>(ord));
       sh.cand[ord] = cd;
     }
   }
@@ -1518,6 +1527,12 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         sh.cmass[q] = (!greedy && q < NC && mc != kNegInf && Z > 0.0)
                           ? zc * exp2((static_cast<double>(mc) - M) * static_cast<double>(a.c2)) / Z
                           : 0.0;
+      // this workgroup's own chunk: the factor from its exponentials to the
+      // row's probabilities (the residual rounds and the terminal weights)
+      if (q == c)
+        sh.fscale[r] = (!greedy && mc != kNegInf && Z > 0.0)
+                           ? exp2((static_cast<double>(mc) - M) * static_cast<double>(a.c2)) / Z
+                           : 0.0;
       if (q == 0) {
         const uint32_t fl = (rb || M == kNegInf) ? EAGLE_FLAG_NONFINITE : 0u;
         if (r == 0) {
@@ -1546,7 +1561,6 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
         cd.qt = exp((static_cast<double>(cd.xq) - static_cast<double>(sh.st.mq)) * a.inv_tau) / sh.st.zq;
         cd.pt = exp((static_cast<double>(cd.yp) - static_cast<double>(sh.st.mp)) * a.inv_tau) / sh.st.zp;
       }
-      cd.r = decision_uniform(a, b, n, static_cast<uint32_t>(tid));
     }
     // greedy: the first child carrying the target argmax
     if (greedy) {
@@ -1602,8 +1616,8 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // ---- residual-mass rounds from LDS
   const bool q_live = mq_c != kNegInf, p_live = two && mp_c != kNegInf;
   const float mqs = q_live ? mq_c : 0.f, mps = p_live ? mp_c : 0.f;
-  const double fq = q_live ? exp2((static_cast<double>(mq_c) - sh.st.mq) * static_cast<double>(a.c2)) / sh.st.zq : 0.0;
-  const double fp = p_live ? exp2((static_cast<double>(mp_c) - sh.st.mp) * static_cast<double>(a.c2)) / sh.st.zp : 0.0;
+  const double fq = q_live ? sh.fscale[0] : 0.0;
+  const double fp = p_live ? sh.fscale[1] : 0.0;
   uint64_t* const rwords = a.round_sum + (static_cast<int64_t>(b) * a.Tm + n) * kRoundWords;
   int round = 0;
   while (sh.st.kind == kNodeNeedsPass) {

@@ -167,6 +167,10 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
   k.Tm = static_cast<int>(Tm);
   k.epoch = ++cs->epoch;
   k.spin_limit = spin_limit;
+  {   // tuning override: EAGLE_VERIFY_NODE_PRIORITY = 0 keeps every wave at the normal priority
+    const char* np = std::getenv("EAGLE_VERIFY_NODE_PRIORITY");
+    k.node_priority = (np && np[0] == '0') ? 0 : 1;
+  }
   // The fused kernel needs every workgroup of a launch resident at once.  A
   // batch that does not fit is verified in slices of whole sequences, one
   // fused launch each, back to back on the stream (each slice is a fused

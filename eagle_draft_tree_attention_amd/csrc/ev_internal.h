@@ -129,6 +129,7 @@ struct AcceptKernelArgs {
   uint64_t epoch;         // strictly increasing per call on a handle
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
   uint64_t* stamps;       // fused path: phase timeline [workgroup][kStampSlots] (diagnostic), or NULL
+  int node_priority;      // fused path: internal nodes' waves at a raised priority
   int fused;              // 1: one co-resident kernel; 0: three-kernel path
   int coop;               // host side: launch the fused kernel cooperatively
   int b0;                 // batch index of sequence 0 of this launch (a slice of the call's batch)
