@@ -18,10 +18,11 @@
 //              logits with their ids (k rounds of a wave argmax per wave, then
 //              a merge of the four waves' lists); one record per chunk.
 //   te_select  one workgroup per sequence: one wave per frontier row reads
-//              the row's chunk records and reduces its maximum and
-//              normaliser, takes its top k as a k-step merge of the chunks'
-//              sorted lists and values them s_f + (x - max)/t - log Z in
-//              fp64 (lists handed over in LDS); then every candidate is
+//              the row's score and chunk records in one round trip (lane c:
+//              chunk c, its sorted list kept in registers), reduces the row's
+//              maximum and normaliser, takes its top k as a k-step merge of
+//              the chunks' lists and values them s_f + (x - max)/t - log Z in
+//              fp64 (the row's candidates go to LDS); then every candidate is
 //              ranked by counting the candidates before it (value, then
 //              frontier index, then position in its row) and written to its
 //              slot; adjacent ranks up to the kept/dropped boundary are
@@ -30,6 +31,7 @@
 // Within a row the value is a monotone function of the logit, so a row's
 // list sorted by logit is sorted by value too.
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "ev_internal.h"
@@ -233,25 +235,20 @@ __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
 }
 
 constexpr int kSelWaves = 8;   // frontier rows worked on at once by one workgroup
-
-// Wave-level hand-over through LDS: the wave's LDS writes are complete and
-// visible to its own lanes before any of them reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+constexpr int kRecVal = static_cast<int>(offsetof(ChunkRecord, val));
+constexpr int kRecId = static_cast<int>(offsetof(ChunkRecord, id));
+static_assert(offsetof(ChunkRecord, z) == 8 && kRecVal % 16 == 0 && kRecId % 16 == 0 && sizeof(ChunkRecord) % 16 == 0,
+              "chunk records are read as 16-byte groups");
 
 // One workgroup per sequence.  Row phase: wave w takes frontier rows
-// w, w + 8, ...; for each, lane c reads chunk c's record, the wave reduces the
-// row's maximum, normaliser and unusable flag, and takes the row's top K as a
-// K-step merge of the chunks' sorted lists (each step the best head), valued
+// w, w + 8, ...; for each, lane c reads chunk c's record (its sorted list
+// stays in the lane's registers), the wave reduces the row's maximum,
+// normaliser and unusable flag, and takes the row's top K as a K-step merge
+// of the chunks' lists (each step the best head), valued
 // s + (x - max)/t - log Z in fp64, into LDS.  Selection phase (all threads):
 // each candidate's rank is the number of candidates before it, and it is
 // written straight to that output slot.
 __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelArgs a) {
-  __shared__ float lv[kSelWaves][kMaxChunksExpand][kMaxTopK];   // chunk lists of the wave's current row
-  __shared__ int li[kSelWaves][kMaxChunksExpand][kMaxTopK];
   __shared__ double sv[kMaxTree][kMaxTopK];   // row f's candidates: value
   __shared__ int st[kMaxTree][kMaxTopK];      // and token, sorted
   __shared__ float sx[kMaxTree][kMaxTopK];    // and logit (equal logits of one row tie exactly)
@@ -261,7 +258,23 @@ __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelAr
 
   for (int f = wave; f < F; f += kSelWaves) {
     const int row = b * F + f;
+    // the row's score and every chunk record (lane c: chunk c) are requested
+    // together: one memory round trip for the row.  The chunk's list stays in
+    // registers (16-byte groups of logits and of ids).
     const float s = a.scores[row];
+    const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC;
+    const int nq = (K + 3) / 4;
+    u32x4_t w0 = {0u, 0u, 0u, 0u}, wv[kMaxTopK / 4], wi[kMaxTopK / 4];
+    if (lane < NC) {
+      const u32x4_t* r4 = reinterpret_cast<const u32x4_t*>(rec + lane);
+      w0 = r4[0];
+#pragma unroll
+      for (int j = 0; j < kMaxTopK / 4; ++j)
+        if (j < nq) {
+          wv[j] = r4[kRecVal / 16 + j];
+          wi[j] = r4[kRecId / 16 + j];
+        }
+    }
     if (!(s > kNegInf)) {   // inactive (NaN and -inf): no candidates, not flagged
       if (lane == 0) {
         scnt[f] = 0;
@@ -269,19 +282,9 @@ __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelAr
       }
       continue;
     }
-    const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC;
-    float mc = kNegInf;
-    uint32_t bad = 0;
-    double zc = 0.0;
-    if (lane < NC) {
-      mc = rec[lane].m;
-      bad = rec[lane].bad;
-      zc = rec[lane].z;
-      for (int q = 0; q < K; ++q) {
-        lv[wave][lane][q] = rec[lane].val[q];
-        li[wave][lane][q] = rec[lane].id[q];
-      }
-    }
+    const float mc = lane < NC ? __uint_as_float(w0[0]) : kNegInf;
+    const uint32_t bad = lane < NC ? w0[1] : 0u;
+    const double zc = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(w0[3]) << 32) | w0[2]));
     const float mx = wave_max_f32(mc);
     if (__any(bad != 0) || mx == kNegInf) {   // unusable row: skipped, the sequence is flagged
       if (lane == 0) {
@@ -293,11 +296,18 @@ __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelAr
     const double z = wave_sum_f64(
         (lane < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - mx) * static_cast<double>(a.c2)) : 0.0);
     const double lz = log(z);
-    wave_lds_sync();   // the chunk lists are in LDS
     int hd = 0, cnt = 0;
     for (int q = 0; q < K; ++q) {
-      const uint64_t key = (lane < NC && hd < K && li[wave][lane][hd] >= 0)
-                               ? cand_key(lv[wave][lane][hd], li[wave][lane][hd]) : 0ull;
+      // this lane's head: entry hd of its chunk's list
+      uint32_t hv = 0u, hi = 0xFFFFFFFFu;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < K && j == hd) {
+          hv = wv[j / 4][j % 4];
+          hi = wi[j / 4][j % 4];
+        }
+      const uint64_t key = (lane < NC && hd < K && static_cast<int>(hi) >= 0)
+                               ? cand_key(__uint_as_float(hv), static_cast<int>(hi)) : 0ull;
       const uint64_t best = wave_max_u64(key);
       if (best == 0ull) break;   // every list is exhausted
       if (key == best) ++hd;     // token ids are unique: one lane wins
@@ -314,7 +324,6 @@ __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelAr
       scnt[f] = cnt;
       sbad[f] = 0;
     }
-    wave_lds_sync();   // the lists are read before the next row overwrites them
   }
   __syncthreads();
 
