@@ -1242,6 +1242,39 @@ __device__ __forceinline__ double local_expsum(const u32x4_t (&w)[NV], float m, 
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
+// local_expsum that also keeps every exponential (index jj * G + e) for the
+// residual rounds; an all -inf chunk (m = -inf) keeps zeros and sums 0.
+template <typename TL, int NV>
+__device__ __forceinline__ double local_expsum_keep(const u32x4_t (&w)[NV], float m, float c2,
+                                                    float (&ex)[NV * Pack<TL>::G]) {
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  const bool live = m != kNegInf;
+  const float ms = live ? m : 0.f;
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) {
+    float f[Pack<TL>::G];
+    Pack<TL>::unpack(w[jj], f);
+#pragma unroll
+    for (int e = 0; e < Pack<TL>::G; ++e) {
+      const float v = ex2(f[e], c2, ms);
+      ex[jj * Pack<TL>::G + e] = v;
+      acc[e & 3] += static_cast<double>(v);
+    }
+  }
+  return live ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : 0.0;
+}
+
+// Residual mass sum max(0, q - C p) of this thread's strided slots from the
+// exponentials the statistics pass kept (the same values local_masses
+// computes from LDS, summed in the same order).
+template <int N>
+__device__ __forceinline__ double kept_masses(const float (&eq)[N], const float (&ep)[N], float K, double fq) {
+  double ra[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < N; ++i) ra[i & 3] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ep[i], eq[i])));
+  return ((ra[0] + ra[1]) + (ra[2] + ra[3])) * fq;
+}
+
 // Residual mass sum max(0, q - C p) and plain mass sum q of this thread's
 // strided slots, from LDS.  With q = fq e_q and p = fp e_p (e = exp2 of the
 // scaled logit minus the chunk maximum; mqs / mps are 0 for an all -inf
@@ -1423,6 +1456,12 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   float mq_c, mp_c = kNegInf;
   int amq = -1;
   double zq_c = 0.0, zp_c = 0.0;
+  // the statistics' exponentials of this thread's slots, kept for the
+  // residual rounds (an internal node's rows only; the path for rows that
+  // are not whole 16-byte groups, short of registers, recomputes them from
+  // LDS in every round instead)
+  constexpr bool kKeep = VEC;
+  float xq[kPerThread], xp[kPerThread];
   {
     if constexpr (VEC) {
       mask_groups<TL, NV>(v0, v1, wq);
@@ -1456,8 +1495,13 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       amq = block_reduce(la, MinI{}, sh.iscr);
     } else {
       double lzq = 0.0, lzp = 0.0;
-      if (mq_c != kNegInf && mq_c != __builtin_inff()) lzq = local_expsum<TL, NV>(wq, mq_c, a.c2);
-      if (two && mp_c != kNegInf && mp_c != __builtin_inff()) lzp = local_expsum<TL, NV>(wd, mp_c, a.c2);
+      if (kKeep && two) {
+        if (mq_c != __builtin_inff()) lzq = local_expsum_keep<TL, NV>(wq, mq_c, a.c2, xq);
+        if (mp_c != __builtin_inff()) lzp = local_expsum_keep<TL, NV>(wd, mp_c, a.c2, xp);
+      } else {
+        if (mq_c != kNegInf && mq_c != __builtin_inff()) lzq = local_expsum<TL, NV>(wq, mq_c, a.c2);
+        if (two && mp_c != kNegInf && mp_c != __builtin_inff()) lzp = local_expsum<TL, NV>(wd, mp_c, a.c2);
+      }
       block_reduce2(lzq, lzp, AddD{}, sh.dscr);
       zq_c = lzq;
       zp_c = lzp;
@@ -1621,8 +1665,13 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   uint64_t* const rwords = a.round_sum + (static_cast<int64_t>(b) * a.Tm + n) * kRoundWords;
   int round = 0;
   while (sh.st.kind == kNodeNeedsPass) {
-    double part, unused;
-    local_masses<TL, NV>(lq, lp, true, mqs, mps, a.c2, fq, fp, sh.st.C, part, unused);
+    double part;
+    if constexpr (kKeep) {
+      part = kept_masses(xq, xp, fq > 0.0 ? static_cast<float>(sh.st.C * fp / fq) : 0.f, fq);
+    } else {
+      double unused;
+      local_masses<TL, NV>(lq, lp, true, mqs, mps, a.c2, fq, fp, sh.st.C, part, unused);
+    }
     part = block_reduce(part, AddD{}, sh.dscr);
     if (tid == 0) {
       const double pc = fmin(fmax(part, 0.0), 2.0);
