@@ -1020,7 +1020,7 @@ struct FusedShared {
   int32_t onpath;
   uint32_t seqflags;
   int32_t seqnear;
-  double scan[kThreads / 64];
+  double gscan[kPerThread / 4][kThreads / 64];   // per group column (at most 8) and wave
   int32_t wfirst[kThreads / 64];
   uint32_t pflags[kMaxTree];   // flags and near-tie counts of the root path's nodes,
   int32_t pnear[kMaxTree];     // decoded from their publication words
@@ -1456,10 +1456,10 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   float mq_c, mp_c = kNegInf;
   int amq = -1;
   double zq_c = 0.0, zp_c = 0.0;
-  // the statistics' exponentials of this thread's slots, kept for the
-  // residual rounds (an internal node's rows only; the path for rows that
-  // are not whole 16-byte groups, short of registers, recomputes them from
-  // LDS in every round instead)
+  // the statistics' exponentials of this thread's slots (the draft row's at
+  // an internal node only), kept for the residual rounds and the terminal
+  // weights; the path for rows that are not whole 16-byte groups, short of
+  // registers, recomputes them from LDS each time instead
   constexpr bool kKeep = VEC;
   float xq[kPerThread], xp[kPerThread];
   {
@@ -1495,9 +1495,9 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       amq = block_reduce(la, MinI{}, sh.iscr);
     } else {
       double lzq = 0.0, lzp = 0.0;
-      if (kKeep && two) {
+      if constexpr (kKeep) {
         if (mq_c != __builtin_inff()) lzq = local_expsum_keep<TL, NV>(wq, mq_c, a.c2, xq);
-        if (mp_c != __builtin_inff()) lzp = local_expsum_keep<TL, NV>(wd, mp_c, a.c2, xp);
+        if (two && mp_c != __builtin_inff()) lzp = local_expsum_keep<TL, NV>(wd, mp_c, a.c2, xp);
       } else {
         if (mq_c != kNegInf && mq_c != __builtin_inff()) lzq = local_expsum<TL, NV>(wq, mq_c, a.c2);
         if (two && mp_c != kNegInf && mp_c != __builtin_inff()) lzp = local_expsum<TL, NV>(wd, mp_c, a.c2);
@@ -1822,59 +1822,33 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // ---- terminal distribution of this node, prepared before the walk is
   // known to end here (it overlaps the walk): inverse CDF of the residual
   // max(0, q - C p) (of q at a leaf; of q again if the residual mass is
-  // zero).  Thread t owns the LDS slots [32t, 32t + 32), i.e. consecutive
-  // tokens.  Every workgroup of the node publishes its chunk mass and
-  // finds the chunk holding u*S; only that workgroup continues once the
-  // walk is known to end here.
+  // zero).  It works in the strided view: group g = jj * kThreads + t of
+  // thread t holds the G consecutive tokens [g G, g G + G) of the chunk, so
+  // token order is group order.  Every workgroup of the node publishes its
+  // chunk mass and finds the chunk holding u*S; only that workgroup
+  // continues once the walk is known to end here.
   const double Ct = leaf ? 0.0 : sh.st.C;
-  const int i0 = tid * kPerThread;
-  // weight of the token at LDS slot i0 + jj * G + e, from its two logits
   const float Kt = fq > 0.0 ? static_cast<float>(Ct * fp / fq) : 0.f;
-  auto weight = [&](bool q_only, float xq, float xp) __attribute__((always_inline)) -> double {
-    const float eq = ex2(xq, a.c2, mqs);
-    return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(xp, a.c2, mps), eq)));
+  // weight of the token at LDS slot s, from its two logits (the same value
+  // as from the kept exponentials)
+  auto weight = [&](bool q_only, int s) __attribute__((always_inline)) -> double {
+    const float eq = ex2(lds_logit<TL>(lq, s), a.c2, mqs);
+    return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(lds_logit<TL>(lp, s), a.c2, mps), eq)));
   };
-  // this thread's sums of the weights and of q
-  auto sums = [&](bool q_only, double& ts, double& tq) __attribute__((always_inline)) {
-    double wa[4] = {0.0, 0.0, 0.0, 0.0}, qa[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-    for (int jj = 0; jj < NV; ++jj) {
-      const u32x4_t gq = *reinterpret_cast<const u32x4_t*>(lq + i0 + jj * G);
-      const u32x4_t gp = q_only ? gq : *reinterpret_cast<const u32x4_t*>(lp + i0 + jj * G);
-      float fa[G], fb[G];
-      Pack<TL>::unpack(gq, fa);
-      Pack<TL>::unpack(gp, fb);
-#pragma unroll
-      for (int e = 0; e < G; ++e) {
-        const float eq = ex2(fa[e], a.c2, mqs);
-        qa[e & 3] += static_cast<double>(eq);
-        wa[e & 3] += static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ex2(fb[e], a.c2, mps), eq)));
-      }
+  // weight and q exponential of this thread's slot i = jj * G + e, from the
+  // kept exponentials (regs) or from LDS
+  auto slot_weight = [&](bool q_only, bool regs, int jj, int e, float& eq) __attribute__((always_inline)) -> double {
+    float ep = 0.f;
+    if (kKeep && regs) {
+      eq = xq[jj * G + e];
+      if (!q_only) ep = xp[jj * G + e];
+    } else {
+      const int s = group_index<TL>(jj) + e;
+      eq = ex2(lds_logit<TL>(lq, s), a.c2, mqs);
+      if (!q_only) ep = ex2(lds_logit<TL>(lp, s), a.c2, mps);
     }
-    ts = ((wa[0] + wa[1]) + (wa[2] + wa[3])) * fq;
-    tq = ((qa[0] + qa[1]) + (qa[2] + qa[3])) * fq;
+    return fq * static_cast<double>(q_only ? eq : fmaxf(0.f, __builtin_fmaf(-Kt, ep, eq)));
   };
-  // block exclusive scan of the per-thread sums: this thread's starting
-  // offset inside the chunk and the chunk total
-  double chunk_total = 0.0;
-  auto scan_offsets = [&](double ts) __attribute__((always_inline)) -> double {
-    const double incl = wave_scan_add(ts);
-    const double excl = wave_prev(incl);
-    __syncthreads();
-    if ((tid & 63) == 63) sh.scan[tid >> 6] = incl;
-    __syncthreads();
-    double off = 0.0, tot = 0.0;
-#pragma unroll
-    for (int wv = 0; wv < kThreads / 64; ++wv) {
-      if (wv < (tid >> 6)) off += sh.scan[wv];
-      tot += sh.scan[wv];
-    }
-    chunk_total = tot;
-    return off + excl;
-  };
-  double ts = 0.0, tq = 0.0, offset = 0.0;
-  int cstar = 0;
-  bool degen = false;
   // without replacement: a tried token's terminal weight is the one it kept
   const bool wr_tail = WR && !leaf && !greedy;
   auto kept_weight = [&](int token, double wdef) __attribute__((always_inline)) -> double {
@@ -1882,16 +1856,70 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
       if (sh.wfz[j] >= 0.0 && sh.cand[j].tok == token) return sh.wfz[j];
     return wdef;
   };
-  if (!greedy) {
-    sums(leaf, ts, tq);
-    if (wr_tail) {   // replace the formula's weight of each tried token in this thread's range
+  // this thread's group weights gw and its q mass tq
+  double gw[NV];
+  double tq = 0.0;
+  auto group_sums = [&](bool q_only, bool regs) __attribute__((always_inline)) {
+    double qa = 0.0;
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      double g = 0.0;
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        float eq;
+        g += slot_weight(q_only, regs, jj, e, eq);
+        qa += static_cast<double>(eq);
+      }
+      gw[jj] = g;
+    }
+    tq = qa * fq;
+    if (wr_tail && !q_only) {   // replace the formula's weight of each tried token in this thread's groups
       for (int j = 0; j < nkids; ++j) {
         const int slot = sh.cand[j].tok - v0;
-        if (sh.wfz[j] >= 0.0 && slot >= i0 && slot < i0 + kPerThread && sh.cand[j].tok < v1)
-          ts += sh.wfz[j] - weight(false, lds_logit<TL>(lq, slot), lds_logit<TL>(lp, slot));
+        if (sh.wfz[j] >= 0.0 && slot >= 0 && slot < kVocabChunk && sh.cand[j].tok < v1 &&
+            (slot / G) % kThreads == tid) {
+          const double d = sh.wfz[j] - weight(false, slot);
+#pragma unroll
+          for (int jj = 0; jj < NV; ++jj)
+            if (jj == (slot / G) / kThreads) gw[jj] += d;
+        }
       }
     }
-    offset = scan_offsets(ts);
+  };
+  // block exclusive scans of the group weights, one per group column: the
+  // starting offset goff of each of this thread's groups inside the chunk,
+  // and the chunk total
+  double goff[NV];
+  double chunk_total = 0.0;
+  auto scan_offsets = [&]() __attribute__((always_inline)) {
+    double excl[NV];
+    __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      const double incl = wave_scan_add(gw[jj]);
+      excl[jj] = wave_prev(incl);
+      if ((tid & 63) == 63) sh.gscan[jj][tid >> 6] = incl;
+    }
+    __syncthreads();
+    double base = 0.0;
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      double off = base, tot = 0.0;
+#pragma unroll
+      for (int wv = 0; wv < kThreads / 64; ++wv) {
+        if (wv < (tid >> 6)) off += sh.gscan[jj][wv];
+        tot += sh.gscan[jj][wv];
+      }
+      goff[jj] = off + excl[jj];
+      base += tot;
+    }
+    chunk_total = base;
+  };
+  int cstar = 0;
+  bool degen = false;
+  if (!greedy) {
+    group_sums(leaf, true);   // the last use of the kept exponentials
+    scan_offsets();
     // residual and q masses of every chunk: four words per chunk (low and
     // high halves of the two doubles) whose high halves carry the call's
     // tag, read back by polling the words themselves (as the statistics)
@@ -1997,54 +2025,63 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     const double S = sh.sample[1], thr = sh.sample[2];
     const bool q_only = leaf || degen;
     if (degen && !leaf) {   // the residual vanished: sample q instead
-      sums(true, ts, tq);
-      offset = scan_offsets(ts);
+      group_sums(true, false);
+      scan_offsets();
     }
-    // the smallest token whose running sum exceeds u*S.  The first thread
-    // whose range reaches u*S is found from per-wave ballots; wave 0 then
-    // scans that thread's 32 tokens one per lane.  A thread starting past
-    // u*S offers its first token (rounding hid the crossing just before it,
-    // which the near-tie test reports).
-    const double start = sh.sample[0] + offset;
+    // the smallest token whose running sum exceeds u*S.  The first group
+    // (in token order) whose range reaches u*S is found by a block minimum;
+    // wave 0 then scans that group's G tokens one per lane.  A group
+    // starting past u*S offers its first token (rounding hid the crossing
+    // just before it, which the near-tie test reports).
     {
-      const uint64_t reach = __ballot(start > thr || thr - start < ts * (1.0 + 1e-9));
-      if ((tid & 63) == 0) sh.wfirst[tid >> 6] = reach ? (tid + __ffsll(static_cast<long long>(reach)) - 1) : 0x7FFFFFFF;
-    }
-    __syncthreads();
-    int tstar = 0x7FFFFFFF;
+      int gfirst = 0x7FFFFFFF;
+      double gstart = 0.0;
 #pragma unroll
-    for (int wv = 0; wv < kThreads / 64; ++wv) tstar = min(tstar, sh.wfirst[wv]);
-    if (tid == tstar) sh.sample[3] = start;
-    __syncthreads();
-    if (tid < 64) {
-      int hit = -1;
-      double lo = 0.0, hi = 0.0;
-      if (tstar != 0x7FFFFFFF) {
-        const double s0 = sh.sample[3];
-        const int t0 = tstar * kPerThread;
-        const int l = tid & 31;
-        const float xq = lds_logit<TL>(lq, t0 + l);
-        const float xp = q_only ? xq : lds_logit<TL>(lp, t0 + l);
-        double w = (tid < 32) ? weight(q_only, xq, xp) : 0.0;
-        if (wr_tail && !q_only && tid < 32) w = kept_weight(v0 + t0 + l, w);
-        const double incl = wave_scan_add(w);   // lanes 32..63 carry 0
-        const double cum = s0 + incl;
-        const uint64_t over = __ballot(tid < 32 && (s0 > thr || cum > thr));
-        if (over) {
-          const int f = __ffsll(static_cast<long long>(over)) - 1;
-          hit = t0 + f;
-          hi = __shfl(cum, f);
-          lo = hi - __shfl(w, f);
-          if (s0 > thr) lo = hi = s0;
-        } else if (tstar + 1 < kThreads) {   // the crossing fell just past this thread
-          hit = t0 + kPerThread;
-          lo = hi = __shfl(cum, 31);
+      for (int jj = NV - 1; jj >= 0; --jj) {   // the smallest reaching column wins
+        const double st = sh.sample[0] + goff[jj];
+        if (st > thr || thr - st < gw[jj] * (1.0 + 1e-9)) {
+          gfirst = jj * kThreads + tid;
+          gstart = st;
         }
       }
-      if (tid == 0) {
-        const bool ok = hit >= 0 && v0 + hit < v1;
-        sh.iscr[1] = ok ? hit : -1;
-        sh.iscr[2] = ok ? (((hi - thr) < kNearTie * S || (thr - lo) < kNearTie * S) ? 1 : 0) : 0;
+      const int wmin = wave_reduce(gfirst, MinI{});
+      if ((tid & 63) == 0) sh.wfirst[tid >> 6] = wmin;
+      __syncthreads();
+      int gstar = 0x7FFFFFFF;
+#pragma unroll
+      for (int wv = 0; wv < kThreads / 64; ++wv) gstar = min(gstar, sh.wfirst[wv]);
+      if (gfirst == gstar && gstar != 0x7FFFFFFF) sh.sample[3] = gstart;
+      __syncthreads();
+      if (tid < 64) {
+        int hit = -1;
+        double lo = 0.0, hi = 0.0;
+        if (gstar != 0x7FFFFFFF) {
+          const double s0 = sh.sample[3];
+          const int t0 = gstar * G;
+          double w = 0.0;
+          if (tid < G) {
+            w = weight(q_only, t0 + tid);
+            if (wr_tail && !q_only) w = kept_weight(v0 + t0 + tid, w);
+          }
+          const double incl = wave_scan_add(w);   // lanes past the group carry 0
+          const double cum = s0 + incl;
+          const uint64_t over = __ballot(tid < G && (s0 > thr || cum > thr));
+          if (over) {
+            const int f = __ffsll(static_cast<long long>(over)) - 1;
+            hit = t0 + f;
+            hi = __shfl(cum, f);
+            lo = hi - __shfl(w, f);
+            if (s0 > thr) lo = hi = s0;
+          } else if (gstar + 1 < NV * kThreads) {   // the crossing fell just past this group
+            hit = t0 + G;
+            lo = hi = __shfl(cum, G - 1);
+          }
+        }
+        if (tid == 0) {
+          const bool ok = hit >= 0 && v0 + hit < v1;
+          sh.iscr[1] = ok ? hit : -1;
+          sh.iscr[2] = ok ? (((hi - thr) < kNearTie * S || (thr - lo) < kNearTie * S) ? 1 : 0) : 0;
+        }
       }
     }
     __syncthreads();
@@ -2054,13 +2091,16 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
     } else {
       // rounding left no crossing: the last token of the chunk with positive weight
       int last = -1;
-#pragma unroll 1
-      for (int e = 0; e < kPerThread; ++e) {
-        const float xq = lds_logit<TL>(lq, i0 + e);
-        const float xp = q_only ? xq : lds_logit<TL>(lp, i0 + e);
-        double we = weight(q_only, xq, xp);
-        if (wr_tail && !q_only) we = kept_weight(v0 + i0 + e, we);
-        if (v0 + i0 + e < v1 && we > 0.0) last = v0 + i0 + e;
+#pragma unroll
+      for (int jj = 0; jj < NV; ++jj) {
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          const int sl = group_index<TL>(jj) + e;
+          float eq;
+          double we = slot_weight(q_only, false, jj, e, eq);
+          if (wr_tail && !q_only) we = kept_weight(v0 + sl, we);
+          if (v0 + sl < v1 && we > 0.0) last = max(last, v0 + sl);
+        }
       }
       if (tid == 0) sh.iscr[2] = -1;
       __syncthreads();

@@ -112,13 +112,14 @@ def test_edge_cases_flags_and_poison():
     ver.close()
 
 
-def test_p_zero_and_degenerate_residual():
+@pytest.mark.parametrize("V", [3, 16])   # per-token loads, and whole 16-byte groups
+def test_p_zero_and_degenerate_residual(V):
     import eagle_draft_tree_attention_amd as ev
-    log("[accept] p = 0 and zero residual")
-    spec = _custom(2, 3, 3)
+    log(f"[accept] p = 0 and zero residual, V={V}")
+    spec = _custom(2, 3, V)
     inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1, 1)), with_kv=False)
-    row = np.log(np.array([0.5, 0.5, 1.0])).astype(np.float32)
-    row[2] = -np.inf
+    row = np.full(V, -np.inf, dtype=np.float32)
+    row[:2] = np.log(0.5)
     tgt = np.stack([np.stack([row] * 3)] * 2)
     drf = tgt.copy()
     par = np.array([[-1, 0, 0], [-1, 0, 0]], dtype=np.int32)
@@ -126,7 +127,7 @@ def test_p_zero_and_degenerate_residual():
     ver = make_verifier(spec.with_(batch=2), 3)
     got = run_accept(ver, inp, 1.0, SEED, 0, target=tgt, draft=drf, parents=par, tokens=tok)
     ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
-    assert compare_accept(got, ref, "p0", par, tok, 3) == 0
+    assert compare_accept(got, ref, "p0", par, tok, V) == 0
     assert got["flags"][0] & ev.FLAG_P_ZERO and got["flags"][0] & ev.FLAG_DEGENERATE_RESIDUAL
     assert got["accept_len"][0] == 1 and got["accepted_nodes"][0, 0] == 2
     # sequence 1: both children rejected (q = 0 at their token), residual 0 -> sample from q
