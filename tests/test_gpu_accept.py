@@ -88,7 +88,7 @@ def _custom(B, T, V, dtype="f32"):
 def test_edge_cases_flags_and_poison():
     import eagle_draft_tree_attention_amd as ev
     log("[accept] edge cases")
-    B, T, V = 6, 4, 64
+    B, T, V = 8, 4, 64
     rng = np.random.default_rng(0)
     spec = _custom(B, T, V)
     inp = synth.make_inputs(spec.with_(q_heads=1, kv_heads=1, prefix_lens=(1,) * B), with_kv=False)
@@ -101,13 +101,18 @@ def test_edge_cases_flags_and_poison():
     tgt[3, 1, 7] = np.nan                           # unusable target row
     tgt[4, 2, :] = -np.inf                          # all -inf target row
     drf[5, 3, :] = np.nan                           # draft row of a leaf: never read
+    tgt[6, 0, :] = -np.inf                          # -inf but for one NaN (root target row)
+    tgt[6, 0, 11] = np.nan
+    drf[7, 1, :] = -np.inf                          # the same in an internal node's draft row
+    drf[7, 1, 40] = np.nan
     ver = make_verifier(spec.with_(batch=B), T)
     got = run_accept(ver, inp, 1.0, SEED, 0, target=tgt, draft=drf, parents=par, tokens=tok)
     ref = oacc.spec_accept(tgt.astype(np.float64), drf.astype(np.float64), par, tok, 1.0, SEED, 0)
     assert got["flags"].tolist() == ref["flags"].tolist() == [0, ev.FLAG_BAD_TREE, ev.FLAG_BAD_TOKEN,
-                                                             ev.FLAG_NONFINITE, ev.FLAG_NONFINITE, 0]
+                                                             ev.FLAG_NONFINITE, ev.FLAG_NONFINITE, 0,
+                                                             ev.FLAG_NONFINITE, ev.FLAG_NONFINITE]
     assert compare_accept(got, ref, "edge", par, tok, V) == 0
-    for b in (1, 2, 3, 4):
+    for b in (1, 2, 3, 4, 6, 7):
         assert got["accept_len"][b] == -1 and (got["out_tokens"][b] == -1).all()
     ver.close()
 
