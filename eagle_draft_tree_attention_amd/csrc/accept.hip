@@ -1334,7 +1334,9 @@ __device__ int root_path(const TreeInfo& ti, int n, int* path) {
 // with straight-line vector requests)
 // WR: siblings drawn without replacement (a separate instantiation, so that
 // the common kernel carries none of it)
-template <typename TL, bool VEC, bool WR>
+// LATE: the target chunk is requested once the node's children are known,
+// a leaf's after a.leaf_wait sleeps (sampled mode on the common path)
+template <typename TL, bool VEC, bool WR, bool LATE = false>
 __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a) {
   constexpr int G = Pack<TL>::G;
   constexpr int NV = kPerThread / G;   // 16-byte groups per thread and row
@@ -1371,11 +1373,13 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
 
   // ---- sequence validity (the same verdict in every workgroup of b) and
   // this node's children, in ascending index = child ordinal.  Every wave
-  // reads the sequence's parents and tokens one per lane and requests its
-  // share of the target chunk right behind them, so the row transfer is
-  // under way while the tree is checked; the draft chunk follows once the
-  // node is known to have children.  (Loads of one wave complete in order:
-  // waiting for the parents leaves the chunk requests outstanding.)
+  // reads the sequence's parents and tokens one per lane.  Without LATE it
+  // requests its share of the target chunk right behind them, so the
+  // transfer is under way while the tree is checked (loads of a wave return
+  // in order: waiting for the parents leaves the chunk requests in flight);
+  // with LATE it requests it once the node's children are known (a leaf
+  // later, see below).  The draft chunk follows once the node is known to
+  // have children.
   const int lane = tid & 63;
   const int v0 = c * kVocabChunk, v1 = min(V, v0 + kVocabChunk);
   const int64_t rowoff = static_cast<int64_t>(b * T + n) * V;
@@ -1385,8 +1389,10 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   int par = a.parents[li];
   int tok = a.tokens[li];
   u32x4_t wq[NV], wd[NV];
-  if constexpr (VEC) request_groups<TL, NV>(trow, v0, v1, wq);
-  else load_groups<TL, NV>(trow, v0, v1, false, wq);
+  if constexpr (!LATE) {
+    if constexpr (VEC) request_groups<TL, NV>(trow, v0, v1, wq);
+    else load_groups<TL, NV>(trow, v0, v1, false, wq);
+  }
   if (lane >= T) par = 0;
   if (lane < 1 || lane >= T) tok = 0;
   const bool good = lane >= T || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
@@ -1427,6 +1433,17 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   // there.  Where the workgroups of a CU compete for the vector ALU, the
   // internal nodes' waves are issued first.
   if (nkids > 0 && a.node_priority) __builtin_amdgcn_s_setprio(2);
+  // LATE: a leaf's row gates nothing until the walk ends, while the internal
+  // nodes' rows gate the first decisions and the residual rounds.  Under the
+  // full-chip burst that stages every chunk, a leaf requests its row
+  // a.leaf_wait sleeps of 640 clocks later (the host sizes the wait to the
+  // launch's bytes), so that HBM serves the internal nodes first.
+  if constexpr (LATE) {
+    if (nkids == 0)
+      for (int i = 0; i < a.leaf_wait; ++i) __builtin_amdgcn_s_sleep(10);
+    if constexpr (VEC) request_groups<TL, NV>(trow, v0, v1, wq);
+    else load_groups<TL, NV>(trow, v0, v1, false, wq);
+  }
   if (two) {
     if constexpr (VEC) request_groups<TL, NV>(drow, v0, v1, wd);
     else load_groups<TL, NV>(drow, v0, v1, false, wd);
@@ -2151,7 +2168,8 @@ hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(a.B * a.T * a.NC));
     const void* fn = a.wr ? (a.vec_ok ? reinterpret_cast<const void*>(&sa_fused<TL, true, true>)
                                       : reinterpret_cast<const void*>(&sa_fused<TL, false, true>))
-                          : (a.vec_ok ? reinterpret_cast<const void*>(&sa_fused<TL, true, false>)
+                          : (a.vec_ok ? (a.leaf_wait > 0 ? reinterpret_cast<const void*>(&sa_fused<TL, true, false, true>)
+                                                         : reinterpret_cast<const void*>(&sa_fused<TL, true, false>))
                                       : reinterpret_cast<const void*>(&sa_fused<TL, false, false>));
     return launch_fused(fn, grid, block, a, st);
   }
@@ -2174,7 +2192,8 @@ hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
 int fused_accept_capacity(int logits_bf16, int num_cus) {
   // every loader and sibling-rule variant must fit: the smallest occupancy decides
   int per_cu = 1 << 30;
-  const void* kernels[4] = {
+  const void* kernels[5] = {
+      logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, true, false, true>) : reinterpret_cast<const void*>(&sa_fused<float, true, false, true>),
       logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, true, false>) : reinterpret_cast<const void*>(&sa_fused<float, true, false>),
       logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, false, false>) : reinterpret_cast<const void*>(&sa_fused<float, false, false>),
       logits_bf16 ? reinterpret_cast<const void*>(&sa_fused<uint16_t, true, true>) : reinterpret_cast<const void*>(&sa_fused<float, true, true>),

@@ -237,6 +237,14 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
     k.round_clear = ws.round_sum + (1 - parity) * half;
     k.zero_b = cs->last_fused_b;
     k.coop = coop ? 1 : 0;
+    // Sampled mode, launches that stage at least 8 MiB of target rows: a leaf
+    // requests its rows 8 steps of 640 clocks (about 2.1 us) later, so that
+    // the internal nodes' rows, which gate the decisions, are served first
+    // from HBM.  Smaller launches gain nothing from the order, and there a
+    // walk that ends at a leaf would wait for it; greedy walks end at leaves
+    // soon after the statistics.  (LATE kernel of the common path.)
+    if (k.tau > 0.f && k.vec_ok && !k.wr && static_cast<int64_t>(k.B) * k.T * row_bytes >= (8ll << 20))
+      k.leaf_wait = 8;
     k.stamps = (stamps && static_cast<int64_t>(k.B) * per_seq * kStampSlots <= stamp_words) ? stamps : nullptr;
     int e = launch_spec_accept(k, bf16, hip_stream);
     if (e == static_cast<int>(hipErrorCooperativeLaunchTooLarge)) {

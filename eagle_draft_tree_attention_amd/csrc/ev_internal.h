@@ -130,6 +130,8 @@ struct AcceptKernelArgs {
   uint32_t spin_limit;    // bounded waits: a wait that exceeds it flags the sequence
   uint64_t* stamps;       // fused path: phase timeline [workgroup][kStampSlots] (diagnostic), or NULL
   int node_priority;      // fused path: internal nodes' waves at a raised priority
+  int leaf_wait;          // fused path, sampled, whole 16-byte groups, siblings with replacement:
+                          // s_sleep(10) steps a leaf waits before requesting its rows (0: none)
   int fused;              // 1: one co-resident kernel; 0: three-kernel path
   int coop;               // host side: launch the fused kernel cooperatively
   int b0;                 // batch index of sequence 0 of this launch (a slice of the call's batch)
