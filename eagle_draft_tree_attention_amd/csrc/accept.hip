@@ -1032,6 +1032,7 @@ struct FusedShared {
   // repeats an earlier sibling's), and the draft mass not yet tried
   double wfz[kMaxTree];
   double zrem;
+  int32_t tok[kMaxTree];   // the sequence's draft tokens by node (the outputs read them from here)
 };
 
 // Siblings drawn without replacement (thread 0): sibling i is tested against
@@ -1450,6 +1451,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
   if (tid < 64) {
     sh.ti.par[lane] = par;
+    sh.tok[lane] = tok;
     if (is_child) {
       const int ord = __popcll(kids_mask & ((1ull << lane) - 1ull));
       Cand cd;
@@ -2146,7 +2148,7 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   }
   for (int j = tid; j < T; j += kThreads) {
     a.accepted_nodes[b * T + j] = (j < len) ? path_lds[j + 1] : -1;
-    a.out_tokens[b * T + j] = (j < len) ? a.tokens[b * T + path_lds[j + 1]] : (j == len ? final_tok : -1);
+    a.out_tokens[b * T + j] = (j < len) ? sh.tok[path_lds[j + 1]] : (j == len ? final_tok : -1);
   }
   stamp(a.stamps, 21);   // outputs written
 }
