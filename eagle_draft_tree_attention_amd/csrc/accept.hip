@@ -1345,6 +1345,17 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   __shared__ int32_t path_lds[kMaxTree];
   __shared__ __attribute__((aligned(16))) TL lq[kVocabChunk];
   __shared__ __attribute__((aligned(16))) TL lp[kVocabChunk];
+  // One field of each 64-byte line of the argument block, requested together
+  // and waited for once: later first uses of the other fields then hit the
+  // scalar cache instead of each paying a round trip.
+  {
+    const void* l0 = a.target;
+    const void* l1 = a.near_ties;
+    const void* l2 = a.node_pub;
+    const int l3 = a.T;
+    const float l4 = a.tau;
+    asm volatile("" ::"s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(l4));
+  }
   const int NC = a.NC, T = a.T, V = a.V, tid = threadIdx.x;
   const int c = blockIdx.x % NC;
   const int n = (blockIdx.x / NC) % T;
