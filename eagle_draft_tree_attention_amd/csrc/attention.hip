@@ -234,22 +234,31 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   __shared__ int32_t par_lds[kMaxTree];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, ln = lane & 15;
-  stamp(a.stamps, 0);
   // KG = 2: waves w and w + 2 own the same row block and take the first and
   // the second 32 keys of every tile; their states are combined at the end
   const int rw = wave % (4 / KG);
   const int kh = __builtin_amdgcn_readfirstlane(wave / (4 / KG));
   // The launch scalars (and the first sequence's split range, prefix length
   // and expected row offset) are requested together and waited for once,
-  // instead of one dependent round trip per use.
+  // instead of one dependent round trip per use: first one field of each
+  // 64-byte line of the argument block that the prologue reads.
+  {
+    const void* l0 = a.k;
+    const int l1 = a.nwg;
+    uint64_t* const l2 = a.stamps;
+    const int l3 = a.L[0], l19 = a.split_base[1], l35 = a.kv0_guess[0];
+    asm volatile("" ::"s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(l19), "s"(l35));
+  }
   const int a_nwg = a.nwg, a_rt = a.row_tiles, a_ts = a.total_splits, a_B = a.B;
   const int T = a.T, g = a.g, R = a.R, Hq = a.Hq;
   const int b0_base = 0, b0_next = a.split_base[1], b0_L = a.L[0], b0_guess = a.kv0_guess[0];
   const void* const a_k = a.k;
   const void* const a_v = a.v;
   const int32_t* const a_par = a.parents;
+  uint64_t* const a_stamps = a.stamps;
   asm volatile("" ::"s"(a_nwg), "s"(a_rt), "s"(a_ts), "s"(a_B), "s"(T), "s"(g), "s"(R), "s"(Hq), "s"(b0_next), "s"(b0_L),
-               "s"(b0_guess), "s"(a_k), "s"(a_v), "s"(a_par));
+               "s"(b0_guess), "s"(a_k), "s"(a_v), "s"(a_par), "s"(a_stamps));
+  stamp(a_stamps, 0);
   const int logical = xcd_remap(blockIdx.x, a_nwg);
   // logical order: row tile fastest, then key split, then KV head, so the
   // row tiles of one K/V chunk share an XCD's L2 and every XCD receives its
