@@ -481,6 +481,15 @@ eagle_status eagle_verify_kv_commit(eagle_verify* h, const eagle_kv_commit_args*
   k.pps = a->pages_per_seq;
   k.num_pages = a->page_size ? a->num_kv_rows / a->page_size : 0;
   for (int b = 0; b < a->batch; ++b) k.L[b] = a->prefix_lens_host[b];
+  // heads per workgroup: split each row into the largest number of head
+  // groups (a power of two dividing Hkv) that keeps the launch within 256
+  // workgroups, so a single sequence still spreads over the chip while a
+  // large batch moves whole rows (thousands of one-head workgroups cost more
+  // in per-workgroup set-up than they gain; 1024 was slower at B = 4)
+  k.head_groups = 1;
+  while (k.head_groups * 2 <= k.Hkv && k.Hkv % (k.head_groups * 2) == 0 &&
+         static_cast<int64_t>(k.layers) * k.B * k.head_groups * 2 <= 256)
+    k.head_groups *= 2;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int e = ev::launch_kv_commit(k, h->desc.kv_dtype == EAGLE_BF16, stream);
   h->last_stream = stream;

@@ -182,6 +182,7 @@ struct CommitKernelArgs {
   int page_size, pps;
   int64_t num_pages;
   int B, T, Hkv, D, layers;
+  int head_groups;     // workgroups per (layer, sequence): each moves the rows of Hkv / head_groups heads
   int32_t L[kMaxBatch];
 };
 

@@ -85,6 +85,9 @@ CASES = [
     ("f32_d64_two_seqs", (5, 64), 16, 2, 64, "f32"),
     ("bf16_d64_max_tree", (300,), 64, 4, 64, "bf16"),
     ("f32_d128_one_node", (9, 3, 17, 1), 1, 1, 128, "f32"),
+    # an odd head count keeps whole rows in one workgroup: a move of
+    # 2 x 129 x 128 x 4 bytes spans several copy chunks
+    ("f32_d128_129_heads", (41, 7), 24, 129, 128, "f32"),
 ]
 
 
@@ -156,17 +159,25 @@ def test_two_calls_in_a_row_act_on_the_committed_cache():
     ver.close()
 
 
-def test_every_layer_in_one_launch():
-    rng = np.random.default_rng(10)
-    T, Hkv, D, layers = 9, 2, 64, 3
-    lens = [6, 14]
+@pytest.mark.parametrize("layers,B,Hkv", [(3, 2, 2), (8, 40, 8)], ids=["3x2_heads2", "8x40_heads8"])
+def test_every_layer_in_one_launch(layers, B, Hkv):
+    # the second shape has 320 (layer, sequence) pairs: each workgroup moves
+    # a group of 4 of the 8 heads
+    rng = np.random.default_rng(10 + B)
+    T, D = 9, 64
+    lens = [6, 14] if B == 2 else [int(x) for x in rng.integers(0, 30, size=B)]
     per = [_case(rng, lens, T, Hkv, D, "bf16") for _ in range(layers)]
     indptr = per[0][2]
     k = np.stack([p[0] for p in per])
     v = np.stack([p[1] for p in per])
-    nodes = _nodes([[2, 5, 8], [3, 4]], T)
-    alen = [3, 2]
-    ver = _verifier(2, Hkv, D, T, "bf16")
+    if B == 2:
+        paths = [[2, 5, 8], [3, 4]]
+    else:
+        paths = [_root_path(_tree(rng, T), int(rng.integers(0, T))) for _ in range(B)]
+    nodes = _nodes(paths, T)
+    alen = [len(p) for p in paths]
+    log(f"[kv_commit] layers {layers} B {B} Hkv {Hkv}")
+    ver = _verifier(B, Hkv, D, T, "bf16")
     got = _gpu_commit(ver, k, v, indptr, lens, alen, nodes, "bf16")
     want_k, want_v = [], []
     for layer in range(layers):
