@@ -200,6 +200,41 @@ __device__ __forceinline__ void lds_dma16_sbase(const void* sbase, uint32_t voff
                : "v"(voff_bytes), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
+// 4 bytes per lane, global -> LDS at lds_base + 4 * lane (lds_base is
+// wave-uniform); like lds_dma16, completion is awaited explicitly.
+__device__ __forceinline__ void lds_dma4(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// 64-bit value of lane src
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(static_cast<uint32_t>(v)), src));
+  const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(static_cast<uint32_t>(v >> 32)), src));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Ancestor word (bit j set for every node j on the root path, the node
+// included) of node `lane`, for a validated parent array (par < lane for
+// lane >= 1), built on the wave's lanes by pointer jumping: lane i holds the
+// nodes of its path from i up to, not including, the node it points at
+// (initially itself and its parent), and each round appends the pointed-at
+// lane's segment and takes over its pointer, doubling the reach.  A depth of
+// at most 63 needs at most 6 rounds.  Lanes at or past T return the root.
+__device__ __forceinline__ uint64_t ancestor_word(int lane, int T, int par) {
+  uint64_t m = lane < T ? (1ull << lane) : 0ull;
+  int p = (lane > 0 && lane < T) ? par : 0;
+  for (int it = 0; it < 6 && __any(p != 0); ++it) {
+    const uint64_t mp = shfl_u64(m, p);
+    const int pp = __shfl(p, p);
+    m |= mp;
+    p = pp;
+  }
+  return m | 1ull;
+}
+
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint64_t u = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
@@ -230,8 +265,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   static_assert(IPW >= 1 && 2 * IPW * (NST - 1) < 64, "load geometry");
 
   __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NST * 2 * TILE];
-  __shared__ uint64_t anc_lds[kMaxTree];
-  __shared__ int32_t par_lds[kMaxTree];
+  __shared__ int32_t par_lds[4][kMaxTree];   // each wave's copy of the parent array
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lg = lane >> 4, ln = lane & 15;
   // KG = 2: waves w and w + 2 own the same row block and take the first and
@@ -274,10 +308,13 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   const int L = b == 0 ? b0_L : a.L[b];
   const int row_base = rt * a.rows_per_tile + rw * 16 * MB;   // lane rows: row_base + 16*rb + ln
 
-  // The first tile is requested from the expected row offset of the
-  // sequence, without waiting for kv_indptr[b]; the parent array is requested
-  // before it, and nothing waits on either until the tile has landed.
-  const int par_lane = lane < T ? a_par[b * T + lane] : 0;
+  // The parent array (each wave its own copy, straight into LDS), the query
+  // rows and the first tile are requested in that order, the tile from the
+  // expected row offset of the sequence, without waiting for kv_indptr[b].
+  // The sequence is validated and its ancestor words are built once the
+  // parents and the query rows have landed, while the tile is in flight.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  lds_dma4(a_par + b * T + min(lane, T - 1), lds_offset(&par_lds[wave_u][0]));
   constexpr bool paged = PAGED;
   const int guess = b == 0 ? b0_guess : a.kv0_guess[b];
   int64_t kv0 = paged ? 0 : (guess >= 0 ? (int64_t)guess : a.kv_indptr[b]);
@@ -298,7 +335,6 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   // softmax) and clamps every row index into the array, so the loads stay in
   // bounds even for a sequence that the validation below rejects.
   const int l_row = lane / CH, l_pos = lane % CH;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_kv = lds_offset(kv_lds);
   // per-lane byte offsets of this wave's transfer lanes inside a tile whose
   // rows are all valid (row r of the tile = row0 + r)
@@ -355,12 +391,6 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
       lds_dma16(vbase + gr * row_stride + (l_pos ^ swz_v<D>(r)) * 8, vdst + static_cast<uint32_t>(r0 * D * 2));
     }
   };
-  // the first tile and the query rows are in flight together; the sequence
-  // is validated once they have landed
-#pragma unroll
-  for (int j = 0; j < NST - 1; ++j)
-    if (j < n_tiles) issue(j);
-
   // query rows -> B operands of S^T = K Q^T (zero for padding rows)
   bool row_ok[MB];
   int node[MB], head[MB];
@@ -378,19 +408,24 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
       qf[rb][s] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
+  static_assert(NST == 2, "the prologue requests one tile");
+  if (n_tiles > 0) issue(0);
 
   const int64_t kv0_true = paged ? 0 : a.kv_indptr[b];
   const int64_t kv1_true = paged ? 0 : a.kv_indptr[b + 1];
-  wait_vmcnt<0>();   // the first tile, the parents and the query rows have landed
-  stamp(a.stamps, 1);
+  // every request before the tile's 2 IPW transfers has completed: the
+  // parents and the query rows
+  if (n_tiles > 0) wait_vmcnt<2 * IPW>();
+  else wait_vmcnt<0>();
+  asm volatile("" ::: "memory");   // the parents are read from LDS only after the wait
+  stamp(a.stamps, 1);   // parents and query rows
+  const int par_lane = lane < T ? par_lds[wave_u][lane] : 0;
   if (kv0 != kv0_true) {   // the expected offset was wrong: request the first tile again
+    wait_vmcnt<0>();       // (the first request has landed: no two transfers into one stage)
     kv0 = kv0_true;
     split_in_bounds = kv0 >= 0 && kv0 + k_end <= a.num_kv_rows;
-#pragma unroll
-    for (int j = 0; j < NST - 1; ++j)
-      if (j < n_tiles) issue(j);
+    if (n_tiles > 0) issue(0);
   }
-  if (wave == 0 && lane < 64) par_lds[lane] = par_lane;
   const uint32_t bad = seq_flags(a, b, lane, par_lane, kv0_true, kv1_true);
   if (s_local == 0 && hk == 0 && rt == 0 && tid == 0) a.flags[b] = bad;
   if (bad) {
@@ -409,12 +444,11 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
     }
     return;
   }
-  __syncthreads();
-  if (tid < T) anc_lds[tid] = ancestors_of(par_lds, tid);
-  __syncthreads();   // ancestor words
+  // ancestor words on the wave's own lanes (no LDS, no barrier)
+  const uint64_t anc_lane = ancestor_word(lane, T, par_lane);
   uint64_t anc_row[MB];
 #pragma unroll
-  for (int rb = 0; rb < MB; ++rb) anc_row[rb] = anc_lds[node[rb]];
+  for (int rb = 0; rb < MB; ++rb) anc_row[rb] = shfl_u64(anc_lane, node[rb]);
   stamp(a.stamps, 2);   // ancestor words
 
   // O^T accumulators, and the row sums of P: the matrix unit adds them as the

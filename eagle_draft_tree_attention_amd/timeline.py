@@ -16,7 +16,7 @@ import sys
 
 import numpy as np
 
-ATTN_MARKS = {0: "start", 1: "first K/V tile and query rows landed", 2: "ancestor words built",
+ATTN_MARKS = {0: "start", 1: "parents and query rows landed", 2: "ancestor words built",
               3: "tile loop done", 4: "partial rows stored", 5: "row statistics published",
               6: "every split of its merge rows arrived", 7: "merged rows written"}
 ACC_MARKS = {0: "start", 1: "chunk in LDS", 2: "chunk statistics", 3: "row statistics combined",
@@ -136,7 +136,8 @@ def main(argv=None):
     print(f"\n## tree_attn_mfma: {plan.workgroups} workgroups, {plan.total_splits} key splits x "
           f"{plan.row_tiles} row tiles, {plan.chunk_keys} keys per split, merge inside: {plan.merge_in_kernel}")
     marks = {k: [] for k in ATTN_MARKS}
-    durs = {"first tile": (0, 1), "ancestors": (1, 2), "tile loop": (2, 3), "epilogue": (3, 4),
+    durs = {"parents and query rows": (0, 1), "ancestors": (1, 2),
+            "tile loop (from the first tile's wait)": (2, 3), "epilogue": (3, 4),
             "publish": (4, 5), "merge wait": (5, 6), "merge": (6, 7)}
     dvals = {k: [] for k in durs}
     ends, tiles = [], []

@@ -431,8 +431,8 @@ EAGLE_API eagle_status eagle_verify_last_attention_plan(const eagle_verify* h, e
  * call.  A call of several fused launches (a batch cut into slices) leaves
  * the last launch's words.  Other kernels record nothing.
  *   tree attention (workgroup = (KV head, key split, row tile)):
- *     0 start, 1 first K/V tile and query rows landed, 2 ancestor words
- *     built, 3 tile loop done, 4 partial (or final) rows stored, 5 row
+ *     0 start, 1 parent array and query rows landed (the first K/V tile
+ *     may still be in flight), 2 ancestor words built, 3 tile loop done, 4 partial (or final) rows stored, 5 row
  *     statistics published (in-kernel merge only), 6 every split of the rows
  *     it merges has arrived, 7 merged rows written; word 30 = tiles of the
  *     workgroup, 31 = split | KV head << 16 | row tile << 32 | sequence << 48
