@@ -799,6 +799,14 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   // rows as soon as the words of all S splits for those rows carry the tag:
   //   out = sum_s w_s O_s,  w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s'
   const uint64_t tag = static_cast<uint64_t>(static_cast<uint32_t>(a.epoch)) << 32;
+  // "some split not arrived" flags of the merge polls, slot it % 3 for poll
+  // it.  Poll it clears the slot of poll it + 1: every wave read that slot
+  // (as poll it - 2's) before reaching the barrier of poll it - 1, and no
+  // wave writes it before passing the barrier of poll it, so one barrier a
+  // poll suffices (the runtime's barrier reductions would also load the
+  // workgroup size from the kernel's hidden arguments first)
+  __shared__ int pending[3];
+  if (tid < 3) pending[tid] = 0;
   stores_done();
   __syncthreads();   // every wave's partial O rows are in memory
 #pragma unroll
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   // [np] and l [np] (the host keeps 2 np floats within the ring)
   f32x4_t* red = reinterpret_cast<f32x4_t*>(kv_lds);
   float* wsm = reinterpret_cast<float*>(kv_lds) + 1024;
-  for (uint32_t it = 0;; ++it) {
+  for (uint32_t it = 0, slot3 = 0;; ++it, slot3 = slot3 == 2 ? 0 : slot3 + 1) {
     int ready = 1;
     for (int p = tid; p < np; p += 256) {
       const int i = p / S, sj = p - i * S;
@@ -834,7 +842,10 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
       wsm[p] = __uint_as_float(static_cast<uint32_t>(wm));
       wsm[np + p] = __uint_as_float(static_cast<uint32_t>(wl));
     }
-    if (__syncthreads_and(ready)) break;
+    if (!ready) pending[slot3] = 1;
+    if (tid == 0) pending[slot3 == 2 ? 0 : slot3 + 1] = 0;   // the slot of poll it + 1
+    __syncthreads();
+    if (pending[slot3] == 0) break;
     if (it >= a.spin_limit) {   // gave up: this split's rows are poisoned and the sequence flagged
       for (int e = tid; e < nr * D; e += 256) {
         const int r = rt * rpt + r_lo + e / D;
