@@ -525,6 +525,8 @@ eagle_status eagle_verify_tree_expand(eagle_verify* h, const eagle_tree_expand_a
   k.M = a->keep;
   k.c2 = static_cast<float>(1.4426950408889634 / a->temperature);
   k.inv_tau = 1.0 / static_cast<double>(a->temperature);
+  k.stamps = (h->stamps && (static_cast<int64_t>(k.B) * k.F * k.NC + k.B) * ev::kStampSlots <= h->stamp_words)
+                 ? h->stamps : nullptr;
   hipStream_t stream = reinterpret_cast<hipStream_t>(hip_stream);
   const int e = ev::launch_tree_expand(k, h->desc.logits_dtype == EAGLE_BF16, stream);
   h->last_stream = stream;

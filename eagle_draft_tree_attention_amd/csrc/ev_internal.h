@@ -217,6 +217,7 @@ struct ExpandKernelArgs {
   int chunk;           // vocabulary tokens per chunk (2048, 4096 or 8192)
   float c2;            // log2(e) / t
   double inv_tau;      // 1 / t
+  uint64_t* stamps;    // diagnostic timeline (32 words per chunk workgroup, then per sequence), or NULL
 };
 
 constexpr int kMaxSteps = 64;         // chained expansion steps one rerank reads

@@ -34,6 +34,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ev_device.h"
 #include "ev_internal.h"
 
 namespace ev {
@@ -134,104 +135,164 @@ __device__ __forceinline__ uint64_t cand_key(float x, int id) {
 __device__ __forceinline__ float key_logit(uint64_t k) { return unord32(static_cast<uint32_t>(k >> 32)); }
 __device__ __forceinline__ int key_token(uint64_t k) { return static_cast<int>(~static_cast<uint32_t>(k)); }
 
-// EPT logits per thread: chunks of 256 * EPT tokens (2048, 4096 or 8192,
-// the smallest that keeps a row within 64 chunks)
-template <typename TL, int EPT>
+// timeline mark k of workgroup slot `slot` (thread 0 only; diagnostic)
+__device__ __forceinline__ void mark(uint64_t* stamps, int64_t slot, int k) {
+  if (stamps && threadIdx.x == 0) stamps[slot * 32 + k] = __builtin_amdgcn_s_memrealtime();
+}
+
+// EPT logits of this thread (tokens v .. v + EPT - 1), -inf at or past `end`.
+// VEC: the row starts on a 16-byte boundary and holds whole 16-byte groups.
+template <typename TL, int EPT, bool VEC>
+__device__ __forceinline__ void load_run(const TL* row, int v, int end, float (&xs)[EPT]) {
+  if constexpr (VEC) {
+    constexpr int G = 16 / static_cast<int>(sizeof(TL));   // tokens per 16-byte group
+    u32x4_t w[EPT / G];
+#pragma unroll
+    for (int g = 0; g < EPT / G; ++g)
+      w[g] = (v + g * G < end) ? *reinterpret_cast<const u32x4_t*>(row + v + g * G) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < EPT / G; ++g) {
+      const bool in = v + g * G < end;
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        float x;
+        if constexpr (sizeof(TL) == 2)
+          x = __uint_as_float((e & 1) ? (w[g][e >> 1] & 0xFFFF0000u) : (w[g][e >> 1] << 16));
+        else
+          x = __uint_as_float(w[g][e]);
+        xs[g * G + e] = in ? x : kNegInf;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) xs[j] = (v + j < end) ? logit_at<TL>(row, v + j) : kNegInf;
+  }
+}
+
+__device__ __forceinline__ uint32_t umax32(uint32_t p, uint32_t q) { return p > q ? p : q; }
+
+// Chunks of 256 * EPT tokens (2048, 4096 or 8192, the smallest that keeps a
+// row within 64 chunks).  Thread t owns the EPT consecutive tokens v0 + EPT t
+// .. + EPT - 1, so lane order and wave order follow token order: among equal
+// logits the lowest lane holds the lowest token id, and a ballot's first
+// lane breaks ties.
+template <typename TL, int EPT, bool VEC>
 __global__ __launch_bounds__(kThreads) void te_chunk(const ExpandKernelArgs a) {
-  constexpr int kPerThread = EPT;
-  constexpr int kChunk = kThreads * EPT;
-  __shared__ float rmax[kThreads / 64];
-  __shared__ uint32_t rbad[kThreads / 64];
-  __shared__ double rsum[kThreads / 64];
+  constexpr int kWaves = kThreads / 64;
+  __shared__ float wmax[kWaves];
+  __shared__ uint32_t wbad[kWaves];
+  __shared__ double wsum[kWaves];
+  __shared__ float wl_v[kWaves][kMaxTopK];
+  __shared__ int wl_t[kWaves][kMaxTopK];
+  __shared__ int wl_n[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NC = a.NC, V = a.V, K = a.K;
   const int c = blockIdx.x % NC;
   const int row = blockIdx.x / NC;   // b * F + f
   const TL* x = reinterpret_cast<const TL*>(a.logits) + static_cast<int64_t>(row) * V;
-  const int v0 = c * kChunk, v1 = min(V, v0 + kChunk);
+  const int v0 = c * a.chunk;
+  const int vt = v0 + EPT * tid;   // this thread's first token
+  mark(a.stamps, blockIdx.x, 0);
 
-  // this thread's logits: tokens v0 + tid + 256 j
-  float xs[kPerThread];
+  float xs[EPT];
+  load_run<TL, EPT, VEC>(x, vt, min(V, v0 + a.chunk), xs);
+  // chunk maximum and NaN/+inf flag (NaN and +inf make the row unusable and
+  // are never candidates; -inf neither)
   float m = kNegInf;
   uint32_t bad = 0;
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int v = v0 + tid + kThreads * j;
-    xs[j] = v < v1 ? logit_at<TL>(x, v) : kNegInf;
-    if (xs[j] != xs[j] || xs[j] == __builtin_inff()) bad = 1;
-    else m = fmaxf(m, xs[j]);
+  for (int j = 0; j < EPT; ++j) {
+    if (xs[j] != xs[j] || xs[j] == __builtin_inff()) {
+      bad = 1;
+      xs[j] = kNegInf;
+    }
+    m = fmaxf(m, xs[j]);
   }
-  // block maximum and bad flag
   m = wave_max_f32(m);
   bad = __any(bad != 0) ? 1u : 0u;
   if (lane == 0) {
-    rmax[wave] = m;
-    rbad[wave] = bad;
+    wmax[wave] = m;
+    wbad[wave] = bad;
   }
   __syncthreads();
-  m = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
-  bad = rbad[0] | rbad[1] | rbad[2] | rbad[3];
-  // sum of exp((x - m) / t) over the chunk: fp32 exponentials, fp64 sum
+  mark(a.stamps, blockIdx.x, 1);
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  bad = wbad[0] | wbad[1] | wbad[2] | wbad[3];
+  // sum of exp((x - m) / t): fp32 exponentials of the exact difference, fp64 sum
   double z = 0.0;
   if (m != kNegInf) {
-    const float mc = -m * a.c2;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) z += static_cast<double>(__builtin_amdgcn_exp2f(__builtin_fmaf(xs[j], a.c2, mc)));
+    for (int j = 0; j < EPT; ++j) z += static_cast<double>(__builtin_amdgcn_exp2f((xs[j] - m) * a.c2));
   }
   z = wave_sum_f64(z);
-  if (lane == 0) rsum[wave] = z;
+  if (lane == 0) wsum[wave] = z;
 
-  // top K of the chunk: each wave first takes the K largest of its 64 * EPT
-  // logits in K rounds (each lane offers its best not yet taken, the wave
-  // keeps the winner), then wave 0 merges the four waves' sorted lists.
-  // NaN and +inf are never candidates (the row is unusable anyway), -inf
-  // neither.  Within a lane, a lower j is a lower token id.
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j)
-    if (!(xs[j] < __builtin_inff())) xs[j] = kNegInf;
-  __shared__ float wl_v[kThreads / 64][kMaxTopK];
-  __shared__ int wl_i[kThreads / 64][kMaxTopK];
+  // the wave's k largest: each round every lane offers its best untaken
+  // logit (lowest token first among equal ones), the wave keeps the largest
+  // (lowest lane among equal ones) and only the winning lane moves on
   uint32_t taken = 0;
-  for (int q = 0; q < K; ++q) {
-    float lb = kNegInf;
-    int lj = -1;
+  float lb = kNegInf;
+  int lj = -1;
+  auto rescan = [&]() {
+    lb = kNegInf;
+    lj = -1;
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j)
-      if (!((taken >> j) & 1u) && xs[j] > lb) {
-        lb = xs[j];
-        lj = j;
-      }
-    const uint64_t key = lj >= 0 ? cand_key(lb, v0 + tid + kThreads * lj) : 0ull;
-    const uint64_t best = wave_max_u64(key);
-    if (lj >= 0 && key == best) taken |= 1u << lj;   // token ids are unique: one lane wins
-    if (lane == 0) {
-      wl_v[wave][q] = best ? key_logit(best) : kNegInf;
-      wl_i[wave][q] = best ? key_token(best) : -1;
+    for (int j = 0; j < EPT; ++j) {
+      const bool better = !((taken >> j) & 1u) && xs[j] > lb;
+      lb = better ? xs[j] : lb;
+      lj = better ? j : lj;
+    }
+  };
+  rescan();
+  int nq = 0;
+  for (; nq < K; ++nq) {
+    const uint32_t key = lj >= 0 ? ord32(lb) : 0u;
+    const uint32_t kmax = wave_reduce32(key, 0u, umax32);
+    if (kmax == 0u) break;   // every logit of the wave is taken or -inf
+    const int wl = __ffsll(static_cast<long long>(__ballot(key == kmax))) - 1;
+    if (lane == wl) {
+      wl_v[wave][nq] = lb;
+      wl_t[wave][nq] = vt + lj;
+      taken |= 1u << lj;
+      rescan();
     }
   }
+  if (lane == 0) wl_n[wave] = nq;
   __syncthreads();
+  mark(a.stamps, blockIdx.x, 2);
+
+  // the chunk's k largest from the waves' lists: lane i holds entry i of the
+  // concatenated lists and counts the entries ahead of it by lane reads
   ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC + c;
-  if (tid == 0) {
-    rec->m = m;
-    rec->bad = bad;
-    rec->z = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
-  }
-  if (wave == 0) {   // lanes 0..3 hold the heads of the four waves' lists
-    int hd = 0;
-    for (int q = 0; q < K; ++q) {
-      const uint64_t key = (lane < kThreads / 64 && hd < K && wl_i[lane][hd] >= 0)
-                               ? cand_key(wl_v[lane][hd], wl_i[lane][hd]) : 0ull;
-      uint64_t best = max_u64(key, dpp_mov64<0xB1, 0xf>(0ull, key));   // quad_perm 1,0,3,2
-      best = max_u64(best, dpp_mov64<0x4E, 0xf>(0ull, best));          // quad_perm 2,3,0,1
-      best = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(best >> 32), 0))) << 32) |
-             static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(best), 0));
-      if (key != 0ull && key == best) ++hd;
-      if (lane == 0) {
-        rec->val[q] = best ? key_logit(best) : kNegInf;
-        rec->id[q] = best ? key_token(best) : -1;
-      }
+  if (wave == 0) {
+    const int wq = min(lane / K, kWaves - 1), rq = lane - (lane / K) * K;
+    const bool valid = lane < kWaves * K && rq < wl_n[wq];
+    const float cv = valid ? wl_v[wq][rq] : kNegInf;
+    const int ct = valid ? wl_t[wq][rq] : 0;
+    const uint64_t key = valid ? cand_key(cv, ct) : 0ull;   // larger logit, then lower token: larger key
+    const uint32_t klo = static_cast<uint32_t>(key), khi = static_cast<uint32_t>(key >> 32);
+    int rank = 0;
+    for (int j = 0; j < kWaves * K; ++j) {
+      const uint64_t kj = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(khi), j))) << 32) |
+                          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(klo), j));
+      rank += kj > key ? 1 : 0;
+    }
+    const int total = wl_n[0] + wl_n[1] + wl_n[2] + wl_n[3];
+    if (valid && rank < K) {
+      rec->val[rank] = cv;
+      rec->id[rank] = ct;
+    }
+    if (lane >= total && lane < K) {   // past the chunk's candidates
+      rec->val[lane] = kNegInf;
+      rec->id[lane] = -1;
+    }
+    if (lane == 0) {
+      rec->m = m;
+      rec->bad = bad;
+      rec->z = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
     }
   }
+  mark(a.stamps, blockIdx.x, 3);
 }
 
 constexpr int kSelWaves = 8;   // frontier rows worked on at once by one workgroup
@@ -242,19 +303,37 @@ static_assert(offsetof(ChunkRecord, z) == 8 && kRecVal % 16 == 0 && kRecId % 16 
 
 // One workgroup per sequence.  Row phase: wave w takes frontier rows
 // w, w + 8, ...; for each, lane c reads chunk c's record (its sorted list
-// stays in the lane's registers), the wave reduces the row's maximum,
-// normaliser and unusable flag, and takes the row's top K as a K-step merge
-// of the chunks' lists (each step the best head), valued
-// s + (x - max)/t - log Z in fp64, into LDS.  Selection phase (all threads):
-// each candidate's rank is the number of candidates before it, and it is
-// written straight to that output slot.
+// stays in the lane's registers, KMAX >= k entries), the wave reduces the
+// row's maximum, normaliser and unusable flag, and takes the row's top k as
+// a k-step merge of the chunks' lists (each step the largest head: a 32-bit
+// key maximum, ties to the lowest chunk, which holds the lowest token ids);
+// then lane q values entry q as s + (x - max)/t - log Z in fp64.  Selection
+// phase: each candidate's rank is the number of candidates before it (every
+// wave counts against its share of the others, read from LDS as broadcasts,
+// and adds its count with an LDS atomic), and it is written straight to
+// that output slot.
+template <int KMAX>
 __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelArgs a) {
-  __shared__ double sv[kMaxTree][kMaxTopK];   // row f's candidates: value
-  __shared__ int st[kMaxTree][kMaxTopK];      // and token, sorted
-  __shared__ float sx[kMaxTree][kMaxTopK];    // and logit (equal logits of one row tie exactly)
-  __shared__ int scnt[kMaxTree], sbad[kMaxTree];
+  constexpr int kSel = 64 * kSelWaves;
+  __shared__ double sv[kMaxTree * kMaxTopK];   // slot f * K + q: candidate value, -inf past a row's list
+  __shared__ int st[kMaxTree * kMaxTopK];      // its token
+  __shared__ float sx[kMaxTree * kMaxTopK];    // and logit (equal logits of one row tie exactly)
+  __shared__ uint64_t skey[kMaxTree * kMaxTopK];   // order-preserving key of the value (0: no candidate)
+  __shared__ int srank[kMaxTree * kMaxTopK];
+  __shared__ int byrank[kMaxKeep + 1];
+  // block-wide counts and flags through LDS words and plain barriers (the
+  // runtime's barrier reductions first load the workgroup size from the
+  // dispatch packet, a scalar-cache miss on the critical path)
+  __shared__ int nvalid_lds, anybad_lds, nnear_lds;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, b = blockIdx.x;
   const int F = a.F, M = a.M, NC = a.NC, K = a.K;
+  const int64_t mslot = static_cast<int64_t>(a.B) * F * NC + b;   // timeline slot
+  mark(a.stamps, mslot, 0);
+  if (threadIdx.x == 0) {   // published by the barrier after the row phase
+    nvalid_lds = 0;
+    anybad_lds = 0;
+    nnear_lds = 0;
+  }
 
   for (int f = wave; f < F; f += kSelWaves) {
     const int row = b * F + f;
@@ -263,129 +342,132 @@ __global__ __launch_bounds__(64 * kSelWaves) void te_select(const ExpandKernelAr
     // registers (16-byte groups of logits and of ids).
     const float s = a.scores[row];
     const ChunkRecord* const rec = a.chunks + static_cast<int64_t>(row) * NC;
-    const int nq = (K + 3) / 4;
-    u32x4_t w0 = {0u, 0u, 0u, 0u}, wv[kMaxTopK / 4], wi[kMaxTopK / 4];
+    u32x4_t w0 = {0u, 0u, 0u, 0u}, wv[KMAX / 4], wi[KMAX / 4];
+#pragma unroll
+    for (int j = 0; j < KMAX / 4; ++j) wv[j] = wi[j] = u32x4_t{0u, 0u, 0u, 0u};
     if (lane < NC) {
       const u32x4_t* r4 = reinterpret_cast<const u32x4_t*>(rec + lane);
       w0 = r4[0];
 #pragma unroll
-      for (int j = 0; j < kMaxTopK / 4; ++j)
-        if (j < nq) {
-          wv[j] = r4[kRecVal / 16 + j];
-          wi[j] = r4[kRecId / 16 + j];
-        }
-    }
-    if (!(s > kNegInf)) {   // inactive (NaN and -inf): no candidates, not flagged
-      if (lane == 0) {
-        scnt[f] = 0;
-        sbad[f] = 0;
+      for (int j = 0; j < KMAX / 4; ++j) {
+        wv[j] = r4[kRecVal / 16 + j];
+        wi[j] = r4[kRecId / 16 + j];
       }
-      continue;
     }
-    const float mc = lane < NC ? __uint_as_float(w0[0]) : kNegInf;
-    const uint32_t bad = lane < NC ? w0[1] : 0u;
-    const double zc = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(w0[3]) << 32) | w0[2]));
-    const float mx = wave_max_f32(mc);
-    if (__any(bad != 0) || mx == kNegInf) {   // unusable row: skipped, the sequence is flagged
-      if (lane == 0) {
-        scnt[f] = 0;
-        sbad[f] = 1;
-      }
-      continue;
-    }
-    const double z = wave_sum_f64(
-        (lane < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - mx) * static_cast<double>(a.c2)) : 0.0);
-    const double lz = log(z);
-    int hd = 0, cnt = 0;
-    for (int q = 0; q < K; ++q) {
-      // this lane's head: entry hd of its chunk's list
-      uint32_t hv = 0u, hi = 0xFFFFFFFFu;
+    int cnt = 0;
+    int rbad = 0;
+    if (s > kNegInf) {   // inactive rows (NaN, -inf) have no candidates and are not flagged
+      const float mc = lane < NC ? __uint_as_float(w0[0]) : kNegInf;
+      const uint32_t cb = lane < NC ? w0[1] : 0u;
+      const double zc = __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(w0[3]) << 32) | w0[2]));
+      const float mx = wave_max_f32(mc);
+      if (f == 0) mark(a.stamps, mslot, 1);
+      if (__any(cb != 0) || mx == kNegInf) {   // unusable row: skipped, the sequence is flagged
+        rbad = 1;
+      } else {
+        const double z = wave_sum_f64(
+            (lane < NC && mc != kNegInf) ? zc * exp2((static_cast<double>(mc) - mx) * static_cast<double>(a.c2)) : 0.0);
+        const double lz = log(z);
+        if (f == 0) mark(a.stamps, mslot, 2);
+        int hd = 0;
+        for (; cnt < K; ++cnt) {
+          // this lane's head: entry hd of its chunk's list (entries past K
+          // are never reached: hd < K is tested below)
+          uint32_t hv = 0u, hi = 0xFFFFFFFFu;
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j)
-        if (j < K && j == hd) {
-          hv = wv[j / 4][j % 4];
-          hi = wi[j / 4][j % 4];
+          for (int j = 0; j < KMAX; ++j)
+            if (j == hd) {
+              hv = wv[j / 4][j % 4];
+              hi = wi[j / 4][j % 4];
+            }
+          const uint32_t key = (lane < NC && hd < K && static_cast<int>(hi) >= 0) ? ord32(__uint_as_float(hv)) : 0u;
+          const uint32_t kmax = wave_reduce32(key, 0u, umax32);
+          if (kmax == 0u) break;   // every list is exhausted
+          const int wl = __ffsll(static_cast<long long>(__ballot(key == kmax))) - 1;
+          const int bi = __builtin_amdgcn_readlane(static_cast<int>(hi), wl);
+          if (lane == wl) ++hd;
+          if (lane == 0) {
+            st[f * K + cnt] = bi;
+            sx[f * K + cnt] = unord32(kmax);
+          }
         }
-      const uint64_t key = (lane < NC && hd < K && static_cast<int>(hi) >= 0)
-                               ? cand_key(__uint_as_float(hv), static_cast<int>(hi)) : 0ull;
-      const uint64_t best = wave_max_u64(key);
-      if (best == 0ull) break;   // every list is exhausted
-      if (key == best) ++hd;     // token ids are unique: one lane wins
-      const float bv = key_logit(best);
-      const int bi = key_token(best);
-      if (lane == 0) {
-        sx[f][cnt] = bv;
-        st[f][cnt] = bi;
-        sv[f][cnt] = static_cast<double>(s) + (static_cast<double>(bv) - mx) * a.inv_tau - lz;
+        if (lane < cnt) {
+          const double v = static_cast<double>(s) + (static_cast<double>(sx[f * K + lane]) - mx) * a.inv_tau - lz;
+          sv[f * K + lane] = v;
+          skey[f * K + lane] = ord64(v);   // candidate values are finite: keys above 0
+        }
       }
-      ++cnt;
     }
+    if (lane >= cnt && lane < K) {   // past the row's candidates
+      sv[f * K + lane] = -__builtin_inf();
+      skey[f * K + lane] = 0ull;
+    }
+    if (lane < K) srank[f * K + lane] = 0;
     if (lane == 0) {
-      scnt[f] = cnt;
-      sbad[f] = 0;
+      if (rbad) anybad_lds = 1;
+      if (cnt) atomicAdd(&nvalid_lds, cnt);
     }
+    if (f == 0) mark(a.stamps, mslot, 3);
   }
   __syncthreads();
+  mark(a.stamps, mslot, 4);
 
-  // Selection by rank: candidate (f, q) of slot t = f * K + q ranks by the
-  // number of candidates before it (larger value, then lower frontier index,
-  // then earlier in its row: lower token id among equal values), so every
-  // thread writes its own output slot; the rows' lists are read from LDS as
-  // broadcasts.  Rank r and r + 1 (up to the kept/dropped boundary) form the
-  // decisions tested for near ties.
-  __shared__ int byrank[kMaxKeep + 1];
-  __shared__ double cv[kMaxTree * kMaxTopK];   // slot f * K + q: candidate value, -inf past a row's list
-  int n_valid = 0;
-  bool any_bad = false;
+  // Selection by rank: candidate slot t = f * K + q ranks by the number of
+  // candidates before it (larger value, then lower frontier index, then
+  // earlier in its row: lower token id among equal values).  Rank r and
+  // r + 1 (up to the kept/dropped boundary) form the decisions tested for
+  // near ties.
   const int tot = F * K;
-  for (int t = threadIdx.x; t < tot; t += 64 * kSelWaves) {
-    const int f = t / K, q = t - f * K;
-    cv[t] = q < scnt[f] ? sv[f][q] : -__builtin_inf();
-  }
-  for (int t = threadIdx.x; t < F; t += 64 * kSelWaves) any_bad = any_bad || sbad[t] != 0;
-  __syncthreads();
+  const int t = threadIdx.x;
   {
-    for (int t0 = 0; t0 < tot; t0 += 64 * kSelWaves) {
-      const int t = t0 + threadIdx.x;
-      const double v = t < tot ? cv[t] : -__builtin_inf();
-      const bool valid = v > -__builtin_inf();   // candidate values are finite
-      n_valid += __syncthreads_count(valid);
-      if (!valid) continue;
-      const int f = t / K, q = t - f * K;
-      // slots before t in (f, q) order are exactly the indices below t
-      int rank = 0;
-#pragma unroll 8
-      for (int j = 0; j < tot; ++j) {
-        const double w = cv[j];
-        rank += (w > v || (w == v && j < t)) ? 1 : 0;
+    // wave w counts, for every candidate (lane = candidate within a block of
+    // 64), the candidates j of its share that come first
+    const int share = (tot + kSelWaves - 1) / kSelWaves;
+    const int j0 = wave * share, j1 = min(tot, j0 + share);
+    for (int c0 = 0; c0 < tot; c0 += 64) {
+      const int cidx = c0 + lane;
+      const uint64_t kc = cidx < tot ? skey[cidx] : 0ull;
+      int part = 0;
+#pragma unroll 4
+      for (int j = j0; j < j1; ++j) {
+        const uint64_t kj = skey[j];
+        part += (kj > kc || (kj == kc && j < cidx)) ? 1 : 0;
       }
-      if (rank <= M) byrank[rank] = (f << 8) | q;
-      if (rank < M) {
-        a.parent[b * M + rank] = f;
-        a.token[b * M + rank] = st[f][q];
-        a.value[b * M + rank] = static_cast<float>(v);
-      }
+      if (cidx < tot && kc != 0ull && part > 0) atomicAdd(&srank[cidx], part);
     }
   }
-  any_bad = __syncthreads_or(any_bad);
+  __syncthreads();
+  mark(a.stamps, mslot, 5);
+  for (int i = t; i < tot; i += kSel) {
+    if (skey[i] == 0ull) continue;
+    const int rank = srank[i];
+    if (rank <= M) byrank[rank] = i;
+    if (rank < M) {
+      a.parent[b * M + rank] = i / K;
+      a.token[b * M + rank] = st[i];
+      a.value[b * M + rank] = static_cast<float>(sv[i]);
+    }
+  }
+  __syncthreads();
+  const int nvalid = nvalid_lds;
   // padding past the candidates, and the near ties of adjacent ranks
-  const int t = threadIdx.x;
-  if (t >= n_valid && t < M) {
+  if (t >= nvalid && t < M) {
     a.parent[b * M + t] = -1;
     a.token[b * M + t] = -1;
     a.value[b * M + t] = kNegInf;
   }
   bool near = false;
-  if (t + 1 < n_valid && t + 1 <= M) {
+  if (t + 1 < nvalid && t + 1 <= M) {
     const int e0 = byrank[t], e1 = byrank[t + 1];
-    const int f0 = e0 >> 8, q0 = e0 & 255, f1 = e1 >> 8, q1 = e1 & 255;
-    near = sv[f0][q0] - sv[f1][q1] < kNear && !(f0 == f1 && sx[f0][q0] == sx[f1][q1]);
+    near = sv[e0] - sv[e1] < kNear && !(e0 / K == e1 / K && sx[e0] == sx[e1]);
   }
-  const int nnear = __syncthreads_count(near);
+  if (near) atomicAdd(&nnear_lds, 1);
+  __syncthreads();
   if (t == 0) {
-    a.flags[b] = any_bad ? EAGLE_FLAG_NONFINITE : 0u;
-    a.near_ties[b] = nnear;
+    a.flags[b] = anybad_lds ? EAGLE_FLAG_NONFINITE : 0u;
+    a.near_ties[b] = nnear_lds;
   }
+  mark(a.stamps, mslot, 6);
 }
 
 // Final draft tree from D chained expansion steps: the N nodes of largest
@@ -457,15 +539,27 @@ __global__ __launch_bounds__(64) void te_rerank(const RerankKernelArgs a) {
   if (lane == 0) a.rows[b] = 1 + taken;
 }
 
+template <typename TL, bool VEC>
+void launch_chunks(const ExpandKernelArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(a.B * a.F * a.NC));
+  if (a.chunk == 2048) hipLaunchKernelGGL((te_chunk<TL, 8, VEC>), grid, dim3(kThreads), 0, st, a);
+  else if (a.chunk == 4096) hipLaunchKernelGGL((te_chunk<TL, 16, VEC>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((te_chunk<TL, 32, VEC>), grid, dim3(kThreads), 0, st, a);
+}
+
 template <typename TL>
 hipError_t launch_t(const ExpandKernelArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(a.B * a.F * a.NC));
-  if (a.chunk == 2048) hipLaunchKernelGGL((te_chunk<TL, 8>), grid, dim3(kThreads), 0, st, a);
-  else if (a.chunk == 4096) hipLaunchKernelGGL((te_chunk<TL, 16>), grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL((te_chunk<TL, 32>), grid, dim3(kThreads), 0, st, a);
+  // whole 16-byte groups per row, from a 16-byte aligned base: vector loads
+  const bool vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) &&
+                   (static_cast<int64_t>(a.V) * static_cast<int64_t>(sizeof(TL))) % 16 == 0;
+  if (vec) launch_chunks<TL, true>(a, st);
+  else launch_chunks<TL, false>(a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(te_select, dim3(static_cast<unsigned>(a.B)), dim3(64 * kSelWaves), 0, st, a);
+  const dim3 sg(static_cast<unsigned>(a.B)), sb(64 * kSelWaves);
+  if (a.K <= 4) hipLaunchKernelGGL(te_select<4>, sg, sb, 0, st, a);
+  else if (a.K <= 8) hipLaunchKernelGGL(te_select<8>, sg, sb, 0, st, a);
+  else hipLaunchKernelGGL(te_select<16>, sg, sb, 0, st, a);
   return hipGetLastError();
 }
 

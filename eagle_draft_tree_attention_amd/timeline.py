@@ -19,6 +19,9 @@ import numpy as np
 ATTN_MARKS = {0: "start", 1: "parents and query rows landed", 2: "ancestor words built",
               3: "tile loop done", 4: "partial rows stored", 5: "row statistics published",
               6: "every split of its merge rows arrived", 7: "merged rows written"}
+CHUNK_MARKS = {0: "start", 1: "chunk maximum", 2: "statistics and the waves' lists", 3: "record written"}
+SEL_MARKS = {0: "start", 1: "row 0: records in", 2: "row 0: normaliser", 3: "row 0 merged", 4: "rows merged",
+             5: "ranked", 6: "outputs written"}
 ACC_MARKS = {0: "start", 1: "chunk in LDS", 2: "chunk statistics", 3: "row statistics combined",
              4: "first decision", 17: "node decided", 18: "terminal preparation starts",
              19: "terminal chunk known", 20: "walk ends here", 21: "outputs written"}
@@ -50,6 +53,8 @@ def main(argv=None):
     ap.add_argument("--calls", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=8)
+    ap.add_argument("--expand", action="store_true",
+                    help="also the expansion step (8-node frontier, top 4, 8 kept, draft rows of set 0)")
     args = ap.parse_args(argv)
 
     import torch
@@ -123,6 +128,22 @@ def main(argv=None):
         torch.cuda.synchronize()
         nwg = B * T * ((V + 8191) // 8192)
         acc_rows.append(words[: nwg * SLOTS].view(-1, SLOTS).cpu().numpy().copy())
+    exp_rows = []
+    if args.expand:
+        F, KE, ME = 8, 4, 8
+        xl = sets[0]["drf"][:, :F].contiguous()
+        fr = torch.zeros((B, F), dtype=torch.float32, device="cuda")
+        eo = None
+        for _ in range(args.warmup):
+            eo = ver.tree_expand(xl, fr, 1.0, KE, ME, outputs=eo, stream=stream)
+        chunk = 2048 if V <= 64 * 2048 else (4096 if V <= 64 * 4096 else 8192)
+        nc_e = (V + chunk - 1) // chunk
+        nslots = B * F * nc_e + B
+        for i in range(args.calls):
+            words.zero_()
+            ver.tree_expand(xl, fr, 1.0, KE, ME, outputs=eo, stream=stream)
+            torch.cuda.synchronize()
+            exp_rows.append(words[: nslots * SLOTS].view(-1, SLOTS).cpu().numpy().copy())
     ver.set_timeline(None)
     ver.close()
 
@@ -143,7 +164,7 @@ def main(argv=None):
     ends, tiles = [], []
     for w in attn_rows:
         t0 = w[:, 0][w[:, 0] > 0].min()
-        ends.append((w[:, :8].max() - t0) * tick)
+        ends.append((w[:, :12].max() - t0) * tick)
         for k in ATTN_MARKS:
             sel = w[:, k] > 0
             marks[k].extend(((w[sel, k] - t0) * tick).tolist())
@@ -194,6 +215,28 @@ def main(argv=None):
     print(f"  last mark of the launch                       {_stats(ends)}")
     print("  workgroups by residual rounds of their node: " +
           ", ".join(f"{r}: {c}" for r, c in sorted(rounds_hist.items())))
+    if exp_rows:
+        nwg = exp_rows[0].shape[0] - B
+        print(f"\n## te_chunk + te_select: {nwg} chunk workgroups ({B} sequences x 8 frontier rows x "
+              f"{nwg // (8 * B)} vocabulary chunks), then {B} selection workgroup(s); top 4, 8 kept; "
+              f"times since the first chunk workgroup started")
+        cm = {k: [] for k in CHUNK_MARKS}
+        sm = {k: [] for k in SEL_MARKS}
+        ends = []
+        for w in exp_rows:
+            t0 = w[:nwg, 0][w[:nwg, 0] > 0].min()
+            ends.append((w[:, :8].max() - t0) * tick)
+            for k in CHUNK_MARKS:
+                sel = w[:nwg, k] > 0
+                cm[k].extend(((w[:nwg][sel, k] - t0) * tick).tolist())
+            for k in SEL_MARKS:
+                sel = w[nwg:, k] > 0
+                sm[k].extend(((w[nwg:][sel, k] - t0) * tick).tolist())
+        for k, name in CHUNK_MARKS.items():
+            print(f"  te_chunk  mark {k} {name:32s} {_stats(cm[k])}")
+        for k, name in SEL_MARKS.items():
+            print(f"  te_select mark {k} {name:32s} {_stats(sm[k])}")
+        print(f"  last mark                                         {_stats(ends)}")
     return 0
 
 

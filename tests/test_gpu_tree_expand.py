@@ -73,6 +73,9 @@ CASES = [
     ("bf16_k16_keep64_f64", 1, 64, 3000, 16, 64, 1.0, "bf16"),
     ("f32_small_vocab", 3, 4, 7, 16, 20, 1.3, "f32"),
     ("bf16_one_root", 4, 1, 32000, 8, 8, 1.0, "bf16"),
+    # a 16-row frontier at V = 128256 has more chunk records per sequence than
+    # the one-launch path stages (two launches then)
+    ("bf16_wide_frontier_128k", 2, 16, 128256, 4, 16, 1.0, "bf16"),
 ]
 
 
