@@ -707,7 +707,7 @@ __global__ __launch_bounds__(256, MB > 1 ? 1 : 2) void tree_attn_mfma(const Attn
   // after another one (or in a later dispatch round) falls behind and ends
   // last.  With several tiles per workgroup, the later half of the grid
   // runs at a raised priority, which evens out the finish times.
-  if (a.late_priority && blockIdx.x >= gridDim.x / 2) __builtin_amdgcn_s_setprio(1);
+  if (a.late_priority && static_cast<int>(blockIdx.x) >= a_nwg / 2) __builtin_amdgcn_s_setprio(1);   // a_nwg = grid size
   // two stages: the stage of every LDS address is a compile-time constant
   static_assert(NST == 2, "the tile loop alternates two ring stages");
   auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
