@@ -2164,6 +2164,407 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
   stamp(a.stamps, 21);   // outputs written
 }
 
+// ------------------------------------------------------ node-parallel path
+// For V <= kNodeVocab a node's whole target and draft rows fit one
+// 512-thread workgroup (64 tokens per thread and row, their exponentials
+// kept in registers: two waves per SIMD with 256 registers each), so one
+// workgroup decides the node
+// with block-level reductions only: the statistics, the first test, the
+// residual rounds and the sample the walk emits if it ends at the node (the
+// bonus token at a leaf).  Every node's outcome depends only on its own rows,
+// its children's tokens and its own uniforms, so the workgroups never wait
+// for each other: no residency requirement, and a large batch is one launch.
+// sa_walk then follows the decisions from each root.
+constexpr int kNodeThreads = 512;
+constexpr int kNodeWaves = kNodeThreads / 64;
+constexpr int kNodePer = kNodeVocab / kNodeThreads;   // tokens per thread and row
+static_assert(kNodePer == 64, "64 tokens per thread and row");
+
+struct NodeOut {        // one per (sequence, node), in the handle's NodeState slots
+  int32_t kind;         // kNodeLeaf / kNodeAccepted / kNodeRejected; -1 for a padding row
+  int32_t outcome;      // the accepted child, else -1
+  int32_t final_tok;    // the token emitted if the walk ends here
+  uint32_t flags;       // P_ZERO / DEGENERATE_RESIDUAL of the node's tests and sample; NONFINITE: an unusable row
+  int32_t near_visit;   // near ties counted when the walk reaches the node (filter boundaries, tests)
+  int32_t near_end;     // near tie of the node's sample (counted when the walk ends here)
+};
+static_assert(sizeof(NodeOut) <= sizeof(NodeState), "node outputs live in the NodeState slots");
+
+struct NodeShared {
+  int32_t kid[kMaxTree];   // children in ascending index
+  int32_t ktok[kMaxTree];
+  double qt[kMaxTree], pt[kMaxTree], r[kMaxTree];
+  int32_t nkids, nreal;
+  double dscr[kNodeWaves];
+  double cscan[kNodeVocab / kNodeThreads / 4][kNodeWaves];   // per group column (at most 16) and wave: weight totals
+  float fscr[kNodeWaves];
+  int32_t iscr[kNodeWaves];
+  int32_t res;
+  double sample[2];
+  int32_t hit;
+};
+
+// reduction over the workgroup (all threads call; the result in every thread)
+template <typename T, typename Op>
+__device__ T node_reduce(T v, Op op, T* scratch /* >= kNodeWaves */) {
+  v = wave_reduce(v, op);
+  __syncthreads();   // the previous use of scratch is over
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = v;
+  __syncthreads();
+  T r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < kNodeWaves; ++i) r = op(r, scratch[i]);
+  return r;
+}
+
+// This thread's kNodePer logits in the strided group view: word jj holds the
+// G consecutive tokens of group g = jj * kNodeThreads + tid, i.e. tokens
+// g G .. g G + G - 1 (token order is group order, and the lanes of a wave
+// read consecutive 16-byte groups); -inf past the row.  VEC: the row starts
+// on a 16-byte boundary and holds whole 16-byte groups.
+template <typename TL>
+__device__ __forceinline__ int node_token(int jj, int e) {
+  return (jj * kNodeThreads + static_cast<int>(threadIdx.x)) * Pack<TL>::G + e;
+}
+template <typename TL, bool VEC>
+__device__ __forceinline__ void node_load(const TL* row, int V, u32x4_t (&w)[kNodePer / Pack<TL>::G]) {
+  constexpr int G = Pack<TL>::G;
+  const uint32_t ni = Pack<TL>::neg_inf_word();
+#pragma unroll
+  for (int jj = 0; jj < kNodePer / G; ++jj) {
+    const int t0 = node_token<TL>(jj, 0);
+    if constexpr (VEC) {
+      w[jj] = t0 < V ? *reinterpret_cast<const u32x4_t*>(row + t0) : u32x4_t{ni, ni, ni, ni};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(TL) == 2) {
+          const int t = t0 + 2 * i;
+          const uint32_t lo = t < V ? static_cast<uint32_t>(row[t]) : (ni & 0xFFFFu);
+          const uint32_t hi = t + 1 < V ? (static_cast<uint32_t>(row[t + 1]) << 16) : (ni & 0xFFFF0000u);
+          w[jj][i] = lo | hi;
+        } else {
+          const int t = t0 + i;
+          w[jj][i] = t < V ? __float_as_uint(row[t]) : ni;
+        }
+      }
+    }
+  }
+}
+
+template <typename TL, bool VEC>
+__global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a) {
+  __shared__ NodeShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, V = a.V;
+  const int b = blockIdx.x / T, n = blockIdx.x - b * T;
+  NodeOut* const out = reinterpret_cast<NodeOut*>(a.nodes) + static_cast<int64_t>(b) * T + n;
+  const bool greedy = a.tau == 0.f;
+
+  // the tree (wave 0, lane = row): this node's children in ascending index
+  if (wave == 0) {
+    const int par = lane < T ? a.parents[b * T + lane] : -1;
+    const int tok = lane < T ? a.tokens[b * T + lane] : -1;
+    const uint64_t padm = __ballot(lane >= 1 && lane < T && tok == -1);
+    const int nreal = padm ? __ffsll(static_cast<long long>(padm)) - 1 : T;
+    const bool is_child = lane > n && lane < nreal && par == n;
+    const uint64_t km = __ballot(is_child);
+    if (is_child) {
+      const int ord = __popcll(km & ((1ull << lane) - 1ull));
+      sh.kid[ord] = lane;
+      sh.ktok[ord] = tok;
+    }
+    if (lane == 0) {
+      sh.nkids = __popcll(km);
+      sh.nreal = nreal;
+    }
+  }
+  __syncthreads();
+  if (n >= sh.nreal) {   // a padding row: never read, never on a walk
+    if (tid == 0) *out = NodeOut{-1, -1, -1, 0u, 0, 0};
+    return;
+  }
+  const int nkids = sh.nkids;
+  const bool two = nkids > 0 && !greedy;
+  const int64_t rowoff = static_cast<int64_t>(b * T + n) * V;
+  const TL* const trow = reinterpret_cast<const TL*>(a.target) + rowoff;
+  const TL* const drow = reinterpret_cast<const TL*>(a.draft) + rowoff;
+  const int v0 = kNodePer * tid;
+
+  constexpr int G = Pack<TL>::G, NV = kNodePer / G;
+  // both rows requested at once, except fp32 rows (64 registers each): the
+  // draft row there once the target row's exponentials exist
+  constexpr bool kLateDraft = sizeof(TL) == 4;
+  u32x4_t wq[NV], wd[NV];
+  node_load<TL, VEC>(trow, V, wq);
+  if (two && !kLateDraft) node_load<TL, VEC>(drow, V, wd);
+  if (a.thr) cut_groups<TL, NV>(wq, thr_of(a, b, n, 0));   // filtered: logits below the threshold count as -inf
+  const float mq = node_reduce(local_max<TL, NV>(wq), MaxOp{}, sh.fscr);
+  const bool tbad = mq == __builtin_inff() || mq == kNegInf;
+
+  if (greedy) {   // the target argmax (lowest id), matched against the children's tokens
+    if (tbad) {   // an unusable row poisons the sequence (the walk reports it)
+      if (tid == 0) *out = NodeOut{kNodeRejected, -1, -1, static_cast<uint32_t>(EAGLE_FLAG_NONFINITE), 0, 0};
+      return;
+    }
+    int la = 0x7FFFFFFF;
+#pragma unroll
+    for (int jj = NV - 1; jj >= 0; --jj) {
+      float f[G];
+      Pack<TL>::unpack(wq[jj], f);
+#pragma unroll
+      for (int e = G - 1; e >= 0; --e)
+        if (f[e] == mq) la = node_token<TL>(jj, e);
+    }
+    const int am = node_reduce(la, MinI{}, sh.iscr);
+    if (tid == 0) {
+      int acc = -1;
+      for (int i = 0; i < nkids; ++i)
+        if (sh.ktok[i] == am) {
+          acc = sh.kid[i];
+          break;
+        }
+      *out = NodeOut{acc >= 0 ? kNodeAccepted : (nkids ? kNodeRejected : kNodeLeaf), acc, am, 0u, 0, 0};
+    }
+    return;
+  }
+
+  // each row's exponentials 2^((x - m) c2), kept in registers (token
+  // node_token(jj, e) at index jj G + e; sums in fp64), the target row first, so that a row's logits
+  // die before the next row's exponentials are made; the exponentials unpack
+  // the words again rather than keeping unpacked logits live across the
+  // reduction
+  float xq[kNodePer], xp[kNodePer];
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) asm volatile("" : "+v"(wq[jj]));
+  double zq = local_expsum_keep<TL, NV>(wq, mq, a.c2, xq);
+  float mp = 0.f;
+  double zp = 0.0;
+  if (two) {
+    if (kLateDraft) node_load<TL, VEC>(drow, V, wd);
+    if (a.thr) cut_groups<TL, NV>(wd, thr_of(a, b, n, 1));
+    mp = node_reduce(local_max<TL, NV>(wd), MaxOp{}, sh.fscr);
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) asm volatile("" : "+v"(wd[jj]));
+    zp = local_expsum_keep<TL, NV>(wd, mp, a.c2, xp);
+  }
+  if (tbad || (two && (mp == __builtin_inff() || mp == kNegInf))) {   // an unusable row (the walk reports it)
+    if (tid == 0) *out = NodeOut{kNodeRejected, -1, -1, static_cast<uint32_t>(EAGLE_FLAG_NONFINITE), 0, 0};
+    return;
+  }
+
+  zq = node_reduce(zq, AddD{}, sh.dscr);
+  if (two) zp = node_reduce(zp, AddD{}, sh.dscr);
+  const double fq = 1.0 / zq, fp = two ? 1.0 / zp : 0.0;
+
+  uint32_t fl = 0;
+  int32_t nr = filter_near(a, b, n, nkids > 0);
+  int kind = kNodeLeaf, outcome = -1;
+  double C = 0.0;
+  if (nkids > 0) {
+    // q(t), p(t) and the uniform of every test, one child per lane
+    if (tid < nkids) {
+      const int tok = sh.ktok[tid];
+      double qt = 0.0, pt = 0.0;
+      if (tok >= 0 && tok < V) {
+        qt = exp((static_cast<double>(cut(logit<TL>(trow, tok), thr_of(a, b, n, 0))) - mq) * a.inv_tau) / zq;
+        pt = exp((static_cast<double>(cut(logit<TL>(drow, tok), thr_of(a, b, n, 1))) - mp) * a.inv_tau) / zp;
+      }
+      sh.qt[tid] = qt;
+      sh.pt[tid] = pt;
+      sh.r[tid] = decision_uniform(a, b, n, static_cast<uint32_t>(tid));
+    }
+    // children in order under the residual max(0, q - C p) / s
+    double s = 1.0;
+    kind = kNodeRejected;
+    for (int i = 0; i < nkids; ++i) {
+      __syncthreads();
+      if (tid == 0) sh.res = decide_pre(sh.qt[i], sh.pt[i], sh.r[i], sh.ktok[i], V, C, s, fl, nr);
+      __syncthreads();
+      const int res = sh.res;
+      if (res > 0) {
+        kind = kNodeAccepted;
+        outcome = sh.kid[i];
+        break;
+      }
+      if (res < 0) break;   // a token outside the vocabulary (the walk reports it)
+      C += s;
+      // the residual mass after this rejection (after the last one it is
+      // the sample's distribution)
+      const double part = kept_masses(xq, xp, static_cast<float>(C * fp / fq), fq);
+      s = node_reduce(part, AddD{}, sh.dscr);
+      if (!(s > 0.0)) {   // nothing left: the residual starts over from q
+        fl |= EAGLE_FLAG_DEGENERATE_RESIDUAL;
+        C = 0.0;
+        s = 1.0;
+      }
+    }
+  }
+  int final_tok = -1, near_end = 0;
+  if (kind != kNodeAccepted) {
+    // The sample: the smallest token whose running sum of the weights
+    // exceeds u * S.  Weights in units of 1/fq (no common factor changes the
+    // comparison): max(0, e_q - K e_p), e_q at a leaf (no draft row, K = 0).
+    // In token order: per-group sums (a thread's word jj is group
+    // jj * kNodeThreads + tid), one block scan per group column, the first
+    // group reaching u * S by a block minimum, then that group's G tokens in
+    // order by the thread that holds it.
+    if (kind == kNodeLeaf) {
+#pragma unroll
+      for (int j = 0; j < kNodePer; ++j) xp[j] = 0.f;
+    }
+    const float K = kind == kNodeLeaf ? 0.f : static_cast<float>(C * fp / fq);
+    auto weight = [&](int j) __attribute__((always_inline)) -> double {
+      return static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, xp[j], xq[j])));
+    };
+    double gw[NV], goff[NV];
+    int lastpos = -1;   // this thread's last token with positive weight
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      double g = 0.0;
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        const double w = weight(jj * G + e);
+        g += w;
+        if (w > 0.0) lastpos = max(lastpos, node_token<TL>(jj, e));
+      }
+      gw[jj] = g;
+      __builtin_amdgcn_sched_barrier(0);   // one group's weights in flight at a time
+    }
+    // the crossing group's scan recomputes its weights (same arithmetic,
+    // same values) instead of keeping them live across the reductions
+#pragma unroll
+    for (int j = 0; j < kNodePer; ++j) asm volatile("" : "+v"(xq[j]), "+v"(xp[j]));
+    // per-column exclusive offsets of this thread's groups, column totals
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      const double incl = wave_scan_add(gw[jj]);
+      goff[jj] = incl - gw[jj];
+      if (lane == 63) sh.cscan[jj][wave] = incl;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    double base = 0.0;
+#pragma unroll
+    for (int jj = 0; jj < NV; ++jj) {
+      double off = base, tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < kNodeWaves; ++w) {
+        if (w < wave) off += sh.cscan[jj][w];
+        tot += sh.cscan[jj][w];
+      }
+      goff[jj] += off;
+      base += tot;
+    }
+    const double S = base;
+    const double thr = decision_uniform(a, b, n, kSampleSlot) * S;
+    // the first group (in token order) whose range reaches past u * S
+    int gfirst = 0x7FFFFFFF;
+#pragma unroll
+    for (int jj = NV - 1; jj >= 0; --jj)
+      if (goff[jj] + gw[jj] > thr) gfirst = jj * kNodeThreads + tid;
+    const int gstar = node_reduce(gfirst, MinI{}, sh.iscr);
+    if (gstar != 0x7FFFFFFF && gfirst == gstar) {
+      const int js = gstar / kNodeThreads;
+      int v = -1, lastg = -1;
+      double lo = 0.0, hi = 0.0;
+#pragma unroll
+      for (int jj = 0; jj < NV; ++jj) {
+        if (jj != js) continue;
+        hi = goff[jj];
+        lo = hi;
+#pragma unroll
+        for (int e = 0; e < G; ++e) {
+          const double w = weight(jj * G + e);
+          if (w > 0.0) {
+            lastg = node_token<TL>(jj, e);
+            if (v < 0) {
+              lo = hi;
+              hi += w;
+              if (hi > thr) v = lastg;
+            }
+          }
+        }
+      }
+      if (v < 0) {   // rounding hid the crossing inside this group: its last positive weight
+        v = lastg;
+        lo = hi = thr;
+      }
+      sh.hit = v;
+      sh.sample[0] = ((hi - thr) < kNearTie * S || (thr - lo) < kNearTie * S) ? 1.0 : 0.0;
+    }
+    if (gstar == 0x7FFFFFFF) {   // no crossing at all: the last token with positive weight
+      const int lm = node_reduce(lastpos, [](int x, int y) { return x > y ? x : y; }, sh.iscr);
+      if (tid == 0) {
+        sh.hit = lm;
+        sh.sample[0] = 0.0;
+      }
+    }
+    __syncthreads();
+    final_tok = sh.hit;
+    near_end = sh.sample[0] > 0.0 ? 1 : 0;
+  }
+  if (tid == 0) *out = NodeOut{kind, outcome, final_tok, fl, nr, near_end};
+}
+
+// One wave per sequence: validation, then the walk over the decided nodes.
+__global__ __launch_bounds__(64) void sa_walk(const AcceptKernelArgs a) {
+  __shared__ NodeOut no[kMaxTree];
+  __shared__ int32_t path[kMaxTree];
+  const int lane = threadIdx.x, b = blockIdx.x, T = a.T, V = a.V;
+  const int par = lane < T ? a.parents[b * T + lane] : -1;
+  const int tok = lane < T ? a.tokens[b * T + lane] : -1;
+  const bool tree_bad = __any(lane < T && (lane == 0 ? par != -1 : (par < 0 || par >= lane)));
+  const uint64_t padm = __ballot(lane >= 1 && lane < T && tok == -1);
+  const int nreal = padm ? __ffsll(static_cast<long long>(padm)) - 1 : T;
+  const bool pad_bad = __any(lane >= nreal && lane < T && tok != -1);   // padding must be a suffix
+  const bool tok_bad = __any(lane >= 1 && lane < nreal && (tok < 0 || tok >= V));
+  if (lane < nreal) no[lane] = reinterpret_cast<const NodeOut*>(a.nodes)[static_cast<int64_t>(b) * T + lane];
+  const bool nonfinite = __any(lane < nreal && (no[lane].flags & EAGLE_FLAG_NONFINITE));
+  uint32_t bad = 0;
+  if (tree_bad || pad_bad) bad = EAGLE_FLAG_BAD_TREE;
+  else bad = (tok_bad ? EAGLE_FLAG_BAD_TOKEN : 0u) | (nonfinite ? EAGLE_FLAG_NONFINITE : 0u);
+  if (bad) {
+    if (lane == 0) {
+      a.accept_len[b] = -1;
+      a.flags[b] = bad;
+      a.near_ties[b] = 0;
+    }
+    for (int j = lane; j < T; j += 64) {
+      a.accepted_nodes[b * T + j] = -1;
+      a.out_tokens[b * T + j] = -1;
+    }
+    return;
+  }
+  __shared__ int32_t walk_len, walk_final;
+  if (lane == 0) {
+    int cur = 0, len = 0, near = 0;
+    uint32_t fl = 0;
+    for (;;) {
+      const NodeOut o = no[cur];
+      fl |= o.flags;
+      near += o.near_visit;
+      if (o.kind != kNodeAccepted) {
+        near += o.near_end;
+        walk_final = o.final_tok;
+        break;
+      }
+      path[len++] = o.outcome;
+      cur = o.outcome;
+    }
+    walk_len = len;
+    a.accept_len[b] = len;
+    a.flags[b] = fl;
+    a.near_ties[b] = near;
+  }
+  __syncthreads();
+  const int len = walk_len;
+  for (int j = lane; j < T; j += 64) {
+    a.accepted_nodes[b * T + j] = j < len ? path[j] : -1;
+    a.out_tokens[b * T + j] = j < len ? a.tokens[b * T + path[j]] : (j == len ? walk_final : -1);
+  }
+}
+
 // The fused kernel's workgroups wait for each other: launched cooperatively,
 // the runtime either makes all of them resident at once or refuses the
 // launch (hipErrorCooperativeLaunchTooLarge, nothing enqueued; the caller
@@ -2177,6 +2578,15 @@ hipError_t launch_fused(const void* fn, dim3 grid, dim3 block, const AcceptKerne
 template <typename TL>
 hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
   const dim3 block(kThreads);
+  if (a.fused == 2) {   // node-parallel path (V <= kNodeVocab, siblings with replacement)
+    const dim3 grid(static_cast<unsigned>(a.B * a.T));
+    if (a.vec_ok) hipLaunchKernelGGL((sa_node<TL, true>), grid, dim3(kNodeThreads), 0, st, a);
+    else hipLaunchKernelGGL((sa_node<TL, false>), grid, dim3(kNodeThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sa_walk, dim3(static_cast<unsigned>(a.B)), dim3(64), 0, st, a);
+    return hipGetLastError();
+  }
   if (a.fused) {
     const dim3 grid(static_cast<unsigned>(a.B * a.T * a.NC));
     const void* fn = a.wr ? (a.vec_ok ? reinterpret_cast<const void*>(&sa_fused<TL, true, true>)

@@ -200,6 +200,21 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
   }
   const int64_t per_seq = static_cast<int64_t>(k.T) * k.NC;
   k.wr = (a->without_replacement && a->temperature > 0.f) ? 1 : 0;
+  // Small vocabularies: one workgroup per node holds both rows whole, so the
+  // nodes never wait for each other and a batch of any size is one launch
+  // (then one wave per sequence walks the decisions).  A node then runs on
+  // one CU instead of ceil(V / 8192), so it pays where the fused kernel
+  // would need slices: batches beyond its co-resident capacity.
+  // EAGLE_VERIFY_NODE_PARALLEL=1 / 0 forces it on / off.
+  const char* npv = std::getenv("EAGLE_VERIFY_NODE_PARALLEL");
+  const bool np_auto = static_cast<int64_t>(k.B) * per_seq > cap;
+  const bool np = npv && (npv[0] == '0' || npv[0] == '1') ? npv[0] == '1' : np_auto;
+  if (V <= kNodeVocab && !k.wr && np) {
+    k.fused = 2;
+    const int e = launch_spec_accept(k, bf16, hip_stream);
+    if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
+    return EAGLE_OK;
+  }
   if (per_seq > cap || k.NC > 64) {
     k.fused = 0;
     k.wr_kept = ws.wr_kept;

@@ -15,6 +15,7 @@ constexpr int kMaxTree = EAGLE_MAX_TREE_ROWS;
 constexpr int kTileKeys = 64;        // keys per attention tile (one LDS stage)
 constexpr int kStampSlots = 32;      // timeline words per workgroup (diagnostic)
 constexpr int kVocabChunk = 8192;    // vocabulary elements per acceptance workgroup
+constexpr int kNodeVocab = 32768;    // largest vocabulary of the node-parallel acceptance (one workgroup per node)
 constexpr int kDefaultCUs = 256;     // MI355X compute units (planning without a device)
 constexpr int64_t kAttnPartFloats = 32ll << 20;   // 128 MiB of split partials
 // (row, split) pairs whose merge weights fit in the smallest (D = 64) MFMA
@@ -132,7 +133,7 @@ struct AcceptKernelArgs {
   int node_priority;      // fused path: internal nodes' waves at a raised priority
   int leaf_wait;          // fused path, sampled, whole 16-byte groups, siblings with replacement:
                           // s_sleep(10) steps a leaf waits before requesting its rows (0: none)
-  int fused;              // 1: one co-resident kernel; 0: three-kernel path
+  int fused;              // 2: node-parallel kernels; 1: one co-resident kernel; 0: three-kernel path
   int coop;               // host side: launch the fused kernel cooperatively
   int b0;                 // batch index of sequence 0 of this launch (a slice of the call's batch)
   int wr;                 // 1: siblings were drawn without replacement

@@ -22,6 +22,16 @@ pytestmark = pytest.mark.gpu
 
 SEED = 0x5EED0000
 
+
+@pytest.fixture(params=["node_parallel", "fused"])
+def accept_path(request, monkeypatch):
+    """Vocabularies up to 32768 go to the node-parallel kernels when the
+    batch exceeds the fused kernel's co-resident capacity;
+    EAGLE_VERIFY_NODE_PARALLEL=1 / 0 (read per call) forces either path, so
+    both are checked on the same cases."""
+    monkeypatch.setenv("EAGLE_VERIFY_NODE_PARALLEL", "1" if request.param == "node_parallel" else "0")
+    return request.param
+
 CASES = [
     small_spec("bf16_t1", B=8, V=1000, levels=(4, 6, 10)),
     small_spec("bf16_t07_unaligned_rows", B=4, V=5003, levels=(10, 10, 10), temperature=0.7),
@@ -45,7 +55,7 @@ def _oracle(inp, temperature, offset, **over):
 
 
 @pytest.mark.parametrize("spec", CASES, ids=lambda s: s.name)
-def test_accept_matches_oracle(spec):
+def test_accept_matches_oracle(spec, accept_path):
     log(f"[accept] {spec.name}")
     inp = synth.make_inputs(spec, with_kv=False)
     ver = make_verifier(spec, inp.T)
@@ -85,7 +95,7 @@ def _custom(B, T, V, dtype="f32"):
     return small_spec("custom", dtype=dtype, B=B, V=V, tree=("chain", T - 1))
 
 
-def test_edge_cases_flags_and_poison():
+def test_edge_cases_flags_and_poison(accept_path):
     import eagle_draft_tree_attention_amd as ev
     log("[accept] edge cases")
     B, T, V = 8, 4, 64
@@ -118,7 +128,7 @@ def test_edge_cases_flags_and_poison():
 
 
 @pytest.mark.parametrize("V", [3, 16])   # per-token loads, and whole 16-byte groups
-def test_p_zero_and_degenerate_residual(V):
+def test_p_zero_and_degenerate_residual(V, accept_path):
     import eagle_draft_tree_attention_amd as ev
     log(f"[accept] p = 0 and zero residual, V={V}")
     spec = _custom(2, 3, V)
@@ -141,7 +151,7 @@ def test_p_zero_and_degenerate_residual(V):
     ver.close()
 
 
-def test_root_only_tree_draws_bonus_from_target():
+def test_root_only_tree_draws_bonus_from_target(accept_path):
     log("[accept] T = 1")
     V, B = 7, 64
     spec = small_spec("root_only", dtype="f32", B=B, V=V, tree=("chain", 0))
@@ -193,7 +203,7 @@ def test_lossless_statistics_over_offsets():
     ver.close()
 
 
-def test_chain_closed_form_on_gpu():
+def test_chain_closed_form_on_gpu(accept_path):
     """E[emitted] = (1 - a^(N+1)) / (1 - a) for a chain with acceptance rate a."""
     log("[accept] chain closed form")
     N, B, K, alpha = 5, 256, 16, 0.8
@@ -216,10 +226,11 @@ def test_chain_closed_form_on_gpu():
     ver.close()
 
 
-def test_large_batch_in_fused_slices():
+def test_large_batch_in_fused_slices(monkeypatch):
     """B*T*chunks beyond what the fused kernel can keep co-resident: the
     batch is verified in slices of whole sequences (the uniforms keep the
     sequence's index in the whole batch)."""
+    monkeypatch.setenv("EAGLE_VERIFY_NODE_PARALLEL", "0")
     spec = small_spec("large_batch", B=40, V=32000, levels=(10,) * 6, sigma_d=1.2)
     log(f"[accept] {spec.name}")
     inp = synth.make_inputs(spec, with_kv=False)
@@ -233,7 +244,23 @@ def test_large_batch_in_fused_slices():
     ver.close()
 
 
-def test_mixed_invalid_inputs_report_every_flag():
+def test_large_batch_in_one_node_parallel_launch():
+    """The same 40-sequence batch on the node-parallel kernels: one workgroup
+    per node, no residency requirement, so no slices."""
+    spec = small_spec("large_batch_np", B=40, V=32000, levels=(10,) * 6, sigma_d=1.2)
+    log(f"[accept] {spec.name}")
+    inp = synth.make_inputs(spec, with_kv=False)
+    ver = make_verifier(spec, inp.T)
+    diverged = 0
+    for off in range(2):
+        got = run_accept(ver, inp, 1.0, SEED, off)
+        ref = _oracle(inp, 1.0, off)
+        diverged += compare_accept(got, ref, f"large batch offset {off}", inp.parents, inp.tokens, spec.vocab)
+    assert diverged <= excused_bound(2 * spec.batch)
+    ver.close()
+
+
+def test_mixed_invalid_inputs_report_every_flag(accept_path):
     import eagle_draft_tree_attention_amd as ev
     log("[accept] bad token together with an unusable row")
     B, T, V = 2, 4, 64
@@ -269,7 +296,7 @@ def _pad(spec, inp, sizes):
 
 
 @pytest.mark.parametrize("temp", [1.0, 0.0])
-def test_trees_of_different_sizes_in_one_batch(temp):
+def test_trees_of_different_sizes_in_one_batch(temp, accept_path):
     spec = small_spec("padded", B=6, V=3000, levels=(10, 10, 10))
     log(f"[accept] trees of different sizes, temperature {temp}")
     inp = synth.make_inputs(spec, with_kv=False)

@@ -27,6 +27,9 @@ def test_acceptance_waits_that_give_up(monkeypatch):
     spec = small_spec("waits_accept", B=8, V=20000, levels=(10, 10, 10))
     inp = synth.make_inputs(spec, with_kv=False)
     monkeypatch.setenv("EAGLE_VERIFY_SPIN_LIMIT", "0")
+    # the fused kernel's waits (the node-parallel kernels, which never wait,
+    # are kept out)
+    monkeypatch.setenv("EAGLE_VERIFY_NODE_PARALLEL", "0")
     ver = make_verifier(spec, inp.T)
     B, T = inp.parents.shape
     internal = 0
