@@ -2168,13 +2168,13 @@ __global__ __launch_bounds__(kThreads, 4) void sa_fused(const AcceptKernelArgs a
 // For V <= kNodeVocab a node's whole target and draft rows fit one
 // 512-thread workgroup (64 tokens per thread and row, their exponentials
 // kept in registers: two waves per SIMD with 256 registers each), so one
-// workgroup decides the node
-// with block-level reductions only: the statistics, the first test, the
-// residual rounds and the sample the walk emits if it ends at the node (the
-// bonus token at a leaf).  Every node's outcome depends only on its own rows,
-// its children's tokens and its own uniforms, so the workgroups never wait
-// for each other: no residency requirement, and a large batch is one launch.
-// sa_walk then follows the decisions from each root.
+// workgroup decides the node with block-level reductions only: the
+// statistics, the tests in order and the residual rounds.  Every node's
+// decisions depend only on its own rows, its children's tokens and its own
+// uniforms, so the workgroups never wait for each other: no residency
+// requirement, and a large batch is one launch.  sa_finish then walks each
+// sequence's decisions and draws the one sample the walk needs, at the node
+// where it ends, from that node's rows.
 constexpr int kNodeThreads = 512;
 constexpr int kNodeWaves = kNodeThreads / 64;
 constexpr int kNodePer = kNodeVocab / kNodeThreads;   // tokens per thread and row
@@ -2183,10 +2183,11 @@ static_assert(kNodePer == 64, "64 tokens per thread and row");
 struct NodeOut {        // one per (sequence, node), in the handle's NodeState slots
   int32_t kind;         // kNodeLeaf / kNodeAccepted / kNodeRejected; -1 for a padding row
   int32_t outcome;      // the accepted child, else -1
-  int32_t final_tok;    // the token emitted if the walk ends here
-  uint32_t flags;       // P_ZERO / DEGENERATE_RESIDUAL of the node's tests and sample; NONFINITE: an unusable row
+  int32_t argmax;       // greedy mode: the target argmax (the emitted token if the walk ends here)
+  uint32_t flags;       // P_ZERO / DEGENERATE_RESIDUAL of the node's tests; NONFINITE: an unusable row
   int32_t near_visit;   // near ties counted when the walk reaches the node (filter boundaries, tests)
-  int32_t near_end;     // near tie of the node's sample (counted when the walk ends here)
+  float K;              // the sample's weights are max(0, e_q - K e_p), e = 2^((x - m) c2) (K = 0 at a leaf)
+  float mq, mp;         // row maxima
 };
 static_assert(sizeof(NodeOut) <= sizeof(NodeState), "node outputs live in the NodeState slots");
 
@@ -2195,13 +2196,10 @@ struct NodeShared {
   int32_t ktok[kMaxTree];
   double qt[kMaxTree], pt[kMaxTree], r[kMaxTree];
   int32_t nkids, nreal;
-  double dscr[kNodeWaves];
-  double cscan[kNodeVocab / kNodeThreads / 4][kNodeWaves];   // per group column (at most 16) and wave: weight totals
-  float fscr[kNodeWaves];
+  double dscr[2 * kNodeWaves];
+  float fscr[2 * kNodeWaves];
   int32_t iscr[kNodeWaves];
   int32_t res;
-  double sample[2];
-  int32_t hit;
 };
 
 // reduction over the workgroup (all threads call; the result in every thread)
@@ -2217,6 +2215,32 @@ __device__ T node_reduce(T v, Op op, T* scratch /* >= kNodeWaves */) {
   return r;
 }
 
+// the same for two values at once (scratch >= 2 kNodeWaves)
+template <typename T, typename Op>
+__device__ void node_reduce2(T& x, T& y, Op op, T* scratch) {
+  x = wave_reduce(x, op);
+  y = wave_reduce(y, op);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    scratch[threadIdx.x >> 6] = x;
+    scratch[kNodeWaves + (threadIdx.x >> 6)] = y;
+  }
+  __syncthreads();
+  x = scratch[0];
+  y = scratch[kNodeWaves];
+#pragma unroll
+  for (int i = 1; i < kNodeWaves; ++i) {
+    x = op(x, scratch[i]);
+    y = op(y, scratch[kNodeWaves + i]);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void words_opaque(u32x4_t (&w)[NV]) {
+#pragma unroll
+  for (int jj = 0; jj < NV; ++jj) asm volatile("" : "+v"(w[jj]));
+}
+
 // This thread's kNodePer logits in the strided group view: word jj holds the
 // G consecutive tokens of group g = jj * kNodeThreads + tid, i.e. tokens
 // g G .. g G + G - 1 (token order is group order, and the lanes of a wave
@@ -2228,24 +2252,40 @@ __device__ __forceinline__ int node_token(int jj, int e) {
 }
 template <typename TL, bool VEC>
 __device__ __forceinline__ void node_load(const TL* row, int V, u32x4_t (&w)[kNodePer / Pack<TL>::G]) {
+  // aligned rows: every load is issued (from the row's start when past its
+  // end) and -inf selected afterwards, with no branch between the loads, so
+  // that all of them are in flight at once.  Unaligned rows (rare): words
+  // inside the row for every thread load without a select (fewer address
+  // registers), the last ones element by element.
   constexpr int G = Pack<TL>::G;
   const uint32_t ni = Pack<TL>::neg_inf_word();
 #pragma unroll
   for (int jj = 0; jj < kNodePer / G; ++jj) {
     const int t0 = node_token<TL>(jj, 0);
     if constexpr (VEC) {
-      w[jj] = t0 < V ? *reinterpret_cast<const u32x4_t*>(row + t0) : u32x4_t{ni, ni, ni, ni};
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(row + (t0 < V ? t0 : 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[jj][i] = t0 < V ? x[i] : ni;
+    } else if ((jj + 1) * kNodeThreads * G <= V) {   // (uniform) inside the row for every thread
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (sizeof(TL) == 2)
+          w[jj][i] = static_cast<uint32_t>(row[t0 + 2 * i]) | (static_cast<uint32_t>(row[t0 + 2 * i + 1]) << 16);
+        else
+          w[jj][i] = __float_as_uint(row[t0 + i]);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (sizeof(TL) == 2) {
           const int t = t0 + 2 * i;
-          const uint32_t lo = t < V ? static_cast<uint32_t>(row[t]) : (ni & 0xFFFFu);
-          const uint32_t hi = t + 1 < V ? (static_cast<uint32_t>(row[t + 1]) << 16) : (ni & 0xFFFF0000u);
-          w[jj][i] = lo | hi;
+          const uint32_t lo = static_cast<uint32_t>(row[t < V ? t : 0]);
+          const uint32_t hi = static_cast<uint32_t>(row[t + 1 < V ? t + 1 : 0]) << 16;
+          w[jj][i] = (t < V ? lo : (ni & 0xFFFFu)) | (t + 1 < V ? hi : (ni & 0xFFFF0000u));
         } else {
           const int t = t0 + i;
-          w[jj][i] = t < V ? __float_as_uint(row[t]) : ni;
+          const uint32_t x = __float_as_uint(row[t < V ? t : 0]);
+          w[jj][i] = t < V ? x : ni;
         }
       }
     }
@@ -2260,6 +2300,8 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
   const int b = blockIdx.x / T, n = blockIdx.x - b * T;
   NodeOut* const out = reinterpret_cast<NodeOut*>(a.nodes) + static_cast<int64_t>(b) * T + n;
   const bool greedy = a.tau == 0.f;
+  stamp(a.stamps, 0);
+  stamp_value(a.stamps, 29, a.stamps ? placement() : 0);
 
   // the tree (wave 0, lane = row): this node's children in ascending index
   if (wave == 0) {
@@ -2281,7 +2323,7 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
   }
   __syncthreads();
   if (n >= sh.nreal) {   // a padding row: never read, never on a walk
-    if (tid == 0) *out = NodeOut{-1, -1, -1, 0u, 0, 0};
+    if (tid == 0) *out = NodeOut{-1, -1, -1, 0u, 0, 0.f, 0.f, 0.f};
     return;
   }
   const int nkids = sh.nkids;
@@ -2289,22 +2331,21 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
   const int64_t rowoff = static_cast<int64_t>(b * T + n) * V;
   const TL* const trow = reinterpret_cast<const TL*>(a.target) + rowoff;
   const TL* const drow = reinterpret_cast<const TL*>(a.draft) + rowoff;
-  const int v0 = kNodePer * tid;
 
-  constexpr int G = Pack<TL>::G, NV = kNodePer / G;
   // both rows requested at once, except fp32 rows (64 registers each): the
   // draft row there once the target row's exponentials exist
+  constexpr int G = Pack<TL>::G, NV = kNodePer / G;
   constexpr bool kLateDraft = sizeof(TL) == 4;
   u32x4_t wq[NV], wd[NV];
   node_load<TL, VEC>(trow, V, wq);
   if (two && !kLateDraft) node_load<TL, VEC>(drow, V, wd);
   if (a.thr) cut_groups<TL, NV>(wq, thr_of(a, b, n, 0));   // filtered: logits below the threshold count as -inf
-  const float mq = node_reduce(local_max<TL, NV>(wq), MaxOp{}, sh.fscr);
-  const bool tbad = mq == __builtin_inff() || mq == kNegInf;
 
   if (greedy) {   // the target argmax (lowest id), matched against the children's tokens
-    if (tbad) {   // an unusable row poisons the sequence (the walk reports it)
-      if (tid == 0) *out = NodeOut{kNodeRejected, -1, -1, static_cast<uint32_t>(EAGLE_FLAG_NONFINITE), 0, 0};
+    const float mq = node_reduce(local_max<TL, NV>(wq), MaxOp{}, sh.fscr);
+    stamp(a.stamps, 1);   // rows in, their maxima
+    if (mq == __builtin_inff() || mq == kNegInf) {   // an unusable row poisons the sequence (the walk reports it)
+      if (tid == 0) *out = NodeOut{kNodeRejected, -1, -1, static_cast<uint32_t>(EAGLE_FLAG_NONFINITE), 0, 0.f, 0.f, 0.f};
       return;
     }
     int la = 0x7FFFFFFF;
@@ -2324,19 +2365,20 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
           acc = sh.kid[i];
           break;
         }
-      *out = NodeOut{acc >= 0 ? kNodeAccepted : (nkids ? kNodeRejected : kNodeLeaf), acc, am, 0u, 0, 0};
+      *out = NodeOut{acc >= 0 ? kNodeAccepted : (nkids ? kNodeRejected : kNodeLeaf), acc, am, 0u, 0, 0.f, mq, 0.f};
     }
     return;
   }
 
   // each row's exponentials 2^((x - m) c2), kept in registers (token
-  // node_token(jj, e) at index jj G + e; sums in fp64), the target row first, so that a row's logits
-  // die before the next row's exponentials are made; the exponentials unpack
-  // the words again rather than keeping unpacked logits live across the
-  // reduction
+  // node_token(jj, e) at index jj G + e; sums in fp64), the target row first,
+  // so that a row's logits die before the next row's exponentials are made;
+  // the exponentials unpack the words again rather than keeping unpacked
+  // logits live across the reduction
   float xq[kNodePer], xp[kNodePer];
-#pragma unroll
-  for (int jj = 0; jj < NV; ++jj) asm volatile("" : "+v"(wq[jj]));
+  const float mq = node_reduce(local_max<TL, NV>(wq), MaxOp{}, sh.fscr);
+  stamp(a.stamps, 1);   // target row in, its maximum
+  words_opaque<NV>(wq);
   double zq = local_expsum_keep<TL, NV>(wq, mq, a.c2, xq);
   float mp = 0.f;
   double zp = 0.0;
@@ -2344,18 +2386,17 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
     if (kLateDraft) node_load<TL, VEC>(drow, V, wd);
     if (a.thr) cut_groups<TL, NV>(wd, thr_of(a, b, n, 1));
     mp = node_reduce(local_max<TL, NV>(wd), MaxOp{}, sh.fscr);
-#pragma unroll
-    for (int jj = 0; jj < NV; ++jj) asm volatile("" : "+v"(wd[jj]));
+    words_opaque<NV>(wd);
     zp = local_expsum_keep<TL, NV>(wd, mp, a.c2, xp);
   }
-  if (tbad || (two && (mp == __builtin_inff() || mp == kNegInf))) {   // an unusable row (the walk reports it)
-    if (tid == 0) *out = NodeOut{kNodeRejected, -1, -1, static_cast<uint32_t>(EAGLE_FLAG_NONFINITE), 0, 0};
+  if (mq == __builtin_inff() || mq == kNegInf || (two && (mp == __builtin_inff() || mp == kNegInf))) {
+    // an unusable row (the walk reports it)
+    if (tid == 0) *out = NodeOut{kNodeRejected, -1, -1, static_cast<uint32_t>(EAGLE_FLAG_NONFINITE), 0, 0.f, 0.f, 0.f};
     return;
   }
-
-  zq = node_reduce(zq, AddD{}, sh.dscr);
-  if (two) zp = node_reduce(zp, AddD{}, sh.dscr);
+  node_reduce2(zq, zp, AddD{}, sh.dscr);
   const double fq = 1.0 / zq, fp = two ? 1.0 / zp : 0.0;
+  stamp(a.stamps, 2);   // row statistics
 
   uint32_t fl = 0;
   int32_t nr = filter_near(a, b, n, nkids > 0);
@@ -2400,48 +2441,136 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
       }
     }
   }
-  int final_tok = -1, near_end = 0;
-  if (kind != kNodeAccepted) {
-    // The sample: the smallest token whose running sum of the weights
-    // exceeds u * S.  Weights in units of 1/fq (no common factor changes the
-    // comparison): max(0, e_q - K e_p), e_q at a leaf (no draft row, K = 0).
-    // In token order: per-group sums (a thread's word jj is group
-    // jj * kNodeThreads + tid), one block scan per group column, the first
-    // group reaching u * S by a block minimum, then that group's G tokens in
-    // order by the thread that holds it.
-    if (kind == kNodeLeaf) {
-#pragma unroll
-      for (int j = 0; j < kNodePer; ++j) xp[j] = 0.f;
+  stamp(a.stamps, 3);   // tests and residual rounds done
+  stamp_value(a.stamps, 30, static_cast<uint64_t>(kind));
+  if (tid == 0) {
+    const float K = kind == kNodeRejected ? static_cast<float>(C * fp / fq) : 0.f;
+    *out = NodeOut{kind, outcome, -1, fl, nr, K, mq, two ? mp : 0.f};
+  }
+}
+
+// One 512-thread workgroup per sequence: wave 0 validates the tree and walks
+// the decided nodes from the root; then (sampled mode) the whole workgroup
+// draws the emitted token at the node where the walk ends, from that node's
+// rows: the smallest token whose running sum of the weights max(0, e_q -
+// K e_p) exceeds u * S (e_q alone at a leaf), the exponentials recomputed
+// exactly as the node's workgroup computed them.  In token order: per-group
+// sums (a thread's word jj is group jj * kNodeThreads + tid), one block scan
+// per group column, the first group reaching u * S by a block minimum, then
+// that group's G tokens in order by the thread that holds it.
+template <typename TL, bool VEC>
+__global__ __launch_bounds__(kNodeThreads) void sa_finish(const AcceptKernelArgs a) {
+  __shared__ NodeOut no[kMaxTree];
+  __shared__ int32_t path[kMaxTree];
+  __shared__ int32_t walk[4];   // length, final node, bad flags, 0
+  __shared__ uint32_t wflags;
+  __shared__ int32_t wnear;
+  __shared__ double cscan[kNodePer / 4][kNodeWaves];   // per group column and wave: weight totals
+  __shared__ int32_t iscr[kNodeWaves];
+  __shared__ int32_t hit, hitnear;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x, T = a.T, V = a.V;
+  const int64_t mslot = static_cast<int64_t>(a.B) * T + b;   // timeline slot
+  if (a.stamps && tid == 0) a.stamps[mslot * 32] = __builtin_amdgcn_s_memrealtime();
+  if (wave == 0) {
+    const int par = lane < T ? a.parents[b * T + lane] : -1;
+    const int tok = lane < T ? a.tokens[b * T + lane] : -1;
+    const bool tree_bad = __any(lane < T && (lane == 0 ? par != -1 : (par < 0 || par >= lane)));
+    const uint64_t padm = __ballot(lane >= 1 && lane < T && tok == -1);
+    const int nreal = padm ? __ffsll(static_cast<long long>(padm)) - 1 : T;
+    const bool pad_bad = __any(lane >= nreal && lane < T && tok != -1);   // padding must be a suffix
+    const bool tok_bad = __any(lane >= 1 && lane < nreal && (tok < 0 || tok >= V));
+    if (lane < nreal) no[lane] = reinterpret_cast<const NodeOut*>(a.nodes)[static_cast<int64_t>(b) * T + lane];
+    const bool nonfinite = __any(lane < nreal && (no[lane].flags & EAGLE_FLAG_NONFINITE));
+    uint32_t bad = 0;
+    if (tree_bad || pad_bad) bad = EAGLE_FLAG_BAD_TREE;
+    else bad = (tok_bad ? EAGLE_FLAG_BAD_TOKEN : 0u) | (nonfinite ? EAGLE_FLAG_NONFINITE : 0u);
+    if (lane == 0) {
+      walk[2] = static_cast<int32_t>(bad);
+      if (!bad) {
+        int cur = 0, len = 0, near = 0;
+        uint32_t fl = 0;
+        for (;;) {
+          const NodeOut o = no[cur];
+          fl |= o.flags;
+          near += o.near_visit;
+          if (o.kind != kNodeAccepted) break;
+          path[len++] = o.outcome;
+          cur = o.outcome;
+        }
+        walk[0] = len;
+        walk[1] = cur;
+        wflags = fl;
+        wnear = near;
+      }
     }
-    const float K = kind == kNodeLeaf ? 0.f : static_cast<float>(C * fp / fq);
-    auto weight = [&](int j) __attribute__((always_inline)) -> double {
-      return static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, xp[j], xq[j])));
+  }
+  __syncthreads();
+  const uint32_t bad = static_cast<uint32_t>(walk[2]);
+  if (bad) {   // an unusable input: every integer output -1
+    if (tid == 0) {
+      a.accept_len[b] = -1;
+      a.flags[b] = bad;
+      a.near_ties[b] = 0;
+    }
+    for (int j = tid; j < T; j += kNodeThreads) {
+      a.accepted_nodes[b * T + j] = -1;
+      a.out_tokens[b * T + j] = -1;
+    }
+    return;
+  }
+  const int len = walk[0], nt = walk[1];
+  const NodeOut o = no[nt];
+  int final_tok;
+  int near_end = 0;
+  if (a.tau == 0.f) {
+    final_tok = o.argmax;
+  } else {
+    constexpr int G = Pack<TL>::G, NV = kNodePer / G;
+    const bool leaf = o.kind == kNodeLeaf;
+    const int64_t rowoff = static_cast<int64_t>(b * T + nt) * V;
+    u32x4_t wq[NV], wd[NV];
+    node_load<TL, VEC>(reinterpret_cast<const TL*>(a.target) + rowoff, V, wq);
+    if (a.thr) cut_groups<TL, NV>(wq, thr_of(a, b, nt, 0));
+    if (leaf) {   // no draft term: logits 0 against the maximum 0 give e_p = 1, and K = 0
+#pragma unroll
+      for (int jj = 0; jj < NV; ++jj) wd[jj] = u32x4_t{0u, 0u, 0u, 0u};
+    } else {
+      node_load<TL, VEC>(reinterpret_cast<const TL*>(a.draft) + rowoff, V, wd);
+      if (a.thr) cut_groups<TL, NV>(wd, thr_of(a, b, nt, 1));
+    }
+    const float K = leaf ? 0.f : o.K, mp = leaf ? 0.f : o.mp;
+    // the weights of this thread's tokens, summed per group (the
+    // exponentials as the node's workgroup made them: ex2 of the same logits
+    // against the same maxima)
+    auto weight = [&](float xq_, float xp_) __attribute__((always_inline)) {
+      return fmaxf(0.f, __builtin_fmaf(-K, ex2(xp_, a.c2, mp), ex2(xq_, a.c2, o.mq)));
     };
     double gw[NV], goff[NV];
     int lastpos = -1;   // this thread's last token with positive weight
 #pragma unroll
+    for (int jj = 0; jj < NV; ++jj) asm volatile("" : "+v"(wq[jj]), "+v"(wd[jj]));
+#pragma unroll
     for (int jj = 0; jj < NV; ++jj) {
+      float fq_[G], fp_[G];
+      Pack<TL>::unpack(wq[jj], fq_);
+      Pack<TL>::unpack(wd[jj], fp_);
       double g = 0.0;
 #pragma unroll
       for (int e = 0; e < G; ++e) {
-        const double w = weight(jj * G + e);
-        g += w;
-        if (w > 0.0) lastpos = max(lastpos, node_token<TL>(jj, e));
+        const float w = weight(fq_[e], fp_[e]);
+        g += static_cast<double>(w);
+        if (w > 0.f) lastpos = node_token<TL>(jj, e);
       }
       gw[jj] = g;
-      __builtin_amdgcn_sched_barrier(0);   // one group's weights in flight at a time
     }
-    // the crossing group's scan recomputes its weights (same arithmetic,
-    // same values) instead of keeping them live across the reductions
-#pragma unroll
-    for (int j = 0; j < kNodePer; ++j) asm volatile("" : "+v"(xq[j]), "+v"(xp[j]));
+    __builtin_amdgcn_sched_barrier(0);
     // per-column exclusive offsets of this thread's groups, column totals
 #pragma unroll
     for (int jj = 0; jj < NV; ++jj) {
       const double incl = wave_scan_add(gw[jj]);
       goff[jj] = incl - gw[jj];
-      if (lane == 63) sh.cscan[jj][wave] = incl;
-      __builtin_amdgcn_sched_barrier(0);
+      if (lane == 63) cscan[jj][wave] = incl;
     }
     __syncthreads();
     double base = 0.0;
@@ -2450,39 +2579,50 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
       double off = base, tot = 0.0;
 #pragma unroll
       for (int w = 0; w < kNodeWaves; ++w) {
-        if (w < wave) off += sh.cscan[jj][w];
-        tot += sh.cscan[jj][w];
+        if (w < wave) off += cscan[jj][w];
+        tot += cscan[jj][w];
       }
       goff[jj] += off;
       base += tot;
+      __builtin_amdgcn_sched_barrier(0);   // one column's LDS words in flight at a time
     }
     const double S = base;
-    const double thr = decision_uniform(a, b, n, kSampleSlot) * S;
+    const double thr = decision_uniform(a, b, nt, kSampleSlot) * S;
     // the first group (in token order) whose range reaches past u * S
     int gfirst = 0x7FFFFFFF;
 #pragma unroll
     for (int jj = NV - 1; jj >= 0; --jj)
       if (goff[jj] + gw[jj] > thr) gfirst = jj * kNodeThreads + tid;
-    const int gstar = node_reduce(gfirst, MinI{}, sh.iscr);
+    const int gstar = node_reduce(gfirst, MinI{}, iscr);
     if (gstar != 0x7FFFFFFF && gfirst == gstar) {
+      // that group's tokens again, from the rows (the same logits, so the
+      // same weights), in token order from the group's offset
       const int js = gstar / kNodeThreads;
+      double hi = 0.0;
+#pragma unroll
+      for (int jj = 0; jj < NV; ++jj)
+        if (jj == js) hi = goff[jj];
+      const float thq = a.thr ? thr_of(a, b, nt, 0) : kNegInf, thp = a.thr ? thr_of(a, b, nt, 1) : kNegInf;
+      const TL* const tr = reinterpret_cast<const TL*>(a.target) + rowoff;
+      const TL* const dr = reinterpret_cast<const TL*>(a.draft) + rowoff;
+      float lq[G], lp[G];
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        const int t = gstar * G + e;
+        lq[e] = t < V ? cut(logit<TL>(tr, t), thq) : kNegInf;
+        lp[e] = leaf ? 0.f : (t < V ? cut(logit<TL>(dr, t), thp) : kNegInf);
+      }
       int v = -1, lastg = -1;
-      double lo = 0.0, hi = 0.0;
+      double lo = hi;
 #pragma unroll
-      for (int jj = 0; jj < NV; ++jj) {
-        if (jj != js) continue;
-        hi = goff[jj];
-        lo = hi;
-#pragma unroll
-        for (int e = 0; e < G; ++e) {
-          const double w = weight(jj * G + e);
-          if (w > 0.0) {
-            lastg = node_token<TL>(jj, e);
-            if (v < 0) {
-              lo = hi;
-              hi += w;
-              if (hi > thr) v = lastg;
-            }
+      for (int e = 0; e < G; ++e) {
+        const double w = weight(lq[e], lp[e]);
+        if (w > 0.0) {
+          lastg = gstar * G + e;
+          if (v < 0) {
+            lo = hi;
+            hi += w;
+            if (hi > thr) v = lastg;
           }
         }
       }
@@ -2490,79 +2630,30 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
         v = lastg;
         lo = hi = thr;
       }
-      sh.hit = v;
-      sh.sample[0] = ((hi - thr) < kNearTie * S || (thr - lo) < kNearTie * S) ? 1.0 : 0.0;
+      hit = v;
+      hitnear = ((hi - thr) < kNearTie * S || (thr - lo) < kNearTie * S) ? 1 : 0;
     }
     if (gstar == 0x7FFFFFFF) {   // no crossing at all: the last token with positive weight
-      const int lm = node_reduce(lastpos, [](int x, int y) { return x > y ? x : y; }, sh.iscr);
+      const int lm = node_reduce(lastpos, [](int x, int y) { return x > y ? x : y; }, iscr);
       if (tid == 0) {
-        sh.hit = lm;
-        sh.sample[0] = 0.0;
+        hit = lm;
+        hitnear = 0;
       }
     }
     __syncthreads();
-    final_tok = sh.hit;
-    near_end = sh.sample[0] > 0.0 ? 1 : 0;
+    final_tok = hit;
+    near_end = hitnear;
   }
-  if (tid == 0) *out = NodeOut{kind, outcome, final_tok, fl, nr, near_end};
-}
-
-// One wave per sequence: validation, then the walk over the decided nodes.
-__global__ __launch_bounds__(64) void sa_walk(const AcceptKernelArgs a) {
-  __shared__ NodeOut no[kMaxTree];
-  __shared__ int32_t path[kMaxTree];
-  const int lane = threadIdx.x, b = blockIdx.x, T = a.T, V = a.V;
-  const int par = lane < T ? a.parents[b * T + lane] : -1;
-  const int tok = lane < T ? a.tokens[b * T + lane] : -1;
-  const bool tree_bad = __any(lane < T && (lane == 0 ? par != -1 : (par < 0 || par >= lane)));
-  const uint64_t padm = __ballot(lane >= 1 && lane < T && tok == -1);
-  const int nreal = padm ? __ffsll(static_cast<long long>(padm)) - 1 : T;
-  const bool pad_bad = __any(lane >= nreal && lane < T && tok != -1);   // padding must be a suffix
-  const bool tok_bad = __any(lane >= 1 && lane < nreal && (tok < 0 || tok >= V));
-  if (lane < nreal) no[lane] = reinterpret_cast<const NodeOut*>(a.nodes)[static_cast<int64_t>(b) * T + lane];
-  const bool nonfinite = __any(lane < nreal && (no[lane].flags & EAGLE_FLAG_NONFINITE));
-  uint32_t bad = 0;
-  if (tree_bad || pad_bad) bad = EAGLE_FLAG_BAD_TREE;
-  else bad = (tok_bad ? EAGLE_FLAG_BAD_TOKEN : 0u) | (nonfinite ? EAGLE_FLAG_NONFINITE : 0u);
-  if (bad) {
-    if (lane == 0) {
-      a.accept_len[b] = -1;
-      a.flags[b] = bad;
-      a.near_ties[b] = 0;
-    }
-    for (int j = lane; j < T; j += 64) {
-      a.accepted_nodes[b * T + j] = -1;
-      a.out_tokens[b * T + j] = -1;
-    }
-    return;
-  }
-  __shared__ int32_t walk_len, walk_final;
-  if (lane == 0) {
-    int cur = 0, len = 0, near = 0;
-    uint32_t fl = 0;
-    for (;;) {
-      const NodeOut o = no[cur];
-      fl |= o.flags;
-      near += o.near_visit;
-      if (o.kind != kNodeAccepted) {
-        near += o.near_end;
-        walk_final = o.final_tok;
-        break;
-      }
-      path[len++] = o.outcome;
-      cur = o.outcome;
-    }
-    walk_len = len;
+  if (tid == 0) {
     a.accept_len[b] = len;
-    a.flags[b] = fl;
-    a.near_ties[b] = near;
+    a.flags[b] = wflags;
+    a.near_ties[b] = wnear + near_end;
   }
-  __syncthreads();
-  const int len = walk_len;
-  for (int j = lane; j < T; j += 64) {
+  for (int j = tid; j < T; j += kNodeThreads) {
     a.accepted_nodes[b * T + j] = j < len ? path[j] : -1;
-    a.out_tokens[b * T + j] = j < len ? a.tokens[b * T + path[j]] : (j == len ? walk_final : -1);
+    a.out_tokens[b * T + j] = j < len ? a.tokens[b * T + path[j]] : (j == len ? final_tok : -1);
   }
+  if (a.stamps && tid == 0) a.stamps[mslot * 32 + 1] = __builtin_amdgcn_s_memrealtime();
 }
 
 // The fused kernel's workgroups wait for each other: launched cooperatively,
@@ -2584,7 +2675,8 @@ hipError_t launch_t(const AcceptKernelArgs& a, hipStream_t st) {
     else hipLaunchKernelGGL((sa_node<TL, false>), grid, dim3(kNodeThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sa_walk, dim3(static_cast<unsigned>(a.B)), dim3(64), 0, st, a);
+    if (a.vec_ok) hipLaunchKernelGGL((sa_finish<TL, true>), dim3(static_cast<unsigned>(a.B)), dim3(kNodeThreads), 0, st, a);
+    else hipLaunchKernelGGL((sa_finish<TL, false>), dim3(static_cast<unsigned>(a.B)), dim3(kNodeThreads), 0, st, a);
     return hipGetLastError();
   }
   if (a.fused) {

@@ -211,6 +211,7 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
   const bool np = npv && (npv[0] == '0' || npv[0] == '1') ? npv[0] == '1' : np_auto;
   if (V <= kNodeVocab && !k.wr && np) {
     k.fused = 2;
+    k.stamps = (stamps && static_cast<int64_t>(k.B) * (k.T + 1) * kStampSlots <= stamp_words) ? stamps : nullptr;
     const int e = launch_spec_accept(k, bf16, hip_stream);
     if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
     return EAGLE_OK;

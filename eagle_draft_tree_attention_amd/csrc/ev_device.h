@@ -52,6 +52,14 @@ __device__ __forceinline__ void stamp_value(uint64_t* stamps, int k, uint64_t v)
   if (stamps && threadIdx.x == 0) stamps[static_cast<int64_t>(blockIdx.x) * 32 + k] = v;
 }
 
+// where the workgroup runs: the hardware-id register (shader engine, CU,
+// SIMD, wave slot) in the low word, the XCD's index in the high word
+__device__ __forceinline__ uint64_t placement() {
+  const uint32_t hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);     // HW_ID, all 32 bits
+  const uint32_t xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // XCC_ID, all 32 bits
+  return (static_cast<uint64_t>(xcc) << 32) | hw;
+}
+
 __device__ __forceinline__ void publish(uint64_t* w, uint64_t v) {
   stores_done();
   __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

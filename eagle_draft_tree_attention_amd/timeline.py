@@ -22,6 +22,8 @@ ATTN_MARKS = {0: "start", 1: "parents and query rows landed", 2: "ancestor words
 CHUNK_MARKS = {0: "start", 1: "chunk maximum", 2: "statistics and the waves' lists", 3: "record written"}
 SEL_MARKS = {0: "start", 1: "row 0: records in", 2: "row 0: normaliser", 3: "row 0 merged", 4: "rows merged",
              5: "ranked", 6: "outputs written"}
+NODE_MARKS = {0: "start", 1: "target row in, its maximum", 2: "row statistics", 3: "tests and rounds done"}
+FINISH_MARKS = {0: "start", 1: "outputs written"}
 ACC_MARKS = {0: "start", 1: "chunk in LDS", 2: "chunk statistics", 3: "row statistics combined",
              4: "first decision", 17: "node decided", 18: "terminal preparation starts",
              19: "terminal chunk known", 20: "walk ends here", 21: "outputs written"}
@@ -44,6 +46,98 @@ def _stats(x):
         return "n=     0"
     return (f"n={x.size:6d}  p10 {np.percentile(x, 10):7.2f}  med {np.median(x):7.2f}  "
             f"p90 {np.percentile(x, 90):7.2f}  max {x.max():7.2f}")
+
+
+def _node_parallel_section(acc_rows, B, T, tick):
+    print(f"\n## sa_node: {B * T} workgroups (one per node: {B} sequences x {T} nodes), "
+          f"then sa_finish: {B} workgroups (one per sequence)")
+    marks = {k: [] for k in NODE_MARKS}
+    fmarks = {k: [] for k in FINISH_MARKS}
+    durs = {"load + maximum": (0, 1), "statistics": (1, 2), "tests and rounds": (2, 3)}
+    dv = {k: [] for k in durs}
+    fin, ends = [], []
+    kinds = {}
+    for w in acc_rows:
+        n, f = w[:B * T], w[B * T:B * T + B]
+        t0 = n[:, 0][n[:, 0] > 0].min()
+        ends.append((max(n[:, :4].max(), f[:, :2].max()) - t0) * tick)
+        for k in NODE_MARKS:
+            sel = n[:, k] > 0
+            marks[k].extend(((n[sel, k] - t0) * tick).tolist())
+        for k in FINISH_MARKS:
+            sel = f[:, k] > 0
+            fmarks[k].extend(((f[sel, k] - t0) * tick).tolist())
+        for name, (x, y) in durs.items():
+            sel = (n[:, x] > 0) & (n[:, y] > 0)
+            dv[name].extend(((n[sel, y] - n[sel, x]) * tick).tolist())
+        sel = (f[:, 0] > 0) & (f[:, 1] > 0)
+        fin.extend(((f[sel, 1] - f[sel, 0]) * tick).tolist())
+        for kd in n[n[:, 3] > 0, 30]:
+            kinds[int(kd)] = kinds.get(int(kd), 0) + 1
+    for k, name in NODE_MARKS.items():
+        print(f"  sa_node   mark {k} {name:32s} {_stats(marks[k])}")
+    for k, name in FINISH_MARKS.items():
+        print(f"  sa_finish mark {k} {name:32s} {_stats(fmarks[k])}")
+    print("  per-workgroup phase durations:")
+    for name in durs:
+        print(f"    sa_node {name:30s}     {_stats(dv[name])}")
+    print(f"    sa_finish walk and sample              {_stats(fin)}")
+    print(f"  last mark of the launches                     {_stats(ends)}")
+    # consecutive workgroups on one compute unit (placement word: XCD index high, hardware id low;
+    # the CU is the hardware id's bits 8..15, shader engine and CU number)
+    gaps, per_cu = [], []
+    for w in acc_rows:
+        n = w[:B * T]
+        live = (n[:, 0] > 0) & (n[:, 3] > 0)
+        cu = (n[:, 29] >> 32) * 256 + ((n[:, 29] >> 8) & 0xFF)
+        for c in np.unique(cu[live]):
+            sel = np.where(live & (cu == c))[0]
+            order = sel[np.argsort(n[sel, 0])]
+            per_cu.append(len(order))
+            for x, y in zip(order[:-1], order[1:]):
+                gaps.append((n[y, 0] - n[x, 3]) * tick)
+    if per_cu:
+        print(f"  sa_node workgroups per compute unit            {_stats(per_cu)}")
+        print(f"  sa_node gap, one workgroup's last mark to the next one's start on that unit {_stats(gaps)}")
+    names = {0: "leaf", 1: "accepted", 2: "rejected"}
+    print("  decided nodes by kind: " + ", ".join(f"{names.get(k, k)}: {c}" for k, c in sorted(kinds.items())))
+
+
+def _fused_section(acc_rows, B, T, V, tick):
+    NC = (V + 8191) // 8192
+    print(f"\n## sa_fused: {B * T * NC} workgroups ({B} sequences x {T} nodes x {NC} vocabulary chunks)")
+    marks = {k: [] for k in ACC_MARKS}
+    rounds_hist = {}
+    round_durs, first_round, terminal, sample_tail, ends = [], [], [], [], []
+    for w in acc_rows:
+        t0 = w[:, 0][w[:, 0] > 0].min()
+        ends.append((w[:, :22].max() - t0) * tick)
+        for k in ACC_MARKS:
+            sel = w[:, k] > 0
+            marks[k].extend(((w[sel, k] - t0) * tick).tolist())
+        live = w[:, 0] > 0
+        nr = w[:, 30]
+        for r in np.unique(nr[live & (w[:, 17] > 0)]):
+            rounds_hist[int(r)] = rounds_hist.get(int(r), 0) + int(((nr == r) & live & (w[:, 17] > 0)).sum())
+        for i in range(12):
+            prev = 4 + i if i > 0 else 4
+            sel = (w[:, 5 + i] > 0) & (w[:, prev] > 0)
+            d = (w[sel, 5 + i] - w[sel, prev]) * tick
+            (first_round if i == 0 else round_durs).extend(d.tolist())
+        sel = (w[:, 18] > 0) & (w[:, 19] > 0)
+        terminal.extend(((w[sel, 19] - w[sel, 18]) * tick).tolist())
+        sel = (w[:, 20] > 0) & (w[:, 21] > 0)
+        sample_tail.extend(((w[sel, 21] - w[sel, 20]) * tick).tolist())
+    for k, name in ACC_MARKS.items():
+        print(f"  mark {k:2d} {name:39s} {_stats(marks[k])}")
+    print("  per-workgroup phase durations:")
+    print(f"    first residual round                      {_stats(first_round)}")
+    print(f"    later residual rounds                     {_stats(round_durs)}")
+    print(f"    terminal preparation (18 -> 19)           {_stats(terminal)}")
+    print(f"    terminal sample and outputs (20 -> 21)    {_stats(sample_tail)}")
+    print(f"  last mark of the launch                       {_stats(ends)}")
+    print("  workgroups by residual rounds of their node: " +
+          ", ".join(f"{r}: {c}" for r, c in sorted(rounds_hist.items())))
 
 
 def main(argv=None):
@@ -127,7 +221,7 @@ def main(argv=None):
         verify.eagle_verify_spec_accept(ver.handle, acc_args[j], sptr)
         torch.cuda.synchronize()
         nwg = B * T * ((V + 8191) // 8192)
-        acc_rows.append(words[: nwg * SLOTS].view(-1, SLOTS).cpu().numpy().copy())
+        acc_rows.append(words[: max(nwg, B * T + B) * SLOTS].view(-1, SLOTS).cpu().numpy().copy())
     exp_rows = []
     if args.expand:
         F, KE, ME = 8, 4, 8
@@ -180,41 +274,13 @@ def main(argv=None):
     print(f"  last mark of the launch                       {_stats(ends)}")
     print(f"  tiles per workgroup: min {min(tiles)} max {max(tiles)}")
 
-    # ---- acceptance
-    NC = (V + 8191) // 8192
-    print(f"\n## sa_fused: {B * T * NC} workgroups ({B} sequences x {T} nodes x {NC} vocabulary chunks)")
-    marks = {k: [] for k in ACC_MARKS}
-    rounds_hist = {}
-    round_durs, first_round, terminal, sample_tail, ends = [], [], [], [], []
-    for w in acc_rows:
-        t0 = w[:, 0][w[:, 0] > 0].min()
-        ends.append((w[:, :22].max() - t0) * tick)
-        for k in ACC_MARKS:
-            sel = w[:, k] > 0
-            marks[k].extend(((w[sel, k] - t0) * tick).tolist())
-        live = w[:, 0] > 0
-        nr = w[:, 30]
-        for r in np.unique(nr[live & (w[:, 17] > 0)]):
-            rounds_hist[int(r)] = rounds_hist.get(int(r), 0) + int(((nr == r) & live & (w[:, 17] > 0)).sum())
-        for i in range(12):
-            prev = 4 + i if i > 0 else 4
-            sel = (w[:, 5 + i] > 0) & (w[:, prev] > 0)
-            d = (w[sel, 5 + i] - w[sel, prev]) * tick
-            (first_round if i == 0 else round_durs).extend(d.tolist())
-        sel = (w[:, 18] > 0) & (w[:, 19] > 0)
-        terminal.extend(((w[sel, 19] - w[sel, 18]) * tick).tolist())
-        sel = (w[:, 20] > 0) & (w[:, 21] > 0)
-        sample_tail.extend(((w[sel, 21] - w[sel, 20]) * tick).tolist())
-    for k, name in ACC_MARKS.items():
-        print(f"  mark {k:2d} {name:39s} {_stats(marks[k])}")
-    print("  per-workgroup phase durations:")
-    print(f"    first residual round                      {_stats(first_round)}")
-    print(f"    later residual rounds                     {_stats(round_durs)}")
-    print(f"    terminal preparation (18 -> 19)           {_stats(terminal)}")
-    print(f"    terminal sample and outputs (20 -> 21)    {_stats(sample_tail)}")
-    print(f"  last mark of the launch                       {_stats(ends)}")
-    print("  workgroups by residual rounds of their node: " +
-          ", ".join(f"{r}: {c}" for r, c in sorted(rounds_hist.items())))
+    # ---- acceptance: node-parallel kernels (one workgroup per node, then one per sequence) or
+    # the fused kernel (which marks 17, "node decided", in every workgroup; sa_node never does)
+    node_parallel = (acc_rows[0][:, 17] == 0).all() and (acc_rows[0][:B * T, 3] > 0).any()
+    if node_parallel:
+        _node_parallel_section(acc_rows, B, T, tick)
+    else:
+        _fused_section(acc_rows, B, T, V, tick)
     if exp_rows:
         nwg = exp_rows[0].shape[0] - B
         print(f"\n## te_chunk + te_select: {nwg} chunk workgroups ({B} sequences x 8 frontier rows x "
