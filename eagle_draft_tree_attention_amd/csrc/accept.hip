@@ -2378,6 +2378,18 @@ __global__ __launch_bounds__(kNodeThreads) void sa_node(const AcceptKernelArgs a
   float xq[kNodePer], xp[kNodePer];
   const float mq = node_reduce(local_max<TL, NV>(wq), MaxOp{}, sh.fscr);
   stamp(a.stamps, 1);   // target row in, its maximum
+  if (nkids == 0) {
+    // a leaf: a walk that ends here samples from its target row, whose
+    // weights the sampling kernel makes again against this maximum; the
+    // row's sum is not needed
+    stamp(a.stamps, 3);
+    stamp_value(a.stamps, 30, static_cast<uint64_t>(kNodeLeaf));
+    if (tid == 0)
+      *out = (mq == __builtin_inff() || mq == kNegInf)
+                 ? NodeOut{kNodeRejected, -1, -1, static_cast<uint32_t>(EAGLE_FLAG_NONFINITE), 0, 0.f, 0.f, 0.f}
+                 : NodeOut{kNodeLeaf, -1, -1, 0u, filter_near(a, b, n, false), 0.f, mq, 0.f};
+    return;
+  }
   words_opaque<NV>(wq);
   double zq = local_expsum_keep<TL, NV>(wq, mq, a.c2, xq);
   float mp = 0.f;
