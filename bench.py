@@ -413,10 +413,16 @@ def main():
         attn_kernels += " with its split merge inside"
     elif aplan.merge_workgroups > 0:
         attn_kernels += " + tree_attn_merge"
+    apaths = ver.last_accept_paths()
+    acc_kernels = " + ".join(name for bit, name in ((ev.ACCEPT_PATH_NODE_PARALLEL, "sa_node + sa_finish"),
+                                                    (ev.ACCEPT_PATH_FUSED, "sa_fused"),
+                                                    (ev.ACCEPT_PATH_THREE_KERNEL, "sa_stats + sa_pass + sa_final"))
+                             if apaths & bit)
     rooflines = {
         "tree_attention": roofline(f"{attn_kernels} (one tree_attention call)",
                                    nb["attention_bytes"], float(attn_ms.mean()) * 1e-3),
-        "spec_accept": roofline("sa_fused (one spec_accept call)", nb["accept_bytes"], float(acc_ms.mean()) * 1e-3),
+        "spec_accept": roofline(f"{acc_kernels} (one spec_accept call)", nb["accept_bytes"],
+                                float(acc_ms.mean()) * 1e-3),
     }
     if expand_ms is not None:
         rooflines["tree_expand"] = roofline(f"te_chunk + te_select (one tree_expand call: {F}-node frontier, "

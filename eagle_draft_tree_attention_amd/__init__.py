@@ -40,9 +40,10 @@ _abi.bind(_lib)
 from .verify import (  # noqa: E402,F401
     eagle_verify_create, eagle_verify_destroy, eagle_verify_tree_attention, eagle_verify_spec_accept,
     eagle_verify_last_error, eagle_verify_check_tree_attention, eagle_verify_check_spec_accept,
-    eagle_verify_last_attention_plan, eagle_verify_kv_commit, eagle_verify_check_kv_commit,
+    eagle_verify_last_attention_plan, eagle_verify_last_accept_paths, eagle_verify_kv_commit, eagle_verify_check_kv_commit,
     eagle_verify_tree_expand, eagle_verify_check_tree_expand, eagle_verify_tree_rerank,
     eagle_verify_check_tree_rerank, eagle_verify_set_timeline, Verifier, make_desc,
+    ACCEPT_PATH_THREE_KERNEL, ACCEPT_PATH_FUSED, ACCEPT_PATH_NODE_PARALLEL,
 )
 
 

@@ -18,7 +18,7 @@ STATUS_NAMES = {0: "EAGLE_OK", 1: "EAGLE_ERR_ARG", 2: "EAGLE_ERR_UNSUPPORTED", 3
 EXPORTED_SYMBOLS = (
     "eagle_verify_create", "eagle_verify_tree_attention", "eagle_verify_spec_accept",
     "eagle_verify_destroy", "eagle_verify_last_error", "eagle_verify_check_tree_attention",
-    "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan", "eagle_verify_kv_commit",
+    "eagle_verify_check_spec_accept", "eagle_verify_last_attention_plan", "eagle_verify_last_accept_paths", "eagle_verify_kv_commit",
     "eagle_verify_check_kv_commit", "eagle_verify_tree_expand", "eagle_verify_check_tree_expand",
     "eagle_verify_tree_rerank", "eagle_verify_check_tree_rerank", "eagle_verify_spec_accept_noalloc",
     "eagle_verify_set_timeline",
@@ -105,6 +105,8 @@ def bind(lib):
     lib.eagle_verify_check_spec_accept.restype = C.c_int
     lib.eagle_verify_last_attention_plan.argtypes = [H, C.POINTER(AttentionPlan)]
     lib.eagle_verify_last_attention_plan.restype = C.c_int
+    lib.eagle_verify_last_accept_paths.argtypes = [H, C.POINTER(C.c_int)]
+    lib.eagle_verify_last_accept_paths.restype = C.c_int
     lib.eagle_verify_set_timeline.argtypes = [H, C.c_void_p, C.c_int64]
     lib.eagle_verify_set_timeline.restype = C.c_int
     lib.eagle_verify_kv_commit.argtypes = [H, C.POINTER(KvCommitArgs), C.c_void_p]

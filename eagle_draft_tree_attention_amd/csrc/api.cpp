@@ -214,6 +214,7 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
     k.stamps = (stamps && static_cast<int64_t>(k.B) * (k.T + 1) * kStampSlots <= stamp_words) ? stamps : nullptr;
     const int e = launch_spec_accept(k, bf16, hip_stream);
     if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
+    cs->last_paths = EAGLE_ACCEPT_PATH_NODE_PARALLEL;
     return EAGLE_OK;
   }
   if (per_seq > cap || k.NC > 64) {
@@ -221,8 +222,10 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
     k.wr_kept = ws.wr_kept;
     const int e = launch_spec_accept(k, bf16, hip_stream);
     if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
+    cs->last_paths = EAGLE_ACCEPT_PATH_THREE_KERNEL;
     return EAGLE_OK;
   }
+  int paths = 0;
   const int slice = static_cast<int>(std::min<int64_t>(k.B, cap / per_seq));
   const int64_t row_bytes = static_cast<int64_t>(V) * esize;
   const AcceptKernelArgs whole = k;
@@ -271,12 +274,15 @@ eagle_status run_spec_accept(const eagle_verify_desc& desc, const Workspace& ws,
       k.wr_kept = ws.wr_kept;
       e = launch_spec_accept(k, bf16, hip_stream);
       if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
+      paths |= EAGLE_ACCEPT_PATH_THREE_KERNEL;
       continue;
     }
     if (e != 0) return hip_fail_to(err, errlen, "spec accept launch", e);
     ++cs->fused_calls;
     cs->last_fused_b = k.B;
+    paths |= EAGLE_ACCEPT_PATH_FUSED;
   }
+  cs->last_paths = paths;
   return EAGLE_OK;
 }
 
@@ -626,6 +632,12 @@ eagle_status eagle_verify_set_timeline(eagle_verify* h, uint64_t* device_words, 
 eagle_status eagle_verify_last_attention_plan(const eagle_verify* h, eagle_attention_plan* plan) {
   if (!h || !plan || !h->have_plan) return EAGLE_ERR_ARG;
   *plan = h->last_plan;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify_last_accept_paths(const eagle_verify* h, int* paths) {
+  if (!h || !paths || h->accept_state.last_paths == 0) return EAGLE_ERR_ARG;
+  *paths = h->accept_state.last_paths;
   return EAGLE_OK;
 }
 

@@ -265,6 +265,7 @@ struct AcceptCallState {
   uint64_t epoch = 0;
   uint64_t fused_calls = 0;
   int last_fused_b = 0;
+  int last_paths = 0;   // EAGLE_ACCEPT_PATH_* bits of the last successful call (0: none yet)
 };
 
 // One spec_accept call on workspace `ws` laid out for Bm x Tm (arguments

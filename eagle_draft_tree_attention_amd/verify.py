@@ -103,6 +103,17 @@ def eagle_verify_last_attention_plan(handle: int) -> AttentionPlan:
     return plan
 
 
+# kernels of a spec_accept call (bits of eagle_verify_last_accept_paths)
+ACCEPT_PATH_THREE_KERNEL, ACCEPT_PATH_FUSED, ACCEPT_PATH_NODE_PARALLEL = 1, 2, 4
+
+
+def eagle_verify_last_accept_paths(handle: int) -> int:
+    """ACCEPT_PATH_* bits of the handle's last successful spec_accept call."""
+    paths = C.c_int(0)
+    _check(_lib().eagle_verify_last_accept_paths(handle, C.byref(paths)), handle)
+    return paths.value
+
+
 # ---------------------------------------------------------------- torch layer
 def eagle_verify_set_timeline(handle: int, device_words: int, num_words: int) -> int:
     return _check(_lib().eagle_verify_set_timeline(handle, device_words, num_words), handle)
@@ -204,6 +215,9 @@ class Verifier:
 
     def last_attention_plan(self) -> AttentionPlan:
         return eagle_verify_last_attention_plan(self.handle)
+
+    def last_accept_paths(self) -> int:
+        return eagle_verify_last_accept_paths(self.handle)
 
     def set_timeline(self, words=None):
         """Diagnostic phase timeline: a contiguous int64 device tensor (32

@@ -412,6 +412,23 @@ EAGLE_API eagle_status eagle_verify_check_kv_commit(const eagle_verify_desc* des
 EAGLE_API eagle_status eagle_verify_check_tree_expand(const eagle_verify_desc* desc, const eagle_tree_expand_args* a);
 EAGLE_API eagle_status eagle_verify_check_tree_rerank(const eagle_verify_desc* desc, const eagle_tree_rerank_args* a);
 
+/* Kernels of the last successful eagle_verify_spec_accept call on h, as a
+ * bitwise OR of the values below (a batch larger than the fused kernel's
+ * co-resident capacity runs in slices, and a slice that cannot be made
+ * resident falls back to the three-kernel path, so a call can use both):
+ *   EAGLE_ACCEPT_PATH_THREE_KERNEL  statistics, pass and final kernels;
+ *   EAGLE_ACCEPT_PATH_FUSED         one co-resident kernel per slice;
+ *   EAGLE_ACCEPT_PATH_NODE_PARALLEL one workgroup per node, then one per
+ *                                   sequence (vocabularies up to 32768).
+ * The results do not depend on the path.  No HIP call is made.
+ * Errors: EAGLE_ERR_ARG when h or paths is NULL or h has made no such call. */
+enum {
+  EAGLE_ACCEPT_PATH_THREE_KERNEL = 1,
+  EAGLE_ACCEPT_PATH_FUSED = 2,
+  EAGLE_ACCEPT_PATH_NODE_PARALLEL = 4
+};
+EAGLE_API eagle_status eagle_verify_last_accept_paths(const eagle_verify* h, int* paths);
+
 /* Launch plan of the last successful eagle_verify_tree_attention call on h
  * (merge_in_kernel included).  No HIP call is made.
  * Errors: EAGLE_ERR_ARG when h or plan is NULL or h has made no such call. */

@@ -113,6 +113,14 @@ def test_last_attention_plan_needs_a_call():
     assert lib.eagle_verify_last_attention_plan(None, None) == ev.EAGLE_ERR_ARG
 
 
+def test_last_accept_paths_needs_a_call():
+    import ctypes as C
+    lib = ev.library()
+    paths = C.c_int(0)
+    assert lib.eagle_verify_last_accept_paths(None, C.byref(paths)) == ev.EAGLE_ERR_ARG
+    assert lib.eagle_verify_last_accept_paths(None, None) == ev.EAGLE_ERR_ARG
+
+
 def test_set_timeline_needs_a_handle():
     lib = ev.library()
     assert lib.eagle_verify_set_timeline(None, None, 0) == ev.EAGLE_ERR_ARG

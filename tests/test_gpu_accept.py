@@ -16,6 +16,7 @@ from scipy.stats import chi2 as chi2_dist
 
 import synth
 from gpu_util import compare_accept, dev, excused_bound, log, make_verifier, run_accept, small_spec
+from eagle_draft_tree_attention_amd import verify as ev
 from oracle import accept as oacc
 
 pytestmark = pytest.mark.gpu
@@ -66,6 +67,12 @@ def test_accept_matches_oracle(spec, accept_path):
         diverged += compare_accept(got, ref, f"{spec.name} offset {off}", inp.parents, inp.tokens, spec.vocab)
     log(f"    near-tie divergences: {diverged}")
     assert diverged <= excused_bound(12 * spec.batch)
+    # the path the fixture asked for is the one that ran
+    paths = ver.last_accept_paths()
+    if accept_path == "node_parallel" and spec.vocab <= 32768:
+        assert paths == ev.ACCEPT_PATH_NODE_PARALLEL
+    else:
+        assert paths & ev.ACCEPT_PATH_NODE_PARALLEL == 0 and paths != 0
     again = run_accept(ver, inp, spec.temperature, SEED, 11)
     for key in again:
         assert np.array_equal(again[key], got[key]), "not bitwise deterministic"
@@ -241,6 +248,7 @@ def test_large_batch_in_fused_slices(monkeypatch):
         ref = _oracle(inp, 1.0, off)
         diverged += compare_accept(got, ref, f"large batch offset {off}", inp.parents, inp.tokens, spec.vocab)
     assert diverged <= excused_bound(2 * spec.batch)
+    assert ver.last_accept_paths() & ev.ACCEPT_PATH_FUSED
     ver.close()
 
 
@@ -257,6 +265,7 @@ def test_large_batch_in_one_node_parallel_launch():
         ref = _oracle(inp, 1.0, off)
         diverged += compare_accept(got, ref, f"large batch offset {off}", inp.parents, inp.tokens, spec.vocab)
     assert diverged <= excused_bound(2 * spec.batch)
+    assert ver.last_accept_paths() == ev.ACCEPT_PATH_NODE_PARALLEL   # chosen without the override
     ver.close()
 
 
