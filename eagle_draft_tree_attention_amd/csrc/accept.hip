@@ -1229,6 +1229,13 @@ __device__ __forceinline__ float local_max(const u32x4_t (&w)[NV]) {
 // which grows with |m| (and overflows for |m| near the float range).
 __device__ __forceinline__ float ex2(float x, float c2, float m) { return __builtin_amdgcn_exp2f((x - m) * c2); }
 
+// The per-thread sums below share one order: the thread's values in its
+// token order i = jj G + e, added in pairs (i, i + 1) in fp32 (one rounding,
+// at most 2^-24 relative, below the exponentials' own error), each pair
+// added in fp64 to accumulator (i / 2) mod 4, the accumulators combined as
+// (a0 + a1) + (a2 + a3).  Half the fp64 conversions and additions of a
+// per-value fp64 sum.
+
 // sum of exp((x - m) / tau) over this thread's values, fp64
 template <typename TL, int NV>
 __device__ __forceinline__ double local_expsum(const u32x4_t (&w)[NV], float m, float c2) {
@@ -1238,7 +1245,8 @@ __device__ __forceinline__ double local_expsum(const u32x4_t (&w)[NV], float m, 
     float f[Pack<TL>::G];
     Pack<TL>::unpack(w[jj], f);
 #pragma unroll
-    for (int e = 0; e < Pack<TL>::G; ++e) acc[e & 3] += static_cast<double>(ex2(f[e], c2, m));
+    for (int e = 0; e < Pack<TL>::G; e += 2)
+      acc[((jj * Pack<TL>::G + e) >> 1) & 3] += static_cast<double>(ex2(f[e], c2, m) + ex2(f[e + 1], c2, m));
   }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
@@ -1256,10 +1264,11 @@ __device__ __forceinline__ double local_expsum_keep(const u32x4_t (&w)[NV], floa
     float f[Pack<TL>::G];
     Pack<TL>::unpack(w[jj], f);
 #pragma unroll
-    for (int e = 0; e < Pack<TL>::G; ++e) {
-      const float v = ex2(f[e], c2, ms);
-      ex[jj * Pack<TL>::G + e] = v;
-      acc[e & 3] += static_cast<double>(v);
+    for (int e = 0; e < Pack<TL>::G; e += 2) {
+      const float v0 = ex2(f[e], c2, ms), v1 = ex2(f[e + 1], c2, ms);
+      ex[jj * Pack<TL>::G + e] = v0;
+      ex[jj * Pack<TL>::G + e + 1] = v1;
+      acc[((jj * Pack<TL>::G + e) >> 1) & 3] += static_cast<double>(v0 + v1);
     }
   }
   return live ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : 0.0;
@@ -1267,12 +1276,15 @@ __device__ __forceinline__ double local_expsum_keep(const u32x4_t (&w)[NV], floa
 
 // Residual mass sum max(0, q - C p) of this thread's strided slots from the
 // exponentials the statistics pass kept (the same values local_masses
-// computes from LDS, summed in the same order).
+// computes from LDS, summed in the same pairs and order).
 template <int N>
 __device__ __forceinline__ double kept_masses(const float (&eq)[N], const float (&ep)[N], float K, double fq) {
+  static_assert(N % 2 == 0, "pairs");
   double ra[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int i = 0; i < N; ++i) ra[i & 3] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ep[i], eq[i])));
+  for (int i = 0; i < N; i += 2)
+    ra[(i >> 1) & 3] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ep[i], eq[i])) +
+                                            fmaxf(0.f, __builtin_fmaf(-K, ep[i + 1], eq[i + 1])));
   return ((ra[0] + ra[1]) + (ra[2] + ra[3])) * fq;
 }
 
@@ -1281,7 +1293,7 @@ __device__ __forceinline__ double kept_masses(const float (&eq)[N], const float 
 // scaled logit minus the chunk maximum; mqs / mps are 0 for an all -inf
 // chunk, whose exponentials are then 0), max(0, q - C p) = fq max(0, e_q -
 // K e_p) with K = C fp / fq: per token two exp2, one fma and one max in
-// fp32, accumulated in fp64.
+// fp32, token pairs added in fp32, the pairs accumulated in fp64.
 template <typename TL, int NV>
 __device__ __forceinline__ void local_masses(const TL* lq, const TL* lp, bool use_p, float mqs, float mps, float c2,
                                              double fq, double fp, double C, double& res, double& qsum) {
@@ -1299,10 +1311,13 @@ __device__ __forceinline__ void local_masses(const TL* lq, const TL* lp, bool us
     Pack<TL>::unpack(wq[jj], fa);
     if (use_p) Pack<TL>::unpack(wp[jj], fb);
 #pragma unroll
-    for (int e = 0; e < Pack<TL>::G; ++e) {
-      const float eq = ex2(fa[e], c2, mqs);
-      qa[e & 3] += static_cast<double>(eq);
-      if (use_p) ra[e & 3] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ex2(fb[e], c2, mps), eq)));
+    for (int e = 0; e < Pack<TL>::G; e += 2) {
+      const int k = ((jj * Pack<TL>::G + e) >> 1) & 3;
+      const float eq0 = ex2(fa[e], c2, mqs), eq1 = ex2(fa[e + 1], c2, mqs);
+      qa[k] += static_cast<double>(eq0 + eq1);
+      if (use_p)
+        ra[k] += static_cast<double>(fmaxf(0.f, __builtin_fmaf(-K, ex2(fb[e], c2, mps), eq0)) +
+                                     fmaxf(0.f, __builtin_fmaf(-K, ex2(fb[e + 1], c2, mps), eq1)));
     }
   }
   qsum = ((qa[0] + qa[1]) + (qa[2] + qa[3])) * fq;
