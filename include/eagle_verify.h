@@ -420,7 +420,9 @@ EAGLE_API eagle_status eagle_verify_check_tree_rerank(const eagle_verify_desc* d
  *   EAGLE_ACCEPT_PATH_FUSED         one co-resident kernel per slice;
  *   EAGLE_ACCEPT_PATH_NODE_PARALLEL one workgroup per node, then one per
  *                                   sequence (vocabularies up to 32768).
- * The results do not depend on the path.  No HIP call is made.
+ * Every path applies the same rule; their sums run in different orders, so
+ * their results can differ only where a near tie is reported (near_ties).
+ * No HIP call is made.
  * Errors: EAGLE_ERR_ARG when h or paths is NULL or h has made no such call. */
 enum {
   EAGLE_ACCEPT_PATH_THREE_KERNEL = 1,
