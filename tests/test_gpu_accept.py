@@ -486,7 +486,7 @@ FILTER_CASES = [
 
 
 @pytest.mark.parametrize("spec,k,p", FILTER_CASES, ids=[c[0].name for c in FILTER_CASES])
-def test_filtered_distributions(spec, k, p):
+def test_filtered_distributions(spec, k, p, accept_path):
     """top-k / top-p filtered target and draft rows (thresholds found by the
     filter kernel), children drawn from the filtered drafts."""
     log(f"[accept] filtered: {spec.name} top_k {k} top_p {p}")
@@ -502,6 +502,8 @@ def test_filtered_distributions(spec, k, p):
         diverged += compare_accept(got, ref, f"{spec.name} offset {off}", inp.parents, tok, spec.vocab)
     log(f"    near-tie divergences: {diverged}")
     assert diverged <= excused_bound(6 * spec.batch)
+    if accept_path == "node_parallel":
+        assert ver.last_accept_paths() == ev.ACCEPT_PATH_NODE_PARALLEL
     ver.close()
 
 
@@ -525,7 +527,7 @@ def test_filtered_distributions_at_the_8b_shape_and_three_kernel_path():
         ver.close()
 
 
-def test_filter_edge_rows():
+def test_filter_edge_rows(accept_path):
     """Rows the threshold search must resolve by its special cases: all
     logits equal (one value), two tied plateaus, a range of 2e37 (coarse first
     bins), -inf entries beyond top-k, a bf16-like row of few distinct values,
@@ -570,6 +572,8 @@ def test_filter_edge_rows():
             assert (ref["flags"] & 7).tolist() == [0] * B
             diverged += compare_accept(got, ref, f"edges k {k} p {p} offset {off}", par, tok, V)
         assert diverged <= 1
+        if accept_path == "node_parallel":
+            assert ver.last_accept_paths() == ev.ACCEPT_PATH_NODE_PARALLEL
     ver.close()
 
 
