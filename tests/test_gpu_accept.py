@@ -177,7 +177,7 @@ def test_root_only_tree_draws_bonus_from_target(accept_path):
     ver.close()
 
 
-def test_lossless_statistics_over_offsets():
+def test_lossless_statistics_over_offsets(accept_path):
     """Root with three i.i.d. draft children: the first emitted token follows
     the target distribution (chi-square), and every run equals the oracle."""
     log("[accept] chi-square over Philox offsets")
@@ -425,7 +425,7 @@ def test_without_replacement_on_the_three_kernel_path():
     ver.close()
 
 
-def test_expected_accept_length_of_a_fixed_tree_on_gpu():
+def test_expected_accept_length_of_a_fixed_tree_on_gpu(accept_path):
     """The GPU's mean accepted length over Philox offsets equals the
     probability flow of a fixed three-level tree (the same tree as the
     oracle's pin), and every run equals the oracle."""
